@@ -1,0 +1,43 @@
+"""Reader for the hand-worked block fixtures in tests/golden/."""
+import glob
+import os
+import re
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _value(tok: str) -> float:
+    m = re.fullmatch(r"(-?[0-9.]+)\*2\^(-?[0-9]+)", tok)
+    if m:
+        return float(m.group(1)) * 2.0 ** int(m.group(2))
+    return float(tok)
+
+
+def load(path: str) -> dict:
+    out = {"name": os.path.basename(path)}
+    with open(path) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, _, rest = line.partition(":")
+            toks = rest.split()
+            if key == "format":
+                out["format"] = toks[0]
+            elif key in ("weights", "dequant"):
+                vals = [_value(t) for t in toks]
+                arr = np.array(vals, dtype=np.float64)
+                if key == "weights":
+                    w32 = arr.astype(np.float32)
+                    assert np.array_equal(w32.astype(np.float64), arr), f"{path}: weight not exact in fp32"
+                    arr = w32
+                out[key] = arr
+            elif key == "bytes":
+                out["bytes"] = np.array([int(t, 16) for t in toks], dtype=np.uint8)
+    return out
+
+
+def all_blocks():
+    return [load(p) for p in sorted(glob.glob(os.path.join(GOLDEN, "*.txt"))) if not p.endswith("README.txt")]

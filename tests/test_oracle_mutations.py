@@ -1,0 +1,125 @@
+"""Planted mistakes in the oracle (on the CPU): each plausible slip must make
+at least one pin in tests/test_oracle.py fail. This shows the pins can tell a
+wrong oracle from a right one."""
+import numpy as np
+import pytest
+
+from oracle import formats as F
+from oracle import ref as R
+from tests import test_oracle as T
+
+
+def _fails(check, *args) -> bool:
+    try:
+        check(*args)
+    except AssertionError:
+        return True
+    return False
+
+
+def _any_golden_fails(fmt=None) -> bool:
+    return any(_fails(T.check_golden_block, b) for b in T.BLOCKS if fmt is None or b["format"] == fmt)
+
+
+def test_half_even_rounding_is_caught(monkeypatch):
+    monkeypatch.setattr(F, "round_half_away", lambda v: np.round(np.asarray(v, np.float64)))
+    assert _any_golden_fails("q8_0")
+
+
+def test_naive_fp32_rounding_is_caught():
+    # trunc(v + 0.5f) in fp32 rounds 0.5 - 2^-25 up to 1.
+    v = np.float32(0.5 - 2.0 ** -25)
+    assert np.trunc(v + np.float32(0.5)) == 1.0
+    assert F.round_half_away(v) == 0.0
+
+
+def test_swapped_nibble_order_is_caught(monkeypatch):
+    monkeypatch.setattr(F, "_nibbles", lambda q: (q[..., 16:] | (q[..., :16] << 4)).astype(np.uint8))
+    monkeypatch.setattr(F, "_unnibble", lambda nb: np.concatenate([nb >> 4, nb & 0x0F], -1).astype(np.uint8))
+    assert _any_golden_fails("q4_0") and _any_golden_fails("affine4")
+
+
+def test_sequential_nibble_pairs_are_caught(monkeypatch):
+    monkeypatch.setattr(F, "_nibbles", lambda q: (q[..., 0::2] | (q[..., 1::2] << 4)).astype(np.uint8))
+    assert _any_golden_fails("q4_0")
+
+
+def test_last_index_signed_max_is_caught(monkeypatch):
+    orig = F._first_index_value
+
+    def last(B, key, pick_max):
+        rb, rk = B[..., ::-1], key[..., ::-1]
+        return orig(rb, rk, pick_max)
+    monkeypatch.setattr(F, "_first_index_value", last)
+    assert _any_golden_fails("q4_0")
+
+
+def test_positive_scale_q4_0_is_caught(monkeypatch):
+    orig = F.to_f16
+    monkeypatch.setattr(F, "to_f16", lambda v: np.abs(orig(v)))
+    assert _any_golden_fails("q4_0")
+
+
+def test_fp32_scale_for_quants_is_caught(monkeypatch):
+    # quants computed from the unrounded fp32 scale/bias (the stored bytes are
+    # still rounded to fp16 by encode)
+    monkeypatch.setattr(F, "to_f16", lambda v: np.asarray(v, np.float32))
+    assert _any_golden_fails("affine4")
+
+
+def test_dropped_q4_0_offset_is_caught(monkeypatch):
+    orig = F.dequantize
+
+    def bad(fmt, fields, rows=None):
+        if fmt == "q4_0":
+            f2 = dict(fields)
+            f2["q"] = fields["q"].astype(np.int32) + 8     # w' = d*q instead of d*(q-8)
+            return orig(fmt, f2, rows)
+        return orig(fmt, fields, rows)
+    monkeypatch.setattr(F, "dequantize", bad)
+    assert _fails(T.check_unit_vectors, "q4_0")
+
+
+def test_dropped_affine_bias_is_caught(monkeypatch):
+    orig = F.dequantize
+
+    def bad(fmt, fields, rows=None):
+        if fmt == "affine4":
+            f2 = dict(fields)
+            f2["b"] = np.zeros_like(fields["b"])
+            return orig(fmt, f2, rows)
+        return orig(fmt, fields, rows)
+    monkeypatch.setattr(F, "dequantize", bad)
+    assert _fails(T.check_unit_vectors, "affine4")
+
+
+def test_transposed_operand_is_caught(monkeypatch):
+    orig = R.gemv
+
+    def bad(fmt, fields, x16, rows=None):
+        y, a = orig(fmt, fields, x16, rows)
+        return y[:, ::-1], a[:, ::-1]          # rows scrambled
+    monkeypatch.setattr(R, "gemv", bad)
+    assert _fails(T.check_exact_small_gemv, "q8_0", 5, 96, 2, 2)
+
+
+def test_wrong_sign_in_dot_is_caught(monkeypatch):
+    orig = R.gemv
+
+    def bad(fmt, fields, x16, rows=None):
+        y, a = orig(fmt, fields, x16, rows)
+        return -y, a
+    monkeypatch.setattr(R, "gemv", bad)
+    assert _fails(T.check_ones_sum, "affine4")
+
+
+def test_dropped_block_is_caught(monkeypatch):
+    orig = F.dequantize
+
+    def bad(fmt, fields, rows=None):
+        w = orig(fmt, fields, rows)
+        if w.shape[1] > 32:
+            w[:, -32:] = 0
+        return w
+    monkeypatch.setattr(F, "dequantize", bad)
+    assert _fails(T.check_exact_small_gemv, "q4_0", 3, 64, 1, 1)
