@@ -1,0 +1,230 @@
+// kq_api.cpp — the C ABI: argument checks (all on the host, before any HIP
+// call), thread-local error messages, and dispatch to the kernel launchers.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "kq_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return KQ_OK;
+}
+
+bool valid_fmt(int fmt) { return fmt == KQ_Q8_0 || fmt == KQ_Q4_0 || fmt == KQ_AFFINE4_G32; }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int check_fmt_k(int fmt, int64_t K) {
+  if (!valid_fmt(fmt)) return fail(KQ_ERR_FORMAT, "unknown format %d", fmt);
+  if (K <= 0 || K % 32 != 0 || K > KQ_MAX_K)
+    return fail(KQ_ERR_SHAPE, "K=%lld must be a positive multiple of 32 and <= %d", (long long)K, KQ_MAX_K);
+  return KQ_OK;
+}
+
+int check_n(int64_t N, const char* what) {
+  if (N < 0 || N > KQ_MAX_N) return fail(KQ_ERR_ARG, "%s=%lld out of range", what, (long long)N);
+  return KQ_OK;
+}
+
+int hip_status(int err, const char* where) {
+  if (err == 0) return ok();
+  return fail(KQ_ERR_HIP, "%s: HIP error %d (%s)", where, err, kq::hip_error_string(err));
+}
+
+}  // namespace
+
+extern "C" {
+
+int kq_version(void) { return KQ_VERSION; }
+
+const char* kq_status_string(int status) {
+  switch (status) {
+    case KQ_OK: return "KQ_OK";
+    case KQ_ERR_ARG: return "KQ_ERR_ARG";
+    case KQ_ERR_FORMAT: return "KQ_ERR_FORMAT";
+    case KQ_ERR_SHAPE: return "KQ_ERR_SHAPE";
+    case KQ_ERR_ALIGN: return "KQ_ERR_ALIGN";
+    case KQ_ERR_RANGE: return "KQ_ERR_RANGE";
+    case KQ_ERR_HIP: return "KQ_ERR_HIP";
+    default: return "KQ_ERR_UNKNOWN";
+  }
+}
+
+const char* kq_last_error(void) { return g_err; }
+
+int64_t kq_block_bytes(int fmt) {
+  if (!valid_fmt(fmt)) return fail(KQ_ERR_FORMAT, "unknown format %d", fmt);
+  return kq::block_bytes(fmt);
+}
+
+int64_t kq_packed_bytes(int fmt, int64_t N, int64_t K) {
+  int st = check_fmt_k(fmt, K);
+  if (st) return st;
+  if ((st = check_n(N, "N"))) return st;
+  return N * (K / 32) * kq::block_bytes(fmt);
+}
+
+int kq_pack(int fmt, const float* W, int64_t N, int64_t K, void* out, int n_threads) {
+  int st = check_fmt_k(fmt, K);
+  if (st) return st;
+  if ((st = check_n(N, "N"))) return st;
+  if (N > 0 && (!W || !out)) return fail(KQ_ERR_ARG, "kq_pack: null pointer");
+  st = kq::pack(fmt, W, N, K, out, n_threads);
+  if (st == KQ_ERR_RANGE)
+    return fail(st, "kq_pack: non-finite weight, or a scale/bias that overflows fp16");
+  return st ? st : ok();
+}
+
+int kq_unpack(int fmt, const void* packed, int64_t N, int64_t K, float* W_out) {
+  int st = check_fmt_k(fmt, K);
+  if (st) return st;
+  if ((st = check_n(N, "N"))) return st;
+  if (N > 0 && (!packed || !W_out)) return fail(KQ_ERR_ARG, "kq_unpack: null pointer");
+  return kq::unpack(fmt, packed, N, K, W_out) ? KQ_ERR_ARG : ok();
+}
+
+int kq_f32_to_f16(const float* in, uint16_t* out, int64_t n) {
+  if (n < 0 || (n > 0 && (!in || !out))) return fail(KQ_ERR_ARG, "kq_f32_to_f16: bad arguments");
+  for (int64_t i = 0; i < n; ++i) out[i] = kq::f32_to_f16_bits(in[i]);
+  return ok();
+}
+
+int kq_gemv(int fmt, const void* W, const uint16_t* x, float* y, int64_t N, int64_t K, int M,
+            void* stream) {
+  int st = check_fmt_k(fmt, K);
+  if (st) return st;
+  if ((st = check_n(N, "N"))) return st;
+  if (M < 0 || M > KQ_MAX_M) return fail(KQ_ERR_ARG, "M=%d must be in [0, %d]", M, KQ_MAX_M);
+  if (M == 0 || N == 0) return ok();
+  if (!W || !x || !y) return fail(KQ_ERR_ARG, "kq_gemv: null pointer");
+  if (!aligned(W, 4) || !aligned(y, 4)) return fail(KQ_ERR_ALIGN, "kq_gemv: W and y must be 4-byte aligned");
+  if (!aligned(x, 16)) return fail(KQ_ERR_ALIGN, "kq_gemv: x must be 16-byte aligned");
+  kq::GemvArgs a{fmt, static_cast<const uint8_t*>(W), x, y, N, K, M, static_cast<hipStream_t>(stream)};
+  return hip_status(kq::launch_gemv(a), "kq_gemv");
+}
+
+int64_t kq_moe_gemv_workspace_bytes(int64_t N, int M, int top_k, int weighted) {
+  if (N < 0 || M < 0 || top_k < 0) return fail(KQ_ERR_ARG, "negative size");
+  if (!weighted) return 0;
+  return (int64_t)M * top_k * N * 4;
+}
+
+static int check_moe_common(int fmt, const void* Wexp, int64_t N, int64_t K, int M, int top_k,
+                            int n_experts) {
+  int st = check_fmt_k(fmt, K);
+  if (st) return st;
+  if ((st = check_n(N, "N"))) return st;
+  if (M < 0 || M > KQ_MAX_M) return fail(KQ_ERR_ARG, "M=%d must be in [0, %d]", M, KQ_MAX_M);
+  if (n_experts < 1) return fail(KQ_ERR_ARG, "n_experts=%d must be >= 1", n_experts);
+  if (top_k < 1 || top_k > n_experts || top_k > 64)
+    return fail(KQ_ERR_ARG, "top_k=%d must be in [1, min(n_experts, 64)]", top_k);
+  const int64_t per = N * (K / 32) * kq::block_bytes(fmt);
+  if (per > 0 && n_experts > INT64_MAX / per) return fail(KQ_ERR_ARG, "expert table too large");
+  if (!aligned(Wexp, 4)) return fail(KQ_ERR_ALIGN, "expert weights must be 4-byte aligned");
+  return KQ_OK;
+}
+
+int kq_moe_gemv(int fmt, const void* W_experts, const uint16_t* x, const int32_t* route_ids,
+                const float* route_w, float* y, int64_t N, int64_t K, int M, int top_k,
+                int n_experts, int x_per_slot, void* workspace, int64_t workspace_bytes,
+                void* stream) {
+  int st = check_moe_common(fmt, W_experts, N, K, M, top_k, n_experts);
+  if (st) return st;
+  if (x_per_slot != 0 && x_per_slot != 1) return fail(KQ_ERR_ARG, "x_per_slot must be 0 or 1");
+  if (M == 0 || N == 0) return ok();
+  if (!W_experts || !x || !route_ids || !y) return fail(KQ_ERR_ARG, "kq_moe_gemv: null pointer");
+  if (!aligned(x, 16)) return fail(KQ_ERR_ALIGN, "kq_moe_gemv: x must be 16-byte aligned");
+  if (!aligned(y, 4) || !aligned(route_ids, 4) || (route_w && !aligned(route_w, 4)))
+    return fail(KQ_ERR_ALIGN, "kq_moe_gemv: y, route_ids, route_w must be 4-byte aligned");
+  const int64_t need = kq_moe_gemv_workspace_bytes(N, M, top_k, route_w != nullptr);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need)
+      return fail(KQ_ERR_ARG, "kq_moe_gemv: workspace of %lld bytes needed", (long long)need);
+    if (!aligned(workspace, 16)) return fail(KQ_ERR_ALIGN, "kq_moe_gemv: workspace must be 16-byte aligned");
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* slots = route_w ? static_cast<float*>(workspace) : y;
+  kq::MoeArgs a{fmt, static_cast<const uint8_t*>(W_experts), x, route_ids, slots, N, K, M, top_k,
+                n_experts, x_per_slot, s};
+  int err = kq::launch_moe_gemv(a);
+  if (!err && route_w) err = kq::launch_weighted_slot_sum(slots, route_w, y, N, M, top_k, s);
+  return hip_status(err, "kq_moe_gemv");
+}
+
+int64_t kq_moe_ffn_workspace_bytes(int64_t hidden, int64_t inter, int M, int top_k) {
+  if (hidden < 0 || inter < 0 || M < 0 || top_k < 0) return fail(KQ_ERR_ARG, "negative size");
+  const int64_t h_bytes = ((int64_t)M * top_k * inter * 2 + 255) / 256 * 256;
+  return h_bytes + (int64_t)M * top_k * hidden * 4;
+}
+
+int kq_moe_ffn(int fmt, const void* W_gate, const void* W_up, const void* W_down, const uint16_t* x,
+               const int32_t* route_ids, const float* route_w, float* y, uint16_t* h_out,
+               int64_t hidden, int64_t inter, int M, int top_k, int n_experts, void* workspace,
+               int64_t workspace_bytes, void* stream) {
+  int st = check_moe_common(fmt, W_gate, inter, hidden, M, top_k, n_experts);
+  if (st) return st;
+  if ((st = check_moe_common(fmt, W_down, hidden, inter, M, top_k, n_experts))) return st;
+  if (!aligned(W_up, 4)) return fail(KQ_ERR_ALIGN, "W_up must be 4-byte aligned");
+  if (fmt != KQ_AFFINE4_G32 && hidden % 64 != 0)
+    return fail(KQ_ERR_SHAPE, "kq_moe_ffn: Q8_0/Q4_0 need hidden %% 64 == 0");
+  if (M == 0 || hidden == 0 || inter == 0) return ok();
+  if (!W_gate || !W_up || !W_down || !x || !route_ids || !route_w || !y)
+    return fail(KQ_ERR_ARG, "kq_moe_ffn: null pointer");
+  if (!aligned(x, 16)) return fail(KQ_ERR_ALIGN, "kq_moe_ffn: x must be 16-byte aligned");
+  if (!aligned(y, 4) || !aligned(route_ids, 4) || !aligned(route_w, 4))
+    return fail(KQ_ERR_ALIGN, "kq_moe_ffn: y, route_ids, route_w must be 4-byte aligned");
+  if (h_out && !aligned(h_out, 16)) return fail(KQ_ERR_ALIGN, "kq_moe_ffn: h_out must be 16-byte aligned");
+  const int64_t need = kq_moe_ffn_workspace_bytes(hidden, inter, M, top_k);
+  if (!workspace || workspace_bytes < need)
+    return fail(KQ_ERR_ARG, "kq_moe_ffn: workspace of %lld bytes needed", (long long)need);
+  if (!aligned(workspace, 16)) return fail(KQ_ERR_ALIGN, "kq_moe_ffn: workspace must be 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t h_bytes = ((int64_t)M * top_k * inter * 2 + 255) / 256 * 256;
+  uint16_t* h = h_out ? h_out : static_cast<uint16_t*>(workspace);
+  float* slots = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + h_bytes);
+  kq::MoeGateUpArgs g{fmt, static_cast<const uint8_t*>(W_gate), static_cast<const uint8_t*>(W_up),
+                      x, route_ids, h, inter, hidden, M, top_k, n_experts, s};
+  int err = kq::launch_moe_gate_up_swiglu(g);
+  if (!err) {
+    kq::MoeArgs d{fmt, static_cast<const uint8_t*>(W_down), h, route_ids, slots, hidden, inter, M,
+                  top_k, n_experts, 1, s};
+    err = kq::launch_moe_gemv(d);
+  }
+  if (!err) err = kq::launch_weighted_slot_sum(slots, route_w, y, hidden, M, top_k, s);
+  return hip_status(err, "kq_moe_ffn");
+}
+
+int64_t kq_argmax_workspace_bytes(int64_t N, int M) {
+  if (N < 0 || M < 0) return fail(KQ_ERR_ARG, "negative size");
+  return (int64_t)M * kq::argmax_partials(N) * 8;
+}
+
+int kq_argmax(const float* y, int64_t N, int M, int32_t* out, void* workspace,
+              int64_t workspace_bytes, void* stream) {
+  if (N < 1 || N > KQ_MAX_N) return fail(KQ_ERR_ARG, "kq_argmax: N=%lld out of range", (long long)N);
+  if (M < 0 || M > KQ_MAX_M) return fail(KQ_ERR_ARG, "kq_argmax: M=%d out of range", M);
+  if (M == 0) return ok();
+  if (!y || !out) return fail(KQ_ERR_ARG, "kq_argmax: null pointer");
+  if (!aligned(y, 4) || !aligned(out, 4)) return fail(KQ_ERR_ALIGN, "kq_argmax: y and out must be 4-byte aligned");
+  const int64_t need = kq_argmax_workspace_bytes(N, M);
+  if (!workspace || workspace_bytes < need)
+    return fail(KQ_ERR_ARG, "kq_argmax: workspace of %lld bytes needed", (long long)need);
+  if (!aligned(workspace, 8)) return fail(KQ_ERR_ALIGN, "kq_argmax: workspace must be 8-byte aligned");
+  return hip_status(kq::launch_argmax(y, N, M, out, workspace, static_cast<hipStream_t>(stream)),
+                    "kq_argmax");
+}
+
+}  // extern "C"

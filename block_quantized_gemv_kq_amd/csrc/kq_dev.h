@@ -1,0 +1,263 @@
+// kq_dev.h — device-side building blocks shared by the GEMV and expert kernels.
+//
+// Decode reads every weight once per token (Kinetic docs, "What makes it
+// fast"), so these kernels are a codec over a weight stream: load packed
+// blocks with wide loads, turn quants into fp16 in registers, and multiply
+// against fp16 activations with fp32 accumulation, applying each block's fp16
+// scale (and bias, affine4) once per 32 weights.
+//
+// Dequantization trick (exact): the fp16 bit pattern 0x6400 | u (u < 1024) is
+// the number 1024 + u. v_perm_b32 builds two such halves from two bytes in
+// one instruction, and v_dot2_f32_f16 multiplies a pair by two activations
+// and adds into fp32 in one more. The offset is removed per block with the
+// block's activation sum sx = sum_k x_k:
+//   Q8_0    (bytes q ^ 0x80 = q + 128):  sum (1152 + q) x = sum q x + 1152 sx
+//   Q4_0    (nibble q):                  sum (1024 + q) x = sum (q - 8) x + 1032 sx
+//   affine4 (nibble q):                  sum (1024 + q) x = sum q x + 1024 sx
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kqd {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+enum { F_Q8_0 = 0, F_Q4_0 = 1, F_AFFINE4 = 2 };
+
+// BB: bytes per block; UB: blocks per load unit (smallest dword-aligned group);
+// UDW: dwords per unit.
+template <int FMT> struct Fmt;
+template <> struct Fmt<F_AFFINE4> { static constexpr int BB = 20, UB = 1, UDW = 5; };
+template <> struct Fmt<F_Q4_0> { static constexpr int BB = 18, UB = 2, UDW = 9; };
+template <> struct Fmt<F_Q8_0> { static constexpr int BB = 34, UB = 2, UDW = 17; };
+
+constexpr uint32_t MAGIC = 0x64646464u;   // four 0x64 bytes: high byte of fp16 1024
+constexpr uint32_t SEL_LO = 0x04010400u;  // (u0, 64, u1, 64) -> fp16 pair (1024+u0, 1024+u1)
+constexpr uint32_t SEL_HI = 0x04030402u;  // (u2, 64, u3, 64)
+constexpr uint32_t ONES = 0x3C003C00u;    // fp16 pair (1, 1)
+constexpr int RSRC_FLAGS = 0x00020000;    // raw 32-bit buffer, range-checked
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c,
+                                false);
+}
+
+__device__ __forceinline__ float h2f(uint32_t bits16) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(bits16 & 0xffffu));
+}
+
+__device__ __forceinline__ uint32_t f2h_bits(float v) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v);
+}
+
+// Index of this wave in its workgroup, as a wave-uniform (scalar) value so
+// that addresses derived from it stay in SGPRs (buffer resources must).
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+}
+
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+__device__ __forceinline__ uint32_t alignbyte2(uint32_t hi, uint32_t lo) {
+  return __builtin_amdgcn_alignbyte(hi, lo, 2u);
+}
+
+// Buffer resource over [base, base + bytes): loads past the end return 0
+// instead of faulting.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           RSRC_FLAGS);
+}
+
+__device__ __forceinline__ u32x4 ld128(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t ld32(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+
+// Load one unit (UB blocks, UDW dwords) at byte offset `off` (4-aligned).
+template <int FMT>
+__device__ __forceinline__ void load_unit(rsrc_t r, uint32_t off, uint32_t (&D)[Fmt<FMT>::UDW]) {
+  constexpr int NV = Fmt<FMT>::UDW / 4;  // full 16-byte pieces
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const u32x4 t = ld128(r, off + 16u * v);
+    D[4 * v + 0] = t.x;
+    D[4 * v + 1] = t.y;
+    D[4 * v + 2] = t.z;
+    D[4 * v + 3] = t.w;
+  }
+  D[Fmt<FMT>::UDW - 1] = ld32(r, off + 16u * NV);
+}
+
+// Four nibble dwords of one 4-bit block -> 16 fp16 pairs (1024 + q), ordered
+// to pair with activation dwords 0..15 of the block (dword i = x[2i], x[2i+1]).
+// Byte t of the nibble area holds element t (low nibble) and t+16 (high).
+__device__ __forceinline__ void unpack_nibbles(const uint32_t (&n)[4], uint32_t* A) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const uint32_t lo = n[t] & 0x0F0F0F0Fu;          // elements 4t..4t+3
+    const uint32_t hi = (n[t] >> 4) & 0x0F0F0F0Fu;   // elements 16+4t..19+4t
+    A[2 * t] = perm(MAGIC, lo, SEL_LO);
+    A[2 * t + 1] = perm(MAGIC, lo, SEL_HI);
+    A[8 + 2 * t] = perm(MAGIC, hi, SEL_LO);
+    A[9 + 2 * t] = perm(MAGIC, hi, SEL_HI);
+  }
+}
+
+// Eight int8 dwords of one Q8_0 block -> 16 fp16 pairs (1152 + q).
+__device__ __forceinline__ void unpack_int8(const uint32_t (&q)[8], uint32_t* A) {
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const uint32_t u = q[t] ^ 0x80808080u;
+    A[2 * t] = perm(MAGIC, u, SEL_LO);
+    A[2 * t + 1] = perm(MAGIC, u, SEL_HI);
+  }
+}
+
+// A unit unpacked: 16 * UB fp16 pairs, and per block the fp32 factors of the
+// fix-up y += c1 * (acc + c0 * sx) + c2 * sx.
+template <int FMT>
+struct Unpacked {
+  uint32_t A[16 * Fmt<FMT>::UB];
+  float scale[Fmt<FMT>::UB];
+  float bias[Fmt<FMT>::UB];  // affine4 only
+};
+
+template <int FMT>
+__device__ __forceinline__ void unpack_unit(const uint32_t (&D)[Fmt<FMT>::UDW], Unpacked<FMT>& u) {
+  if constexpr (FMT == F_AFFINE4) {
+    const uint32_t n[4] = {D[1], D[2], D[3], D[4]};
+    unpack_nibbles(n, u.A);
+    u.scale[0] = h2f(D[0]);
+    u.bias[0] = h2f(D[0] >> 16);
+  } else if constexpr (FMT == F_Q4_0) {
+    // block a: d at bytes 0-1, nibbles at bytes 2-17; block b: d at 18-19, nibbles 20-35
+    const uint32_t na[4] = {alignbyte2(D[1], D[0]), alignbyte2(D[2], D[1]), alignbyte2(D[3], D[2]),
+                            alignbyte2(D[4], D[3])};
+    const uint32_t nb[4] = {D[5], D[6], D[7], D[8]};
+    unpack_nibbles(na, u.A);
+    unpack_nibbles(nb, u.A + 16);
+    u.scale[0] = h2f(D[0]);
+    u.scale[1] = h2f(D[4] >> 16);
+    u.bias[0] = u.bias[1] = 0.0f;
+  } else {
+    // block a: d at bytes 0-1, quants 2-33; block b: d at 34-35, quants 36-67
+    uint32_t qa[8], qb[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      qa[t] = alignbyte2(D[t + 1], D[t]);
+      qb[t] = D[9 + t];
+    }
+    unpack_int8(qa, u.A);
+    unpack_int8(qb, u.A + 16);
+    u.scale[0] = h2f(D[0]);
+    u.scale[1] = h2f(D[8] >> 16);
+    u.bias[0] = u.bias[1] = 0.0f;
+  }
+}
+
+template <int FMT> struct Offset;
+template <> struct Offset<F_AFFINE4> { static constexpr float v = -1024.0f; };
+template <> struct Offset<F_Q4_0> { static constexpr float v = -1032.0f; };
+template <> struct Offset<F_Q8_0> { static constexpr float v = -1152.0f; };
+
+// Dot of one block (16 pairs) with 16 activation dwords; add its
+// dequantized contribution to y.
+template <int FMT>
+__device__ __forceinline__ float block_dot(const uint32_t* A, const uint32_t* X, float sx,
+                                           float scale, float bias, float y) {
+  float acc = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc = dot2(A[i], X[i], acc);
+  const float t = __builtin_fmaf(Offset<FMT>::v, sx, acc);   // sum of (q or q-8) * x
+  y = __builtin_fmaf(scale, t, y);
+  if constexpr (FMT == F_AFFINE4) y = __builtin_fmaf(bias, sx, y);
+  return y;
+}
+
+// Activation sum of one block (16 dwords = 32 fp16).
+__device__ __forceinline__ float block_xsum(const uint32_t* X) {
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) s = dot2(X[i], ONES, s);
+  return s;
+}
+
+// Load the activations of one unit for one column: 16 * UB dwords.
+template <int FMT>
+__device__ __forceinline__ void load_x_unit(const uint16_t* xcol, int unit, uint32_t* X) {
+  constexpr int UK = 32 * Fmt<FMT>::UB;
+  const u32x4* p = reinterpret_cast<const u32x4*>(xcol + (int64_t)unit * UK);
+#pragma unroll
+  for (int v = 0; v < UK / 8; ++v) {
+    const u32x4 t = p[v];
+    X[4 * v + 0] = t.x;
+    X[4 * v + 1] = t.y;
+    X[4 * v + 2] = t.z;
+    X[4 * v + 3] = t.w;
+  }
+}
+
+// One wave's share of a GEMV: R rows per lane, MT columns, lanes in groups of
+// G = 2^log2g along K. Lane (rho = lane >> log2g, g = lane & (G-1)) handles
+// tile rows rho + rpw*r (r < R, rpw = 64/G) and units g, g+G, g+2G, ...
+// `rs` covers the tile's rows (rows past the matrix end read as zero).
+// On return every lane of a group holds the group's full sums (butterfly
+// reduction in a fixed order, so results are deterministic).
+template <int FMT, int MT, int R>
+__device__ __forceinline__ void valu_tile(rsrc_t rs, uint32_t row_bytes, int units, int log2g,
+                                          const uint16_t* const (&xc)[MT], float (&acc)[R][MT]) {
+  constexpr int UB = Fmt<FMT>::UB;
+  constexpr int UBYTES = Fmt<FMT>::BB * UB;
+  const int lane = threadIdx.x & 63;
+  const int G = 1 << log2g;
+  const int rpw = 64 >> log2g;
+  const int rho = lane >> log2g;
+  const int g = lane & (G - 1);
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[r][m] = 0.0f;
+
+  uint32_t roff[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) roff[r] = (uint32_t)(rho + rpw * r) * row_bytes;
+
+  for (int u = g; u < units; u += G) {
+    uint32_t D[R][Fmt<FMT>::UDW];
+#pragma unroll
+    for (int r = 0; r < R; ++r) load_unit<FMT>(rs, roff[r] + (uint32_t)u * UBYTES, D[r]);
+    Unpacked<FMT> up[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) unpack_unit<FMT>(D[r], up[r]);
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      uint32_t X[16 * UB];
+      load_x_unit<FMT>(xc[m], u, X);
+#pragma unroll
+      for (int b = 0; b < UB; ++b) {
+        const float sx = block_xsum(X + 16 * b);
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+          acc[r][m] = block_dot<FMT>(up[r].A + 16 * b, X + 16 * b, sx, up[r].scale[b],
+                                     up[r].bias[b], acc[r][m]);
+      }
+    }
+  }
+  for (int off = 1; off < G; off <<= 1) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int m = 0; m < MT; ++m) acc[r][m] += __shfl_xor(acc[r][m], off, 64);
+  }
+}
+
+}  // namespace kqd

@@ -1,0 +1,219 @@
+// kq_gemv.hip — dense block-quantized GEMV for gfx950: y[M][N] = W'[N][K] x[M][K]^T.
+//
+// The decode step reads all of a dense model's weights once per token, and a
+// speculative verify pass checks several guessed tokens "in one pass over the
+// weights" (Kinetic docs, "What makes it fast"), so every kernel here streams
+// each weight byte exactly once per call whatever M is.
+//
+// Paths:
+//  * VALU path (kq_dev.h valu_tile): fp16 magic-number dequant + v_dot2_f32_f16,
+//    used for small M (a few activation columns).
+//  * MFMA path (kq_mfma.hip): v_mfma_f32_16x16x32_f16 for larger M.
+//  * Generic path: Q4_0/Q8_0 rows whose length is an odd number of blocks are
+//    only 2-byte aligned; a simple per-block kernel handles them.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#include "kq_dev.h"
+#include "kq_internal.h"
+
+namespace kqd {
+
+// ----------------------------------------------------------------- VALU path
+
+template <int FMT, int MT, int R>
+__global__ __launch_bounds__(256) void k_gemv_valu(const uint8_t* __restrict__ W,
+                                                   const uint16_t* __restrict__ x,
+                                                   float* __restrict__ y, int N, int K, int log2g,
+                                                   int m0) {
+  const int lane = threadIdx.x & 63;
+  const int wave = blockIdx.x * 4 + wave_id();
+  const int rpw = 64 >> log2g;
+  const int tile_rows = rpw * R;
+  const int64_t row_base = (int64_t)wave * tile_rows;
+  if (row_base >= N) return;
+  const uint32_t row_bytes = (uint32_t)(K / 32) * Fmt<FMT>::BB;
+  const int valid = (int)min<int64_t>(tile_rows, N - row_base);
+  const rsrc_t rs = make_rsrc(W + row_base * row_bytes, (uint32_t)valid * row_bytes);
+  const uint16_t* xc[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) xc[m] = x + (int64_t)(m0 + m) * K;
+  float acc[R][MT];
+  valu_tile<FMT, MT, R>(rs, row_bytes, K / (32 * Fmt<FMT>::UB), log2g, xc, acc);
+  const int G = 1 << log2g;
+  if ((lane & (G - 1)) == 0) {
+    const int rho = lane >> log2g;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int64_t row = row_base + rho + rpw * r;
+      if (row < N) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) y[(int64_t)(m0 + m) * N + row] = acc[r][m];
+      }
+    }
+  }
+}
+
+// -------------------------------------------------------------- generic path
+// One wave per row, one lane per block, 16-bit loads (blocks may be only
+// 2-byte aligned), plain fp32 dequantization. Loops over all M columns.
+template <int FMT>
+__global__ __launch_bounds__(256) void k_gemv_generic(const uint8_t* __restrict__ W,
+                                                      const uint16_t* __restrict__ x,
+                                                      float* __restrict__ y, int N, int K, int M) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + wave_id();
+  if (row >= N) return;
+  const int nb = K / 32;
+  const int64_t row_bytes = (int64_t)nb * Fmt<FMT>::BB;
+  for (int m = 0; m < M; ++m) {
+    float acc = 0.0f;
+    for (int b = lane; b < nb; b += 64) {
+      const uint16_t* blk = reinterpret_cast<const uint16_t*>(W + row * row_bytes + (int64_t)b * Fmt<FMT>::BB);
+      const uint16_t* xb = x + (int64_t)m * K + b * 32;
+      const float s = h2f(blk[0]);
+      if constexpr (FMT == F_Q8_0) {
+        for (int j = 0; j < 16; ++j) {
+          const uint32_t two = blk[1 + j];
+          acc = __builtin_fmaf(s * (float)(int8_t)(two & 0xff), h2f(xb[2 * j]), acc);
+          acc = __builtin_fmaf(s * (float)(int8_t)(two >> 8), h2f(xb[2 * j + 1]), acc);
+        }
+      } else {
+        const float bias = FMT == F_AFFINE4 ? h2f(blk[1]) : 0.0f;
+        const uint16_t* nib = blk + (FMT == F_AFFINE4 ? 2 : 1);
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t two = nib[j];
+          const int q0 = two & 15, q1 = (two >> 4) & 15, q2 = (two >> 8) & 15, q3 = (two >> 12) & 15;
+          const int e = 2 * j;  // bytes 2j, 2j+1 hold elements 2j, 2j+16, 2j+1, 2j+17
+          float w0, w1, w2, w3;
+          if constexpr (FMT == F_AFFINE4) {
+            w0 = __builtin_fmaf(s, (float)q0, bias);
+            w1 = __builtin_fmaf(s, (float)q1, bias);
+            w2 = __builtin_fmaf(s, (float)q2, bias);
+            w3 = __builtin_fmaf(s, (float)q3, bias);
+          } else {
+            w0 = s * (float)(q0 - 8);
+            w1 = s * (float)(q1 - 8);
+            w2 = s * (float)(q2 - 8);
+            w3 = s * (float)(q3 - 8);
+          }
+          acc = __builtin_fmaf(w0, h2f(xb[e]), acc);
+          acc = __builtin_fmaf(w1, h2f(xb[e + 16]), acc);
+          acc = __builtin_fmaf(w2, h2f(xb[e + 1]), acc);
+          acc = __builtin_fmaf(w3, h2f(xb[e + 17]), acc);
+        }
+      }
+    }
+    for (int off = 1; off < 64; off <<= 1) acc += __shfl_xor(acc, off, 64);
+    if (lane == 0) y[(int64_t)m * N + row] = acc;
+  }
+}
+
+}  // namespace kqd
+
+namespace kq {
+
+using namespace kqd;
+
+const char* hip_error_string(int err) { return hipGetErrorString(static_cast<hipError_t>(err)); }
+
+namespace {
+
+int ilog2(int v) {
+  int l = 0;
+  while ((1 << (l + 1)) <= v) ++l;
+  return l;
+}
+
+struct ValuCfg {
+  int log2g;
+  int R;
+};
+
+// Lanes per row (G) and rows per lane (R) for the VALU path. G is a power of
+// two near units/4, so each lane walks a few units of a row; R grows while
+// the grid still holds >= 2048 waves (8 per CU) to keep loads in flight.
+// KQ_VALU_G / KQ_VALU_R override the choice (tuning sweeps and tests).
+int env_int(const char* name) {
+  const char* v = getenv(name);
+  return v ? atoi(v) : 0;
+}
+
+ValuCfg valu_cfg(int64_t N, int units) {
+  const int env_g = env_int("KQ_VALU_G");
+  const int env_r = env_int("KQ_VALU_R");
+  int G = 1 << ilog2(units / 4 > 0 ? units / 4 : 1);
+  G = G < 4 ? 4 : (G > 64 ? 64 : G);
+  if (env_g == 1 || env_g == 2 || env_g == 4 || env_g == 8 || env_g == 16 || env_g == 32 || env_g == 64) G = env_g;
+  int R = 1;
+  const int64_t rpw = 64 / G;
+  for (int cand : {4, 2}) {
+    if ((N + rpw * cand - 1) / (rpw * cand) >= 2048) { R = cand; break; }
+  }
+  if (env_r == 1 || env_r == 2 || env_r == 4) R = env_r;
+  return {ilog2(G), R};
+}
+
+template <int FMT, int MT>
+int launch_valu_mt(const GemvArgs& a, int m0, ValuCfg c) {
+  const int64_t tile = (int64_t)(64 >> c.log2g) * c.R;
+  const int64_t waves = (a.N + tile - 1) / tile;
+  const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
+  if (c.R == 4)
+    hipLaunchKernelGGL((k_gemv_valu<FMT, MT, 4>), grid, block, 0, a.stream, a.W, a.x, a.y, (int)a.N, (int)a.K, c.log2g, m0);
+  else if (c.R == 2)
+    hipLaunchKernelGGL((k_gemv_valu<FMT, MT, 2>), grid, block, 0, a.stream, a.W, a.x, a.y, (int)a.N, (int)a.K, c.log2g, m0);
+  else
+    hipLaunchKernelGGL((k_gemv_valu<FMT, MT, 1>), grid, block, 0, a.stream, a.W, a.x, a.y, (int)a.N, (int)a.K, c.log2g, m0);
+  return (int)hipGetLastError();
+}
+
+template <int FMT>
+int launch_valu(const GemvArgs& a) {
+  const int units = (int)(a.K / (32 * Fmt<FMT>::UB));
+  const ValuCfg c = valu_cfg(a.N, units);
+  for (int m0 = 0; m0 < a.M; m0 += 8) {
+    const int mt = a.M - m0 < 8 ? a.M - m0 : 8;
+    int err = 0;
+    switch (mt) {
+      case 1: err = launch_valu_mt<FMT, 1>(a, m0, c); break;
+      case 2: err = launch_valu_mt<FMT, 2>(a, m0, c); break;
+      case 3: err = launch_valu_mt<FMT, 3>(a, m0, c); break;
+      case 4: err = launch_valu_mt<FMT, 4>(a, m0, c); break;
+      case 5: err = launch_valu_mt<FMT, 5>(a, m0, c); break;
+      case 6: err = launch_valu_mt<FMT, 6>(a, m0, c); break;
+      case 7: err = launch_valu_mt<FMT, 7>(a, m0, c); break;
+      default: err = launch_valu_mt<FMT, 8>(a, m0, c); break;
+    }
+    if (err) return err;
+  }
+  return 0;
+}
+
+template <int FMT>
+int launch_generic(const GemvArgs& a) {
+  const dim3 grid((unsigned)((a.N + 3) / 4)), block(256);
+  hipLaunchKernelGGL((k_gemv_generic<FMT>), grid, block, 0, a.stream, a.W, a.x, a.y, (int)a.N, (int)a.K, a.M);
+  return (int)hipGetLastError();
+}
+
+template <int FMT>
+int dispatch(const GemvArgs& a) {
+  if (a.K % (32 * Fmt<FMT>::UB) != 0) return launch_generic<FMT>(a);
+  const char* force = getenv("KQ_FORCE_PATH");  // tests: run a given path at any shape
+  if (force && force[0] == 'g') return launch_generic<FMT>(a);
+  return launch_valu<FMT>(a);
+}
+
+}  // namespace
+
+int launch_gemv(const GemvArgs& a) {
+  switch (a.fmt) {
+    case KQ_Q8_0: return dispatch<F_Q8_0>(a);
+    case KQ_Q4_0: return dispatch<F_Q4_0>(a);
+    default: return dispatch<F_AFFINE4>(a);
+  }
+}
+
+}  // namespace kq

@@ -1,0 +1,107 @@
+// kq_misc.hip — small kernels around the GEMVs: the fixed-order weighted sum
+// of routed-expert outputs, and the greedy argmax over a vocabulary-sized
+// output layer (Kinetic docs, "What makes it fast": choosing the next token
+// reads an output layer of up to a quarter of a million rows).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kq_dev.h"
+#include "kq_internal.h"
+
+namespace kqd {
+
+// y[m][n] = sum_j w[m][j] * ys[m][j][n], accumulated in slot order j = 0..top_k-1.
+__global__ __launch_bounds__(256) void k_weighted_slot_sum(const float* __restrict__ ys,
+                                                           const float* __restrict__ w,
+                                                           float* __restrict__ y, int64_t N,
+                                                           int top_k) {
+  const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int m = blockIdx.y;
+  if (n >= N) return;
+  const float* base = ys + (int64_t)m * top_k * N + n;
+  float acc = 0.0f;
+  for (int j = 0; j < top_k; ++j) acc = __builtin_fmaf(w[(int64_t)m * top_k + j], base[(int64_t)j * N], acc);
+  y[(int64_t)m * N + n] = acc;
+}
+
+// (value, index) pairs: the larger value wins; on equal values the lower
+// index; NaN never wins. Index INT32_MAX marks "nothing yet".
+struct Best {
+  float v;
+  int32_t i;
+};
+
+__device__ __forceinline__ Best better(Best a, Best b) {
+  if (b.v > a.v || (b.v == a.v && b.i < a.i)) return b;
+  return a;
+}
+
+__device__ __forceinline__ Best block_best(Best b, Best* s_red) {
+  for (int off = 32; off > 0; off >>= 1) {
+    Best o{__shfl_xor(b.v, off, 64), __shfl_xor(b.i, off, 64)};
+    b = better(b, o);
+  }
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (lane == 0) s_red[wave] = b;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    Best r = s_red[0];
+    for (int w = 1; w < (int)(blockDim.x >> 6); ++w) r = better(r, s_red[w]);
+    s_red[0] = r;
+  }
+  __syncthreads();
+  return s_red[0];
+}
+
+constexpr int ARGMAX_CHUNK = 16384;
+
+__global__ __launch_bounds__(256) void k_argmax_partial(const float* __restrict__ y, int64_t N,
+                                                        Best* __restrict__ part, int nparts) {
+  __shared__ Best s_red[4];
+  const int m = blockIdx.y;
+  const int64_t c0 = (int64_t)blockIdx.x * ARGMAX_CHUNK;
+  const int64_t c1 = c0 + ARGMAX_CHUNK < N ? c0 + ARGMAX_CHUNK : N;
+  const float* row = y + (int64_t)m * N;
+  Best b{-__builtin_inff(), INT32_MAX};
+  for (int64_t i = c0 + threadIdx.x; i < c1; i += 256) b = better(b, Best{row[i], (int32_t)i});
+  b = block_best(b, s_red);
+  if (threadIdx.x == 0) part[(int64_t)m * nparts + blockIdx.x] = b;
+}
+
+__global__ __launch_bounds__(256) void k_argmax_final(const Best* __restrict__ part, int nparts,
+                                                      int32_t* __restrict__ out) {
+  __shared__ Best s_red[4];
+  const int m = blockIdx.x;
+  Best b{-__builtin_inff(), INT32_MAX};
+  for (int i = threadIdx.x; i < nparts; i += 256) b = better(b, part[(int64_t)m * nparts + i]);
+  b = block_best(b, s_red);
+  if (threadIdx.x == 0) out[m] = b.i == INT32_MAX ? 0 : b.i;
+}
+
+}  // namespace kqd
+
+namespace kq {
+
+using namespace kqd;
+
+int launch_weighted_slot_sum(const float* ys, const float* w, float* y, int64_t N, int M, int top_k,
+                             hipStream_t stream) {
+  const dim3 grid((unsigned)((N + 255) / 256), (unsigned)M), block(256);
+  hipLaunchKernelGGL(k_weighted_slot_sum, grid, block, 0, stream, ys, w, y, N, top_k);
+  return (int)hipGetLastError();
+}
+
+int64_t argmax_partials(int64_t N) { return (N + ARGMAX_CHUNK - 1) / ARGMAX_CHUNK; }
+
+int launch_argmax(const float* y, int64_t N, int M, int32_t* out, void* ws, hipStream_t stream) {
+  const int nparts = (int)argmax_partials(N);
+  Best* part = static_cast<Best*>(ws);
+  hipLaunchKernelGGL(k_argmax_partial, dim3((unsigned)nparts, (unsigned)M), dim3(256), 0, stream, y, N,
+                     part, nparts);
+  int err = (int)hipGetLastError();
+  if (err) return err;
+  hipLaunchKernelGGL(k_argmax_final, dim3((unsigned)M), dim3(256), 0, stream, part, nparts, out);
+  return (int)hipGetLastError();
+}
+
+}  // namespace kq

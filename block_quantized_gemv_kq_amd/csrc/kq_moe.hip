@@ -1,0 +1,323 @@
+// kq_moe.hip — routed-expert (mixture-of-experts) decode GEMVs for gfx950.
+//
+// A mixture of experts uses only a few experts per token (kinfer page,
+// "Models bigger than the machine": 10 of 512; Kinetic docs, "What makes it
+// fast": experts in use stay on the GPU), so only the routed experts' weights
+// are read, and each distinct expert is read once per call for all of the
+// tokens routed to it.
+//
+// Grid: (row tiles, M * top_k route slots). The workgroup of slot p handles
+// expert e = ids[p] only if no earlier slot names e; it then gathers every
+// slot routed to e (on the device, no host synchronisation) and runs the
+// VALU tile over them as the activation columns, so e's rows stream once.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kq_dev.h"
+#include "kq_internal.h"
+
+namespace kqd {
+
+constexpr int MOE_MAX_SLOTS = 64 * 64;  // M * top_k upper bound
+constexpr int MOE_COLS = 4;             // activation columns per VALU pass
+
+// Returns the number of slots routed to ids[p] (0 if an earlier slot owns the
+// expert). Slot indices are written to s_list in increasing order.
+__device__ int gather_expert_slots(const int32_t* __restrict__ ids, int p, int P, int* s_list,
+                                   int* s_cnt) {
+  const int e = ids[p];
+  int dup = 0;
+  for (int q = threadIdx.x; q < p; q += blockDim.x) dup |= (ids[q] == e);
+  dup = __syncthreads_or(dup);
+  if (dup) return 0;
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    int cnt = 0;
+    for (int base = p; base < P; base += 64) {
+      const int q = base + lane;
+      const bool hit = q < P && ids[q] == e;
+      const uint64_t mask = __ballot(hit);
+      if (hit) s_list[cnt + __popcll(mask & ((1ull << lane) - 1ull))] = q;
+      cnt += __popcll(mask);
+    }
+    if (lane == 0) *s_cnt = cnt;
+  }
+  __syncthreads();
+  return *s_cnt;
+}
+
+// Per-slot GEMV outputs y_slot[p][n] for the rows of this wave's tile.
+template <int FMT, int MT, int R>
+__device__ __forceinline__ void moe_cols(rsrc_t rs, uint32_t row_bytes, int units, int log2g,
+                                         const uint16_t* __restrict__ x, const int* list, int c0,
+                                         int K, int top_k, int x_per_slot, float* __restrict__ y_slot,
+                                         int64_t N, int64_t row_base) {
+  const uint16_t* xc[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const int p = list[c0 + m];
+    const int64_t xrow = x_per_slot ? p : p / top_k;
+    xc[m] = x + xrow * K;
+  }
+  float acc[R][MT];
+  valu_tile<FMT, MT, R>(rs, row_bytes, units, log2g, xc, acc);
+  const int lane = threadIdx.x & 63;
+  const int G = 1 << log2g, rpw = 64 >> log2g;
+  if ((lane & (G - 1)) == 0) {
+    const int rho = lane >> log2g;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int64_t row = row_base + rho + rpw * r;
+      if (row < N) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) y_slot[(int64_t)list[c0 + m] * N + row] = acc[r][m];
+      }
+    }
+  }
+}
+
+template <int FMT, int R>
+__global__ __launch_bounds__(256) void k_moe_valu(const uint8_t* __restrict__ W,
+                                                  const uint16_t* __restrict__ x,
+                                                  const int32_t* __restrict__ ids,
+                                                  float* __restrict__ y_slot, int N, int K, int M,
+                                                  int top_k, int n_experts, int x_per_slot,
+                                                  int log2g, int64_t expert_bytes) {
+  __shared__ int s_list[MOE_MAX_SLOTS];
+  __shared__ int s_cnt;
+  const int P = M * top_k;
+  const int p = blockIdx.y;
+  const int cnt = gather_expert_slots(ids, p, P, s_list, &s_cnt);
+  if (cnt == 0) return;
+  const int e = ids[p];
+  const int rpw = 64 >> log2g;
+  const int tile_rows = rpw * R;
+  const int wave = blockIdx.x * 4 + wave_id();
+  const int64_t row_base = (int64_t)wave * tile_rows;
+  if (row_base >= N) return;
+  if (e < 0 || e >= n_experts) {  // precondition violated: read nothing, flag with NaN
+    const int lane = threadIdx.x & 63;
+    for (int c = 0; c < cnt; ++c)
+      for (int r = lane; r < tile_rows; r += 64)
+        if (row_base + r < N) y_slot[(int64_t)s_list[c] * N + row_base + r] = __builtin_nanf("");
+    return;
+  }
+  const uint32_t row_bytes = (uint32_t)(K / 32) * Fmt<FMT>::BB;
+  const int valid = (int)min<int64_t>(tile_rows, N - row_base);
+  const uint8_t* We = W + (int64_t)e * expert_bytes;
+  const rsrc_t rs = make_rsrc(We + row_base * row_bytes, (uint32_t)valid * row_bytes);
+  const int units = K / (32 * Fmt<FMT>::UB);
+  for (int c0 = 0; c0 < cnt; c0 += MOE_COLS) {
+    const int mt = cnt - c0 < MOE_COLS ? cnt - c0 : MOE_COLS;
+    switch (mt) {
+      case 1: moe_cols<FMT, 1, R>(rs, row_bytes, units, log2g, x, s_list, c0, K, top_k, x_per_slot, y_slot, N, row_base); break;
+      case 2: moe_cols<FMT, 2, R>(rs, row_bytes, units, log2g, x, s_list, c0, K, top_k, x_per_slot, y_slot, N, row_base); break;
+      case 3: moe_cols<FMT, 3, R>(rs, row_bytes, units, log2g, x, s_list, c0, K, top_k, x_per_slot, y_slot, N, row_base); break;
+      default: moe_cols<FMT, 4, R>(rs, row_bytes, units, log2g, x, s_list, c0, K, top_k, x_per_slot, y_slot, N, row_base); break;
+    }
+  }
+}
+
+// Gate and up rows of one expert in the same pass, SwiGLU in registers:
+// h[p][n] = fp16(silu(gate_n . x) * (up_n . x)), silu(z) = z / (1 + e^-z).
+template <int FMT, int MT, int R>
+__device__ __forceinline__ void gate_up_cols(rsrc_t rg, rsrc_t ru, uint32_t row_bytes, int units,
+                                             int log2g, const uint16_t* __restrict__ x,
+                                             const int* list, int c0, int K, int top_k,
+                                             uint16_t* __restrict__ h, int64_t N, int64_t row_base) {
+  const uint16_t* xc[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) xc[m] = x + (int64_t)(list[c0 + m] / top_k) * K;
+  float g[R][MT], u[R][MT];
+  valu_tile<FMT, MT, R>(rg, row_bytes, units, log2g, xc, g);
+  valu_tile<FMT, MT, R>(ru, row_bytes, units, log2g, xc, u);
+  const int lane = threadIdx.x & 63;
+  const int G = 1 << log2g, rpw = 64 >> log2g;
+  if ((lane & (G - 1)) == 0) {
+    const int rho = lane >> log2g;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int64_t row = row_base + rho + rpw * r;
+      if (row < N) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          const float z = g[r][m];
+          const float hv = z / (1.0f + __expf(-z)) * u[r][m];
+          h[(int64_t)list[c0 + m] * N + row] = (uint16_t)f2h_bits(hv);
+        }
+      }
+    }
+  }
+}
+
+template <int FMT, int R>
+__global__ __launch_bounds__(256) void k_moe_gate_up(const uint8_t* __restrict__ Wg,
+                                                     const uint8_t* __restrict__ Wu,
+                                                     const uint16_t* __restrict__ x,
+                                                     const int32_t* __restrict__ ids,
+                                                     uint16_t* __restrict__ h, int N, int K, int M,
+                                                     int top_k, int n_experts, int log2g,
+                                                     int64_t expert_bytes) {
+  __shared__ int s_list[MOE_MAX_SLOTS];
+  __shared__ int s_cnt;
+  const int P = M * top_k;
+  const int p = blockIdx.y;
+  const int cnt = gather_expert_slots(ids, p, P, s_list, &s_cnt);
+  if (cnt == 0) return;
+  const int e = ids[p];
+  const int rpw = 64 >> log2g;
+  const int tile_rows = rpw * R;
+  const int wave = blockIdx.x * 4 + wave_id();
+  const int64_t row_base = (int64_t)wave * tile_rows;
+  if (row_base >= N) return;
+  if (e < 0 || e >= n_experts) {
+    const int lane = threadIdx.x & 63;
+    const uint16_t nan16 = 0x7e00;
+    for (int c = 0; c < cnt; ++c)
+      for (int r = lane; r < tile_rows; r += 64)
+        if (row_base + r < N) h[(int64_t)s_list[c] * N + row_base + r] = nan16;
+    return;
+  }
+  const uint32_t row_bytes = (uint32_t)(K / 32) * Fmt<FMT>::BB;
+  const int valid = (int)min<int64_t>(tile_rows, N - row_base);
+  const int64_t off = (int64_t)e * expert_bytes + row_base * row_bytes;
+  const rsrc_t rg = make_rsrc(Wg + off, (uint32_t)valid * row_bytes);
+  const rsrc_t ru = make_rsrc(Wu + off, (uint32_t)valid * row_bytes);
+  const int units = K / (32 * Fmt<FMT>::UB);
+  for (int c0 = 0; c0 < cnt; c0 += MOE_COLS) {
+    const int mt = cnt - c0 < MOE_COLS ? cnt - c0 : MOE_COLS;
+    switch (mt) {
+      case 1: gate_up_cols<FMT, 1, R>(rg, ru, row_bytes, units, log2g, x, s_list, c0, K, top_k, h, N, row_base); break;
+      case 2: gate_up_cols<FMT, 2, R>(rg, ru, row_bytes, units, log2g, x, s_list, c0, K, top_k, h, N, row_base); break;
+      case 3: gate_up_cols<FMT, 3, R>(rg, ru, row_bytes, units, log2g, x, s_list, c0, K, top_k, h, N, row_base); break;
+      default: gate_up_cols<FMT, 4, R>(rg, ru, row_bytes, units, log2g, x, s_list, c0, K, top_k, h, N, row_base); break;
+    }
+  }
+}
+
+// Generic routed kernel for rows that are only 2-byte aligned (Q4_0/Q8_0 with
+// an odd number of blocks per row): one wave per (row, slot), per-block loads.
+template <int FMT>
+__global__ __launch_bounds__(256) void k_moe_generic(const uint8_t* __restrict__ W,
+                                                     const uint16_t* __restrict__ x,
+                                                     const int32_t* __restrict__ ids,
+                                                     float* __restrict__ y_slot, int N, int K,
+                                                     int top_k, int n_experts, int x_per_slot,
+                                                     int64_t expert_bytes) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + wave_id();
+  const int p = blockIdx.y;
+  if (row >= N) return;
+  const int e = ids[p];
+  if (e < 0 || e >= n_experts) {
+    if (lane == 0) y_slot[(int64_t)p * N + row] = __builtin_nanf("");
+    return;
+  }
+  const int nb = K / 32;
+  const int64_t row_bytes = (int64_t)nb * Fmt<FMT>::BB;
+  const uint8_t* Wr = W + (int64_t)e * expert_bytes + row * row_bytes;
+  const uint16_t* xr = x + (int64_t)(x_per_slot ? p : p / top_k) * K;
+  float acc = 0.0f;
+  for (int b = lane; b < nb; b += 64) {
+    const uint16_t* blk = reinterpret_cast<const uint16_t*>(Wr + (int64_t)b * Fmt<FMT>::BB);
+    const uint16_t* xb = xr + b * 32;
+    const float s = h2f(blk[0]);
+    if constexpr (FMT == F_Q8_0) {
+      for (int j = 0; j < 16; ++j) {
+        const uint32_t two = blk[1 + j];
+        acc = __builtin_fmaf(s * (float)(int8_t)(two & 0xff), h2f(xb[2 * j]), acc);
+        acc = __builtin_fmaf(s * (float)(int8_t)(two >> 8), h2f(xb[2 * j + 1]), acc);
+      }
+    } else {
+      const float bias = FMT == F_AFFINE4 ? h2f(blk[1]) : 0.0f;
+      const uint16_t* nib = blk + (FMT == F_AFFINE4 ? 2 : 1);
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t two = nib[j];
+        const int q[4] = {(int)(two & 15), (int)((two >> 4) & 15), (int)((two >> 8) & 15), (int)((two >> 12) & 15)};
+        const int el[4] = {2 * j, 2 * j + 16, 2 * j + 1, 2 * j + 17};
+        for (int i = 0; i < 4; ++i) {
+          const float w = FMT == F_AFFINE4 ? __builtin_fmaf(s, (float)q[i], bias) : s * (float)(q[i] - 8);
+          acc = __builtin_fmaf(w, h2f(xb[el[i]]), acc);
+        }
+      }
+    }
+  }
+  for (int off = 1; off < 64; off <<= 1) acc += __shfl_xor(acc, off, 64);
+  if (lane == 0) y_slot[(int64_t)p * N + row] = acc;
+}
+
+}  // namespace kqd
+
+namespace kq {
+
+using namespace kqd;
+
+namespace {
+
+int ilog2(int v) {
+  int l = 0;
+  while ((1 << (l + 1)) <= v) ++l;
+  return l;
+}
+
+// Expert matrices are small (a few MB), so prefer many waves: G near units/4,
+// one row per lane.
+int moe_log2g(int units) {
+  int G = 1 << ilog2(units / 4 > 0 ? units / 4 : 1);
+  G = G < 4 ? 4 : (G > 64 ? 64 : G);
+  return ilog2(G);
+}
+
+template <int FMT>
+int moe_dispatch(const MoeArgs& a) {
+  const int64_t eb = a.N * (a.K / 32) * Fmt<FMT>::BB;
+  const int P = a.M * a.top_k;
+  if (a.K % (32 * Fmt<FMT>::UB) != 0) {
+    const dim3 grid((unsigned)((a.N + 3) / 4), (unsigned)P), block(256);
+    hipLaunchKernelGGL((k_moe_generic<FMT>), grid, block, 0, a.stream, a.W, a.x, a.ids, a.y_slot,
+                       (int)a.N, (int)a.K, a.top_k, a.n_experts, a.x_per_slot, eb);
+    return (int)hipGetLastError();
+  }
+  const int units = (int)(a.K / (32 * Fmt<FMT>::UB));
+  const int log2g = moe_log2g(units);
+  const int64_t tile = 64 >> log2g;
+  const int64_t waves = (a.N + tile - 1) / tile;
+  const dim3 grid((unsigned)((waves + 3) / 4), (unsigned)P), block(256);
+  hipLaunchKernelGGL((k_moe_valu<FMT, 1>), grid, block, 0, a.stream, a.W, a.x, a.ids, a.y_slot,
+                     (int)a.N, (int)a.K, a.M, a.top_k, a.n_experts, a.x_per_slot, log2g, eb);
+  return (int)hipGetLastError();
+}
+
+template <int FMT>
+int gate_up_dispatch(const MoeGateUpArgs& a) {
+  const int64_t eb = a.inter * (a.hidden / 32) * Fmt<FMT>::BB;
+  const int P = a.M * a.top_k;
+  const int units = (int)(a.hidden / (32 * Fmt<FMT>::UB));
+  const int log2g = moe_log2g(units);
+  const int64_t tile = 64 >> log2g;
+  const int64_t waves = (a.inter + tile - 1) / tile;
+  const dim3 grid((unsigned)((waves + 3) / 4), (unsigned)P), block(256);
+  hipLaunchKernelGGL((k_moe_gate_up<FMT, 1>), grid, block, 0, a.stream, a.Wg, a.Wu, a.x, a.ids, a.h,
+                     (int)a.inter, (int)a.hidden, a.M, a.top_k, a.n_experts, log2g, eb);
+  return (int)hipGetLastError();
+}
+
+}  // namespace
+
+int launch_moe_gemv(const MoeArgs& a) {
+  switch (a.fmt) {
+    case KQ_Q8_0: return moe_dispatch<F_Q8_0>(a);
+    case KQ_Q4_0: return moe_dispatch<F_Q4_0>(a);
+    default: return moe_dispatch<F_AFFINE4>(a);
+  }
+}
+
+int launch_moe_gate_up_swiglu(const MoeGateUpArgs& a) {
+  switch (a.fmt) {
+    case KQ_Q8_0: return gate_up_dispatch<F_Q8_0>(a);
+    case KQ_Q4_0: return gate_up_dispatch<F_Q4_0>(a);
+    default: return gate_up_dispatch<F_AFFINE4>(a);
+  }
+}
+
+}  // namespace kq

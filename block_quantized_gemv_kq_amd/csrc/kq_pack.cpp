@@ -1,0 +1,236 @@
+// kq_pack.cpp — host-side block-format packer and unpacker.
+//
+// Encodes fp32 weight rows into Q8_0, Q4_0 and affine4 gs32 blocks (the block
+// definitions are in include/kq.h). The 4-bit formats are the two the Kipp
+// README, "How fast" contrasts: affine4 carries a bias term, Q4_0 is
+// scale-only. Kinetic docs, "Switching from llama.cpp" describe a quantizer
+// that writes fixed bytes per format; this packer writes the bytes fixed by
+// those definitions (byte equality with any other tool is not claimed).
+//
+// Built with -ffp-contract=off: every step is a single IEEE fp32 operation
+// with round-to-nearest-even, so the bytes are reproducible.
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+#include <cmath>
+#include <thread>
+#include <vector>
+
+#include "kq_internal.h"
+
+namespace kq {
+
+// fp32 -> fp16 bits, round to nearest even, subnormals kept, overflow to inf.
+uint16_t f32_to_f16_bits(float f) {
+  uint32_t x;
+  memcpy(&x, &f, 4);
+  const uint32_t sign = (x >> 16) & 0x8000u;
+  const uint32_t ax = x & 0x7fffffffu;
+  if (ax >= 0x7f800000u) {                    // inf or NaN
+    return (uint16_t)(sign | 0x7c00u | (ax > 0x7f800000u ? (0x0200u | ((ax >> 13) & 0x3ffu)) : 0u));
+  }
+  const uint32_t e = ax >> 23;                // biased fp32 exponent
+  if (e >= 113) {                             // |f| >= 2^-14: normal fp16 (or overflow)
+    uint32_t h = ((e - 112) << 10) | ((ax >> 13) & 0x3ffu);
+    const uint32_t rem = ax & 0x1fffu;
+    if (rem > 0x1000u || (rem == 0x1000u && (h & 1u))) h += 1;   // carry may reach inf
+    if (h >= 0x7c00u) h = 0x7c00u;
+    return (uint16_t)(sign | h);
+  }
+  if (e < 102) return (uint16_t)sign;         // |f| < 2^-25: rounds to zero
+  // subnormal: value = m * 2^(e-150), unit 2^-24 -> k = m >> (126 - e), RNE
+  const uint32_t m = (ax & 0x7fffffu) | 0x800000u;
+  const int shift = 126 - (int)e;             // 14..24
+  uint32_t k = m >> shift;
+  const uint32_t rem = m & ((1u << shift) - 1u);
+  const uint32_t half = 1u << (shift - 1);
+  if (rem > half || (rem == half && (k & 1u))) k += 1;
+  return (uint16_t)(sign | k);                // k == 0x400 is the smallest normal
+}
+
+float f16_bits_to_f32(uint16_t h) {
+  const uint32_t sign = (uint32_t)(h & 0x8000u) << 16;
+  const uint32_t e = (h >> 10) & 0x1fu;
+  const uint32_t m = h & 0x3ffu;
+  uint32_t x;
+  if (e == 0x1f) {
+    x = sign | 0x7f800000u | (m << 13);
+  } else if (e == 0) {
+    // subnormal or zero: m * 2^-24, exact in fp32
+    const float v = (float)m * 5.9604644775390625e-08f;
+    memcpy(&x, &v, 4);
+    x |= sign;
+  } else {
+    x = sign | ((e + 112) << 23) | (m << 13);
+  }
+  float f;
+  memcpy(&f, &x, 4);
+  return f;
+}
+
+namespace {
+
+inline float round_half_away(float v) { return std::round(v); }  // C round(): half away from zero
+
+inline bool finite16(uint16_t h) { return (h & 0x7c00u) != 0x7c00u; }
+
+inline void put16(uint8_t* p, uint16_t v) {
+  p[0] = (uint8_t)(v & 0xff);
+  p[1] = (uint8_t)(v >> 8);
+}
+
+// One block of 32 weights -> bytes. Returns false on a range error.
+bool pack_q8_0(const float* w, uint8_t* out) {
+  float a = 0.0f;
+  for (int j = 0; j < 32; ++j) a = std::max(a, std::fabs(w[j]));
+  const uint16_t dh = f32_to_f16_bits(a / 127.0f);
+  if (!finite16(dh)) return false;
+  const float d = f16_bits_to_f32(dh);
+  put16(out, dh);
+  for (int j = 0; j < 32; ++j) {
+    int q = 0;
+    if (d != 0.0f) {
+      const float r = round_half_away(w[j] / d);
+      q = (int)std::min(127.0f, std::max(-127.0f, r));
+    }
+    out[2 + j] = (uint8_t)(int8_t)q;
+  }
+  return true;
+}
+
+bool pack_q4_0(const float* w, uint8_t* out) {
+  int istar = 0;
+  float amax = std::fabs(w[0]);
+  for (int j = 1; j < 32; ++j) {
+    const float a = std::fabs(w[j]);
+    if (a > amax) { amax = a; istar = j; }     // strict: first index wins ties
+  }
+  const uint16_t dh = f32_to_f16_bits(w[istar] / -8.0f);
+  if (!finite16(dh)) return false;
+  const float d = f16_bits_to_f32(dh);
+  put16(out, dh);
+  uint8_t q[32];
+  for (int j = 0; j < 32; ++j) {
+    int v = 8;
+    if (d != 0.0f) {
+      const float r = round_half_away(w[j] / d) + 8.0f;
+      v = (int)std::min(15.0f, std::max(0.0f, r));
+    }
+    q[j] = (uint8_t)v;
+  }
+  for (int j = 0; j < 16; ++j) out[2 + j] = (uint8_t)(q[j] | (q[j + 16] << 4));
+  return true;
+}
+
+bool pack_affine4(const float* w, uint8_t* out) {
+  float lo = w[0], hi = w[0];
+  for (int j = 1; j < 32; ++j) {               // strict: first index wins ties
+    if (w[j] < lo) lo = w[j];
+    if (w[j] > hi) hi = w[j];
+  }
+  const float range = hi - lo;
+  const uint16_t sh = f32_to_f16_bits(range / 15.0f);
+  const uint16_t bh = f32_to_f16_bits(lo);
+  if (!finite16(sh) || !finite16(bh)) return false;
+  const float s = f16_bits_to_f32(sh);
+  const float b = f16_bits_to_f32(bh);
+  put16(out, sh);
+  put16(out + 2, bh);
+  uint8_t q[32];
+  for (int j = 0; j < 32; ++j) {
+    int v = 0;
+    if (s != 0.0f) {
+      const float diff = w[j] - b;
+      const float r = round_half_away(diff / s);
+      v = (int)std::min(15.0f, std::max(0.0f, r));
+    }
+    q[j] = (uint8_t)v;
+  }
+  for (int j = 0; j < 16; ++j) out[4 + j] = (uint8_t)(q[j] | (q[j + 16] << 4));
+  return true;
+}
+
+bool pack_rows(int fmt, const float* W, int64_t r0, int64_t r1, int64_t K, uint8_t* out) {
+  const int64_t nb = K / 32;
+  const int64_t bb = block_bytes(fmt);
+  for (int64_t r = r0; r < r1; ++r) {
+    const float* wr = W + r * K;
+    uint8_t* orow = out + r * nb * bb;
+    for (int64_t b = 0; b < nb; ++b) {
+      const float* w = wr + b * 32;
+      for (int j = 0; j < 32; ++j)
+        if (!std::isfinite(w[j])) return false;
+      bool ok = fmt == KQ_Q8_0 ? pack_q8_0(w, orow + b * bb)
+              : fmt == KQ_Q4_0 ? pack_q4_0(w, orow + b * bb)
+                               : pack_affine4(w, orow + b * bb);
+      if (!ok) return false;
+    }
+  }
+  return true;
+}
+
+}  // namespace
+
+int64_t block_bytes(int fmt) {
+  switch (fmt) {
+    case KQ_Q8_0: return 34;
+    case KQ_Q4_0: return 18;
+    case KQ_AFFINE4_G32: return 20;
+    default: return -1;
+  }
+}
+
+int pack(int fmt, const float* W, int64_t N, int64_t K, void* out, int n_threads) {
+  uint8_t* o = static_cast<uint8_t*>(out);
+  if (N == 0) return KQ_OK;
+  int nt = n_threads;
+  if (nt <= 0) nt = (int)std::min<unsigned>(64u, std::max(1u, std::thread::hardware_concurrency()));
+  const int64_t work = N * K;
+  if (work < (1 << 20)) nt = 1;
+  nt = (int)std::min<int64_t>(nt, N);
+  if (nt <= 1) return pack_rows(fmt, W, 0, N, K, o) ? KQ_OK : KQ_ERR_RANGE;
+  std::vector<std::thread> th;
+  std::vector<char> ok(nt, 1);
+  for (int t = 0; t < nt; ++t) {
+    const int64_t r0 = N * t / nt, r1 = N * (t + 1) / nt;
+    th.emplace_back([=, &ok] { ok[t] = pack_rows(fmt, W, r0, r1, K, o) ? 1 : 0; });
+  }
+  for (auto& t : th) t.join();
+  for (char c : ok)
+    if (!c) return KQ_ERR_RANGE;
+  return KQ_OK;
+}
+
+int unpack(int fmt, const void* packed, int64_t N, int64_t K, float* W) {
+  const uint8_t* p = static_cast<const uint8_t*>(packed);
+  const int64_t nb = K / 32;
+  const int64_t bb = block_bytes(fmt);
+  for (int64_t r = 0; r < N; ++r) {
+    for (int64_t b = 0; b < nb; ++b) {
+      const uint8_t* blk = p + (r * nb + b) * bb;
+      float* w = W + r * K + b * 32;
+      const uint16_t h0 = (uint16_t)(blk[0] | (blk[1] << 8));
+      if (fmt == KQ_Q8_0) {
+        const float d = f16_bits_to_f32(h0);
+        for (int j = 0; j < 32; ++j) w[j] = d * (float)(int8_t)blk[2 + j];
+      } else if (fmt == KQ_Q4_0) {
+        const float d = f16_bits_to_f32(h0);
+        for (int j = 0; j < 16; ++j) {
+          w[j] = d * (float)((blk[2 + j] & 15) - 8);
+          w[j + 16] = d * (float)((blk[2 + j] >> 4) - 8);
+        }
+      } else {
+        const float s = f16_bits_to_f32(h0);
+        const float bias = f16_bits_to_f32((uint16_t)(blk[2] | (blk[3] << 8)));
+        for (int j = 0; j < 16; ++j) {
+          w[j] = std::fma(s, (float)(blk[4 + j] & 15), bias);
+          w[j + 16] = std::fma(s, (float)(blk[4 + j] >> 4), bias);
+        }
+      }
+    }
+  }
+  return KQ_OK;
+}
+
+}  // namespace kq

@@ -1,0 +1,190 @@
+/*
+ * kq.h — block-quantized decode GEMV for AMD Instinct MI355X (gfx950).
+ *
+ * A C ABI over hand-written HIP kernels for the memory-bound decode step of
+ * LLM inference: dequantize-and-multiply of block-quantized weights against a
+ * few activation columns, and the routed-expert (mixture-of-experts) variant.
+ *
+ * Where the operation comes from (page title, section):
+ *  - Kinetic docs, "What makes it fast": generating a token reads every weight
+ *    of a dense model once, so decode is bound by memory bandwidth; guessed
+ *    tokens are checked "in one pass over the weights" (M columns share one
+ *    weight pass); up to four requests share every pass; choosing the next
+ *    token reads an output layer of up to a quarter of a million rows; a
+ *    mixture of experts keeps only the experts in use busy.
+ *  - Kipp README, "How fast" (footnote to the 4-bit row): affine4 gs32 stores
+ *    a scale and a bias per 32 weights, Q4_0 only a scale.
+ *  - Kapitsa README, "What's new" and "How it works": a verify pass checks 8
+ *    rows (draft-tree candidates); three requests can share one verify pass.
+ *  - kinfer page, "Models bigger than the machine": a mixture of experts uses
+ *    a few experts per token (10 of 512), so only those weights are read.
+ *
+ * Block formats (32 weights per block along K; a packed row is K/32 blocks
+ * back to back, a packed matrix is its N rows back to back, no padding):
+ *   KQ_Q8_0        34 B: fp16 d, 32 x int8 q;            w' = d*q
+ *   KQ_Q4_0        18 B: fp16 d, 16 B nibbles;            w' = d*(q-8)
+ *   KQ_AFFINE4_G32 20 B: fp16 s, fp16 b, 16 B nibbles;    w' = s*q + b
+ * fp16 values are little-endian; in the 4-bit formats element j sits in the
+ * low nibble of byte j and element j+16 in the high nibble.
+ *
+ * Conventions for every call:
+ *  - Return 0 (KQ_OK) or a negative kq_status. kq_last_error() gives a
+ *    thread-local message for the last failure on the calling thread.
+ *  - All argument checks run on the host before any HIP call; a call that
+ *    fails them touches no memory and launches nothing.
+ *  - "device" pointers are HIP device memory of the current device; "host"
+ *    pointers are ordinary CPU memory. The caller owns every buffer; the
+ *    library keeps no pointer after a call returns and allocates nothing.
+ *  - GPU calls are asynchronous on `stream` (a hipStream_t; NULL = the
+ *    default stream) and never synchronise. Faults inside a kernel surface at
+ *    the caller's next synchronisation of that stream.
+ *  - Calls that share a workspace must not overlap in time.
+ */
+#ifndef KQ_H_
+#define KQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KQ_VERSION 100  /* 1.0.0 */
+
+typedef enum kq_format {
+  KQ_Q8_0 = 0,
+  KQ_Q4_0 = 1,
+  KQ_AFFINE4_G32 = 2
+} kq_format;
+
+typedef enum kq_status {
+  KQ_OK = 0,
+  KQ_ERR_ARG = -1,     /* null pointer, negative or too large size, bad M/top_k */
+  KQ_ERR_FORMAT = -2,  /* unknown kq_format */
+  KQ_ERR_SHAPE = -3,   /* K <= 0 or K % 32 != 0, or K beyond KQ_MAX_K */
+  KQ_ERR_ALIGN = -4,   /* pointer misaligned (see each call) */
+  KQ_ERR_RANGE = -5,   /* kq_pack: non-finite weight, or scale/bias overflows fp16 */
+  KQ_ERR_HIP = -6      /* HIP launch/runtime error (message in kq_last_error) */
+} kq_status;
+
+#define KQ_MAX_M 64            /* activation columns per call */
+#define KQ_MAX_K (1 << 20)     /* inputs per row */
+#define KQ_MAX_N 0x7fffffff    /* output rows per call */
+
+/* Library version (KQ_VERSION of the built library). */
+int kq_version(void);
+
+/* Human-readable name of a kq_status value. Never NULL. */
+const char* kq_status_string(int status);
+
+/* Message describing the last failure on this thread ("" if none). */
+const char* kq_last_error(void);
+
+/* Bytes per 32-weight block of `fmt` (34, 18, 20), or a negative kq_status. */
+int64_t kq_block_bytes(int fmt);
+
+/* Bytes of a packed N x K matrix: N * (K/32) * kq_block_bytes(fmt).
+ * Returns a negative kq_status for a bad format, N < 0 or a bad K. */
+int64_t kq_packed_bytes(int fmt, int64_t N, int64_t K);
+
+/* kq_pack — quantize a row-major fp32 matrix W[N][K] (host) into packed blocks
+ * written to `out` (host, kq_packed_bytes(fmt,N,K) bytes).
+ * Per block of 32 consecutive weights w_j of one row (all arithmetic IEEE fp32
+ * with round-to-nearest-even; fp16() rounds to nearest even, keeping
+ * subnormals; round() is round-half-away-from-zero; q uses the STORED fp16
+ * scale/bias):
+ *   Q8_0:    d = fp16(max|w_j| / 127); q_j = clamp(round(w_j/d), -127, 127), 0 if d == 0
+ *   Q4_0:    m = w_i at the first i maximising |w_i|; d = fp16(m / -8);
+ *            q_j = clamp(round(w_j/d) + 8, 0, 15), 8 if d == 0
+ *   AFFINE4: lo/hi = min/max w_j (first index on ties); s = fp16((hi-lo)/15),
+ *            b = fp16(lo); q_j = clamp(round((w_j-b)/s), 0, 15), 0 if s == 0
+ * The bytes are identical to those of the library's CPU reference.
+ * Errors: KQ_ERR_ARG (null, N < 0), KQ_ERR_FORMAT, KQ_ERR_SHAPE,
+ * KQ_ERR_RANGE (non-finite weight, or a scale/bias that is infinite in fp16;
+ * `out` is then left partly written). Uses up to `n_threads` host threads
+ * (<= 0: one per hardware thread, capped at 64). */
+int kq_pack(int fmt, const float* W, int64_t N, int64_t K, void* out, int n_threads);
+
+/* kq_unpack — dequantize packed blocks (host) to fp32 W_out[N][K] (host):
+ * w' as above, computed in fp32 (exact for Q8_0 and Q4_0; affine4 is
+ * s*q + b rounded once, exact unless s and b differ by more than 2^13 in scale). */
+int kq_unpack(int fmt, const void* packed, int64_t N, int64_t K, float* W_out);
+
+/* kq_gemv — y[m][n] = sum_k w'[n][k] * x[m][k] for m < M, n < N.
+ *   W: device, packed N x K matrix (kq_pack layout), 4-byte aligned.
+ *   x: device, fp16 bits [M][K] (column m contiguous), 16-byte aligned.
+ *   y: device, fp32 [M][N], 4-byte aligned; overwritten, never accumulated.
+ * Every weight byte is read once per call whatever M is. Accumulation is fp32;
+ * results are run-to-run deterministic (fixed reduction order, no atomics).
+ * M == 0 or N == 0 is a valid empty call. 1 <= M <= KQ_MAX_M.
+ * Errors: KQ_ERR_ARG, KQ_ERR_FORMAT, KQ_ERR_SHAPE, KQ_ERR_ALIGN, KQ_ERR_HIP. */
+int kq_gemv(int fmt, const void* W, const uint16_t* x, float* y,
+            int64_t N, int64_t K, int M, void* stream);
+
+/* Workspace bytes kq_moe_gemv needs (0 when route_w is NULL). */
+int64_t kq_moe_gemv_workspace_bytes(int64_t N, int M, int top_k, int weighted);
+
+/* kq_moe_gemv — routed-expert GEMV for M decode tokens with top_k slots each.
+ *   W_experts: device, n_experts packed N x K matrices back to back (expert e
+ *              starts at e * kq_packed_bytes(fmt, N, K)), 4-byte aligned.
+ *   x: device fp16 bits; x_per_slot == 0: [M][K] (every slot of token m reads
+ *      x[m]); x_per_slot == 1: [M][top_k][K] (slot j reads x[m][j]). 16-B aligned.
+ *   route_ids: device int32 [M][top_k]; ids must lie in [0, n_experts).
+ *      An id outside that range reads nothing and yields NaN outputs for its slot.
+ *   route_w: device fp32 [M][top_k] or NULL.
+ *   y: device fp32. route_w == NULL: per-slot outputs y[M][top_k][N].
+ *      route_w != NULL: y[M][N] = sum_j route_w[m][j] * (W_{id[m][j]} x_{m,j}),
+ *      summed in slot order j = 0..top_k-1.
+ *   workspace: device, kq_moe_gemv_workspace_bytes(N, M, top_k, route_w != NULL)
+ *      bytes, 16-B aligned (may be NULL when that size is 0).
+ * Each distinct expert's weights are read once per call, for all the tokens
+ * routed to it (found on the device; no host synchronisation).
+ * Errors: KQ_ERR_ARG (incl. top_k not in [1, n_experts], small workspace),
+ * KQ_ERR_FORMAT, KQ_ERR_SHAPE, KQ_ERR_ALIGN, KQ_ERR_HIP. */
+int kq_moe_gemv(int fmt, const void* W_experts, const uint16_t* x,
+                const int32_t* route_ids, const float* route_w, float* y,
+                int64_t N, int64_t K, int M, int top_k, int n_experts, int x_per_slot,
+                void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes kq_moe_ffn needs. */
+int64_t kq_moe_ffn_workspace_bytes(int64_t hidden, int64_t inter, int M, int top_k);
+
+/* kq_moe_ffn — the routed-expert FFN of M decode tokens:
+ *   for token m, slot j, expert e = route_ids[m][j]:
+ *     g = Gate_e x_m, u = Up_e x_m            (inter outputs each)
+ *     h = fp16(silu(g) * u), silu(z) = z / (1 + e^-z) in fp32
+ *   y[m] = sum_j route_w[m][j] * (Down_e h)    (hidden outputs, slot order)
+ *   W_gate, W_up: device, n_experts packed inter x hidden matrices back to back.
+ *   W_down: device, n_experts packed hidden x inter matrices back to back.
+ *   x: device fp16 [M][hidden]; y: device fp32 [M][hidden]; route_* as above
+ *   (route_w must not be NULL). Gate and up rows of one expert are read in
+ *   the same pass and SwiGLU is applied in registers.
+ *   h_out: optional device fp16 [M][top_k][inter] copy of h (NULL: not kept).
+ *   workspace: kq_moe_ffn_workspace_bytes(hidden, inter, M, top_k) bytes, 16-B aligned.
+ * Errors: as kq_moe_gemv; KQ_ERR_SHAPE also when hidden % 64 != 0 for Q8_0/Q4_0. */
+int kq_moe_ffn(int fmt, const void* W_gate, const void* W_up, const void* W_down,
+               const uint16_t* x, const int32_t* route_ids, const float* route_w,
+               float* y, uint16_t* h_out, int64_t hidden, int64_t inter,
+               int M, int top_k, int n_experts,
+               void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes kq_argmax needs. */
+int64_t kq_argmax_workspace_bytes(int64_t N, int M);
+
+/* kq_argmax — for each column m < M of y (device fp32 [M][N]), the index of
+ * its largest value; the lowest index wins ties; NaN never wins (all-NaN
+ * columns give 0). Written to out (device int32 [M]). This is the greedy
+ * next-token choice over a vocabulary-sized output layer.
+ * Errors: KQ_ERR_ARG, KQ_ERR_ALIGN, KQ_ERR_HIP. */
+int kq_argmax(const float* y, int64_t N, int M, int32_t* out,
+              void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Test hook: convert n fp32 values (host) to fp16 bits (host) with the
+ * packer's own round-to-nearest-even conversion. */
+int kq_f32_to_f16(const float* in, uint16_t* out, int64_t n);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KQ_H_ */

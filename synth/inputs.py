@@ -15,13 +15,18 @@ regenerated on its own:
 * activations:  ``(workload_id, layer, input_slot, 1, column)``
 * MoE route ids ``(workload_id, 1, token)``, route logits ``(workload_id, 2, token)``
 
-Draw recipe: ``rng.standard_normal(shape, dtype=float32) * float32(0.02)`` for
-weights (fp32), ``rng.standard_normal(K, dtype=float32).astype(float16)`` for
-one activation column.
+Draw recipe: weights are drawn in blocks of 4096 rows; row block ``b`` of a
+matrix with seed ``s`` is ``default_rng(s + (b,)).standard_normal((rows, K),
+dtype=float32) * float32(0.02)`` (so blocks can be drawn in parallel and a
+sampled row can be regenerated alone). One activation column is
+``default_rng(seed).standard_normal(K, dtype=float32).astype(float16)``.
 """
 from __future__ import annotations
 
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
+import os
+
 import numpy as np
 
 __all__ = [
@@ -32,14 +37,48 @@ __all__ = [
 ]
 
 WEIGHT_STD = np.float32(0.02)
+ROW_BLOCK = 4096
+_THREADS = max(1, min(16, os.cpu_count() or 1))
+
+
+def _row_block(seed, b: int, rows: int, k: int) -> np.ndarray:
+    rng = np.random.default_rng(list(seed) + [b])
+    w = rng.standard_normal((rows, k), dtype=np.float32)
+    w *= WEIGHT_STD
+    return w
 
 
 def weights(seed, n: int, k: int) -> np.ndarray:
-    """fp32 [n, k] drawn from N(0, 0.02) with ``default_rng(seed)``."""
-    rng = np.random.default_rng(list(seed))
-    w = rng.standard_normal((n, k), dtype=np.float32)
-    w *= WEIGHT_STD
-    return w
+    """fp32 [n, k] drawn from N(0, 0.02), row blocks of 4096 seeded seed + (b,)."""
+    out = np.empty((n, k), np.float32)
+    nb = (n + ROW_BLOCK - 1) // ROW_BLOCK
+
+    def fill(b):
+        r0 = b * ROW_BLOCK
+        r1 = min(n, r0 + ROW_BLOCK)
+        out[r0:r1] = _row_block(seed, b, r1 - r0, k)
+
+    if nb <= 1:
+        for b in range(nb):
+            fill(b)
+    else:
+        with ThreadPoolExecutor(min(_THREADS, nb)) as ex:
+            list(ex.map(fill, range(nb)))
+    return out
+
+
+def weight_rows(seed, n: int, k: int, rows) -> np.ndarray:
+    """Only the given rows of ``weights(seed, n, k)`` (regenerates just the
+    row blocks that hold them)."""
+    rows = np.asarray(rows)
+    out = np.empty((rows.size, k), np.float32)
+    for b in np.unique(rows // ROW_BLOCK):
+        r0 = int(b) * ROW_BLOCK
+        r1 = min(n, r0 + ROW_BLOCK)
+        blk = _row_block(seed, int(b), r1 - r0, k)
+        sel = np.nonzero(rows // ROW_BLOCK == b)[0]
+        out[sel] = blk[rows[sel] - r0]
+    return out
 
 
 def activation_column(seed, k: int) -> np.ndarray:

@@ -1,0 +1,154 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import block_quantized_gemv_kq_amd as kq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kq.h")
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kq_\w+)\s*\(", src)))
+
+
+def test_library_loads():
+    assert kq.kq_version() == 100
+
+
+def test_exports_every_declared_symbol():
+    names = header_functions()
+    assert len(names) >= 15
+    L = ctypes.CDLL(kq.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), f"libkq.so does not export {n}"
+    assert set(names) == set(kq.SIGNATURES), "binding and header disagree"
+
+
+def test_status_strings():
+    for code, name in [(0, "KQ_OK"), (-1, "KQ_ERR_ARG"), (-2, "KQ_ERR_FORMAT"), (-3, "KQ_ERR_SHAPE"),
+                       (-4, "KQ_ERR_ALIGN"), (-5, "KQ_ERR_RANGE"), (-6, "KQ_ERR_HIP")]:
+        assert kq.status_name(code) == name
+    assert kq.status_name(-99) == "KQ_ERR_UNKNOWN"
+
+
+def test_sizes():
+    assert [kq.kq_block_bytes(f) for f in ("q8_0", "q4_0", "affine4")] == [34, 18, 20]
+    assert kq.kq_packed_bytes("affine4", 4096, 2560) == 4096 * 80 * 20
+    assert kq.kq_packed_bytes("q8_0", 151936, 2560) == 413265920
+    assert kq.kq_packed_bytes("q4_0", 0, 1024) == 0
+    L = kq.lib()
+    assert L.kq_packed_bytes(3, 1, 32) == kq.KQ_ERR_FORMAT
+    assert L.kq_packed_bytes(0, 1, 33) == kq.KQ_ERR_SHAPE
+    assert L.kq_packed_bytes(0, 1, 0) == kq.KQ_ERR_SHAPE
+    assert L.kq_packed_bytes(0, -1, 32) == kq.KQ_ERR_ARG
+    assert L.kq_packed_bytes(0, 1, (1 << 20) + 32) == kq.KQ_ERR_SHAPE
+    assert L.kq_block_bytes(7) == kq.KQ_ERR_FORMAT
+
+
+# Fake, never-dereferenced device addresses: every call below must fail in
+# validation, before any HIP call.
+A16 = 0x10000
+A4 = 0x10004
+
+
+def _gemv(fmt=0, W=A16, x=A16, y=A16, N=8, K=64, M=1):
+    return kq.lib().kq_gemv(fmt, W, x, y, N, K, M, 0)
+
+
+def test_gemv_validation():
+    assert _gemv(fmt=5) == kq.KQ_ERR_FORMAT
+    assert _gemv(K=48) == kq.KQ_ERR_SHAPE
+    assert _gemv(K=0) == kq.KQ_ERR_SHAPE
+    assert _gemv(K=-32) == kq.KQ_ERR_SHAPE
+    assert _gemv(N=-1) == kq.KQ_ERR_ARG
+    assert _gemv(M=65) == kq.KQ_ERR_ARG
+    assert _gemv(M=-1) == kq.KQ_ERR_ARG
+    assert _gemv(W=None) == kq.KQ_ERR_ARG
+    assert _gemv(x=None) == kq.KQ_ERR_ARG
+    assert _gemv(y=None) == kq.KQ_ERR_ARG
+    assert _gemv(W=A16 + 2) == kq.KQ_ERR_ALIGN
+    assert _gemv(y=A16 + 1) == kq.KQ_ERR_ALIGN
+    assert _gemv(x=A4) == kq.KQ_ERR_ALIGN
+    assert "16-byte" in kq.last_error()
+    # empty problems are valid and launch nothing
+    assert _gemv(M=0, W=None, x=None, y=None) == kq.KQ_OK
+    assert _gemv(N=0, W=None, x=None, y=None) == kq.KQ_OK
+
+
+def _moe(fmt=1, W=A16, x=A16, ids=A16, rw=None, y=A16, N=64, K=64, M=2, top_k=2, E=4, xps=0,
+         ws=None, wsb=0):
+    return kq.lib().kq_moe_gemv(fmt, W, x, ids, rw, y, N, K, M, top_k, E, xps, ws, wsb, 0)
+
+
+def test_moe_validation():
+    assert _moe(top_k=0) == kq.KQ_ERR_ARG
+    assert _moe(top_k=5) == kq.KQ_ERR_ARG        # > n_experts
+    assert _moe(E=0) == kq.KQ_ERR_ARG
+    assert _moe(xps=2) == kq.KQ_ERR_ARG
+    assert _moe(fmt=9) == kq.KQ_ERR_FORMAT
+    assert _moe(K=40) == kq.KQ_ERR_SHAPE
+    assert _moe(ids=None) == kq.KQ_ERR_ARG
+    assert _moe(x=A4) == kq.KQ_ERR_ALIGN
+    assert _moe(W=A16 + 2) == kq.KQ_ERR_ALIGN
+    # weighted output needs M*top_k*N*4 bytes of workspace
+    need = kq.kq_moe_gemv_workspace_bytes(64, 2, 2, True)
+    assert need == 2 * 2 * 64 * 4
+    assert kq.kq_moe_gemv_workspace_bytes(64, 2, 2, False) == 0
+    assert _moe(rw=A16) == kq.KQ_ERR_ARG
+    assert _moe(rw=A16, ws=A16, wsb=need - 1) == kq.KQ_ERR_ARG
+    assert _moe(rw=A16, ws=A4, wsb=need) == kq.KQ_ERR_ALIGN
+    assert _moe(M=0) == kq.KQ_OK
+
+
+def test_moe_ffn_validation():
+    L = kq.lib()
+    need = kq.kq_moe_ffn_workspace_bytes(2048, 768, 4, 8)
+    assert need >= 4 * 8 * 768 * 2 + 4 * 8 * 2048 * 4
+
+    def call(fmt=1, rw=A16, ws=A16, wsb=need, hidden=2048, inter=768, top_k=8, E=128):
+        return L.kq_moe_ffn(fmt, A16, A16, A16, A16, A16, rw, A16, None, hidden, inter, 4, top_k, E,
+                            ws, wsb, 0)
+    assert call(rw=None) == kq.KQ_ERR_ARG
+    assert call(wsb=need - 1) == kq.KQ_ERR_ARG
+    assert call(ws=A4) == kq.KQ_ERR_ALIGN
+    assert call(hidden=2080) == kq.KQ_ERR_SHAPE    # Q4_0 needs hidden % 64 == 0
+    assert call(inter=770) == kq.KQ_ERR_SHAPE
+    assert call(top_k=129) == kq.KQ_ERR_ARG
+
+
+def test_argmax_validation():
+    L = kq.lib()
+    need = kq.kq_argmax_workspace_bytes(151936, 3)
+    assert need == 3 * ((151936 + 16383) // 16384) * 8
+    assert L.kq_argmax(A16, 0, 1, A16, A16, need, 0) == kq.KQ_ERR_ARG
+    assert L.kq_argmax(A16, 151936, 65, A16, A16, need, 0) == kq.KQ_ERR_ARG
+    assert L.kq_argmax(A16, 151936, 3, A16, A16, need - 8, 0) == kq.KQ_ERR_ARG
+    assert L.kq_argmax(A16 + 2, 151936, 3, A16, A16, need, 0) == kq.KQ_ERR_ALIGN
+    assert L.kq_argmax(A16, 151936, 0, A16, None, 0, 0) == kq.KQ_OK
+
+
+def test_pack_validation():
+    W = np.zeros((2, 32), np.float32)
+    with pytest.raises(kq.KQError) as e:
+        kq.kq_pack(4, W)
+    assert e.value.status == kq.KQ_ERR_FORMAT
+    W[0, 3] = np.inf
+    with pytest.raises(kq.KQError) as e:
+        kq.kq_pack("q8_0", W)
+    assert e.value.status == kq.KQ_ERR_RANGE
+    W[0, 3] = 1e6   # affine4: range/15 fine, but bias fp16(lo) ok; q8_0 d = 1e6/127 < 65504
+    kq.kq_pack("q8_0", W)
+    W[0, 3] = -70000.0
+    with pytest.raises(kq.KQError) as e:
+        kq.kq_pack("affine4", W)    # b = fp16(-70000) overflows
+    assert e.value.status == kq.KQ_ERR_RANGE
+    assert kq.lib().kq_pack(0, None, 1, 32, None, 1) == kq.KQ_ERR_ARG
+    assert kq.lib().kq_pack(0, None, 0, 32, None, 1) == kq.KQ_OK

@@ -1,0 +1,150 @@
+"""GPU parity of kq_gemv against the fp64 oracle, through the C ABI.
+
+Bar: |y - y_ref| <= 2e-3 * sum|w'x| + 1e-6 per output, plus closed-form
+probes (unit vectors give w' exactly, y(2x) == 2 y(x) bitwise), run-to-run
+bitwise determinism, and row/column independence.
+"""
+import numpy as np
+import pytest
+
+import block_quantized_gemv_kq_amd as kq
+from oracle import formats as F
+from oracle import ref as R
+from synth import inputs as S
+from tests import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+FMTS = ("q8_0", "q4_0", "affine4")
+M_LIST = (1, 2, 3, 4, 7, 8, 9, 15, 16, 17, 32, 48, 64)
+
+
+def _case(fmt, N, K, M, seed):
+    W = S.weights((80, seed, N, K), N, K)
+    x = S.activations((80, seed, K), K, M)
+    packed, fields = U.quantize_both(fmt, W)
+    return packed, fields, x
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("M", M_LIST)
+def test_parity_small(fmt, M):
+    N, K = 333, 1024                  # several tiles and a ragged tail
+    packed, fields, x = _case(fmt, N, K, M, 0)
+    y = U.gemv_gpu(fmt, U.to_dev(packed), x, N, K)
+    yr, ad = R.gemv(fmt, fields, x)
+    U.assert_parity(y, yr, ad, f"{fmt} M={M}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("N,K", [(1, 64), (5, 128), (64, 256), (77, 2560), (130, 4096), (41, 9728),
+                                 (3, 32), (9, 96), (17, 160)])
+@pytest.mark.parametrize("M", (1, 5, 16))
+def test_parity_shapes(fmt, N, K, M):
+    packed, fields, x = _case(fmt, N, K, M, 1)
+    y = U.gemv_gpu(fmt, U.to_dev(packed), x, N, K)
+    yr, ad = R.gemv(fmt, fields, x)
+    U.assert_parity(y, yr, ad, f"{fmt} N={N} K={K} M={M}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_generic_path_parity(fmt):
+    N, K, M = 70, 1024, 3
+    packed, fields, x = _case(fmt, N, K, M, 2)
+    y = U.gemv_gpu(fmt, U.to_dev(packed), x, N, K, path="generic")
+    yr, ad = R.gemv(fmt, fields, x)
+    U.assert_parity(y, yr, ad, f"{fmt} generic")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_unit_vectors_exact(fmt):
+    """x = e_k gives y[n] = w'[n][k] exactly (w' is representable in fp32 for
+    these value ranges): pins nibble order and block indexing."""
+    N, K = 96, 512
+    W = S.weights((81, 0, 0, 0), N, K)
+    packed, fields = U.quantize_both(fmt, W)
+    Wd = F.dequantize(fmt, fields)
+    ks = [0, 1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 200, 255, 256, 500, 511]
+    x = np.zeros((len(ks), K), np.float16)
+    for i, k in enumerate(ks):
+        x[i, k] = 1.0
+    Wdev = U.to_dev(packed)
+    for m0 in range(0, len(ks), 4):            # VALU path, 4 columns at a time
+        y = U.gemv_gpu(fmt, Wdev, x[m0:m0 + 4], N, K)
+        for i in range(y.shape[0]):
+            assert np.array_equal(y[i].astype(np.float64), Wd[:, ks[m0 + i]]), (fmt, ks[m0 + i])
+    y = U.gemv_gpu(fmt, Wdev, x, N, K)       # all columns in one call
+    for i, k in enumerate(ks):
+        assert np.array_equal(y[i].astype(np.float64), Wd[:, k]), (fmt, k, "M=16")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("M", (1, 3, 16))
+def test_scale_by_two_bitwise_and_deterministic(fmt, M):
+    N, K = 300, 2560
+    packed, fields, x = _case(fmt, N, K, M, 3)
+    Wdev = U.to_dev(packed)
+    y1 = U.gemv_gpu(fmt, Wdev, x, N, K)
+    y1b = U.gemv_gpu(fmt, Wdev, x, N, K)
+    assert np.array_equal(y1.view(np.uint32), y1b.view(np.uint32)), "not deterministic"
+    x2 = (x.astype(np.float32) * 2).astype(np.float16)
+    y2 = U.gemv_gpu(fmt, Wdev, x2, N, K)
+    assert np.array_equal(y2, 2 * y1)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_columns_match_single_column_runs(fmt):
+    """Each column of an M-column call equals its own M=1 call (within the
+    tolerance; bitwise on the VALU path, which keeps each column's summation
+    order)."""
+    N, K, M = 200, 2048, 8
+    packed, fields, x = _case(fmt, N, K, M, 4)
+    Wdev = U.to_dev(packed)
+    y = U.gemv_gpu(fmt, Wdev, x, N, K)
+    for m in range(M):
+        y1 = U.gemv_gpu(fmt, Wdev, x[m:m + 1], N, K)
+        assert np.array_equal(y[m], y1[0]), (fmt, m)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_row_concatenation_bitwise(fmt):
+    K = 1024
+    Wa = S.weights((82, 0, 0, 0), 100, K)
+    Wb = S.weights((82, 1, 0, 0), 61, K)
+    x = S.activations((82, 0, 0), K, 2)
+    pa = kq.kq_pack(fmt, Wa)
+    pb = kq.kq_pack(fmt, Wb)
+    pab = kq.kq_pack(fmt, np.concatenate([Wa, Wb]))
+    assert np.array_equal(pab, np.concatenate([pa, pb]))
+    ya = U.gemv_gpu(fmt, U.to_dev(pa), x, 100, K)
+    yb = U.gemv_gpu(fmt, U.to_dev(pb), x, 61, K)
+    yab = U.gemv_gpu(fmt, U.to_dev(pab), x, 161, K)
+    assert np.array_equal(yab, np.concatenate([ya, yb], axis=1))
+
+
+def test_single_q8_0_workload():
+    """The single 1024 x 1024 Q8_0 GEMV (weights seed 0, activation seed 1)."""
+    w = S.SINGLE_Q8_0
+    W = S.weights(w.weight_seed, w.n, w.k)
+    x = S.activation_column(w.act_seed, w.k)[None, :]
+    packed, fields = U.quantize_both("q8_0", W)
+    y = U.gemv_gpu("q8_0", U.to_dev(packed), x, w.n, w.k)
+    yr, ad = R.gemv("q8_0", fields, x)
+    ratio = U.assert_parity(y, yr, ad, "single q8_0")
+    assert ratio < 1e-4
+    assert int(np.argmax(y[0])) == int(R.argmax_lowest(yr[0]))
+
+
+def test_zero_and_constant_weights():
+    K = 256
+    W = np.zeros((8, K), np.float32)
+    W[1] = 0.5
+    W[2] = -3.0
+    W[3, ::3] = -0.0
+    x = S.activations((83, 0, 0), K, 2)
+    for fmt in FMTS:
+        packed, fields = U.quantize_both(fmt, W)
+        y = U.gemv_gpu(fmt, U.to_dev(packed), x, 8, K)
+        yr, ad = R.gemv(fmt, fields, x)
+        U.assert_parity(y, yr, ad, f"{fmt} constant rows")
+        assert np.all(y[:, 0] == 0.0)

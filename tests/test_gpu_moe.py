@@ -1,0 +1,129 @@
+"""GPU parity of the routed-expert calls (kq_moe_gemv, kq_moe_ffn) against the
+oracle, through the C ABI. Experts nobody routes to are filled with bytes
+that dequantize to NaN/huge values, so reading one would show in the output."""
+import numpy as np
+import pytest
+
+import block_quantized_gemv_kq_amd as kq
+from oracle import formats as F
+from oracle import ref as R
+from synth import inputs as S
+from tests import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+
+class Experts:
+    """n_experts packed matrices back to back on the device; only the ones
+    in `used` hold real weights (the oracle quantizes only those)."""
+
+    def __init__(self, fmt, n_experts, N, K, used, seed_fn):
+        self.fmt, self.N, self.K = fmt, N, K
+        eb = kq.kq_packed_bytes(fmt, N, K)
+        host = np.full((n_experts, eb), 0xFF, np.uint8)      # poison: fp16 NaN scales
+        self.fields = {}
+        for e in sorted(set(int(v) for v in used)):
+            W = S.weights(seed_fn(e), N, K)
+            packed, fields = U.quantize_both(fmt, W)
+            host[e] = packed.reshape(-1)
+            self.fields[e] = fields
+        self.dev = U.to_dev(host)
+
+    def field_list(self, n):
+        return [self.fields.get(e) for e in range(n)]
+
+
+def _route(M, E, top_k, seed):
+    ids, rw = S.route_table(70 + seed, M, E, top_k)
+    return ids, rw
+
+
+@pytest.mark.parametrize("fmt", ("q4_0", "q8_0", "affine4"))
+@pytest.mark.parametrize("M,top_k,E", [(1, 8, 32), (4, 8, 32), (16, 8, 32), (3, 1, 4), (5, 4, 4)])
+def test_moe_gemv_per_slot(fmt, M, top_k, E):
+    N, K = 96, 512
+    ids, rw = _route(M, E, top_k, M)
+    ex = Experts(fmt, E, N, K, ids.ravel(), lambda e: (71, e, 0, 0))
+    x = S.activations((71, 0, 0), K, M)
+    y = U.empty_dev((M, top_k, N))
+    kq.kq_moe_gemv(fmt, ex.dev, U.to_dev(x), U.to_dev(ids), None, y, N, K, M, top_k, E, 0)
+    yg = U.to_host(y)
+    yr, ad = R.moe_gemv(fmt, ex.field_list(E), x, ids, None, False)
+    U.assert_parity(yg, yr, ad, f"moe per-slot {fmt} M={M}")
+
+
+@pytest.mark.parametrize("fmt", ("q4_0", "affine4"))
+@pytest.mark.parametrize("M", (1, 4, 16))
+def test_moe_gemv_weighted_x_per_slot(fmt, M):
+    N, K, E, top_k = 128, 256, 16, 4
+    ids, rw = _route(M, E, top_k, 10 + M)
+    ex = Experts(fmt, E, N, K, ids.ravel(), lambda e: (72, e, 0, 0))
+    x = S.activations((72, 0, 0), K, M * top_k).reshape(M, top_k, K)
+    y = U.empty_dev((M, N))
+    wsb = kq.kq_moe_gemv_workspace_bytes(N, M, top_k, True)
+    ws = U.empty_dev((wsb // 4,))
+    kq.kq_moe_gemv(fmt, ex.dev, U.to_dev(x), U.to_dev(ids), U.to_dev(rw), y, N, K, M, top_k, E, 1, ws, wsb)
+    yg = U.to_host(y)
+    yr, ad = R.moe_gemv(fmt, ex.field_list(E), x, ids, rw, True)
+    U.assert_parity(yg, yr, ad, f"moe weighted {fmt} M={M}")
+
+
+def test_moe_shared_expert_dedup_and_duplicates():
+    """Every token routed to the same experts (and one token naming an expert
+    twice): each expert's weights serve all its slots."""
+    fmt, N, K, E = "q4_0", 64, 256, 8
+    ids = np.array([[3, 5], [3, 5], [5, 3], [1, 1]], np.int32)
+    rw = np.full(ids.shape, 0.5, np.float32)
+    ex = Experts(fmt, E, N, K, ids.ravel(), lambda e: (73, e, 0, 0))
+    x = S.activations((73, 0, 0), K, 4)
+    y = U.empty_dev((4, 2, N))
+    kq.kq_moe_gemv(fmt, ex.dev, U.to_dev(x), U.to_dev(ids), None, y, N, K, 4, 2, E, 0)
+    yr, ad = R.moe_gemv(fmt, ex.field_list(E), x, ids, None, False)
+    U.assert_parity(U.to_host(y), yr, ad, "dedup")
+
+
+def test_moe_bad_route_id_gives_nan_without_reading():
+    fmt, N, K, E = "q4_0", 64, 256, 4
+    ids = np.array([[0, 7], [-1, 2]], np.int32)
+    ex = Experts(fmt, E, N, K, [0, 2], lambda e: (74, e, 0, 0))
+    x = S.activations((74, 0, 0), K, 2)
+    y = U.empty_dev((2, 2, N))
+    kq.kq_moe_gemv(fmt, ex.dev, U.to_dev(x), U.to_dev(ids), None, y, N, K, 2, 2, E, 0)
+    yg = U.to_host(y)
+    assert np.all(np.isnan(yg[0, 1])) and np.all(np.isnan(yg[1, 0]))
+    assert np.all(np.isfinite(yg[0, 0])) and np.all(np.isfinite(yg[1, 1]))
+
+
+@pytest.mark.parametrize("M", (1, 4, 16))
+def test_moe_ffn_workload(M):
+    """The 128-expert top-8 Q4_0 MoE layer (hidden 2048, expert FFN 768):
+    gate/up with SwiGLU then down with the fixed-order weighted sum."""
+    L = S.MOE_Q4_0
+    ids, rw = S.route_table(L.workload_id, M, L.n_experts, L.top_k)
+    used = ids.ravel()
+    gate = Experts(L.fmt, L.n_experts, L.inter, L.hidden, used, lambda e: L.weight_seed(e, 0))
+    up = Experts(L.fmt, L.n_experts, L.inter, L.hidden, used, lambda e: L.weight_seed(e, 1))
+    down = Experts(L.fmt, L.n_experts, L.hidden, L.inter, used, lambda e: L.weight_seed(e, 2))
+    x = S.activations(L.act_seed_prefix(), L.hidden, M)
+    y = U.empty_dev((M, L.hidden))
+    h = U.empty_dev((M, L.top_k, L.inter), "float16")
+    wsb = kq.kq_moe_ffn_workspace_bytes(L.hidden, L.inter, M, L.top_k)
+    ws = U.empty_dev((wsb // 4 + 1,))
+    kq.kq_moe_ffn(L.fmt, gate.dev, up.dev, down.dev, U.to_dev(x), U.to_dev(ids), U.to_dev(rw), y, h,
+                  L.hidden, L.inter, M, L.top_k, L.n_experts, ws, wsb)
+    yg, hg = U.to_host(y), U.to_host(h)
+    E = L.n_experts
+    # h: the GPU's g and u may differ from the oracle's within the GEMV
+    # tolerance; h may then differ by that error carried through
+    # silu(g)*u, plus one fp16 rounding step (2^-10 relative, 2^-24 absolute).
+    _, _, (g, g_abs), (u, u_abs), h_ref = R.moe_ffn(L.fmt, gate.field_list(E), up.field_list(E),
+                                                   down.field_list(E), x, ids, rw)
+    sig = 1.0 / (1.0 + np.exp(-g))
+    dsilu = sig * (1.0 + g * (1.0 - sig))
+    tol_h = (np.abs(dsilu * u) * R.tolerance(g_abs) + np.abs(g * sig) * R.tolerance(u_abs)
+             + 2.0 ** -10 * np.abs(h_ref.astype(np.float64)) + 2.0 ** -24)
+    assert np.all(np.abs(hg.astype(np.float64) - h_ref.astype(np.float64)) <= tol_h)
+    # down + weighted sum checked on exactly the GPU's h
+    yr, ad, *_ = R.moe_ffn(L.fmt, gate.field_list(E), up.field_list(E), down.field_list(E), x, ids,
+                           rw, h_override=hg)
+    U.assert_parity(yg, yr, ad, f"moe ffn M={M}")
