@@ -56,6 +56,13 @@ def lib() -> ctypes.CDLL:
     """Load libkq.so (raises if it has not been built)."""
     global _lib
     if _lib is None:
+        # PyTorch-ROCm carries its own HIP runtime (same soname as ROCm's). Load
+        # it first so libkq.so binds to that one runtime: two runtimes in one
+        # process do not share devices, streams or allocations.
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is not built; run python -m block_quantized_gemv_kq_amd.build")
         L = ctypes.CDLL(LIB_PATH)

@@ -5,6 +5,12 @@ step is one IEEE fp32 operation); HIP sources with hipcc for gfx950 only, with
 packed-fp32 instructions disabled. Objects go to _build/, the library next to
 this file.
 
+One HIP runtime per process: PyTorch-ROCm ships its own libamdhip64.so with
+the same soname (libamdhip64.so.7) as ROCm's. The binding imports torch before
+it loads libkq.so, so the loader matches this library's dependency to the
+runtime torch already holds, and torch's streams and allocations are valid
+handles here. Without torch in the process the RUNPATH finds ROCm's own.
+
     python -m block_quantized_gemv_kq_amd.build [-v]
 """
 from __future__ import annotations
@@ -62,7 +68,9 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     with ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
     tmp = LIB + ".tmp"
-    _run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp, *objs, "-lpthread"], verbose)
+    _run([shutil.which("g++") or "g++", "-shared", "-fPIC", "-o", tmp, *objs,
+          "-L" + os.path.join(ROCM, "lib"), "-lamdhip64",
+          "-Wl,-rpath," + os.path.join(ROCM, "lib"), "-lpthread"], verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -117,7 +117,8 @@ def moe_gemv(fmt: str, expert_fields, x16: np.ndarray, route_ids: np.ndarray,
     """
     ids = np.asarray(route_ids)
     m_tokens, top_k = ids.shape
-    n = F.rows_of(expert_fields[0])
+    # experts no token is routed to may be absent (None)
+    n = next(F.rows_of(f) for f in expert_fields if f is not None)
     per = np.zeros((m_tokens, top_k, n))
     per_abs = np.zeros((m_tokens, top_k, n))
     for t in range(m_tokens):
