@@ -1,0 +1,359 @@
+"""Benchmark: decode GEMV throughput on one MI355X.
+
+Default workload: the Qwen3-4B-shaped dense stack in affine4 gs32 (36 layers,
+hidden 2560, intermediate 9728, q 4096 x 2560, k/v 1024 x 2560, o 2560 x 4096)
+plus a 151936 x 2560 Q8_0 lm_head and its argmax, at M = 1 (one decode token),
+on seeded synthetic weights. One step = one token through the whole stack:
+per layer the row-concatenated q|k|v GEMV, o, row-concatenated gate|up, down
+(the order a decoder layer consumes them in), then lm_head and argmax. The
+step is captured once as a HIP graph and replayed.
+
+Also measured (extra fields of the same JSON line): the same stack as an
+M = 8 speculative-verify pass (t(8)/t(1)), per-kernel durations from HIP
+events, and the CPU oracle on a bounded sample (2 layers + lm_head) on the
+host cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+GROUP_NAMES = ("qkv", "o", "gate_up", "down")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class DeviceStack:
+    """Packed weights of the stack resident in HBM, activations and outputs."""
+
+    def __init__(self, torch, kq, S, stack, M, act_workload_id=None, layers=None):
+        self.torch, self.kq = torch, kq
+        self.stack = stack
+        self.M = M
+        self.layers = stack.layers if layers is None else layers
+        dev = torch.device("cuda")
+        self.groups = []          # per layer: list of (fmt, W_dev, x_dev, y_dev, N, K, name)
+        self.weight_bytes = 0
+        self.alg_bytes = 0
+        wid = stack.workload_id if act_workload_id is None else act_workload_id
+
+        def build_group(layer, gi, group):
+            mats = [stack.per_layer[i] for i in group]
+            K = mats[0].k
+            fmt = mats[0].fmt
+            N = sum(m.n for m in mats)
+            packed = np.empty((N, kq.kq_packed_bytes(fmt, 1, K)), np.uint8)
+            r0 = 0
+            for i, m in zip(group, mats):
+                W = S.weights(stack.weight_seed(layer, i), m.n, m.k)
+                kq.kq_pack(fmt, W, out=packed[r0:r0 + m.n])
+                r0 += m.n
+            x = S.activations((wid, layer, mats[0].input_slot), K, M)
+            return layer, gi, fmt, packed, x, N, K
+
+        jobs = [(l, gi, g) for l in range(self.layers) for gi, g in enumerate(stack.launch_groups)]
+        per_layer = [[None] * len(stack.launch_groups) for _ in range(self.layers)]
+        with ThreadPoolExecutor(4) as ex:
+            for layer, gi, fmt, packed, x, N, K in ex.map(lambda j: build_group(*j), jobs):
+                Wd = torch.from_numpy(packed).to(dev)
+                xd = torch.from_numpy(x).to(dev)
+                yd = torch.empty((M, N), dtype=torch.float32, device=dev)
+                per_layer[layer][gi] = (fmt, Wd, xd, yd, N, K, GROUP_NAMES[gi])
+                self.weight_bytes += packed.nbytes
+                self.alg_bytes += packed.nbytes + x.nbytes + M * N * 4
+        self.groups = per_layer
+        h = stack.head
+        self.head = None
+        if h is not None:
+            W = S.weights(stack.weight_seed(stack.layers, 0), h.n, h.k)
+            packed = kq.kq_pack(h.fmt, W)
+            del W
+            x = S.activations((wid, stack.layers, 0), h.k, M)
+            Wd = torch.from_numpy(packed).to(dev)
+            yd = torch.empty((M, h.n), dtype=torch.float32, device=dev)
+            wsb = kq.kq_argmax_workspace_bytes(h.n, M)
+            ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+            am = torch.empty(M, dtype=torch.int32, device=dev)
+            self.head = (h.fmt, Wd, torch.from_numpy(x).to(dev), yd, h.n, h.k, ws, wsb, am)
+            self.weight_bytes += packed.nbytes
+            self.alg_bytes += packed.nbytes + x.nbytes + M * h.n * 4 + M * h.n * 4 + M * 4
+
+    def with_columns(self, S, M, act_workload_id):
+        """A view with the same resident weights and M fresh activation columns."""
+        torch = self.torch
+        v = object.__new__(DeviceStack)
+        v.torch, v.kq, v.stack, v.M, v.layers = torch, self.kq, self.stack, M, self.layers
+        v.weight_bytes, v.alg_bytes = self.weight_bytes, 0
+        v.groups = []
+        for layer, row in enumerate(self.groups):
+            new_row = []
+            for gi, (fmt, Wd, _, _, N, K, name) in enumerate(row):
+                slot = self.stack.per_layer[self.stack.launch_groups[gi][0]].input_slot
+                x = S.activations((act_workload_id, layer, slot), K, M)
+                xd = torch.from_numpy(x).to("cuda")
+                yd = torch.empty((M, N), dtype=torch.float32, device="cuda")
+                new_row.append((fmt, Wd, xd, yd, N, K, name))
+                v.alg_bytes += Wd.numel() + x.nbytes + M * N * 4
+            v.groups.append(new_row)
+        v.head = None
+        if self.head is not None:
+            fmt, Wd, _, _, N, K, _, _, _ = self.head
+            x = S.activations((act_workload_id, self.stack.layers, 0), K, M)
+            yd = torch.empty((M, N), dtype=torch.float32, device="cuda")
+            wsb = self.kq.kq_argmax_workspace_bytes(N, M)
+            ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+            am = torch.empty(M, dtype=torch.int32, device="cuda")
+            v.head = (fmt, Wd, torch.from_numpy(x).to("cuda"), yd, N, K, ws, wsb, am)
+            v.alg_bytes += Wd.numel() + x.nbytes + 2 * M * N * 4 + M * 4
+        return v
+
+    def launch_group(self, layer, gi):
+        fmt, Wd, xd, yd, N, K, _ = self.groups[layer][gi]
+        self.kq.kq_gemv(fmt, Wd, xd, yd, N, K, self.M)
+
+    def launch_head(self):
+        fmt, Wd, xd, yd, N, K, ws, wsb, am = self.head
+        self.kq.kq_gemv(fmt, Wd, xd, yd, N, K, self.M)
+        self.kq.kq_argmax(yd, N, self.M, am, ws, wsb)
+
+    def step(self):
+        for layer in range(self.layers):
+            for gi in range(len(self.groups[layer])):
+                self.launch_group(layer, gi)
+        if self.head is not None:
+            self.launch_head()
+
+
+def capture(torch, fn):
+    """Capture fn's launches (on torch's capture stream) as one graph."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()                                   # warm (first-launch setup outside capture)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(torch, g, reps, warmup):
+    """Per-replay times (ms) from events around each replay, plus the total
+    wall time of the `reps` timed replays bracketed by synchronisations."""
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    t0 = time.perf_counter()
+    evs[0].record()
+    for i in range(reps):
+        g.replay()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(reps)])
+    total_ms = evs[0].elapsed_time(evs[reps])
+    return per, total_ms, wall
+
+
+def kernel_table(torch, ds, reps=10):
+    """Average duration of each launch group's GEMV (graph of that group's
+    launches over all layers, timed with events on the replay stream)."""
+    out = {}
+    for gi, name in enumerate(GROUP_NAMES):
+        g = capture(torch, lambda gi=gi: [ds.launch_group(l, gi) for l in range(ds.layers)])
+        per, total_ms, _ = time_graph(torch, g, reps, 2)
+        fmt, Wd, xd, yd, N, K, _ = ds.groups[0][gi]
+        nbytes = Wd.numel() + xd.numel() * 2 + yd.numel() * 4
+        us = float(np.median(per)) * 1000.0 / ds.layers
+        out[name] = {"N": N, "K": K, "fmt": fmt, "launches_per_step": ds.layers,
+                     "us_per_launch": us, "bytes_per_launch": int(nbytes),
+                     "gbps": nbytes / (us * 1e-6) / 1e9}
+        del g
+    if ds.head is not None:
+        fmt, Wd, xd, yd, N, K, ws, wsb, am = ds.head
+        g = capture(torch, lambda: ds.kq.kq_gemv(fmt, Wd, xd, yd, N, K, ds.M))
+        per, _, _ = time_graph(torch, g, reps, 2)
+        nbytes = Wd.numel() + xd.numel() * 2 + yd.numel() * 4
+        us = float(np.median(per)) * 1000.0
+        out["lm_head"] = {"N": N, "K": K, "fmt": fmt, "launches_per_step": 1, "us_per_launch": us,
+                          "bytes_per_launch": int(nbytes), "gbps": nbytes / (us * 1e-6) / 1e9}
+        g = capture(torch, lambda: ds.kq.kq_argmax(yd, N, ds.M, am, ws, wsb))
+        per, _, _ = time_graph(torch, g, reps, 2)
+        us = float(np.median(per)) * 1000.0
+        out["argmax"] = {"N": N, "launches_per_step": 2, "us_per_launch": us / 2,
+                         "bytes_per_launch": int(yd.numel() * 4 // 2),
+                         "gbps": yd.numel() * 4 / (us * 1e-6) / 1e9}
+    return out
+
+
+def cpu_baseline(S, stack, kq, budget_s=15.0):
+    """The oracle as it stands (decode packed bytes, dequantize, fp64 dot) on
+    the host cores, on a bounded sample: the lm_head plus as many layers of
+    the stack as fit in about `budget_s` seconds of oracle work (at least 1),
+    extrapolated to one token; unit GB/s of packed weights."""
+    from oracle import formats as F
+    from oracle import ref as R
+    h = stack.head
+    W = S.weights(stack.weight_seed(stack.layers, 0), h.n, h.k)
+    packed = kq.kq_pack(h.fmt, W)
+    del W
+    x = S.activations((stack.workload_id, stack.layers, 0), h.k, 1)
+    t0 = time.perf_counter()
+    y, _ = R.gemv(h.fmt, F.decode(h.fmt, packed, h.n, h.k), x)
+    R.argmax_lowest(y[0])
+    t_head = time.perf_counter() - t0
+    head_bytes = packed.nbytes
+    del packed
+    t_layers = []
+    bytes_layer = 0
+    for layer in range(stack.layers):
+        t = 0.0
+        bytes_layer = 0
+        for i, m in enumerate(stack.per_layer):
+            W = S.weights(stack.weight_seed(layer, i), m.n, m.k)
+            packed = kq.kq_pack(m.fmt, W)
+            del W
+            x = S.activations((stack.workload_id, layer, m.input_slot), m.k, 1)
+            t0 = time.perf_counter()
+            R.gemv(m.fmt, F.decode(m.fmt, packed, m.n, m.k), x)
+            t += time.perf_counter() - t0
+            bytes_layer += packed.nbytes
+        t_layers.append(t)
+        if t_head + sum(t_layers) >= budget_s:
+            break
+    t_token = float(np.mean(t_layers)) * stack.layers + t_head
+    total_bytes = bytes_layer * stack.layers + head_bytes
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": total_bytes / t_token / 1e9, "unit": "GB/s", "cores": int(blas_threads),
+            "kind": "oracle",
+            "sample": f"{len(t_layers)} of {stack.layers} layers + lm_head + argmax at M=1, "
+                      f"{sum(t_layers) + t_head:.1f} s of oracle work, extrapolated to one token",
+            "s_per_token": t_token, "tokens_per_s": 1.0 / t_token,
+            "host_cpu_count": os.cpu_count()}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-verify", action="store_true", help="skip the M=8 verify measurement")
+    ap.add_argument("--kernels-only", action="store_true",
+                    help="short run for counter collection: per-kernel graphs and a copy of known size")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on one GPU only: the decode GEMV is measured on "
+                          "one MI355X; see the sharding notes in DESIGN.md", "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import block_quantized_gemv_kq_amd as kq
+    from synth import inputs as S
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    kq.lib()
+    stack = S.QWEN3_4B_AFFINE4
+
+    t0 = time.perf_counter()
+    log("packing and uploading the 4B-shaped stack (M=1) ...")
+    ds = DeviceStack(torch, kq, S, stack, 1)
+    log(f"  {ds.weight_bytes / 1e9:.3f} GB of packed weights resident in {time.perf_counter() - t0:.1f} s")
+
+    if args.kernels_only:
+        ktab = kernel_table(torch, ds, reps=5)
+        n = 256 << 20
+        a = torch.empty(n // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)                       # plain copy kernel: 256 MiB read, 256 MiB written
+        torch.cuda.synchronize()
+        print(json.dumps({"kernels": ktab, "copy_bytes_each_way": n}))
+        return
+
+    g = capture(torch, ds.step)
+    per, total_ms, wall = time_graph(torch, g, args.steps, args.warmup)
+    ms_per_step = total_ms / args.steps
+    gbps = ds.alg_bytes / (ms_per_step * 1e-3) / 1e9
+    log(f"M=1 step: {ms_per_step * 1000:.1f} us, {gbps:.0f} GB/s, {1000 / ms_per_step:.0f} tok/s")
+    del g
+
+    ktab = kernel_table(torch, ds)
+    # dominant kernel: the launch group with the largest time per step
+    dom = max(ktab, key=lambda k: ktab[k]["us_per_launch"] * ktab[k]["launches_per_step"])
+    d = ktab[dom]
+    roofline = {"bound": "hbm", "achieved": d["gbps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": d["gbps"] / HBM_PEAK_GBS, "traffic": None,
+                "kernel": f"kq_gemv {dom} ({d['fmt']}, {d['N']}x{d['K']}, M=1)",
+                "us_per_launch": d["us_per_launch"], "bytes_per_launch": d["bytes_per_launch"]}
+
+    verify = None
+    if not args.no_verify:
+        dv = ds.with_columns(S, 8, S.VERIFY_WORKLOAD_ID)
+        gv = capture(torch, dv.step)
+        perv, total_v, _ = time_graph(torch, gv, max(5, args.steps // 2), 3)
+        ms_v = total_v / max(5, args.steps // 2)
+        verify = {"M": 8, "ms_per_pass": ms_v, "gbps": dv.alg_bytes / (ms_v * 1e-3) / 1e9,
+                  "t_ratio_vs_m1": ms_v / ms_per_step,
+                  "tokens_per_s_upper_bound": 8 / (ms_v * 1e-3)}
+        log(f"M=8 pass: {ms_v * 1000:.1f} us, t(8)/t(1) = {ms_v / ms_per_step:.2f}")
+        del gv, dv
+        torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on 2 layers + lm_head ...")
+        cpu = cpu_baseline(S, stack, kq)
+
+    out = {
+        "metric": "achieved HBM GB/s (% of peak) + equiv. decode tokens/s, M=1 and M=8 verify",
+        "value": gbps,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "affine4/q8_0 weights, f16 activations, f32 accumulate",
+        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) fp16 activations)",
+        "config": {"workload": "qwen3_4b_shaped_affine4_stack+q8_0_lm_head, M=1, one decode token",
+                   "layers": stack.layers, "hidden": 2560, "intermediate": 9728, "vocab": 151936,
+                   "global_batch": 1, "seq_len": 1, "parallelism": "none (1 GPU)"},
+        "pct_of_peak": 100.0 * gbps / HBM_PEAK_GBS,
+        "tokens_per_s": 1000.0 / ms_per_step,
+        "step_us_p10_p50_p90": [float(np.percentile(per, q)) * 1000 for q in (10, 50, 90)],
+        "alg_bytes_per_step": ds.alg_bytes,
+        "roofline": roofline,
+        "kernels": ktab,
+        "verify_m8": verify,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -260,4 +260,195 @@ __device__ __forceinline__ void valu_tile(rsrc_t rs, uint32_t row_bytes, int uni
   }
 }
 
+
+// ------------------------------------------------------------------------
+// Latency-bound layout (used for small M): a lane issues the loads of ALL the
+// units it owns before any arithmetic, so a whole tile costs one memory round
+// trip, and the activations are staged once per workgroup in LDS (copied
+// with LDS-DMA loads that need no registers) while those loads are in flight.
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+// Copy n16 16-byte chunks from global `src` to LDS `dst` (both 16-byte
+// aligned). Every thread of the workgroup must call it; follow with
+// __syncthreads() (which waits for the copies).
+__device__ __forceinline__ void stage_to_lds(const void* src, uint32_t* dst, int n16) {
+  for (int i = threadIdx.x; i < n16; i += blockDim.x) {
+    const int wave_first = i - (int)(threadIdx.x & 63);   // lane L lands at wave_first + L
+    __builtin_amdgcn_global_load_lds((glb_void_t*)(reinterpret_cast<const u32x4*>(src) + i),
+                                     (lds_void_t*)(dst + 4 * wave_first), 16, 0, 0);
+  }
+}
+
+// Offset that lies past every buffer's num_records: loads there return 0.
+constexpr uint32_t OOB = 0x80000000u;
+
+template <int FMT, int ITERS>
+struct Loaded {
+  uint32_t D[ITERS][Fmt<FMT>::UDW];
+};
+
+// Issue the loads of units first, first+G, ... (ITERS of them) of the row at
+// byte offset `roff` of `rs`; units at or past `units` read as zero.
+template <int FMT, int ITERS>
+__device__ __forceinline__ void issue_units(rsrc_t rs, uint32_t roff, int first, int G, int units,
+                                            Loaded<FMT, ITERS>& w) {
+  constexpr uint32_t UBYTES = Fmt<FMT>::BB * Fmt<FMT>::UB;
+#pragma unroll
+  for (int it = 0; it < ITERS; ++it) {
+    const int u = first + it * G;
+    const uint32_t off = u < units ? roff + (uint32_t)u * UBYTES : OOB;
+    load_unit<FMT>(rs, off, w.D[it]);
+  }
+}
+
+// Four nibble dwords of one 4-bit block -> 16 fp16 pairs without shifts:
+// low nibbles give 1024 + q (elements 0..15), high nibbles masked in place
+// give 1024 + 16 q (elements 16..31). The 16x is removed in the fix-up.
+__device__ __forceinline__ void unpack_nibbles_split(const uint32_t (&n)[4], uint32_t* A) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const uint32_t lo = n[t] & 0x0F0F0F0Fu;
+    const uint32_t hi = n[t] & 0xF0F0F0F0u;
+    A[2 * t] = perm(MAGIC, lo, SEL_LO);
+    A[2 * t + 1] = perm(MAGIC, lo, SEL_HI);
+    A[8 + 2 * t] = perm(MAGIC, hi, SEL_LO);
+    A[9 + 2 * t] = perm(MAGIC, hi, SEL_HI);
+  }
+}
+
+template <int FMT>
+__device__ __forceinline__ void unpack_unit_split(const uint32_t (&D)[Fmt<FMT>::UDW], Unpacked<FMT>& u) {
+  if constexpr (FMT == F_AFFINE4) {
+    const uint32_t n[4] = {D[1], D[2], D[3], D[4]};
+    unpack_nibbles_split(n, u.A);
+    u.scale[0] = h2f(D[0]);
+    u.bias[0] = h2f(D[0] >> 16);
+  } else if constexpr (FMT == F_Q4_0) {
+    const uint32_t na[4] = {alignbyte2(D[1], D[0]), alignbyte2(D[2], D[1]), alignbyte2(D[3], D[2]),
+                            alignbyte2(D[4], D[3])};
+    const uint32_t nb[4] = {D[5], D[6], D[7], D[8]};
+    unpack_nibbles_split(na, u.A);
+    unpack_nibbles_split(nb, u.A + 16);
+    u.scale[0] = h2f(D[0]);
+    u.scale[1] = h2f(D[4] >> 16);
+    u.bias[0] = u.bias[1] = 0.0f;
+  } else {
+    unpack_unit<FMT>(D, u);
+  }
+}
+
+// One block against 16 activation dwords, with the block's activation sums
+// (elements 0..15 and 16..31) precomputed. Adds the block's dequantized dot
+// product to y.
+template <int FMT>
+__device__ __forceinline__ float block_dot_split(const uint32_t* A, const uint32_t* X, float sx_lo,
+                                                 float sx_hi, float scale, float bias, float y) {
+  if constexpr (FMT == F_Q8_0) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc = dot2(A[i], X[i], acc);
+    const float t = __builtin_fmaf(-1152.0f, sx_lo + sx_hi, acc);   // sum q x
+    return __builtin_fmaf(scale, t, y);
+  } else {
+    float lo = 0.0f, hi = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) lo = dot2(A[i], X[i], lo);
+#pragma unroll
+    for (int i = 8; i < 16; ++i) hi = dot2(A[i], X[i], hi);
+    // Q4_0: sum (q-8) x = (lo - 1032 sx_lo) + (hi - 1152 sx_hi) / 16
+    // affine4: sum q x  = (lo - 1024 sx_lo) + (hi - 1024 sx_hi) / 16
+    const float c_lo = FMT == F_Q4_0 ? -1032.0f : -1024.0f;
+    const float c_hi = FMT == F_Q4_0 ? -1152.0f : -1024.0f;
+    const float t_lo = __builtin_fmaf(c_lo, sx_lo, lo);
+    const float t_hi = __builtin_fmaf(c_hi, sx_hi, hi);
+    y = __builtin_fmaf(scale, t_lo, y);
+    y = __builtin_fmaf(scale * 0.0625f, t_hi, y);
+    if constexpr (FMT == F_AFFINE4) {
+      y = __builtin_fmaf(bias, sx_lo, y);
+      y = __builtin_fmaf(bias, sx_hi, y);
+    }
+    return y;
+  }
+}
+
+// Per-block activation sums for MT columns staged in LDS: for column m and
+// block b, xs[(m * nblk + b) * 2 + {0,1}] = sum of elements 0..15 / 16..31.
+// Every thread of the workgroup takes part; follow with __syncthreads().
+__device__ __forceinline__ void block_sums_to_lds(const uint32_t* xl, int kdw, int mt, float* xs) {
+  const int nblk = kdw / 16;
+  for (int i = threadIdx.x; i < mt * nblk; i += blockDim.x) {
+    const int m = i / nblk, b = i - m * nblk;
+    const u32x4* p = reinterpret_cast<const u32x4*>(xl + m * kdw + b * 16);
+    float lo = 0.0f, hi = 0.0f;
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      const u32x4 t = p[v];
+      lo = dot2(t.x, ONES, lo);
+      lo = dot2(t.y, ONES, lo);
+      lo = dot2(t.z, ONES, lo);
+      lo = dot2(t.w, ONES, lo);
+    }
+#pragma unroll
+    for (int v = 2; v < 4; ++v) {
+      const u32x4 t = p[v];
+      hi = dot2(t.x, ONES, hi);
+      hi = dot2(t.y, ONES, hi);
+      hi = dot2(t.z, ONES, hi);
+      hi = dot2(t.w, ONES, hi);
+    }
+    xs[2 * i] = lo;
+    xs[2 * i + 1] = hi;
+  }
+}
+
+// Consume loaded units against MT activation columns held in LDS (column m
+// at xl + m * kdw dwords) with their per-block sums in xs.
+template <int FMT, int MT, int ITERS>
+__device__ __forceinline__ void consume_units(const Loaded<FMT, ITERS>& w, const uint32_t* xl,
+                                              const float* xs, int kdw, int first, int G, int units,
+                                              float (&acc)[MT]) {
+  constexpr int UB = Fmt<FMT>::UB;
+  const int nblk = kdw / 16;
+#pragma unroll
+  for (int it = 0; it < ITERS; ++it) {
+    const int u = first + it * G;
+    if (u < units) {
+      Unpacked<FMT> up;
+      unpack_unit_split<FMT>(w.D[it], up);
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const u32x4* xp = reinterpret_cast<const u32x4*>(xl + m * kdw + u * 16 * UB);
+        const float2* sp = reinterpret_cast<const float2*>(xs) + m * nblk + u * UB;
+        uint32_t X[16 * UB];
+#pragma unroll
+        for (int v = 0; v < 4 * UB; ++v) {
+          const u32x4 t = xp[v];
+          X[4 * v] = t.x;
+          X[4 * v + 1] = t.y;
+          X[4 * v + 2] = t.z;
+          X[4 * v + 3] = t.w;
+        }
+#pragma unroll
+        for (int b = 0; b < UB; ++b) {
+          const float2 sx = sp[b];
+          acc[m] = block_dot_split<FMT>(up.A + 16 * b, X + 16 * b, sx.x, sx.y, up.scale[b],
+                                        up.bias[b], acc[m]);
+        }
+      }
+    }
+  }
+}
+
+// Sum over the G lanes of a group (butterfly, fixed order: deterministic and
+// every lane of the group ends with the same value).
+template <int MT>
+__device__ __forceinline__ void group_reduce(float (&acc)[MT], int G) {
+  for (int off = 1; off < G; off <<= 1) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[m] += __shfl_xor(acc[m], off, 64);
+  }
+}
+
 }  // namespace kqd

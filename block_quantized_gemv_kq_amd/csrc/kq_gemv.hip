@@ -55,6 +55,55 @@ __global__ __launch_bounds__(256) void k_gemv_valu(const uint8_t* __restrict__ W
   }
 }
 
+// ------------------------------------------- VALU path, loads-first + LDS x
+// One row per lane group (G lanes), 64/G rows per wave. Each lane issues the
+// loads of all ITERS units it owns, the workgroup stages the MT activation
+// columns in LDS meanwhile, and only then does any arithmetic: one memory
+// round trip per tile. `passes` > 1 only when units > G * ITERS.
+template <int FMT, int MT, int ITERS>
+__global__ __launch_bounds__(256) void k_gemv_lds(const uint8_t* __restrict__ W,
+                                                  const uint16_t* __restrict__ x,
+                                                  float* __restrict__ y, int N, int K, int log2g,
+                                                  int m0, int passes) {
+  extern __shared__ u32x4 x_lds4[];
+  uint32_t* xl = reinterpret_cast<uint32_t*>(x_lds4);
+  const int lane = threadIdx.x & 63;
+  const int wave = blockIdx.x * 4 + wave_id();
+  const int G = 1 << log2g;
+  const int rpw = 64 >> log2g;
+  const int64_t row_base = (int64_t)wave * rpw;
+  const uint32_t row_bytes = (uint32_t)(K / 32) * Fmt<FMT>::BB;
+  const int units = K / (32 * Fmt<FMT>::UB);
+  const int valid = row_base < N ? (int)min<int64_t>(rpw, N - row_base) : 0;
+  const rsrc_t rs = make_rsrc(W + (valid ? row_base * row_bytes : 0), (uint32_t)valid * row_bytes);
+  const int rho = lane >> log2g;
+  const int g = lane & (G - 1);
+  const uint32_t roff = (uint32_t)rho * row_bytes;
+  Loaded<FMT, ITERS> w;
+  issue_units<FMT, ITERS>(rs, roff, g, G, units, w);
+  const int kdw = K / 2;
+  float* xs = reinterpret_cast<float*>(xl + MT * kdw);
+#pragma unroll
+  for (int m = 0; m < MT; ++m) stage_to_lds(x + (int64_t)(m0 + m) * K, xl + m * kdw, K / 8);
+  __syncthreads();
+  block_sums_to_lds(xl, kdw, MT, xs);
+  __syncthreads();
+  float acc[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
+  const int span = G * ITERS;
+  for (int p = 0;;) {
+    consume_units<FMT, MT, ITERS>(w, xl, xs, kdw, p * span + g, G, units, acc);
+    if (++p >= passes) break;
+    issue_units<FMT, ITERS>(rs, roff, p * span + g, G, units, w);
+  }
+  group_reduce<MT>(acc, G);
+  if (g == 0 && rho < valid) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m) y[(int64_t)(m0 + m) * N + row_base + rho] = acc[m];
+  }
+}
+
 // -------------------------------------------------------------- generic path
 // One wave per row, one lane per block, 16-bit loads (blocks may be only
 // 2-byte aligned), plain fp32 dequantization. Loops over all M columns.
@@ -191,6 +240,72 @@ int launch_valu(const GemvArgs& a) {
   return 0;
 }
 
+constexpr int LDS_MAX_MT = 4;
+constexpr int LDS_MAX_BYTES = 64 * 1024;
+constexpr int MAX_ITERS = 5;
+
+struct LdsCfg {
+  int log2g;
+  int iters;
+  int passes;
+};
+
+// G (lanes per row, power of two) and ITERS (units per lane per pass): G is
+// the smallest that covers a row in MAX_ITERS units per lane, then doubled
+// while the grid has fewer than 2048 waves (8 per CU) and lanes would still
+// have work, so small matrices spread over more waves.
+LdsCfg lds_cfg(int64_t N, int units) {
+  int G = 1;
+  while (G < 64 && G * MAX_ITERS < units) G <<= 1;
+  while (G < 64 && N * G / 64 < 2048 && G < units) G <<= 1;
+  const int env_g = env_int("KQ_VALU_G");
+  if (env_g == 1 || env_g == 2 || env_g == 4 || env_g == 8 || env_g == 16 || env_g == 32 || env_g == 64) G = env_g;
+  int iters = (units + G - 1) / G;
+  if (iters > MAX_ITERS) iters = MAX_ITERS;
+  const int passes = (units + G * iters - 1) / (G * iters);
+  return {ilog2(G), iters, passes};
+}
+
+template <int FMT, int MT, int ITERS>
+int launch_lds_it(const GemvArgs& a, int m0, LdsCfg c) {
+  const int64_t rpw = 64 >> c.log2g;
+  const int64_t waves = (a.N + rpw - 1) / rpw;
+  const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
+  const size_t lds = (size_t)MT * a.K * 2 + (size_t)MT * (a.K / 32) * 8;  // x + block sums
+  hipLaunchKernelGGL((k_gemv_lds<FMT, MT, ITERS>), grid, block, lds, a.stream, a.W, a.x, a.y, (int)a.N,
+                     (int)a.K, c.log2g, m0, c.passes);
+  return (int)hipGetLastError();
+}
+
+template <int FMT, int MT>
+int launch_lds_mt(const GemvArgs& a, int m0, LdsCfg c) {
+  switch (c.iters) {
+    case 1: return launch_lds_it<FMT, MT, 1>(a, m0, c);
+    case 2: return launch_lds_it<FMT, MT, 2>(a, m0, c);
+    case 3: return launch_lds_it<FMT, MT, 3>(a, m0, c);
+    case 4: return launch_lds_it<FMT, MT, 4>(a, m0, c);
+    default: return launch_lds_it<FMT, MT, 5>(a, m0, c);
+  }
+}
+
+template <int FMT>
+int launch_lds(const GemvArgs& a) {
+  const int units = (int)(a.K / (32 * Fmt<FMT>::UB));
+  const LdsCfg c = lds_cfg(a.N, units);
+  for (int m0 = 0; m0 < a.M; m0 += LDS_MAX_MT) {
+    const int mt = a.M - m0 < LDS_MAX_MT ? a.M - m0 : LDS_MAX_MT;
+    int err;
+    switch (mt) {
+      case 1: err = launch_lds_mt<FMT, 1>(a, m0, c); break;
+      case 2: err = launch_lds_mt<FMT, 2>(a, m0, c); break;
+      case 3: err = launch_lds_mt<FMT, 3>(a, m0, c); break;
+      default: err = launch_lds_mt<FMT, 4>(a, m0, c); break;
+    }
+    if (err) return err;
+  }
+  return 0;
+}
+
 template <int FMT>
 int launch_generic(const GemvArgs& a) {
   const dim3 grid((unsigned)((a.N + 3) / 4)), block(256);
@@ -203,6 +318,10 @@ int dispatch(const GemvArgs& a) {
   if (a.K % (32 * Fmt<FMT>::UB) != 0) return launch_generic<FMT>(a);
   const char* force = getenv("KQ_FORCE_PATH");  // tests: run a given path at any shape
   if (force && force[0] == 'g') return launch_generic<FMT>(a);
+  const bool lds_fits = (int64_t)(a.M < LDS_MAX_MT ? a.M : LDS_MAX_MT) * (a.K * 2 + a.K / 4) <= LDS_MAX_BYTES;
+  if (force && force[0] == 'v') return launch_valu<FMT>(a);     // register-x VALU kernel
+  if (force && force[0] == 'l' && lds_fits) return launch_lds<FMT>(a);
+  if (a.M <= LDS_MAX_MT && lds_fits) return launch_lds<FMT>(a);
   return launch_valu<FMT>(a);
 }
 

@@ -53,7 +53,7 @@ __device__ __forceinline__ Best block_best(Best b, Best* s_red) {
   return s_red[0];
 }
 
-constexpr int ARGMAX_CHUNK = 16384;
+constexpr int ARGMAX_CHUNK = 2048;  // 8 values per thread: many workgroups per column
 
 __global__ __launch_bounds__(256) void k_argmax_partial(const float* __restrict__ y, int64_t N,
                                                         Best* __restrict__ part, int nparts) {

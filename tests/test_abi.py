@@ -127,7 +127,7 @@ def test_moe_ffn_validation():
 def test_argmax_validation():
     L = kq.lib()
     need = kq.kq_argmax_workspace_bytes(151936, 3)
-    assert need == 3 * ((151936 + 16383) // 16384) * 8
+    assert need == 3 * ((151936 + 2047) // 2048) * 8
     assert L.kq_argmax(A16, 0, 1, A16, A16, need, 0) == kq.KQ_ERR_ARG
     assert L.kq_argmax(A16, 151936, 65, A16, A16, need, 0) == kq.KQ_ERR_ARG
     assert L.kq_argmax(A16, 151936, 3, A16, A16, need - 8, 0) == kq.KQ_ERR_ARG
