@@ -132,11 +132,35 @@ class DeviceStack:
         self.kq.kq_argmax(yd, N, self.M, am, ws, wsb)
 
     def step(self):
+        """One token as separate launches: 4 GEMVs per layer, lm_head, argmax."""
         for layer in range(self.layers):
             for gi in range(len(self.groups[layer])):
                 self.launch_group(layer, gi)
         if self.head is not None:
             self.launch_head()
+
+    def make_plan(self):
+        """The whole chain (every layer's GEMVs, then the lm_head) as one
+        persistent-kernel plan (kq_stack_plan); M must be 1."""
+        torch, kq = self.torch, self.kq
+        stages = []
+        for row in self.groups:
+            for fmt, Wd, xd, yd, N, K, _ in row:
+                stages.append(dict(fmt=fmt, W=Wd, x=xd, y=yd, N=N, K=K))
+        if self.head is not None:
+            fmt, Wd, xd, yd, N, K, _, _, _ = self.head
+            stages.append(dict(fmt=fmt, W=Wd, x=xd, y=yd, N=N, K=K))
+        nb = kq.kq_stack_plan_bytes(len(stages))
+        self.plan = torch.zeros(nb, dtype=torch.uint8, device="cuda")
+        self.info = kq.kq_stack_plan(stages, self.plan, nb)
+        self.n_stages = len(stages)
+
+    def step_stacked(self):
+        """One token in one persistent launch, then the argmax."""
+        self.kq.kq_stack_run(self.plan, self.info)
+        if self.head is not None:
+            fmt, Wd, xd, yd, N, K, ws, wsb, am = self.head
+            self.kq.kq_argmax(yd, N, self.M, am, ws, wsb)
 
 
 def capture(torch, fn):
@@ -293,11 +317,23 @@ def main():
         print(json.dumps({"kernels": ktab, "copy_bytes_each_way": n}))
         return
 
+    # per-launch path: every GEMV its own kernel, the step replayed as a graph
     g = capture(torch, ds.step)
+    per_l, total_l, _ = time_graph(torch, g, args.steps, args.warmup)
+    ms_launches = total_l / args.steps
+    log(f"M=1 step as {ds.layers * 4 + 3} launches: {ms_launches * 1000:.1f} us")
+    del g
+    # headline path: the chain in one persistent launch (+ argmax), as a graph
+    ds.make_plan()
+    g = capture(torch, ds.step_stacked)
     per, total_ms, wall = time_graph(torch, g, args.steps, args.warmup)
+    err = kq.kq_stack_status(ds.plan, ds.info)
+    if err:
+        raise SystemExit(f"persistent stack reported a barrier timeout (error word {err})")
     ms_per_step = total_ms / args.steps
     gbps = ds.alg_bytes / (ms_per_step * 1e-3) / 1e9
-    log(f"M=1 step: {ms_per_step * 1000:.1f} us, {gbps:.0f} GB/s, {1000 / ms_per_step:.0f} tok/s")
+    log(f"M=1 step, one persistent launch: {ms_per_step * 1000:.1f} us, {gbps:.0f} GB/s, "
+        f"{1000 / ms_per_step:.0f} tok/s")
     del g
 
     ktab = kernel_table(torch, ds)
@@ -346,6 +382,9 @@ def main():
         "pct_of_peak": 100.0 * gbps / HBM_PEAK_GBS,
         "tokens_per_s": 1000.0 / ms_per_step,
         "step_us_p10_p50_p90": [float(np.percentile(per, q)) * 1000 for q in (10, 50, 90)],
+        "path": f"kq_stack_run: {ds.n_stages} dependent GEMV stages in one persistent launch, then kq_argmax",
+        "per_launch_path": {"ms_per_step": ms_launches, "gbps": ds.alg_bytes / (ms_launches * 1e-3) / 1e9,
+                            "launches_per_step": ds.layers * 4 + 3},
         "alg_bytes_per_step": ds.alg_bytes,
         "roofline": roofline,
         "kernels": ktab,

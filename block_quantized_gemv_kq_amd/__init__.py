@@ -40,7 +40,23 @@ SIGNATURES = {
     "kq_argmax_workspace_bytes": (_I64, [_I64, _I32]),
     "kq_argmax": (_I32, [_P, _I64, _I32, _P, _P, _I64, _P]),
     "kq_f32_to_f16": (_I32, [_P, _P, _I64]),
+    "kq_stack_plan_bytes": (_I64, [_I32]),
+    "kq_stack_plan": (_I32, [_P, _I32, _P, _I64, _P, _P]),
+    "kq_stack_run": (_I32, [_P, _P, _P]),
+    "kq_stack_status": (_I32, [_P, _P, _P, _P]),
 }
+
+
+class kq_stage(ctypes.Structure):
+    """Mirror of the C struct kq_stage (include/kq.h)."""
+    _fields_ = [("fmt", ctypes.c_int32), ("reserved", ctypes.c_int32), ("W", ctypes.c_void_p),
+                ("x", ctypes.c_void_p), ("y", ctypes.c_void_p), ("N", ctypes.c_int64),
+                ("K", ctypes.c_int64), ("y16", ctypes.c_void_p)]
+
+
+class kq_stack_info(ctypes.Structure):
+    _fields_ = [("n_stages", ctypes.c_int32), ("fmt_mask", ctypes.c_int32), ("k_max", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 class KQError(RuntimeError):
@@ -201,3 +217,37 @@ def kq_argmax_workspace_bytes(N: int, M: int) -> int:
 def kq_argmax(y, N: int, M: int, out, workspace, workspace_bytes: int, stream=None) -> None:
     _check(lib().kq_argmax(_ptr(y), N, M, _ptr(out), _ptr(workspace), workspace_bytes, _stream(stream)),
            "kq_argmax")
+
+
+def kq_stack_plan_bytes(n_stages: int) -> int:
+    return _check(lib().kq_stack_plan_bytes(n_stages), "kq_stack_plan_bytes")
+
+
+def kq_stack_plan(stages, plan, plan_bytes: int, stream=None) -> kq_stack_info:
+    """stages: list of dicts with fmt, W, x, y, N, K and optional y16 (device
+    tensors or addresses). Returns the filled kq_stack_info."""
+    arr = (kq_stage * len(stages))()
+    for i, st in enumerate(stages):
+        arr[i].fmt = _fmt(st["fmt"])
+        arr[i].reserved = 0
+        arr[i].W = _ptr(st["W"])
+        arr[i].x = _ptr(st["x"])
+        arr[i].y = _ptr(st["y"])
+        arr[i].N = int(st["N"])
+        arr[i].K = int(st["K"])
+        arr[i].y16 = _ptr(st.get("y16"))
+    info = kq_stack_info()
+    _check(lib().kq_stack_plan(ctypes.cast(arr, ctypes.c_void_p), len(stages), _ptr(plan), plan_bytes,
+                               ctypes.addressof(info), _stream(stream)), "kq_stack_plan")
+    return info
+
+
+def kq_stack_run(plan, info: kq_stack_info, stream=None) -> None:
+    _check(lib().kq_stack_run(_ptr(plan), ctypes.addressof(info), _stream(stream)), "kq_stack_run")
+
+
+def kq_stack_status(plan, info: kq_stack_info, stream=None) -> int:
+    err = ctypes.c_int(0)
+    _check(lib().kq_stack_status(_ptr(plan), ctypes.addressof(info), ctypes.addressof(err),
+                                 _stream(stream)), "kq_stack_status")
+    return err.value

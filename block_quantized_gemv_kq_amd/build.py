@@ -30,7 +30,7 @@ HIPCC = os.path.join(ROCM, "bin", "hipcc")
 ARCH = "gfx950"
 
 HOST_SOURCES = ["kq_api.cpp", "kq_pack.cpp"]
-HIP_SOURCES = ["kq_gemv.hip", "kq_mfma.hip", "kq_moe.hip", "kq_misc.hip"]
+HIP_SOURCES = ["kq_gemv.hip", "kq_mfma.hip", "kq_moe.hip", "kq_misc.hip", "kq_stack.hip"]
 
 HOST_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-ffp-contract=off", "-Wall", "-Wextra",
               "-Wno-unused-parameter"]

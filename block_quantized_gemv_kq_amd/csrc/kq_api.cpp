@@ -4,6 +4,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <vector>
+
 #include "kq_internal.h"
 
 namespace {
@@ -205,6 +207,110 @@ int kq_moe_ffn(int fmt, const void* W_gate, const void* W_up, const void* W_down
   }
   if (!err) err = kq::launch_weighted_slot_sum(slots, route_w, y, hidden, M, top_k, s);
   return hip_status(err, "kq_moe_ffn");
+}
+
+static int64_t stack_descs_bytes(int n) {
+  return ((int64_t)n * (int64_t)sizeof(kq::StackStage) + 255) / 256 * 256;
+}
+
+int64_t kq_stack_plan_bytes(int n_stages) {
+  if (n_stages < 1 || n_stages > KQ_STACK_MAX_STAGES)
+    return fail(KQ_ERR_ARG, "n_stages=%d must be in [1, %d]", n_stages, KQ_STACK_MAX_STAGES);
+  return stack_descs_bytes(n_stages) + (kq::stack_sync_words(n_stages) * 4 + 255) / 256 * 256;
+}
+
+int kq_stack_plan(const kq_stage* stages, int n_stages, void* plan, int64_t plan_bytes,
+                  kq_stack_info* info, void* stream) {
+  const int64_t need = kq_stack_plan_bytes(n_stages);
+  if (need < 0) return (int)need;
+  if (!stages || !plan || !info) return fail(KQ_ERR_ARG, "kq_stack_plan: null pointer");
+  if (plan_bytes < need) return fail(KQ_ERR_ARG, "kq_stack_plan: plan of %lld bytes needed", (long long)need);
+  if (!aligned(plan, 256)) return fail(KQ_ERR_ALIGN, "kq_stack_plan: plan must be 256-byte aligned");
+  // all argument checks first (no HIP call before they pass)
+  for (int i = 0; i < n_stages; ++i) {
+    const kq_stage& s = stages[i];
+    int st = check_fmt_k(s.fmt, s.K);
+    if (st) return fail(st, "stage %d: %s", i, kq_last_error());
+    if (s.reserved != 0) return fail(KQ_ERR_ARG, "stage %d: reserved must be 0", i);
+    if (s.N < 1 || s.N > KQ_MAX_N) return fail(KQ_ERR_ARG, "stage %d: N=%lld out of range", i, (long long)s.N);
+    if (!s.W || !s.x || !s.y) return fail(KQ_ERR_ARG, "stage %d: null pointer", i);
+    if (!aligned(s.W, 4) || !aligned(s.y, 4) || !aligned(s.x, 16) || (s.y16 && !aligned(s.y16, 2)))
+      return fail(KQ_ERR_ALIGN, "stage %d: W, y need 4-byte, x 16-byte, y16 2-byte alignment", i);
+    const int ub = s.fmt == KQ_AFFINE4_G32 ? 1 : 2;
+    if (s.K % (32 * ub) != 0) return fail(KQ_ERR_SHAPE, "stage %d: K must be a multiple of %d", i, 32 * ub);
+    if (s.K / (32 * ub) > 64 * kq::stack_iters(s.fmt))
+      return fail(KQ_ERR_SHAPE, "stage %d: K=%lld too long for the stacked kernel", i, (long long)s.K);
+  }
+  int cus = 0;
+  int err = kq::stack_device_info(&cus);
+  if (err) return hip_status(err, "kq_stack_plan");
+  const int target_tiles = cus;      // one workgroup per CU
+  const int waves = kq::stack_waves();
+  std::vector<kq::StackStage> d((size_t)n_stages);
+  int fmask = 0, kmax = 0;
+  for (int i = 0; i < n_stages; ++i) {
+    const kq_stage& s = stages[i];
+    const int ub = s.fmt == KQ_AFFINE4_G32 ? 1 : 2;
+    const int units = (int)(s.K / (32 * ub));
+    const int iters = kq::stack_iters(s.fmt);
+    int G = 1;
+    while (G * iters < units) G <<= 1;
+    for (;;) {   // more, smaller tiles while the stage has fewer than one per CU
+      const int64_t rows = waves * (64 / G);
+      if (G >= 64 || G >= units || (s.N + rows - 1) / rows >= target_tiles) break;
+      G <<= 1;
+    }
+    const int64_t tile_rows = waves * (64 / G);
+    kq::StackStage& o = d[(size_t)i];
+    o.W = static_cast<const uint8_t*>(s.W);
+    o.x = s.x;
+    o.y = s.y;
+    o.y16 = s.y16;
+    o.N = s.N;
+    o.K = (int32_t)s.K;
+    o.fmt = s.fmt;
+    o.block_bytes = (int32_t)kq::block_bytes(s.fmt);
+    int l = 0;
+    while ((1 << (l + 1)) <= G) ++l;
+    o.log2g = l;
+    o.tiles = (int32_t)((s.N + tile_rows - 1) / tile_rows);
+    o.units = units;
+    fmask |= 1 << s.fmt;
+    if (s.K > kmax) kmax = (int)s.K;
+  }
+  const int64_t dbytes = stack_descs_bytes(n_stages);
+  std::vector<uint8_t> host((size_t)need, 0);
+  memcpy(host.data(), d.data(), d.size() * sizeof(kq::StackStage));
+  err = kq::copy_to_device(plan, host.data(), need, static_cast<hipStream_t>(stream));
+  if (err) return hip_status(err, "kq_stack_plan");
+  info->n_stages = n_stages;
+  info->fmt_mask = fmask;
+  info->k_max = kmax;
+  info->reserved = (int32_t)(dbytes / 4);   // offset of the counters, in words
+  return ok();
+}
+
+int kq_stack_run(const void* plan, const kq_stack_info* info, void* stream) {
+  if (!plan || !info) return fail(KQ_ERR_ARG, "kq_stack_run: null pointer");
+  if (info->n_stages < 1 || info->n_stages > KQ_STACK_MAX_STAGES || info->fmt_mask < 1 ||
+      info->fmt_mask > 7 || info->k_max < 32 || info->reserved * 4 != stack_descs_bytes(info->n_stages))
+    return fail(KQ_ERR_ARG, "kq_stack_run: info was not filled by kq_stack_plan");
+  const kq::StackStage* st = static_cast<const kq::StackStage*>(plan);
+  uint32_t* sync = reinterpret_cast<uint32_t*>(const_cast<void*>(plan)) + info->reserved;
+  return hip_status(kq::launch_stack(st, info->n_stages, sync, info->fmt_mask, info->k_max,
+                                     static_cast<hipStream_t>(stream)),
+                    "kq_stack_run");
+}
+
+int kq_stack_status(const void* plan, const kq_stack_info* info, int* error, void* stream) {
+  if (!plan || !info || !error) return fail(KQ_ERR_ARG, "kq_stack_status: null pointer");
+  const uint32_t* sync = reinterpret_cast<const uint32_t*>(plan) + info->reserved;
+  uint32_t word = 0;
+  int err = kq::read_from_device(&word, sync + kq::stack_error_word(info->n_stages), 4,
+                                 static_cast<hipStream_t>(stream));
+  if (err) return hip_status(err, "kq_stack_status");
+  *error = (int)word;
+  return ok();
 }
 
 int64_t kq_argmax_workspace_bytes(int64_t N, int M) {

@@ -68,6 +68,30 @@ int launch_moe_gate_up_swiglu(const MoeGateUpArgs& a);
 int launch_weighted_slot_sum(const float* ys, const float* w, float* y, int64_t N, int M,
                              int top_k, hipStream_t stream);
 
+// One stage of a persistent GEMV chain (M = 1), as the kernel reads it.
+struct StackStage {
+  const uint8_t* W;
+  const uint16_t* x;
+  float* y;
+  uint16_t* y16;   // optional fp16 copy of y
+  int64_t N;
+  int32_t K;
+  int32_t fmt;
+  int32_t block_bytes;
+  int32_t log2g;   // lanes per row = 2^log2g; a tile is waves * (64 >> log2g) rows
+  int32_t tiles;
+  int32_t units;   // load units per row (1 block for affine4, 2 for Q4_0/Q8_0)
+};
+int stack_iters(int fmt);
+int stack_waves();
+int64_t stack_sync_words(int n_stages);
+int64_t stack_error_word(int n_stages);
+int launch_stack(const StackStage* stages, int n_stages, uint32_t* sync, int fmask, int kmax,
+                 hipStream_t stream);
+int stack_device_info(int* cus);
+int copy_to_device(void* dst, const void* src, int64_t bytes, hipStream_t stream);
+int read_from_device(void* dst, const void* src, int64_t bytes, hipStream_t stream);
+
 int64_t argmax_partials(int64_t N);
 int launch_argmax(const float* y, int64_t N, int M, int32_t* out, void* ws, hipStream_t stream);
 

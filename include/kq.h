@@ -180,6 +180,63 @@ int64_t kq_argmax_workspace_bytes(int64_t N, int M);
 int kq_argmax(const float* y, int64_t N, int M, int32_t* out,
               void* workspace, int64_t workspace_bytes, void* stream);
 
+/* ---- A chain of dependent M = 1 GEMVs in one persistent launch ----------
+ * Kinetic docs, "What makes it fast": a decode step is hundreds of small GPU
+ * kernels, recorded once and replayed with one call per token. kq_stack_run
+ * goes further: the whole chain (e.g. every projection of every layer of a
+ * dense model, then its output layer) is ONE kernel launch. Stage s reads its
+ * activations only after every output row of stage s-1 is written (so
+ * stages[s].x may be stages[s-1].y16), while its weights are already being
+ * loaded: weights never depend on activations. */
+typedef struct kq_stage {
+  int32_t fmt;          /* kq_format */
+  int32_t reserved;     /* must be 0 */
+  const void* W;        /* device, packed N x K (kq_pack layout), 4-byte aligned */
+  const uint16_t* x;    /* device, fp16 bits [K], 16-byte aligned */
+  float* y;             /* device, fp32 [N], 4-byte aligned; overwritten */
+  int64_t N;            /* 1 <= N < 2^31 */
+  int64_t K;            /* multiple of 32 (of 64 for Q8_0/Q4_0); K/32 <= 320 for
+                           affine4, K/64 <= 320 for Q4_0, K/64 <= 128 for Q8_0 */
+  uint16_t* y16;        /* device or NULL: also store fp16(y) (round to nearest
+                           even), 2-byte aligned, so a later stage can read it as x */
+} kq_stage;
+
+/* Filled by kq_stack_plan, passed to kq_stack_run (host memory). */
+typedef struct kq_stack_info {
+  int32_t n_stages;
+  int32_t fmt_mask;
+  int32_t k_max;
+  int32_t reserved;
+} kq_stack_info;
+
+#define KQ_STACK_MAX_STAGES 4096
+
+/* Device bytes of a plan for n_stages stages. */
+int64_t kq_stack_plan_bytes(int n_stages);
+
+/* kq_stack_plan — validate `stages` (host array of n_stages) and write the
+ * device-side plan (`plan`: device, kq_stack_plan_bytes bytes, 256-byte
+ * aligned) plus `info` (host). Copies over `stream` and synchronises it: call
+ * it once at set-up, not inside graph capture. The plan stays valid while the
+ * buffers it names do. Errors: KQ_ERR_ARG, KQ_ERR_FORMAT, KQ_ERR_SHAPE,
+ * KQ_ERR_ALIGN, KQ_ERR_HIP. */
+int kq_stack_plan(const kq_stage* stages, int n_stages, void* plan, int64_t plan_bytes,
+                  kq_stack_info* info, void* stream);
+
+/* kq_stack_run — run every stage of a plan, in order, in one launch on
+ * `stream` (asynchronous; may be captured in a graph). Results are
+ * deterministic run to run, bit for bit, and each output is within the
+ * kq_gemv tolerance of the exact value. Runs on one plan must not
+ * overlap in time (they share its counters). The grid (one workgroup per CU)
+ * waits on itself; a wait that exceeds its spin limit counts in the plan's
+ * error word (kq_stack_status; sticky until the next kq_stack_plan) and lets
+ * the launch finish instead of hanging. */
+int kq_stack_run(const void* plan, const kq_stack_info* info, void* stream);
+
+/* kq_stack_status — synchronise `stream`, then read the plan's error word
+ * into *error (0: every wait completed). */
+int kq_stack_status(const void* plan, const kq_stack_info* info, int* error, void* stream);
+
 /* Test hook: convert n fp32 values (host) to fp16 bits (host) with the
  * packer's own round-to-nearest-even conversion. */
 int kq_f32_to_f16(const float* in, uint16_t* out, int64_t n);

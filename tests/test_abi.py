@@ -152,3 +152,36 @@ def test_pack_validation():
     assert e.value.status == kq.KQ_ERR_RANGE
     assert kq.lib().kq_pack(0, None, 1, 32, None, 1) == kq.KQ_ERR_ARG
     assert kq.lib().kq_pack(0, None, 0, 32, None, 1) == kq.KQ_OK
+
+
+def test_stack_validation():
+    L = kq.lib()
+    assert L.kq_stack_plan_bytes(0) == kq.KQ_ERR_ARG
+    assert L.kq_stack_plan_bytes(4097) == kq.KQ_ERR_ARG
+    nb = kq.kq_stack_plan_bytes(3)
+    assert nb >= 3 * 64
+
+    def plan(**over):
+        st = dict(fmt="affine4", W=A16, x=A16, y=A16, N=64, K=2560)
+        st.update(over)
+        arr = (kq.kq_stage * 1)()
+        arr[0].fmt = kq._fmt(st["fmt"])
+        arr[0].reserved = st.get("reserved", 0)
+        arr[0].W, arr[0].x, arr[0].y = st["W"], st["x"], st["y"]
+        arr[0].N, arr[0].K = st["N"], st["K"]
+        arr[0].y16 = st.get("y16")
+        info = kq.kq_stack_info()
+        return L.kq_stack_plan(ctypes.cast(arr, ctypes.c_void_p), 1, 0x100000, nb,
+                               ctypes.addressof(info), 0)
+    assert plan(fmt=9) == kq.KQ_ERR_FORMAT
+    assert plan(K=48) == kq.KQ_ERR_SHAPE
+    assert plan(fmt="q8_0", K=96) == kq.KQ_ERR_SHAPE            # Q8_0 needs K % 64 == 0
+    assert plan(K=32 * 321) == kq.KQ_ERR_SHAPE                   # too long for one pass
+    assert plan(fmt="q8_0", K=64 * 129) == kq.KQ_ERR_SHAPE
+    assert plan(N=0) == kq.KQ_ERR_ARG
+    assert plan(W=None) == kq.KQ_ERR_ARG
+    assert plan(reserved=1) == kq.KQ_ERR_ARG
+    assert plan(x=A4) == kq.KQ_ERR_ALIGN
+    assert plan(y16=A16 + 1) == kq.KQ_ERR_ALIGN
+    info = kq.kq_stack_info()
+    assert L.kq_stack_run(0x100000, ctypes.addressof(info), 0) == kq.KQ_ERR_ARG   # info not filled
