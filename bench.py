@@ -140,27 +140,23 @@ class DeviceStack:
             self.launch_head()
 
     def make_plan(self):
-        """The whole chain (every layer's GEMVs, then the lm_head) as one
-        persistent-kernel plan (kq_stack_plan); M must be 1."""
+        """Every layer's GEMVs as one persistent-kernel plan (kq_stack_plan);
+        the lm_head, one large GEMV, runs as its own launch after it. M = 1."""
         torch, kq = self.torch, self.kq
         stages = []
         for row in self.groups:
             for fmt, Wd, xd, yd, N, K, _ in row:
                 stages.append(dict(fmt=fmt, W=Wd, x=xd, y=yd, N=N, K=K))
-        if self.head is not None:
-            fmt, Wd, xd, yd, N, K, _, _, _ = self.head
-            stages.append(dict(fmt=fmt, W=Wd, x=xd, y=yd, N=N, K=K))
         nb = kq.kq_stack_plan_bytes(len(stages))
         self.plan = torch.zeros(nb, dtype=torch.uint8, device="cuda")
         self.info = kq.kq_stack_plan(stages, self.plan, nb)
         self.n_stages = len(stages)
 
     def step_stacked(self):
-        """One token in one persistent launch, then the argmax."""
+        """One token: all layers in one persistent launch, then lm_head and argmax."""
         self.kq.kq_stack_run(self.plan, self.info)
         if self.head is not None:
-            fmt, Wd, xd, yd, N, K, ws, wsb, am = self.head
-            self.kq.kq_argmax(yd, N, self.M, am, ws, wsb)
+            self.launch_head()
 
 
 def capture(torch, fn):
@@ -382,7 +378,8 @@ def main():
         "pct_of_peak": 100.0 * gbps / HBM_PEAK_GBS,
         "tokens_per_s": 1000.0 / ms_per_step,
         "step_us_p10_p50_p90": [float(np.percentile(per, q)) * 1000 for q in (10, 50, 90)],
-        "path": f"kq_stack_run: {ds.n_stages} dependent GEMV stages in one persistent launch, then kq_argmax",
+        "path": f"kq_stack_run: {ds.n_stages} dependent GEMV stages in one persistent launch, "
+                "then the lm_head (kq_gemv) and kq_argmax",
         "per_launch_path": {"ms_per_step": ms_launches, "gbps": ds.alg_bytes / (ms_launches * 1e-3) / 1e9,
                             "launches_per_step": ds.layers * 4 + 3},
         "alg_bytes_per_step": ds.alg_bytes,

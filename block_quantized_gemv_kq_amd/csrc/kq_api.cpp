@@ -244,23 +244,25 @@ int kq_stack_plan(const kq_stage* stages, int n_stages, void* plan, int64_t plan
   int cus = 0;
   int err = kq::stack_device_info(&cus);
   if (err) return hip_status(err, "kq_stack_plan");
-  const int target_tiles = cus;      // one workgroup per CU
-  const int waves = kq::stack_waves();
-  std::vector<kq::StackStage> d((size_t)n_stages);
   int fmask = 0, kmax = 0;
+  for (int i = 0; i < n_stages; ++i) {
+    fmask |= 1 << stages[i].fmt;
+    if (stages[i].K > kmax) kmax = (int)stages[i].K;
+  }
+  const int waves = kq::stack_waves(fmask);
+  std::vector<kq::StackStage> d((size_t)n_stages);
   for (int i = 0; i < n_stages; ++i) {
     const kq_stage& s = stages[i];
     const int ub = s.fmt == KQ_AFFINE4_G32 ? 1 : 2;
     const int units = (int)(s.K / (32 * ub));
     const int iters = kq::stack_iters(s.fmt);
+    // G: at least enough lanes to cover a row in `iters` units each; more
+    // (fewer rows per wave) while one round of all waves still covers the
+    // workgroup's share of rows, so every wave has work.
     int G = 1;
     while (G * iters < units) G <<= 1;
-    for (;;) {   // more, smaller tiles while the stage has fewer than one per CU
-      const int64_t rows = waves * (64 / G);
-      if (G >= 64 || G >= units || (s.N + rows - 1) / rows >= target_tiles) break;
-      G <<= 1;
-    }
-    const int64_t tile_rows = waves * (64 / G);
+    const int64_t share = (s.N + cus - 1) / cus;
+    while (G < 64 && G < units && (int64_t)waves * (64 / (2 * G)) >= share) G <<= 1;
     kq::StackStage& o = d[(size_t)i];
     o.W = static_cast<const uint8_t*>(s.W);
     o.x = s.x;
@@ -273,10 +275,8 @@ int kq_stack_plan(const kq_stage* stages, int n_stages, void* plan, int64_t plan
     int l = 0;
     while ((1 << (l + 1)) <= G) ++l;
     o.log2g = l;
-    o.tiles = (int32_t)((s.N + tile_rows - 1) / tile_rows);
+    o.tiles = 0;
     o.units = units;
-    fmask |= 1 << s.fmt;
-    if (s.K > kmax) kmax = (int)s.K;
   }
   const int64_t dbytes = stack_descs_bytes(n_stages);
   std::vector<uint8_t> host((size_t)need, 0);

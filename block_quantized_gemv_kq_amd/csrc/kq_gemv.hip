@@ -241,6 +241,7 @@ int launch_valu(const GemvArgs& a) {
 }
 
 constexpr int LDS_MAX_MT = 4;
+constexpr int MFMA_MIN_M = 2;   // from 2 columns on, products go to the matrix cores
 constexpr int LDS_MAX_BYTES = 64 * 1024;
 constexpr int MAX_ITERS = 5;
 
@@ -315,12 +316,14 @@ int launch_generic(const GemvArgs& a) {
 
 template <int FMT>
 int dispatch(const GemvArgs& a) {
-  if (a.K % (32 * Fmt<FMT>::UB) != 0) return launch_generic<FMT>(a);
+  if (a.K % (32 * Fmt<FMT>::UB) != 0) return a.M >= MFMA_MIN_M ? launch_gemv_mfma(a) : launch_generic<FMT>(a);
   const char* force = getenv("KQ_FORCE_PATH");  // tests: run a given path at any shape
   if (force && force[0] == 'g') return launch_generic<FMT>(a);
   const bool lds_fits = (int64_t)(a.M < LDS_MAX_MT ? a.M : LDS_MAX_MT) * (a.K * 2 + a.K / 4) <= LDS_MAX_BYTES;
   if (force && force[0] == 'v') return launch_valu<FMT>(a);     // register-x VALU kernel
   if (force && force[0] == 'l' && lds_fits) return launch_lds<FMT>(a);
+  if (force && force[0] == 'm') return launch_gemv_mfma(a);
+  if (a.M >= MFMA_MIN_M) return launch_gemv_mfma(a);
   if (a.M <= LDS_MAX_MT && lds_fits) return launch_lds<FMT>(a);
   return launch_valu<FMT>(a);
 }

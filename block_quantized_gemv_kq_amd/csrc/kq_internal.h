@@ -31,6 +31,7 @@ struct GemvArgs {
   hipStream_t stream;
 };
 int launch_gemv(const GemvArgs& a);
+int launch_gemv_mfma(const GemvArgs& a);
 
 struct MoeArgs {
   int fmt;
@@ -78,12 +79,12 @@ struct StackStage {
   int32_t K;
   int32_t fmt;
   int32_t block_bytes;
-  int32_t log2g;   // lanes per row = 2^log2g; a tile is waves * (64 >> log2g) rows
-  int32_t tiles;
+  int32_t log2g;   // lanes per row = 2^log2g; a wave takes 64 >> log2g rows per round
+  int32_t tiles;   // unused (0)
   int32_t units;   // load units per row (1 block for affine4, 2 for Q4_0/Q8_0)
 };
 int stack_iters(int fmt);
-int stack_waves();
+int stack_waves(int fmask);
 int64_t stack_sync_words(int n_stages);
 int64_t stack_error_word(int n_stages);
 int launch_stack(const StackStage* stages, int n_stages, uint32_t* sync, int fmask, int kmax,

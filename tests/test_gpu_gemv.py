@@ -48,6 +48,19 @@ def test_parity_shapes(fmt, N, K, M):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("K", (32, 96, 160, 2592))
+@pytest.mark.parametrize("M", (2, 17))
+def test_mfma_odd_block_counts(fmt, K, M):
+    """Rows whose length is an odd number of blocks leave Q4_0/Q8_0 blocks
+    only 2-byte aligned; the matrix-core path realigns them in registers."""
+    N = 45
+    packed, fields, x = _case(fmt, N, K, M, 6)
+    y = U.gemv_gpu(fmt, U.to_dev(packed), x, N, K)
+    yr, ad = R.gemv(fmt, fields, x)
+    U.assert_parity(y, yr, ad, f"{fmt} mfma N={N} K={K} M={M}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
 def test_generic_path_parity(fmt):
     N, K, M = 70, 1024, 3
     packed, fields, x = _case(fmt, N, K, M, 2)
@@ -109,7 +122,7 @@ def test_columns_match_single_column_runs(fmt, M):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("path", ("lds", "valu", "generic"))
+@pytest.mark.parametrize("path", ("lds", "valu", "generic", "mfma"))
 @pytest.mark.parametrize("M", (1, 3))
 def test_every_path_parity(fmt, path, M):
     """Each kernel path on the same shapes (the dispatcher would pick only one)."""
