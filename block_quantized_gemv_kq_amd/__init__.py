@@ -40,7 +40,7 @@ SIGNATURES = {
     "kq_argmax_workspace_bytes": (_I64, [_I64, _I32]),
     "kq_argmax": (_I32, [_P, _I64, _I32, _P, _P, _I64, _P]),
     "kq_f32_to_f16": (_I32, [_P, _P, _I64]),
-    "kq_stack_plan_bytes": (_I64, [_I32]),
+    "kq_stack_plan_bytes": (_I64, [_P, _I32]),
     "kq_stack_plan": (_I32, [_P, _I32, _P, _I64, _P, _P]),
     "kq_stack_run": (_I32, [_P, _P, _P]),
     "kq_stack_status": (_I32, [_P, _P, _P, _P]),
@@ -56,7 +56,7 @@ class kq_stage(ctypes.Structure):
 
 class kq_stack_info(ctypes.Structure):
     _fields_ = [("n_stages", ctypes.c_int32), ("fmt_mask", ctypes.c_int32), ("k_max", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("workgroups", ctypes.c_int32)]
 
 
 class KQError(RuntimeError):
@@ -219,13 +219,7 @@ def kq_argmax(y, N: int, M: int, out, workspace, workspace_bytes: int, stream=No
            "kq_argmax")
 
 
-def kq_stack_plan_bytes(n_stages: int) -> int:
-    return _check(lib().kq_stack_plan_bytes(n_stages), "kq_stack_plan_bytes")
-
-
-def kq_stack_plan(stages, plan, plan_bytes: int, stream=None) -> kq_stack_info:
-    """stages: list of dicts with fmt, W, x, y, N, K and optional y16 (device
-    tensors or addresses). Returns the filled kq_stack_info."""
+def _stage_array(stages):
     arr = (kq_stage * len(stages))()
     for i, st in enumerate(stages):
         arr[i].fmt = _fmt(st["fmt"])
@@ -236,6 +230,20 @@ def kq_stack_plan(stages, plan, plan_bytes: int, stream=None) -> kq_stack_info:
         arr[i].N = int(st["N"])
         arr[i].K = int(st["K"])
         arr[i].y16 = _ptr(st.get("y16"))
+    return arr
+
+
+def kq_stack_plan_bytes(stages) -> int:
+    """stages: list of dicts with fmt, W, x, y, N, K and optional y16 (device
+    tensors or addresses)."""
+    arr = _stage_array(stages)
+    return _check(lib().kq_stack_plan_bytes(ctypes.cast(arr, ctypes.c_void_p), len(stages)),
+                  "kq_stack_plan_bytes")
+
+
+def kq_stack_plan(stages, plan, plan_bytes: int, stream=None) -> kq_stack_info:
+    """stages: as for kq_stack_plan_bytes. Returns the filled kq_stack_info."""
+    arr = _stage_array(stages)
     info = kq_stack_info()
     _check(lib().kq_stack_plan(ctypes.cast(arr, ctypes.c_void_p), len(stages), _ptr(plan), plan_bytes,
                                ctypes.addressof(info), _stream(stream)), "kq_stack_plan")

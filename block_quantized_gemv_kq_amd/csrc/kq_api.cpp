@@ -213,21 +213,32 @@ static int64_t stack_descs_bytes(int n) {
   return ((int64_t)n * (int64_t)sizeof(kq::StackStage) + 255) / 256 * 256;
 }
 
-int64_t kq_stack_plan_bytes(int n_stages) {
-  if (n_stages < 1 || n_stages > KQ_STACK_MAX_STAGES)
-    return fail(KQ_ERR_ARG, "n_stages=%d must be in [1, %d]", n_stages, KQ_STACK_MAX_STAGES);
-  return stack_descs_bytes(n_stages) + (kq::stack_sync_words(n_stages) * 4 + 255) / 256 * 256;
-}
+namespace {
 
-int kq_stack_plan(const kq_stage* stages, int n_stages, void* plan, int64_t plan_bytes,
-                  kq_stack_info* info, void* stream) {
-  const int64_t need = kq_stack_plan_bytes(n_stages);
-  if (need < 0) return (int)need;
-  if (!stages || !plan || !info) return fail(KQ_ERR_ARG, "kq_stack_plan: null pointer");
-  if (plan_bytes < need) return fail(KQ_ERR_ARG, "kq_stack_plan: plan of %lld bytes needed", (long long)need);
-  if (!aligned(plan, 256)) return fail(KQ_ERR_ALIGN, "kq_stack_plan: plan must be 256-byte aligned");
-  // all argument checks first (no HIP call before they pass)
-  for (int i = 0; i < n_stages; ++i) {
+struct Range {
+  uintptr_t lo, hi;   // [lo, hi)
+  bool overlaps(const Range& o) const { return lo < o.hi && o.lo < hi; }
+  bool contains(const Range& o) const { return lo <= o.lo && o.hi <= hi; }
+};
+
+// The dataflow of a chain: for each stage, the earlier stage whose fp16
+// output holds its x (or -1) and the element offset of x in it; plus the
+// layout of the tagged buffers in the plan. Checks the stage fields and that
+// no stage writes memory that another stage reads or writes (the kernel runs
+// stages concurrently across workgroups, so only the x-in-an-earlier-y16
+// pattern has a defined order).
+struct ChainLayout {
+  std::vector<int> dep;
+  std::vector<int64_t> dep_off;     // elements
+  std::vector<int64_t> ll_word;     // first tagged word of a stage's outputs, or -1
+  int64_t ll_words = 0;
+};
+
+int check_stages(const kq_stage* stages, int n, ChainLayout& L) {
+  if (n < 1 || n > KQ_STACK_MAX_STAGES)
+    return fail(KQ_ERR_ARG, "n_stages=%d must be in [1, %d]", n, KQ_STACK_MAX_STAGES);
+  if (!stages) return fail(KQ_ERR_ARG, "stages is null");
+  for (int i = 0; i < n; ++i) {
     const kq_stage& s = stages[i];
     int st = check_fmt_k(s.fmt, s.K);
     if (st) return fail(st, "stage %d: %s", i, kq_last_error());
@@ -238,47 +249,118 @@ int kq_stack_plan(const kq_stage* stages, int n_stages, void* plan, int64_t plan
       return fail(KQ_ERR_ALIGN, "stage %d: W, y need 4-byte, x 16-byte, y16 2-byte alignment", i);
     const int ub = s.fmt == KQ_AFFINE4_G32 ? 1 : 2;
     if (s.K % (32 * ub) != 0) return fail(KQ_ERR_SHAPE, "stage %d: K must be a multiple of %d", i, 32 * ub);
-    if (s.K / (32 * ub) > 64 * kq::stack_iters(s.fmt))
-      return fail(KQ_ERR_SHAPE, "stage %d: K=%lld too long for the stacked kernel", i, (long long)s.K);
+    if (s.K > kq::STACK_MAX_K)
+      return fail(KQ_ERR_SHAPE, "stage %d: K=%lld exceeds %d for the stacked kernel", i, (long long)s.K,
+                  kq::STACK_MAX_K);
   }
+  std::vector<Range> xr(n), yr(n), hr(n);
+  for (int i = 0; i < n; ++i) {
+    const kq_stage& s = stages[i];
+    const uintptr_t x = reinterpret_cast<uintptr_t>(s.x), y = reinterpret_cast<uintptr_t>(s.y);
+    const uintptr_t h = reinterpret_cast<uintptr_t>(s.y16);
+    xr[i] = {x, x + (uintptr_t)s.K * 2};
+    yr[i] = {y, y + (uintptr_t)s.N * 4};
+    hr[i] = s.y16 ? Range{h, h + (uintptr_t)s.N * 2} : Range{0, 0};
+  }
+  L.dep.assign(n, -1);
+  L.dep_off.assign(n, 0);
+  L.ll_word.assign(n, -1);
+  for (int i = 0; i < n; ++i) {
+    if (stages[i].y16 && yr[i].overlaps(hr[i])) return fail(KQ_ERR_ARG, "stage %d: y and y16 overlap", i);
+    for (int j = 0; j < n; ++j) {
+      if (j == i) continue;
+      if (yr[i].overlaps(yr[j]) || (stages[j].y16 && yr[i].overlaps(hr[j])) ||
+          (stages[i].y16 && stages[j].y16 && hr[i].overlaps(hr[j])))
+        return fail(KQ_ERR_ARG, "stages %d and %d write overlapping outputs", i, j);
+    }
+    for (int j = 0; j < n; ++j) {
+      if (xr[i].overlaps(yr[j]))
+        return fail(KQ_ERR_ARG, "stage %d reads x from the fp32 output of stage %d", i, j);
+      if (!stages[j].y16 || !xr[i].overlaps(hr[j])) continue;
+      if (j >= i)
+        return fail(KQ_ERR_ARG, "stage %d reads x from the fp16 output of stage %d, which is not earlier", i, j);
+      if (!hr[j].contains(xr[i]))
+        return fail(KQ_ERR_ARG, "stage %d: x only partly inside the fp16 output of stage %d", i, j);
+      const int64_t off = (int64_t)(xr[i].lo - hr[j].lo) / 2;
+      if (off % 4 != 0)
+        return fail(KQ_ERR_ALIGN, "stage %d: x starts at element %lld of stage %d's y16 (need a multiple of 4)", i,
+                    (long long)off, j);
+      L.dep[i] = j;
+      L.dep_off[i] = off;
+    }
+  }
+  for (int i = 0; i < n; ++i) {
+    if (L.dep[i] >= 0 && L.ll_word[L.dep[i]] < 0) {
+      L.ll_word[L.dep[i]] = L.ll_words;
+      L.ll_words += (stages[L.dep[i]].N + 63) / 64 * 64;   // 256-byte aligned runs
+    }
+  }
+  return KQ_OK;
+}
+
+int64_t plan_bytes(int n, const ChainLayout& L) {
+  return stack_descs_bytes(n) + kq::STACK_SYNC_WORDS * 4 + L.ll_words * 4;
+}
+
+}  // namespace
+
+int64_t kq_stack_plan_bytes(const kq_stage* stages, int n_stages) {
+  ChainLayout L;
+  int st = check_stages(stages, n_stages, L);
+  if (st) return st;
+  return plan_bytes(n_stages, L);
+}
+
+int kq_stack_plan(const kq_stage* stages, int n_stages, void* plan, int64_t plan_bytes_given,
+                  kq_stack_info* info, void* stream) {
+  if (!plan || !info) return fail(KQ_ERR_ARG, "kq_stack_plan: null pointer");
+  ChainLayout L;
+  int st = check_stages(stages, n_stages, L);
+  if (st) return st;
+  const int64_t need = plan_bytes(n_stages, L);
+  if (plan_bytes_given < need) return fail(KQ_ERR_ARG, "kq_stack_plan: plan of %lld bytes needed", (long long)need);
+  if (!aligned(plan, 256)) return fail(KQ_ERR_ALIGN, "kq_stack_plan: plan must be 256-byte aligned");
   int cus = 0;
   int err = kq::stack_device_info(&cus);
   if (err) return hip_status(err, "kq_stack_plan");
+  if (cus < 1 || cus > kq::STACK_MAX_WG) return fail(KQ_ERR_HIP, "kq_stack_plan: %d compute units", cus);
+  for (int i = 0; i < n_stages; ++i) {
+    if ((stages[i].N + cus - 1) / cus > kq::STACK_MAX_SHARE_ROWS)
+      return fail(KQ_ERR_SHAPE, "stage %d: N=%lld exceeds %lld rows (%d per compute unit)", i,
+                  (long long)stages[i].N, (long long)cus * kq::STACK_MAX_SHARE_ROWS,
+                  kq::STACK_MAX_SHARE_ROWS);
+  }
   int fmask = 0, kmax = 0;
   for (int i = 0; i < n_stages; ++i) {
     fmask |= 1 << stages[i].fmt;
     if (stages[i].K > kmax) kmax = (int)stages[i].K;
   }
-  const int waves = kq::stack_waves(fmask);
+  uint8_t* base = static_cast<uint8_t*>(plan);
+  uint32_t* ll = reinterpret_cast<uint32_t*>(base + stack_descs_bytes(n_stages) + kq::STACK_SYNC_WORDS * 4);
   std::vector<kq::StackStage> d((size_t)n_stages);
   for (int i = 0; i < n_stages; ++i) {
     const kq_stage& s = stages[i];
     const int ub = s.fmt == KQ_AFFINE4_G32 ? 1 : 2;
-    const int units = (int)(s.K / (32 * ub));
-    const int iters = kq::stack_iters(s.fmt);
-    // G: at least enough lanes to cover a row in `iters` units each; more
-    // (fewer rows per wave) while one round of all waves still covers the
-    // workgroup's share of rows, so every wave has work.
-    int G = 1;
-    while (G * iters < units) G <<= 1;
-    const int64_t share = (s.N + cus - 1) / cus;
-    while (G < 64 && G < units && (int64_t)waves * (64 / (2 * G)) >= share) G <<= 1;
     kq::StackStage& o = d[(size_t)i];
+    memset(&o, 0, sizeof(o));
     o.W = static_cast<const uint8_t*>(s.W);
     o.x = s.x;
     o.y = s.y;
     o.y16 = s.y16;
-    o.N = s.N;
+    o.ll_out = L.ll_word[i] >= 0 ? ll + L.ll_word[i] : nullptr;
+    o.ll_in = L.dep[i] >= 0 ? ll + L.ll_word[L.dep[i]] + L.dep_off[i] : nullptr;
+    o.N = (int32_t)s.N;
     o.K = (int32_t)s.K;
     o.fmt = s.fmt;
-    o.block_bytes = (int32_t)kq::block_bytes(s.fmt);
-    int l = 0;
-    while ((1 << (l + 1)) <= G) ++l;
-    o.log2g = l;
-    o.tiles = 0;
-    o.units = units;
+    o.upr = (int32_t)(s.K / (32 * ub));
+    o.row_bytes = (int32_t)((s.K / 32) * kq::block_bytes(s.fmt));
+    o.rows_per = (int32_t)(s.N / cus);
+    o.rows_rem = (int32_t)(s.N % cus);
+    o.stride = (kq::STACK_NT / o.upr) * o.upr;
+    o.dep = L.dep[i];
   }
-  const int64_t dbytes = stack_descs_bytes(n_stages);
+  // descriptors, then the sync words and tagged buffers: all zero (no error,
+  // epoch 0, no tag; a zero word carries tag 0, which no stage of epoch 0 uses)
   std::vector<uint8_t> host((size_t)need, 0);
   memcpy(host.data(), d.data(), d.size() * sizeof(kq::StackStage));
   err = kq::copy_to_device(plan, host.data(), need, static_cast<hipStream_t>(stream));
@@ -286,28 +368,37 @@ int kq_stack_plan(const kq_stage* stages, int n_stages, void* plan, int64_t plan
   info->n_stages = n_stages;
   info->fmt_mask = fmask;
   info->k_max = kmax;
-  info->reserved = (int32_t)(dbytes / 4);   // offset of the counters, in words
+  info->workgroups = cus;
   return ok();
 }
 
 int kq_stack_run(const void* plan, const kq_stack_info* info, void* stream) {
   if (!plan || !info) return fail(KQ_ERR_ARG, "kq_stack_run: null pointer");
   if (info->n_stages < 1 || info->n_stages > KQ_STACK_MAX_STAGES || info->fmt_mask < 1 ||
-      info->fmt_mask > 7 || info->k_max < 32 || info->reserved * 4 != stack_descs_bytes(info->n_stages))
+      info->fmt_mask > 7 || info->k_max < 32 || info->k_max > kq::STACK_MAX_K ||
+      info->workgroups < 1 || info->workgroups > kq::STACK_MAX_WG)
     return fail(KQ_ERR_ARG, "kq_stack_run: info was not filled by kq_stack_plan");
+  int cus = 0;
+  int err = kq::stack_device_info(&cus);
+  if (err) return hip_status(err, "kq_stack_run");
+  if (cus != info->workgroups)
+    return fail(KQ_ERR_ARG, "kq_stack_run: plan made for %d compute units, device has %d", info->workgroups, cus);
   const kq::StackStage* st = static_cast<const kq::StackStage*>(plan);
-  uint32_t* sync = reinterpret_cast<uint32_t*>(const_cast<void*>(plan)) + info->reserved;
-  return hip_status(kq::launch_stack(st, info->n_stages, sync, info->fmt_mask, info->k_max,
-                                     static_cast<hipStream_t>(stream)),
+  uint32_t* sync = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(const_cast<void*>(plan)) +
+                                               stack_descs_bytes(info->n_stages));
+  return hip_status(kq::launch_stack(st, info->n_stages, sync, info->fmt_mask, info->workgroups,
+                                     info->k_max, static_cast<hipStream_t>(stream)),
                     "kq_stack_run");
 }
 
 int kq_stack_status(const void* plan, const kq_stack_info* info, int* error, void* stream) {
   if (!plan || !info || !error) return fail(KQ_ERR_ARG, "kq_stack_status: null pointer");
-  const uint32_t* sync = reinterpret_cast<const uint32_t*>(plan) + info->reserved;
+  if (info->n_stages < 1 || info->n_stages > KQ_STACK_MAX_STAGES)
+    return fail(KQ_ERR_ARG, "kq_stack_status: info was not filled by kq_stack_plan");
+  const uint32_t* sync = reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(plan) +
+                                                           stack_descs_bytes(info->n_stages));
   uint32_t word = 0;
-  int err = kq::read_from_device(&word, sync + kq::stack_error_word(info->n_stages), 4,
-                                 static_cast<hipStream_t>(stream));
+  int err = kq::read_from_device(&word, sync + kq::STACK_ERR_WORD, 4, static_cast<hipStream_t>(stream));
   if (err) return hip_status(err, "kq_stack_status");
   *error = (int)word;
   return ok();

@@ -69,25 +69,44 @@ int launch_moe_gate_up_swiglu(const MoeGateUpArgs& a);
 int launch_weighted_slot_sum(const float* ys, const float* w, float* y, int64_t N, int M,
                              int top_k, hipStream_t stream);
 
-// One stage of a persistent GEMV chain (M = 1), as the kernel reads it.
+// The persistent chain's workgroup shape: STACK_CWAVES compute waves and one
+// control wave; STACK_NT compute lanes.
+constexpr int STACK_CWAVES = 11;
+constexpr int STACK_NT = 64 * STACK_CWAVES;
+
+// One stage of a persistent GEMV chain (M = 1), as the kernel reads it (128 B).
+// The plan fixes the number of workgroups nb (one per CU): workgroup b owns
+// rows [b*rows_per + min(b, rows_rem), ...), rows_per + (b < rows_rem) of them.
 struct StackStage {
   const uint8_t* W;
-  const uint16_t* x;
+  const uint16_t* x;       // activations from outside the chain (ll_in == nullptr)
   float* y;
-  uint16_t* y16;   // optional fp16 copy of y
-  int64_t N;
+  uint16_t* y16;           // optional fp16 copy of y
+  uint32_t* ll_out;        // tagged fp16 outputs that later stages read, or nullptr
+  const uint32_t* ll_in;   // the K tagged words holding x, or nullptr
+  int32_t N;
   int32_t K;
   int32_t fmt;
-  int32_t block_bytes;
-  int32_t log2g;   // lanes per row = 2^log2g; a wave takes 64 >> log2g rows per round
-  int32_t tiles;   // unused (0)
-  int32_t units;   // load units per row (1 block for affine4, 2 for Q4_0/Q8_0)
+  int32_t upr;             // load units per row (1 block for affine4, 2 for Q4_0/Q8_0)
+  int32_t row_bytes;
+  int32_t rows_per;        // N / nb
+  int32_t rows_rem;        // N % nb
+  int32_t stride;          // units per lane step: (STACK_NT / upr) * upr
+  int32_t dep;             // stage whose outputs ll_in points into, or -1
+  int32_t pad[11];
 };
-int stack_iters(int fmt);
-int stack_waves(int fmask);
-int64_t stack_sync_words(int n_stages);
-int64_t stack_error_word(int n_stages);
-int launch_stack(const StackStage* stages, int n_stages, uint32_t* sync, int fmask, int kmax,
+static_assert(sizeof(StackStage) == 128, "stage descriptor is 128 bytes");
+
+// Limits of the persistent chain and the layout of its sync words (32-bit
+// words after the stage descriptors; each has a 128-byte line of its own).
+constexpr int STACK_MAX_WG = 1024;          // workgroups (CUs) a plan can span
+constexpr int STACK_MAX_SHARE_ROWS = 4096;  // rows of one stage per workgroup
+constexpr int STACK_MAX_K = 16384;          // inputs per row
+constexpr int64_t STACK_ERR_WORD = 0;
+constexpr int64_t STACK_EPOCH_WORD = 32;                         // + 32 * workgroup
+constexpr int64_t STACK_SYNC_WORDS = 32 + 32 * STACK_MAX_WG;
+int64_t stack_lds_bytes(int kmax);
+int launch_stack(const StackStage* stages, int n_stages, uint32_t* sync, int fmask, int nb, int kmax,
                  hipStream_t stream);
 int stack_device_info(int* cus);
 int copy_to_device(void* dst, const void* src, int64_t bytes, hipStream_t stream);

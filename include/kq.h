@@ -184,19 +184,27 @@ int kq_argmax(const float* y, int64_t N, int M, int32_t* out,
  * Kinetic docs, "What makes it fast": a decode step is hundreds of small GPU
  * kernels, recorded once and replayed with one call per token. kq_stack_run
  * goes further: the whole chain (e.g. every projection of every layer of a
- * dense model, then its output layer) is ONE kernel launch. Stage s reads its
- * activations only after every output row of stage s-1 is written (so
- * stages[s].x may be stages[s-1].y16), while its weights are already being
- * loaded: weights never depend on activations. */
+ * dense model, then its output layer) is ONE kernel launch, and each stage's
+ * weights stream in while earlier stages finish: weights never depend on
+ * activations.
+ *
+ * Dataflow: a stage whose x lies inside the y16 (fp16 output) of an EARLIER
+ * stage waits for exactly those values of that launch; that is how a chain
+ * is expressed (stages[s].x = stages[s-1].y16, or any 4-element-aligned run
+ * of it, e.g. the q part of a fused q|k|v output). Any other x is read as it
+ * is at the start of the launch, and stages that do not depend on each other
+ * may run at the same time. So that this is well defined, kq_stack_plan
+ * rejects (KQ_ERR_ARG) stages whose outputs (y, y16) overlap each other,
+ * and an x that overlaps any y, a later (or the same) stage's y16, or only
+ * part of an earlier stage's y16. */
 typedef struct kq_stage {
   int32_t fmt;          /* kq_format */
   int32_t reserved;     /* must be 0 */
   const void* W;        /* device, packed N x K (kq_pack layout), 4-byte aligned */
   const uint16_t* x;    /* device, fp16 bits [K], 16-byte aligned */
   float* y;             /* device, fp32 [N], 4-byte aligned; overwritten */
-  int64_t N;            /* 1 <= N < 2^31 */
-  int64_t K;            /* multiple of 32 (of 64 for Q8_0/Q4_0); K/32 <= 320 for
-                           affine4, K/64 <= 320 for Q4_0, K/64 <= 128 for Q8_0 */
+  int64_t N;            /* 1 <= N <= 4096 * (compute units of the device) */
+  int64_t K;            /* multiple of 32 (of 64 for Q8_0/Q4_0), at most 16384 */
   uint16_t* y16;        /* device or NULL: also store fp16(y) (round to nearest
                            even), 2-byte aligned, so a later stage can read it as x */
 } kq_stage;
@@ -206,31 +214,39 @@ typedef struct kq_stack_info {
   int32_t n_stages;
   int32_t fmt_mask;
   int32_t k_max;
-  int32_t reserved;
+  int32_t workgroups;   /* one per compute unit of the device the plan was made on */
 } kq_stack_info;
 
 #define KQ_STACK_MAX_STAGES 4096
 
-/* Device bytes of a plan for n_stages stages. */
-int64_t kq_stack_plan_bytes(int n_stages);
+/* Device bytes of a plan for these stages (the plan holds the stage
+ * descriptors, per-workgroup sync words and a tagged copy of every fp16
+ * output that a later stage reads). Checks the stages as kq_stack_plan does
+ * (host only) and returns a negative kq_status if they are not valid. */
+int64_t kq_stack_plan_bytes(const kq_stage* stages, int n_stages);
 
 /* kq_stack_plan — validate `stages` (host array of n_stages) and write the
  * device-side plan (`plan`: device, kq_stack_plan_bytes bytes, 256-byte
  * aligned) plus `info` (host). Copies over `stream` and synchronises it: call
  * it once at set-up, not inside graph capture. The plan stays valid while the
- * buffers it names do. Errors: KQ_ERR_ARG, KQ_ERR_FORMAT, KQ_ERR_SHAPE,
- * KQ_ERR_ALIGN, KQ_ERR_HIP. */
+ * buffers it names do, on the device it was made on (kq_stack_run checks the
+ * compute-unit count). Errors: KQ_ERR_ARG (also the overlaps above),
+ * KQ_ERR_FORMAT, KQ_ERR_SHAPE (also K > 16384, or N above 4096 rows per
+ * compute unit), KQ_ERR_ALIGN (also an x starting at an element of an earlier
+ * y16 that is not a multiple of 4), KQ_ERR_HIP. */
 int kq_stack_plan(const kq_stage* stages, int n_stages, void* plan, int64_t plan_bytes,
                   kq_stack_info* info, void* stream);
 
-/* kq_stack_run — run every stage of a plan, in order, in one launch on
- * `stream` (asynchronous; may be captured in a graph). Results are
- * deterministic run to run, bit for bit, and each output is within the
- * kq_gemv tolerance of the exact value. Runs on one plan must not
- * overlap in time (they share its counters). The grid (one workgroup per CU)
- * waits on itself; a wait that exceeds its spin limit counts in the plan's
- * error word (kq_stack_status; sticky until the next kq_stack_plan) and lets
- * the launch finish instead of hanging. */
+/* kq_stack_run — run every stage of a plan in one launch on `stream`
+ * (asynchronous; may be captured in a graph). Results are deterministic run
+ * to run, bit for bit, and each output is within the kq_gemv tolerance of the
+ * exact value. Runs on one plan must not overlap in time (they share its sync
+ * words). The grid (one workgroup per CU) needs every CU free; a wait that
+ * exceeds its spin limit counts in the plan's error word (kq_stack_status;
+ * sticky until the next kq_stack_plan) and lets the launch finish instead of
+ * hanging; outputs of such a run are undefined. The plan needs no reset
+ * between runs (each run advances epochs stored in the plan), so a captured
+ * graph can replay it with nothing else in the graph. */
 int kq_stack_run(const void* plan, const kq_stack_info* info, void* stream);
 
 /* kq_stack_status — synchronise `stream`, then read the plan's error word

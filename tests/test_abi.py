@@ -154,34 +154,78 @@ def test_pack_validation():
     assert kq.lib().kq_pack(0, None, 0, 32, None, 1) == kq.KQ_OK
 
 
+def _stage_arr(sts):
+    arr = (kq.kq_stage * len(sts))()
+    for i, st in enumerate(sts):
+        arr[i].fmt = kq._fmt(st["fmt"])
+        arr[i].reserved = st.get("reserved", 0)
+        arr[i].W, arr[i].x, arr[i].y = st["W"], st["x"], st["y"]
+        arr[i].N, arr[i].K = st["N"], st["K"]
+        arr[i].y16 = st.get("y16")
+    return arr
+
+
 def test_stack_validation():
     L = kq.lib()
-    assert L.kq_stack_plan_bytes(0) == kq.KQ_ERR_ARG
-    assert L.kq_stack_plan_bytes(4097) == kq.KQ_ERR_ARG
-    nb = kq.kq_stack_plan_bytes(3)
-    assert nb >= 3 * 64
+    base = dict(fmt="affine4", W=A16, x=A16, y=0x200000, N=64, K=2560)
+
+    def nbytes(*sts):
+        return L.kq_stack_plan_bytes(ctypes.cast(_stage_arr(sts), ctypes.c_void_p), len(sts))
 
     def plan(**over):
-        st = dict(fmt="affine4", W=A16, x=A16, y=A16, N=64, K=2560)
+        st = dict(base)
         st.update(over)
-        arr = (kq.kq_stage * 1)()
-        arr[0].fmt = kq._fmt(st["fmt"])
-        arr[0].reserved = st.get("reserved", 0)
-        arr[0].W, arr[0].x, arr[0].y = st["W"], st["x"], st["y"]
-        arr[0].N, arr[0].K = st["N"], st["K"]
-        arr[0].y16 = st.get("y16")
         info = kq.kq_stack_info()
-        return L.kq_stack_plan(ctypes.cast(arr, ctypes.c_void_p), 1, 0x100000, nb,
+        return L.kq_stack_plan(ctypes.cast(_stage_arr([st]), ctypes.c_void_p), 1, 0x100000, 1 << 30,
                                ctypes.addressof(info), 0)
+    assert L.kq_stack_plan_bytes(ctypes.cast(_stage_arr([base]), ctypes.c_void_p), 0) == kq.KQ_ERR_ARG
+    assert L.kq_stack_plan_bytes(None, 1) == kq.KQ_ERR_ARG
+    one = nbytes(base)
+    assert one >= 128 + 32 * 4 * 1024
     assert plan(fmt=9) == kq.KQ_ERR_FORMAT
     assert plan(K=48) == kq.KQ_ERR_SHAPE
     assert plan(fmt="q8_0", K=96) == kq.KQ_ERR_SHAPE            # Q8_0 needs K % 64 == 0
-    assert plan(K=32 * 321) == kq.KQ_ERR_SHAPE                   # too long for one pass
-    assert plan(fmt="q8_0", K=64 * 129) == kq.KQ_ERR_SHAPE
+    assert plan(K=16384 + 32) == kq.KQ_ERR_SHAPE                # longer than the x stage in LDS
+    assert plan(fmt="q8_0", K=16384 + 64) == kq.KQ_ERR_SHAPE
     assert plan(N=0) == kq.KQ_ERR_ARG
     assert plan(W=None) == kq.KQ_ERR_ARG
     assert plan(reserved=1) == kq.KQ_ERR_ARG
     assert plan(x=A4) == kq.KQ_ERR_ALIGN
-    assert plan(y16=A16 + 1) == kq.KQ_ERR_ALIGN
+    assert plan(y16=0x300001) == kq.KQ_ERR_ALIGN
+    assert plan(y16=0x200000 + 64) == kq.KQ_ERR_ARG             # y and y16 overlap
+
+
+def test_stack_dataflow_rules():
+    """Which stage pairs a plan accepts, and the tagged buffers it sizes: a
+    stage may read x from inside an earlier stage's y16 (4-element aligned);
+    every other overlap of outputs with outputs or inputs is refused."""
+    L = kq.lib()
+
+    def nbytes(*sts):
+        return L.kq_stack_plan_bytes(ctypes.cast(_stage_arr(sts), ctypes.c_void_p), len(sts))
+    s0 = dict(fmt="affine4", W=A16, x=0x100000, y=0x200000, N=6144, K=2560, y16=0x300000)
+    free = nbytes(s0, dict(s0, x=0x110000, y=0x210000, y16=0x310000, N=2560, K=4096))
+    # stage 1 reads the first 4096 values of stage 0's fp16 output: stage 0's
+    # 6144 outputs get a tagged copy (4 bytes each) in the plan
+    chained = nbytes(s0, dict(s0, x=0x300000, y=0x210000, y16=None, N=2560, K=4096))
+    assert chained - free == 6144 * 4
+    # reading from the middle of it (element 2048, a multiple of 4) is allowed
+    assert nbytes(s0, dict(s0, x=0x300000 + 2 * 2048, y=0x210000, y16=None, N=2560, K=4096)) == chained
+    # ... from element 2 is not (the tagged words are read in 16-byte chunks)
+    assert nbytes(s0, dict(s0, x=0x300000 + 4, y=0x210000, y16=None, N=2560, K=2560)) == kq.KQ_ERR_ALIGN
+    # x running past the end of the earlier output
+    assert nbytes(s0, dict(s0, x=0x300000 + 2 * 4096, y=0x210000, y16=None, N=2560, K=4096)) == kq.KQ_ERR_ARG
+    # x inside a LATER stage's output, or the stage's own
+    assert nbytes(dict(s0, x=0x310000, y16=None), dict(s0, x=0x110000, y=0x210000, y16=0x310000)) == kq.KQ_ERR_ARG
+    assert nbytes(dict(s0, x=0x300000)) == kq.KQ_ERR_ARG
+    # x inside an fp32 output
+    assert nbytes(s0, dict(s0, x=0x200000, y=0x210000, y16=None)) == kq.KQ_ERR_ARG
+    # two stages writing overlapping outputs
+    assert nbytes(s0, dict(s0, x=0x110000, y=0x200000 + 4 * 100, y16=None)) == kq.KQ_ERR_ARG
+    assert nbytes(s0, dict(s0, x=0x110000, y=0x210000, y16=0x300000 + 8)) == kq.KQ_ERR_ARG
+
+
+def test_stack_run_checks():
+    L = kq.lib()
     info = kq.kq_stack_info()
     assert L.kq_stack_run(0x100000, ctypes.addressof(info), 0) == kq.KQ_ERR_ARG   # info not filled
