@@ -231,6 +231,7 @@ struct ChainLayout {
   std::vector<int> dep;
   std::vector<int64_t> dep_off;     // elements
   std::vector<int64_t> ll_word;     // first tagged word of a stage's outputs, or -1
+  std::vector<int64_t> ll_stride;   // words between the copies of a stage's outputs
   int64_t ll_words = 0;
 };
 
@@ -265,6 +266,7 @@ int check_stages(const kq_stage* stages, int n, ChainLayout& L) {
   L.dep.assign(n, -1);
   L.dep_off.assign(n, 0);
   L.ll_word.assign(n, -1);
+  L.ll_stride.assign(n, 0);
   for (int i = 0; i < n; ++i) {
     if (stages[i].y16 && yr[i].overlaps(hr[i])) return fail(KQ_ERR_ARG, "stage %d: y and y16 overlap", i);
     for (int j = 0; j < n; ++j) {
@@ -291,8 +293,11 @@ int check_stages(const kq_stage* stages, int n, ChainLayout& L) {
   }
   for (int i = 0; i < n; ++i) {
     if (L.dep[i] >= 0 && L.ll_word[L.dep[i]] < 0) {
+      // STACK_LL_COPIES copies, each a 256-byte aligned run
+      const int64_t run = (stages[L.dep[i]].N + 63) / 64 * 64;
       L.ll_word[L.dep[i]] = L.ll_words;
-      L.ll_words += (stages[L.dep[i]].N + 63) / 64 * 64;   // 256-byte aligned runs
+      L.ll_stride[L.dep[i]] = run;
+      L.ll_words += run * kq::STACK_LL_COPIES;
     }
   }
   return KQ_OK;
@@ -356,8 +361,11 @@ int kq_stack_plan(const kq_stage* stages, int n_stages, void* plan, int64_t plan
     o.row_bytes = (int32_t)((s.K / 32) * kq::block_bytes(s.fmt));
     o.rows_per = (int32_t)(s.N / cus);
     o.rows_rem = (int32_t)(s.N % cus);
-    o.stride = (kq::STACK_NT / o.upr) * o.upr;
+    o.log2g = kq::stack_log2g((s.N + cus - 1) / cus, o.upr);
+    o.kpr = (o.upr + (1 << o.log2g) - 1) >> o.log2g;
     o.dep = L.dep[i];
+    o.ll_out_stride = (int32_t)L.ll_stride[i];
+    o.ll_in_stride = L.dep[i] >= 0 ? (int32_t)L.ll_stride[L.dep[i]] : 0;
   }
   // descriptors, then the sync words and tagged buffers: all zero (no error,
   // epoch 0, no tag; a zero word carries tag 0, which no stage of epoch 0 uses)

@@ -373,33 +373,26 @@ __device__ __forceinline__ float block_dot_split(const uint32_t* A, const uint32
   }
 }
 
-// Per-block activation sums for MT columns staged in LDS: for column m and
-// block b, xs[(m * nblk + b) * 2 + {0,1}] = sum of elements 0..15 / 16..31.
-// Every thread of the workgroup takes part; follow with __syncthreads().
+// Per-block activation sums for MT columns staged in LDS (column m at
+// xl + m * kdw dwords, so the columns are one contiguous run): for column m
+// and block b, xs[(m * nblk + b) * 2 + {0,1}] = sum of elements 0..15 / 16..31,
+// i.e. xs[h] is the sum of half-block h of the run. Every thread of the
+// workgroup takes part; follow with __syncthreads().
 __device__ __forceinline__ void block_sums_to_lds(const uint32_t* xl, int kdw, int mt, float* xs) {
-  const int nblk = kdw / 16;
-  for (int i = threadIdx.x; i < mt * nblk; i += blockDim.x) {
-    const int m = i / nblk, b = i - m * nblk;
-    const u32x4* p = reinterpret_cast<const u32x4*>(xl + m * kdw + b * 16);
-    float lo = 0.0f, hi = 0.0f;
-#pragma unroll
-    for (int v = 0; v < 2; ++v) {
-      const u32x4 t = p[v];
-      lo = dot2(t.x, ONES, lo);
-      lo = dot2(t.y, ONES, lo);
-      lo = dot2(t.z, ONES, lo);
-      lo = dot2(t.w, ONES, lo);
-    }
-#pragma unroll
-    for (int v = 2; v < 4; ++v) {
-      const u32x4 t = p[v];
-      hi = dot2(t.x, ONES, hi);
-      hi = dot2(t.y, ONES, hi);
-      hi = dot2(t.z, ONES, hi);
-      hi = dot2(t.w, ONES, hi);
-    }
-    xs[2 * i] = lo;
-    xs[2 * i + 1] = hi;
+  const int halves = mt * kdw / 8;
+  for (int h = threadIdx.x; h < halves; h += blockDim.x) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(xl) + 2 * h;
+    const u32x4 a = p[0], c = p[1];
+    float s = 0.0f;
+    s = dot2(a.x, ONES, s);
+    s = dot2(a.y, ONES, s);
+    s = dot2(a.z, ONES, s);
+    s = dot2(a.w, ONES, s);
+    s = dot2(c.x, ONES, s);
+    s = dot2(c.y, ONES, s);
+    s = dot2(c.z, ONES, s);
+    s = dot2(c.w, ONES, s);
+    xs[h] = s;
   }
 }
 

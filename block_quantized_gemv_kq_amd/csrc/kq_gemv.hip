@@ -55,12 +55,14 @@ __global__ __launch_bounds__(256) void k_gemv_valu(const uint8_t* __restrict__ W
   }
 }
 
+constexpr int XREG_CHUNKS = 5;   // 16-byte activation chunks per thread in the register variant
+
 // ------------------------------------------- VALU path, loads-first + LDS x
 // One row per lane group (G lanes), 64/G rows per wave. Each lane issues the
 // loads of all ITERS units it owns, the workgroup stages the MT activation
 // columns in LDS meanwhile, and only then does any arithmetic: one memory
 // round trip per tile. `passes` > 1 only when units > G * ITERS.
-template <int FMT, int MT, int ITERS>
+template <int FMT, int MT, int ITERS, bool XREG>
 __global__ __launch_bounds__(256) void k_gemv_lds(const uint8_t* __restrict__ W,
                                                   const uint16_t* __restrict__ x,
                                                   float* __restrict__ y, int N, int K, int log2g,
@@ -79,12 +81,41 @@ __global__ __launch_bounds__(256) void k_gemv_lds(const uint8_t* __restrict__ W,
   const int rho = lane >> log2g;
   const int g = lane & (G - 1);
   const uint32_t roff = (uint32_t)rho * row_bytes;
-  Loaded<FMT, ITERS> w;
-  issue_units<FMT, ITERS>(rs, roff, g, G, units, w);
   const int kdw = K / 2;
   float* xs = reinterpret_cast<float*>(xl + MT * kdw);
+  // XREG: the activations go ahead of the weights in this CU's memory queue,
+  // loaded into registers (at most XREG_CHUNKS 16-byte chunks per thread), so
+  // writing them to LDS waits for them alone and the block sums below overlap
+  // the weights' latency. Otherwise they are copied by LDS DMA (any K), which
+  // the first barrier waits for together with the weights. The two variants
+  // are separate kernels: with an LDS DMA anywhere in the kernel the compiler
+  // would make the register path's LDS writes wait for every load.
+  constexpr int XCH = XREG_CHUNKS;
+  const int n16 = MT * K / 8;   // columns m0 .. m0+MT-1 are contiguous
+  u32x4 xr[XCH];
+  const u32x4* xsrc = reinterpret_cast<const u32x4*>(x + (int64_t)m0 * K);
+  if constexpr (XREG) {
 #pragma unroll
-  for (int m = 0; m < MT; ++m) stage_to_lds(x + (int64_t)(m0 + m) * K, xl + m * kdw, K / 8);
+    for (int c = 0; c < XCH; ++c) {
+      const int i = (int)threadIdx.x + 256 * c;
+      xr[c] = i < n16 ? xsrc[i] : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  Loaded<FMT, ITERS> w;
+  issue_units<FMT, ITERS>(rs, roff, g, G, units, w);
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (XREG) {
+    u32x4* xl4 = reinterpret_cast<u32x4*>(xl);
+#pragma unroll
+    for (int c = 0; c < XCH; ++c) {
+      const int i = (int)threadIdx.x + 256 * c;
+      if (i < n16) xl4[i] = xr[c];
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < MT; ++m) stage_to_lds(x + (int64_t)(m0 + m) * K, xl + m * kdw, K / 8);
+  }
   __syncthreads();
   block_sums_to_lds(xl, kdw, MT, xs);
   __syncthreads();
@@ -251,13 +282,26 @@ struct LdsCfg {
   int passes;
 };
 
-// G (lanes per row, power of two) and ITERS (units per lane per pass): G is
-// the smallest that covers a row in MAX_ITERS units per lane, then doubled
-// while the grid has fewer than 2048 waves (8 per CU) and lanes would still
-// have work, so small matrices spread over more waves.
-LdsCfg lds_cfg(int64_t N, int units) {
-  int G = 1;
-  while (G < 64 && G * MAX_ITERS < units) G <<= 1;
+// G (lanes per row, power of two) and ITERS (units per lane per pass): G
+// gives each lane about LANE_BYTES of weights (at most MAX_ITERS units; the
+// larger G on a tie), then is doubled while the grid has fewer than 2048 waves
+// (8 per CU) and lanes would still have work, so small matrices spread over
+// more waves. On MI355X (cold weights, graph-replayed) this picks the fastest
+// or nearly fastest G for the 4B-shaped projections and the Q8_0 lm_head.
+constexpr int LANE_BYTES = 128;
+
+LdsCfg lds_cfg(int64_t N, int units, int unit_bytes) {
+  int G = 64;
+  int best = -1;
+  for (int g = 64; g >= 1; g >>= 1) {
+    const int iters = (units + g - 1) / g;
+    if (iters > MAX_ITERS) break;
+    const int dev = iters * unit_bytes > LANE_BYTES ? iters * unit_bytes - LANE_BYTES : LANE_BYTES - iters * unit_bytes;
+    if (best < 0 || dev < best) {
+      best = dev;
+      G = g;
+    }
+  }
   while (G < 64 && N * G / 64 < 2048 && G < units) G <<= 1;
   const int env_g = env_int("KQ_VALU_G");
   if (env_g == 1 || env_g == 2 || env_g == 4 || env_g == 8 || env_g == 16 || env_g == 32 || env_g == 64) G = env_g;
@@ -273,8 +317,12 @@ int launch_lds_it(const GemvArgs& a, int m0, LdsCfg c) {
   const int64_t waves = (a.N + rpw - 1) / rpw;
   const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
   const size_t lds = (size_t)MT * a.K * 2 + (size_t)MT * (a.K / 32) * 8;  // x + block sums
-  hipLaunchKernelGGL((k_gemv_lds<FMT, MT, ITERS>), grid, block, lds, a.stream, a.W, a.x, a.y, (int)a.N,
-                     (int)a.K, c.log2g, m0, c.passes);
+  if ((int64_t)MT * a.K / 8 <= 256 * XREG_CHUNKS)
+    hipLaunchKernelGGL((k_gemv_lds<FMT, MT, ITERS, true>), grid, block, lds, a.stream, a.W, a.x, a.y, (int)a.N,
+                       (int)a.K, c.log2g, m0, c.passes);
+  else
+    hipLaunchKernelGGL((k_gemv_lds<FMT, MT, ITERS, false>), grid, block, lds, a.stream, a.W, a.x, a.y, (int)a.N,
+                       (int)a.K, c.log2g, m0, c.passes);
   return (int)hipGetLastError();
 }
 
@@ -292,7 +340,7 @@ int launch_lds_mt(const GemvArgs& a, int m0, LdsCfg c) {
 template <int FMT>
 int launch_lds(const GemvArgs& a) {
   const int units = (int)(a.K / (32 * Fmt<FMT>::UB));
-  const LdsCfg c = lds_cfg(a.N, units);
+  const LdsCfg c = lds_cfg(a.N, units, Fmt<FMT>::BB * Fmt<FMT>::UB);
   for (int m0 = 0; m0 < a.M; m0 += LDS_MAX_MT) {
     const int mt = a.M - m0 < LDS_MAX_MT ? a.M - m0 : LDS_MAX_MT;
     int err;

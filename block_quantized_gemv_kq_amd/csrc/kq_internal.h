@@ -77,6 +77,9 @@ constexpr int STACK_NT = 64 * STACK_CWAVES;
 // One stage of a persistent GEMV chain (M = 1), as the kernel reads it (128 B).
 // The plan fixes the number of workgroups nb (one per CU): workgroup b owns
 // rows [b*rows_per + min(b, rows_rem), ...), rows_per + (b < rows_rem) of them.
+// Within a workgroup, G = 2^log2g lanes share a row; lane group gamma of the
+// STACK_NT / G groups takes rows gamma, gamma + groups, ... and lane g of it
+// units g, g + G, ... of each row: kpr = ceil(upr / G) steps per row.
 struct StackStage {
   const uint8_t* W;
   const uint16_t* x;       // activations from outside the chain (ll_in == nullptr)
@@ -91,9 +94,12 @@ struct StackStage {
   int32_t row_bytes;
   int32_t rows_per;        // N / nb
   int32_t rows_rem;        // N % nb
-  int32_t stride;          // units per lane step: (STACK_NT / upr) * upr
+  int32_t log2g;           // lanes per row = 2^log2g
+  int32_t kpr;             // steps per row = ceil(upr / G)
   int32_t dep;             // stage whose outputs ll_in points into, or -1
-  int32_t pad[11];
+  int32_t ll_out_stride;   // words between the replicas of ll_out
+  int32_t ll_in_stride;    // words between the replicas of ll_in
+  int32_t pad[8];
 };
 static_assert(sizeof(StackStage) == 128, "stage descriptor is 128 bytes");
 
@@ -102,9 +108,16 @@ static_assert(sizeof(StackStage) == 128, "stage descriptor is 128 bytes");
 constexpr int STACK_MAX_WG = 1024;          // workgroups (CUs) a plan can span
 constexpr int STACK_MAX_SHARE_ROWS = 4096;  // rows of one stage per workgroup
 constexpr int STACK_MAX_K = 16384;          // inputs per row
+// Copies of each tagged output: workgroup b reads copy b % STACK_LL_COPIES, so
+// each copy is read by a fraction of the grid instead of all of it.
+constexpr int STACK_LL_COPIES = 8;
 constexpr int64_t STACK_ERR_WORD = 0;
 constexpr int64_t STACK_EPOCH_WORD = 32;                         // + 32 * workgroup
-constexpr int64_t STACK_SYNC_WORDS = 32 + 32 * STACK_MAX_WG;
+constexpr int64_t STACK_HINT_WORD = 32 + 32 * STACK_MAX_WG;      // + 32 * workgroup
+constexpr int64_t STACK_SYNC_WORDS = 32 + 2 * 32 * STACK_MAX_WG;
+// Lanes per row for a stage of `rows_max` rows per workgroup and `upr` units
+// per row: the G in {4, ..., 64} with the fewest steps per lane.
+int stack_log2g(int64_t rows_max, int upr);
 int64_t stack_lds_bytes(int kmax);
 int launch_stack(const StackStage* stages, int n_stages, uint32_t* sync, int fmask, int nb, int kmax,
                  hipStream_t stream);

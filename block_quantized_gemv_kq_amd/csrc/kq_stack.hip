@@ -16,31 +16,32 @@
 //    it is consumed. These waves issue no other vector memory operation, so
 //    waiting for a slot never waits for an activation or an output.
 //  * 1 CONTROL wave does everything that touches activations, outputs and
-//    other workgroups: it brings x of each stage into LDS, sums the compute
-//    waves' per-unit partial dot products into rows in a fixed order, and
-//    writes the outputs.
+//    other workgroups: it brings x of each stage into LDS with its per-block
+//    sums, and writes the outputs the compute waves leave in LDS.
 //
-// Work split: a workgroup owns a contiguous share of stage s's rows, i.e. a
-// contiguous run of U load units (1 affine4 block, or 2 Q4_0/Q8_0 blocks). Let
-// S = (704 / upr) * upr, the largest multiple of the row length that fits the
-// 704 compute lanes. Lane t < S takes units t, t + S, t + 2S, ...: all in the
-// same column t mod upr, so the lane holds that column's activations in
-// registers for the whole stage, and each load instruction of a wave covers
-// consecutive units. Each unit's partial goes to LDS; the control wave sums
-// each row's partials in unit order (deterministic run to run).
+// Work split: a workgroup owns a contiguous share of stage s's rows. Within
+// it, G lanes share a row (G in 4..64, chosen per stage so that the busiest
+// lane has the fewest steps): lane group gamma takes rows gamma, gamma +
+// groups, ... and lane g of it units g, g + G, ... of each row (a unit is one
+// affine4 block or two Q4_0/Q8_0 blocks), accumulating in a register; the G
+// lanes combine a finished row by a fixed butterfly (deterministic run to
+// run). The activations of a stage sit in LDS with their 16-byte pieces
+// rotated per column, so that the G consecutive columns one instruction reads
+// fall in different banks. A wave's load instruction covers G consecutive
+// units of each of its 64/G rows.
 //
 // Dataflow between stages without barriers: a stage whose x lies in an
 // earlier stage's fp16 output reads it from that stage's tagged buffer, in
 // which every element is one 32-bit word {fp16 value, 16-bit tag}; the tag
 // names the producing stage and the launch (epoch * (n + 1) + s + 1), so one
-// device-coherent store publishes value and readiness together. A consumer
-// copies the words into LDS and copies again only the 16-byte chunks whose
-// tags are not yet current: one memory round trip after the last producer's
-// store, instead of a grid barrier (arrive, gather, release) per stage. Each
-// workgroup keeps its own epoch word and advances it at the end of a launch,
-// so nothing is reset between runs and a captured graph replays as is. Every
-// wait is bounded: a wait that times out counts in the error word and the
-// workgroup goes on, so the grid always drains.
+// device-coherent store publishes value and readiness together. Producers
+// also raise a per-workgroup hint word after each stage; a consumer polls the
+// hints (one small round trip) and then copies the tagged words, copying
+// again only chunks whose tags are not yet current. Each workgroup keeps its
+// own epoch word and advances it at the end of a launch, so nothing is reset
+// between runs and a captured graph replays as is. Every wait is bounded: a
+// wait that times out counts in the error word and the workgroup goes on, so
+// the grid always drains.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -52,12 +53,10 @@ namespace kqd {
 using kq::StackStage;
 
 constexpr int CWAVES = kq::STACK_CWAVES;    // compute waves per workgroup
-constexpr int NT = kq::STACK_NT;            // compute lanes per workgroup
 constexpr int SLOT_DW = 20;                 // dwords per lane per register slot
-constexpr int PART_N = 4 * NT;              // partials of one round (largest CU)
 constexpr int LINE = 32;                    // words per sync line (128 bytes)
-constexpr int YROWS = kq::STACK_MAX_SHARE_ROWS;
 constexpr uint32_t SPIN_LIMIT = 1u << 20;
+constexpr int SC1 = 16;                     // cache-policy bit: device-scope coherent access
 
 // Load units per compute lane per round: one slot (SLOT_DW dwords).
 template <int FMT> struct ChainCU;
@@ -94,29 +93,39 @@ __device__ __forceinline__ StackStage load_stage(const StackStage* st, int s) {
   return d;
 }
 
-// A workgroup's share of a stage: rows [r0, r0 + rows), U units, rounds.
+// A workgroup's share of a stage: rows [r0, r0 + rows).
 struct Share {
-  int r0, rows, U, rounds;
+  int r0, rows;
 };
 
 __device__ __forceinline__ Share share_of(const StackStage& d, int b) {
   Share s;
   s.rows = d.rows_per + (b < d.rows_rem ? 1 : 0);
   s.r0 = b * d.rows_per + (b < d.rows_rem ? b : d.rows_rem);
-  s.U = s.rows * d.upr;
-  const int per = cu_of(d.fmt) * d.stride;
-  s.rounds = (s.U + per - 1) / per;
   return s;
+}
+
+// Lane groups of a stage: `groups` groups of G = 2^log2g lanes; wave w holds
+// groups w*gpw .. w*gpw + gpw - 1 (gpw = 64 / G).
+__device__ __forceinline__ int groups_of(int log2g) { return CWAVES << (6 - log2g); }
+
+// Steps of wave w in a stage with `rows` rows in this workgroup: its first
+// group has the most rows (ceil((rows - gamma0) / groups)), each kpr steps.
+__device__ __forceinline__ int wave_steps(const StackStage& d, int rows, int w) {
+  const int groups = groups_of(d.log2g);
+  const int gamma0 = w << (6 - d.log2g);
+  const int mcount = rows > gamma0 ? (rows - gamma0 + groups - 1) / groups : 0;
+  return mcount * d.kpr;
 }
 
 // ------------------------------------------------------------ compute waves
 
 // One register slot: four pieces of 20 bytes, piece i = a 16-byte load (v[i],
 // dwords 5i..5i+3) and a 4-byte load (e[i], dword 5i+4). Piece i of a round
-// holds bytes 20*p .. 20*p+19 of unit i >> log2ppu, p = i & (ppu - 1), so a
-// unit's bytes land in consecutive slot dwords: affine4 unit u (20 B) at dword
-// 5u, Q4_0 unit u (36 B) at dword 10u, the Q8_0 unit (68 B) at dword 0. The
-// load sequence is the same for every format; pieces past the share read 0.
+// holds bytes 20*p .. 20*p+19 of step i >> log2ppu's unit, p = i & (ppu - 1),
+// so a unit's bytes land in consecutive slot dwords: affine4 unit u (20 B) at
+// dword 5u, Q4_0 unit u (36 B) at dword 10u, the Q8_0 unit (68 B) at dword 0.
+// The load sequence is the same for every format; invalid pieces read 0.
 struct Slot {
   u32x4 v[4];
   uint32_t e[4];
@@ -161,23 +170,37 @@ __device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t bytes) {
   return r;
 }
 
-// Where the next weight round to load comes from.
+// Step position (row slot m, unit slot k) of a lane group walking a stage:
+// unit g + G*k of row gamma + groups*m; k runs over kpr per row.
+__device__ __forceinline__ void step_advance(int& m, int& k, int kpr) {
+  if (++k == kpr) {
+    k = 0;
+    ++m;
+  }
+}
+
+// Where the next weight round of this wave comes from.
 struct IssueCursor {
-  int s, j, rounds, U, cu, stride, log2ppu, ubytes;
+  int s, j, rounds, m, k;
+  int rows, upr, kpr, log2g, cu, log2ppu, ubytes;
   u32x4 rs;
 };
 
-// Move to the first stage >= c.s that has work for this workgroup.
-__device__ __forceinline__ void seek_stage(IssueCursor& c, const StackStage* st, int n, int b) {
+// Move to the first stage >= c.s in which this wave has work.
+__device__ __forceinline__ void seek_stage(IssueCursor& c, const StackStage* st, int n, int b, int w) {
   for (; c.s < n; ++c.s) {
     const StackStage d = load_stage(st, c.s);
     const Share sh = share_of(d, b);
-    if (sh.rounds > 0) {
-      c.j = 0;
-      c.rounds = sh.rounds;
-      c.U = sh.U;
-      c.cu = cu_of(d.fmt);
-      c.stride = d.stride;
+    const int cu = cu_of(d.fmt);
+    const int rounds = (wave_steps(d, sh.rows, w) + cu - 1) / cu;
+    if (rounds > 0) {
+      c.j = c.m = c.k = 0;
+      c.rounds = rounds;
+      c.rows = sh.rows;
+      c.upr = d.upr;
+      c.kpr = d.kpr;
+      c.log2g = d.log2g;
+      c.cu = cu;
       c.log2ppu = d.fmt == F_AFFINE4 ? 0 : (d.fmt == F_Q4_0 ? 1 : 2);
       c.ubytes = d.fmt == F_AFFINE4 ? 20 : (d.fmt == F_Q4_0 ? 36 : 68);
       c.rs = rsrc_words(d.W + (int64_t)sh.r0 * d.row_bytes, (uint32_t)sh.rows * (uint32_t)d.row_bytes);
@@ -186,27 +209,64 @@ __device__ __forceinline__ void seek_stage(IssueCursor& c, const StackStage* st,
   }
 }
 
-// Load the cursor's round into slot `sl` (zeros once the chain is exhausted,
-// and for lanes t >= stride) and advance the cursor. Always exactly 8 load
-// instructions.
-__device__ __forceinline__ void issue_next(Slot& sl, IssueCursor& c, const StackStage* st, int n, int b,
-                                           int t) {
-  const bool live = c.s < n && t < c.stride;
+// Load the cursor's round into slot `sl` (zeros once the chain is exhausted
+// and for steps past a lane group's rows) and advance the cursor. Always
+// exactly 8 load instructions.
+__device__ __forceinline__ void issue_next(Slot& sl, IssueCursor& c, const StackStage* st, int n, int b, int w,
+                                           int lane) {
+  const bool live = c.s < n;
+  // positions of the round's steps 0..3 and of the step after the round
+  int ms[5], ks[5];
+  ms[0] = c.m;
+  ks[0] = c.k;
+#pragma unroll
+  for (int u = 1; u < 5; ++u) {
+    ms[u] = ms[u - 1];
+    ks[u] = ks[u - 1];
+    step_advance(ms[u], ks[u], live ? c.kpr : 1);
+  }
+  const int gamma = (w << (6 - c.log2g)) + (lane >> c.log2g);
+  const int g = lane & ((1 << c.log2g) - 1);
+  const int groups = groups_of(c.log2g);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int u = i >> c.log2ppu, p = i & ((1 << c.log2ppu) - 1);
-    const int v = t + (c.j * c.cu + u) * c.stride;
-    const uint32_t off = live && v < c.U ? (uint32_t)v * (uint32_t)c.ubytes + 20u * (uint32_t)p : OOB;
+    const int row = gamma + groups * ms[u];
+    const int unit = g + (ks[u] << c.log2g);
+    const bool ok = live && row < c.rows && unit < c.upr;
+    const uint32_t off = ok ? (uint32_t)(row * c.upr + unit) * (uint32_t)c.ubytes + 20u * (uint32_t)p : OOB;
     asm_load_piece(sl.v[i], sl.e[i], off, c.rs);
   }
-  if (c.s < n && ++c.j >= c.rounds) {
-    ++c.s;
-    seek_stage(c, st, n, b);
+  if (live) {
+    c.m = c.cu == 4 ? ms[4] : (c.cu == 2 ? ms[2] : ms[1]);
+    c.k = c.cu == 4 ? ks[4] : (c.cu == 2 ? ks[2] : ks[1]);
+    if (++c.j >= c.rounds) {
+      ++c.s;
+      seek_stage(c, st, n, b, w);
+    }
   }
 }
 
-// Dot product of one load unit (dwords D) with this lane's activations: X
-// holds the unit's 16*UB activation dwords, SX its 2*UB half-block sums.
+// Activations of column c (16*UB dwords) from the rotated LDS layout: piece p
+// of column c is quad c*P + ((p + rot(c)) mod P), P = 4*UB pieces per column,
+// rot(c) = c >> 1 for P = 4 and c for P = 8.
+template <int UB>
+__device__ __forceinline__ void load_x_col(const uint32_t* xl, int c, uint32_t (&X)[32]) {
+  constexpr int P = 4 * UB;
+  const int rot = UB == 1 ? (c >> 1) : c;
+  const u32x4* q = reinterpret_cast<const u32x4*>(xl) + c * P;
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    const u32x4 t = q[(p + rot) & (P - 1)];
+    X[4 * p] = t.x;
+    X[4 * p + 1] = t.y;
+    X[4 * p + 2] = t.z;
+    X[4 * p + 3] = t.w;
+  }
+}
+
+// Dot product of one load unit (dwords D) with its activations: X holds the
+// unit's 16*UB activation dwords, SX its 2*UB half-block sums.
 template <int FMT>
 __device__ __forceinline__ float unit_partial(const uint32_t* D, const uint32_t (&X)[32], const float (&SX)[4]) {
   uint32_t A[16];
@@ -237,76 +297,73 @@ __device__ __forceinline__ float unit_partial(const uint32_t* D, const uint32_t 
   }
 }
 
+// Consumption side: stage s, round j of this wave's `rounds`, at step (m, k);
+// acc is the lane's running sum of its current row.
+struct ConsCursor {
+  int s, j, rounds, m, k, rows;
+  StackStage d;
+};
+
 template <int FMT>
-__device__ __forceinline__ void consume_fmt(const uint32_t (&raw)[SLOT_DW], const StackStage& d, int U,
-                                            int j, int t, const uint32_t (&X)[32], const float (&SX)[4],
-                                            float* part) {
-  constexpr int CU = ChainCU<FMT>::v;
+__device__ __forceinline__ void consume_fmt(const uint32_t (&raw)[SLOT_DW], ConsCursor& c, int w, int lane,
+                                            const uint32_t* xl, const float* xs, float* yacc, float& acc) {
+  constexpr int CU = ChainCU<FMT>::v, UB = Fmt<FMT>::UB;
   constexpr int UDW = SLOT_DW / CU;   // slot dwords per unit (see Slot)
+  const int log2g = c.d.log2g;
+  const int gamma = (w << (6 - log2g)) + (lane >> log2g);
+  const int g = lane & ((1 << log2g) - 1);
+  const int groups = groups_of(log2g);
 #pragma unroll
   for (int i = 0; i < CU; ++i) {
-    const int v = t + (j * CU + i) * d.stride;
-    if (t < d.stride && v < U) part[i * d.stride + t] = unit_partial<FMT>(raw + i * UDW, X, SX);
+    const int row = gamma + groups * c.m;
+    const int unit = g + (c.k << log2g);
+    if (row < c.rows && unit < c.d.upr) {
+      uint32_t X[32];
+      float SX[4];
+      load_x_col<UB>(xl, unit, X);
+#pragma unroll
+      for (int h = 0; h < 2 * UB; ++h) SX[h] = xs[unit * 2 * UB + h];
+      acc += unit_partial<FMT>(raw + i * UDW, X, SX);
+    }
+    if (c.k == c.d.kpr - 1) {   // the group's row is complete (uniform over the wave)
+      for (int o = 1; o < (1 << log2g); o <<= 1) acc += __shfl_xor(acc, o, 64);
+      if (g == 0 && row < c.rows) yacc[row] = acc;
+      acc = 0.0f;
+    }
+    step_advance(c.m, c.k, c.d.kpr);
     // one unit at a time: interleaving units would hold several units'
-    // dequantized weights at once and spill the slots
+    // activations and dequantized weights at once and spill the slots
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
 template <int FMASK>
-__device__ __forceinline__ void consume(Slot& sl, const StackStage& d, int U, int j, int t,
-                                        const uint32_t (&X)[32], const float (&SX)[4], float* part) {
+__device__ __forceinline__ void consume(Slot& sl, ConsCursor& c, int w, int lane, const uint32_t* xl,
+                                        const float* xs, float* yacc, float& acc) {
   wait_oldest_slot(sl);
   uint32_t raw[SLOT_DW];
   slot_dwords(sl, raw);
-  if ((FMASK & (1 << F_AFFINE4)) && d.fmt == F_AFFINE4) consume_fmt<F_AFFINE4>(raw, d, U, j, t, X, SX, part);
-  else if ((FMASK & (1 << F_Q4_0)) && d.fmt == F_Q4_0) consume_fmt<F_Q4_0>(raw, d, U, j, t, X, SX, part);
-  else if ((FMASK & (1 << F_Q8_0)) && d.fmt == F_Q8_0) consume_fmt<F_Q8_0>(raw, d, U, j, t, X, SX, part);
+  const int fmt = c.d.fmt;
+  if ((FMASK & (1 << F_AFFINE4)) && fmt == F_AFFINE4) consume_fmt<F_AFFINE4>(raw, c, w, lane, xl, xs, yacc, acc);
+  else if ((FMASK & (1 << F_Q4_0)) && fmt == F_Q4_0) consume_fmt<F_Q4_0>(raw, c, w, lane, xl, xs, yacc, acc);
+  else if ((FMASK & (1 << F_Q8_0)) && fmt == F_Q8_0) consume_fmt<F_Q8_0>(raw, c, w, lane, xl, xs, yacc, acc);
 }
 
-// Consumption side of the round sequence: stage s, round j of its `rounds`.
-struct ConsCursor {
-  int s, j, rounds;
-  StackStage d;
-  Share sh;
-};
-
-// This lane's activations for stage d: its column's 16*UB dwords of x from
-// LDS and their half-block sums (lanes t >= stride have no column).
-__device__ __forceinline__ void load_column(const StackStage& d, int t, const uint32_t* xl, uint32_t (&X)[32],
-                                            float (&SX)[4]) {
-  const int ub = d.fmt == F_AFFINE4 ? 1 : 2;
-  const int col = t < d.stride ? t % d.upr : 0;
-  const u32x4* p = reinterpret_cast<const u32x4*>(xl + col * 16 * ub);
-#pragma unroll
-  for (int v = 0; v < 8; ++v) {
-    const u32x4 w = v < 4 * ub ? p[v] : u32x4{0u, 0u, 0u, 0u};
-    X[4 * v] = w.x;
-    X[4 * v + 1] = w.y;
-    X[4 * v + 2] = w.z;
-    X[4 * v + 3] = w.w;
-  }
-#pragma unroll
-  for (int h = 0; h < 4; ++h) {
-    float s = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) s = dot2(X[8 * h + i], ONES, s);
-    SX[h] = s;
-  }
-}
-
-// Move to the next round, entering stages (one workgroup barrier each, after
-// which their x is in LDS) until one has work. False once every stage is done.
-__device__ __forceinline__ bool next_round(ConsCursor& c, const StackStage* st, int n, int b, int t,
-                                           const uint32_t* xl, uint32_t (&X)[32], float (&SX)[4]) {
+// Move to the next round, passing stage boundaries: every stage, with or
+// without work for this wave, is one barrier after its x is in LDS and one
+// after its rows are in yacc. False once every stage is done.
+__device__ __forceinline__ bool next_round(ConsCursor& c, const StackStage* st, int n, int b, int w, float& acc) {
   while (c.j >= c.rounds) {
+    if (c.s >= 0) __syncthreads();   // stage s done: its rows are in yacc
     if (++c.s >= n) return false;
     c.d = load_stage(st, c.s);
-    c.sh = share_of(c.d, b);
-    c.rounds = c.sh.rounds;
-    c.j = 0;
-    __syncthreads();   // x of stage s is in LDS
-    if (c.rounds > 0) load_column(c.d, t, xl, X, SX);
+    const Share sh = share_of(c.d, b);
+    c.rows = sh.rows;
+    const int cu = cu_of(c.d.fmt);
+    c.rounds = (wave_steps(c.d, sh.rows, w) + cu - 1) / cu;
+    c.j = c.m = c.k = 0;
+    acc = 0.0f;
+    __syncthreads();   // x of stage s and its sums are in LDS
   }
   return true;
 }
@@ -315,104 +372,56 @@ __device__ __forceinline__ bool next_round(ConsCursor& c, const StackStage* st, 
 // the one loaded longest ago.
 template <int FMASK>
 __device__ __forceinline__ void compute_wave(const StackStage* st, int n, int b, const uint32_t* xl,
-                                             float* part) {
-  const int t = threadIdx.x;   // 0 .. NT-1
+                                             const float* xs, float* yacc) {
+  const int w = wave_id(), lane = threadIdx.x & 63;
   Slot A, B, C;
   IssueCursor ic;
-  ic.s = 0;
-  ic.j = ic.rounds = ic.U = ic.cu = ic.stride = ic.log2ppu = ic.ubytes = 0;
+  ic.s = ic.j = ic.rounds = ic.m = ic.k = 0;
+  ic.rows = ic.upr = ic.kpr = ic.log2g = ic.cu = ic.log2ppu = ic.ubytes = 0;
   ic.rs = rsrc_words(st, 0u);   // empty range: every load reads zero
-  seek_stage(ic, st, n, b);
-  issue_next(A, ic, st, n, b, t);
-  issue_next(B, ic, st, n, b, t);
-  issue_next(C, ic, st, n, b, t);
+  seek_stage(ic, st, n, b, w);
+  issue_next(A, ic, st, n, b, w, lane);
+  issue_next(B, ic, st, n, b, w, lane);
+  issue_next(C, ic, st, n, b, w, lane);
   ConsCursor cc;
   cc.s = -1;
-  cc.j = cc.rounds = 0;
-  uint32_t X[32];
-  float SX[4];
-  int q = 0;
+  cc.j = cc.rounds = cc.m = cc.k = cc.rows = 0;
+  float acc = 0.0f;
   for (;;) {
-    if (!next_round(cc, st, n, b, t, xl, X, SX)) break;
-    consume<FMASK>(A, cc.d, cc.sh.U, cc.j, t, X, SX, part + (q & 1) * PART_N);
-    issue_next(A, ic, st, n, b, t);
-    ++q;
+    if (!next_round(cc, st, n, b, w, acc)) break;
+    consume<FMASK>(A, cc, w, lane, xl, xs, yacc, acc);
+    issue_next(A, ic, st, n, b, w, lane);
     ++cc.j;
-    __syncthreads();   // partials of this round are in LDS
-    if (!next_round(cc, st, n, b, t, xl, X, SX)) break;
-    consume<FMASK>(B, cc.d, cc.sh.U, cc.j, t, X, SX, part + (q & 1) * PART_N);
-    issue_next(B, ic, st, n, b, t);
-    ++q;
+    if (!next_round(cc, st, n, b, w, acc)) break;
+    consume<FMASK>(B, cc, w, lane, xl, xs, yacc, acc);
+    issue_next(B, ic, st, n, b, w, lane);
     ++cc.j;
-    __syncthreads();
-    if (!next_round(cc, st, n, b, t, xl, X, SX)) break;
-    consume<FMASK>(C, cc.d, cc.sh.U, cc.j, t, X, SX, part + (q & 1) * PART_N);
-    issue_next(C, ic, st, n, b, t);
-    ++q;
+    if (!next_round(cc, st, n, b, w, acc)) break;
+    consume<FMASK>(C, cc, w, lane, xl, xs, yacc, acc);
+    issue_next(C, ic, st, n, b, w, lane);
     ++cc.j;
-    __syncthreads();
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no load outlives the wave
 }
 
 // ------------------------------------------------------------- control wave
 
-// Sum the partials of one round into the share's row accumulators: units
-// [R0, R1) of the share, partial of unit u at part[u - R0]. Lanes split rows
-// (L lanes per row, L a power of two); each lane sums a contiguous run in unit
-// order with four interleaved accumulators, then the L lanes combine by a
-// fixed butterfly. The order depends only on the shapes: deterministic.
-__device__ __forceinline__ void reduce_round(const float* part, float* yacc, int R0, int R1, int upr,
-                                             int lane) {
-  const int rA = R0 / upr, rB = (R1 - 1) / upr;
-  const int nrows = rB - rA + 1;
-  int log2l = 0;
-  while (log2l < 6 && (nrows << (log2l + 1)) <= 64) ++log2l;
-  const int L = 1 << log2l, rpp = 64 >> log2l;
-  for (int base = 0; base < nrows; base += rpp) {
-    const int rr = base + (lane >> log2l), sub = lane & (L - 1);
-    float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
-    if (rr < nrows) {
-      const int r = rA + rr;
-      const int a = max(R0, r * upr), e = min(R1, (r + 1) * upr);
-      const int chunk = (e - a + L - 1) >> log2l;
-      const int u0 = a + sub * chunk, u1 = min(e, u0 + chunk);
-      const float* p = part - R0;
-      int u = u0;
-      for (; u + 4 <= u1; u += 4) {
-        s0 += p[u];
-        s1 += p[u + 1];
-        s2 += p[u + 2];
-        s3 += p[u + 3];
-      }
-      for (; u < u1; ++u) s0 += p[u];
-    }
-    float sum = (s0 + s1) + (s2 + s3);
-    for (int o = 1; o < L; o <<= 1) sum += __shfl_xor(sum, o, 64);
-    if (rr < nrows && sub == 0) yacc[rA + rr] += sum;
-  }
-}
-
-constexpr int SC1 = 16;   // cache-policy bit: device-scope coherent access
-
-// Copy x (K fp16, from outside the chain) into LDS.
-__device__ __forceinline__ void stage_x(const uint16_t* x, int K, uint32_t* xl, int lane) {
-  const int n16 = K / 8;
+// Copy `n16` 16-byte chunks from `src` (global) to `stg` (LDS), reading at the
+// device coherence point; chunk i lands at stg + 4i dwords.
+__device__ __forceinline__ void dma_chunks(const void* src, int n16, uint32_t* stg, int lane) {
   for (int i = lane; i < n16; i += 64) {
-    __builtin_amdgcn_global_load_lds((glb_void_t*)(reinterpret_cast<const u32x4*>(x) + i),
-                                     (lds_void_t*)(xl + 4 * (i - lane)), 16, 0, SC1);
+    __builtin_amdgcn_global_load_lds((glb_void_t*)(reinterpret_cast<const u32x4*>(src) + i),
+                                     (lds_void_t*)(stg + 4 * (i - lane)), 16, 0, SC1);
   }
   wait_vmem();
 }
 
-// Copy the K tagged words at `src` into LDS x as fp16, once every word carries
-// `tag`. Chunk i (words 4i..4i+3) of lane i % 64 is fetched (LDS DMA, at the
-// device coherence point) into the staging area; chunks whose four tags are
-// current are unpacked into x, the others are fetched again. False if the wait
-// timed out (x then holds whatever had arrived).
-__device__ __forceinline__ bool ingest_tagged(const uint32_t* src, int K, uint32_t tag, uint32_t* xl,
-                                              uint32_t* stg, uint32_t* err, int lane, bool broken) {
-  const int nch = K / 4;
+// Bring the K tagged words at `src` into the staging area, once every word
+// carries `tag`: all chunks first, then only the chunks not yet current, with
+// a short pause between passes. False if the wait timed out.
+__device__ __forceinline__ bool fetch_tagged(const uint32_t* src, int K, uint32_t tag, uint32_t* stg,
+                                             uint32_t* err, int lane, bool broken) {
+  const int nch = K / 4;   // 16-byte chunks of 4 words
   const int rounds = (nch + 63) / 64;
   uint64_t pend = 0;
   for (int k = 0; k < rounds; ++k)
@@ -427,14 +436,9 @@ __device__ __forceinline__ bool ingest_tagged(const uint32_t* src, int K, uint32
     wait_vmem();
     for (int k = 0; k < rounds; ++k) {
       if ((pend >> k) & 1ull) {
-        const int i = 64 * k + lane;
-        const u32x4 w = *reinterpret_cast<const u32x4*>(stg + 4 * i);
-        if ((w.x >> 16) == tag && (w.y >> 16) == tag && (w.z >> 16) == tag && (w.w >> 16) == tag) {
-          uint32_t* o = xl + 2 * i;
-          o[0] = perm(w.y, w.x, 0x05040100u);   // fp16 of words 4i, 4i+1
-          o[1] = perm(w.w, w.z, 0x05040100u);
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + 4 * (64 * k + lane));
+        if ((v.x >> 16) == tag && (v.y >> 16) == tag && (v.z >> 16) == tag && (v.w >> 16) == tag)
           pend &= ~(1ull << k);
-        }
       }
     }
     if (!__any(pend != 0)) return true;
@@ -442,51 +446,111 @@ __device__ __forceinline__ bool ingest_tagged(const uint32_t* src, int K, uint32
       if (!broken && lane == 0) add_dev(err, 1u);
       return false;
     }
+    __builtin_amdgcn_s_sleep(2);
   }
 }
 
-__device__ __forceinline__ void control_wave(const StackStage* st, int n, uint32_t* sync, int b, uint32_t* xl,
-                                             uint32_t* stg, const float* part, float* yacc) {
+// Wait until every workgroup's hint word has reached `tag32` (it finished the
+// stage with that tag). One batched round trip per poll. False on timeout.
+__device__ __forceinline__ bool wait_hints(const uint32_t* hint, int nb, uint32_t tag32, uint32_t* err, int lane) {
+  const rsrc_t hs = make_rsrc(hint, (uint32_t)nb * LINE * 4u);
+  uint32_t spins = 0;
+  for (;;) {
+    // plain loads at the device coherence point (SC1), which the compiler may
+    // batch; the memory clobber makes each poll load again
+    asm volatile("" ::: "memory");
+    bool behind = false;
+#pragma unroll
+    for (int k = 0; k < kq::STACK_MAX_WG / 64; ++k) {
+      const int i = lane + 64 * k;
+      const uint32_t v = __builtin_amdgcn_raw_buffer_load_b32(hs, (uint32_t)i * LINE * 4u, 0, SC1);
+      behind |= i < nb && (int32_t)(v - tag32) < 0;
+    }
+    if (!__any(behind)) return true;
+    if (++spins > SPIN_LIMIT) {
+      if (lane == 0) add_dev(err, 1u);
+      return false;
+    }
+  }
+}
+
+// Turn the staged x (plain fp16, or tagged words) into the rotated LDS layout
+// (see load_x_col) and form the half-block sums xs[h] of elements 16h..16h+15.
+__device__ __forceinline__ void place_x(const uint32_t* stg, bool tagged, int K, int ub, uint32_t* xl, float* xs,
+                                        int lane) {
+  const int P = 4 * ub;
+  u32x4* xq = reinterpret_cast<u32x4*>(xl);
+  for (int h = lane; h < K / 16; h += 64) {
+    float sum = 0.0f;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int Q = 2 * h + half;   // quad of x: elements 8Q .. 8Q+7
+      u32x4 v;
+      if (tagged) {
+        const u32x4* t = reinterpret_cast<const u32x4*>(stg + 8 * Q);
+        const u32x4 a = t[0], c = t[1];
+        v.x = perm(a.y, a.x, 0x05040100u);   // fp16 of words 8Q, 8Q+1
+        v.y = perm(a.w, a.z, 0x05040100u);
+        v.z = perm(c.y, c.x, 0x05040100u);
+        v.w = perm(c.w, c.z, 0x05040100u);
+      } else {
+        v = *reinterpret_cast<const u32x4*>(stg + 4 * Q);
+      }
+      sum = dot2(v.x, ONES, sum);
+      sum = dot2(v.y, ONES, sum);
+      sum = dot2(v.z, ONES, sum);
+      sum = dot2(v.w, ONES, sum);
+      const int c = Q / P, p = Q - c * P;
+      const int rot = ub == 1 ? (c >> 1) : c;
+      xq[c * P + ((p + rot) & (P - 1))] = v;
+    }
+    xs[h] = sum;
+  }
+}
+
+__device__ __forceinline__ void control_wave(const StackStage* st, int n, uint32_t* sync, int b, int nb,
+                                             uint32_t* xl, float* xs, uint32_t* stg, const float* yacc) {
   const int lane = threadIdx.x & 63;
   uint32_t* err = sync + kq::STACK_ERR_WORD;
   uint32_t* epoch_word = sync + kq::STACK_EPOCH_WORD + (int64_t)b * LINE;
-  for (int r = lane; r < YROWS; r += 64) yacc[r] = 0.0f;
+  uint32_t* hints = sync + kq::STACK_HINT_WORD;
   const uint32_t epoch = ld_dev(epoch_word);
-  const uint32_t tag_base = epoch * (uint32_t)(n + 1) + 1u;   // tag of stage s: (tag_base + s) mod 2^16
+  const uint32_t tag_base = epoch * (uint32_t)(n + 1) + 1u;   // tag of stage s: tag_base + s
   bool broken = false;
-  int q = 0;
   for (int s = 0; s < n; ++s) {
     const StackStage d = load_stage(st, s);
     const Share sh = share_of(d, b);
-    if (sh.rounds > 0) {
+    if (sh.rows > 0) {
+      const int ub = d.fmt == F_AFFINE4 ? 1 : 2;
       if (d.ll_in) {
-        const uint32_t tag = (tag_base + (uint32_t)d.dep) & 0xffffu;
-        if (!ingest_tagged(d.ll_in, d.K, tag, xl, stg, err, lane, broken)) broken = true;
+        const uint32_t dep_tag = tag_base + (uint32_t)d.dep;
+        if (!broken && !wait_hints(hints, nb, dep_tag, err, lane)) broken = true;
+        const uint32_t* src = d.ll_in + (int64_t)(b % kq::STACK_LL_COPIES) * d.ll_in_stride;
+        if (!fetch_tagged(src, d.K, dep_tag & 0xffffu, stg, err, lane, broken)) broken = true;
+        place_x(stg, true, d.K, ub, xl, xs, lane);
       } else {
-        stage_x(d.x, d.K, xl, lane);
+        dma_chunks(d.x, d.K / 8, stg, lane);
+        place_x(stg, false, d.K, ub, xl, xs, lane);
       }
     }
     __syncthreads();   // x of stage s is in LDS
-    const int per = cu_of(d.fmt) * d.stride;
-    for (int j = 0; j < sh.rounds; ++j) {
-      __syncthreads();   // the compute waves' partials of round j are in LDS
-      const int R0 = j * per;
-      reduce_round(part + (q & 1) * PART_N, yacc, R0, min(sh.U, R0 + per), d.upr, lane);
-      ++q;
-    }
+    __syncthreads();   // the compute waves have left every row of the share in yacc
     // Outputs: y and y16 with ordinary stores (read after the launch); the
     // tagged copy for later stages with device-coherent stores, value and tag
-    // in one word, so a reader on any XCD sees both or neither.
+    // in one word, so a reader on any XCD sees both or neither; then the hint.
     const uint32_t out_tag = ((tag_base + (uint32_t)s) & 0xffffu) << 16;
     for (int r = lane; r < sh.rows; r += 64) {
       const float v = yacc[r];
-      yacc[r] = 0.0f;
       const int64_t row = sh.r0 + r;
       d.y[row] = v;
       const uint32_t h = f2h_bits(v);
       if (d.y16) d.y16[row] = (uint16_t)h;
-      if (d.ll_out) st_dev(d.ll_out + row, h | out_tag);
+      if (d.ll_out) {
+#pragma unroll
+        for (int c = 0; c < kq::STACK_LL_COPIES; ++c) st_dev(d.ll_out + (int64_t)c * d.ll_out_stride + row, h | out_tag);
+      }
     }
+    if (lane == 0) st_dev(hints + (int64_t)b * LINE, tag_base + (uint32_t)s);
   }
   wait_vmem();
   if (lane == 0) st_dev(epoch_word, epoch + 1u);
@@ -496,15 +560,15 @@ template <int FMASK>
 __global__ __launch_bounds__(64 * (CWAVES + 1)) void k_stack(const StackStage* __restrict__ st, int n,
                                                             uint32_t* __restrict__ sync, int kmax) {
   extern __shared__ u32x4 lds4[];
-  uint32_t* xl = reinterpret_cast<uint32_t*>(lds4);   // x: kmax/2 dwords
-  uint32_t* stg = xl + kmax / 2;                        // tagged words: kmax
-  float* part = reinterpret_cast<float*>(stg + kmax);   // 2 x PART_N
-  float* yacc = part + 2 * PART_N;                      // YROWS
+  uint32_t* xl = reinterpret_cast<uint32_t*>(lds4);      // x, rotated: kmax/2 dwords
+  float* xs = reinterpret_cast<float*>(xl + kmax / 2);     // half-block sums: kmax/16
+  uint32_t* stg = reinterpret_cast<uint32_t*>(xs + kmax / 16);   // staging: kmax dwords
+  float* yacc = reinterpret_cast<float*>(stg + kmax);      // rows of the share
   const int b = blockIdx.x;
   if (wave_id() == CWAVES)
-    control_wave(st, n, sync, b, xl, stg, part, yacc);
+    control_wave(st, n, sync, b, gridDim.x, xl, xs, stg, yacc);
   else
-    compute_wave<FMASK>(st, n, b, xl, part);
+    compute_wave<FMASK>(st, n, b, xl, xs, yacc);
 }
 
 }  // namespace kqd
@@ -512,6 +576,20 @@ __global__ __launch_bounds__(64 * (CWAVES + 1)) void k_stack(const StackStage* _
 namespace kq {
 
 using namespace kqd;
+
+int stack_log2g(int64_t rows_max, int upr) {
+  int best = 2;
+  int64_t best_steps = -1;
+  for (int l = 2; l <= 6; ++l) {
+    const int64_t groups = (int64_t)STACK_CWAVES << (6 - l);
+    const int64_t steps = (rows_max + groups - 1) / groups * ((upr + (1 << l) - 1) >> l);
+    if (best_steps < 0 || steps < best_steps) {
+      best = l;
+      best_steps = steps;
+    }
+  }
+  return best;
+}
 
 int stack_device_info(int* cus) {
   int dev = 0;
@@ -533,7 +611,7 @@ int read_from_device(void* dst, const void* src, int64_t bytes, hipStream_t stre
 }
 
 int64_t stack_lds_bytes(int kmax) {
-  return ((int64_t)kmax / 2 + kmax + 2 * PART_N + YROWS) * 4;
+  return ((int64_t)kmax / 2 + kmax / 16 + kmax + STACK_MAX_SHARE_ROWS) * 4;
 }
 
 namespace {

@@ -208,7 +208,7 @@ def test_stack_dataflow_rules():
     # stage 1 reads the first 4096 values of stage 0's fp16 output: stage 0's
     # 6144 outputs get a tagged copy (4 bytes each) in the plan
     chained = nbytes(s0, dict(s0, x=0x300000, y=0x210000, y16=None, N=2560, K=4096))
-    assert chained - free == 6144 * 4
+    assert chained - free == 6144 * 4 * 8    # 8 copies, read by different workgroups
     # reading from the middle of it (element 2048, a multiple of 4) is allowed
     assert nbytes(s0, dict(s0, x=0x300000 + 2 * 2048, y=0x210000, y16=None, N=2560, K=4096)) == chained
     # ... from element 2 is not (the tagged words are read in 16-byte chunks)
