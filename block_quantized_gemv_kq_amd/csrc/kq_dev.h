@@ -59,6 +59,43 @@ __device__ __forceinline__ int wave_id() {
   return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 }
 
+// v plus the value of lane ^ 16 (permlane16 swap) or lane ^ 32 (permlane32
+// swap) as one fp32 add. The swap is written out: this compiler reads the
+// first result register for both results when one instruction consumes the
+// two results of the swap builtin. s_nop 1 gives the swap's VGPR reads the
+// wait states they need after a VALU write.
+__device__ __forceinline__ float add_lane_xor16(float v) {
+  uint32_t a = __builtin_bit_cast(uint32_t, v), b = a;
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
+}
+__device__ __forceinline__ float add_lane_xor32(float v) {
+  uint32_t a = __builtin_bit_cast(uint32_t, v), b = a;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over the G lanes of a group (G a power of two, groups aligned): a
+// butterfly in fixed order, so it is deterministic and every lane of the group
+// ends with the same value. Partners 1 and 2 apart come through DPP quad
+// permutes; once each quad (each 8) holds one value, the row half-mirror
+// (mirror) pairs it with the neighbouring quad (8); the gfx950 permlane swaps
+// give the lane 16 and 32 apart. No step goes through LDS.
+__device__ __forceinline__ float group_sum(float v, int G) {
+  if (G >= 2) v += dpp_f<0xB1>(v);    // quad_perm [1,0,3,2]: lane ^ 1
+  if (G >= 4) v += dpp_f<0x4E>(v);    // quad_perm [2,3,0,1]: lane ^ 2
+  if (G >= 8) v += dpp_f<0x141>(v);   // row_half_mirror: the other quad of 8
+  if (G >= 16) v += dpp_f<0x140>(v);  // row_mirror: the other 8 of 16
+  if (G >= 32) v = add_lane_xor16(v);
+  if (G >= 64) v = add_lane_xor32(v);
+  return v;
+}
+
 __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
   return __builtin_amdgcn_perm(hi, lo, sel);
 }
@@ -252,12 +289,10 @@ __device__ __forceinline__ void valu_tile(rsrc_t rs, uint32_t row_bytes, int uni
       }
     }
   }
-  for (int off = 1; off < G; off <<= 1) {
 #pragma unroll
-    for (int r = 0; r < R; ++r)
+  for (int r = 0; r < R; ++r)
 #pragma unroll
-      for (int m = 0; m < MT; ++m) acc[r][m] += __shfl_xor(acc[r][m], off, 64);
-  }
+    for (int m = 0; m < MT; ++m) acc[r][m] = group_sum(acc[r][m], G);
 }
 
 
@@ -480,14 +515,10 @@ __device__ __forceinline__ float consume_units_raw(const uint32_t* raw, const ui
   return acc;
 }
 
-// Sum over the G lanes of a group (butterfly, fixed order: deterministic and
-// every lane of the group ends with the same value).
 template <int MT>
 __device__ __forceinline__ void group_reduce(float (&acc)[MT], int G) {
-  for (int off = 1; off < G; off <<= 1) {
 #pragma unroll
-    for (int m = 0; m < MT; ++m) acc[m] += __shfl_xor(acc[m], off, 64);
-  }
+  for (int m = 0; m < MT; ++m) acc[m] = group_sum(acc[m], G);
 }
 
 }  // namespace kqd

@@ -185,7 +185,7 @@ __global__ __launch_bounds__(256) void k_gemv_generic(const uint8_t* __restrict_
         }
       }
     }
-    for (int off = 1; off < 64; off <<= 1) acc += __shfl_xor(acc, off, 64);
+    acc = group_sum(acc, 64);
     if (lane == 0) y[(int64_t)m * N + row] = acc;
   }
 }

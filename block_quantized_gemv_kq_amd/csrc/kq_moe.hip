@@ -242,7 +242,7 @@ __global__ __launch_bounds__(256) void k_moe_generic(const uint8_t* __restrict__
       }
     }
   }
-  for (int off = 1; off < 64; off <<= 1) acc += __shfl_xor(acc, off, 64);
+  acc = group_sum(acc, 64);
   if (lane == 0) y_slot[(int64_t)p * N + row] = acc;
 }
 

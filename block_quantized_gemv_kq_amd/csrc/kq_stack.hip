@@ -326,7 +326,7 @@ __device__ __forceinline__ void consume_fmt(const uint32_t (&raw)[SLOT_DW], Cons
       acc += unit_partial<FMT>(raw + i * UDW, X, SX);
     }
     if (c.k == c.d.kpr - 1) {   // the group's row is complete (uniform over the wave)
-      for (int o = 1; o < (1 << log2g); o <<= 1) acc += __shfl_xor(acc, o, 64);
+      acc = group_sum(acc, 1 << log2g);
       if (g == 0 && row < c.rows) yacc[row] = acc;
       acc = 0.0f;
     }
