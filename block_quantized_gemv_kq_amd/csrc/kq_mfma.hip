@@ -13,16 +13,23 @@
 //   y[m][n] += s[n] * D + (b[n] - 1024 s[n]) * Dx    (affine4, per block)
 //   (Q4_0: c = -1032 d; Q8_0: 1152 + q, c = -1152 d; no bias)
 //
-// Work split: a workgroup owns 16 weight rows; its 8 waves split K into
-// contiguous ranges of 4-block groups and sum their partial results in LDS in
-// a fixed order (deterministic). A lane (n = lane % 16, g = lane / 16) loads
-// block b0 + g of row n, then four lanes exchange 16-lane groups with
-// permlane swaps so that lane group g holds quant dword g of all four blocks:
-// the MFMA's 32 k of a block are, for lane group g, the elements 4g..4g+3 and
-// 16+4g..19+4g (both nibbles of byte 4g..4g+3), and the activations use the
-// same order.
+// Work split: a workgroup owns 16 weight rows; its S waves (up to 16) split K
+// into contiguous ranges of 4-block groups and sum their partial results in
+// LDS in a fixed order (deterministic). Decode shapes have few rows and short
+// K ranges per wave, so a wave is latency-bound unless many loads are in
+// flight: each wave issues the loads of its first P groups (weights and
+// activations alike, as range-checked buffer loads, so invalid rows, columns
+// and blocks read zero with no branch) before any arithmetic, and refills a
+// group's registers as soon as it has consumed it. A lane (n = lane % 16,
+// g = lane / 16) loads block b0 + g of row n, then four lanes exchange 16-lane
+// groups with permlane swaps so that lane group g holds quant dword g of all
+// four blocks: the MFMA's 32 k of a block are, for lane group g, the elements
+// 4g..4g+3 and 16+4g..19+4g (both nibbles of byte 4g..4g+3), and the
+// activations use the same order.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include "kq_dev.h"
 #include "kq_internal.h"
@@ -32,8 +39,6 @@ namespace kqd {
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-constexpr int MF_WAVES = 8;
 
 __device__ __forceinline__ half8_t as_half8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   u32x4 v = {a, b, c, d};
@@ -94,34 +99,105 @@ struct GroupX {
   u32x2 lo[4], hi[4];
 };
 
-__device__ __forceinline__ void load_group_x(const uint16_t* __restrict__ xcol, bool col_ok, int b0,
-                                             int nblk, int g, GroupX& gx) {
+// `xs` covers the M columns of x; `xoff` is this lane's column start in bytes,
+// or OOB for a column past M (all its loads read zero).
+__device__ __forceinline__ void load_group_x(rsrc_t xs, uint32_t xoff, int b0, int nblk, int g, GroupX& gx) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int b = b0 + j;
-    if (col_ok && b < nblk) {
-      const u32x2* p = reinterpret_cast<const u32x2*>(xcol + 32 * b + 4 * g);
-      gx.lo[j] = p[0];
-      gx.hi[j] = p[4];   // + 16 elements
+    const uint32_t o = b < nblk ? xoff + 64u * (uint32_t)b + 8u * (uint32_t)g : OOB;
+    gx.lo[j] = __builtin_amdgcn_raw_buffer_load_b64(xs, o, 0, 0);
+    gx.hi[j] = __builtin_amdgcn_raw_buffer_load_b64(xs, o + 32u, 0, 0);
+  }
+}
+
+// One 4-block group of one row tile against T column tiles: exchange the
+// loaded blocks into MFMA operand order, dequantize, multiply, fix up.
+template <int FMT, int T>
+__device__ __forceinline__ void consume_group(const GroupRaw<FMT>& cur, const GroupX (&cx)[T], uint32_t roff,
+                                              int gi, int g, int nblk, float4_t (&acc)[T]) {
+  const half8_t ones = as_half8(ONES, ONES, ONES, ONES);
+  uint32_t hdr, q0, q1, q2, q3, p0 = 0, p1 = 0, p2 = 0, p3 = 0;
+  if constexpr (FMT == F_AFFINE4) {
+    hdr = cur.D[0];
+    q0 = cur.D[1]; q1 = cur.D[2]; q2 = cur.D[3]; q3 = cur.D[4];
+  } else {
+    const uint32_t r2 = ((roff + (uint32_t)(4 * gi + g) * Fmt<FMT>::BB + 2u) & 3u) * 8u;  // bit shift 0/16
+    hdr = r2 ? (cur.D[1] & 0xffffu) : (cur.D[0] >> 16);
+    const uint32_t sh = r2 >> 3;   // byte shift 0 or 2
+    q0 = __builtin_amdgcn_alignbyte(cur.D[2], cur.D[1], sh);
+    q1 = __builtin_amdgcn_alignbyte(cur.D[3], cur.D[2], sh);
+    q2 = __builtin_amdgcn_alignbyte(cur.D[4], cur.D[3], sh);
+    q3 = __builtin_amdgcn_alignbyte(cur.D[5], cur.D[4], sh);
+    if constexpr (FMT == F_Q8_0) {
+      p0 = __builtin_amdgcn_alignbyte(cur.D[6], cur.D[5], sh);
+      p1 = __builtin_amdgcn_alignbyte(cur.D[7], cur.D[6], sh);
+      p2 = __builtin_amdgcn_alignbyte(cur.D[8], cur.D[7], sh);
+      p3 = __builtin_amdgcn_alignbyte(cur.D[9], cur.D[8], sh);
+    }
+  }
+  transpose4(q0, q1, q2, q3);
+  if constexpr (FMT == F_Q8_0) transpose4(p0, p1, p2, p3);
+  uint32_t h0 = hdr, h1 = hdr, h2 = hdr, h3 = hdr;
+  transpose4(h0, h1, h2, h3);
+  const uint32_t qs[4] = {q0, q1, q2, q3};
+  const uint32_t ps[4] = {p0, p1, p2, p3};
+  const uint32_t hs[4] = {h0, h1, h2, h3};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (4 * gi + j >= nblk) break;      // uniform
+    // B operand: 8 fp16 (offset + q) for elements {4g..4g+3, 16+4g..19+4g}
+    uint32_t b0, b1, b2, b3;
+    if constexpr (FMT == F_Q8_0) {
+      const uint32_t u = qs[j] ^ 0x80808080u, v = ps[j] ^ 0x80808080u;
+      b0 = perm(MAGIC, u, SEL_LO); b1 = perm(MAGIC, u, SEL_HI);
+      b2 = perm(MAGIC, v, SEL_LO); b3 = perm(MAGIC, v, SEL_HI);
     } else {
-      gx.lo[j] = u32x2{0u, 0u};
-      gx.hi[j] = u32x2{0u, 0u};
+      const uint32_t lo = qs[j] & 0x0F0F0F0Fu, hi = (qs[j] >> 4) & 0x0F0F0F0Fu;
+      b0 = perm(MAGIC, lo, SEL_LO); b1 = perm(MAGIC, lo, SEL_HI);
+      b2 = perm(MAGIC, hi, SEL_LO); b3 = perm(MAGIC, hi, SEL_HI);
+    }
+    const half8_t B = as_half8(b0, b1, b2, b3);
+    const float sc = h2f(hs[j]);
+    float c;
+    if constexpr (FMT == F_AFFINE4) c = __builtin_fmaf(-1024.0f, sc, h2f(hs[j] >> 16));
+    else if constexpr (FMT == F_Q4_0) c = -1032.0f * sc;
+    else c = -1152.0f * sc;
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const half8_t A = as_half8(cx[t].lo[j].x, cx[t].lo[j].y, cx[t].hi[j].x, cx[t].hi[j].y);
+      const float4_t D = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      const float4_t Dx = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, ones, float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        acc[t][v] = __builtin_fmaf(sc, D[v], acc[t][v]);
+        acc[t][v] = __builtin_fmaf(c, Dx[v], acc[t][v]);
+      }
     }
   }
 }
 
-template <int FMT, int T>
-__global__ __launch_bounds__(64 * MF_WAVES) void k_gemv_mfma(const uint8_t* __restrict__ W,
-                                                            const uint16_t* __restrict__ x,
-                                                            float* __restrict__ y, int N, int K, int M) {
-  __shared__ float4_t red[MF_WAVES][T][64];
+// Grid: one workgroup per 16 rows, S = blockDim.x / 64 waves, wave w owns
+// groups [w * gpw, (w + 1) * gpw) of the rows (clipped to the row length).
+// Dynamic LDS: S * T * 64 float4 partial results.
+// Waves per workgroup at most: 16, or 8 with three or more column tiles (their
+// activations need more than the 128 registers a 16-wave workgroup allows).
+template <int T> struct MfmaMaxWaves { static constexpr int v = T >= 3 ? 8 : 16; };
+
+template <int FMT, int T, int P>
+__global__ __launch_bounds__(64 * MfmaMaxWaves<T>::v) void k_gemv_mfma(const uint8_t* __restrict__ W,
+                                                   const uint16_t* __restrict__ x,
+                                                   float* __restrict__ y, int N, int K, int M, int gpw) {
+  extern __shared__ float4_t red[];
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
+  const int S = blockDim.x >> 6;
   const int n = lane & 15, g = lane >> 4;
   const int64_t row0 = (int64_t)blockIdx.x * 16;
   const int nblk = K / 32;
   const int ngroups = (nblk + 3) / 4;
-  const int gb = ngroups * wave / MF_WAVES, ge = ngroups * (wave + 1) / MF_WAVES;
+  const int gb = wave * gpw;
+  const int ge = min(gb + gpw, ngroups);
   const uint32_t row_bytes = (uint32_t)nblk * Fmt<FMT>::BB;
   const int valid_rows = (int)min<int64_t>(16, N - row0);
   // Range rounded up to whole dwords: Q4_0/Q8_0 blocks are only 2-byte
@@ -130,111 +206,55 @@ __global__ __launch_bounds__(64 * MF_WAVES) void k_gemv_mfma(const uint8_t* __re
   const rsrc_t rs = make_rsrc(W + row0 * row_bytes, ((uint32_t)valid_rows * row_bytes + 3u) & ~3u);
   const uint32_t roff = (uint32_t)n * row_bytes;
   const bool row_ok = n < valid_rows;
-
-  const uint16_t* xc[T];
-  bool col_ok[T];
+  const rsrc_t xs = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
+  uint32_t xoff[T];
 #pragma unroll
   for (int t = 0; t < T; ++t) {
     const int col = 16 * t + n;
-    col_ok[t] = col < M;
-    xc[t] = x + (int64_t)(col_ok[t] ? col : 0) * K;
+    xoff[t] = col < M ? (uint32_t)col * (uint32_t)K * 2u : OOB;
   }
 
   float4_t acc[T];
 #pragma unroll
   for (int t = 0; t < T; ++t) acc[t] = float4_t{0.f, 0.f, 0.f, 0.f};
-  const half8_t ones = as_half8(ONES, ONES, ONES, ONES);
 
-  GroupRaw<FMT> cur, nxt;
-  GroupX cx[T], nx[T];
-  if (gb < ge) {
-    load_group<FMT>(rs, roff, 4 * gb + g, row_ok && 4 * gb + g < nblk, cur);
+  GroupRaw<FMT> wr[P];
+  GroupX xr[P][T];
+  // Loads first: the first P groups of this wave's range (past its end: zero).
 #pragma unroll
-    for (int t = 0; t < T; ++t) load_group_x(xc[t], col_ok[t], 4 * gb, nblk, g, cx[t]);
+  for (int p = 0; p < P; ++p) {
+    const int gi = gb + p;
+    load_group<FMT>(rs, roff, 4 * gi + g, gi < ge && row_ok && 4 * gi + g < nblk, wr[p]);
+#pragma unroll
+    for (int t = 0; t < T; ++t) load_group_x(xs, gi < ge ? xoff[t] : OOB, 4 * gi, nblk, g, xr[p][t]);
+    __builtin_amdgcn_sched_barrier(0);   // groups are issued in order: consuming one waits for it alone
   }
-  for (int gi = gb; gi < ge; ++gi) {
-    if (gi + 1 < ge) {
-      load_group<FMT>(rs, roff, 4 * (gi + 1) + g, row_ok && 4 * (gi + 1) + g < nblk, nxt);
+  for (int base = gb; base < ge; base += P) {
 #pragma unroll
-      for (int t = 0; t < T; ++t) load_group_x(xc[t], col_ok[t], 4 * (gi + 1), nblk, g, nx[t]);
-    }
-    // ---- this lane's block (b0 + g): scale/bias and quant dwords, then
-    // exchange so lane group g holds quant dword(s) g of blocks b0..b0+3
-    uint32_t hdr, q0, q1, q2, q3, p0 = 0, p1 = 0, p2 = 0, p3 = 0;
-    if constexpr (FMT == F_AFFINE4) {
-      hdr = cur.D[0];
-      q0 = cur.D[1]; q1 = cur.D[2]; q2 = cur.D[3]; q3 = cur.D[4];
-    } else {
-      const uint32_t r2 = ((roff + (uint32_t)(4 * gi + g) * Fmt<FMT>::BB + 2u) & 3u) * 8u;  // bit shift 0/16
-      hdr = r2 ? (cur.D[1] & 0xffffu) : (cur.D[0] >> 16);
-      const uint32_t sh = r2 >> 3;   // byte shift 0 or 2
-      q0 = __builtin_amdgcn_alignbyte(cur.D[2], cur.D[1], sh);
-      q1 = __builtin_amdgcn_alignbyte(cur.D[3], cur.D[2], sh);
-      q2 = __builtin_amdgcn_alignbyte(cur.D[4], cur.D[3], sh);
-      q3 = __builtin_amdgcn_alignbyte(cur.D[5], cur.D[4], sh);
-      if constexpr (FMT == F_Q8_0) {
-        p0 = __builtin_amdgcn_alignbyte(cur.D[6], cur.D[5], sh);
-        p1 = __builtin_amdgcn_alignbyte(cur.D[7], cur.D[6], sh);
-        p2 = __builtin_amdgcn_alignbyte(cur.D[8], cur.D[7], sh);
-        p3 = __builtin_amdgcn_alignbyte(cur.D[9], cur.D[8], sh);
-      }
-    }
-    transpose4(q0, q1, q2, q3);
-    if constexpr (FMT == F_Q8_0) transpose4(p0, p1, p2, p3);
-    uint32_t h0 = hdr, h1 = hdr, h2 = hdr, h3 = hdr;
-    transpose4(h0, h1, h2, h3);
-    const uint32_t qs[4] = {q0, q1, q2, q3};
-    const uint32_t ps[4] = {p0, p1, p2, p3};
-    const uint32_t hs[4] = {h0, h1, h2, h3};
+    for (int p = 0; p < P; ++p) {
+      const int gi = base + p;
+      if (gi < ge) consume_group<FMT, T>(wr[p], xr[p], roff, gi, g, nblk, acc);   // uniform
+      // Refill the slot with the group one round ahead. Past the range the
+      // loads read zero; they are issued anyway, so that every path leaves the
+      // same loads in flight in the same order and each consume waits only
+      // for its own group.
+      const int gn = gi + P;
+      load_group<FMT>(rs, roff, 4 * gn + g, gn < ge && row_ok && 4 * gn + g < nblk, wr[p]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (4 * gi + j >= nblk) break;      // uniform
-      // B operand: 8 fp16 (offset + q) for elements {4g..4g+3, 16+4g..19+4g}
-      uint32_t b0, b1, b2, b3;
-      if constexpr (FMT == F_Q8_0) {
-        const uint32_t u = qs[j] ^ 0x80808080u, v = ps[j] ^ 0x80808080u;
-        b0 = perm(MAGIC, u, SEL_LO); b1 = perm(MAGIC, u, SEL_HI);
-        b2 = perm(MAGIC, v, SEL_LO); b3 = perm(MAGIC, v, SEL_HI);
-      } else {
-        const uint32_t lo = qs[j] & 0x0F0F0F0Fu, hi = (qs[j] >> 4) & 0x0F0F0F0Fu;
-        b0 = perm(MAGIC, lo, SEL_LO); b1 = perm(MAGIC, lo, SEL_HI);
-        b2 = perm(MAGIC, hi, SEL_LO); b3 = perm(MAGIC, hi, SEL_HI);
-      }
-      const half8_t B = as_half8(b0, b1, b2, b3);
-      const float sc = h2f(hs[j]);
-      float c;
-      if constexpr (FMT == F_AFFINE4) c = __builtin_fmaf(-1024.0f, sc, h2f(hs[j] >> 16));
-      else if constexpr (FMT == F_Q4_0) c = -1032.0f * sc;
-      else c = -1152.0f * sc;
-#pragma unroll
-      for (int t = 0; t < T; ++t) {
-        const half8_t A = as_half8(cx[t].lo[j].x, cx[t].lo[j].y, cx[t].hi[j].x, cx[t].hi[j].y);
-        const float4_t D = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-        const float4_t Dx = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, ones, float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          acc[t][v] = __builtin_fmaf(sc, D[v], acc[t][v]);
-          acc[t][v] = __builtin_fmaf(c, Dx[v], acc[t][v]);
-        }
-      }
-    }
-    if (gi + 1 < ge) {
-      cur = nxt;
-#pragma unroll
-      for (int t = 0; t < T; ++t) cx[t] = nx[t];
+      for (int t = 0; t < T; ++t) load_group_x(xs, gn < ge ? xoff[t] : OOB, 4 * gn, nblk, g, xr[p][t]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
-  // fixed-order sum of the 8 waves' partial results
+  // fixed-order sum of the S waves' partial results
 #pragma unroll
-  for (int t = 0; t < T; ++t) red[wave][t][lane] = acc[t];
+  for (int t = 0; t < T; ++t) red[(wave * T + t) * 64 + lane] = acc[t];
   __syncthreads();
   if (wave == 0) {
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-      float4_t s = red[0][t][lane];
-#pragma unroll
-      for (int w = 1; w < MF_WAVES; ++w) {
-        const float4_t o = red[w][t][lane];
+      float4_t s = red[t * 64 + lane];
+      for (int w = 1; w < S; ++w) {
+        const float4_t o = red[(w * T + t) * 64 + lane];
 #pragma unroll
         for (int v = 0; v < 4; ++v) s[v] += o[v];
       }
@@ -248,6 +268,328 @@ __global__ __launch_bounds__(64 * MF_WAVES) void k_gemv_mfma(const uint8_t* __re
   }
 }
 
+// ---------------------------------------------------------------------------
+// Activations staged in LDS (M <= 16 and the copy fits): the workgroup copies
+// x once, with 16-byte loads, into the MFMA operand order, so that a wave's
+// per-group memory instructions are its weight loads alone (otherwise the
+// texture address path, not HBM, bounds the kernel). With Mp = M rounded up
+// to a power of two and K rounded up to whole 4-block groups (zeros past K):
+//   x slots: for block b, lane group g, column c, 16 bytes at ((4 b + g) Mp + c) 16
+//            holding x[c][32 b + 4 g .. +3] then x[c][32 b + 16 + 4 g .. +3]
+//            (the lanes of one read take contiguous bytes: no bank conflicts);
+//   sums:    sx[b][c] = sum of block b of column c, fp32.
+// The per-block fix-up splits in two. The scale term sc * D needs D per block
+// (4 FMAs per lane). The offset term sum_b c[row][b] sx[c][b] is itself a small
+// product, done per group as one fp32 MFMA (16x16x4) whose B operand is the
+// constant of the lane's own loaded block, so it needs no exchange. Blocks
+// past K have zero weights (loads out of range), zero x and zero sums, so they
+// add exactly zero and need no test.
+//
+// Grid: R 16-row tiles per workgroup, S waves per tile (R S <= 16); wave
+// (r, s) owns groups [s P, (s + 1) P) of tile r, all loaded before any
+// arithmetic. Columns >= M: their lanes read a real column and their outputs
+// are discarded.
+constexpr int XST_MAX = 12;   // 16-byte x pieces per thread while staging
+
+template <int FMT, int P, bool SX>
+__global__ __launch_bounds__(1024) void k_gemv_mfma_lds(const uint8_t* __restrict__ W,
+                                                       const uint16_t* __restrict__ x,
+                                                       float* __restrict__ y, int N, int K, int M, int R,
+                                                       int S, int log2mp);
+
+// One 4-block group of a 16-row tile (the lane's raw block `cur`, block
+// index 4 gi + g) against the staged x: the group's offset term as one fp32
+// MFMA, then per block D = x . (offset + q) and acc += scale * D.
+template <int FMT, bool SX = true>
+__device__ __forceinline__ void mfma_group(const GroupRaw<FMT>& cur, uint32_t roff, int gi, int g,
+                                           const u32x4* xa, const float* sxa, int Mp, float4_t& acc) {
+  uint32_t hdr, q0, q1, q2, q3, p0 = 0, p1 = 0, p2 = 0, p3 = 0;
+  if constexpr (FMT == F_AFFINE4) {
+    hdr = cur.D[0];
+    q0 = cur.D[1]; q1 = cur.D[2]; q2 = cur.D[3]; q3 = cur.D[4];
+  } else {
+    const uint32_t r2 = ((roff + (uint32_t)(4 * gi + g) * Fmt<FMT>::BB + 2u) & 3u) * 8u;
+    hdr = r2 ? (cur.D[1] & 0xffffu) : (cur.D[0] >> 16);
+    const uint32_t sh = r2 >> 3;
+    q0 = __builtin_amdgcn_alignbyte(cur.D[2], cur.D[1], sh);
+    q1 = __builtin_amdgcn_alignbyte(cur.D[3], cur.D[2], sh);
+    q2 = __builtin_amdgcn_alignbyte(cur.D[4], cur.D[3], sh);
+    q3 = __builtin_amdgcn_alignbyte(cur.D[5], cur.D[4], sh);
+    if constexpr (FMT == F_Q8_0) {
+      p0 = __builtin_amdgcn_alignbyte(cur.D[6], cur.D[5], sh);
+      p1 = __builtin_amdgcn_alignbyte(cur.D[7], cur.D[6], sh);
+      p2 = __builtin_amdgcn_alignbyte(cur.D[8], cur.D[7], sh);
+      p3 = __builtin_amdgcn_alignbyte(cur.D[9], cur.D[8], sh);
+    }
+  }
+  if constexpr (SX) {
+    float cown;
+    const float so = h2f(hdr);
+    if constexpr (FMT == F_AFFINE4) cown = __builtin_fmaf(-1024.0f, so, h2f(hdr >> 16));
+    else if constexpr (FMT == F_Q4_0) cown = -1032.0f * so;
+    else cown = -1152.0f * so;
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sxa[4 * gi * Mp], cown, acc, 0, 0, 0);
+  }
+  transpose4(q0, q1, q2, q3);
+  if constexpr (FMT == F_Q8_0) transpose4(p0, p1, p2, p3);
+  uint32_t h0 = hdr, h1 = hdr, h2 = hdr, h3 = hdr;
+  transpose4(h0, h1, h2, h3);
+  const uint32_t qs[4] = {q0, q1, q2, q3};
+  const uint32_t ps[4] = {p0, p1, p2, p3};
+  const uint32_t hs[4] = {h0, h1, h2, h3};
+  const int bstride = 4 * Mp;
+  float4_t D[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const half8_t A = __builtin_bit_cast(half8_t, xa[(4 * gi + j) * bstride]);
+    uint32_t b0, b1, b2, b3;
+    if constexpr (FMT == F_Q8_0) {
+      const uint32_t u = qs[j] ^ 0x80808080u, v = ps[j] ^ 0x80808080u;
+      b0 = perm(MAGIC, u, SEL_LO); b1 = perm(MAGIC, u, SEL_HI);
+      b2 = perm(MAGIC, v, SEL_LO); b3 = perm(MAGIC, v, SEL_HI);
+    } else {
+      const uint32_t lo = qs[j] & 0x0F0F0F0Fu, hi = (qs[j] >> 4) & 0x0F0F0F0Fu;
+      b0 = perm(MAGIC, lo, SEL_LO); b1 = perm(MAGIC, lo, SEL_HI);
+      b2 = perm(MAGIC, hi, SEL_LO); b3 = perm(MAGIC, hi, SEL_HI);
+    }
+    D[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, as_half8(b0, b1, b2, b3), float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float sc = h2f(hs[j]);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) acc[v] = __builtin_fmaf(sc, D[j][v], acc[v]);
+  }
+  if constexpr (!SX) {
+    // no block sums in LDS: the offset term per block from an MFMA against ones
+    const half8_t ones = as_half8(ONES, ONES, ONES, ONES);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const half8_t A = __builtin_bit_cast(half8_t, xa[(4 * gi + j) * bstride]);
+      const float4_t Dx = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, ones, float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      const float sc = h2f(hs[j]);
+      float c;
+      if constexpr (FMT == F_AFFINE4) c = __builtin_fmaf(-1024.0f, sc, h2f(hs[j] >> 16));
+      else if constexpr (FMT == F_Q4_0) c = -1032.0f * sc;
+      else c = -1152.0f * sc;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[v] = __builtin_fmaf(c, Dx[v], acc[v]);
+    }
+  }
+}
+
+// Stage x (M columns, K) into LDS in the operand order described above, plus
+// the block sums. Called by every thread of the workgroup; `issue_more` runs
+// between issuing the x loads and writing them (the caller's weight loads),
+// after a barrier that puts every wave's x loads ahead of them in the queue.
+template <bool SX, typename F>
+__device__ __forceinline__ void stage_x_mfma(const uint16_t* __restrict__ x, int M, int K, int ngroups,
+                                             int log2mp, uint8_t* xlb, F issue_more) {
+  const int Mp = 1 << log2mp;
+  const int kq8 = K / 8, kq8p = 16 * ngroups;
+  const uint32_t sx_base = (uint32_t)kq8p * (uint32_t)Mp * 16u;
+  const uint32_t dummy = SX ? sx_base + (uint32_t)(4 * ngroups * Mp) * 4u : sx_base;
+  const int npieces = Mp * kq8p;
+  const int nthreads = (int)blockDim.x;
+  const rsrc_t xs = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
+  u32x4 xr[XST_MAX];
+#pragma unroll
+  for (int c = 0; c < XST_MAX; ++c) {
+    const int i = (int)threadIdx.x + nthreads * c;
+    const int col = i & (Mp - 1), k8 = i >> log2mp;
+    const bool ok = i < npieces && col < M && k8 < kq8;
+    xr[c] = ld128(xs, ok ? ((uint32_t)col * (uint32_t)kq8 + (uint32_t)k8) * 16u : OOB);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  issue_more();
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int c = 0; c < XST_MAX; ++c) {
+    const int i = (int)threadIdx.x + nthreads * c;
+    const int col = i & (Mp - 1), k8 = i >> log2mp;
+    const int bb = k8 >> 2, h = k8 & 3;
+    const int g0 = 2 * (h & 1);
+    const uint32_t part = 8u * (uint32_t)(h >> 1);
+    const bool ok = i < npieces;
+    const uint32_t a0 = ok ? (uint32_t)((4 * bb + g0) * Mp + col) * 16u + part : dummy;
+    const uint32_t a1 = ok ? (uint32_t)((4 * bb + g0 + 1) * Mp + col) * 16u + part : dummy + 8u;
+    *reinterpret_cast<u32x2*>(xlb + a0) = u32x2{xr[c].x, xr[c].y};
+    *reinterpret_cast<u32x2*>(xlb + a1) = u32x2{xr[c].z, xr[c].w};
+  }
+  __syncthreads();
+  if constexpr (!SX) return;
+  const u32x4* xl4 = reinterpret_cast<const u32x4*>(xlb);
+  float* sx = reinterpret_cast<float*>(xlb + sx_base);
+  const int ntask = 4 * ngroups * Mp;
+  for (int t = (int)threadIdx.x; t < ntask; t += nthreads) {
+    const int bb = t >> log2mp, col = t & (Mp - 1);
+    float v = 0.0f;
+#pragma unroll
+    for (int gg = 0; gg < 4; ++gg) {
+      const u32x4 q = xl4[(4 * bb + gg) * Mp + col];
+      v = dot2(q.x, ONES, v);
+      v = dot2(q.y, ONES, v);
+      v = dot2(q.z, ONES, v);
+      v = dot2(q.w, ONES, v);
+    }
+    sx[t] = v;
+  }
+  __syncthreads();
+}
+
+// Many tiles (large N): persistent waves. x is staged once per workgroup;
+// then every wave on its own streams whole 16-row tiles (no K split, so no
+// reduction), tiles t0, t0 + T, ... (T = waves in the grid, `tpw` tiles per
+// wave at most), as one sequence of 4-block groups with P groups in flight:
+// a slot is refilled with the group P steps ahead (of this tile or the next)
+// as soon as it has been consumed. A finished tile's outputs are stored at
+// once by the wave that owns it.
+// Few tiles (small N): a workgroup of R tiles x S waves; wave (r, s) owns
+// groups [s P, (s + 1) P) of tile r, all loaded before any arithmetic, and the
+// S partial results of a tile are summed in LDS in a fixed order. SX: block
+// sums in LDS (else, when x alone just fits, from an MFMA per block).
+template <int FMT, int P, bool SX>
+__global__ __launch_bounds__(1024) void k_gemv_mfma_lds(const uint8_t* __restrict__ W,
+                                                       const uint16_t* __restrict__ x,
+                                                       float* __restrict__ y, int N, int K, int M, int R,
+                                                       int S, int log2mp) {
+  extern __shared__ u32x4 xl4[];
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  const int r = wave / S, s = wave - r * S;
+  const int n = lane & 15, g = lane >> 4;
+  const int64_t row0 = ((int64_t)blockIdx.x * R + r) * 16;
+  const int nblk = K / 32;
+  const int ngroups = (nblk + 3) / 4;
+  const int Mp = 1 << log2mp;
+  const int gb = s * P;
+  const uint32_t row_bytes = (uint32_t)nblk * Fmt<FMT>::BB;
+  const int valid_rows = row0 < N ? (int)min<int64_t>(16, N - row0) : 0;
+  const rsrc_t rs = make_rsrc(W + (valid_rows ? row0 * row_bytes : 0), ((uint32_t)valid_rows * row_bytes + 3u) & ~3u);
+  const uint32_t roff = (uint32_t)n * row_bytes;
+  const bool row_ok = n < valid_rows;
+  uint8_t* xlb = reinterpret_cast<uint8_t*>(xl4);
+  GroupRaw<FMT> wr[P];
+  stage_x_mfma<SX>(x, M, K, ngroups, log2mp, xlb, [&]() {
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const int gi = gb + p;
+      load_group<FMT>(rs, roff, 4 * gi + g, gi < ngroups && row_ok && 4 * gi + g < nblk, wr[p]);
+    }
+  });
+  const int ncol = n < M ? n : M - 1;
+  const u32x4* xa = xl4 + g * Mp + ncol;
+  const float* sxa = reinterpret_cast<const float*>(xlb + (uint32_t)(16 * ngroups) * (uint32_t)Mp * 16u) + g * Mp + ncol;
+  float4_t acc = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    const int gi = gb + p;
+    if (gi >= ngroups) break;   // uniform
+    mfma_group<FMT, SX>(wr[p], roff, gi, g, xa, sxa, Mp, acc);
+  }
+  // fixed-order sum over the S waves of each tile (the x area is reused)
+  __syncthreads();
+  float4_t* red = reinterpret_cast<float4_t*>(xl4);
+  red[wave * 64 + lane] = acc;
+  __syncthreads();
+  if (s == 0 && valid_rows > 0) {
+    float4_t t = red[(r * S) * 64 + lane];
+    for (int w = 1; w < S; ++w) {
+      const float4_t o = red[(r * S + w) * 64 + lane];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) t[v] += o[v];
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int col = 4 * g + v;
+      if (col < M && row_ok) y[(int64_t)col * N + row0 + n] = t[v];
+    }
+  }
+}
+
+constexpr int MFMA_PERS_TPW = 8;   // tiles per wave at most
+
+template <int FMT, int P>
+__global__ __launch_bounds__(512) void k_gemv_mfma_pers(const uint8_t* __restrict__ W,
+                                                       const uint16_t* __restrict__ x,
+                                                       float* __restrict__ y, int N, int K, int M,
+                                                       int log2mp, int tpw) {
+  extern __shared__ u32x4 xl4[];
+  const int lane = threadIdx.x & 63;
+  const int nw = (int)(blockDim.x >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  const int nblk = K / 32;
+  const int ngroups = (nblk + 3) / 4;
+  const int Mp = 1 << log2mp;
+  const int64_t tiles = (N + 15) / 16;
+  const int64_t T = (int64_t)gridDim.x * nw;
+  const int64_t t0 = (int64_t)blockIdx.x * nw + wave_id();
+  const uint32_t row_bytes = (uint32_t)nblk * Fmt<FMT>::BB;
+  const uint32_t roff = (uint32_t)n * row_bytes;
+  // this wave's sequence: tiles t0 + k T (k < tpw, tile < tiles), groups 0..ngroups-1 each
+  const int64_t mine = t0 < tiles ? min<int64_t>(tpw, (tiles - 1 - t0) / T + 1) : 0;
+  const int Q = (int)mine * ngroups;
+  GroupRaw<FMT> wr[P];
+  // issue pointer (tile index k, group) of the next group to load
+  int ik = 0, ig = 0;
+  auto issue = [&](GroupRaw<FMT>& slot, bool live) {
+    const int64_t tile = t0 + (int64_t)ik * T;
+    const int64_t row0 = tile * 16;
+    const int valid_rows = live ? (int)min<int64_t>(16, N - row0) : 0;
+    const rsrc_t rs = make_rsrc(W + (valid_rows ? row0 * row_bytes : 0), ((uint32_t)valid_rows * row_bytes + 3u) & ~3u);
+    load_group<FMT>(rs, roff, 4 * ig + g, n < valid_rows && 4 * ig + g < nblk, slot);
+    if (++ig == ngroups) { ig = 0; ++ik; }
+  };
+  uint8_t* xlb = reinterpret_cast<uint8_t*>(xl4);
+  stage_x_mfma<true>(x, M, K, ngroups, log2mp, xlb, [&]() {
+#pragma unroll
+    for (int p = 0; p < P; ++p) issue(wr[p], p < Q);
+  });
+  const int ncol = n < M ? n : M - 1;
+  const u32x4* xa = xl4 + g * Mp + ncol;
+  const float* sxa = reinterpret_cast<const float*>(xlb + (uint32_t)(16 * ngroups) * (uint32_t)Mp * 16u) + g * Mp + ncol;
+  float4_t acc = float4_t{0.f, 0.f, 0.f, 0.f};
+  // Finished tiles wait in registers (newest first) and are stored after the
+  // loop: a store counts as a memory operation in flight too, and one taken
+  // only at tile ends would make the loads' waits depend on the path.
+  float4_t done[MFMA_PERS_TPW];
+  int cg = 0;   // consume pointer (group within the current tile)
+  for (int base = 0; base < Q; base += P) {
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const int q = base + p;
+      if (q < Q) {   // uniform
+        mfma_group<FMT>(wr[p], roff, cg, g, xa, sxa, Mp, acc);
+        if (++cg == ngroups) {   // tile complete: lane holds D[col 4g+v][row n]
+#pragma unroll
+          for (int k = MFMA_PERS_TPW - 1; k > 0; --k) done[k] = done[k - 1];
+          done[0] = acc;
+          acc = float4_t{0.f, 0.f, 0.f, 0.f};
+          cg = 0;
+        }
+      }
+      // refill the slot with the group P steps ahead (zero past the end: the
+      // same loads on every path keep each wait to its own group)
+      issue(wr[p], q + P < Q);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < MFMA_PERS_TPW; ++k) {
+    if (k >= mine) break;   // uniform
+    const int64_t row = (t0 + (mine - 1 - k) * T) * 16 + n;
+    if (row < N) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int col = 4 * g + v;
+        if (col < M) y[(int64_t)col * N + row] = done[k][v];
+      }
+    }
+  }
+}
+
 }  // namespace kqd
 
 namespace kq {
@@ -256,16 +598,192 @@ using namespace kqd;
 
 namespace {
 
+// Groups in flight per wave, by register footprint (T column tiles of x).
+template <int FMT, int T> struct MfmaDepth { static constexpr int v = T == 1 ? (FMT == F_Q8_0 ? 3 : 4) : (T == 2 && FMT != F_Q8_0 ? 2 : 1); };
+
+struct MfmaCfg {
+  int waves;   // per workgroup (16 rows)
+  int gpw;     // 4-block groups per wave
+};
+
+// Waves per 16-row tile: at least enough to cover the row with P groups per
+// wave, then doubled (up to smax) while the grid has fewer than 2048 waves, so
+// that short or few rows still keep enough loads in flight. KQ_MFMA_S
+// overrides it (tuning sweeps and tests).
+MfmaCfg mfma_cfg(int64_t N, int64_t K, int P, int smax) {
+  const int ngroups = (int)((K / 32 + 3) / 4);
+  const int64_t tiles = (N + 15) / 16;
+  int S = (ngroups + P - 1) / P;
+  if (S > smax) S = smax;
+  while (S < smax && S < ngroups && tiles * S < 2048) S *= 2;
+  if (S > smax) S = smax;
+  const char* e = getenv("KQ_MFMA_S");
+  if (e) {
+    const int v = atoi(e);
+    if (v >= 1 && v <= smax) S = v;
+  }
+  if (S > ngroups) S = ngroups;
+  const int gpw = (ngroups + S - 1) / S;
+  S = (ngroups + gpw - 1) / gpw;   // no idle waves
+  return {S, gpw};
+}
+
 template <int FMT, int T>
 int launch_mfma_t(const GemvArgs& a, int m0, int mt) {
-  const dim3 grid((unsigned)((a.N + 15) / 16)), block(64 * MF_WAVES);
-  hipLaunchKernelGGL((k_gemv_mfma<FMT, T>), grid, block, 0, a.stream, a.W, a.x + (int64_t)m0 * a.K,
-                     a.y + (int64_t)m0 * a.N, (int)a.N, (int)a.K, mt);
+  constexpr int P = MfmaDepth<FMT, T>::v;
+  const MfmaCfg c = mfma_cfg(a.N, a.K, P, MfmaMaxWaves<T>::v);
+  const dim3 grid((unsigned)((a.N + 15) / 16)), block((unsigned)(64 * c.waves));
+  const size_t lds = (size_t)c.waves * T * 64 * sizeof(float4_t);
+  hipLaunchKernelGGL((k_gemv_mfma<FMT, T, P>), grid, block, lds, a.stream, a.W, a.x + (int64_t)m0 * a.K,
+                     a.y + (int64_t)m0 * a.N, (int)a.N, (int)a.K, mt, c.gpw);
   return (int)hipGetLastError();
 }
 
+constexpr int MFMA_LDS_MAX_BYTES = 160 * 1024;
+// Groups per wave at most (registers within the 128 of a 16-wave workgroup).
+template <int FMT> struct MfmaLdsMaxP { static constexpr int v = FMT == F_Q8_0 ? 4 : 6; };
+
+struct MfmaLdsCfg {
+  int R, S, P, log2mp;
+  bool sx;     // block sums in LDS (else an MFMA per block)
+  size_t lds;
+  bool ok;
+};
+
+// LDS bytes of staged x (M columns padded to Mp, K to whole groups), with or
+// without the block sums, plus a 16-byte slot for idle threads.
+int64_t mfma_x_lds_bytes(int64_t K, int log2mp, bool sums) {
+  const int64_t ngroups = (K / 32 + 3) / 4, Mp = (int64_t)1 << log2mp;
+  return Mp * 16 * ngroups * 16 + (sums ? 4 * ngroups * Mp * 4 : 0) + 16;
+}
+
+// Waves per tile S: enough that each wave holds at most maxp groups,
+// doubled while the grid has fewer than 2048 waves; then tiles per workgroup R
+// (R S <= 8, so that several workgroups share a CU and one computes while
+// another loads) while at least 1024 workgroups remain, so that one staged
+// copy of x serves several tiles. Not usable (ok = false) when x does not fit in LDS
+// or needs more than XST_MAX pieces per thread.
+MfmaLdsCfg mfma_lds_cfg(int64_t N, int64_t K, int M, int maxp, bool no_sums) {
+  MfmaLdsCfg c{1, 1, 1, 0, true, 0, false};
+  const int ngroups = (int)((K / 32 + 3) / 4);
+  const int64_t tiles = (N + 15) / 16;
+  int S = (ngroups + maxp - 1) / maxp;
+  if (S > 16) return c;
+  while (S < 16 && S < ngroups && tiles * S < 2048) S *= 2;
+  if (S > 16) S = 16;
+  const char* e = getenv("KQ_MFMA_S");
+  if (e) {
+    const int v = atoi(e);
+    if (v >= 1 && v <= 16) S = v;
+  }
+  if (S > ngroups) S = ngroups;
+  const int P = (ngroups + S - 1) / S;
+  if (P > maxp) return c;
+  S = (ngroups + P - 1) / P;
+  int R = 1;
+  while (2 * R * S <= 8 && (tiles + 2 * R - 1) / (2 * R) >= 1024) R *= 2;
+  const char* er = getenv("KQ_MFMA_R");
+  if (er) {
+    const int v = atoi(er);
+    if (v >= 1 && v * S <= 16) R = v;
+  }
+  int log2mp = 0;
+  while ((1 << log2mp) < M) ++log2mp;
+  const int64_t pieces = ((int64_t)1 << log2mp) * 16 * ngroups;   // x padded to whole groups
+  const int64_t rbytes = (int64_t)R * S * 64 * 16;
+  if (pieces > (int64_t)XST_MAX * 64 * R * S) return c;
+  for (int sums = no_sums ? 0 : 1; sums >= 0; --sums) {
+    const int64_t xb = mfma_x_lds_bytes(K, log2mp, sums != 0);
+    const int64_t lds = xb > rbytes ? xb : rbytes;
+    if (lds <= MFMA_LDS_MAX_BYTES) return {R, S, P, log2mp, sums != 0, (size_t)lds, true};
+  }
+  return c;
+}
+
+template <int FMT, int P, bool SX>
+int launch_mfma_lds_p(const GemvArgs& a, int m0, int mt, const MfmaLdsCfg& c) {
+  const int64_t tiles = (a.N + 15) / 16;
+  const dim3 grid((unsigned)((tiles + c.R - 1) / c.R)), block((unsigned)(64 * c.R * c.S));
+  hipLaunchKernelGGL((k_gemv_mfma_lds<FMT, P, SX>), grid, block, c.lds, a.stream, a.W, a.x + (int64_t)m0 * a.K,
+                     a.y + (int64_t)m0 * a.N, (int)a.N, (int)a.K, mt, c.R, c.S, c.log2mp);
+  return (int)hipGetLastError();
+}
+
+template <int FMT, bool SX>
+int launch_mfma_lds_sx(const GemvArgs& a, int m0, int mt, const MfmaLdsCfg& c) {
+  switch (c.P) {
+    case 1: return launch_mfma_lds_p<FMT, 1, SX>(a, m0, mt, c);
+    case 2: return launch_mfma_lds_p<FMT, 2, SX>(a, m0, mt, c);
+    case 3: return launch_mfma_lds_p<FMT, 3, SX>(a, m0, mt, c);
+    case 4: return launch_mfma_lds_p<FMT, 4, SX>(a, m0, mt, c);
+    default:
+      if constexpr (MfmaLdsMaxP<FMT>::v >= 6) {
+        if (c.P == 5) return launch_mfma_lds_p<FMT, 5, SX>(a, m0, mt, c);
+        return launch_mfma_lds_p<FMT, 6, SX>(a, m0, mt, c);
+      }
+      return (int)hipErrorInvalidValue;
+  }
+}
+
+template <int FMT>
+int launch_mfma_lds(const GemvArgs& a, int m0, int mt, const MfmaLdsCfg& c) {
+  return c.sx ? launch_mfma_lds_sx<FMT, true>(a, m0, mt, c) : launch_mfma_lds_sx<FMT, false>(a, m0, mt, c);
+}
+
+// Persistent waves for many tiles: 8 waves per workgroup, as many workgroups
+// as fit at once (up to one wave per tile), tiles dealt evenly: tpw =
+// ceil(tiles / waves) (at most MFMA_PERS_TPW), then only as many waves as
+// that needs.
+template <int FMT, int P>
+int launch_mfma_pers_p(const GemvArgs& a, int log2mp, size_t lds) {
+  static int cus_of[64] = {0};   // compute units per device, looked up once
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return (int)hipErrorInvalidDevice;
+  if (!cus_of[dev] && hipDeviceGetAttribute(&cus_of[dev], hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return (int)hipErrorInvalidDevice;
+  const int cus = cus_of[dev];
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_gemv_mfma_pers<FMT, P>, 512, lds) != hipSuccess || per_cu < 1)
+    per_cu = 1;
+  const int64_t tiles = (a.N + 15) / 16;
+  const int64_t max_waves = (int64_t)cus * per_cu * 8;
+  int64_t tpw = (tiles + max_waves - 1) / max_waves;
+  if (tpw > MFMA_PERS_TPW) tpw = MFMA_PERS_TPW;   // more workgroups than fit at once
+  const char* et = getenv("KQ_MFMA_PERS_TPW");     // tests: several tiles per wave at any size
+  if (et && atoi(et) >= 1 && atoi(et) <= MFMA_PERS_TPW) tpw = atoi(et);
+  const int64_t waves = (tiles + tpw - 1) / tpw;
+  const dim3 grid((unsigned)((waves + 7) / 8)), block(512);
+  hipLaunchKernelGGL((k_gemv_mfma_pers<FMT, P>), grid, block, lds, a.stream, a.W, a.x, a.y, (int)a.N, (int)a.K,
+                     (int)a.M, log2mp, (int)tpw);
+  return (int)hipGetLastError();
+}
+
+template <int FMT> struct MfmaPersP { static constexpr int v = FMT == F_Q8_0 ? 6 : 8; };
+// From this many 16-row tiles on, persistent waves (one tile at a time per
+// wave) fill the device; below it, tiles are split over the waves of a workgroup.
+constexpr int64_t MFMA_PERS_MIN_TILES = 4096;
+
+// KQ_MFMA_VARIANT (tests and sweeps) forces one kernel where it applies:
+// "pers", "teams", "teams_nosx" (block sums by MFMA) or "direct".
 template <int FMT>
 int launch_mfma_fmt(const GemvArgs& a) {
+  const char* var = getenv("KQ_MFMA_VARIANT");
+  const bool want_direct = var && !strcmp(var, "direct");
+  const bool want_pers = var && !strcmp(var, "pers");
+  const bool want_teams = var && !strncmp(var, "teams", 5);
+  if (a.M <= 16 && !want_direct) {
+    const int64_t tiles = (a.N + 15) / 16;
+    const int ngroups = (int)((a.K / 32 + 3) / 4);
+    int log2mp = 0;
+    while ((1 << log2mp) < a.M) ++log2mp;
+    const int64_t pieces = ((int64_t)1 << log2mp) * 16 * ngroups;
+    const int64_t lds = mfma_x_lds_bytes(a.K, log2mp, true);
+    if ((tiles >= MFMA_PERS_MIN_TILES || want_pers) && !want_teams && lds <= MFMA_LDS_MAX_BYTES &&
+        pieces <= (int64_t)XST_MAX * 512)
+      return launch_mfma_pers_p<FMT, MfmaPersP<FMT>::v>(a, log2mp, (size_t)lds);
+    const MfmaLdsCfg c = mfma_lds_cfg(a.N, a.K, (int)a.M, MfmaLdsMaxP<FMT>::v, var && !strcmp(var, "teams_nosx"));
+    if (c.ok) return launch_mfma_lds<FMT>(a, 0, (int)a.M, c);
+  }
   for (int m0 = 0; m0 < a.M; m0 += 64) {
     const int mt = a.M - m0 < 64 ? a.M - m0 : 64;
     int err;

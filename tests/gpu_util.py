@@ -1,5 +1,6 @@
 """Helpers for the GPU parity tests: upload inputs, call the library through
 its C ABI, and compare with the oracle."""
+import contextlib
 import os
 
 import numpy as np
@@ -39,6 +40,22 @@ def quantize_both(fmt, W):
     ref = F.encode(fmt, fields)
     assert np.array_equal(packed, ref), "packer bytes differ from the oracle's"
     return packed, fields
+
+
+@contextlib.contextmanager
+def env_vars(values: dict):
+    """Set environment variables (read by the library at each launch) for the
+    duration of a block."""
+    old = {k: os.environ.get(k) for k in values}
+    os.environ.update(values)
+    try:
+        yield
+    finally:
+        for k, v in old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
 
 
 def gemv_gpu(fmt, packed_dev, x16: np.ndarray, N: int, K: int, path: str | None = None) -> np.ndarray:

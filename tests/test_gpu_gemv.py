@@ -175,3 +175,23 @@ def test_zero_and_constant_weights():
         yr, ad = R.gemv(fmt, fields, x)
         U.assert_parity(y, yr, ad, f"{fmt} constant rows")
         assert np.all(y[:, 0] == 0.0)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("variant", ("pers", "pers_tpw3", "teams", "teams_nosx", "direct"))
+@pytest.mark.parametrize("N,K,M", [(1000, 2560, 8), (37, 96, 5), (300, 4128, 16), (16, 32, 2), (529, 640, 13)])
+def test_mfma_variants_parity(fmt, variant, N, K, M):
+    """Each matrix-core kernel (the dispatcher picks one by shape: persistent
+    waves for many tiles, split-K teams with x staged in LDS with or without
+    block sums, per-wave activation loads) on ragged rows, partial groups and
+    odd block counts; pers_tpw3 gives each wave three tiles."""
+    packed, fields, x = _case(fmt, N, K, M, 9)
+    env = {"KQ_MFMA_VARIANT": variant.split("_tpw")[0]}
+    if variant == "pers_tpw3":
+        env["KQ_MFMA_PERS_TPW"] = "3"
+    with U.env_vars(env):
+        y = U.gemv_gpu(fmt, U.to_dev(packed), x, N, K, path="mfma")
+        y2 = U.gemv_gpu(fmt, U.to_dev(packed), x, N, K, path="mfma")
+    yr, ad = R.gemv(fmt, fields, x)
+    U.assert_parity(y, yr, ad, f"{fmt} {variant} N={N} K={K} M={M}")
+    assert np.array_equal(y, y2), "not deterministic run to run"

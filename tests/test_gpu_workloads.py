@@ -137,16 +137,29 @@ def test_lm_head_m1_full_and_argmax(lm_head):
     assert int(am[0]) == int(R.argmax_lowest(yr[0]))
 
 
-def test_lm_head_verify_m48_argmax(lm_head):
+@pytest.fixture(scope="module")
+def lm_head_verify_ref(lm_head):
+    """The oracle over the 48 verify columns once: columns are seeded one by
+    one, so the first M columns of this draw are the M-column input."""
     h, packed, fields = lm_head
-    x = S.activations((S.VERIFY_WORKLOAD_ID, 36, 0), h.k, 48)
-    y_dev, y = _head_run(lm_head, x)
+    x = S.activations((S.VERIFY_WORKLOAD_ID, 36, 0), h.k, max(S.VERIFY_M))
     yr, ad = R.gemv(h.fmt, fields, x)
-    U.assert_parity(y, yr, ad, "lm_head M=48")
-    am = _argmax_gpu(y_dev, h.n, 48)
+    return x, yr, ad
+
+
+@pytest.mark.parametrize("M", S.VERIFY_M)
+def test_lm_head_verify_argmax(lm_head, lm_head_verify_ref, M):
+    """cfg-4 verify on the lm_head: every column within tolerance of the
+    oracle, bit-identical argmax, and each column's argmax equal to its own
+    M=1 run's."""
+    h, packed, fields = lm_head
+    x48, yr48, ad48 = lm_head_verify_ref
+    x, yr, ad = x48[:M], yr48[:M], ad48[:M]
+    y_dev, y = _head_run(lm_head, x)
+    U.assert_parity(y, yr, ad, f"lm_head M={M}")
+    am = _argmax_gpu(y_dev, h.n, M)
     assert np.array_equal(am, R.argmax_lowest(yr))
-    # each column's argmax equals its own M=1 run's
-    for m in (0, 17, 47):
+    for m in sorted({0, M // 2, M - 1}):
         y1_dev, _ = _head_run(lm_head, x[m:m + 1])
         assert int(_argmax_gpu(y1_dev, h.n, 1)[0]) == int(am[m])
 
