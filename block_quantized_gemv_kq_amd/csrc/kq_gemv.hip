@@ -62,15 +62,15 @@ constexpr int XREG_CHUNKS = 5;   // 16-byte activation chunks per thread in the 
 // loads of all ITERS units it owns, the workgroup stages the MT activation
 // columns in LDS meanwhile, and only then does any arithmetic: one memory
 // round trip per tile. `passes` > 1 only when units > G * ITERS.
-template <int FMT, int MT, int ITERS, bool XREG>
-__global__ __launch_bounds__(256) void k_gemv_lds(const uint8_t* __restrict__ W,
+template <int FMT, int MT, int ITERS, bool XREG, int WPG = 4>
+__global__ __launch_bounds__(64 * WPG) void k_gemv_lds(const uint8_t* __restrict__ W,
                                                   const uint16_t* __restrict__ x,
                                                   float* __restrict__ y, int N, int K, int log2g,
                                                   int m0, int passes) {
   extern __shared__ u32x4 x_lds4[];
   uint32_t* xl = reinterpret_cast<uint32_t*>(x_lds4);
   const int lane = threadIdx.x & 63;
-  const int wave = blockIdx.x * 4 + wave_id();
+  const int wave = blockIdx.x * WPG + wave_id();
   const int G = 1 << log2g;
   const int rpw = 64 >> log2g;
   const int64_t row_base = (int64_t)wave * rpw;
@@ -97,7 +97,7 @@ __global__ __launch_bounds__(256) void k_gemv_lds(const uint8_t* __restrict__ W,
   if constexpr (XREG) {
 #pragma unroll
     for (int c = 0; c < XCH; ++c) {
-      const int i = (int)threadIdx.x + 256 * c;
+      const int i = (int)threadIdx.x + 64 * WPG * c;
       xr[c] = i < n16 ? xsrc[i] : u32x4{0u, 0u, 0u, 0u};
     }
   }
@@ -109,7 +109,7 @@ __global__ __launch_bounds__(256) void k_gemv_lds(const uint8_t* __restrict__ W,
     u32x4* xl4 = reinterpret_cast<u32x4*>(xl);
 #pragma unroll
     for (int c = 0; c < XCH; ++c) {
-      const int i = (int)threadIdx.x + 256 * c;
+      const int i = (int)threadIdx.x + 64 * WPG * c;
       if (i < n16) xl4[i] = xr[c];
     }
   } else {
@@ -280,6 +280,7 @@ struct LdsCfg {
   int log2g;
   int iters;
   int passes;
+  int wpg;     // waves per workgroup (one staged copy of x per workgroup)
 };
 
 // G (lanes per row, power of two) and ITERS (units per lane per pass): G
@@ -288,15 +289,21 @@ struct LdsCfg {
 // (8 per CU) and lanes would still have work, so small matrices spread over
 // more waves. On MI355X (cold weights, graph-replayed) this picks the fastest
 // or nearly fastest G for the 4B-shaped projections and the Q8_0 lm_head.
+// Outputs with at least LARGE_N rows (a vocabulary-sized output layer) have
+// waves to spare, and there longer runs per lane (LANE_BYTES_LARGE) measure
+// faster (Q8_0 151936 x 2560: 67 us at G = 16 against 78 us at G = 32).
 constexpr int LANE_BYTES = 128;
+constexpr int LANE_BYTES_LARGE = 200;
+constexpr int64_t LARGE_N = 65536;
 
 LdsCfg lds_cfg(int64_t N, int units, int unit_bytes) {
   int G = 64;
   int best = -1;
+  const int target = N >= LARGE_N ? LANE_BYTES_LARGE : LANE_BYTES;
   for (int g = 64; g >= 1; g >>= 1) {
     const int iters = (units + g - 1) / g;
     if (iters > MAX_ITERS) break;
-    const int dev = iters * unit_bytes > LANE_BYTES ? iters * unit_bytes - LANE_BYTES : LANE_BYTES - iters * unit_bytes;
+    const int dev = iters * unit_bytes > target ? iters * unit_bytes - target : target - iters * unit_bytes;
     if (best < 0 || dev < best) {
       best = dev;
       G = g;
@@ -308,22 +315,34 @@ LdsCfg lds_cfg(int64_t N, int units, int unit_bytes) {
   int iters = (units + G - 1) / G;
   if (iters > MAX_ITERS) iters = MAX_ITERS;
   const int passes = (units + G * iters - 1) / (G * iters);
-  return {ilog2(G), iters, passes};
+  int wpg = 4;
+  const int env_w = env_int("KQ_LDS_WPG");
+  if (env_w == 4 || env_w == 8 || env_w == 16) wpg = env_w;
+  return {ilog2(G), iters, passes, wpg};
+}
+
+template <int FMT, int MT, int ITERS, int WPG>
+int launch_lds_wpg(const GemvArgs& a, int m0, LdsCfg c) {
+  const int64_t rpw = 64 >> c.log2g;
+  const int64_t waves = (a.N + rpw - 1) / rpw;
+  const dim3 grid((unsigned)((waves + WPG - 1) / WPG)), block(64 * WPG);
+  const size_t lds = (size_t)MT * a.K * 2 + (size_t)MT * (a.K / 32) * 8;  // x + block sums
+  if ((int64_t)MT * a.K / 8 <= 64 * WPG * XREG_CHUNKS)
+    hipLaunchKernelGGL((k_gemv_lds<FMT, MT, ITERS, true, WPG>), grid, block, lds, a.stream, a.W, a.x, a.y,
+                       (int)a.N, (int)a.K, c.log2g, m0, c.passes);
+  else
+    hipLaunchKernelGGL((k_gemv_lds<FMT, MT, ITERS, false, WPG>), grid, block, lds, a.stream, a.W, a.x, a.y,
+                       (int)a.N, (int)a.K, c.log2g, m0, c.passes);
+  return (int)hipGetLastError();
 }
 
 template <int FMT, int MT, int ITERS>
 int launch_lds_it(const GemvArgs& a, int m0, LdsCfg c) {
-  const int64_t rpw = 64 >> c.log2g;
-  const int64_t waves = (a.N + rpw - 1) / rpw;
-  const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
-  const size_t lds = (size_t)MT * a.K * 2 + (size_t)MT * (a.K / 32) * 8;  // x + block sums
-  if ((int64_t)MT * a.K / 8 <= 256 * XREG_CHUNKS)
-    hipLaunchKernelGGL((k_gemv_lds<FMT, MT, ITERS, true>), grid, block, lds, a.stream, a.W, a.x, a.y, (int)a.N,
-                       (int)a.K, c.log2g, m0, c.passes);
-  else
-    hipLaunchKernelGGL((k_gemv_lds<FMT, MT, ITERS, false>), grid, block, lds, a.stream, a.W, a.x, a.y, (int)a.N,
-                       (int)a.K, c.log2g, m0, c.passes);
-  return (int)hipGetLastError();
+  if constexpr (MT == 1) {
+    if (c.wpg == 16) return launch_lds_wpg<FMT, MT, ITERS, 16>(a, m0, c);
+    if (c.wpg == 8) return launch_lds_wpg<FMT, MT, ITERS, 8>(a, m0, c);
+  }
+  return launch_lds_wpg<FMT, MT, ITERS, 4>(a, m0, c);
 }
 
 template <int FMT, int MT>
