@@ -271,6 +271,142 @@ def kernel_table(torch, ds, reps=10):
     return out
 
 
+def _graph_time_us(torch, fns, reps, per):
+    """Median over `reps` replays of a graph of `fns`, divided by `per`."""
+    g = capture(torch, lambda: [f() for f in fns])
+    t, _, _ = time_graph(torch, g, reps, 2)
+    del g
+    return float(np.median(t)) * 1000.0 / per, [float(np.percentile(t, q)) * 1000.0 / per for q in (10, 50, 90)]
+
+
+def bench_single_q8_0(torch, kq, S):
+    """Config 1: one Q8_0 1024x1024 GEMV, M=1 (seeded weights and x). Cold:
+    rotating through copies totalling >= 1 GB (four times the 256 MB
+    last-level cache); warm: one copy, back to back. Each launch in a graph:
+    the time includes the dispatch gap between dependent kernels."""
+    c = S.SINGLE_Q8_0
+    W = S.weights(c.weight_seed, c.n, c.k)
+    packed = torch.from_numpy(kq.kq_pack(c.fmt, W)).to("cuda")
+    x = torch.from_numpy(S.activation_column(c.act_seed, c.k)[None, :]).to("cuda")
+    y = torch.empty((1, c.n), dtype=torch.float32, device="cuda")
+    alg = packed.numel() + x.numel() * 2 + y.numel() * 4
+    copies = (1 << 30) // packed.numel() + 1
+    Ws = packed.reshape(-1).repeat(copies).view(copies, -1)
+    cold, cold_p = _graph_time_us(torch, [lambda i=i: kq.kq_gemv(c.fmt, Ws[i], x, y, c.n, c.k, 1)
+                                          for i in range(copies)], 7, copies)
+    warm, warm_p = _graph_time_us(torch, [lambda: kq.kq_gemv(c.fmt, packed, x, y, c.n, c.k, 1)] * 200, 7, 200)
+    del Ws
+    return {"shape": f"q8_0 {c.n}x{c.k}, M=1", "alg_bytes": int(alg), "cold_copies": int(copies),
+            "us_per_call_cold": cold, "gbps_cold": alg / (cold * 1e-6) / 1e9, "us_p10_p50_p90_cold": cold_p,
+            "us_per_call_warm": warm, "gbps_warm": alg / (warm * 1e-6) / 1e9}
+
+
+def bench_small_stack(torch, kq, S, steps):
+    """Config 2: the 0.6B-shaped Q4_0 stack (28 layers, q|k|v, o, gate|up,
+    down per layer), M=1, in decode order. Its 248 MB fit the 256 MB
+    last-level cache, so the cold figure rotates through 4 copies of the
+    packed weights (the same bytes at four addresses); warm replays one."""
+    st = S.QWEN3_0_6B_Q4_0
+    ds = DeviceStack(torch, kq, S, st, 1)
+    copies = 4
+    banks = [[[Wd.clone() for (_, Wd, *_r) in row] for row in ds.groups] for _ in range(copies - 1)]
+
+    def step_copy(cpy):
+        for layer, row in enumerate(ds.groups):
+            for gi, (fmt, Wd, xd, yd, N, K, _) in enumerate(row):
+                W = Wd if cpy == 0 else banks[cpy - 1][layer][gi]
+                kq.kq_gemv(fmt, W, xd, yd, N, K, 1)
+    cold, cold_p = _graph_time_us(torch, [lambda c=c: step_copy(c) for c in range(copies)], steps, copies)
+    warm, warm_p = _graph_time_us(torch, [lambda: step_copy(0)], steps, 1)
+    out = {"workload": f"{st.name}, M=1, one decode token ({st.layers} layers x 4 launches)",
+           "alg_bytes_per_step": int(ds.alg_bytes), "weight_bytes": int(ds.weight_bytes),
+           "us_per_step_cold": cold, "us_p10_p50_p90_cold": cold_p,
+           "gbps_cold": ds.alg_bytes / (cold * 1e-6) / 1e9, "tokens_per_s_cold": 1e6 / cold,
+           "us_per_step_warm": warm, "gbps_warm": ds.alg_bytes / (warm * 1e-6) / 1e9,
+           "tokens_per_s_warm": 1e6 / warm}
+    del banks, ds
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_verify_all(torch, kq, S, ds, t1_ms, steps):
+    """Config 4: the verify pass at every M on the resident 4B-shaped
+    weights: time per pass, t(M)/t(1), M / t as the upper bound on accepted
+    tokens per second."""
+    out = {}
+    for M in S.VERIFY_M:
+        dv = ds.with_columns(S, M, S.VERIFY_WORKLOAD_ID)
+        g = capture(torch, dv.step)
+        per, total, _ = time_graph(torch, g, steps, 3)
+        ms = float(np.median(per))
+        out[str(M)] = {"ms_per_pass": ms, "ms_p10_p90": [float(np.percentile(per, 10)), float(np.percentile(per, 90))],
+                       "alg_bytes": int(dv.alg_bytes), "gbps": dv.alg_bytes / (ms * 1e-3) / 1e9,
+                       "t_ratio_vs_m1": ms / t1_ms, "tokens_per_s_upper_bound": M / (ms * 1e-3)}
+        log(f"verify M={M}: {ms * 1000:.1f} us per pass, t(M)/t(1) = {ms / t1_ms:.2f}")
+        del g, dv
+        torch.cuda.empty_cache()
+    return out
+
+
+def bench_moe(torch, kq, S, steps):
+    """Config 5: the Q4_0 MoE layer (128 experts, hidden 2048, FFN 768,
+    top-8) through kq_moe_ffn at M in {1, 4, 16} tokens, with the workload's
+    route tables. One expert's packed gate/up/down (seeded) is replicated to
+    all 128 experts (time does not depend on values) and the whole set to 3
+    copies (1 GB) that the timed calls rotate through. Algorithmic bytes:
+    the unique routed experts' weights, plus activations, h and outputs."""
+    L = S.MOE_Q4_0
+    E = L.n_experts
+    mats = []
+    for which, (n, k) in enumerate(((L.inter, L.hidden), (L.inter, L.hidden), (L.hidden, L.inter))):
+        W = S.weights(L.weight_seed(0, which), n, k)
+        mats.append(torch.from_numpy(kq.kq_pack(L.fmt, W)).to("cuda"))
+    per_expert = sum(m.numel() for m in mats)
+    copies = 3
+    banks = [[m.reshape(-1).repeat(E) for m in mats] for _ in range(copies)]
+    out = {}
+    for M in S.MOE_M:
+        ids, rw = S.route_table(L.workload_id, M, E, L.top_k)
+        U = len(np.unique(ids))
+        x = torch.from_numpy(S.activations(L.act_seed_prefix(), L.hidden, M)).to("cuda")
+        idd = torch.from_numpy(ids).to("cuda")
+        rwd = torch.from_numpy(rw).to("cuda")
+        y = torch.empty((M, L.hidden), dtype=torch.float32, device="cuda")
+        h = torch.empty((M, L.top_k, L.inter), dtype=torch.float16, device="cuda")
+        wsb = kq.kq_moe_ffn_workspace_bytes(L.hidden, L.inter, M, L.top_k)
+        ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+        fns = [lambda c=c: kq.kq_moe_ffn(L.fmt, banks[c][0], banks[c][1], banks[c][2], x, idd, rwd, y, h,
+                                         L.hidden, L.inter, M, L.top_k, E, ws, wsb) for c in range(copies)]
+        us, p = _graph_time_us(torch, fns * 4, steps, 4 * copies)
+        alg = U * per_expert + x.numel() * 2 + 2 * h.numel() * 2 + y.numel() * 4
+        out[str(M)] = {"unique_experts": int(U), "alg_bytes": int(alg), "us_per_layer": us, "us_p10_p50_p90": p,
+                       "gbps": alg / (us * 1e-6) / 1e9, "tokens_per_s_per_layer": M / (us * 1e-6)}
+        log(f"moe M={M}: {U} experts, {us:.1f} us per layer, {alg / (us * 1e-6) / 1e9:.0f} GB/s")
+    del banks
+    torch.cuda.empty_cache()
+    return out
+
+
+def stream_ceiling(torch):
+    """A measured read-only streaming rate on this GPU: torch's sum over 1 GiB
+    of fp32 (a library reduction kernel), median of 10."""
+    a = torch.ones((1 << 28,), dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        a.sum()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(10):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        a.sum()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    del a
+    torch.cuda.empty_cache()
+    return {"kernel": "torch.sum over 1 GiB fp32", "gbps": (1 << 30) / (float(np.median(ts)) * 1e-3) / 1e9}
+
+
 def cpu_baseline(S, stack, kq, budget_s=15.0):
     """The oracle as it stands (decode packed bytes, dequantize, fp64 dot) on
     the host cores, on a bounded sample: the lm_head plus as many layers of
@@ -327,7 +463,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-verify", action="store_true", help="skip the M=8 verify measurement")
+    ap.add_argument("--no-verify", action="store_true", help="skip the verify measurements (M > 1)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other configurations (single Q8_0 GEMV, 0.6B stack, MoE layer)")
     ap.add_argument("--kernels-only", action="store_true",
                     help="short run for counter collection: per-kernel graphs and a copy of known size")
     args = ap.parse_args()
@@ -424,6 +562,22 @@ def main():
         del gv, dv
         torch.cuda.empty_cache()
 
+    configs = None
+    if not args.no_verify:
+        verify_all = bench_verify_all(torch, kq, S, ds, float(np.median(per)), max(5, args.steps // 2))
+    else:
+        verify_all = None
+    alg_bytes_step = ds.alg_bytes
+    if not args.no_configs:
+        del ds
+        torch.cuda.empty_cache()
+        configs = {"single_q8_0": bench_single_q8_0(torch, kq, S)}
+        log(f"single q8_0: {configs['single_q8_0']['us_per_call_cold']:.2f} us cold")
+        configs["qwen3_0.6b_q4_0_stack"] = bench_small_stack(torch, kq, S, args.steps)
+        log(f"0.6B stack: {configs['qwen3_0.6b_q4_0_stack']['us_per_step_cold']:.1f} us cold")
+        configs["moe_q4_0"] = bench_moe(torch, kq, S, max(5, args.steps // 2))
+        configs["stream_ceiling"] = stream_ceiling(torch)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on 2 layers + lm_head ...")
@@ -450,10 +604,12 @@ def main():
         "step_us_p10_p50_p90": [float(np.percentile(per, q)) * 1000 for q in (10, 50, 90)],
         "path": path,
         "other_path": other,
-        "alg_bytes_per_step": ds.alg_bytes,
+        "alg_bytes_per_step": alg_bytes_step,
         "roofline": roofline,
         "kernels": ktab,
         "verify_m8": verify,
+        "verify_all": verify_all,
+        "other_configs": configs,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))

@@ -509,6 +509,208 @@ __global__ __launch_bounds__(1024) void k_gemv_mfma_lds(const uint8_t* __restric
   }
 }
 
+// Many columns (T tiles of 16) or long rows: the workgroup walks K in chunks
+// of CG 4-block groups (CG a power of two), staging x of the chunk for all T
+// column tiles at once (tile t at t * 4096 CG bytes, each in the operand
+// order above with Mp = 16), with block sums. Per chunk, each wave loads its
+// P groups of the chunk, then consumes them: the dequantized weights of a
+// block serve all T column tiles. R row tiles x S waves per workgroup (at most
+// 8 waves: the staged pieces, the loaded groups and T accumulators need more
+// than the 128 registers of a 16-wave workgroup); the S partial results of a
+// tile are summed in a fixed order at the end.
+template <int FMT, int P, int T>
+__global__ __launch_bounds__(512) void k_gemv_mfma_chunk(const uint8_t* __restrict__ W,
+                                                         const uint16_t* __restrict__ x,
+                                                         float* __restrict__ y, int N, int K, int M, int R,
+                                                         int S, int log2cg) {
+  extern __shared__ u32x4 xl4[];
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  const int r = wave / S, s = wave - r * S;
+  const int n = lane & 15, g = lane >> 4;
+  const int64_t row0 = ((int64_t)blockIdx.x * R + r) * 16;
+  const int nblk = K / 32;
+  const int ngroups = (nblk + 3) / 4;
+  const int CG = 1 << log2cg;
+  const int nchunks = (ngroups + CG - 1) / CG;
+  const uint32_t row_bytes = (uint32_t)nblk * Fmt<FMT>::BB;
+  const int valid_rows = row0 < N ? (int)min<int64_t>(16, N - row0) : 0;
+  const rsrc_t rs = make_rsrc(W + (valid_rows ? row0 * row_bytes : 0), ((uint32_t)valid_rows * row_bytes + 3u) & ~3u);
+  const uint32_t roff = (uint32_t)n * row_bytes;
+  const bool row_ok = n < valid_rows;
+  uint8_t* xlb = reinterpret_cast<uint8_t*>(xl4);
+  const int kq8 = K / 8;
+  const uint32_t tile_bytes = 4096u << log2cg;                 // x of one column tile, one chunk (4 CG blocks x 1 KB)
+  const uint32_t sx_base = (uint32_t)T * tile_bytes;           // fp32 [T][4 CG][16]
+  const uint32_t dummy = sx_base + (uint32_t)T * (64u << log2cg) * 4u;
+  const int npieces = T * (256 << log2cg);
+  const int nthreads = (int)blockDim.x;
+  const rsrc_t xs = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
+  float4_t acc[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) acc[t] = float4_t{0.f, 0.f, 0.f, 0.f};
+  const half8_t ones = as_half8(ONES, ONES, ONES, ONES);
+  (void)ones;
+
+  for (int c = 0; c < nchunks; ++c) {
+    const int cg0 = c * CG;
+    const int gb = cg0 + s * P;                // this wave's first group of the chunk
+    const int ge = min(gb + P, min(cg0 + CG, ngroups));
+    // 1. x pieces of the chunk: piece i is tile i >> (8 + log2cg), then column
+    //    i & 15, then chunk piece (i >> 4) & (16 CG - 1)
+    u32x4 xr[XST_MAX];
+#pragma unroll
+    for (int q = 0; q < XST_MAX; ++q) {
+      const int i = (int)threadIdx.x + nthreads * q;
+      const int t = i >> (8 + log2cg);
+      const int col = 16 * t + (i & 15);
+      const int k8 = 16 * cg0 + ((i >> 4) & ((16 << log2cg) - 1));
+      const bool ok = i < npieces && col < M && k8 < kq8;
+      xr[q] = ld128(xs, ok ? ((uint32_t)col * (uint32_t)kq8 + (uint32_t)k8) * 16u : OOB);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    // 2. this wave's weights of the chunk
+    GroupRaw<FMT> wr[P];
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const int gi = gb + p;
+      load_group<FMT>(rs, roff, 4 * gi + g, gi < ge && row_ok && 4 * gi + g < nblk, wr[p]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // 3. x into LDS (branch-free, as above)
+#pragma unroll
+    for (int q = 0; q < XST_MAX; ++q) {
+      const int i = (int)threadIdx.x + nthreads * q;
+      const int t = i >> (8 + log2cg);
+      const int col = i & 15, k8l = (i >> 4) & ((16 << log2cg) - 1);
+      const int bb = k8l >> 2, h = k8l & 3;
+      const int g0 = 2 * (h & 1);
+      const uint32_t part = 8u * (uint32_t)(h >> 1);
+      const bool ok = i < npieces;
+      const uint32_t base = (uint32_t)t * tile_bytes;
+      const uint32_t a0 = ok ? base + (uint32_t)((4 * bb + g0) * 16 + col) * 16u + part : dummy;
+      const uint32_t a1 = ok ? base + (uint32_t)((4 * bb + g0 + 1) * 16 + col) * 16u + part : dummy + 8u;
+      *reinterpret_cast<u32x2*>(xlb + a0) = u32x2{xr[q].x, xr[q].y};
+      *reinterpret_cast<u32x2*>(xlb + a1) = u32x2{xr[q].z, xr[q].w};
+    }
+    __syncthreads();
+    // 4. block sums of the chunk
+    {
+      float* sx = reinterpret_cast<float*>(xlb + sx_base);
+      const int ntask = T * (64 << log2cg);
+      for (int tk = (int)threadIdx.x; tk < ntask; tk += nthreads) {
+        const int t = tk >> (6 + log2cg), rem = tk & ((64 << log2cg) - 1);
+        const int bb = rem >> 4, col = rem & 15;
+        const u32x4* xt = reinterpret_cast<const u32x4*>(xlb + (uint32_t)t * tile_bytes);
+        float v = 0.0f;
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+          const u32x4 qv = xt[(4 * bb + gg) * 16 + col];
+          v = dot2(qv.x, ONES, v);
+          v = dot2(qv.y, ONES, v);
+          v = dot2(qv.z, ONES, v);
+          v = dot2(qv.w, ONES, v);
+        }
+        sx[tk] = v;
+      }
+    }
+    __syncthreads();
+    // 5. multiply: local group index gl = gi - cg0 addresses the chunk's LDS
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const int gi = gb + p;
+      if (gi >= ge) break;   // uniform
+      const int gl = gi - cg0;
+      const GroupRaw<FMT>& cur = wr[p];
+      uint32_t hdr, q0, q1, q2, q3, p0 = 0, p1 = 0, p2 = 0, p3 = 0;
+      if constexpr (FMT == F_AFFINE4) {
+        hdr = cur.D[0];
+        q0 = cur.D[1]; q1 = cur.D[2]; q2 = cur.D[3]; q3 = cur.D[4];
+      } else {
+        const uint32_t r2 = ((roff + (uint32_t)(4 * gi + g) * Fmt<FMT>::BB + 2u) & 3u) * 8u;
+        hdr = r2 ? (cur.D[1] & 0xffffu) : (cur.D[0] >> 16);
+        const uint32_t sh = r2 >> 3;
+        q0 = __builtin_amdgcn_alignbyte(cur.D[2], cur.D[1], sh);
+        q1 = __builtin_amdgcn_alignbyte(cur.D[3], cur.D[2], sh);
+        q2 = __builtin_amdgcn_alignbyte(cur.D[4], cur.D[3], sh);
+        q3 = __builtin_amdgcn_alignbyte(cur.D[5], cur.D[4], sh);
+        if constexpr (FMT == F_Q8_0) {
+          p0 = __builtin_amdgcn_alignbyte(cur.D[6], cur.D[5], sh);
+          p1 = __builtin_amdgcn_alignbyte(cur.D[7], cur.D[6], sh);
+          p2 = __builtin_amdgcn_alignbyte(cur.D[8], cur.D[7], sh);
+          p3 = __builtin_amdgcn_alignbyte(cur.D[9], cur.D[8], sh);
+        }
+      }
+      {
+        float cown;
+        const float so = h2f(hdr);
+        if constexpr (FMT == F_AFFINE4) cown = __builtin_fmaf(-1024.0f, so, h2f(hdr >> 16));
+        else if constexpr (FMT == F_Q4_0) cown = -1032.0f * so;
+        else cown = -1152.0f * so;
+        const float* sx = reinterpret_cast<const float*>(xlb + sx_base);
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(sx[(t << (6 + log2cg)) + (4 * gl + g) * 16 + n], cown,
+                                                        acc[t], 0, 0, 0);
+      }
+      transpose4(q0, q1, q2, q3);
+      if constexpr (FMT == F_Q8_0) transpose4(p0, p1, p2, p3);
+      uint32_t h0 = hdr, h1 = hdr, h2 = hdr, h3 = hdr;
+      transpose4(h0, h1, h2, h3);
+      const uint32_t qs[4] = {q0, q1, q2, q3};
+      const uint32_t ps[4] = {p0, p1, p2, p3};
+      const uint32_t hs[4] = {h0, h1, h2, h3};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t b0, b1, b2, b3;
+        if constexpr (FMT == F_Q8_0) {
+          const uint32_t u = qs[j] ^ 0x80808080u, v = ps[j] ^ 0x80808080u;
+          b0 = perm(MAGIC, u, SEL_LO); b1 = perm(MAGIC, u, SEL_HI);
+          b2 = perm(MAGIC, v, SEL_LO); b3 = perm(MAGIC, v, SEL_HI);
+        } else {
+          const uint32_t lo = qs[j] & 0x0F0F0F0Fu, hi = (qs[j] >> 4) & 0x0F0F0F0Fu;
+          b0 = perm(MAGIC, lo, SEL_LO); b1 = perm(MAGIC, lo, SEL_HI);
+          b2 = perm(MAGIC, hi, SEL_LO); b3 = perm(MAGIC, hi, SEL_HI);
+        }
+        const half8_t B = as_half8(b0, b1, b2, b3);
+        const float sc = h2f(hs[j]);
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          const u32x4* xt = reinterpret_cast<const u32x4*>(xlb + (uint32_t)t * tile_bytes);
+          const half8_t A = __builtin_bit_cast(half8_t, xt[(4 * (4 * gl + j) + g) * 16 + n]);
+          const float4_t D = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[t][v] = __builtin_fmaf(sc, D[v], acc[t][v]);
+        }
+      }
+    }
+    __syncthreads();   // the chunk's LDS is restaged next
+  }
+  // fixed-order sum over the S waves of each tile (the x area is reused)
+  float4_t* red = reinterpret_cast<float4_t*>(xl4);
+#pragma unroll
+  for (int t = 0; t < T; ++t) red[(wave * T + t) * 64 + lane] = acc[t];
+  __syncthreads();
+  if (s == 0 && valid_rows > 0) {
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      float4_t sum = red[((r * S) * T + t) * 64 + lane];
+      for (int w = 1; w < S; ++w) {
+        const float4_t o = red[((r * S + w) * T + t) * 64 + lane];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sum[v] += o[v];
+      }
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int col = 16 * t + 4 * g + v;
+        if (col < M && row_ok) y[(int64_t)col * N + row0 + n] = sum[v];
+      }
+    }
+  }
+}
+
 constexpr int MFMA_PERS_TPW = 8;   // tiles per wave at most
 
 template <int FMT, int P>
@@ -677,9 +879,9 @@ MfmaLdsCfg mfma_lds_cfg(int64_t N, int64_t K, int M, int maxp, bool no_sums) {
     if (v >= 1 && v <= 16) S = v;
   }
   if (S > ngroups) S = ngroups;
-  const int P = (ngroups + S - 1) / S;
-  if (P > maxp) return c;
-  S = (ngroups + P - 1) / P;
+  const int P1 = (ngroups + S - 1) / S;
+  if (P1 > maxp) return c;
+  S = (ngroups + P1 - 1) / P1;
   int R = 1;
   while (2 * R * S <= 8 && (tiles + 2 * R - 1) / (2 * R) >= 1024) R *= 2;
   const char* er = getenv("KQ_MFMA_R");
@@ -690,6 +892,15 @@ MfmaLdsCfg mfma_lds_cfg(int64_t N, int64_t K, int M, int maxp, bool no_sums) {
   int log2mp = 0;
   while ((1 << log2mp) < M) ++log2mp;
   const int64_t pieces = ((int64_t)1 << log2mp) * 16 * ngroups;   // x padded to whole groups
+  // enough threads to stage x (at most XST_MAX pieces each): more tiles per
+  // workgroup, else more waves per tile
+  while (pieces > (int64_t)XST_MAX * 64 * R * S && 2 * R * S <= 16 && (tiles + 2 * R - 1) / (2 * R) >= 256) R *= 2;
+  while (pieces > (int64_t)XST_MAX * 64 * R * S && R * (S + 1) <= 16 && S < ngroups) {
+    ++S;
+  }
+  const int P2 = (ngroups + S - 1) / S;
+  const int P = P2 < P1 ? P2 : P1;
+  S = (ngroups + P - 1) / P;
   const int64_t rbytes = (int64_t)R * S * 64 * 16;
   if (pieces > (int64_t)XST_MAX * 64 * R * S) return c;
   for (int sums = no_sums ? 0 : 1; sums >= 0; --sums) {
@@ -730,6 +941,80 @@ int launch_mfma_lds(const GemvArgs& a, int m0, int mt, const MfmaLdsCfg& c) {
   return c.sx ? launch_mfma_lds_sx<FMT, true>(a, m0, mt, c) : launch_mfma_lds_sx<FMT, false>(a, m0, mt, c);
 }
 
+struct MfmaChunkCfg {
+  int R, S, P, log2cg;
+  size_t lds;
+  bool ok;
+};
+
+// Groups per wave per chunk at most, by registers (T column tiles).
+template <int FMT, int T> struct MfmaChunkMaxP {
+  static constexpr int v = T == 1 ? (FMT == F_Q8_0 ? 4 : 6) : (T == 2 ? 3 : 2);
+};
+
+// Chunk of CG groups: the largest power of two (at most the row's group count
+// rounded up) whose x and block sums for all T tiles fit in 128 KB and need at
+// most XST_MAX pieces per thread of an 8-wave workgroup. Waves per tile S:
+// at most maxp groups each, more (smaller P) while the grid has fewer than
+// 2048 waves. Tiles per workgroup R: only as many as staging x needs threads.
+MfmaChunkCfg mfma_chunk_cfg(int64_t N, int64_t K, int T, int maxp) {
+  MfmaChunkCfg c{1, 1, 1, 0, 0, false};
+  const int ngroups = (int)((K / 32 + 3) / 4);
+  const int64_t tiles = (N + 15) / 16;
+  int log2cg = 0;
+  while ((1 << log2cg) < ngroups) ++log2cg;
+  auto x_bytes = [&](int l2) { return (int64_t)T * (4352 << l2) + 16; };   // x (4 KB per group) + sums (256 B per group)
+  while (log2cg > 0 && (x_bytes(log2cg) > 128 * 1024 || (int64_t)T * (256 << log2cg) > (int64_t)XST_MAX * 512)) --log2cg;
+  const int CG = 1 << log2cg;
+  int P = maxp < CG ? maxp : CG;
+  int S = (CG + P - 1) / P;
+  while (S < 8 && P > 1 && tiles * S < 2048) {
+    --P;
+    S = (CG + P - 1) / P;
+  }
+  if (S > 8) return c;
+  int R = 1;
+  const int64_t pieces = (int64_t)T * (256 << log2cg);
+  while (pieces > (int64_t)XST_MAX * 64 * R * S && 2 * R * S <= 8) R *= 2;
+  while (pieces > (int64_t)XST_MAX * 64 * R * S && R * (S + 1) <= 8 && S < CG) ++S;
+  if (pieces > (int64_t)XST_MAX * 64 * R * S) return c;
+  const int64_t xb = x_bytes(log2cg), rb = (int64_t)R * S * T * 1024;
+  const int64_t lds = xb > rb ? xb : rb;
+  if (lds > MFMA_LDS_MAX_BYTES) return c;
+  return {R, S, P, log2cg, (size_t)lds, true};
+}
+
+template <int FMT, int P, int T>
+int launch_mfma_chunk_p(const GemvArgs& a, int m0, int mt, const MfmaChunkCfg& c) {
+  const int64_t tiles = (a.N + 15) / 16;
+  const dim3 grid((unsigned)((tiles + c.R - 1) / c.R)), block((unsigned)(64 * c.R * c.S));
+  hipLaunchKernelGGL((k_gemv_mfma_chunk<FMT, P, T>), grid, block, c.lds, a.stream, a.W, a.x + (int64_t)m0 * a.K,
+                     a.y + (int64_t)m0 * a.N, (int)a.N, (int)a.K, mt, c.R, c.S, c.log2cg);
+  return (int)hipGetLastError();
+}
+
+template <int FMT, int T>
+int launch_mfma_chunk(const GemvArgs& a, int m0, int mt) {
+  const MfmaChunkCfg c = mfma_chunk_cfg(a.N, a.K, T, MfmaChunkMaxP<FMT, T>::v);
+  if (!c.ok) return -1;   // not applicable: the caller falls back
+  switch (c.P) {
+    case 1: return launch_mfma_chunk_p<FMT, 1, T>(a, m0, mt, c);
+    case 2: return launch_mfma_chunk_p<FMT, 2, T>(a, m0, mt, c);
+    case 3:
+      if constexpr (MfmaChunkMaxP<FMT, T>::v >= 3) return launch_mfma_chunk_p<FMT, 3, T>(a, m0, mt, c);
+      return (int)hipErrorInvalidValue;
+    case 4:
+      if constexpr (MfmaChunkMaxP<FMT, T>::v >= 4) return launch_mfma_chunk_p<FMT, 4, T>(a, m0, mt, c);
+      return (int)hipErrorInvalidValue;
+    case 5:
+      if constexpr (MfmaChunkMaxP<FMT, T>::v >= 5) return launch_mfma_chunk_p<FMT, 5, T>(a, m0, mt, c);
+      return (int)hipErrorInvalidValue;
+    default:
+      if constexpr (MfmaChunkMaxP<FMT, T>::v >= 6) return launch_mfma_chunk_p<FMT, 6, T>(a, m0, mt, c);
+      return (int)hipErrorInvalidValue;
+  }
+}
+
 // Persistent waves for many tiles: 8 waves per workgroup, as many workgroups
 // as fit at once (up to one wave per tile), tiles dealt evenly: tpw =
 // ceil(tiles / waves) (at most MFMA_PERS_TPW), then only as many waves as
@@ -763,14 +1048,18 @@ template <int FMT> struct MfmaPersP { static constexpr int v = FMT == F_Q8_0 ? 6
 // wave) fill the device; below it, tiles are split over the waves of a workgroup.
 constexpr int64_t MFMA_PERS_MIN_TILES = 4096;
 
-// KQ_MFMA_VARIANT (tests and sweeps) forces one kernel where it applies:
-// "pers", "teams", "teams_nosx" (block sums by MFMA) or "direct".
+// Order: persistent waves (many tiles, M <= 16), split-K teams with all of x
+// in LDS (M <= 16), K-chunked staging (any M up to 64 per launch), and per-wave
+// activation loads as the fallback. KQ_MFMA_VARIANT (tests and sweeps) forces
+// one kernel where it applies: "pers", "teams", "teams_nosx" (block sums by
+// MFMA), "chunk" or "direct".
 template <int FMT>
 int launch_mfma_fmt(const GemvArgs& a) {
   const char* var = getenv("KQ_MFMA_VARIANT");
   const bool want_direct = var && !strcmp(var, "direct");
   const bool want_pers = var && !strcmp(var, "pers");
   const bool want_teams = var && !strncmp(var, "teams", 5);
+  const bool want_chunk = var && !strcmp(var, "chunk");
   if (a.M <= 16 && !want_direct) {
     const int64_t tiles = (a.N + 15) / 16;
     const int ngroups = (int)((a.K / 32 + 3) / 4);
@@ -778,15 +1067,23 @@ int launch_mfma_fmt(const GemvArgs& a) {
     while ((1 << log2mp) < a.M) ++log2mp;
     const int64_t pieces = ((int64_t)1 << log2mp) * 16 * ngroups;
     const int64_t lds = mfma_x_lds_bytes(a.K, log2mp, true);
-    if ((tiles >= MFMA_PERS_MIN_TILES || want_pers) && !want_teams && lds <= MFMA_LDS_MAX_BYTES &&
+    if ((tiles >= MFMA_PERS_MIN_TILES || want_pers) && !want_teams && !want_chunk && lds <= MFMA_LDS_MAX_BYTES &&
         pieces <= (int64_t)XST_MAX * 512)
       return launch_mfma_pers_p<FMT, MfmaPersP<FMT>::v>(a, log2mp, (size_t)lds);
     const MfmaLdsCfg c = mfma_lds_cfg(a.N, a.K, (int)a.M, MfmaLdsMaxP<FMT>::v, var && !strcmp(var, "teams_nosx"));
-    if (c.ok) return launch_mfma_lds<FMT>(a, 0, (int)a.M, c);
+    if (c.ok && !want_chunk) return launch_mfma_lds<FMT>(a, 0, (int)a.M, c);
   }
   for (int m0 = 0; m0 < a.M; m0 += 64) {
     const int mt = a.M - m0 < 64 ? a.M - m0 : 64;
-    int err;
+    int err = -1;
+    if (!want_direct) {
+      if (mt <= 16) err = launch_mfma_chunk<FMT, 1>(a, m0, mt);
+      else if (mt <= 32) err = launch_mfma_chunk<FMT, 2>(a, m0, mt);
+      else if (mt <= 48) err = launch_mfma_chunk<FMT, 3>(a, m0, mt);
+      else err = launch_mfma_chunk<FMT, 4>(a, m0, mt);
+      if (err == 0) continue;
+      if (err != -1) return err;
+    }
     if (mt <= 16) err = launch_mfma_t<FMT, 1>(a, m0, mt);
     else if (mt <= 32) err = launch_mfma_t<FMT, 2>(a, m0, mt);
     else if (mt <= 48) err = launch_mfma_t<FMT, 3>(a, m0, mt);

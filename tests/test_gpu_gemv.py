@@ -178,13 +178,16 @@ def test_zero_and_constant_weights():
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("variant", ("pers", "pers_tpw3", "teams", "teams_nosx", "direct"))
-@pytest.mark.parametrize("N,K,M", [(1000, 2560, 8), (37, 96, 5), (300, 4128, 16), (16, 32, 2), (529, 640, 13)])
+@pytest.mark.parametrize("variant", ("pers", "pers_tpw3", "teams", "teams_nosx", "chunk", "direct"))
+@pytest.mark.parametrize("N,K,M", [(1000, 2560, 8), (37, 96, 5), (300, 4128, 16), (16, 32, 2), (529, 640, 13),
+                                   (300, 4128, 40), (77, 9728, 33)])
 def test_mfma_variants_parity(fmt, variant, N, K, M):
     """Each matrix-core kernel (the dispatcher picks one by shape: persistent
     waves for many tiles, split-K teams with x staged in LDS with or without
-    block sums, per-wave activation loads) on ragged rows, partial groups and
-    odd block counts; pers_tpw3 gives each wave three tiles."""
+    block sums, K-chunked staging for many columns or long rows, per-wave
+    activation loads) on ragged rows, partial groups and odd block counts;
+    pers_tpw3 gives each wave three tiles. Past 16 columns only the chunked
+    and per-wave kernels apply."""
     packed, fields, x = _case(fmt, N, K, M, 9)
     env = {"KQ_MFMA_VARIANT": variant.split("_tpw")[0]}
     if variant == "pers_tpw3":
