@@ -195,6 +195,146 @@ __global__ __launch_bounds__(256) void k_moe_gate_up(const uint8_t* __restrict__
   }
 }
 
+// Routed-expert GEMV with the tokens' activations staged in LDS (rows of
+// whole load units). Grid (row tiles, M * top_k route slots); the workgroup
+// of slot p owns expert e = ids[p] when no earlier slot names e, and serves
+// every slot routed to e. The route ids are read once into LDS; then, in this
+// order: the activations of the first (up to MOE_COLS) routed tokens into
+// registers, this wave's weight loads (G lanes per row, ITERS units each),
+// the activations into LDS with their block sums, and the products through
+// LDS. More tokens on one expert take further passes, which reload the
+// weights (by then in L2). GATE_UP: W0 = gate, W1 = up of the same rows, and
+// the output is h = fp16(silu(gate . x) * (up . x)); otherwise W0 alone and
+// fp32 per-slot outputs. Dynamic LDS: MOE_COLS columns of x and their block
+// sums, then the ids and the gathered slot list (P ints each), then a 16-byte
+// idle slot. K <= 256 * MOE_XCH * 8 / MOE_COLS.
+constexpr int MOE_XCH = 4;   // 16-byte x pieces per thread per pass
+
+template <int FMT, int ITERS, bool GATE_UP>
+__global__ __launch_bounds__(256) void k_moe_lds(const uint8_t* __restrict__ W0, const uint8_t* __restrict__ W1,
+                                                const uint16_t* __restrict__ x, const int32_t* __restrict__ ids,
+                                                void* __restrict__ out, int N, int K, int M, int top_k,
+                                                int n_experts, int x_per_slot, int log2g, int64_t expert_bytes) {
+  extern __shared__ u32x4 x_lds4[];
+  uint32_t* xl = reinterpret_cast<uint32_t*>(x_lds4);
+  const int kdw = K / 2;
+  const int nblk = K / 32;
+  float* xs = reinterpret_cast<float*>(xl + MOE_COLS * kdw);
+  int* s_ids = reinterpret_cast<int*>(xs + MOE_COLS * nblk * 2);
+  const int P = M * top_k;
+  int* s_list = s_ids + P;
+  __shared__ int s_cnt;
+  const int p = blockIdx.y;
+  // 1. routing: ids into LDS, then the owner test and the gather from LDS
+  for (int q = threadIdx.x; q < P; q += blockDim.x) s_ids[q] = ids[q];
+  __syncthreads();
+  const int e = s_ids[p];
+  int dup = 0;
+  for (int q = threadIdx.x; q < p; q += blockDim.x) dup |= (s_ids[q] == e);
+  if (__syncthreads_or(dup)) return;
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    int cnt = 0;
+    for (int base = p; base < P; base += 64) {
+      const int q = base + lane;
+      const bool hit = q < P && s_ids[q] == e;
+      const uint64_t mask = __ballot(hit);
+      if (hit) s_list[cnt + __popcll(mask & ((1ull << lane) - 1ull))] = q;
+      cnt += __popcll(mask);
+    }
+    if (lane == 0) s_cnt = cnt;
+  }
+  __syncthreads();
+  const int cnt = s_cnt;
+  const int lane = threadIdx.x & 63;
+  const int G = 1 << log2g;
+  const int rpw = 64 >> log2g;
+  const int64_t row_base = (int64_t)(blockIdx.x * 4 + wave_id()) * rpw;
+  const int rho = lane >> log2g, g = lane & (G - 1);
+  if (e < 0 || e >= n_experts) {   // precondition violated: read nothing, flag with NaN
+    if (g == 0 && row_base + rho < N) {
+      for (int c = 0; c < cnt; ++c) {
+        if constexpr (GATE_UP) static_cast<uint16_t*>(out)[(int64_t)s_list[c] * N + row_base + rho] = 0x7e00;
+        else static_cast<float*>(out)[(int64_t)s_list[c] * N + row_base + rho] = __builtin_nanf("");
+      }
+    }
+    return;
+  }
+  const uint32_t row_bytes = (uint32_t)nblk * Fmt<FMT>::BB;
+  const int valid = row_base < N ? (int)min<int64_t>(rpw, N - row_base) : 0;
+  const int64_t off = (int64_t)e * expert_bytes + (valid ? row_base * row_bytes : 0);
+  const rsrc_t r0 = make_rsrc(W0 + off, (uint32_t)valid * row_bytes);
+  const rsrc_t r1 = make_rsrc((GATE_UP ? W1 : W0) + off, (uint32_t)valid * row_bytes);
+  const uint32_t roff = (uint32_t)rho * row_bytes;
+  const int units = K / (32 * Fmt<FMT>::UB);
+  const int kq8 = K / 8;
+  const int xrows = (GATE_UP || !x_per_slot) ? M : P;
+  const rsrc_t xsrc = make_rsrc(x, (uint32_t)xrows * (uint32_t)K * 2u);
+  // a 16-byte slot after the slot list for pieces past the x area
+  const int idle = (int)(((uint32_t)(MOE_COLS * kdw + MOE_COLS * nblk * 2 + 2 * P) * 4u + 15u) / 16u);
+  for (int c0 = 0; c0 < cnt; c0 += MOE_COLS) {
+    const int mt = cnt - c0 < MOE_COLS ? cnt - c0 : MOE_COLS;
+    if (c0 > 0) __syncthreads();   // the previous pass has finished reading LDS
+    // x of this pass's tokens, then the weights (so writing x waits for x alone)
+    // (branch-free: a load used only inside a branch would be moved behind
+    // the weight loads, and writing x would then wait for them too)
+    u32x4 xr[MOE_XCH];
+#pragma unroll
+    for (int c = 0; c < MOE_XCH; ++c) {
+      const int i = (int)threadIdx.x + 256 * c;
+      const int m = i / kq8, k8 = i - m * kq8;
+      const int q = s_list[c0 + (m < mt ? m : 0)];
+      const uint32_t xrow = (uint32_t)((GATE_UP || !x_per_slot) ? q / top_k : q);
+      xr[c] = ld128(xsrc, m < mt ? (xrow * (uint32_t)kq8 + (uint32_t)k8) * 16u : OOB);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    Loaded<FMT, ITERS> w0, w1;
+    issue_units<FMT, ITERS>(r0, roff, g, G, units, w0);
+    if constexpr (GATE_UP) issue_units<FMT, ITERS>(r1, roff, g, G, units, w1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int c = 0; c < MOE_XCH; ++c) {
+      const int i = (int)threadIdx.x + 256 * c;
+      x_lds4[i < MOE_COLS * kq8 ? i : idle] = xr[c];   // unused pieces land past the x of this pass
+    }
+    __syncthreads();
+    block_sums_to_lds(xl, kdw, mt, xs);
+    __syncthreads();
+    float a0[MOE_COLS], a1[MOE_COLS];
+#pragma unroll
+    for (int m = 0; m < MOE_COLS; ++m) a0[m] = a1[m] = 0.0f;
+    switch (mt) {
+#define KQ_MOE_CONSUME(MTV)                                                                                  \
+  case MTV: {                                                                                                \
+    float b0[MTV], b1[MTV];                                                                                  \
+    for (int m = 0; m < MTV; ++m) b0[m] = b1[m] = 0.0f;                                                      \
+    consume_units<FMT, MTV, ITERS>(w0, xl, xs, kdw, g, G, units, b0);                                        \
+    if constexpr (GATE_UP) consume_units<FMT, MTV, ITERS>(w1, xl, xs, kdw, g, G, units, b1);                 \
+    group_reduce<MTV>(b0, G);                                                                                \
+    if constexpr (GATE_UP) group_reduce<MTV>(b1, G);                                                         \
+    for (int m = 0; m < MTV; ++m) { a0[m] = b0[m]; a1[m] = b1[m]; }                                          \
+    break;                                                                                                   \
+  }
+      KQ_MOE_CONSUME(1)
+      KQ_MOE_CONSUME(2)
+      KQ_MOE_CONSUME(3)
+      default: KQ_MOE_CONSUME(4)
+#undef KQ_MOE_CONSUME
+    }
+    if (g == 0 && rho < valid) {
+      for (int m = 0; m < mt; ++m) {
+        const int64_t o = (int64_t)s_list[c0 + m] * N + row_base + rho;
+        if constexpr (GATE_UP) {
+          const float z = a0[m];
+          static_cast<uint16_t*>(out)[o] = (uint16_t)f2h_bits(z / (1.0f + __expf(-z)) * a1[m]);
+        } else {
+          static_cast<float*>(out)[o] = a0[m];
+        }
+      }
+    }
+  }
+}
+
 // Generic routed kernel for rows that are only 2-byte aligned (Q4_0/Q8_0 with
 // an odd number of blocks per row): one wave per (row, slot), per-block loads.
 template <int FMT>
@@ -268,6 +408,53 @@ int moe_log2g(int units) {
   return ilog2(G);
 }
 
+// The LDS-staged kernel: rows of whole units, and MOE_COLS tokens' x within
+// 256 threads x MOE_XCH pieces.
+bool moe_lds_fits(int64_t K) { return (int64_t)MOE_COLS * (K / 8) <= 256 * MOE_XCH; }
+
+// G lanes per row giving each lane about 128 bytes of weights (at most 5
+// units; the larger G on a tie).
+template <int FMT>
+int moe_lds_log2g(int units) {
+  constexpr int UBYTES = Fmt<FMT>::BB * Fmt<FMT>::UB;
+  int best = -1, G = 64;
+  for (int g = 64; g >= 1; g >>= 1) {
+    const int it = (units + g - 1) / g;
+    if (it > 5) break;
+    const int dev = it * UBYTES > 128 ? it * UBYTES - 128 : 128 - it * UBYTES;
+    if (best < 0 || dev < best) {
+      best = dev;
+      G = g;
+    }
+  }
+  return ilog2(G);
+}
+
+template <int FMT, bool GATE_UP>
+int launch_moe_lds(const uint8_t* W0, const uint8_t* W1, const uint16_t* x, const int32_t* ids, void* out, int64_t N,
+                   int64_t K, int M, int top_k, int n_experts, int x_per_slot, int64_t eb, hipStream_t stream) {
+  const int units = (int)(K / (32 * Fmt<FMT>::UB));
+  const int log2g = moe_lds_log2g<FMT>(units);
+  const int iters = (units + (1 << log2g) - 1) >> log2g;
+  const int64_t rpw = 64 >> log2g;
+  const int64_t waves = (N + rpw - 1) / rpw;
+  const int P = M * top_k;
+  const dim3 grid((unsigned)((waves + 3) / 4), (unsigned)P), block(256);
+  const size_t lds = (size_t)MOE_COLS * K * 2 + (size_t)MOE_COLS * (K / 32) * 8 + (size_t)2 * P * 4 + 32;
+#define KQ_MOE_LAUNCH(IT)                                                                                       \
+  hipLaunchKernelGGL((k_moe_lds<FMT, IT, GATE_UP>), grid, block, lds, stream, W0, W1, x, ids, out, (int)N, (int)K, \
+                     M, top_k, n_experts, x_per_slot, log2g, eb)
+  switch (iters) {
+    case 1: KQ_MOE_LAUNCH(1); break;
+    case 2: KQ_MOE_LAUNCH(2); break;
+    case 3: KQ_MOE_LAUNCH(3); break;
+    case 4: KQ_MOE_LAUNCH(4); break;
+    default: KQ_MOE_LAUNCH(5); break;
+  }
+#undef KQ_MOE_LAUNCH
+  return (int)hipGetLastError();
+}
+
 template <int FMT>
 int moe_dispatch(const MoeArgs& a) {
   const int64_t eb = a.N * (a.K / 32) * Fmt<FMT>::BB;
@@ -279,6 +466,8 @@ int moe_dispatch(const MoeArgs& a) {
     return (int)hipGetLastError();
   }
   const int units = (int)(a.K / (32 * Fmt<FMT>::UB));
+  if (moe_lds_fits(a.K)) return launch_moe_lds<FMT, false>(a.W, nullptr, a.x, a.ids, a.y_slot, a.N, a.K, a.M,
+                                                            a.top_k, a.n_experts, a.x_per_slot, eb, a.stream);
   const int log2g = moe_log2g(units);
   const int64_t tile = 64 >> log2g;
   const int64_t waves = (a.N + tile - 1) / tile;
@@ -293,6 +482,9 @@ int gate_up_dispatch(const MoeGateUpArgs& a) {
   const int64_t eb = a.inter * (a.hidden / 32) * Fmt<FMT>::BB;
   const int P = a.M * a.top_k;
   const int units = (int)(a.hidden / (32 * Fmt<FMT>::UB));
+  if (moe_lds_fits(a.hidden))
+    return launch_moe_lds<FMT, true>(a.Wg, a.Wu, a.x, a.ids, a.h, a.inter, a.hidden, a.M, a.top_k, a.n_experts, 0,
+                                     eb, a.stream);
   const int log2g = moe_log2g(units);
   const int64_t tile = 64 >> log2g;
   const int64_t waves = (a.inter + tile - 1) / tile;
