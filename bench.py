@@ -388,23 +388,27 @@ def bench_moe(torch, kq, S, steps):
 
 
 def stream_ceiling(torch):
-    """A measured read-only streaming rate on this GPU: torch's sum over 1 GiB
-    of fp32 (a library reduction kernel), median of 10."""
-    a = torch.ones((1 << 28,), dtype=torch.float32, device="cuda")
+    """A measured streaming rate on this GPU: a 1 GiB device-to-device copy
+    (torch copy_, the runtime's copy kernel), bytes read plus bytes written
+    per second, median of 10."""
+    n = 1 << 28
+    a = torch.ones((n,), dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
     for _ in range(3):
-        a.sum()
+        b.copy_(a)
     torch.cuda.synchronize()
     ts = []
     for _ in range(10):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        a.sum()
+        b.copy_(a)
         e1.record()
         torch.cuda.synchronize()
         ts.append(e0.elapsed_time(e1))
-    del a
+    del a, b
     torch.cuda.empty_cache()
-    return {"kernel": "torch.sum over 1 GiB fp32", "gbps": (1 << 30) / (float(np.median(ts)) * 1e-3) / 1e9}
+    return {"kernel": "1 GiB device-to-device copy (read + write)",
+            "gbps": 2 * (n * 4) / (float(np.median(ts)) * 1e-3) / 1e9}
 
 
 def cpu_baseline(S, stack, kq, budget_s=15.0):
