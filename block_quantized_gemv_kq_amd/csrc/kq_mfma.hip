@@ -274,10 +274,13 @@ __global__ __launch_bounds__(64 * MfmaMaxWaves<T>::v) void k_gemv_mfma(const uin
 // per-group memory instructions are its weight loads alone (otherwise the
 // texture address path, not HBM, bounds the kernel). With Mp = M rounded up
 // to a power of two and K rounded up to whole 4-block groups (zeros past K):
-//   x slots: for block b, lane group g, column c, 16 bytes at ((4 b + g) Mp + c) 16
-//            holding x[c][32 b + 4 g .. +3] then x[c][32 b + 16 + 4 g .. +3]
-//            (the lanes of one read take contiguous bytes: no bank conflicts);
-//   sums:    sx[b][c] = sum of block b of column c, fp32.
+//   x slots: for block b, lane group g, column c, 16 bytes at ((4 b + g) Mp + c') 16
+//            with c' = c ^ xsw(b, g), holding x[c][32 b + 4 g .. +3] then
+//            x[c][32 b + 16 + 4 g .. +3]. The lanes of one operand read take one
+//            contiguous row (no bank conflicts); the column swizzle
+//            xsw(b, g) = ((b & 3) << 1 | g >> 1) & (Mp - 1) spreads the writes of
+//            the staging, whose lanes hold consecutive pieces of one column;
+//   sums:    sx[b][c] = sum of block b of column c, fp32 (not swizzled).
 // The per-block fix-up splits in two. The scale term sc * D needs D per block
 // (4 FMAs per lane). The offset term sum_b c[row][b] sx[c][b] is itself a small
 // product, done per group as one fp32 MFMA (16x16x4) whose B operand is the
@@ -291,7 +294,10 @@ __global__ __launch_bounds__(64 * MfmaMaxWaves<T>::v) void k_gemv_mfma(const uin
 // are discarded.
 constexpr int XST_MAX = 12;   // 16-byte x pieces per thread while staging
 
-template <int FMT, int P, bool SX>
+// Column swizzle of the x slots of block b, lane group g.
+__device__ __forceinline__ int xsw(int b, int g, int Mp) { return (((b & 3) << 1) | (g >> 1)) & (Mp - 1); }
+
+template <int FMT, int P, bool SX, bool XF>
 __global__ __launch_bounds__(1024) void k_gemv_mfma_lds(const uint8_t* __restrict__ W,
                                                        const uint16_t* __restrict__ x,
                                                        float* __restrict__ y, int N, int K, int M, int R,
@@ -301,7 +307,7 @@ __global__ __launch_bounds__(1024) void k_gemv_mfma_lds(const uint8_t* __restric
 // index 4 gi + g) against the staged x: the group's offset term as one fp32
 // MFMA, then per block D = x . (offset + q) and acc += scale * D.
 template <int FMT, bool SX = true>
-__device__ __forceinline__ void mfma_group(const GroupRaw<FMT>& cur, uint32_t roff, int gi, int g,
+__device__ __forceinline__ void mfma_group(const GroupRaw<FMT>& cur, uint32_t roff, int gi, int g, int ncol,
                                            const u32x4* xa, const float* sxa, int Mp, float4_t& acc) {
   uint32_t hdr, q0, q1, q2, q3, p0 = 0, p1 = 0, p2 = 0, p3 = 0;
   if constexpr (FMT == F_AFFINE4) {
@@ -341,7 +347,7 @@ __device__ __forceinline__ void mfma_group(const GroupRaw<FMT>& cur, uint32_t ro
   float4_t D[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const half8_t A = __builtin_bit_cast(half8_t, xa[(4 * gi + j) * bstride]);
+    const half8_t A = __builtin_bit_cast(half8_t, xa[(4 * gi + j) * bstride + (ncol ^ xsw(j, g, Mp))]);
     uint32_t b0, b1, b2, b3;
     if constexpr (FMT == F_Q8_0) {
       const uint32_t u = qs[j] ^ 0x80808080u, v = ps[j] ^ 0x80808080u;
@@ -365,7 +371,7 @@ __device__ __forceinline__ void mfma_group(const GroupRaw<FMT>& cur, uint32_t ro
     const half8_t ones = as_half8(ONES, ONES, ONES, ONES);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const half8_t A = __builtin_bit_cast(half8_t, xa[(4 * gi + j) * bstride]);
+      const half8_t A = __builtin_bit_cast(half8_t, xa[(4 * gi + j) * bstride + (ncol ^ xsw(j, g, Mp))]);
       const float4_t Dx = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, ones, float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
       const float sc = h2f(hs[j]);
       float c;
@@ -382,41 +388,57 @@ __device__ __forceinline__ void mfma_group(const GroupRaw<FMT>& cur, uint32_t ro
 // the block sums. Called by every thread of the workgroup; `issue_more` runs
 // between issuing the x loads and writing them (the caller's weight loads),
 // after a barrier that puts every wave's x loads ahead of them in the queue.
-template <bool SX, typename F>
+template <bool SX, typename F, bool XF = false>
 __device__ __forceinline__ void stage_x_mfma(const uint16_t* __restrict__ x, int M, int K, int ngroups,
                                              int log2mp, uint8_t* xlb, F issue_more) {
   const int Mp = 1 << log2mp;
   const int kq8 = K / 8, kq8p = 16 * ngroups;
   const uint32_t sx_base = (uint32_t)kq8p * (uint32_t)Mp * 16u;
   const uint32_t dummy = SX ? sx_base + (uint32_t)(4 * ngroups * Mp) * 4u : sx_base;
-  const int npieces = Mp * kq8p;
   const int nthreads = (int)blockDim.x;
+  const int nwaves = nthreads >> 6;
+  const int lane = (int)threadIdx.x & 63;
+  const int wv = wave_id();
   const rsrc_t xs = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
+  // Wave chunk q = wv + nwaves * c: 64 consecutive 16-byte pieces of one
+  // column, column q & (Mp - 1), pieces 64 (q >> log2mp) + lane, so the lanes
+  // of one load read 1 KB of contiguous memory.
   u32x4 xr[XST_MAX];
 #pragma unroll
   for (int c = 0; c < XST_MAX; ++c) {
-    const int i = (int)threadIdx.x + nthreads * c;
-    const int col = i & (Mp - 1), k8 = i >> log2mp;
-    const bool ok = i < npieces && col < M && k8 < kq8;
+    const int q = wv + nwaves * c;
+    const int col = q & (Mp - 1), k8 = 64 * (q >> log2mp) + lane;
+    const bool ok = col < M && k8 < kq8;
     xr[c] = ld128(xs, ok ? ((uint32_t)col * (uint32_t)kq8 + (uint32_t)k8) * 16u : OOB);
   }
   __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_sched_barrier(0);
-  issue_more();
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int c = 0; c < XST_MAX; ++c) {
-    const int i = (int)threadIdx.x + nthreads * c;
-    const int col = i & (Mp - 1), k8 = i >> log2mp;
-    const int bb = k8 >> 2, h = k8 & 3;
-    const int g0 = 2 * (h & 1);
+  if constexpr (!XF) {
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    issue_more();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  {
+    // piece k8 = 4 b + h: elements 0-3 go to lane group g0 = 2 (h & 1), 4-7 to
+    // g0 + 1, at byte 8 (h >> 1) of the slot; b & 3 and h are the lane's own.
+    const int h = lane & 3, g0 = 2 * (h & 1);
+    const int sw = xsw(lane >> 2, g0, Mp);
     const uint32_t part = 8u * (uint32_t)(h >> 1);
-    const bool ok = i < npieces;
-    const uint32_t a0 = ok ? (uint32_t)((4 * bb + g0) * Mp + col) * 16u + part : dummy;
-    const uint32_t a1 = ok ? (uint32_t)((4 * bb + g0 + 1) * Mp + col) * 16u + part : dummy + 8u;
-    *reinterpret_cast<u32x2*>(xlb + a0) = u32x2{xr[c].x, xr[c].y};
-    *reinterpret_cast<u32x2*>(xlb + a1) = u32x2{xr[c].z, xr[c].w};
+#pragma unroll
+    for (int c = 0; c < XST_MAX; ++c) {
+      const int q = wv + nwaves * c;
+      const int col = q & (Mp - 1), k8 = 64 * (q >> log2mp) + lane;
+      const bool ok = k8 < kq8p;
+      const uint32_t a0 = ok ? (uint32_t)((4 * (k8 >> 2) + g0) * Mp + (col ^ sw)) * 16u + part : dummy;
+      const uint32_t a1 = ok ? a0 + (uint32_t)Mp * 16u : dummy + 8u;
+      *reinterpret_cast<u32x2*>(xlb + a0) = u32x2{xr[c].x, xr[c].y};
+      *reinterpret_cast<u32x2*>(xlb + a1) = u32x2{xr[c].z, xr[c].w};
+    }
+  }
+  if constexpr (XF) {
+    __builtin_amdgcn_sched_barrier(0);
+    issue_more();
+    __builtin_amdgcn_sched_barrier(0);
   }
   __syncthreads();
   if constexpr (!SX) return;
@@ -428,7 +450,7 @@ __device__ __forceinline__ void stage_x_mfma(const uint16_t* __restrict__ x, int
     float v = 0.0f;
 #pragma unroll
     for (int gg = 0; gg < 4; ++gg) {
-      const u32x4 q = xl4[(4 * bb + gg) * Mp + col];
+      const u32x4 q = xl4[(4 * bb + gg) * Mp + (col ^ xsw(bb, gg, Mp))];
       v = dot2(q.x, ONES, v);
       v = dot2(q.y, ONES, v);
       v = dot2(q.z, ONES, v);
@@ -450,7 +472,7 @@ __device__ __forceinline__ void stage_x_mfma(const uint16_t* __restrict__ x, int
 // groups [s P, (s + 1) P) of tile r, all loaded before any arithmetic, and the
 // S partial results of a tile are summed in LDS in a fixed order. SX: block
 // sums in LDS (else, when x alone just fits, from an MFMA per block).
-template <int FMT, int P, bool SX>
+template <int FMT, int P, bool SX, bool XF>
 __global__ __launch_bounds__(1024) void k_gemv_mfma_lds(const uint8_t* __restrict__ W,
                                                        const uint16_t* __restrict__ x,
                                                        float* __restrict__ y, int N, int K, int M, int R,
@@ -472,22 +494,23 @@ __global__ __launch_bounds__(1024) void k_gemv_mfma_lds(const uint8_t* __restric
   const bool row_ok = n < valid_rows;
   uint8_t* xlb = reinterpret_cast<uint8_t*>(xl4);
   GroupRaw<FMT> wr[P];
-  stage_x_mfma<SX>(x, M, K, ngroups, log2mp, xlb, [&]() {
+  auto issue = [&]() {
 #pragma unroll
     for (int p = 0; p < P; ++p) {
       const int gi = gb + p;
       load_group<FMT>(rs, roff, 4 * gi + g, gi < ngroups && row_ok && 4 * gi + g < nblk, wr[p]);
     }
-  });
+  };
+  stage_x_mfma<SX, decltype(issue), XF>(x, M, K, ngroups, log2mp, xlb, issue);
   const int ncol = n < M ? n : M - 1;
-  const u32x4* xa = xl4 + g * Mp + ncol;
+  const u32x4* xa = xl4 + g * Mp;
   const float* sxa = reinterpret_cast<const float*>(xlb + (uint32_t)(16 * ngroups) * (uint32_t)Mp * 16u) + g * Mp + ncol;
   float4_t acc = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int p = 0; p < P; ++p) {
     const int gi = gb + p;
     if (gi >= ngroups) break;   // uniform
-    mfma_group<FMT, SX>(wr[p], roff, gi, g, xa, sxa, Mp, acc);
+    mfma_group<FMT, SX>(wr[p], roff, gi, g, ncol, xa, sxa, Mp, acc);
   }
   // fixed-order sum over the S waves of each tile (the x area is reused)
   __syncthreads();
@@ -750,7 +773,7 @@ __global__ __launch_bounds__(512) void k_gemv_mfma_pers(const uint8_t* __restric
     for (int p = 0; p < P; ++p) issue(wr[p], p < Q);
   });
   const int ncol = n < M ? n : M - 1;
-  const u32x4* xa = xl4 + g * Mp + ncol;
+  const u32x4* xa = xl4 + g * Mp;
   const float* sxa = reinterpret_cast<const float*>(xlb + (uint32_t)(16 * ngroups) * (uint32_t)Mp * 16u) + g * Mp + ncol;
   float4_t acc = float4_t{0.f, 0.f, 0.f, 0.f};
   // Finished tiles wait in registers (newest first) and are stored after the
@@ -763,7 +786,7 @@ __global__ __launch_bounds__(512) void k_gemv_mfma_pers(const uint8_t* __restric
     for (int p = 0; p < P; ++p) {
       const int q = base + p;
       if (q < Q) {   // uniform
-        mfma_group<FMT>(wr[p], roff, cg, g, xa, sxa, Mp, acc);
+        mfma_group<FMT>(wr[p], roff, cg, g, ncol, xa, sxa, Mp, acc);
         if (++cg == ngroups) {   // tile complete: lane holds D[col 4g+v][row n]
 #pragma unroll
           for (int k = MFMA_PERS_TPW - 1; k > 0; --k) done[k] = done[k - 1];
@@ -842,6 +865,12 @@ int launch_mfma_t(const GemvArgs& a, int m0, int mt) {
 }
 
 constexpr int MFMA_LDS_MAX_BYTES = 160 * 1024;
+
+// 16-byte pieces that stage_x_mfma loads: Mp columns of whole 64-piece
+// chunks (x padded to whole 4-block groups, then to a multiple of 64 pieces).
+int64_t mfma_x_pieces(int ngroups, int log2mp) {
+  return ((int64_t)1 << log2mp) * 64 * ((16 * (int64_t)ngroups + 63) / 64);
+}
 // Groups per wave at most (registers within the 128 of a 16-wave workgroup).
 template <int FMT> struct MfmaLdsMaxP { static constexpr int v = FMT == F_Q8_0 ? 4 : 6; };
 
@@ -891,7 +920,7 @@ MfmaLdsCfg mfma_lds_cfg(int64_t N, int64_t K, int M, int maxp, bool no_sums) {
   }
   int log2mp = 0;
   while ((1 << log2mp) < M) ++log2mp;
-  const int64_t pieces = ((int64_t)1 << log2mp) * 16 * ngroups;   // x padded to whole groups
+  const int64_t pieces = mfma_x_pieces(ngroups, log2mp);
   // enough threads to stage x (at most XST_MAX pieces each): more tiles per
   // workgroup, else more waves per tile
   while (pieces > (int64_t)XST_MAX * 64 * R * S && 2 * R * S <= 16 && (tiles + 2 * R - 1) / (2 * R) >= 256) R *= 2;
@@ -915,8 +944,13 @@ template <int FMT, int P, bool SX>
 int launch_mfma_lds_p(const GemvArgs& a, int m0, int mt, const MfmaLdsCfg& c) {
   const int64_t tiles = (a.N + 15) / 16;
   const dim3 grid((unsigned)((tiles + c.R - 1) / c.R)), block((unsigned)(64 * c.R * c.S));
-  hipLaunchKernelGGL((k_gemv_mfma_lds<FMT, P, SX>), grid, block, c.lds, a.stream, a.W, a.x + (int64_t)m0 * a.K,
-                     a.y + (int64_t)m0 * a.N, (int)a.N, (int)a.K, mt, c.R, c.S, c.log2mp);
+  const char* e = getenv("KQ_MFMA_XF");
+  if (e && atoi(e))
+    hipLaunchKernelGGL((k_gemv_mfma_lds<FMT, P, SX, true>), grid, block, c.lds, a.stream, a.W, a.x + (int64_t)m0 * a.K,
+                       a.y + (int64_t)m0 * a.N, (int)a.N, (int)a.K, mt, c.R, c.S, c.log2mp);
+  else
+    hipLaunchKernelGGL((k_gemv_mfma_lds<FMT, P, SX, false>), grid, block, c.lds, a.stream, a.W, a.x + (int64_t)m0 * a.K,
+                       a.y + (int64_t)m0 * a.N, (int)a.N, (int)a.K, mt, c.R, c.S, c.log2mp);
   return (int)hipGetLastError();
 }
 
@@ -1065,7 +1099,7 @@ int launch_mfma_fmt(const GemvArgs& a) {
     const int ngroups = (int)((a.K / 32 + 3) / 4);
     int log2mp = 0;
     while ((1 << log2mp) < a.M) ++log2mp;
-    const int64_t pieces = ((int64_t)1 << log2mp) * 16 * ngroups;
+    const int64_t pieces = mfma_x_pieces(ngroups, log2mp);
     const int64_t lds = mfma_x_lds_bytes(a.K, log2mp, true);
     if ((tiles >= MFMA_PERS_MIN_TILES || want_pers) && !want_teams && !want_chunk && lds <= MFMA_LDS_MAX_BYTES &&
         pieces <= (int64_t)XST_MAX * 512)
