@@ -579,15 +579,15 @@ __global__ __launch_bounds__(512) void k_gemv_mfma_chunk(const uint8_t* __restri
     const int cg0 = c * CG;
     const int gb = cg0 + s * P;                // this wave's first group of the chunk
     const int ge = min(gb + P, min(cg0 + CG, ngroups));
-    // 1. x pieces of the chunk: piece i is tile i >> (8 + log2cg), then column
-    //    i & 15, then chunk piece (i >> 4) & (16 CG - 1)
+    // 1. x pieces of the chunk: piece i is column i >> (4 + log2cg) (tile
+    //    column >> 4), chunk piece i & (16 CG - 1), so that the lanes of one
+    //    load read contiguous runs of a column
     u32x4 xr[XST_MAX];
 #pragma unroll
     for (int q = 0; q < XST_MAX; ++q) {
       const int i = (int)threadIdx.x + nthreads * q;
-      const int t = i >> (8 + log2cg);
-      const int col = 16 * t + (i & 15);
-      const int k8 = 16 * cg0 + ((i >> 4) & ((16 << log2cg) - 1));
+      const int col = i >> (4 + log2cg);
+      const int k8 = 16 * cg0 + (i & ((16 << log2cg) - 1));
       const bool ok = i < npieces && col < M && k8 < kq8;
       xr[q] = ld128(xs, ok ? ((uint32_t)col * (uint32_t)kq8 + (uint32_t)k8) * 16u : OOB);
     }
@@ -602,19 +602,21 @@ __global__ __launch_bounds__(512) void k_gemv_mfma_chunk(const uint8_t* __restri
       load_group<FMT>(rs, roff, 4 * gi + g, gi < ge && row_ok && 4 * gi + g < nblk, wr[p]);
     }
     __builtin_amdgcn_sched_barrier(0);
-    // 3. x into LDS (branch-free, as above)
+    // 3. x into LDS (branch-free, as above; slots swizzled as in the Mp = 16
+    //    layout, and (k8 >> 2) & 3 and k8 & 3 are the lane's own)
 #pragma unroll
     for (int q = 0; q < XST_MAX; ++q) {
       const int i = (int)threadIdx.x + nthreads * q;
-      const int t = i >> (8 + log2cg);
-      const int col = i & 15, k8l = (i >> 4) & ((16 << log2cg) - 1);
+      const int cl = i >> (4 + log2cg);
+      const int t = cl >> 4, col = cl & 15, k8l = i & ((16 << log2cg) - 1);
       const int bb = k8l >> 2, h = k8l & 3;
       const int g0 = 2 * (h & 1);
+      const int csw = col ^ xsw(bb, g0, 16);
       const uint32_t part = 8u * (uint32_t)(h >> 1);
       const bool ok = i < npieces;
       const uint32_t base = (uint32_t)t * tile_bytes;
-      const uint32_t a0 = ok ? base + (uint32_t)((4 * bb + g0) * 16 + col) * 16u + part : dummy;
-      const uint32_t a1 = ok ? base + (uint32_t)((4 * bb + g0 + 1) * 16 + col) * 16u + part : dummy + 8u;
+      const uint32_t a0 = ok ? base + (uint32_t)((4 * bb + g0) * 16 + csw) * 16u + part : dummy;
+      const uint32_t a1 = ok ? base + (uint32_t)((4 * bb + g0 + 1) * 16 + csw) * 16u + part : dummy + 8u;
       *reinterpret_cast<u32x2*>(xlb + a0) = u32x2{xr[q].x, xr[q].y};
       *reinterpret_cast<u32x2*>(xlb + a1) = u32x2{xr[q].z, xr[q].w};
     }
@@ -630,7 +632,7 @@ __global__ __launch_bounds__(512) void k_gemv_mfma_chunk(const uint8_t* __restri
         float v = 0.0f;
 #pragma unroll
         for (int gg = 0; gg < 4; ++gg) {
-          const u32x4 qv = xt[(4 * bb + gg) * 16 + col];
+          const u32x4 qv = xt[(4 * bb + gg) * 16 + (col ^ xsw(bb, gg, 16))];
           v = dot2(qv.x, ONES, v);
           v = dot2(qv.y, ONES, v);
           v = dot2(qv.z, ONES, v);
@@ -702,7 +704,7 @@ __global__ __launch_bounds__(512) void k_gemv_mfma_chunk(const uint8_t* __restri
 #pragma unroll
         for (int t = 0; t < T; ++t) {
           const u32x4* xt = reinterpret_cast<const u32x4*>(xlb + (uint32_t)t * tile_bytes);
-          const half8_t A = __builtin_bit_cast(half8_t, xt[(4 * (4 * gl + j) + g) * 16 + n]);
+          const half8_t A = __builtin_bit_cast(half8_t, xt[(4 * (4 * gl + j) + g) * 16 + (n ^ xsw(j, g, 16))]);
           const float4_t D = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
           for (int v = 0; v < 4; ++v) acc[t][v] = __builtin_fmaf(sc, D[v], acc[t][v]);
