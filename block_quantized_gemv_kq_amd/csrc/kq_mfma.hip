@@ -1079,7 +1079,10 @@ int launch_mfma_pers_p(const GemvArgs& a, int log2mp, size_t lds) {
   return (int)hipGetLastError();
 }
 
-template <int FMT> struct MfmaPersP { static constexpr int v = FMT == F_Q8_0 ? 6 : 8; };
+// Groups in flight per wave. Deeper rings win even where they cost occupancy
+// (measured at M = 8 on 151936 x 2560: Q8_0 P = 6 / 8: 95.6 / 94.0 us, Q4_0
+// P = 8 / 10: 78.1 / 65.6 us, affine4 P = 8 / 12: 74.1 / 64.8 us).
+template <int FMT> struct MfmaPersP { static constexpr int v = FMT == F_Q8_0 ? 8 : (FMT == F_Q4_0 ? 10 : 12); };
 // From this many 16-row tiles on, persistent waves (one tile at a time per
 // wave) fill the device; below it, tiles are split over the waves of a workgroup.
 constexpr int64_t MFMA_PERS_MIN_TILES = 4096;
