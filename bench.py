@@ -143,13 +143,18 @@ class DeviceStack:
             v.alg_bytes += Wd.numel() + x.nbytes + 2 * M * N * 4 + M * 4
         return v
 
+    invariant = False   # kq_gemv_invariant (per-column bits of one-column calls) instead of kq_gemv
+
+    def _gemv(self):
+        return self.kq.kq_gemv_invariant if self.invariant else self.kq.kq_gemv
+
     def launch_group(self, layer, gi):
         fmt, Wd, xd, yd, N, K, _ = self.groups[layer][gi]
-        self.kq.kq_gemv(fmt, Wd, xd, yd, N, K, self.M)
+        self._gemv()(fmt, Wd, xd, yd, N, K, self.M)
 
     def launch_head(self):
         fmt, Wd, xd, yd, N, K, ws, wsb, am = self.head
-        self.kq.kq_gemv(fmt, Wd, xd, yd, N, K, self.M)
+        self._gemv()(fmt, Wd, xd, yd, N, K, self.M)
         self.kq.kq_argmax(yd, N, self.M, am, ws, wsb)
 
     def step(self):
@@ -329,6 +334,9 @@ def bench_small_stack(torch, kq, S, steps):
     return out
 
 
+VERIFY_INVARIANT_M = (4, 8)   # verify widths also timed through kq_gemv_invariant
+
+
 def bench_verify_all(torch, kq, S, ds, t1_ms, steps):
     """Config 4: the verify pass at every M on the resident 4B-shaped
     weights: time per pass, t(M)/t(1), M / t as the upper bound on accepted
@@ -343,6 +351,16 @@ def bench_verify_all(torch, kq, S, ds, t1_ms, steps):
                        "alg_bytes": int(dv.alg_bytes), "gbps": dv.alg_bytes / (ms * 1e-3) / 1e9,
                        "t_ratio_vs_m1": ms / t1_ms, "tokens_per_s_upper_bound": M / (ms * 1e-3)}
         log(f"verify M={M}: {ms * 1000:.1f} us per pass, t(M)/t(1) = {ms / t1_ms:.2f}")
+        if M in VERIFY_INVARIANT_M:
+            dv.invariant = True
+            g2 = capture(torch, dv.step)
+            per2, _, _ = time_graph(torch, g2, steps, 3)
+            ms2 = float(np.median(per2))
+            out[str(M)]["invariant"] = {"entry": "kq_gemv_invariant", "ms_per_pass": ms2,
+                                        "gbps": dv.alg_bytes / (ms2 * 1e-3) / 1e9, "t_ratio_vs_m1": ms2 / t1_ms,
+                                        "tokens_per_s_upper_bound": M / (ms2 * 1e-3)}
+            log(f"verify M={M} batch-invariant: {ms2 * 1000:.1f} us per pass, t(M)/t(1) = {ms2 / t1_ms:.2f}")
+            del g2
         del g, dv
         torch.cuda.empty_cache()
     return out

@@ -33,6 +33,7 @@ SIGNATURES = {
     "kq_pack": (_I32, [_I32, _P, _I64, _I64, _P, _I32]),
     "kq_unpack": (_I32, [_I32, _P, _I64, _I64, _P]),
     "kq_gemv": (_I32, [_I32, _P, _P, _P, _I64, _I64, _I32, _P]),
+    "kq_gemv_invariant": (_I32, [_I32, _P, _P, _P, _I64, _I64, _I32, _P]),
     "kq_moe_gemv_workspace_bytes": (_I64, [_I64, _I32, _I32, _I32]),
     "kq_moe_gemv": (_I32, [_I32, _P, _P, _P, _P, _P, _I64, _I64, _I32, _I32, _I32, _I32, _P, _I64, _P]),
     "kq_moe_ffn_workspace_bytes": (_I64, [_I64, _I64, _I32, _I32]),
@@ -182,6 +183,12 @@ def kq_f32_to_f16(a: np.ndarray) -> np.ndarray:
 def kq_gemv(fmt, W, x, y, N: int, K: int, M: int, stream=None) -> None:
     """y[M][N] (fp32, device) = dequant(W)[N][K] @ x[M][K]^T (x fp16 bits, device)."""
     _check(lib().kq_gemv(_fmt(fmt), _ptr(W), _ptr(x), _ptr(y), N, K, M, _stream(stream)), "kq_gemv")
+
+
+def kq_gemv_invariant(fmt, W, x, y, N: int, K: int, M: int, stream=None) -> None:
+    """As kq_gemv, with column m bit-identical to a one-column call on x[m]."""
+    _check(lib().kq_gemv_invariant(_fmt(fmt), _ptr(W), _ptr(x), _ptr(y), N, K, M, _stream(stream)),
+           "kq_gemv_invariant")
 
 
 def kq_moe_gemv_workspace_bytes(N: int, M: int, top_k: int, weighted: bool) -> int:

@@ -118,6 +118,21 @@ int kq_gemv(int fmt, const void* W, const uint16_t* x, float* y, int64_t N, int6
   return hip_status(kq::launch_gemv(a), "kq_gemv");
 }
 
+int kq_gemv_invariant(int fmt, const void* W, const uint16_t* x, float* y, int64_t N, int64_t K, int M,
+                      void* stream) {
+  int st = check_fmt_k(fmt, K);
+  if (st) return st;
+  if ((st = check_n(N, "N"))) return st;
+  if (M < 0 || M > KQ_MAX_M) return fail(KQ_ERR_ARG, "M=%d must be in [0, %d]", M, KQ_MAX_M);
+  if (M == 0 || N == 0) return ok();
+  if (!W || !x || !y) return fail(KQ_ERR_ARG, "kq_gemv_invariant: null pointer");
+  if (!aligned(W, 4) || !aligned(y, 4))
+    return fail(KQ_ERR_ALIGN, "kq_gemv_invariant: W and y must be 4-byte aligned");
+  if (!aligned(x, 16)) return fail(KQ_ERR_ALIGN, "kq_gemv_invariant: x must be 16-byte aligned");
+  kq::GemvArgs a{fmt, static_cast<const uint8_t*>(W), x, y, N, K, M, static_cast<hipStream_t>(stream)};
+  return hip_status(kq::launch_gemv_invariant(a), "kq_gemv_invariant");
+}
+
 int64_t kq_moe_gemv_workspace_bytes(int64_t N, int M, int top_k, int weighted) {
   if (N < 0 || M < 0 || top_k < 0) return fail(KQ_ERR_ARG, "negative size");
   if (!weighted) return 0;

@@ -31,6 +31,7 @@ struct GemvArgs {
   hipStream_t stream;
 };
 int launch_gemv(const GemvArgs& a);
+int launch_gemv_invariant(const GemvArgs& a);
 int launch_gemv_mfma(const GemvArgs& a);
 
 struct MoeArgs {

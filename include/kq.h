@@ -122,6 +122,17 @@ int kq_unpack(int fmt, const void* packed, int64_t N, int64_t K, float* W_out);
 int kq_gemv(int fmt, const void* W, const uint16_t* x, float* y,
             int64_t N, int64_t K, int M, void* stream);
 
+/* kq_gemv_invariant — the product of kq_gemv, batch-invariant: column m of y
+ * has the same bits as kq_gemv returns for column m alone (M = 1), whatever M
+ * is (Kinetic docs, "What makes it fast": every row of a batch is summed in
+ * the order that token would be summed on its own). It runs the one-column
+ * kernel over the M columns, up to 4 (LDS-staged rows) or 8 (other rows) per
+ * pass, so the weights are read once per pass, not once per call; use kq_gemv
+ * when a tolerance is enough. Arguments, layout, ownership, determinism and
+ * errors as kq_gemv. */
+int kq_gemv_invariant(int fmt, const void* W, const uint16_t* x, float* y,
+                      int64_t N, int64_t K, int M, void* stream);
+
 /* Workspace bytes kq_moe_gemv needs (0 when route_w is NULL). */
 int64_t kq_moe_gemv_workspace_bytes(int64_t N, int M, int top_k, int weighted);
 

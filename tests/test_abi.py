@@ -1,6 +1,7 @@
 """C-ABI checks that need no GPU: the library loads, exports every symbol the
 header declares, and rejects bad arguments on the host before any HIP call."""
 import ctypes
+import functools
 import os
 import re
 
@@ -59,11 +60,13 @@ A16 = 0x10000
 A4 = 0x10004
 
 
-def _gemv(fmt=0, W=A16, x=A16, y=A16, N=8, K=64, M=1):
-    return kq.lib().kq_gemv(fmt, W, x, y, N, K, M, 0)
+def _gemv_any(fmt=0, W=A16, x=A16, y=A16, N=8, K=64, M=1, entry="kq_gemv"):
+    return getattr(kq.lib(), entry)(fmt, W, x, y, N, K, M, 0)
 
 
-def test_gemv_validation():
+@pytest.mark.parametrize("entry", ["kq_gemv", "kq_gemv_invariant"])
+def test_gemv_validation(entry):
+    _gemv = functools.partial(_gemv_any, entry=entry)
     assert _gemv(fmt=5) == kq.KQ_ERR_FORMAT
     assert _gemv(K=48) == kq.KQ_ERR_SHAPE
     assert _gemv(K=0) == kq.KQ_ERR_SHAPE
