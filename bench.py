@@ -488,6 +488,8 @@ def main():
     ap.add_argument("--no-verify", action="store_true", help="skip the verify measurements (M > 1)")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the other configurations (single Q8_0 GEMV, 0.6B stack, MoE layer)")
+    ap.add_argument("--verify-only", type=int, default=0, metavar="M",
+                    help="short run for kernel traces: only the M-column verify pass, graph-replayed")
     ap.add_argument("--kernels-only", action="store_true",
                     help="short run for counter collection: per-kernel graphs and a copy of known size")
     args = ap.parse_args()
@@ -525,6 +527,16 @@ def main():
             b.copy_(a)                       # plain copy kernel: 256 MiB read, 256 MiB written
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_each_way": n}))
+        return
+
+    if args.verify_only:
+        # the M-column verify pass alone (same resident weights, seeded
+        # columns), replayed as a graph: the kernels of one verify width
+        dv = ds.with_columns(S, args.verify_only, S.VERIFY_WORKLOAD_ID)
+        g = capture(torch, dv.step)
+        per, total, _ = time_graph(torch, g, args.steps, args.warmup)
+        print(json.dumps({"verify_only": args.verify_only, "ms_per_pass": float(np.median(per)),
+                          "steps": args.steps}))
         return
 
     # path A: every GEMV its own kernel, the step replayed as a graph
