@@ -738,7 +738,7 @@ __global__ __launch_bounds__(512) void k_gemv_mfma_chunk(const uint8_t* __restri
 
 constexpr int MFMA_PERS_TPW = 8;   // tiles per wave at most
 
-template <int FMT, int P>
+template <int FMT, int P, bool SX>
 __global__ __launch_bounds__(512) void k_gemv_mfma_pers(const uint8_t* __restrict__ W,
                                                        const uint16_t* __restrict__ x,
                                                        float* __restrict__ y, int N, int K, int M,
@@ -770,7 +770,7 @@ __global__ __launch_bounds__(512) void k_gemv_mfma_pers(const uint8_t* __restric
     if (++ig == ngroups) { ig = 0; ++ik; }
   };
   uint8_t* xlb = reinterpret_cast<uint8_t*>(xl4);
-  stage_x_mfma<true>(x, M, K, ngroups, log2mp, xlb, [&]() {
+  stage_x_mfma<SX>(x, M, K, ngroups, log2mp, xlb, [&]() {
 #pragma unroll
     for (int p = 0; p < P; ++p) issue(wr[p], p < Q);
   });
@@ -788,7 +788,7 @@ __global__ __launch_bounds__(512) void k_gemv_mfma_pers(const uint8_t* __restric
     for (int p = 0; p < P; ++p) {
       const int q = base + p;
       if (q < Q) {   // uniform
-        mfma_group<FMT>(wr[p], roff, cg, g, ncol, xa, sxa, Mp, acc);
+        mfma_group<FMT, SX>(wr[p], roff, cg, g, ncol, xa, sxa, Mp, acc);
         if (++cg == ngroups) {   // tile complete: lane holds D[col 4g+v][row n]
 #pragma unroll
           for (int k = MFMA_PERS_TPW - 1; k > 0; --k) done[k] = done[k - 1];
@@ -895,7 +895,11 @@ int64_t mfma_x_lds_bytes(int64_t K, int log2mp, bool sums) {
 // (R S <= 8, so that several workgroups share a CU and one computes while
 // another loads) while at least 1024 workgroups remain, so that one staged
 // copy of x serves several tiles. Not usable (ok = false) when x does not fit in LDS
-// or needs more than XST_MAX pieces per thread.
+// or needs more than XST_MAX pieces per thread. no_sums: take the offset term
+// from an MFMA against ones per block rather than block sums staged in LDS
+// (measured faster at M = 8 and 16 on the decode shapes: the sums cost a
+// pass over x and a barrier before the first product; q|k|v 8.24 -> 7.88 us,
+// gate|up 13.99 -> 12.99 us at M = 8).
 MfmaLdsCfg mfma_lds_cfg(int64_t N, int64_t K, int M, int maxp, bool no_sums) {
   MfmaLdsCfg c{1, 1, 1, 0, true, 0, false};
   const int ngroups = (int)((K / 32 + 3) / 4);
@@ -1055,7 +1059,7 @@ int launch_mfma_chunk(const GemvArgs& a, int m0, int mt) {
 // as fit at once (up to one wave per tile), tiles dealt evenly: tpw =
 // ceil(tiles / waves) (at most MFMA_PERS_TPW), then only as many waves as
 // that needs.
-template <int FMT, int P>
+template <int FMT, int P, bool SX>
 int launch_mfma_pers_p(const GemvArgs& a, int log2mp, size_t lds) {
   static int cus_of[64] = {0};   // compute units per device, looked up once
   int dev = 0;
@@ -1064,7 +1068,7 @@ int launch_mfma_pers_p(const GemvArgs& a, int log2mp, size_t lds) {
     return (int)hipErrorInvalidDevice;
   const int cus = cus_of[dev];
   int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_gemv_mfma_pers<FMT, P>, 512, lds) != hipSuccess || per_cu < 1)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_gemv_mfma_pers<FMT, P, SX>, 512, lds) != hipSuccess || per_cu < 1)
     per_cu = 1;
   const int64_t tiles = (a.N + 15) / 16;
   const int64_t max_waves = (int64_t)cus * per_cu * 8;
@@ -1074,7 +1078,7 @@ int launch_mfma_pers_p(const GemvArgs& a, int log2mp, size_t lds) {
   if (et && atoi(et) >= 1 && atoi(et) <= MFMA_PERS_TPW) tpw = atoi(et);
   const int64_t waves = (tiles + tpw - 1) / tpw;
   const dim3 grid((unsigned)((waves + 7) / 8)), block(512);
-  hipLaunchKernelGGL((k_gemv_mfma_pers<FMT, P>), grid, block, lds, a.stream, a.W, a.x, a.y, (int)a.N, (int)a.K,
+  hipLaunchKernelGGL((k_gemv_mfma_pers<FMT, P, SX>), grid, block, lds, a.stream, a.W, a.x, a.y, (int)a.N, (int)a.K,
                      (int)a.M, log2mp, (int)tpw);
   return (int)hipGetLastError();
 }
@@ -1090,8 +1094,8 @@ constexpr int64_t MFMA_PERS_MIN_TILES = 4096;
 // Order: persistent waves (many tiles, M <= 16), split-K teams with all of x
 // in LDS (M <= 16), K-chunked staging (any M up to 64 per launch), and per-wave
 // activation loads as the fallback. KQ_MFMA_VARIANT (tests and sweeps) forces
-// one kernel where it applies: "pers", "teams", "teams_nosx" (block sums by
-// MFMA), "chunk" or "direct".
+// one kernel where it applies: "pers", "teams", "teams_sx" (block sums staged
+// in LDS instead of an MFMA against ones per block), "chunk" or "direct".
 template <int FMT>
 int launch_mfma_fmt(const GemvArgs& a) {
   const char* var = getenv("KQ_MFMA_VARIANT");
@@ -1108,8 +1112,8 @@ int launch_mfma_fmt(const GemvArgs& a) {
     const int64_t lds = mfma_x_lds_bytes(a.K, log2mp, true);
     if ((tiles >= MFMA_PERS_MIN_TILES || want_pers) && !want_teams && !want_chunk && lds <= MFMA_LDS_MAX_BYTES &&
         pieces <= (int64_t)XST_MAX * 512)
-      return launch_mfma_pers_p<FMT, MfmaPersP<FMT>::v>(a, log2mp, (size_t)lds);
-    const MfmaLdsCfg c = mfma_lds_cfg(a.N, a.K, (int)a.M, MfmaLdsMaxP<FMT>::v, var && !strcmp(var, "teams_nosx"));
+      return launch_mfma_pers_p<FMT, MfmaPersP<FMT>::v, true>(a, log2mp, (size_t)lds);
+    const MfmaLdsCfg c = mfma_lds_cfg(a.N, a.K, (int)a.M, MfmaLdsMaxP<FMT>::v, !(var && !strcmp(var, "teams_sx")));
     if (c.ok && !want_chunk) return launch_mfma_lds<FMT>(a, 0, (int)a.M, c);
   }
   for (int m0 = 0; m0 < a.M; m0 += 64) {

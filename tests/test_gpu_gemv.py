@@ -178,7 +178,7 @@ def test_zero_and_constant_weights():
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("variant", ("pers", "pers_tpw3", "teams", "teams_nosx", "chunk", "direct"))
+@pytest.mark.parametrize("variant", ("pers", "pers_tpw3", "teams", "teams_sx", "chunk", "direct"))
 @pytest.mark.parametrize("N,K,M", [(1000, 2560, 8), (37, 96, 5), (300, 4128, 16), (16, 32, 2), (529, 640, 13),
                                    (300, 4128, 40), (77, 9728, 33)])
 def test_mfma_variants_parity(fmt, variant, N, K, M):
