@@ -107,7 +107,7 @@ class DeviceStack:
             x = S.activations((wid, stack.layers, 0), h.k, M)
             Wd = torch.from_numpy(packed).to(dev)
             yd = torch.empty((M, h.n), dtype=torch.float32, device=dev)
-            wsb = kq.kq_argmax_workspace_bytes(h.n, M)
+            wsb = max(kq.kq_argmax_workspace_bytes(h.n, M), kq.kq_gemv_argmax_workspace_bytes(h.fmt, h.n, h.k, M))
             ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
             am = torch.empty(M, dtype=torch.int32, device=dev)
             self.head = (h.fmt, Wd, torch.from_numpy(x).to(dev), yd, h.n, h.k, ws, wsb, am)
@@ -136,7 +136,7 @@ class DeviceStack:
             fmt, Wd, _, _, N, K, _, _, _ = self.head
             x = S.activations((act_workload_id, self.stack.layers, 0), K, M)
             yd = torch.empty((M, N), dtype=torch.float32, device="cuda")
-            wsb = self.kq.kq_argmax_workspace_bytes(N, M)
+            wsb = max(self.kq.kq_argmax_workspace_bytes(N, M), self.kq.kq_gemv_argmax_workspace_bytes(fmt, N, K, M))
             ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
             am = torch.empty(M, dtype=torch.int32, device="cuda")
             v.head = (fmt, Wd, torch.from_numpy(x).to("cuda"), yd, N, K, ws, wsb, am)
@@ -154,8 +154,11 @@ class DeviceStack:
 
     def launch_head(self):
         fmt, Wd, xd, yd, N, K, ws, wsb, am = self.head
-        self._gemv()(fmt, Wd, xd, yd, N, K, self.M)
-        self.kq.kq_argmax(yd, N, self.M, am, ws, wsb)
+        if self.invariant:
+            self.kq.kq_gemv_invariant(fmt, Wd, xd, yd, N, K, self.M)
+            self.kq.kq_argmax(yd, N, self.M, am, ws, wsb)
+        else:
+            self.kq.kq_gemv_argmax(fmt, Wd, xd, yd, N, K, self.M, am, ws, wsb)
 
     def step(self):
         """One token as separate launches: 4 GEMVs per layer, lm_head, argmax."""
@@ -269,6 +272,10 @@ def kernel_table(torch, ds, reps=10):
         out["lm_head"] = {"N": N, "K": K, "fmt": fmt, "M": ds.M, "launches_per_step": 1,
                           "us_per_launch": us, "bytes_per_launch": int(nbytes),
                           "gbps": nbytes / (us * 1e-6) / 1e9}
+        fused = lambda: ds.kq.kq_gemv_argmax(fmt, Wd, xd, yd, N, K, ds.M, am, ws, wsb)
+        us_f = _graph_us(torch, [fused] * 8, reps)
+        out["lm_head_argmax"] = {"entry": "kq_gemv_argmax", "us_per_call": us_f,
+                                 "kernels_per_call": 2 if ds.M == 1 else 3}
         am_fn = lambda: ds.kq.kq_argmax(yd, N, ds.M, am, ws, wsb)
         us = _graph_us(torch, [am_fn] * 8, reps)
         out["argmax"] = {"N": N, "kernels_per_call": 2, "us_per_call": us,
@@ -558,8 +565,8 @@ def main():
     # the headline is the faster of the two (both run the same work)
     if ms_launches <= ms_stacked:
         ms_per_step, per = ms_launches, per_l
-        path = (f"{ds.layers * 4 + 1} kq_gemv launches + kq_argmax (2 kernels), "
-                "captured once as a HIP graph and replayed")
+        path = (f"{ds.layers * 4} kq_gemv launches + kq_gemv_argmax (the lm_head kernel leaves per-workgroup "
+                "argmax partials, one reduction kernel), captured once as a HIP graph and replayed")
         other = {"path": "kq_stack_run (persistent, decode order) + argmax", "ms_per_step": ms_stacked}
     else:
         ms_per_step, per = ms_stacked, per_s

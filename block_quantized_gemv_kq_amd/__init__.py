@@ -34,6 +34,8 @@ SIGNATURES = {
     "kq_unpack": (_I32, [_I32, _P, _I64, _I64, _P]),
     "kq_gemv": (_I32, [_I32, _P, _P, _P, _I64, _I64, _I32, _P]),
     "kq_gemv_invariant": (_I32, [_I32, _P, _P, _P, _I64, _I64, _I32, _P]),
+    "kq_gemv_argmax_workspace_bytes": (_I64, [_I32, _I64, _I64, _I32]),
+    "kq_gemv_argmax": (_I32, [_I32, _P, _P, _P, _I64, _I64, _I32, _P, _P, _I64, _P]),
     "kq_moe_gemv_workspace_bytes": (_I64, [_I64, _I32, _I32, _I32]),
     "kq_moe_gemv": (_I32, [_I32, _P, _P, _P, _P, _P, _I64, _I64, _I32, _I32, _I32, _I32, _P, _I64, _P]),
     "kq_moe_ffn_workspace_bytes": (_I64, [_I64, _I64, _I32, _I32]),
@@ -183,6 +185,17 @@ def kq_f32_to_f16(a: np.ndarray) -> np.ndarray:
 def kq_gemv(fmt, W, x, y, N: int, K: int, M: int, stream=None) -> None:
     """y[M][N] (fp32, device) = dequant(W)[N][K] @ x[M][K]^T (x fp16 bits, device)."""
     _check(lib().kq_gemv(_fmt(fmt), _ptr(W), _ptr(x), _ptr(y), N, K, M, _stream(stream)), "kq_gemv")
+
+
+def kq_gemv_argmax_workspace_bytes(fmt, N: int, K: int, M: int) -> int:
+    return _check(lib().kq_gemv_argmax_workspace_bytes(_fmt(fmt), N, K, M), "kq_gemv_argmax_workspace_bytes")
+
+
+def kq_gemv_argmax(fmt, W, x, y, N: int, K: int, M: int, out, workspace, workspace_bytes: int,
+                   stream=None) -> None:
+    """kq_gemv into y, then out[m] = argmax of y[m] (int32, device)."""
+    _check(lib().kq_gemv_argmax(_fmt(fmt), _ptr(W), _ptr(x), _ptr(y), N, K, M, _ptr(out), _ptr(workspace),
+                                workspace_bytes, _stream(stream)), "kq_gemv_argmax")
 
 
 def kq_gemv_invariant(fmt, W, x, y, N: int, K: int, M: int, stream=None) -> None:

@@ -427,6 +427,39 @@ int kq_stack_status(const void* plan, const kq_stack_info* info, int* error, voi
   return ok();
 }
 
+int64_t kq_gemv_argmax_workspace_bytes(int fmt, int64_t N, int64_t K, int M) {
+  int st = check_fmt_k(fmt, K);
+  if (st) return st;
+  if ((st = check_n(N, "N"))) return st;
+  if (M < 0 || M > KQ_MAX_M) return fail(KQ_ERR_ARG, "M=%d must be in [0, %d]", M, KQ_MAX_M);
+  if (N > KQ_MAX_N) return fail(KQ_ERR_ARG, "N=%lld out of range", (long long)N);
+  kq::GemvArgs a{fmt, nullptr, nullptr, nullptr, N, K, M, nullptr};
+  const int64_t fused = (int64_t)M * kq::gemv_argmax_fused_parts(a) * 8;
+  const int64_t plain = (int64_t)M * kq::argmax_partials(N) * 8;
+  return fused > plain ? fused : plain;
+}
+
+int kq_gemv_argmax(int fmt, const void* W, const uint16_t* x, float* y, int64_t N, int64_t K, int M,
+                   int32_t* out, void* workspace, int64_t workspace_bytes, void* stream) {
+  int st = check_fmt_k(fmt, K);
+  if (st) return st;
+  if ((st = check_n(N, "N"))) return st;
+  if (N < 1 || N > KQ_MAX_N) return fail(KQ_ERR_ARG, "kq_gemv_argmax: N=%lld out of range", (long long)N);
+  if (M < 0 || M > KQ_MAX_M) return fail(KQ_ERR_ARG, "M=%d must be in [0, %d]", M, KQ_MAX_M);
+  if (M == 0) return ok();
+  if (!W || !x || !y || !out) return fail(KQ_ERR_ARG, "kq_gemv_argmax: null pointer");
+  if (!aligned(W, 4) || !aligned(y, 4) || !aligned(out, 4))
+    return fail(KQ_ERR_ALIGN, "kq_gemv_argmax: W, y and out must be 4-byte aligned");
+  if (!aligned(x, 16)) return fail(KQ_ERR_ALIGN, "kq_gemv_argmax: x must be 16-byte aligned");
+  const int64_t need = kq_gemv_argmax_workspace_bytes(fmt, N, K, M);
+  if (need < 0) return (int)need;
+  if (!workspace || workspace_bytes < need)
+    return fail(KQ_ERR_ARG, "kq_gemv_argmax: workspace of %lld bytes needed", (long long)need);
+  if (!aligned(workspace, 8)) return fail(KQ_ERR_ALIGN, "kq_gemv_argmax: workspace must be 8-byte aligned");
+  kq::GemvArgs a{fmt, static_cast<const uint8_t*>(W), x, y, N, K, M, static_cast<hipStream_t>(stream)};
+  return hip_status(kq::launch_gemv_argmax(a, out, workspace), "kq_gemv_argmax");
+}
+
 int64_t kq_argmax_workspace_bytes(int64_t N, int M) {
   if (N < 0 || M < 0) return fail(KQ_ERR_ARG, "negative size");
   return (int64_t)M * kq::argmax_partials(N) * 8;

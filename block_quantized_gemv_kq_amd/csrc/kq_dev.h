@@ -134,6 +134,35 @@ __device__ __forceinline__ void load_unit(rsrc_t r, uint32_t off, uint32_t* D) {
   D[Fmt<FMT>::UDW - 1] = ld32(r, off + 16u * NV);
 }
 
+// (value, index) pairs for the argmax: the larger value wins; on equal values
+// the lower index; NaN never wins. Index INT32_MAX marks "nothing yet".
+struct Best {
+  float v;
+  int32_t i;
+};
+
+__device__ __forceinline__ Best better(Best a, Best b) {
+  if (b.v > a.v || (b.v == a.v && b.i < a.i)) return b;
+  return a;
+}
+
+// The same order as one 64-bit key, for atomic max: high word the value
+// mapped to an unsigned order (NaN -> 0, below every number; -0 as +0, as
+// they compare equal), low word the complement of the index (the lower index
+// is the larger key). Key 0 is "nothing yet".
+__device__ __forceinline__ unsigned long long best_key(float v, int32_t i) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v) == 0x80000000u ? 0u : __builtin_bit_cast(uint32_t, v);
+  const uint32_t o = v != v ? 0u : ((u & 0x80000000u) ? ~u : (u | 0x80000000u));
+  return o == 0u ? 0ull : ((unsigned long long)o << 32) | (uint32_t)~(uint32_t)i;
+}
+
+__device__ __forceinline__ Best best_of_key(unsigned long long k) {
+  if (k == 0ull) return Best{-__builtin_inff(), INT32_MAX};
+  const uint32_t o = (uint32_t)(k >> 32);
+  const uint32_t u = (o & 0x80000000u) ? (o & 0x7fffffffu) : ~o;
+  return Best{__builtin_bit_cast(float, u), (int32_t)~(uint32_t)k};
+}
+
 // Four nibble dwords of one 4-bit block -> 16 fp16 pairs (1024 + q), ordered
 // to pair with activation dwords 0..15 of the block (dword i = x[2i], x[2i+1]).
 // Byte t of the nibble area holds element t (low nibble) and t+16 (high).

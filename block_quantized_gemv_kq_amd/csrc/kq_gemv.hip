@@ -62,16 +62,28 @@ constexpr int XREG_CHUNKS = 5;   // 16-byte activation chunks per thread in the 
 // loads of all ITERS units it owns, the workgroup stages the MT activation
 // columns in LDS meanwhile, and only then does any arithmetic: one memory
 // round trip per tile. `passes` > 1 only when units > G * ITERS.
-template <int FMT, int MT, int ITERS, bool XREG, int WPG = 4>
+// AM: also the argmax epilogue: the workgroup's best (value, row) of each
+// column goes to part[column][blockIdx.x] (nparts per column), for
+// k_argmax_final.
+template <int FMT, int MT, int ITERS, bool XREG, int WPG = 4, bool AM = false>
 __global__ __launch_bounds__(64 * WPG) void k_gemv_lds(const uint8_t* __restrict__ W,
                                                   const uint16_t* __restrict__ x,
                                                   float* __restrict__ y, int N, int K, int log2g,
-                                                  int m0, int passes) {
+                                                  int m0, int passes, Best* __restrict__ part, int nparts) {
   extern __shared__ u32x4 x_lds4[];
   uint32_t* xl = reinterpret_cast<uint32_t*>(x_lds4);
   const int lane = threadIdx.x & 63;
   const int wave = blockIdx.x * WPG + wave_id();
   const int G = 1 << log2g;
+  __shared__ unsigned long long s_am_key[AM ? MT : 1];
+  __shared__ uint32_t s_am_count;
+  if constexpr (AM) {
+    if (threadIdx.x == 0) {   // ordered before every update by the staging barrier below
+#pragma unroll
+      for (int m = 0; m < MT; ++m) s_am_key[m] = 0ull;
+      s_am_count = 0u;
+    }
+  }
   const int rpw = 64 >> log2g;
   const int64_t row_base = (int64_t)wave * rpw;
   const uint32_t row_bytes = (uint32_t)(K / 32) * Fmt<FMT>::BB;
@@ -132,6 +144,25 @@ __global__ __launch_bounds__(64 * WPG) void k_gemv_lds(const uint8_t* __restrict
   if (g == 0 && rho < valid) {
 #pragma unroll
     for (int m = 0; m < MT; ++m) y[(int64_t)(m0 + m) * N + row_base + rho] = acc[m];
+  }
+  if constexpr (AM) {
+    // No barrier: each row's (value, row) key goes into the workgroup's slot
+    // by an LDS 64-bit atomic max, then the wave bumps a counter; the wave
+    // that completes the count publishes the slot.
+    if (g == 0 && rho < valid) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m) atomicMax(&s_am_key[m], best_key(acc[m], (int32_t)(row_base + rho)));
+    }
+    if (lane == 0) {
+      const uint32_t done = __hip_atomic_fetch_add(&s_am_count, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+      if (done == WPG - 1) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          const unsigned long long k = __hip_atomic_load(&s_am_key[m], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
+          part[(int64_t)(m0 + m) * nparts + blockIdx.x] = best_of_key(k);
+        }
+      }
+    }
   }
 }
 
@@ -327,37 +358,50 @@ LdsCfg lds_cfg(int64_t N, int units, int unit_bytes) {
 }
 
 template <int FMT, int MT, int ITERS, int WPG>
-int launch_lds_wpg(const GemvArgs& a, int m0, LdsCfg c) {
+int launch_lds_wpg(const GemvArgs& a, int m0, LdsCfg c, Best* part) {
   const int64_t rpw = 64 >> c.log2g;
   const int64_t waves = (a.N + rpw - 1) / rpw;
-  const dim3 grid((unsigned)((waves + WPG - 1) / WPG)), block(64 * WPG);
+  const int64_t nwg = (waves + WPG - 1) / WPG;
+  const dim3 grid((unsigned)nwg), block(64 * WPG);
   const size_t lds = (size_t)MT * a.K * 2 + (size_t)MT * (a.K / 32) * 8;  // x + block sums
-  if ((int64_t)MT * a.K / 8 <= 64 * WPG * XREG_CHUNKS)
+  const bool xreg = (int64_t)MT * a.K / 8 <= 64 * WPG * XREG_CHUNKS;
+  if (MT == 1 && part) {   // the argmax epilogue (one column only)
+    if (xreg)
+      hipLaunchKernelGGL((k_gemv_lds<FMT, MT, ITERS, true, WPG, MT == 1>), grid, block, lds, a.stream, a.W, a.x, a.y,
+                         (int)a.N, (int)a.K, c.log2g, m0, c.passes, part, (int)nwg);
+    else
+      hipLaunchKernelGGL((k_gemv_lds<FMT, MT, ITERS, false, WPG, MT == 1>), grid, block, lds, a.stream, a.W, a.x,
+                         a.y, (int)a.N, (int)a.K, c.log2g, m0, c.passes, part, (int)nwg);
+  } else if (xreg) {
     hipLaunchKernelGGL((k_gemv_lds<FMT, MT, ITERS, true, WPG>), grid, block, lds, a.stream, a.W, a.x, a.y,
-                       (int)a.N, (int)a.K, c.log2g, m0, c.passes);
-  else
+                       (int)a.N, (int)a.K, c.log2g, m0, c.passes, nullptr, 0);
+  } else {
     hipLaunchKernelGGL((k_gemv_lds<FMT, MT, ITERS, false, WPG>), grid, block, lds, a.stream, a.W, a.x, a.y,
-                       (int)a.N, (int)a.K, c.log2g, m0, c.passes);
+                       (int)a.N, (int)a.K, c.log2g, m0, c.passes, nullptr, 0);
+  }
   return (int)hipGetLastError();
 }
 
 template <int FMT, int MT, int ITERS>
-int launch_lds_it(const GemvArgs& a, int m0, LdsCfg c) {
+int launch_lds_it(const GemvArgs& a, int m0, LdsCfg c, Best* part) {
   if constexpr (MT == 1) {
-    if (c.wpg == 16) return launch_lds_wpg<FMT, MT, ITERS, 16>(a, m0, c);
-    if (c.wpg == 8) return launch_lds_wpg<FMT, MT, ITERS, 8>(a, m0, c);
+    if (c.wpg == 16) return launch_lds_wpg<FMT, MT, ITERS, 16>(a, m0, c, part);
+    if (c.wpg == 8) return launch_lds_wpg<FMT, MT, ITERS, 8>(a, m0, c, part);
   }
-  return launch_lds_wpg<FMT, MT, ITERS, 4>(a, m0, c);
+  return launch_lds_wpg<FMT, MT, ITERS, 4>(a, m0, c, part);
 }
 
+// Waves per workgroup the LDS kernel runs with (c.wpg applies to one column).
+int lds_wpg(const LdsCfg& c, int mt) { return mt == 1 ? c.wpg : 4; }
+
 template <int FMT, int MT>
-int launch_lds_mt(const GemvArgs& a, int m0, LdsCfg c) {
+int launch_lds_mt(const GemvArgs& a, int m0, LdsCfg c, Best* part = nullptr) {
   switch (c.iters) {
-    case 1: return launch_lds_it<FMT, MT, 1>(a, m0, c);
-    case 2: return launch_lds_it<FMT, MT, 2>(a, m0, c);
-    case 3: return launch_lds_it<FMT, MT, 3>(a, m0, c);
-    case 4: return launch_lds_it<FMT, MT, 4>(a, m0, c);
-    default: return launch_lds_it<FMT, MT, 5>(a, m0, c);
+    case 1: return launch_lds_it<FMT, MT, 1>(a, m0, c, part);
+    case 2: return launch_lds_it<FMT, MT, 2>(a, m0, c, part);
+    case 3: return launch_lds_it<FMT, MT, 3>(a, m0, c, part);
+    case 4: return launch_lds_it<FMT, MT, 4>(a, m0, c, part);
+    default: return launch_lds_it<FMT, MT, 5>(a, m0, c, part);
   }
 }
 
@@ -441,6 +485,69 @@ int dispatch_invariant(const GemvArgs& a) {
 }
 
 }  // namespace
+
+namespace {
+
+// GEMV + argmax of every column. For one column on the one-pass LDS kernel
+// (rows of whole units, x fits), that kernel leaves each workgroup's best
+// (value, row) in `ws` and one small kernel reduces them; otherwise the GEMV,
+// then kq_argmax's two kernels. Measured on the 151936 x 2560 Q8_0 output
+// layer: 72.4 against 75.4 us at M = 1; at M = 2 the fused form was 1.7 us
+// slower, so it stops at one column.
+template <int FMT>
+bool argmax_fusable(const GemvArgs& a, LdsCfg* cfg) {
+  if (a.K % (32 * Fmt<FMT>::UB) != 0 || a.M != 1) return false;
+  if ((int64_t)a.M * (a.K * 2 + a.K / 4) > LDS_MAX_BYTES) return false;
+  if (getenv("KQ_FORCE_PATH")) return false;
+  const int units = (int)(a.K / (32 * Fmt<FMT>::UB));
+  *cfg = lds_cfg(a.N, units, Fmt<FMT>::BB * Fmt<FMT>::UB);
+  return true;
+}
+
+int64_t fused_parts(const GemvArgs& a, const LdsCfg& c) {
+  const int64_t rpw = 64 >> c.log2g;
+  const int64_t waves = (a.N + rpw - 1) / rpw;
+  const int wpg = lds_wpg(c, a.M);
+  return (waves + wpg - 1) / wpg;
+}
+
+template <int FMT>
+int64_t gemv_argmax_parts_fmt(const GemvArgs& a) {
+  LdsCfg c;
+  return argmax_fusable<FMT>(a, &c) ? fused_parts(a, c) : 0;
+}
+
+template <int FMT>
+int gemv_argmax_fmt(const GemvArgs& a, int32_t* out, void* ws) {
+  LdsCfg c;
+  if (!argmax_fusable<FMT>(a, &c)) {
+    int err = launch_gemv(a);
+    if (err) return err;
+    return launch_argmax(a.y, a.N, a.M, out, ws, a.stream);
+  }
+  Best* part = static_cast<Best*>(ws);
+  const int err = launch_lds_mt<FMT, 1>(a, 0, c, part);
+  if (err) return err;
+  return launch_argmax_final(part, (int)fused_parts(a, c), a.M, out, a.stream);
+}
+
+}  // namespace
+
+int64_t gemv_argmax_fused_parts(const GemvArgs& a) {
+  switch (a.fmt) {
+    case KQ_Q8_0: return gemv_argmax_parts_fmt<F_Q8_0>(a);
+    case KQ_Q4_0: return gemv_argmax_parts_fmt<F_Q4_0>(a);
+    default: return gemv_argmax_parts_fmt<F_AFFINE4>(a);
+  }
+}
+
+int launch_gemv_argmax(const GemvArgs& a, int32_t* out, void* ws) {
+  switch (a.fmt) {
+    case KQ_Q8_0: return gemv_argmax_fmt<F_Q8_0>(a, out, ws);
+    case KQ_Q4_0: return gemv_argmax_fmt<F_Q4_0>(a, out, ws);
+    default: return gemv_argmax_fmt<F_AFFINE4>(a, out, ws);
+  }
+}
 
 int launch_gemv_invariant(const GemvArgs& a) {
   switch (a.fmt) {

@@ -32,6 +32,10 @@ struct GemvArgs {
 };
 int launch_gemv(const GemvArgs& a);
 int launch_gemv_invariant(const GemvArgs& a);
+// GEMV then the argmax of every column (out: device int32 [M]); ws holds the
+// partials (gemv_argmax_fused_parts(a) per column when fused, else kq_argmax's).
+int launch_gemv_argmax(const GemvArgs& a, int32_t* out, void* ws);
+int64_t gemv_argmax_fused_parts(const GemvArgs& a);
 int launch_gemv_mfma(const GemvArgs& a);
 
 struct MoeArgs {
@@ -128,6 +132,7 @@ int read_from_device(void* dst, const void* src, int64_t bytes, hipStream_t stre
 
 int64_t argmax_partials(int64_t N);
 int launch_argmax(const float* y, int64_t N, int M, int32_t* out, void* ws, hipStream_t stream);
+int launch_argmax_final(const void* part, int nparts, int M, int32_t* out, hipStream_t stream);
 
 const char* hip_error_string(int err);
 

@@ -24,17 +24,6 @@ __global__ __launch_bounds__(256) void k_weighted_slot_sum(const float* __restri
   y[(int64_t)m * N + n] = acc;
 }
 
-// (value, index) pairs: the larger value wins; on equal values the lower
-// index; NaN never wins. Index INT32_MAX marks "nothing yet".
-struct Best {
-  float v;
-  int32_t i;
-};
-
-__device__ __forceinline__ Best better(Best a, Best b) {
-  if (b.v > a.v || (b.v == a.v && b.i < a.i)) return b;
-  return a;
-}
 
 __device__ __forceinline__ Best block_best(Best b, Best* s_red) {
   for (int off = 32; off > 0; off >>= 1) {
@@ -68,12 +57,19 @@ __global__ __launch_bounds__(256) void k_argmax_partial(const float* __restrict_
   if (threadIdx.x == 0) part[(int64_t)m * nparts + blockIdx.x] = b;
 }
 
-__global__ __launch_bounds__(256) void k_argmax_final(const Best* __restrict__ part, int nparts,
-                                                      int32_t* __restrict__ out) {
-  __shared__ Best s_red[4];
+__global__ __launch_bounds__(1024) void k_argmax_final(const Best* __restrict__ part, int nparts,
+                                                       int32_t* __restrict__ out) {
+  __shared__ Best s_red[16];
   const int m = blockIdx.x;
+  const Best* p = part + (int64_t)m * nparts;
   Best b{-__builtin_inff(), INT32_MAX};
-  for (int i = threadIdx.x; i < nparts; i += 256) b = better(b, part[(int64_t)m * nparts + i]);
+  const int nt = (int)blockDim.x;
+  int i = threadIdx.x;
+  for (; i + 3 * nt < nparts; i += 4 * nt) {   // four loads in flight per thread
+    const Best a0 = p[i], a1 = p[i + nt], a2 = p[i + 2 * nt], a3 = p[i + 3 * nt];
+    b = better(better(b, a0), better(better(a1, a2), a3));
+  }
+  for (; i < nparts; i += nt) b = better(b, p[i]);
   b = block_best(b, s_red);
   if (threadIdx.x == 0) out[m] = b.i == INT32_MAX ? 0 : b.i;
 }
@@ -92,6 +88,12 @@ int launch_weighted_slot_sum(const float* ys, const float* w, float* y, int64_t 
 }
 
 int64_t argmax_partials(int64_t N) { return (N + ARGMAX_CHUNK - 1) / ARGMAX_CHUNK; }
+
+int launch_argmax_final(const void* part, int nparts, int M, int32_t* out, hipStream_t stream) {
+  hipLaunchKernelGGL(k_argmax_final, dim3((unsigned)M), dim3(nparts >= 4096 ? 1024 : 256), 0, stream,
+                     static_cast<const Best*>(part), nparts, out);
+  return (int)hipGetLastError();
+}
 
 int launch_argmax(const float* y, int64_t N, int M, int32_t* out, void* ws, hipStream_t stream) {
   const int nparts = (int)argmax_partials(N);

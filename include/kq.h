@@ -191,6 +191,25 @@ int64_t kq_argmax_workspace_bytes(int64_t N, int M);
 int kq_argmax(const float* y, int64_t N, int M, int32_t* out,
               void* workspace, int64_t workspace_bytes, void* stream);
 
+/* Workspace bytes kq_gemv_argmax needs for this shape (< 0: the error of an
+ * invalid shape). */
+int64_t kq_gemv_argmax_workspace_bytes(int fmt, int64_t N, int64_t K, int M);
+
+/* kq_gemv_argmax — kq_gemv, then kq_argmax of every column: y as kq_gemv
+ * writes it, and out[m] (device int32 [M]) the index of column m's largest
+ * value with kq_argmax's rules. The argmax is the output layer's greedy
+ * next-token choice (Kinetic docs, "What makes it fast": choosing the next
+ * token reads an output layer of up to a quarter of a million rows, and the
+ * choice is exact). For one column on rows of whole units, the GEMV kernel
+ * itself leaves each workgroup's best (value, row) in the workspace and one
+ * small kernel picks the winner, instead of two kernels over y.
+ * workspace: device, >= kq_gemv_argmax_workspace_bytes, 8-byte aligned,
+ * caller-owned, no initial contents. Arguments otherwise as kq_gemv; out is
+ * 4-byte aligned. Errors: those of kq_gemv, KQ_ERR_ARG (N < 1, workspace). */
+int kq_gemv_argmax(int fmt, const void* W, const uint16_t* x, float* y,
+                   int64_t N, int64_t K, int M, int32_t* out,
+                   void* workspace, int64_t workspace_bytes, void* stream);
+
 /* ---- A chain of dependent M = 1 GEMVs in one persistent launch ----------
  * Kinetic docs, "What makes it fast": a decode step is hundreds of small GPU
  * kernels, recorded once and replayed with one call per token. kq_stack_run

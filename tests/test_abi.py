@@ -127,6 +127,26 @@ def test_moe_ffn_validation():
     assert call(top_k=129) == kq.KQ_ERR_ARG
 
 
+def test_gemv_argmax_validation():
+    L = kq.lib()
+    need = kq.kq_gemv_argmax_workspace_bytes(0, 151936, 2560, 1)
+    assert need >= 151936 // 16 * 8 // 4          # partials of every workgroup
+    assert kq.kq_gemv_argmax_workspace_bytes(0, 151936, 2560, 8) >= 8 * kq.kq_argmax_workspace_bytes(151936, 1)
+    assert L.kq_gemv_argmax_workspace_bytes(0, 100, 48, 1) == kq.KQ_ERR_SHAPE
+
+    def call(fmt=0, W=A16, x=A16, y=A16, N=151936, K=2560, M=1, out=A16, ws=A16, wsb=need):
+        return L.kq_gemv_argmax(fmt, W, x, y, N, K, M, out, ws, wsb, 0)
+    assert call(fmt=7) == kq.KQ_ERR_FORMAT
+    assert call(N=0) == kq.KQ_ERR_ARG
+    assert call(out=None) == kq.KQ_ERR_ARG
+    assert call(wsb=need - 8) == kq.KQ_ERR_ARG
+    assert call(ws=None) == kq.KQ_ERR_ARG
+    assert call(out=A16 + 2) == kq.KQ_ERR_ALIGN
+    assert call(ws=A16 + 4) == kq.KQ_ERR_ALIGN
+    assert call(x=A4) == kq.KQ_ERR_ALIGN
+    assert call(M=0, W=None, x=None, y=None, out=None, ws=None, wsb=0) == kq.KQ_OK
+
+
 def test_argmax_validation():
     L = kq.lib()
     need = kq.kq_argmax_workspace_bytes(151936, 3)
