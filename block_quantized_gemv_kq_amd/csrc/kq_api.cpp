@@ -2,6 +2,7 @@
 // call), thread-local error messages, and dispatch to the kernel launchers.
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <vector>
@@ -176,6 +177,8 @@ int kq_moe_gemv(int fmt, const void* W_experts, const uint16_t* x, const int32_t
   float* slots = route_w ? static_cast<float*>(workspace) : y;
   kq::MoeArgs a{fmt, static_cast<const uint8_t*>(W_experts), x, route_ids, slots, N, K, M, top_k,
                 n_experts, x_per_slot, s};
+  if (route_w && kq::moe_down_sum_applies(a) && !getenv("KQ_MOE_UNFUSED"))
+    return hip_status(kq::launch_moe_down_sum(a, route_w, y), "kq_moe_gemv");
   int err = kq::launch_moe_gemv(a);
   if (!err && route_w) err = kq::launch_weighted_slot_sum(slots, route_w, y, N, M, top_k, s);
   return hip_status(err, "kq_moe_gemv");
@@ -215,11 +218,12 @@ int kq_moe_ffn(int fmt, const void* W_gate, const void* W_up, const void* W_down
   kq::MoeGateUpArgs g{fmt, static_cast<const uint8_t*>(W_gate), static_cast<const uint8_t*>(W_up),
                       x, route_ids, h, inter, hidden, M, top_k, n_experts, s};
   int err = kq::launch_moe_gate_up_swiglu(g);
-  if (!err) {
-    kq::MoeArgs d{fmt, static_cast<const uint8_t*>(W_down), h, route_ids, slots, hidden, inter, M,
-                  top_k, n_experts, 1, s};
-    err = kq::launch_moe_gemv(d);
-  }
+  if (err) return hip_status(err, "kq_moe_ffn");
+  kq::MoeArgs d{fmt, static_cast<const uint8_t*>(W_down), h, route_ids, slots, hidden, inter, M,
+                top_k, n_experts, 1, s};
+  if (kq::moe_down_sum_applies(d) && !getenv("KQ_MOE_UNFUSED"))
+    return hip_status(kq::launch_moe_down_sum(d, route_w, y), "kq_moe_ffn");
+  err = kq::launch_moe_gemv(d);
   if (!err) err = kq::launch_weighted_slot_sum(slots, route_w, y, hidden, M, top_k, s);
   return hip_status(err, "kq_moe_ffn");
 }

@@ -53,6 +53,11 @@ struct MoeArgs {
   hipStream_t stream;
 };
 int launch_moe_gemv(const MoeArgs& a);
+// One token, weighted: per-slot outputs and their slot-order weighted sum in
+// one launch (same bits as launch_moe_gemv + launch_weighted_slot_sum);
+// moe_down_sum_applies tells whether the shape allows it.
+bool moe_down_sum_applies(const MoeArgs& a);
+int launch_moe_down_sum(const MoeArgs& a, const float* route_w, float* y);
 
 struct MoeGateUpArgs {
   int fmt;

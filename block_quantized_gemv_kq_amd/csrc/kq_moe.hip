@@ -335,6 +335,82 @@ __global__ __launch_bounds__(256) void k_moe_lds(const uint8_t* __restrict__ W0,
   }
 }
 
+// One token (M = 1), weighted: the down projection of every routed slot and
+// their weighted sum in one launch. Workgroup = top_k waves over the same rpw
+// rows; wave j computes slot j exactly as k_moe_lds does for one column (x of
+// the slot staged in LDS with its block sums, the same lane groups and units),
+// leaves its row results in LDS, and the first wave adds them in slot order as
+// k_weighted_slot_sum does, so y has the same bits as the three-kernel path.
+// An id outside [0, n_experts) makes that slot's result, and so y, NaN.
+// Dynamic LDS: per slot the x row (K fp16) and its block sums (K/32 x 2 fp32),
+// then top_k x rpw fp32 slot results.
+template <int FMT, int ITERS>
+__global__ __launch_bounds__(1024) void k_moe_down_sum(const uint8_t* __restrict__ W, const uint16_t* __restrict__ x,
+                                                      const int32_t* __restrict__ ids, const float* __restrict__ rw,
+                                                      float* __restrict__ y, int N, int K, int top_k, int n_experts,
+                                                      int x_per_slot, int log2g, int64_t expert_bytes) {
+  extern __shared__ u32x4 x_lds4[];
+  const int lane = threadIdx.x & 63;
+  const int j = wave_id();                       // this wave's slot
+  const int kdw = K / 2, nblk = K / 32;
+  const int slot_dw = kdw + nblk * 2;            // x dwords + block sums of one slot
+  uint32_t* xl = reinterpret_cast<uint32_t*>(x_lds4) + (int64_t)j * slot_dw;
+  float* xs = reinterpret_cast<float*>(xl + kdw);
+  float* s_y = reinterpret_cast<float*>(reinterpret_cast<uint32_t*>(x_lds4) + (int64_t)top_k * slot_dw);
+  const int G = 1 << log2g;
+  const int rpw = 64 >> log2g;
+  const int64_t row_base = (int64_t)blockIdx.x * rpw;
+  const int rho = lane >> log2g, g = lane & (G - 1);
+  const int valid = row_base < N ? (int)min<int64_t>(rpw, N - row_base) : 0;
+  const int e = ids[j];
+  const bool e_ok = e >= 0 && e < n_experts;
+  const uint32_t row_bytes = (uint32_t)nblk * Fmt<FMT>::BB;
+  const int64_t off = (int64_t)(e_ok ? e : 0) * expert_bytes + (valid ? row_base * row_bytes : 0);
+  const rsrc_t rs = make_rsrc(W + off, e_ok ? (uint32_t)valid * row_bytes : 0u);
+  const uint32_t roff = (uint32_t)rho * row_bytes;
+  const int units = K / (32 * Fmt<FMT>::UB);
+  const int kq8 = K / 8;
+  // x of this slot into registers, then the weights, then x into LDS
+  const rsrc_t xsrc = make_rsrc(x + (int64_t)(x_per_slot ? j : 0) * K, (uint32_t)K * 2u);
+  u32x4 xr[MOE_XCH];
+#pragma unroll
+  for (int c = 0; c < MOE_XCH; ++c) {
+    const int i = lane + 64 * c;
+    xr[c] = ld128(xsrc, i < kq8 ? (uint32_t)i * 16u : OOB);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  Loaded<FMT, ITERS> w;
+  issue_units<FMT, ITERS>(rs, roff, g, G, units, w);
+  __builtin_amdgcn_sched_barrier(0);
+  u32x4* xl4 = reinterpret_cast<u32x4*>(xl);
+#pragma unroll
+  for (int c = 0; c < MOE_XCH; ++c) {
+    const int i = lane + 64 * c;
+    if (i < kq8) xl4[i] = xr[c];
+  }
+  __syncthreads();
+  // block sums of this slot's x (as block_sums_to_lds for one column)
+  for (int h = lane; h < kdw / 8; h += 64) {
+    const u32x4* q = reinterpret_cast<const u32x4*>(xl) + 2 * h;
+    const u32x4 a = q[0], c = q[1];
+    float v = 0.0f;
+    v = dot2(a.x, ONES, v); v = dot2(a.y, ONES, v); v = dot2(a.z, ONES, v); v = dot2(a.w, ONES, v);
+    v = dot2(c.x, ONES, v); v = dot2(c.y, ONES, v); v = dot2(c.z, ONES, v); v = dot2(c.w, ONES, v);
+    xs[h] = v;
+  }
+  __syncthreads();
+  float acc[1] = {0.0f};
+  consume_units<FMT, 1, ITERS>(w, xl, xs, kdw, g, G, units, acc);
+  group_reduce<1>(acc, G);
+  if (g == 0 && rho < valid) s_y[j * rpw + rho] = e_ok ? acc[0] : __builtin_nanf("");
+  __syncthreads();
+  if (j == 0 && g == 0 && rho < valid) {
+    float t = 0.0f;
+    for (int q = 0; q < top_k; ++q) t = __builtin_fmaf(rw[q], s_y[q * rpw + rho], t);
+    y[row_base + rho] = t;
+  }
+}
+
 // Generic routed kernel for rows that are only 2-byte aligned (Q4_0/Q8_0 with
 // an odd number of blocks per row): one wave per (row, slot), per-block loads.
 template <int FMT>
@@ -494,7 +570,44 @@ int gate_up_dispatch(const MoeGateUpArgs& a) {
   return (int)hipGetLastError();
 }
 
+template <int FMT>
+int launch_moe_down_sum_fmt(const MoeArgs& a, const float* rw, float* y) {
+  const int64_t eb = a.N * (a.K / 32) * Fmt<FMT>::BB;
+  const int units = (int)(a.K / (32 * Fmt<FMT>::UB));
+  const int log2g = moe_lds_log2g<FMT>(units);
+  const int iters = (units + (1 << log2g) - 1) >> log2g;
+  const int64_t rpw = 64 >> log2g;
+  const dim3 grid((unsigned)((a.N + rpw - 1) / rpw)), block((unsigned)(64 * a.top_k));
+  const size_t lds = (size_t)a.top_k * ((size_t)a.K * 2 + (size_t)(a.K / 32) * 8) + (size_t)a.top_k * rpw * 4;
+#define KQ_MOE_DS(IT)                                                                                          \
+  hipLaunchKernelGGL((k_moe_down_sum<FMT, IT>), grid, block, lds, a.stream, a.W, a.x, a.ids, rw, y, (int)a.N,   \
+                     (int)a.K, a.top_k, a.n_experts, a.x_per_slot, log2g, eb)
+  switch (iters) {
+    case 1: KQ_MOE_DS(1); break;
+    case 2: KQ_MOE_DS(2); break;
+    case 3: KQ_MOE_DS(3); break;
+    case 4: KQ_MOE_DS(4); break;
+    default: KQ_MOE_DS(5); break;
+  }
+#undef KQ_MOE_DS
+  return (int)hipGetLastError();
+}
+
 }  // namespace
+
+bool moe_down_sum_applies(const MoeArgs& a) {
+  const int ub = a.fmt == KQ_AFFINE4_G32 ? 1 : 2;
+  return a.M == 1 && a.top_k >= 1 && a.top_k <= 16 && a.K % (32 * ub) == 0 && moe_lds_fits(a.K) &&
+         a.K / 8 <= 64 * MOE_XCH;
+}
+
+int launch_moe_down_sum(const MoeArgs& a, const float* route_w, float* y) {
+  switch (a.fmt) {
+    case KQ_Q8_0: return launch_moe_down_sum_fmt<F_Q8_0>(a, route_w, y);
+    case KQ_Q4_0: return launch_moe_down_sum_fmt<F_Q4_0>(a, route_w, y);
+    default: return launch_moe_down_sum_fmt<F_AFFINE4>(a, route_w, y);
+  }
+}
 
 int launch_moe_gemv(const MoeArgs& a) {
   switch (a.fmt) {

@@ -127,3 +127,63 @@ def test_moe_ffn_workload(M):
     yr, ad, *_ = R.moe_ffn(L.fmt, gate.field_list(E), up.field_list(E), down.field_list(E), x, ids,
                            rw, h_override=hg)
     U.assert_parity(yg, yr, ad, f"moe ffn M={M}")
+
+
+def _weighted_gemv(fmt, ex, x, ids, rw, N, K, M, top_k, E, xps, unfused):
+    y = U.empty_dev((M, N))
+    wsb = kq.kq_moe_gemv_workspace_bytes(N, M, top_k, True)
+    ws = U.empty_dev((wsb // 4 + 1,))
+    with U.env_vars({"KQ_MOE_UNFUSED": "1"} if unfused else {}):
+        kq.kq_moe_gemv(fmt, ex.dev, U.to_dev(x), U.to_dev(ids), U.to_dev(rw), y, N, K, M, top_k, E, xps, ws, wsb)
+    return U.to_host(y)
+
+
+@pytest.mark.parametrize("fmt", ("q4_0", "q8_0", "affine4"))
+@pytest.mark.parametrize("xps", (0, 1))
+@pytest.mark.parametrize("top_k,ids_row", [(8, None), (2, [3, 3]), (3, [5, -1, 2]), (16, None)])
+def test_moe_one_token_weighted_is_one_launch_with_same_bits(fmt, xps, top_k, ids_row):
+    """One token, weighted: the single-launch down + slot-order sum gives the
+    bits of the per-slot kernel followed by the weighted-sum kernel (the
+    KQ_MOE_UNFUSED path), including a duplicated expert and a bad id (NaN)."""
+    N, K, E = 300, 768, 32
+    if ids_row is None:
+        ids, rw = _route(1, E, top_k, 40 + top_k)
+    else:
+        ids = np.array([ids_row], np.int32)
+        rw = np.linspace(0.2, 0.9, top_k, dtype=np.float32)[None, :]
+    ex = Experts(fmt, E, N, K, [v for v in ids.ravel() if 0 <= v < E], lambda e: (75, e, 0, 0))
+    x = S.activations((75, top_k, 0), K, top_k if xps else 1)
+    if xps:
+        x = x.reshape(1, top_k, K)
+    y1 = _weighted_gemv(fmt, ex, x, ids, rw, N, K, 1, top_k, E, xps, False)
+    y2 = _weighted_gemv(fmt, ex, x, ids, rw, N, K, 1, top_k, E, xps, True)
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32)) or (
+        np.all(np.isnan(y1)) and np.all(np.isnan(y2)))
+    if np.any(ids < 0):
+        assert np.all(np.isnan(y1))
+    else:
+        yr, ad = R.moe_gemv(fmt, ex.field_list(E), x, ids, rw, bool(xps))
+        U.assert_parity(y1, yr, ad, f"moe one token {fmt} top_k={top_k}")
+
+
+def test_moe_ffn_one_token_same_bits_as_three_kernels():
+    """The workload's MoE layer at one token: kq_moe_ffn's fused down + sum
+    against the per-slot + weighted-sum kernels, bit for bit."""
+    L = S.MOE_Q4_0
+    ids, rw = S.route_table(L.workload_id, 1, L.n_experts, L.top_k)
+    used = ids.ravel()
+    gate = Experts(L.fmt, L.n_experts, L.inter, L.hidden, used, lambda e: L.weight_seed(e, 0))
+    up = Experts(L.fmt, L.n_experts, L.inter, L.hidden, used, lambda e: L.weight_seed(e, 1))
+    down = Experts(L.fmt, L.n_experts, L.hidden, L.inter, used, lambda e: L.weight_seed(e, 2))
+    x = S.activations(L.act_seed_prefix(), L.hidden, 1)
+    wsb = kq.kq_moe_ffn_workspace_bytes(L.hidden, L.inter, 1, L.top_k)
+    outs = []
+    for unfused in (False, True):
+        y = U.empty_dev((1, L.hidden))
+        ws = U.empty_dev((wsb // 4 + 1,))
+        with U.env_vars({"KQ_MOE_UNFUSED": "1"} if unfused else {}):
+            kq.kq_moe_ffn(L.fmt, gate.dev, up.dev, down.dev, U.to_dev(x), U.to_dev(ids), U.to_dev(rw), y, None,
+                          L.hidden, L.inter, 1, L.top_k, L.n_experts, ws, wsb)
+        outs.append(U.to_host(y))
+    assert np.all(np.isfinite(outs[0]))
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
