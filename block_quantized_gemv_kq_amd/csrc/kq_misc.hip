@@ -19,8 +19,17 @@ __global__ __launch_bounds__(256) void k_weighted_slot_sum(const float* __restri
   const int m = blockIdx.y;
   if (n >= N) return;
   const float* base = ys + (int64_t)m * top_k * N + n;
+  const float* wm = w + (int64_t)m * top_k;
   float acc = 0.0f;
-  for (int j = 0; j < top_k; ++j) acc = __builtin_fmaf(w[(int64_t)m * top_k + j], base[(int64_t)j * N], acc);
+  int j = 0;
+  for (; j + 8 <= top_k; j += 8) {   // eight independent loads in flight, then the sums in order
+    float v[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) v[t] = base[(int64_t)(j + t) * N];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc = __builtin_fmaf(wm[j + t], v[t], acc);
+  }
+  for (; j < top_k; ++j) acc = __builtin_fmaf(wm[j], base[(int64_t)j * N], acc);
   y[(int64_t)m * N + n] = acc;
 }
 
