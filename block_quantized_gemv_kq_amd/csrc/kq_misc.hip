@@ -61,7 +61,15 @@ __global__ __launch_bounds__(256) void k_argmax_partial(const float* __restrict_
   const int64_t c1 = c0 + ARGMAX_CHUNK < N ? c0 + ARGMAX_CHUNK : N;
   const float* row = y + (int64_t)m * N;
   Best b{-__builtin_inff(), INT32_MAX};
-  for (int64_t i = c0 + threadIdx.x; i < c1; i += 256) b = better(b, Best{row[i], (int32_t)i});
+  int64_t i = c0 + threadIdx.x;
+  for (; i + 7 * 256 < c1; i += 8 * 256) {   // eight loads in flight, then the comparisons in order
+    float v[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) v[t] = row[i + t * 256];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) b = better(b, Best{v[t], (int32_t)(i + t * 256)});
+  }
+  for (; i < c1; i += 256) b = better(b, Best{row[i], (int32_t)i});
   b = block_best(b, s_red);
   if (threadIdx.x == 0) part[(int64_t)m * nparts + blockIdx.x] = b;
 }
