@@ -891,7 +891,9 @@ int64_t mfma_x_lds_bytes(int64_t K, int log2mp, bool sums) {
 }
 
 // Waves per tile S: enough that each wave holds at most maxp groups,
-// doubled while the grid has fewer than 2048 waves; then tiles per workgroup R
+// doubled while the grid has fewer than 1024 waves (measured against 2048 at
+// M = 4, 8, 16 on the decode shapes: q|k|v 8.0 -> 7.0 us, o 7.3 -> 6.6 us at
+// M = 8, with x issued first); then tiles per workgroup R
 // (R S <= 8, so that several workgroups share a CU and one computes while
 // another loads) while at least 1024 workgroups remain, so that one staged
 // copy of x serves several tiles. Not usable (ok = false) when x does not fit in LDS
@@ -906,7 +908,12 @@ MfmaLdsCfg mfma_lds_cfg(int64_t N, int64_t K, int M, int maxp, bool no_sums) {
   const int64_t tiles = (N + 15) / 16;
   int S = (ngroups + maxp - 1) / maxp;
   if (S > 16) return c;
-  while (S < 16 && S < ngroups && tiles * S < 2048) S *= 2;
+  int min_waves = 1024;
+  {
+    const char* ew = getenv("KQ_MFMA_WAVES");   // sweeps
+    if (ew && atoi(ew) > 0) min_waves = atoi(ew);
+  }
+  while (S < 16 && S < ngroups && tiles * S < min_waves) S *= 2;
   if (S > 16) S = 16;
   const char* e = getenv("KQ_MFMA_S");
   if (e) {
@@ -950,8 +957,8 @@ template <int FMT, int P, bool SX>
 int launch_mfma_lds_p(const GemvArgs& a, int m0, int mt, const MfmaLdsCfg& c) {
   const int64_t tiles = (a.N + 15) / 16;
   const dim3 grid((unsigned)((tiles + c.R - 1) / c.R)), block((unsigned)(64 * c.R * c.S));
-  const char* e = getenv("KQ_MFMA_XF");
-  if (e && atoi(e))
+  const char* e = getenv("KQ_MFMA_XF");   // x before the weights unless KQ_MFMA_XF=0
+  if (!e || atoi(e))
     hipLaunchKernelGGL((k_gemv_mfma_lds<FMT, P, SX, true>), grid, block, c.lds, a.stream, a.W, a.x + (int64_t)m0 * a.K,
                        a.y + (int64_t)m0 * a.N, (int)a.N, (int)a.K, mt, c.R, c.S, c.log2mp);
   else
