@@ -335,10 +335,11 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
 
 // Copy n16 16-byte chunks from global `src` to LDS `dst` (both 16-byte
-// aligned). Every thread of the workgroup must call it; follow with
-// __syncthreads() (which waits for the copies).
-__device__ __forceinline__ void stage_to_lds(const void* src, uint32_t* dst, int n16) {
-  for (int i = threadIdx.x; i < n16; i += blockDim.x) {
+// aligned). Every thread of the workgroup (nthreads of them, a compile-time
+// constant at the call sites, so no kernel argument is read for it) must
+// call it; follow with __syncthreads() (which waits for the copies).
+__device__ __forceinline__ void stage_to_lds(const void* src, uint32_t* dst, int n16, int nthreads) {
+  for (int i = threadIdx.x; i < n16; i += nthreads) {
     const int wave_first = i - (int)(threadIdx.x & 63);   // lane L lands at wave_first + L
     __builtin_amdgcn_global_load_lds((glb_void_t*)(reinterpret_cast<const u32x4*>(src) + i),
                                      (lds_void_t*)(dst + 4 * wave_first), 16, 0, 0);
@@ -441,10 +442,11 @@ __device__ __forceinline__ float block_dot_split(const uint32_t* A, const uint32
 // xl + m * kdw dwords, so the columns are one contiguous run): for column m
 // and block b, xs[(m * nblk + b) * 2 + {0,1}] = sum of elements 0..15 / 16..31,
 // i.e. xs[h] is the sum of half-block h of the run. Every thread of the
-// workgroup takes part; follow with __syncthreads().
-__device__ __forceinline__ void block_sums_to_lds(const uint32_t* xl, int kdw, int mt, float* xs) {
+// workgroup (nthreads, as for stage_to_lds) takes part; follow with
+// __syncthreads().
+__device__ __forceinline__ void block_sums_to_lds(const uint32_t* xl, int kdw, int mt, float* xs, int nthreads) {
   const int halves = mt * kdw / 8;
-  for (int h = threadIdx.x; h < halves; h += blockDim.x) {
+  for (int h = threadIdx.x; h < halves; h += nthreads) {
     const u32x4* p = reinterpret_cast<const u32x4*>(xl) + 2 * h;
     const u32x4 a = p[0], c = p[1];
     float s = 0.0f;

@@ -126,10 +126,10 @@ __global__ __launch_bounds__(64 * WPG) void k_gemv_lds(const uint8_t* __restrict
     }
   } else {
 #pragma unroll
-    for (int m = 0; m < MT; ++m) stage_to_lds(x + (int64_t)(m0 + m) * K, xl + m * kdw, K / 8);
+    for (int m = 0; m < MT; ++m) stage_to_lds(x + (int64_t)(m0 + m) * K, xl + m * kdw, K / 8, 64 * WPG);
   }
   __syncthreads();
-  block_sums_to_lds(xl, kdw, MT, xs);
+  block_sums_to_lds(xl, kdw, MT, xs, 64 * WPG);
   __syncthreads();
   float acc[MT];
 #pragma unroll

@@ -298,7 +298,7 @@ __global__ __launch_bounds__(256) void k_moe_lds(const uint8_t* __restrict__ W0,
       x_lds4[i < MOE_COLS * kq8 ? i : idle] = xr[c];   // unused pieces land past the x of this pass
     }
     __syncthreads();
-    block_sums_to_lds(xl, kdw, mt, xs);
+    block_sums_to_lds(xl, kdw, mt, xs, 256);
     __syncthreads();
     float a0[MOE_COLS], a1[MOE_COLS];
 #pragma unroll
