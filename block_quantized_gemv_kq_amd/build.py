@@ -2,8 +2,12 @@
 
 Host sources are compiled with g++ (the packer with -ffp-contract=off so every
 step is one IEEE fp32 operation); HIP sources with hipcc for gfx950 only, with
-packed-fp32 instructions disabled. Objects go to _build/, the library next to
-this file.
+packed-fp32 instructions disabled and kernel arguments preloaded into SGPRs
+(the command processor writes the first kernel-argument dwords into scalar
+registers before a wave starts, so a kernel does not wait on a scalar load of
+its arguments before issuing its first memory loads; the code object keeps a
+prologue that loads them for firmware without preloading). Objects go to
+_build/, the library next to this file.
 
 One HIP runtime per process: PyTorch-ROCm ships its own libamdhip64.so with
 the same soname (libamdhip64.so.7) as ROCm's. The binding imports torch before
@@ -36,7 +40,8 @@ HOST_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-ffp-contract=off", "-Wall", "-Wext
               "-Wno-unused-parameter"]
 HIP_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-fPIC", "-std=c++17",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-             "-Wno-unused-command-line-argument"]
+             "-Wno-unused-command-line-argument",
+             "-mllvm", "-amdgpu-kernarg-preload-count=16"]
 
 
 def _run(cmd, verbose):
