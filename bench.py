@@ -36,20 +36,22 @@ GROUP_NAMES = ("qkv", "o", "gate_up", "down")
 # HBM bytes per launch of the M = 1 GEMV kernels, from two counter passes
 # (FETCH_SIZE, then WRITE_SIZE, rocprofv3 --pmc over `bench.py --kernels-only`),
 # scaled by what the same counters read for a plain 256 MiB copy (FETCH x 2.0,
-# WRITE x 1.0). They hold only for the kernel sources they were taken on: a
-# changed source (sha256 prefix below) reports traffic as unknown.
+# WRITE x 1.0). They hold only for the kernel sources and build flags they were
+# taken with: a changed file (sha256 prefix below, paths under the package)
+# reports traffic as unknown.
 MEASURED_TRAFFIC = {
-    "sources": {"kq_gemv.hip": "5541a8597f30f82c", "kq_dev.h": "587ccf354365243d"},
-    "bytes": {"qkv": 9962890, "o": 6697490, "gate_up": 31327855, "down": 15820786,
-              "lm_head": 414292357},
+    "sources": {"csrc/kq_gemv.hip": "6149ab1b4e03a268", "csrc/kq_dev.h": "c74b68a6ea6363ea",
+                "build.py": "4539a7654dd76413"},
+    "bytes": {"qkv": 9960482, "o": 6692455, "gate_up": 31327734, "down": 15815098,
+              "lm_head": 414309058},
 }
 
 
 def measured_traffic(group):
     import hashlib
-    csrc = os.path.join(ROOT, "block_quantized_gemv_kq_amd", "csrc")
+    pkg = os.path.join(ROOT, "block_quantized_gemv_kq_amd")
     for name, want in MEASURED_TRAFFIC["sources"].items():
-        with open(os.path.join(csrc, name), "rb") as f:
+        with open(os.path.join(pkg, name), "rb") as f:
             if hashlib.sha256(f.read()).hexdigest()[:16] != want:
                 return None
     return MEASURED_TRAFFIC["bytes"].get(group)
