@@ -501,6 +501,8 @@ def main():
                     help="short run for kernel traces: only the M-column verify pass, graph-replayed")
     ap.add_argument("--kernels-only", action="store_true",
                     help="short run for counter collection: per-kernel graphs and a copy of known size")
+    ap.add_argument("--moe-only", action="store_true",
+                    help="short run for kernel traces: only the Q4_0 MoE layer at each token count")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -514,6 +516,11 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     kq.lib()
     stack = S.QWEN3_4B_AFFINE4
+
+    if args.moe_only:
+        moe = bench_moe(torch, kq, S, args.steps)
+        print(json.dumps({"moe_only": {m: round(v["us_per_layer"], 3) for m, v in moe.items()}}))
+        return
 
     t0 = time.perf_counter()
     log("packing and uploading the 4B-shaped stack (M=1) ...")
