@@ -957,13 +957,16 @@ template <int FMT, int P, bool SX>
 int launch_mfma_lds_p(const GemvArgs& a, int m0, int mt, const MfmaLdsCfg& c) {
   const int64_t tiles = (a.N + 15) / 16;
   const dim3 grid((unsigned)((tiles + c.R - 1) / c.R)), block((unsigned)(64 * c.R * c.S));
-  // x written to LDS before the weight loads are issued. Measured with cold
-  // x on the decode shapes at M = 2..16, this wins or ties everywhere but
-  // gate|up at M = 8 (14.30 against 13.55 us); e.g. o at M = 8 6.52 against
-  // 7.23 us, gate|up at M = 16 19.13 against 21.13 us. KQ_MFMA_XF=0 selects
-  // the other order (x loads, an issue-only barrier, weights, LDS writes).
+  // x written to LDS before the weight loads are issued, except for grids of
+  // at least 1024 tiles at 5..8 columns, which issue x loads, an issue-only
+  // barrier, the weights, then the LDS writes. Measured with cold x on the
+  // decode shapes: x first wins or ties at M = 2..16 on q|k|v, o and down
+  // (o at M = 8 6.52 against 7.23 us) and on gate|up at M = 2..4 and 12..16
+  // (M = 16 19.13 against 21.13 us), but gate|up (1216 tiles) at M = 5..8
+  // takes 0.5-1.1 us longer that way (M = 8 14.1-14.3 against 13.0-13.8 us).
+  // KQ_MFMA_XF=0 / 1 forces one order.
   const char* e = getenv("KQ_MFMA_XF");
-  const bool xf = !e || atoi(e) != 0;
+  const bool xf = e ? atoi(e) != 0 : !(c.log2mp == 3 && tiles >= 1024);
   if (xf)
     hipLaunchKernelGGL((k_gemv_mfma_lds<FMT, P, SX, true>), grid, block, c.lds, a.stream, a.W, a.x + (int64_t)m0 * a.K,
                        a.y + (int64_t)m0 * a.N, (int)a.N, (int)a.K, mt, c.R, c.S, c.log2mp);

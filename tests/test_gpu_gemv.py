@@ -178,7 +178,8 @@ def test_zero_and_constant_weights():
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("variant", ("pers", "pers_tpw3", "teams", "teams_sx", "teams_x0", "chunk", "direct"))
+@pytest.mark.parametrize("variant", ("pers", "pers_tpw3", "teams", "teams_sx", "teams_x0", "teams_x1", "chunk",
+                                     "direct"))
 @pytest.mark.parametrize("N,K,M", [(1000, 2560, 8), (37, 96, 5), (300, 4128, 16), (16, 32, 2), (529, 640, 13),
                                    (300, 4128, 40), (77, 9728, 33)])
 def test_mfma_variants_parity(fmt, variant, N, K, M):
@@ -194,6 +195,8 @@ def test_mfma_variants_parity(fmt, variant, N, K, M):
         env["KQ_MFMA_PERS_TPW"] = "3"
     if variant == "teams_x0":          # weights issued before x is written (the other load order)
         env["KQ_MFMA_XF"] = "0"
+    if variant == "teams_x1":          # x written before the weights are issued, at any grid size
+        env["KQ_MFMA_XF"] = "1"
     with U.env_vars(env):
         y = U.gemv_gpu(fmt, U.to_dev(packed), x, N, K, path="mfma")
         y2 = U.gemv_gpu(fmt, U.to_dev(packed), x, N, K, path="mfma")
