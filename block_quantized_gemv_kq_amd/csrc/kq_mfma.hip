@@ -935,8 +935,10 @@ MfmaLdsCfg mfma_lds_cfg(int64_t N, int64_t K, int M, int maxp, bool no_sums) {
   while ((1 << log2mp) < M) ++log2mp;
   const int64_t pieces = mfma_x_pieces(ngroups, log2mp);
   // enough threads to stage x (at most XST_MAX pieces each): more tiles per
-  // workgroup, else more waves per tile
-  while (pieces > (int64_t)XST_MAX * 64 * R * S && 2 * R * S <= 16 && (tiles + 2 * R - 1) / (2 * R) >= 256) R *= 2;
+  // workgroup while at least 128 workgroups remain, else more waves per tile
+  // (one staged copy of x then serves two tiles: q|k|v at M = 16, 384 tiles,
+  // 10.0 us as 384 workgroups of 7 waves against 7.4 us as 192 of 2 x 4)
+  while (pieces > (int64_t)XST_MAX * 64 * R * S && 2 * R * S <= 16 && (tiles + 2 * R - 1) / (2 * R) >= 128) R *= 2;
   while (pieces > (int64_t)XST_MAX * 64 * R * S && R * (S + 1) <= 16 && S < ngroups) {
     ++S;
   }
