@@ -1023,6 +1023,18 @@ MfmaChunkCfg mfma_chunk_cfg(int64_t N, int64_t K, int T, int maxp) {
   while ((1 << log2cg) < ngroups) ++log2cg;
   auto x_bytes = [&](int l2) { return (int64_t)T * (4352 << l2) + 16; };   // x (4 KB per group) + sums (256 B per group)
   while (log2cg > 0 && (x_bytes(log2cg) > 128 * 1024 || (int64_t)T * (256 << log2cg) > (int64_t)XST_MAX * 512)) --log2cg;
+  const int max_log2cg = log2cg;
+  // With at least one tile per compute unit, chunks small enough for two
+  // workgroups per CU (x of a chunk <= 64 KB): at M = 48, q|k|v 23.0 -> 15.7 us,
+  // gate|up 40.9 -> 26.3 us and the Q8_0 lm_head 280 -> 165-180 us with
+  // 4-group chunks instead of 8. With fewer tiles (o, down: 160) the extra
+  // chunk rounds cost more (14.8 -> 18.4 us, 34.8 -> 45.6 us).
+  if (tiles >= 256)
+    while (log2cg > 0 && x_bytes(log2cg) > 64 * 1024) --log2cg;
+  {
+    const char* e = getenv("KQ_MFMA_CHUNK_L2CG");   // sweeps
+    if (e && atoi(e) >= 0 && atoi(e) <= max_log2cg) log2cg = atoi(e);
+  }
   const int CG = 1 << log2cg;
   int P = maxp < CG ? maxp : CG;
   int S = (CG + P - 1) / P;
