@@ -547,6 +547,14 @@ __global__ __launch_bounds__(512) void k_gemv_mfma_chunk(const uint8_t* __restri
                                                          float* __restrict__ y, int N, int K, int M, int R,
                                                          int S, int log2cg) {
   extern __shared__ u32x4 xl4[];
+  // Column groups of 16 T columns along the grid's y (one group when the
+  // grid has no y extent): this workgroup's columns start at col0.
+  {
+    const int col0 = (int)blockIdx.y * 16 * T;
+    x += (int64_t)col0 * K;
+    y += (int64_t)col0 * N;
+    M = min(M - col0, 16 * T);
+  }
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
   const int r = wave / S, s = wave - r * S;
@@ -1057,7 +1065,8 @@ MfmaChunkCfg mfma_chunk_cfg(int64_t N, int64_t K, int T, int maxp) {
 template <int FMT, int P, int T>
 int launch_mfma_chunk_p(const GemvArgs& a, int m0, int mt, const MfmaChunkCfg& c) {
   const int64_t tiles = (a.N + 15) / 16;
-  const dim3 grid((unsigned)((tiles + c.R - 1) / c.R)), block((unsigned)(64 * c.R * c.S));
+  const unsigned cgroups = (unsigned)((mt + 16 * T - 1) / (16 * T));   // column groups of 16 T along y
+  const dim3 grid((unsigned)((tiles + c.R - 1) / c.R), cgroups), block((unsigned)(64 * c.R * c.S));
   hipLaunchKernelGGL((k_gemv_mfma_chunk<FMT, P, T>), grid, block, c.lds, a.stream, a.W, a.x + (int64_t)m0 * a.K,
                      a.y + (int64_t)m0 * a.N, (int)a.N, (int)a.K, mt, c.R, c.S, c.log2cg);
   return (int)hipGetLastError();
@@ -1125,7 +1134,11 @@ constexpr int64_t MFMA_PERS_MIN_TILES = 4096;
 // in LDS (M <= 16), K-chunked staging (any M up to 64 per launch), and per-wave
 // activation loads as the fallback. KQ_MFMA_VARIANT (tests and sweeps) forces
 // one kernel where it applies: "pers", "teams", "teams_sx" (block sums staged
-// in LDS instead of an MFMA against ones per block), "chunk" or "direct".
+// in LDS instead of an MFMA against ones per block), "chunk" or "direct";
+// past 16 columns "chunk_whole" / "chunk_split" force one workgroup per tile
+// for all columns / per tile and 16 columns (measured at M = 48: the split
+// wins below 256 tiles, o 15.1 -> 12.8 us and down 34.8 -> 24.8 us, and
+// loses above, q|k|v 15.6 -> 25.5 us, gate|up 26.2 -> 41.3 us).
 template <int FMT>
 int launch_mfma_fmt(const GemvArgs& a) {
   const char* var = getenv("KQ_MFMA_VARIANT");
@@ -1150,7 +1163,15 @@ int launch_mfma_fmt(const GemvArgs& a) {
     const int mt = a.M - m0 < 64 ? a.M - m0 : 64;
     int err = -1;
     if (!want_direct) {
-      if (mt <= 16) err = launch_mfma_chunk<FMT, 1>(a, m0, mt);
+      // Fewer row tiles than compute units: one workgroup per (tile, 16
+      // columns) instead of one per tile for all columns, so more CUs work
+      // and each stages a third of x at 48 columns; the column groups of a
+      // tile land on the same XCD when the tile count is a multiple of 8
+      // (workgroups go to XCDs round-robin), so its weights are read from
+      // HBM about once.
+      const bool split = mt > 16 && ((a.N + 15) / 16 < 256 || (var && !strcmp(var, "chunk_split"))) &&
+                         !(var && !strcmp(var, "chunk_whole"));
+      if (mt <= 16 || split) err = launch_mfma_chunk<FMT, 1>(a, m0, mt);
       else if (mt <= 32) err = launch_mfma_chunk<FMT, 2>(a, m0, mt);
       else if (mt <= 48) err = launch_mfma_chunk<FMT, 3>(a, m0, mt);
       else err = launch_mfma_chunk<FMT, 4>(a, m0, mt);

@@ -179,7 +179,7 @@ def test_zero_and_constant_weights():
 
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("variant", ("pers", "pers_tpw3", "teams", "teams_sx", "teams_x0", "teams_x1", "chunk",
-                                     "direct"))
+                                     "chunk_whole", "direct"))
 @pytest.mark.parametrize("N,K,M", [(1000, 2560, 8), (37, 96, 5), (300, 4128, 16), (16, 32, 2), (529, 640, 13),
                                    (300, 4128, 40), (77, 9728, 33)])
 def test_mfma_variants_parity(fmt, variant, N, K, M):
@@ -188,7 +188,9 @@ def test_mfma_variants_parity(fmt, variant, N, K, M):
     block sums, K-chunked staging for many columns or long rows, per-wave
     activation loads) on ragged rows, partial groups and odd block counts;
     pers_tpw3 gives each wave three tiles. Past 16 columns only the chunked
-    and per-wave kernels apply."""
+    and per-wave kernels apply; with fewer than 256 row tiles the chunked
+    kernel runs one workgroup per 16 columns (chunk), or one for all columns
+    of a tile (chunk_whole)."""
     packed, fields, x = _case(fmt, N, K, M, 9)
     env = {"KQ_MFMA_VARIANT": variant.split("_tpw")[0]}
     if variant == "pers_tpw3":
