@@ -55,7 +55,10 @@ __global__ __launch_bounds__(256) void k_gemv_valu(const uint8_t* __restrict__ W
   }
 }
 
-constexpr int XREG_CHUNKS = 5;   // 16-byte activation chunks per thread in the register variant
+// 16-byte activation chunks per thread in the register variant: 5, or 10 for
+// two columns (so that two 9728-long columns go through registers rather
+// than LDS DMA).
+template <int MT> constexpr int xreg_chunks() { return MT == 2 ? 10 : 5; }
 
 // ------------------------------------------- VALU path, loads-first + LDS x
 // One row per lane group (G lanes), 64/G rows per wave. Each lane issues the
@@ -96,13 +99,13 @@ __global__ __launch_bounds__(64 * WPG) void k_gemv_lds(const uint8_t* __restrict
   const int kdw = K / 2;
   float* xs = reinterpret_cast<float*>(xl + MT * kdw);
   // XREG: the activations go ahead of the weights in this CU's memory queue,
-  // loaded into registers (at most XREG_CHUNKS 16-byte chunks per thread), so
+  // loaded into registers (at most xreg_chunks 16-byte chunks per thread), so
   // writing them to LDS waits for them alone and the block sums below overlap
   // the weights' latency. Otherwise they are copied by LDS DMA (any K), which
   // the first barrier waits for together with the weights. The two variants
   // are separate kernels: with an LDS DMA anywhere in the kernel the compiler
   // would make the register path's LDS writes wait for every load.
-  constexpr int XCH = XREG_CHUNKS;
+  constexpr int XCH = xreg_chunks<MT>();
   const int n16 = MT * K / 8;   // columns m0 .. m0+MT-1 are contiguous
   u32x4 xr[XCH];
   const u32x4* xsrc = reinterpret_cast<const u32x4*>(x + (int64_t)m0 * K);
@@ -364,7 +367,7 @@ int launch_lds_wpg(const GemvArgs& a, int m0, LdsCfg c, Best* part) {
   const int64_t nwg = (waves + WPG - 1) / WPG;
   const dim3 grid((unsigned)nwg), block(64 * WPG);
   const size_t lds = (size_t)MT * a.K * 2 + (size_t)MT * (a.K / 32) * 8;  // x + block sums
-  const bool xreg = (int64_t)MT * a.K / 8 <= 64 * WPG * XREG_CHUNKS;
+  const bool xreg = (int64_t)MT * a.K / 8 <= 64 * WPG * xreg_chunks<MT>();
   if (MT == 1 && part) {   // the argmax epilogue (one column only)
     if (xreg)
       hipLaunchKernelGGL((k_gemv_lds<FMT, MT, ITERS, true, WPG, MT == 1>), grid, block, lds, a.stream, a.W, a.x, a.y,
