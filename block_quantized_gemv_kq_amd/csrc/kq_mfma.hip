@@ -1165,10 +1165,10 @@ int launch_mfma_fmt(const GemvArgs& a) {
     if (!want_direct) {
       // Fewer row tiles than compute units: one workgroup per (tile, 16
       // columns) instead of one per tile for all columns, so more CUs work
-      // and each stages a third of x at 48 columns; the column groups of a
-      // tile land on the same XCD when the tile count is a multiple of 8
-      // (workgroups go to XCDs round-robin), so its weights are read from
-      // HBM about once.
+      // and each stages a third of x at 48 columns. The column groups of a
+      // tile land on the same XCD when the grid's x extent is a multiple of
+      // 8 (workgroups go to XCDs round-robin), where they can share its L2
+      // for the tile's weights.
       const bool split = mt > 16 && ((a.N + 15) / 16 < 256 || (var && !strcmp(var, "chunk_split"))) &&
                          !(var && !strcmp(var, "chunk_whole"));
       if (mt <= 16 || split) err = launch_mfma_chunk<FMT, 1>(a, m0, mt);
