@@ -1167,8 +1167,9 @@ int launch_mfma_fmt(const GemvArgs& a) {
       // columns) instead of one per tile for all columns, so more CUs work
       // and each stages a third of x at 48 columns. The column groups of a
       // tile land on the same XCD when the grid's x extent is a multiple of
-      // 8 (workgroups go to XCDs round-robin), where they can share its L2
-      // for the tile's weights.
+      // 8 (workgroups go to XCDs round-robin) and share its L2 for the
+      // tile's weights: down at M = 48 fetches the same bytes past L2 in both
+      // layouts (FETCH_SIZE 11.30 MiB per launch).
       const bool split = mt > 16 && ((a.N + 15) / 16 < 256 || (var && !strcmp(var, "chunk_split"))) &&
                          !(var && !strcmp(var, "chunk_whole"));
       if (mt <= 16 || split) err = launch_mfma_chunk<FMT, 1>(a, m0, mt);
