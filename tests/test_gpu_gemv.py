@@ -205,3 +205,18 @@ def test_mfma_variants_parity(fmt, variant, N, K, M):
     yr, ad = R.gemv(fmt, fields, x)
     U.assert_parity(y, yr, ad, f"{fmt} {variant} N={N} K={K} M={M}")
     assert np.array_equal(y, y2), "not deterministic run to run"
+
+
+@pytest.mark.parametrize("fmt", ("q8_0", "q4_0", "affine4"))
+@pytest.mark.parametrize("N,K,M", [(50, 2048, 17), (130, 1024, 64), (4000, 256, 48), (4096, 512, 33)])
+def test_chunk_column_groups(fmt, N, K, M):
+    """Past 16 columns the chunked kernel runs one workgroup per tile and 16
+    columns below 256 row tiles (a grid y of column groups, the last one
+    partial) and one per tile for all columns from 256 tiles on (4096 rows):
+    parity with the oracle either way, and run-to-run determinism."""
+    packed, fields, x = _case(fmt, N, K, M, 11)
+    y = U.gemv_gpu(fmt, U.to_dev(packed), x, N, K, path="mfma")
+    y2 = U.gemv_gpu(fmt, U.to_dev(packed), x, N, K, path="mfma")
+    yr, ad = R.gemv(fmt, fields, x)
+    U.assert_parity(y, yr, ad, f"{fmt} chunk column groups N={N} K={K} M={M}")
+    assert np.array_equal(y, y2), "not deterministic run to run"
