@@ -205,6 +205,3 @@ def dequantize(fmt: str, fields: dict, rows: slice | None = None) -> np.ndarray:
 def rows_of(fields: dict) -> int:
     return fields["q"].shape[0]
 
-
-def slice_rows(fields: dict, rows: slice) -> dict:
-    return {key: val[rows] for key, val in fields.items()}

@@ -51,13 +51,6 @@ def gemv(fmt: str, fields: dict, x16: np.ndarray, rows: slice | None = None):
     return np.concatenate(ys, axis=1), np.concatenate(absd, axis=1)
 
 
-def gemv_rows(fmt: str, fields: dict, x16: np.ndarray, row_ids) -> tuple:
-    """Same as gemv but for an arbitrary list of rows (sampled checks)."""
-    row_ids = np.asarray(row_ids)
-    sub = {key: val[row_ids] for key, val in fields.items()}
-    return gemv(fmt, sub, x16)
-
-
 def tolerance(abs_dot: np.ndarray) -> np.ndarray:
     return REL_TOL * np.asarray(abs_dot) + ABS_TOL
 

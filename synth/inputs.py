@@ -67,20 +67,6 @@ def weights(seed, n: int, k: int) -> np.ndarray:
     return out
 
 
-def weight_rows(seed, n: int, k: int, rows) -> np.ndarray:
-    """Only the given rows of ``weights(seed, n, k)`` (regenerates just the
-    row blocks that hold them)."""
-    rows = np.asarray(rows)
-    out = np.empty((rows.size, k), np.float32)
-    for b in np.unique(rows // ROW_BLOCK):
-        r0 = int(b) * ROW_BLOCK
-        r1 = min(n, r0 + ROW_BLOCK)
-        blk = _row_block(seed, int(b), r1 - r0, k)
-        sel = np.nonzero(rows // ROW_BLOCK == b)[0]
-        out[sel] = blk[rows[sel] - r0]
-    return out
-
-
 def activation_column(seed, k: int) -> np.ndarray:
     """One fp16 activation vector of length k from N(0, 1)."""
     rng = np.random.default_rng(list(seed))

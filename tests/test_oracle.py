@@ -100,6 +100,49 @@ def check_exact_small_gemv(fmt: str, n: int, k: int, m: int, seed: int) -> None:
             assert abs(float(absd[c, r]) - float(absx)) <= 1e-12 * float(absx) + 1e-300
 
 
+def check_acceptance_bound() -> None:
+    """The bar every GPU result is held to, per output: |y - y_ref| <=
+    2e-3 * sum_k |w'[n][k] x[m][k]| + 1e-6. Points worked by hand: at
+    sum|w'x| = 1000 the bound is 2.000001, at 0 it is 1e-6, at 0.5 it is
+    0.001001; differences just inside pass and just outside fail, in both
+    directions."""
+    cases = [  # (sum|w'x|, y_ref, y_gpu, inside?)
+        (1000.0, 0.0, 2.0000009, True), (1000.0, 0.0, 2.0000011, False),
+        (1000.0, 5.0, 5.0 - 2.0000009, True), (1000.0, 5.0, 5.0 - 2.0000011, False),
+        (0.0, 0.0, 0.9e-6, True), (0.0, 0.0, 1.1e-6, False), (0.0, 3.0, 3.0 - 1.1e-6, False),
+        (0.5, 1.0, 1.0 + 0.00100099, True), (0.5, 1.0, 1.0 + 0.00100101, False),
+    ]
+    a = np.array([c[0] for c in cases])
+    ref = np.array([c[1] for c in cases])
+    gpu = np.array([c[2] for c in cases])
+    expect = np.array([c[3] for c in cases])
+    got = R.within_tolerance(gpu, ref, a)
+    assert np.array_equal(got, expect), f"acceptance {got} != {expect}"
+    assert abs(float(R.tolerance(np.array([1000.0]))[0]) - 2.000001) < 1e-12
+    assert abs(float(R.tolerance(np.array([0.0]))[0]) - 1e-6) < 1e-18
+
+
+def check_error_ratio() -> None:
+    """max |y - y_ref| / sum|w'x| on a hand-worked case: differences 0.1,
+    0 and 0.03 over sums 10, 4 and 1 give ratios 0.01, 0 and 0.03."""
+    r = R.error_ratio(np.array([1.0, 2.0, -0.03]), np.array([1.1, 2.0, 0.0]), np.array([10.0, 4.0, 1.0]))
+    assert abs(r - 0.03) < 1e-12, r
+
+
+def check_abs_dot(fmt: str) -> None:
+    """The sum in the bound is of |w'x| term by term, not |sum w'x|: with x
+    alternating +1/-1 it equals sum_k |w'[n][k]| exactly (Fractions of the
+    hand-derived dequant values of the golden blocks)."""
+    rows = [b for b in BLOCKS if b["format"] == fmt]
+    packed = np.stack([b["bytes"] for b in rows])
+    fields = F.decode(fmt, packed, len(rows), 32)
+    x = np.array([[1.0 if k % 2 == 0 else -1.0 for k in range(32)]], np.float16)
+    _, absd = R.gemv(fmt, fields, x)
+    for i, b in enumerate(rows):
+        exact = sum(abs(Fraction(float(v))) for v in b["dequant"])
+        assert Fraction(float(absd[0, i])) == exact, f"{b['name']}: {absd[0, i]} != {float(exact)}"
+
+
 # ------------------------------------------------------------ the pins
 
 @pytest.mark.parametrize("blk", BLOCKS, ids=lambda b: b["name"])
@@ -171,6 +214,30 @@ def test_gemv_matches_textbook_dgemv():
         for c in range(2):
             ref = np.array([math.fsum(Wd[r] * x[c].astype(np.float64)) for r in range(40)])
             np.testing.assert_allclose(y[c], ref, rtol=0, atol=1e-15 * np.abs(Wd).sum(1).max() * 4)
+
+
+def test_acceptance_bound():
+    check_acceptance_bound()
+
+
+def test_error_ratio():
+    check_error_ratio()
+
+
+@pytest.mark.parametrize("fmt", F.FORMATS)
+def test_abs_dot_is_termwise(fmt):
+    check_abs_dot(fmt)
+
+
+def test_packed_bytes_match_block_sizes():
+    """Block sizes as the workloads state them (Q8_0 34, Q4_0 18, affine4 20
+    bytes per 32 weights), and the 1024 x 1024 Q8_0 matrix at 1,114,112 B."""
+    assert F.packed_bytes("q8_0", 1024, 1024) == 1024 * 32 * 34 == 1114112
+    assert F.packed_bytes("q4_0", 3, 64) == 3 * 2 * 18
+    assert F.packed_bytes("affine4", 5, 96) == 5 * 3 * 20
+    W = S.weights((77,), 3, 64)
+    for fmt in F.FORMATS:
+        assert F.encode(fmt, F.quantize(fmt, W)).nbytes == F.packed_bytes(fmt, 3, 64)
 
 
 # ------------------------------------------------------------ invariants

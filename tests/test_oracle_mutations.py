@@ -123,3 +123,44 @@ def test_dropped_block_is_caught(monkeypatch):
         return w
     monkeypatch.setattr(F, "dequantize", bad)
     assert _fails(T.check_exact_small_gemv, "q4_0", 3, 64, 1, 1)
+
+
+def test_loose_relative_tolerance_is_caught(monkeypatch):
+    monkeypatch.setattr(R, "REL_TOL", 2e-2)
+    assert _fails(T.check_acceptance_bound)
+
+
+def test_loose_absolute_tolerance_is_caught(monkeypatch):
+    monkeypatch.setattr(R, "ABS_TOL", 1e-3)
+    assert _fails(T.check_acceptance_bound)
+
+
+def test_dropped_relative_term_is_caught(monkeypatch):
+    monkeypatch.setattr(R, "tolerance", lambda abs_dot: np.zeros_like(np.asarray(abs_dot, np.float64)) + R.ABS_TOL)
+    assert _fails(T.check_acceptance_bound)
+
+
+def test_strict_comparison_is_caught(monkeypatch):
+    # a bound applied to twice the difference (e.g. a relative error taken
+    # against the midpoint of y and y_ref) rejects results the bar accepts
+    orig = R.tolerance
+    monkeypatch.setattr(R, "tolerance", lambda abs_dot: orig(abs_dot) / 2)
+    assert _fails(T.check_acceptance_bound)
+
+
+def test_error_ratio_against_reference_magnitude_is_caught(monkeypatch):
+    def bad(y_gpu, y_ref, abs_dot):
+        d = np.abs(np.asarray(y_gpu, np.float64) - y_ref)
+        return float(np.max(d / np.maximum(np.abs(y_ref), 1e-300)))
+    monkeypatch.setattr(R, "error_ratio", bad)
+    assert _fails(T.check_error_ratio)
+
+
+def test_abs_of_sum_instead_of_sum_of_abs_is_caught(monkeypatch):
+    orig = R.gemv
+
+    def bad(fmt, fields, x16, rows=None):
+        y, _ = orig(fmt, fields, x16, rows)
+        return y, np.abs(y)
+    monkeypatch.setattr(R, "gemv", bad)
+    assert _fails(T.check_abs_dot, "affine4")
