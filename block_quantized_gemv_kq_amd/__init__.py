@@ -43,6 +43,7 @@ SIGNATURES = {
     "kq_argmax_workspace_bytes": (_I64, [_I64, _I32]),
     "kq_argmax": (_I32, [_P, _I64, _I32, _P, _P, _I64, _P]),
     "kq_f32_to_f16": (_I32, [_P, _P, _I64]),
+    "kq_set_tuning": (_I32, [ctypes.c_char_p, ctypes.c_char_p]),
     "kq_stack_plan_bytes": (_I64, [_P, _I32]),
     "kq_stack_plan": (_I32, [_P, _I32, _P, _I64, _P, _P]),
     "kq_stack_run": (_I32, [_P, _P, _P]),
@@ -178,6 +179,12 @@ def kq_f32_to_f16(a: np.ndarray) -> np.ndarray:
     out = np.empty(a.shape, np.uint16)
     _check(lib().kq_f32_to_f16(a.ctypes.data, out.ctypes.data, a.size), "kq_f32_to_f16")
     return out
+
+
+def kq_set_tuning(name: str | None, value: str | None) -> None:
+    """Tests and sweeps: force a kernel or launch configuration (see kq.h)."""
+    _check(lib().kq_set_tuning(None if name is None else name.encode(),
+                               None if value is None else str(value).encode()), "kq_set_tuning")
 
 
 # ------------------------------------------------------------------ GPU calls

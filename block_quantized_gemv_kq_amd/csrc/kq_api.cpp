@@ -5,6 +5,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
 #include <vector>
 
 #include "kq_internal.h"
@@ -42,12 +43,58 @@ int check_n(int64_t N, const char* what) {
   return KQ_OK;
 }
 
+// Overrides stored as value + 1, so the zero-initialised table means "none set".
+std::atomic<int> g_tune[kq::TUNE_COUNT] = {};
+
+struct TuneName {
+  const char* name;
+  kq::TuneKey key;
+};
+const TuneName kTuneNames[] = {
+    {"force_path", kq::TUNE_FORCE_PATH},         {"valu_g", kq::TUNE_VALU_G},
+    {"valu_r", kq::TUNE_VALU_R},                 {"lds_wpg", kq::TUNE_LDS_WPG},
+    {"mfma_variant", kq::TUNE_MFMA_VARIANT},     {"mfma_s", kq::TUNE_MFMA_S},
+    {"mfma_r", kq::TUNE_MFMA_R},                 {"mfma_waves", kq::TUNE_MFMA_WAVES},
+    {"mfma_xf", kq::TUNE_MFMA_XF},               {"mfma_pers_tpw", kq::TUNE_MFMA_PERS_TPW},
+    {"mfma_chunk_l2cg", kq::TUNE_MFMA_CHUNK_L2CG}, {"moe_unfused", kq::TUNE_MOE_UNFUSED},
+};
+
+// Parse a tuning value: force_path and mfma_variant take names, the others integers.
+bool parse_tune(kq::TuneKey key, const char* v, int* out) {
+  if (key == kq::TUNE_FORCE_PATH) {
+    if (strlen(v) != 1 || !strchr("gvlm", v[0])) return false;
+    *out = v[0];
+    return true;
+  }
+  if (key == kq::TUNE_MFMA_VARIANT) {
+    static const char* names[] = {"pers", "teams", "teams_sx", "chunk", "chunk_whole", "chunk_split", "direct"};
+    for (int i = 0; i < 7; ++i)
+      if (!strcmp(v, names[i])) {
+        *out = kq::MV_PERS + i;
+        return true;
+      }
+    return false;
+  }
+  char* end = nullptr;
+  const long n = strtol(v, &end, 10);
+  if (end == v || *end != '\0' || n < 0 || n > 1 << 20) return false;
+  *out = (int)n;
+  return true;
+}
+
 int hip_status(int err, const char* where) {
   if (err == 0) return ok();
   return fail(KQ_ERR_HIP, "%s: HIP error %d (%s)", where, err, kq::hip_error_string(err));
 }
 
 }  // namespace
+
+namespace kq {
+int tune(TuneKey k) {
+  const int v = g_tune[k].load(std::memory_order_relaxed);
+  return v == 0 ? TUNE_UNSET : v - 1;
+}
+}  // namespace kq
 
 extern "C" {
 
@@ -67,6 +114,25 @@ const char* kq_status_string(int status) {
 }
 
 const char* kq_last_error(void) { return g_err; }
+
+int kq_set_tuning(const char* name, const char* value) {
+  if (!name) {
+    for (auto& t : g_tune) t.store(0, std::memory_order_relaxed);
+    return ok();
+  }
+  for (const TuneName& t : kTuneNames) {
+    if (strcmp(t.name, name)) continue;
+    if (!value || !value[0]) {
+      g_tune[t.key].store(0, std::memory_order_relaxed);
+      return ok();
+    }
+    int v;
+    if (!parse_tune(t.key, value, &v)) return fail(KQ_ERR_ARG, "kq_set_tuning: bad value '%s' for %s", value, name);
+    g_tune[t.key].store(v + 1, std::memory_order_relaxed);
+    return ok();
+  }
+  return fail(KQ_ERR_ARG, "kq_set_tuning: unknown name '%s'", name);
+}
 
 int64_t kq_block_bytes(int fmt) {
   if (!valid_fmt(fmt)) return fail(KQ_ERR_FORMAT, "unknown format %d", fmt);
@@ -177,7 +243,7 @@ int kq_moe_gemv(int fmt, const void* W_experts, const uint16_t* x, const int32_t
   float* slots = route_w ? static_cast<float*>(workspace) : y;
   kq::MoeArgs a{fmt, static_cast<const uint8_t*>(W_experts), x, route_ids, slots, N, K, M, top_k,
                 n_experts, x_per_slot, s};
-  if (route_w && kq::moe_down_sum_applies(a) && !getenv("KQ_MOE_UNFUSED"))
+  if (route_w && kq::moe_down_sum_applies(a) && kq::tune(kq::TUNE_MOE_UNFUSED) != 1)
     return hip_status(kq::launch_moe_down_sum(a, route_w, y), "kq_moe_gemv");
   int err = kq::launch_moe_gemv(a);
   if (!err && route_w) err = kq::launch_weighted_slot_sum(slots, route_w, y, N, M, top_k, s);
@@ -221,7 +287,7 @@ int kq_moe_ffn(int fmt, const void* W_gate, const void* W_up, const void* W_down
   if (err) return hip_status(err, "kq_moe_ffn");
   kq::MoeArgs d{fmt, static_cast<const uint8_t*>(W_down), h, route_ids, slots, hidden, inter, M,
                 top_k, n_experts, 1, s};
-  if (kq::moe_down_sum_applies(d) && !getenv("KQ_MOE_UNFUSED"))
+  if (kq::moe_down_sum_applies(d) && kq::tune(kq::TUNE_MOE_UNFUSED) != 1)
     return hip_status(kq::launch_moe_down_sum(d, route_w, y), "kq_moe_ffn");
   err = kq::launch_moe_gemv(d);
   if (!err) err = kq::launch_weighted_slot_sum(slots, route_w, y, hidden, M, top_k, s);

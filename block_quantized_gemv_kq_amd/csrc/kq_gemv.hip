@@ -248,15 +248,15 @@ struct ValuCfg {
 // Lanes per row (G) and rows per lane (R) for the VALU path. G is a power of
 // two near units/4, so each lane walks a few units of a row; R grows while
 // the grid still holds >= 2048 waves (8 per CU) to keep loads in flight.
-// KQ_VALU_G / KQ_VALU_R override the choice (tuning sweeps and tests).
-int env_int(const char* name) {
-  const char* v = getenv(name);
-  return v ? atoi(v) : 0;
+// The valu_g / valu_r tuning overrides replace the choice (sweeps and tests).
+int tune_int(TuneKey k) {
+  const int v = tune(k);
+  return v == TUNE_UNSET ? 0 : v;
 }
 
 ValuCfg valu_cfg(int64_t N, int units) {
-  const int env_g = env_int("KQ_VALU_G");
-  const int env_r = env_int("KQ_VALU_R");
+  const int env_g = tune_int(TUNE_VALU_G);
+  const int env_r = tune_int(TUNE_VALU_R);
   int G = 1 << ilog2(units / 4 > 0 ? units / 4 : 1);
   G = G < 4 ? 4 : (G > 64 ? 64 : G);
   if (env_g == 1 || env_g == 2 || env_g == 4 || env_g == 8 || env_g == 16 || env_g == 32 || env_g == 64) G = env_g;
@@ -349,13 +349,13 @@ LdsCfg lds_cfg(int64_t N, int units, int unit_bytes) {
     }
   }
   while (G < 64 && N * G / 64 < 2048 && G < units) G <<= 1;
-  const int env_g = env_int("KQ_VALU_G");
+  const int env_g = tune_int(TUNE_VALU_G);
   if (env_g == 1 || env_g == 2 || env_g == 4 || env_g == 8 || env_g == 16 || env_g == 32 || env_g == 64) G = env_g;
   int iters = (units + G - 1) / G;
   if (iters > MAX_ITERS) iters = MAX_ITERS;
   const int passes = (units + G * iters - 1) / (G * iters);
   int wpg = 4;
-  const int env_w = env_int("KQ_LDS_WPG");
+  const int env_w = tune_int(TUNE_LDS_WPG);
   if (env_w == 4 || env_w == 8 || env_w == 16) wpg = env_w;
   return {ilog2(G), iters, passes, wpg};
 }
@@ -436,12 +436,12 @@ int launch_generic(const GemvArgs& a) {
 template <int FMT>
 int dispatch(const GemvArgs& a) {
   if (a.K % (32 * Fmt<FMT>::UB) != 0) return a.M >= MFMA_MIN_M_UNALIGNED ? launch_gemv_mfma(a) : launch_generic<FMT>(a);
-  const char* force = getenv("KQ_FORCE_PATH");  // tests: run a given path at any shape
-  if (force && force[0] == 'g') return launch_generic<FMT>(a);
+  const int force = tune_int(TUNE_FORCE_PATH);  // tests: run a given path at any shape
+  if (force == 'g') return launch_generic<FMT>(a);
   const bool lds_fits = (int64_t)(a.M < LDS_MAX_MT ? a.M : LDS_MAX_MT) * (a.K * 2 + a.K / 4) <= LDS_MAX_BYTES;
-  if (force && force[0] == 'v') return launch_valu<FMT>(a);     // register-x VALU kernel
-  if (force && force[0] == 'l' && lds_fits) return launch_lds<FMT>(a);
-  if (force && force[0] == 'm') return launch_gemv_mfma(a);
+  if (force == 'v') return launch_valu<FMT>(a);     // register-x VALU kernel
+  if (force == 'l' && lds_fits) return launch_lds<FMT>(a);
+  if (force == 'm') return launch_gemv_mfma(a);
   if (a.M >= MFMA_MIN_M) return launch_gemv_mfma(a);
   if (a.M <= LDS_MAX_MT && lds_fits) return launch_lds<FMT>(a);
   return launch_valu<FMT>(a);
@@ -501,7 +501,7 @@ template <int FMT>
 bool argmax_fusable(const GemvArgs& a, LdsCfg* cfg) {
   if (a.K % (32 * Fmt<FMT>::UB) != 0 || a.M != 1) return false;
   if ((int64_t)a.M * (a.K * 2 + a.K / 4) > LDS_MAX_BYTES) return false;
-  if (getenv("KQ_FORCE_PATH")) return false;
+  if (tune(TUNE_FORCE_PATH) != TUNE_UNSET) return false;
   const int units = (int)(a.K / (32 * Fmt<FMT>::UB));
   *cfg = lds_cfg(a.N, units, Fmt<FMT>::BB * Fmt<FMT>::UB);
   return true;

@@ -10,6 +10,30 @@ typedef struct ihipStream_t* hipStream_t;
 
 namespace kq {
 
+// ---- tuning overrides (kq_set_tuning). Every default is the measured
+// choice; an override forces another kernel or configuration so that tests
+// can reach each path at small shapes and sweeps can compare them. The
+// environment is never read.
+enum TuneKey {
+  TUNE_FORCE_PATH,       // 'g' generic, 'v' register-x VALU, 'l' LDS VALU, 'm' matrix cores
+  TUNE_VALU_G,           // lanes per row of the VALU kernels
+  TUNE_VALU_R,           // rows per lane of the register-x kernel
+  TUNE_LDS_WPG,          // waves per workgroup of the one-column LDS kernel
+  TUNE_MFMA_VARIANT,     // MfmaVariant below
+  TUNE_MFMA_S,           // waves per tile (split-K teams kernel)
+  TUNE_MFMA_R,           // tiles per workgroup (split-K teams kernel)
+  TUNE_MFMA_WAVES,       // wave count below which the teams kernel doubles S
+  TUNE_MFMA_XF,          // teams kernel issue order: 1 x first, 0 weights first
+  TUNE_MFMA_PERS_TPW,    // persistent kernel: tiles per wave
+  TUNE_MFMA_CHUNK_L2CG,  // chunked kernel: log2 of groups per chunk
+  TUNE_MOE_UNFUSED,      // 1: one-token MoE down + weighted sum as two kernels
+  TUNE_COUNT
+};
+enum MfmaVariant { MV_PERS = 1, MV_TEAMS, MV_TEAMS_SX, MV_CHUNK, MV_CHUNK_WHOLE, MV_CHUNK_SPLIT, MV_DIRECT };
+constexpr int TUNE_UNSET = -0x7fffffff;
+// The override of `k`, or TUNE_UNSET.
+int tune(TuneKey k);
+
 // ---- host packer (kq_pack.cpp)
 int64_t block_bytes(int fmt);
 int pack(int fmt, const float* W, int64_t N, int64_t K, void* out, int n_threads);

@@ -843,8 +843,8 @@ struct MfmaCfg {
 
 // Waves per 16-row tile: at least enough to cover the row with P groups per
 // wave, then doubled (up to smax) while the grid has fewer than 2048 waves, so
-// that short or few rows still keep enough loads in flight. KQ_MFMA_S
-// overrides it (tuning sweeps and tests).
+// that short or few rows still keep enough loads in flight. The mfma_s
+// tuning override replaces it (sweeps and tests).
 MfmaCfg mfma_cfg(int64_t N, int64_t K, int P, int smax) {
   const int ngroups = (int)((K / 32 + 3) / 4);
   const int64_t tiles = (N + 15) / 16;
@@ -852,9 +852,8 @@ MfmaCfg mfma_cfg(int64_t N, int64_t K, int P, int smax) {
   if (S > smax) S = smax;
   while (S < smax && S < ngroups && tiles * S < 2048) S *= 2;
   if (S > smax) S = smax;
-  const char* e = getenv("KQ_MFMA_S");
-  if (e) {
-    const int v = atoi(e);
+  {
+    const int v = tune(TUNE_MFMA_S);
     if (v >= 1 && v <= smax) S = v;
   }
   if (S > ngroups) S = ngroups;
@@ -917,15 +916,11 @@ MfmaLdsCfg mfma_lds_cfg(int64_t N, int64_t K, int M, int maxp, bool no_sums) {
   int S = (ngroups + maxp - 1) / maxp;
   if (S > 16) return c;
   int min_waves = 1024;
-  {
-    const char* ew = getenv("KQ_MFMA_WAVES");   // sweeps
-    if (ew && atoi(ew) > 0) min_waves = atoi(ew);
-  }
+  if (tune(TUNE_MFMA_WAVES) > 0) min_waves = tune(TUNE_MFMA_WAVES);   // sweeps
   while (S < 16 && S < ngroups && tiles * S < min_waves) S *= 2;
   if (S > 16) S = 16;
-  const char* e = getenv("KQ_MFMA_S");
-  if (e) {
-    const int v = atoi(e);
+  {
+    const int v = tune(TUNE_MFMA_S);
     if (v >= 1 && v <= 16) S = v;
   }
   if (S > ngroups) S = ngroups;
@@ -934,9 +929,8 @@ MfmaLdsCfg mfma_lds_cfg(int64_t N, int64_t K, int M, int maxp, bool no_sums) {
   S = (ngroups + P1 - 1) / P1;
   int R = 1;
   while (2 * R * S <= 8 && (tiles + 2 * R - 1) / (2 * R) >= 1024) R *= 2;
-  const char* er = getenv("KQ_MFMA_R");
-  if (er) {
-    const int v = atoi(er);
+  {
+    const int v = tune(TUNE_MFMA_R);
     if (v >= 1 && v * S <= 16) R = v;
   }
   int log2mp = 0;
@@ -974,9 +968,9 @@ int launch_mfma_lds_p(const GemvArgs& a, int m0, int mt, const MfmaLdsCfg& c) {
   // (o at M = 8 6.52 against 7.23 us) and on gate|up at M = 2..4 and 12..16
   // (M = 16 19.13 against 21.13 us), but gate|up (1216 tiles) at M = 5..8
   // takes 0.5-1.1 us longer that way (M = 8 14.1-14.3 against 13.0-13.8 us).
-  // KQ_MFMA_XF=0 / 1 forces one order.
-  const char* e = getenv("KQ_MFMA_XF");
-  const bool xf = e ? atoi(e) != 0 : !(c.log2mp == 3 && tiles >= 1024);
+  // The mfma_xf tuning override (0 / 1) forces one order.
+  const int exf = tune(TUNE_MFMA_XF);
+  const bool xf = exf != TUNE_UNSET ? exf != 0 : !(c.log2mp == 3 && tiles >= 1024);
   if (xf)
     hipLaunchKernelGGL((k_gemv_mfma_lds<FMT, P, SX, true>), grid, block, c.lds, a.stream, a.W, a.x + (int64_t)m0 * a.K,
                        a.y + (int64_t)m0 * a.N, (int)a.N, (int)a.K, mt, c.R, c.S, c.log2mp);
@@ -1040,8 +1034,8 @@ MfmaChunkCfg mfma_chunk_cfg(int64_t N, int64_t K, int T, int maxp) {
   if (tiles >= 256)
     while (log2cg > 0 && x_bytes(log2cg) > 64 * 1024) --log2cg;
   {
-    const char* e = getenv("KQ_MFMA_CHUNK_L2CG");   // sweeps
-    if (e && atoi(e) >= 0 && atoi(e) <= max_log2cg) log2cg = atoi(e);
+    const int v = tune(TUNE_MFMA_CHUNK_L2CG);   // sweeps
+    if (v >= 0 && v <= max_log2cg) log2cg = v;
   }
   const int CG = 1 << log2cg;
   int P = maxp < CG ? maxp : CG;
@@ -1113,8 +1107,10 @@ int launch_mfma_pers_p(const GemvArgs& a, int log2mp, size_t lds) {
   const int64_t max_waves = (int64_t)cus * per_cu * 8;
   int64_t tpw = (tiles + max_waves - 1) / max_waves;
   if (tpw > MFMA_PERS_TPW) tpw = MFMA_PERS_TPW;   // more workgroups than fit at once
-  const char* et = getenv("KQ_MFMA_PERS_TPW");     // tests: several tiles per wave at any size
-  if (et && atoi(et) >= 1 && atoi(et) <= MFMA_PERS_TPW) tpw = atoi(et);
+  {
+    const int v = tune(TUNE_MFMA_PERS_TPW);     // tests: several tiles per wave at any size
+    if (v >= 1 && v <= MFMA_PERS_TPW) tpw = v;
+  }
   const int64_t waves = (tiles + tpw - 1) / tpw;
   const dim3 grid((unsigned)((waves + 7) / 8)), block(512);
   hipLaunchKernelGGL((k_gemv_mfma_pers<FMT, P, SX>), grid, block, lds, a.stream, a.W, a.x, a.y, (int)a.N, (int)a.K,
@@ -1132,7 +1128,7 @@ constexpr int64_t MFMA_PERS_MIN_TILES = 4096;
 
 // Order: persistent waves (many tiles, M <= 16), split-K teams with all of x
 // in LDS (M <= 16), K-chunked staging (any M up to 64 per launch), and per-wave
-// activation loads as the fallback. KQ_MFMA_VARIANT (tests and sweeps) forces
+// activation loads as the fallback. The mfma_variant tuning override (tests and sweeps) forces
 // one kernel where it applies: "pers", "teams", "teams_sx" (block sums staged
 // in LDS instead of an MFMA against ones per block), "chunk" or "direct";
 // past 16 columns "chunk_whole" / "chunk_split" force one workgroup per tile
@@ -1141,11 +1137,11 @@ constexpr int64_t MFMA_PERS_MIN_TILES = 4096;
 // loses above, q|k|v 15.6 -> 25.5 us, gate|up 26.2 -> 41.3 us).
 template <int FMT>
 int launch_mfma_fmt(const GemvArgs& a) {
-  const char* var = getenv("KQ_MFMA_VARIANT");
-  const bool want_direct = var && !strcmp(var, "direct");
-  const bool want_pers = var && !strcmp(var, "pers");
-  const bool want_teams = var && !strncmp(var, "teams", 5);
-  const bool want_chunk = var && !strcmp(var, "chunk");
+  const int var = tune(TUNE_MFMA_VARIANT);
+  const bool want_direct = var == MV_DIRECT;
+  const bool want_pers = var == MV_PERS;
+  const bool want_teams = var == MV_TEAMS || var == MV_TEAMS_SX;
+  const bool want_chunk = var == MV_CHUNK;
   if (a.M <= 16 && !want_direct) {
     const int64_t tiles = (a.N + 15) / 16;
     const int ngroups = (int)((a.K / 32 + 3) / 4);
@@ -1156,7 +1152,7 @@ int launch_mfma_fmt(const GemvArgs& a) {
     if ((tiles >= MFMA_PERS_MIN_TILES || want_pers) && !want_teams && !want_chunk && lds <= MFMA_LDS_MAX_BYTES &&
         pieces <= (int64_t)XST_MAX * 512)
       return launch_mfma_pers_p<FMT, MfmaPersP<FMT>::v, true>(a, log2mp, (size_t)lds);
-    const MfmaLdsCfg c = mfma_lds_cfg(a.N, a.K, (int)a.M, MfmaLdsMaxP<FMT>::v, !(var && !strcmp(var, "teams_sx")));
+    const MfmaLdsCfg c = mfma_lds_cfg(a.N, a.K, (int)a.M, MfmaLdsMaxP<FMT>::v, var != MV_TEAMS_SX);
     if (c.ok && !want_chunk) return launch_mfma_lds<FMT>(a, 0, (int)a.M, c);
   }
   for (int m0 = 0; m0 < a.M; m0 += 64) {
@@ -1170,8 +1166,8 @@ int launch_mfma_fmt(const GemvArgs& a) {
       // 8 (workgroups go to XCDs round-robin) and share its L2 for the
       // tile's weights: down at M = 48 fetches the same bytes past L2 in both
       // layouts (FETCH_SIZE 11.30 MiB per launch).
-      const bool split = mt > 16 && ((a.N + 15) / 16 < 256 || (var && !strcmp(var, "chunk_split"))) &&
-                         !(var && !strcmp(var, "chunk_whole"));
+      const bool split = mt > 16 && ((a.N + 15) / 16 < 256 || var == MV_CHUNK_SPLIT) &&
+                         var != MV_CHUNK_WHOLE;
       if (mt <= 16 || split) err = launch_mfma_chunk<FMT, 1>(a, m0, mt);
       else if (mt <= 32) err = launch_mfma_chunk<FMT, 2>(a, m0, mt);
       else if (mt <= 48) err = launch_mfma_chunk<FMT, 3>(a, m0, mt);

@@ -89,7 +89,12 @@ int64_t kq_block_bytes(int fmt);
 int64_t kq_packed_bytes(int fmt, int64_t N, int64_t K);
 
 /* kq_pack — quantize a row-major fp32 matrix W[N][K] (host) into packed blocks
- * written to `out` (host, kq_packed_bytes(fmt,N,K) bytes).
+ * written to `out` (host, kq_packed_bytes(fmt,N,K) bytes). The formats are
+ * those the pages name: Q8_0 and Q4_0 among the GGUF weight formats (Kinetic
+ * docs, "Supported models"; its quantize command writes them), affine4 gs32 as
+ * the scale-and-bias 4-bit scheme beside scale-only Q4_0 (Kipp README, "How
+ * fast", footnote to the 4-bit row). The pages print no block layout or
+ * quantizer formula; the steps below are the reading this library takes.
  * Per block of 32 consecutive weights w_j of one row (all arithmetic IEEE fp32
  * with round-to-nearest-even; fp16() rounds to nearest even, keeping
  * subnormals; round() is round-half-away-from-zero; q uses the STORED fp16
@@ -106,12 +111,19 @@ int64_t kq_packed_bytes(int fmt, int64_t N, int64_t K);
  * (<= 0: one per hardware thread, capped at 64). */
 int kq_pack(int fmt, const float* W, int64_t N, int64_t K, void* out, int n_threads);
 
-/* kq_unpack — dequantize packed blocks (host) to fp32 W_out[N][K] (host):
+/* kq_unpack — dequantize packed blocks (host) to fp32 W_out[N][K] (host), the
+ * inverse view of kq_pack's formats (Kinetic docs, "Supported models"; Kipp
+ * README, "How fast", footnote to the 4-bit row):
  * w' as above, computed in fp32 (exact for Q8_0 and Q4_0; affine4 is
  * s*q + b rounded once, exact unless s and b differ by more than 2^13 in scale). */
 int kq_unpack(int fmt, const void* packed, int64_t N, int64_t K, float* W_out);
 
-/* kq_gemv — y[m][n] = sum_k w'[n][k] * x[m][k] for m < M, n < N.
+/* kq_gemv — y[m][n] = sum_k w'[n][k] * x[m][k] for m < M, n < N: the decode
+ * step's weight pass (Kinetic docs, "What makes it fast": a token reads every
+ * weight once; several guessed tokens, or up to four requests, share one pass
+ * over the weights, so M columns ride on one read of W; Kapitsa README, "How it
+ * works": a verify pass checks 8 rows, and "What's new": three requests share
+ * one verify pass, M = 48 here).
  *   W: device, packed N x K matrix (kq_pack layout), 4-byte aligned.
  *   x: device, fp16 bits [M][K] (column m contiguous), 16-byte aligned.
  *   y: device, fp32 [M][N], 4-byte aligned; overwritten, never accumulated.
@@ -136,7 +148,10 @@ int kq_gemv_invariant(int fmt, const void* W, const uint16_t* x, float* y,
 /* Workspace bytes kq_moe_gemv needs (0 when route_w is NULL). */
 int64_t kq_moe_gemv_workspace_bytes(int64_t N, int M, int top_k, int weighted);
 
-/* kq_moe_gemv — routed-expert GEMV for M decode tokens with top_k slots each.
+/* kq_moe_gemv — routed-expert GEMV for M decode tokens with top_k slots each:
+ * only the experts a token is routed to are read (kinfer page, "Models bigger
+ * than the machine": a few experts of many per token; Kinetic docs, "What makes
+ * it fast": a mixture of experts keeps only the experts in use busy).
  *   W_experts: device, n_experts packed N x K matrices back to back (expert e
  *              starts at e * kq_packed_bytes(fmt, N, K)), 4-byte aligned.
  *   x: device fp16 bits; x_per_slot == 0: [M][K] (every slot of token m reads
@@ -161,7 +176,10 @@ int kq_moe_gemv(int fmt, const void* W_experts, const uint16_t* x,
 /* Workspace bytes kq_moe_ffn needs. */
 int64_t kq_moe_ffn_workspace_bytes(int64_t hidden, int64_t inter, int M, int top_k);
 
-/* kq_moe_ffn — the routed-expert FFN of M decode tokens:
+/* kq_moe_ffn — the routed-expert FFN of M decode tokens (kinfer page, "Models
+ * bigger than the machine"; Kinetic docs, "What makes it fast": only the
+ * experts in use are read). The pages do not name the operation between the
+ * gate/up and down projections; the gated SiLU below is the reading taken:
  *   for token m, slot j, expert e = route_ids[m][j]:
  *     g = Gate_e x_m, u = Up_e x_m            (inter outputs each)
  *     h = fp16(silu(g) * u), silu(z) = z / (1 + e^-z) in fp32
@@ -183,7 +201,9 @@ int kq_moe_ffn(int fmt, const void* W_gate, const void* W_up, const void* W_down
 /* Workspace bytes kq_argmax needs. */
 int64_t kq_argmax_workspace_bytes(int64_t N, int M);
 
-/* kq_argmax — for each column m < M of y (device fp32 [M][N]), the index of
+/* kq_argmax — (Kinetic docs, "What makes it fast": choosing the next token
+ * reads an output layer of up to a quarter of a million rows, and no speed-up
+ * changes the answer) for each column m < M of y (device fp32 [M][N]), the index of
  * its largest value; the lowest index wins ties; NaN never wins (all-NaN
  * columns give 0). Written to out (device int32 [M]). This is the greedy
  * next-token choice over a vocabulary-sized output layer.
@@ -282,6 +302,21 @@ int kq_stack_run(const void* plan, const kq_stack_info* info, void* stream);
 /* kq_stack_status — synchronise `stream`, then read the plan's error word
  * into *error (0: every wait completed). */
 int kq_stack_status(const void* plan, const kq_stack_info* info, int* error, void* stream);
+
+/* kq_set_tuning — tests and tuning sweeps only: force a kernel or a launch
+ * configuration that the library would not choose by itself, so that every
+ * path can be reached at small shapes. Results change by at most the
+ * floating-point summation order (every path meets the kq_gemv tolerance).
+ * Process-wide; the environment is never read. name NULL clears every
+ * override; value NULL or "" clears one. Names and values:
+ *   force_path       "g" generic, "v" register-x VALU, "l" LDS VALU, "m" matrix cores
+ *   mfma_variant     "pers", "teams", "teams_sx", "chunk", "chunk_whole",
+ *                    "chunk_split", "direct"
+ *   valu_g, valu_r, lds_wpg, mfma_s, mfma_r, mfma_waves, mfma_xf,
+ *   mfma_pers_tpw, mfma_chunk_l2cg, moe_unfused   (decimal integers)
+ * Errors: KQ_ERR_ARG (unknown name or malformed value). Not synchronised
+ * with calls running on other threads. */
+int kq_set_tuning(const char* name, const char* value);
 
 /* Test hook: convert n fp32 values (host) to fp16 bits (host) with the
  * packer's own round-to-nearest-even conversion. */

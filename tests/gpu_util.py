@@ -1,7 +1,6 @@
 """Helpers for the GPU parity tests: upload inputs, call the library through
 its C ABI, and compare with the oracle."""
 import contextlib
-import os
 
 import numpy as np
 
@@ -43,19 +42,15 @@ def quantize_both(fmt, W):
 
 
 @contextlib.contextmanager
-def env_vars(values: dict):
-    """Set environment variables (read by the library at each launch) for the
-    duration of a block."""
-    old = {k: os.environ.get(k) for k in values}
-    os.environ.update(values)
+def tuning(values: dict):
+    """Force kernels or configurations (kq_set_tuning) for the duration of a
+    block; every override is cleared afterwards."""
     try:
+        for k, v in values.items():
+            kq.kq_set_tuning(k, v)
         yield
     finally:
-        for k, v in old.items():
-            if v is None:
-                os.environ.pop(k, None)
-            else:
-                os.environ[k] = v
+        kq.kq_set_tuning(None, None)
 
 
 def gemv_gpu(fmt, packed_dev, x16: np.ndarray, N: int, K: int, path: str | None = None) -> np.ndarray:
@@ -64,17 +59,8 @@ def gemv_gpu(fmt, packed_dev, x16: np.ndarray, N: int, K: int, path: str | None 
     xd = to_dev(x16)
     y = empty_dev((M, N))
     y.fill_(float("nan"))
-    old = os.environ.get("KQ_FORCE_PATH")
-    try:
-        if path:
-            os.environ["KQ_FORCE_PATH"] = path
+    with tuning({"force_path": path} if path else {}):
         kq.kq_gemv(fmt, packed_dev, xd, y, N, K, M)
-    finally:
-        if path:
-            if old is None:
-                del os.environ["KQ_FORCE_PATH"]
-            else:
-                os.environ["KQ_FORCE_PATH"] = old
     return to_host(y)
 
 

@@ -252,3 +252,26 @@ def test_stack_run_checks():
     L = kq.lib()
     info = kq.kq_stack_info()
     assert L.kq_stack_run(0x100000, ctypes.addressof(info), 0) == kq.KQ_ERR_ARG   # info not filled
+
+
+def test_set_tuning_validates_and_clears():
+    L = kq.lib()
+    assert L.kq_set_tuning(b"no_such_knob", b"1") == kq.KQ_ERR_ARG
+    assert L.kq_set_tuning(b"force_path", b"x") == kq.KQ_ERR_ARG
+    assert L.kq_set_tuning(b"mfma_variant", b"fast") == kq.KQ_ERR_ARG
+    assert L.kq_set_tuning(b"mfma_s", b"3q") == kq.KQ_ERR_ARG
+    assert L.kq_set_tuning(b"mfma_s", b"-1") == kq.KQ_ERR_ARG
+    for name, value in [(b"force_path", b"m"), (b"mfma_variant", b"chunk_split"), (b"mfma_xf", b"0"),
+                        (b"moe_unfused", b"1")]:
+        assert L.kq_set_tuning(name, value) == kq.KQ_OK
+        assert L.kq_set_tuning(name, None) == kq.KQ_OK
+    assert L.kq_set_tuning(b"valu_g", b"16") == kq.KQ_OK
+    assert L.kq_set_tuning(None, None) == kq.KQ_OK
+
+
+def test_environment_does_not_steer_the_library():
+    """The library never reads the environment: no getenv in its sources."""
+    csrc = os.path.join(ROOT, "block_quantized_gemv_kq_amd", "csrc")
+    for name in os.listdir(csrc):
+        with open(os.path.join(csrc, name)) as f:
+            assert "getenv" not in f.read(), name

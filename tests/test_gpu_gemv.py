@@ -192,14 +192,14 @@ def test_mfma_variants_parity(fmt, variant, N, K, M):
     kernel runs one workgroup per 16 columns (chunk), or one for all columns
     of a tile (chunk_whole)."""
     packed, fields, x = _case(fmt, N, K, M, 9)
-    env = {"KQ_MFMA_VARIANT": variant.split("_tpw")[0]}
+    env = {"mfma_variant": variant.split("_tpw")[0]}
     if variant == "pers_tpw3":
-        env["KQ_MFMA_PERS_TPW"] = "3"
+        env["mfma_pers_tpw"] = "3"
     if variant == "teams_x0":          # weights issued before x is written (the other load order)
-        env["KQ_MFMA_XF"] = "0"
+        env["mfma_xf"] = "0"
     if variant == "teams_x1":          # x written before the weights are issued, at any grid size
-        env["KQ_MFMA_XF"] = "1"
-    with U.env_vars(env):
+        env["mfma_xf"] = "1"
+    with U.tuning(env):
         y = U.gemv_gpu(fmt, U.to_dev(packed), x, N, K, path="mfma")
         y2 = U.gemv_gpu(fmt, U.to_dev(packed), x, N, K, path="mfma")
     yr, ad = R.gemv(fmt, fields, x)

@@ -133,7 +133,7 @@ def _weighted_gemv(fmt, ex, x, ids, rw, N, K, M, top_k, E, xps, unfused):
     y = U.empty_dev((M, N))
     wsb = kq.kq_moe_gemv_workspace_bytes(N, M, top_k, True)
     ws = U.empty_dev((wsb // 4 + 1,))
-    with U.env_vars({"KQ_MOE_UNFUSED": "1"} if unfused else {}):
+    with U.tuning({"moe_unfused": "1"} if unfused else {}):
         kq.kq_moe_gemv(fmt, ex.dev, U.to_dev(x), U.to_dev(ids), U.to_dev(rw), y, N, K, M, top_k, E, xps, ws, wsb)
     return U.to_host(y)
 
@@ -144,7 +144,7 @@ def _weighted_gemv(fmt, ex, x, ids, rw, N, K, M, top_k, E, xps, unfused):
 def test_moe_one_token_weighted_is_one_launch_with_same_bits(fmt, xps, top_k, ids_row):
     """One token, weighted: the single-launch down + slot-order sum gives the
     bits of the per-slot kernel followed by the weighted-sum kernel (the
-    KQ_MOE_UNFUSED path), including a duplicated expert and a bad id (NaN)."""
+    moe_unfused path), including a duplicated expert and a bad id (NaN)."""
     N, K, E = 300, 768, 32
     if ids_row is None:
         ids, rw = _route(1, E, top_k, 40 + top_k)
@@ -181,7 +181,7 @@ def test_moe_ffn_one_token_same_bits_as_three_kernels():
     for unfused in (False, True):
         y = U.empty_dev((1, L.hidden))
         ws = U.empty_dev((wsb // 4 + 1,))
-        with U.env_vars({"KQ_MOE_UNFUSED": "1"} if unfused else {}):
+        with U.tuning({"moe_unfused": "1"} if unfused else {}):
             kq.kq_moe_ffn(L.fmt, gate.dev, up.dev, down.dev, U.to_dev(x), U.to_dev(ids), U.to_dev(rw), y, None,
                           L.hidden, L.inter, 1, L.top_k, L.n_experts, ws, wsb)
         outs.append(U.to_host(y))

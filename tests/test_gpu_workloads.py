@@ -157,6 +157,9 @@ def test_lm_head_verify_argmax(lm_head, lm_head_verify_ref, M):
     x, yr, ad = x48[:M], yr48[:M], ad48[:M]
     y_dev, y = _head_run(lm_head, x)
     U.assert_parity(y, yr, ad, f"lm_head M={M}")
+    gaps = R.top2_gap(yr)
+    errs = np.max(np.abs(y - yr), axis=1)
+    assert np.all(gaps > 4 * errs), f"argmax not pinned by these seeds: gaps {gaps} errors {errs}"
     am = _argmax_gpu(y_dev, h.n, M)
     assert np.array_equal(am, R.argmax_lowest(yr))
     for m in sorted({0, M // 2, M - 1}):
