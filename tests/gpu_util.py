@@ -41,16 +41,25 @@ def quantize_both(fmt, W):
     return packed, fields
 
 
+_TUNING: dict = {}   # the overrides in force (blocks nest)
+
+
 @contextlib.contextmanager
 def tuning(values: dict):
     """Force kernels or configurations (kq_set_tuning) for the duration of a
-    block; every override is cleared afterwards."""
+    block; afterwards the overrides of the enclosing block are back."""
+    global _TUNING
+    outer = dict(_TUNING)
     try:
         for k, v in values.items():
             kq.kq_set_tuning(k, v)
+        _TUNING = {**outer, **values}
         yield
     finally:
         kq.kq_set_tuning(None, None)
+        for k, v in outer.items():
+            kq.kq_set_tuning(k, v)
+        _TUNING = outer
 
 
 def gemv_gpu(fmt, packed_dev, x16: np.ndarray, N: int, K: int, path: str | None = None) -> np.ndarray:
@@ -59,7 +68,7 @@ def gemv_gpu(fmt, packed_dev, x16: np.ndarray, N: int, K: int, path: str | None 
     xd = to_dev(x16)
     y = empty_dev((M, N))
     y.fill_(float("nan"))
-    with tuning({"force_path": path} if path else {}):
+    with tuning({"force_path": path[0]} if path else {}):   # "generic", "valu", "lds", "mfma"
         kq.kq_gemv(fmt, packed_dev, xd, y, N, K, M)
     return to_host(y)
 

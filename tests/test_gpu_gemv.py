@@ -192,7 +192,7 @@ def test_mfma_variants_parity(fmt, variant, N, K, M):
     kernel runs one workgroup per 16 columns (chunk), or one for all columns
     of a tile (chunk_whole)."""
     packed, fields, x = _case(fmt, N, K, M, 9)
-    env = {"mfma_variant": variant.split("_tpw")[0]}
+    env = {"mfma_variant": {"pers_tpw3": "pers", "teams_x0": "teams", "teams_x1": "teams"}.get(variant, variant)}
     if variant == "pers_tpw3":
         env["mfma_pers_tpw"] = "3"
     if variant == "teams_x0":          # weights issued before x is written (the other load order)
