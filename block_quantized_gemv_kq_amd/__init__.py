@@ -36,6 +36,7 @@ SIGNATURES = {
     "kq_gemv_invariant": (_I32, [_I32, _P, _P, _P, _I64, _I64, _I32, _P]),
     "kq_gemv_argmax_workspace_bytes": (_I64, [_I32, _I64, _I64, _I32]),
     "kq_gemv_argmax": (_I32, [_I32, _P, _P, _P, _I64, _I64, _I32, _P, _P, _I64, _P]),
+    "kq_gemv_argmax_noalloc": (_I32, [_I32, _P, _P, _P, _I64, _I64, _I32, _P, _P]),
     "kq_moe_gemv_workspace_bytes": (_I64, [_I64, _I32, _I32, _I32]),
     "kq_moe_gemv": (_I32, [_I32, _P, _P, _P, _P, _P, _I64, _I64, _I32, _I32, _I32, _I32, _P, _I64, _P]),
     "kq_moe_ffn_workspace_bytes": (_I64, [_I64, _I64, _I32, _I32]),
@@ -203,6 +204,12 @@ def kq_gemv_argmax(fmt, W, x, y, N: int, K: int, M: int, out, workspace, workspa
     """kq_gemv into y, then out[m] = argmax of y[m] (int32, device)."""
     _check(lib().kq_gemv_argmax(_fmt(fmt), _ptr(W), _ptr(x), _ptr(y), N, K, M, _ptr(out), _ptr(workspace),
                                 workspace_bytes, _stream(stream)), "kq_gemv_argmax")
+
+
+def kq_gemv_argmax_noalloc(fmt, W, x, y, N: int, K: int, M: int, out, stream=None) -> None:
+    """kq_gemv_argmax with the library's static scratch instead of a workspace."""
+    _check(lib().kq_gemv_argmax_noalloc(_fmt(fmt), _ptr(W), _ptr(x), _ptr(y), N, K, M, _ptr(out),
+                                        _stream(stream)), "kq_gemv_argmax_noalloc")
 
 
 def kq_gemv_invariant(fmt, W, x, y, N: int, K: int, M: int, stream=None) -> None:

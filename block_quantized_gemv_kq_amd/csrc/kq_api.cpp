@@ -530,6 +530,28 @@ int kq_gemv_argmax(int fmt, const void* W, const uint16_t* x, float* y, int64_t 
   return hip_status(kq::launch_gemv_argmax(a, out, workspace), "kq_gemv_argmax");
 }
 
+int kq_gemv_argmax_noalloc(int fmt, const void* W, const uint16_t* x, float* y, int64_t N, int64_t K, int M,
+                           int32_t* out, void* stream) {
+  int st = check_fmt_k(fmt, K);
+  if (st) return st;
+  if ((st = check_n(N, "N"))) return st;
+  if (N < 1 || N > KQ_MAX_N) return fail(KQ_ERR_ARG, "kq_gemv_argmax_noalloc: N=%lld out of range", (long long)N);
+  if (M < 0 || M > KQ_MAX_M) return fail(KQ_ERR_ARG, "M=%d must be in [0, %d]", M, KQ_MAX_M);
+  if (M == 0) return ok();
+  if (!W || !x || !y || !out) return fail(KQ_ERR_ARG, "kq_gemv_argmax_noalloc: null pointer");
+  if (!aligned(W, 4) || !aligned(y, 4) || !aligned(out, 4))
+    return fail(KQ_ERR_ALIGN, "kq_gemv_argmax_noalloc: W, y and out must be 4-byte aligned");
+  if (!aligned(x, 16)) return fail(KQ_ERR_ALIGN, "kq_gemv_argmax_noalloc: x must be 16-byte aligned");
+  const int64_t need = kq_gemv_argmax_workspace_bytes(fmt, N, K, M);
+  if (need < 0) return (int)need;
+  if (need > KQ_NOALLOC_SCRATCH_BYTES)
+    return fail(KQ_ERR_ARG, "kq_gemv_argmax_noalloc: this shape needs %lld bytes of partials, more than the "
+                "%d-byte static scratch; use kq_gemv_argmax with a workspace", (long long)need,
+                KQ_NOALLOC_SCRATCH_BYTES);
+  kq::GemvArgs a{fmt, static_cast<const uint8_t*>(W), x, y, N, K, M, static_cast<hipStream_t>(stream)};
+  return hip_status(kq::launch_gemv_argmax_noalloc(a, out), "kq_gemv_argmax_noalloc");
+}
+
 int64_t kq_argmax_workspace_bytes(int64_t N, int M) {
   if (N < 0 || M < 0) return fail(KQ_ERR_ARG, "negative size");
   return (int64_t)M * kq::argmax_partials(N) * 8;

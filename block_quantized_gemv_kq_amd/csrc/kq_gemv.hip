@@ -15,6 +15,8 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <mutex>
+
 #include "kq_dev.h"
 #include "kq_internal.h"
 
@@ -550,6 +552,46 @@ int launch_gemv_argmax(const GemvArgs& a, int32_t* out, void* ws) {
     case KQ_Q4_0: return gemv_argmax_fmt<F_Q4_0>(a, out, ws);
     default: return gemv_argmax_fmt<F_AFFINE4>(a, out, ws);
   }
+}
+
+// ------------------------------------------------- allocation-free argmax
+// Device memory for the partial argmax results of kq_gemv_argmax_noalloc,
+// for callers that cannot allocate. Each device holds its own copy, at its own
+// address, until the process ends. In host code the name is not a device
+// address: kernels get the address hipGetSymbolAddress returns for the current
+// device (noalloc_scratch below). Calls on one device share it, so calls that
+// overlap in time on one device race. Every slot a call reads was written
+// earlier in that call, so nothing needs clearing between calls.
+static __device__ __align__(256) uint8_t scratch[KQ_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int NOALLOC_MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[NOALLOC_MAX_DEVICES] = {};
+}  // namespace
+
+int noalloc_scratch(void** ptr) {
+  int dev = -1;
+  int err = (int)hipGetDevice(&dev);
+  if (err) return err;
+  if (dev < 0 || dev >= NOALLOC_MAX_DEVICES) return (int)hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    err = (int)hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err) return err;
+    if (!p) return (int)hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return 0;
+}
+
+int launch_gemv_argmax_noalloc(const GemvArgs& a, int32_t* out) {
+  void* ws = nullptr;
+  const int err = noalloc_scratch(&ws);
+  if (err) return err;
+  return launch_gemv_argmax(a, out, ws);
 }
 
 int launch_gemv_invariant(const GemvArgs& a) {

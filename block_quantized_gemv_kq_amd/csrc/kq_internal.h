@@ -60,6 +60,9 @@ int launch_gemv_invariant(const GemvArgs& a);
 // partials (gemv_argmax_fused_parts(a) per column when fused, else kq_argmax's).
 int launch_gemv_argmax(const GemvArgs& a, int32_t* out, void* ws);
 int64_t gemv_argmax_fused_parts(const GemvArgs& a);
+// The same with the partials in the library's static scratch array of the
+// current device (KQ_NOALLOC_SCRATCH_BYTES; the caller checks the size).
+int launch_gemv_argmax_noalloc(const GemvArgs& a, int32_t* out);
 int launch_gemv_mfma(const GemvArgs& a);
 
 struct MoeArgs {

@@ -230,6 +230,21 @@ int kq_gemv_argmax(int fmt, const void* W, const uint16_t* x, float* y,
                    int64_t N, int64_t K, int M, int32_t* out,
                    void* workspace, int64_t workspace_bytes, void* stream);
 
+/* kq_gemv_argmax_noalloc — for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): kq_gemv_argmax with no workspace argument. The argmax partials
+ * go to a static device array of KQ_NOALLOC_SCRATCH_BYTES that the library
+ * holds on each device it runs on until the process ends; the call allocates
+ * nothing. y and out are as kq_gemv_argmax writes them, bit for bit. Every
+ * call on one device shares that array: calls that overlap in time on one
+ * device (other streams, other threads) race and must be serialised by the
+ * caller. Errors: those of kq_gemv_argmax, and KQ_ERR_ARG when the shape
+ * needs more than KQ_NOALLOC_SCRATCH_BYTES of partials
+ * (kq_gemv_argmax_workspace_bytes tells; 151936 rows need 76 KB at M = 1). */
+#define KQ_NOALLOC_SCRATCH_BYTES (1 << 20)
+int kq_gemv_argmax_noalloc(int fmt, const void* W, const uint16_t* x, float* y,
+                           int64_t N, int64_t K, int M, int32_t* out, void* stream);
+
 /* ---- A chain of dependent M = 1 GEMVs in one persistent launch ----------
  * Kinetic docs, "What makes it fast": a decode step is hundreds of small GPU
  * kernels, recorded once and replayed with one call per token. kq_stack_run
