@@ -8,16 +8,20 @@ per layer the row-concatenated q|k|v GEMV, o, row-concatenated gate|up, down
 (the order a decoder layer consumes them in), then lm_head and argmax. The
 step is captured once as a HIP graph and replayed.
 
-Also measured (extra fields of the same JSON line): the same stack as an
-M = 8 speculative-verify pass (t(8)/t(1)), per-kernel durations from HIP
-events, and the CPU oracle on a bounded sample (2 layers + lm_head) on the
-host cores.
+Also measured (extra fields of the same JSON line): the same stack as a
+speculative-verify pass at M = 2, 4, 8, 16 and 48 (t(M)/t(1)), per-kernel
+durations from HIP events, the single Q8_0 GEMV, the 0.6B-shaped Q4_0 stack
+and the Q4_0 MoE layer, a read-only streaming ceiling at the sizes of the
+step's matrices, and the CPU oracle (median of 3 after a warm-up) on a bounded
+sample of every configuration on the host cores, which also checks the GPU's
+outputs of that sample against the oracle at run time.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -40,15 +44,34 @@ GROUP_NAMES = ("qkv", "o", "gate_up", "down")
 # taken with: a changed file (sha256 prefix below, paths under the package)
 # reports traffic as unknown.
 MEASURED_TRAFFIC = {
-    "sources": {"csrc/kq_gemv.hip": "b7dc83393a53d887", "csrc/kq_dev.h": "c74b68a6ea6363ea",
-                "build.py": "4539a7654dd76413"},
-    "bytes": {"qkv": 9957769, "o": 6694411, "gate_up": 31327809, "down": 15820980,
-              "lm_head": 414277662},
+    "sources": {"csrc/kq_gemv.hip": "43a62a509d5dc06a", "csrc/kq_dev.h": "c74b68a6ea6363ea",
+                "build.py": "61a208a975511b09"},
+    "bytes": {"qkv": 9958424, "o": 6695350, "gate_up": 31328970, "down": 15821590,
+              "lm_head": 414301811},
 }
 
 
+MFMA_PEAK_F16_TFLOPS = 2500.0   # MI355X dense fp16 matrix-core peak, published
+
+# MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE * SIMDs), percent) per
+# launch group of the verify pass, from a counter run over `bench.py
+# --kernels-only M`; valid only for the kernel sources it was taken with.
+MEASURED_MFMA = {"sources": {'csrc/kq_mfma.hip': '9fa086e455bbd459', 'csrc/kq_dev.h': 'c74b68a6ea6363ea', 'build.py': '61a208a975511b09'},
+                 "verify_m8": {'qkv': 2.62, 'o': 1.82, 'gate_up': 6.23, 'down': 3.2, 'lm_head': 7.88}}
+
+
+def measured_mfma(run, group):
+    pkg = os.path.join(ROOT, "block_quantized_gemv_kq_amd")
+    if not MEASURED_MFMA["sources"]:
+        return None
+    for name, want in MEASURED_MFMA["sources"].items():
+        with open(os.path.join(pkg, name), "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest()[:16] != want:
+                return None
+    return MEASURED_MFMA.get(run, {}).get(group)
+
+
 def measured_traffic(group):
-    import hashlib
     pkg = os.path.join(ROOT, "block_quantized_gemv_kq_amd")
     for name, want in MEASURED_TRAFFIC["sources"].items():
         with open(os.path.join(pkg, name), "rb") as f:
@@ -87,12 +110,15 @@ class DeviceStack:
                 kq.kq_pack(fmt, W, out=packed[r0:r0 + m.n])
                 r0 += m.n
             x = S.activations((wid, layer, mats[0].input_slot), K, M)
-            return layer, gi, fmt, packed, x, N, K
+            digest = hashlib.sha256(packed).digest() + hashlib.sha256(x).digest()
+            return layer, gi, fmt, packed, x, N, K, digest
 
         jobs = [(l, gi, g) for l in range(self.layers) for gi, g in enumerate(stack.launch_groups)]
         per_layer = [[None] * len(stack.launch_groups) for _ in range(self.layers)]
+        digests = {}
         with ThreadPoolExecutor(4) as ex:
-            for layer, gi, fmt, packed, x, N, K in ex.map(lambda j: build_group(*j), jobs):
+            for layer, gi, fmt, packed, x, N, K, digest in ex.map(lambda j: build_group(*j), jobs):
+                digests[(layer, gi)] = digest
                 Wd = torch.from_numpy(packed).to(dev)
                 xd = torch.from_numpy(x).to(dev)
                 yd = torch.empty((M, N), dtype=torch.float32, device=dev)
@@ -115,6 +141,9 @@ class DeviceStack:
             self.head = (h.fmt, Wd, torch.from_numpy(x).to(dev), yd, h.n, h.k, ws, wsb, am)
             self.weight_bytes += packed.nbytes
             self.alg_bytes += packed.nbytes + x.nbytes + M * h.n * 4 + M * h.n * 4 + M * 4
+            digests[(self.layers, 0)] = hashlib.sha256(packed).digest() + hashlib.sha256(x).digest()
+        # SHA-256 over every launch's packed weights and activations, in step order
+        self.input_sha256 = hashlib.sha256(b"".join(digests[k] for k in sorted(digests))).hexdigest()
 
     def with_columns(self, S, M, act_workload_id):
         """A view with the same resident weights and M fresh activation columns."""
@@ -293,7 +322,7 @@ def _graph_time_us(torch, fns, reps, per):
     return float(np.median(t)) * 1000.0 / per, [float(np.percentile(t, q)) * 1000.0 / per for q in (10, 50, 90)]
 
 
-def bench_single_q8_0(torch, kq, S):
+def bench_single_q8_0(torch, kq, S, gpu_out=None):
     """Config 1: one Q8_0 1024x1024 GEMV, M=1 (seeded weights and x). Cold:
     rotating through copies totalling >= 1 GB (four times the 256 MB
     last-level cache); warm: one copy, back to back. Each launch in a graph:
@@ -309,6 +338,8 @@ def bench_single_q8_0(torch, kq, S):
     cold, cold_p = _graph_time_us(torch, [lambda i=i: kq.kq_gemv(c.fmt, Ws[i], x, y, c.n, c.k, 1)
                                           for i in range(copies)], 7, copies)
     warm, warm_p = _graph_time_us(torch, [lambda: kq.kq_gemv(c.fmt, packed, x, y, c.n, c.k, 1)] * 200, 7, 200)
+    if gpu_out is not None:
+        gpu_out["single_y"] = _host(y)
     del Ws
     return {"shape": f"q8_0 {c.n}x{c.k}, M=1", "alg_bytes": int(alg), "cold_copies": int(copies),
             "us_per_call_cold": cold, "gbps_cold": alg / (cold * 1e-6) / 1e9, "us_p10_p50_p90_cold": cold_p,
@@ -414,78 +445,277 @@ def bench_moe(torch, kq, S, steps):
     return out
 
 
-def stream_ceiling(torch):
-    """A measured streaming rate on this GPU: a 1 GiB device-to-device copy
-    (torch copy_, the runtime's copy kernel), bytes read plus bytes written
-    per second, median of 10."""
-    n = 1 << 28
-    a = torch.ones((n,), dtype=torch.float32, device="cuda")
+def bench_moe_eager(torch, kq, S):
+    """The Q4_0 MoE layer at each token count, eager (for counter runs): one
+    seeded expert replicated to all 128, each call twice."""
+    L = S.MOE_Q4_0
+    E = L.n_experts
+    mats = []
+    for which, (n, k) in enumerate(((L.inter, L.hidden), (L.inter, L.hidden), (L.hidden, L.inter))):
+        W = S.weights(L.weight_seed(0, which), n, k)
+        mats.append(torch.from_numpy(kq.kq_pack(L.fmt, W)).to("cuda").reshape(-1).repeat(E))
+    for M in S.MOE_M:
+        ids, rw = S.route_table(L.workload_id, M, E, L.top_k)
+        x = torch.from_numpy(S.activations(L.act_seed_prefix(), L.hidden, M)).to("cuda")
+        idd, rwd = torch.from_numpy(ids).to("cuda"), torch.from_numpy(rw).to("cuda")
+        y = torch.empty((M, L.hidden), dtype=torch.float32, device="cuda")
+        h = torch.empty((M, L.top_k, L.inter), dtype=torch.float16, device="cuda")
+        wsb = kq.kq_moe_ffn_workspace_bytes(L.hidden, L.inter, M, L.top_k)
+        ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+        torch.cuda.synchronize()
+        for _ in range(2):
+            kq.kq_moe_ffn(L.fmt, mats[0], mats[1], mats[2], x, idd, rwd, y, h, L.hidden, L.inter, M, L.top_k, E,
+                          ws, wsb)
+        torch.cuda.synchronize()
+    del mats
+
+
+def _probe_lib():
+    import ctypes
+    L = ctypes.CDLL(os.path.join(ROOT, "block_quantized_gemv_kq_amd", "libkq_probe.so"))
+    L.kq_probe_stream_read.restype = ctypes.c_int
+    L.kq_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
+                                       ctypes.c_void_p]
+    return L
+
+
+# bytes per launch of the step's matrices (packed weights) and a large read
+CEILING_SIZES = {"o": 6553600, "qkv": 15728640, "down": 15564800, "gate_up": 31129600,
+                 "lm_head": 413265920, "1GiB": 1 << 30}
+
+
+def stream_ceiling(torch, reps=7):
+    """A measured read-only ceiling: a plain streaming kernel (libkq_probe.so:
+    each workgroup reads one contiguous chunk, every lane issuing all its
+    16-byte buffer loads before using any, XOR-folded, one word per workgroup
+    written) reading buffers of the sizes of the step's matrices, cold (each
+    launch reads other bytes of a 1 GiB buffer, four times the last-level
+    cache), launched back to back in a graph like the GEMVs; the best of 1, 2,
+    4, 8 and 16 loads per lane. Also the plain-read step: the same reads in the
+    order and number of the M = 1 step's launches."""
+    L = _probe_lib()
+    buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    buf.fill_(7)
+    sink = torch.empty(1 << 20, dtype=torch.int32, device="cuda")
+    base = buf.data_ptr()
+    out = {}
+    for name, nbytes in CEILING_SIZES.items():
+        span = (nbytes + 4095) // 4096 * 4096
+        copies = max(1, (1 << 30) // span)
+        best = None
+        for per in (1, 2, 4, 8, 16):
+            def launches(per=per):
+                s_ = torch.cuda.current_stream().cuda_stream
+                for c in range(copies):
+                    st = L.kq_probe_stream_read(base + c * span, nbytes, sink.data_ptr(), per, s_)
+                    if st < 0:
+                        raise RuntimeError(f"kq_probe_stream_read failed ({st})")
+            us, _ = _graph_time_us(torch, [launches], reps, copies)
+            if best is None or us < best[0]:
+                best = (us, per)
+        out[name] = {"bytes": nbytes, "us_per_launch": best[0], "gbps": nbytes / (best[0] * 1e-6) / 1e9,
+                     "loads_per_lane": best[1], "workgroups": -(-nbytes // (4096 * best[1])),
+                     "cold_copies": copies}
+    step_us = 36 * sum(out[k]["us_per_launch"] for k in ("qkv", "o", "gate_up", "down")) + out["lm_head"]["us_per_launch"]
+    del buf, sink
+    torch.cuda.empty_cache()
+    return {"kernel": "read-only streaming (libkq_probe.so), one launch per buffer, cold, graph-timed",
+            "sizes": out, "plain_read_step_us": step_us,
+            "plain_read_step_gbps": (36 * sum(CEILING_SIZES[k] for k in ("qkv", "o", "gate_up", "down"))
+                                     + CEILING_SIZES["lm_head"]) / (step_us * 1e-6) / 1e9}
+
+
+def _median_timed(fn, reps=3):
+    """One warm-up, then the median of `reps` timed runs; returns (median s,
+    all times, the last result)."""
+    fn()
+    ts, out = [], None
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        out = fn()
+        ts.append(time.perf_counter() - t0)
+    return float(np.median(ts)), ts, out
+
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        return int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+
+
+def _parity(y_gpu, y_ref, abs_dot):
+    """Max error ratio, whether every output is within the bar, and for
+    vocabulary-sized outputs the argmax of both sides and the oracle's top-2
+    gap per column."""
+    from oracle import ref as R
+    y_gpu = np.asarray(y_gpu, np.float64).reshape(y_ref.shape)
+    return {"max_err_ratio": R.error_ratio(y_gpu, y_ref, abs_dot),
+            "within_tolerance": bool(np.all(R.within_tolerance(y_gpu, y_ref, abs_dot)))}
+
+
+def _argmax_parity(y_gpu, y_ref, am_gpu):
+    from oracle import ref as R
+    y_gpu = np.asarray(y_gpu, np.float64).reshape(y_ref.shape)
+    ref = np.atleast_1d(R.argmax_lowest(y_ref))
+    gap = np.atleast_1d(R.top2_gap(y_ref))
+    err = np.max(np.abs(y_gpu - y_ref), axis=-1).reshape(-1)
+    return {"argmax_gpu": [int(v) for v in np.atleast_1d(am_gpu)], "argmax_ref": [int(v) for v in ref],
+            "argmax_equal": bool(np.array_equal(np.atleast_1d(am_gpu), ref)),
+            "top2_gap_min": float(gap.min()), "max_abs_err": float(err.max()),
+            "pinned": bool(np.all(gap > 4 * err))}
+
+
+def cpu_baseline(S, stack, kq, gpu_out, budget_layers=2):
+    """The oracle as it stands (decode packed bytes, dequantize, fp64 dot) on
+    the host cores: for the headline workload, `budget_layers` layers and the
+    lm_head with its argmax at M = 1, each timed as the median of 3 runs after
+    one warm-up, extrapolated to one token; unit GB/s of packed weights. The
+    same oracle results check the GPU's outputs of that sample (gpu_out:
+    the M = 1 step's y of those layers' launches and of the lm_head, and the
+    argmax) at run time."""
+    from oracle import formats as F
+    from oracle import ref as R
+    units = []
+    for layer in range(budget_layers):
+        for gi, group in enumerate(stack.launch_groups):
+            mats = [stack.per_layer[i] for i in group]
+            K, fmt = mats[0].k, mats[0].fmt
+            N = sum(m.n for m in mats)
+            packed = np.concatenate([kq.kq_pack(fmt, S.weights(stack.weight_seed(layer, i), m.n, m.k))
+                                     for i, m in zip(group, mats)])
+            x = S.activations((stack.workload_id, layer, mats[0].input_slot), K, 1)
+            units.append((layer, gi, fmt, packed, x, N, K))
+    h = stack.head
+    W = S.weights(stack.weight_seed(stack.layers, 0), h.n, h.k)
+    head_packed = kq.kq_pack(h.fmt, W)
+    del W
+    head_x = S.activations((stack.workload_id, stack.layers, 0), h.k, 1)
+    t_layers, ts_l, res = _median_timed(
+        lambda: [R.gemv(f, F.decode(f, p, n, k), x) for (_, _, f, p, x, n, k) in units])
+    t_head, ts_h, (yh, ah) = _median_timed(
+        lambda: R.gemv(h.fmt, F.decode(h.fmt, head_packed, h.n, h.k), head_x))
+    R.argmax_lowest(yh[0])
+    t_token = t_layers / budget_layers * stack.layers + t_head
+    layer_bytes = sum(u[3].nbytes for u in units) / budget_layers
+    total_bytes = layer_bytes * stack.layers + head_packed.nbytes
+    parity = None
+    if gpu_out is not None:
+        ratios, ok = [], True
+        for (layer, gi, *_), (yr, ad) in zip(units, res):
+            p = _parity(gpu_out["layers"][(layer, gi)], yr, ad)
+            ratios.append(p["max_err_ratio"])
+            ok = ok and p["within_tolerance"]
+        ph = _parity(gpu_out["head_y"], yh, ah)
+        parity = {"sample": f"{len(units)} launches of layers 0..{budget_layers - 1} and the lm_head, M=1",
+                  "max_err_ratio": max(ratios + [ph["max_err_ratio"]]),
+                  "within_tolerance": bool(ok and ph["within_tolerance"]),
+                  "lm_head": _argmax_parity(gpu_out["head_y"], yh, gpu_out["head_argmax"])}
+    return {"value": total_bytes / t_token / 1e9, "unit": "GB/s", "cores": int(_blas_threads()),
+            "kind": "oracle",
+            "sample": f"{budget_layers} of {stack.layers} layers (as the step's launch groups) + lm_head + "
+                      f"argmax at M=1, median of 3 after a warm-up ({t_layers + t_head:.1f} s per sample), "
+                      f"extrapolated to one token",
+            "s_per_token": t_token, "tokens_per_s": 1.0 / t_token,
+            "runs_s": {"layers": ts_l, "lm_head": ts_h},
+            "host_cpu_count": os.cpu_count(), "parity": parity}
+
+
+def oracle_other_configs(S, kq, gpu_out):
+    """The oracle on a bounded sample of every other configuration, median of
+    3 after a warm-up, with the GPU's outputs checked where the run kept
+    them: the single Q8_0 GEMV (whole), the 0.6B stack (2 of 28 layers,
+    extrapolated), the verify pass at M = 8 (its lm_head, whose argmax per
+    column is compared), and the MoE layer at M = 1 and 4 (whole layer)."""
+    from oracle import formats as F
+    from oracle import ref as R
+    out = {}
+    c = S.SINGLE_Q8_0
+    packed = kq.kq_pack(c.fmt, S.weights(c.weight_seed, c.n, c.k))
+    x = S.activation_column(c.act_seed, c.k)[None, :]
+    t, _, (yr, ad) = _median_timed(lambda: R.gemv(c.fmt, F.decode(c.fmt, packed, c.n, c.k), x))
+    out["single_q8_0"] = {"s_per_call": t, "gbps": packed.nbytes / t / 1e9}
+    if gpu_out and "single_y" in gpu_out:
+        out["single_q8_0"]["parity"] = _parity(gpu_out["single_y"], yr, ad)
+    st = S.QWEN3_0_6B_Q4_0
+    units = []
+    for layer in range(2):
+        for m_i, m in enumerate(st.per_layer):
+            units.append((m.fmt, kq.kq_pack(m.fmt, S.weights(st.weight_seed(layer, m_i), m.n, m.k)),
+                          S.activations(st.act_seed_prefix(layer, m.input_slot), m.k, 1), m.n, m.k))
+    t, _, _ = _median_timed(lambda: [R.gemv(f, F.decode(f, p, n, k), x) for (f, p, x, n, k) in units])
+    tok = t / 2 * st.layers
+    out["qwen3_0.6b_q4_0_stack"] = {"s_per_token": tok, "tokens_per_s": 1 / tok,
+                                    "gbps": sum(u[1].nbytes for u in units) / 2 * st.layers / tok / 1e9,
+                                    "sample": "2 of 28 layers, extrapolated"}
+    if gpu_out and "verify8_head_y" in gpu_out:
+        h = S.QWEN3_4B_AFFINE4.head
+        hp = kq.kq_pack(h.fmt, S.weights(S.QWEN3_4B_AFFINE4.weight_seed(S.QWEN3_4B_AFFINE4.layers, 0), h.n, h.k))
+        xv = S.activations((S.VERIFY_WORKLOAD_ID, S.QWEN3_4B_AFFINE4.layers, 0), h.k, 8)
+        t, _, (yr, ad) = _median_timed(lambda: R.gemv(h.fmt, F.decode(h.fmt, hp, h.n, h.k), xv))
+        out["verify_m8_lm_head"] = {"s_per_pass_head_only": t, "gbps": hp.nbytes / t / 1e9,
+                                    "parity": {**_parity(gpu_out["verify8_head_y"], yr, ad),
+                                               **_argmax_parity(gpu_out["verify8_head_y"], yr,
+                                                                gpu_out["verify8_head_argmax"])}}
+        del hp
+    L = S.MOE_Q4_0
+    for M in (1, 4):
+        ids, rw = S.route_table(L.workload_id, M, L.n_experts, L.top_k)
+        used = sorted(set(ids.reshape(-1).tolist()))
+        packs = {}
+        for e in used:
+            packs[e] = [kq.kq_pack(L.fmt, S.weights(L.weight_seed(e, w), n, k))
+                        for w, (n, k) in enumerate(((L.inter, L.hidden), (L.inter, L.hidden), (L.hidden, L.inter)))]
+        x = S.activations(L.act_seed_prefix(), L.hidden, M)
+
+        def run():
+            fl = [[None] * L.n_experts for _ in range(3)]
+            for e in used:
+                for w, (n, k) in enumerate(((L.inter, L.hidden), (L.inter, L.hidden), (L.hidden, L.inter))):
+                    fl[w][e] = F.decode(L.fmt, packs[e][w], n, k)
+            return R.moe_ffn(L.fmt, fl[0], fl[1], fl[2], x, ids, rw)
+        t, _, _ = _median_timed(run)
+        out[f"moe_q4_0_m{M}"] = {"s_per_layer": t, "unique_experts": len(used),
+                                 "gbps": len(used) * 2654208 / t / 1e9}
+    return out
+
+
+def env_info(torch):
+    """GPU, ROCm, torch and numpy versions, and the clocks rocm-smi reports."""
+    import subprocess
+    props = torch.cuda.get_device_properties(0)
+    info = {"gpu": f"{torch.cuda.get_device_name(0)} ({getattr(props, 'gcnArchName', '?')}, "
+                   f"{props.multi_processor_count} CUs)",
+            "torch": torch.__version__, "numpy": np.__version__}
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            info["rocm"] = f.read().strip()
+    except OSError:
+        info["rocm"] = None
+    try:
+        p = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20)
+        info["clocks"] = [ln.split(":", 1)[1].strip() for ln in p.stdout.splitlines()
+                          if "clock level" in ln][:4]
+    except Exception:
+        info["clocks"] = None
+    return info
+
+
+def _copy_calibration(torch):
+    """A plain copy of known size (256 MiB read, 256 MiB written), three times,
+    to scale the traffic counters against."""
+    n = 256 << 20
+    a = torch.empty(n // 4, dtype=torch.float32, device="cuda").fill_(1.0)
     b = torch.empty_like(a)
     for _ in range(3):
         b.copy_(a)
     torch.cuda.synchronize()
-    ts = []
-    for _ in range(10):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        b.copy_(a)
-        e1.record()
-        torch.cuda.synchronize()
-        ts.append(e0.elapsed_time(e1))
-    del a, b
-    torch.cuda.empty_cache()
-    return {"kernel": "1 GiB device-to-device copy (read + write)",
-            "gbps": 2 * (n * 4) / (float(np.median(ts)) * 1e-3) / 1e9}
+    return n
 
 
-def cpu_baseline(S, stack, kq, budget_s=15.0):
-    """The oracle as it stands (decode packed bytes, dequantize, fp64 dot) on
-    the host cores, on a bounded sample: the lm_head plus as many layers of
-    the stack as fit in about `budget_s` seconds of oracle work (at least 1),
-    extrapolated to one token; unit GB/s of packed weights."""
-    from oracle import formats as F
-    from oracle import ref as R
-    h = stack.head
-    W = S.weights(stack.weight_seed(stack.layers, 0), h.n, h.k)
-    packed = kq.kq_pack(h.fmt, W)
-    del W
-    x = S.activations((stack.workload_id, stack.layers, 0), h.k, 1)
-    t0 = time.perf_counter()
-    y, _ = R.gemv(h.fmt, F.decode(h.fmt, packed, h.n, h.k), x)
-    R.argmax_lowest(y[0])
-    t_head = time.perf_counter() - t0
-    head_bytes = packed.nbytes
-    del packed
-    t_layers = []
-    bytes_layer = 0
-    for layer in range(stack.layers):
-        t = 0.0
-        bytes_layer = 0
-        for i, m in enumerate(stack.per_layer):
-            W = S.weights(stack.weight_seed(layer, i), m.n, m.k)
-            packed = kq.kq_pack(m.fmt, W)
-            del W
-            x = S.activations((stack.workload_id, layer, m.input_slot), m.k, 1)
-            t0 = time.perf_counter()
-            R.gemv(m.fmt, F.decode(m.fmt, packed, m.n, m.k), x)
-            t += time.perf_counter() - t0
-            bytes_layer += packed.nbytes
-        t_layers.append(t)
-        if t_head + sum(t_layers) >= budget_s:
-            break
-    t_token = float(np.mean(t_layers)) * stack.layers + t_head
-    total_bytes = bytes_layer * stack.layers + head_bytes
-    try:
-        from threadpoolctl import threadpool_info
-        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        blas_threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return {"value": total_bytes / t_token / 1e9, "unit": "GB/s", "cores": int(blas_threads),
-            "kind": "oracle",
-            "sample": f"{len(t_layers)} of {stack.layers} layers + lm_head + argmax at M=1, "
-                      f"{sum(t_layers) + t_head:.1f} s of oracle work, extrapolated to one token",
-            "s_per_token": t_token, "tokens_per_s": 1.0 / t_token,
-            "host_cpu_count": os.cpu_count()}
+def _host(t):
+    return t.detach().cpu().numpy()
 
 
 def main():
@@ -499,10 +729,13 @@ def main():
                     help="skip the other configurations (single Q8_0 GEMV, 0.6B stack, MoE layer)")
     ap.add_argument("--verify-only", type=int, default=0, metavar="M",
                     help="short run for kernel traces: only the M-column verify pass, graph-replayed")
-    ap.add_argument("--kernels-only", action="store_true",
-                    help="short run for counter collection: per-kernel graphs and a copy of known size")
+    ap.add_argument("--kernels-only", type=int, nargs="?", const=1, default=0, metavar="M",
+                    help="short run for counter collection: eager launches of 4 layers and the lm_head at M "
+                         "columns (default 1), then a copy of known size")
     ap.add_argument("--moe-only", action="store_true",
-                    help="short run for kernel traces: only the Q4_0 MoE layer at each token count")
+                    help="short run: only the Q4_0 MoE layer at each token count")
+    ap.add_argument("--eager", action="store_true",
+                    help="with --moe-only: eager launches (for counter collection) instead of graphs")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -518,32 +751,37 @@ def main():
     stack = S.QWEN3_4B_AFFINE4
 
     if args.moe_only:
+        if args.eager:
+            bench_moe_eager(torch, kq, S)
+            n = _copy_calibration(torch)
+            print(json.dumps({"moe_only_eager": list(S.MOE_M), "copy_bytes_each_way": n}))
+            return
         moe = bench_moe(torch, kq, S, args.steps)
         print(json.dumps({"moe_only": {m: round(v["us_per_layer"], 3) for m, v in moe.items()}}))
+        return
+
+    if args.kernels_only:
+        # eager launches only (no graphs), for counter collection: each group
+        # of the first 4 layers and the lm_head (with its argmax) twice at M
+        # columns, then a plain copy of known size to calibrate the counters
+        ds = DeviceStack(torch, kq, S, stack, 1, layers=4)
+        if args.kernels_only > 1:
+            ds = ds.with_columns(S, args.kernels_only, S.VERIFY_WORKLOAD_ID)
+        torch.cuda.synchronize()
+        for layer in range(4):
+            for gi in range(len(GROUP_NAMES)):
+                ds.launch_group(layer, gi)
+        for _ in range(2):
+            ds.launch_head()
+        torch.cuda.synchronize()
+        n = _copy_calibration(torch)
+        print(json.dumps({"kernels_only_M": args.kernels_only, "copy_bytes_each_way": n}))
         return
 
     t0 = time.perf_counter()
     log("packing and uploading the 4B-shaped stack (M=1) ...")
     ds = DeviceStack(torch, kq, S, stack, 1)
     log(f"  {ds.weight_bytes / 1e9:.3f} GB of packed weights resident in {time.perf_counter() - t0:.1f} s")
-
-    if args.kernels_only:
-        # eager launches only (no graphs), for counter collection: each group
-        # of the first 4 layers, the lm_head and argmax twice, then a plain
-        # copy of known size to calibrate the counters against
-        for layer in range(4):
-            for gi in range(len(GROUP_NAMES)):
-                ds.launch_group(layer, gi)
-        for _ in range(2):
-            ds.launch_head()
-        n = 256 << 20
-        a = torch.empty(n // 4, dtype=torch.float32, device="cuda").fill_(1.0)
-        b = torch.empty_like(a)
-        for _ in range(3):
-            b.copy_(a)                       # plain copy kernel: 256 MiB read, 256 MiB written
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_bytes_each_way": n}))
-        return
 
     if args.verify_only:
         # the M-column verify pass alone (same resident weights, seeded
@@ -561,6 +799,9 @@ def main():
     ms_launches = total_l / args.steps
     log(f"M=1 step as {ds.layers * 4 + 3} launches: {ms_launches * 1000:.1f} us")
     del g
+    # the GPU's outputs of the last replay that the oracle checks at the end
+    gpu_out = {"layers": {(l, gi): _host(ds.groups[l][gi][3]) for l in range(2) for gi in range(4)},
+               "head_y": _host(ds.head[3]), "head_argmax": _host(ds.head[8])}
     # path B: the whole token in one persistent launch in decode order (+ argmax), as a graph
     ds.make_plan()
     g = capture(torch, ds.step_stacked)
@@ -604,10 +845,24 @@ def main():
         gv = capture(torch, dv.step)
         perv, total_v, _ = time_graph(torch, gv, max(5, args.steps // 2), 3)
         ms_v = total_v / max(5, args.steps // 2)
+        gpu_out["verify8_head_y"] = _host(dv.head[3])
+        gpu_out["verify8_head_argmax"] = _host(dv.head[8])
+        vk = kernel_table(torch, dv, reps=5)
+        vdom = max((k for k in vk if "gbps" in vk[k]),
+                   key=lambda k: vk[k]["us_per_launch"] * vk[k]["launches_per_step"])
+        vd = vk[vdom]
+        tflops = 2.0 * 8 * vd["N"] * vd["K"] / (vd["us_per_launch"] * 1e-6) / 1e12
         verify = {"M": 8, "ms_per_pass": ms_v, "gbps": dv.alg_bytes / (ms_v * 1e-3) / 1e9,
                   "t_ratio_vs_m1": ms_v / ms_per_step,
                   "tokens_per_s_upper_bound": 8 / (ms_v * 1e-3),
-                  "kernels": kernel_table(torch, dv, reps=5)}
+                  "roofline": {"bound": "hbm", "achieved": vd["gbps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                               "frac": vd["gbps"] / HBM_PEAK_GBS,
+                               "kernel": f"kq_gemv {vdom} ({vd['fmt']}, {vd['N']}x{vd['K']}, M=8)",
+                               "us_per_launch": vd["us_per_launch"],
+                               "mfma_useful_tflops": tflops, "mfma_peak_tflops_f16": MFMA_PEAK_F16_TFLOPS,
+                               "mfma_util_alg": tflops / MFMA_PEAK_F16_TFLOPS,
+                               "mfma_busy_counter": measured_mfma("verify_m8", vdom)},
+                  "kernels": vk}
         log(f"M=8 pass: {ms_v * 1000:.1f} us, t(8)/t(1) = {ms_v / ms_per_step:.2f}")
         del gv, dv
         torch.cuda.empty_cache()
@@ -618,20 +873,31 @@ def main():
     else:
         verify_all = None
     alg_bytes_step = ds.alg_bytes
+    input_sha = ds.input_sha256
     if not args.no_configs:
         del ds
         torch.cuda.empty_cache()
-        configs = {"single_q8_0": bench_single_q8_0(torch, kq, S)}
+        configs = {"single_q8_0": bench_single_q8_0(torch, kq, S, gpu_out)}
         log(f"single q8_0: {configs['single_q8_0']['us_per_call_cold']:.2f} us cold")
         configs["qwen3_0.6b_q4_0_stack"] = bench_small_stack(torch, kq, S, args.steps)
         log(f"0.6B stack: {configs['qwen3_0.6b_q4_0_stack']['us_per_step_cold']:.1f} us cold")
         configs["moe_q4_0"] = bench_moe(torch, kq, S, max(5, args.steps // 2))
         configs["stream_ceiling"] = stream_ceiling(torch)
+        sc = configs["stream_ceiling"]
+        log(f"read-only ceiling: {sc['sizes']['1GiB']['gbps']:.0f} GB/s at 1 GiB, plain-read step "
+            f"{sc['plain_read_step_us']:.1f} us")
+        for name, row in ktab.items():
+            if name in sc["sizes"] and "gbps" in row:
+                row["pct_of_read_ceiling"] = 100.0 * row["gbps"] / sc["sizes"][name]["gbps"]
 
     cpu = None
+    oracle_configs = None
     if not args.no_cpu_baseline:
-        log("timing the CPU oracle on 2 layers + lm_head ...")
-        cpu = cpu_baseline(S, stack, kq)
+        log("timing the CPU oracle on 2 layers + lm_head (median of 3) and checking the GPU's outputs ...")
+        cpu = cpu_baseline(S, stack, kq, gpu_out)
+        log(f"  oracle {cpu['s_per_token']:.2f} s per token; parity {cpu['parity']}")
+        if not args.no_configs:
+            oracle_configs = oracle_other_configs(S, kq, gpu_out)
 
     out = {
         "metric": "achieved HBM GB/s (% of peak) + equiv. decode tokens/s, M=1 and M=8 verify",
@@ -661,7 +927,11 @@ def main():
         "verify_all": verify_all,
         "other_configs": configs,
         "cpu_baseline": cpu,
+        "oracle_other_configs": oracle_configs,
+        "env": {**env_info(torch), "input_sha256": input_sha},
     }
+    if configs is not None:
+        out["pct_of_read_ceiling_step"] = 100.0 * configs["stream_ceiling"]["plain_read_step_us"] / (ms_per_step * 1000)
     print(json.dumps(out))
 
 

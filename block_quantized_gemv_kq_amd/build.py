@@ -35,6 +35,10 @@ ARCH = "gfx950"
 
 HOST_SOURCES = ["kq_api.cpp", "kq_pack.cpp"]
 HIP_SOURCES = ["kq_gemv.hip", "kq_mfma.hip", "kq_moe.hip", "kq_misc.hip", "kq_stack.hip"]
+# Measurement only: a read-only streaming kernel for the benchmark's ceiling,
+# in a library of its own that the GEMV library never loads.
+PROBE_SOURCES = ["kq_probe.hip"]
+PROBE_LIB = os.path.join(HERE, "libkq_probe.so")
 
 HOST_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-ffp-contract=off", "-Wall", "-Wextra",
               "-Wno-unused-parameter"]
@@ -66,7 +70,8 @@ def _compile(src, verbose):
 
 
 def build(verbose: bool = False, jobs: int | None = None) -> str:
-    """Compile every source and link libkq.so. Always rebuilds."""
+    """Compile every source and link libkq.so (and the benchmark's
+    libkq_probe.so). Always rebuilds."""
     os.makedirs(BUILD, exist_ok=True)
     srcs = [s for s in HOST_SOURCES + HIP_SOURCES if os.path.exists(os.path.join(CSRC, s))]
     jobs = jobs or min(len(srcs), max(1, min(16, os.cpu_count() or 1)))
@@ -77,6 +82,11 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
           "-L" + os.path.join(ROCM, "lib"), "-lamdhip64",
           "-Wl,-rpath," + os.path.join(ROCM, "lib"), "-lpthread"], verbose)
     os.replace(tmp, LIB)
+    pobjs = [_compile(s, verbose) for s in PROBE_SOURCES]
+    tmp = PROBE_LIB + ".tmp"
+    _run([shutil.which("g++") or "g++", "-shared", "-fPIC", "-o", tmp, *pobjs,
+          "-L" + os.path.join(ROCM, "lib"), "-lamdhip64", "-Wl,-rpath," + os.path.join(ROCM, "lib")], verbose)
+    os.replace(tmp, PROBE_LIB)
     return LIB
 
 
