@@ -57,6 +57,7 @@ const TuneName kTuneNames[] = {
     {"mfma_r", kq::TUNE_MFMA_R},                 {"mfma_waves", kq::TUNE_MFMA_WAVES},
     {"mfma_xf", kq::TUNE_MFMA_XF},               {"mfma_pers_tpw", kq::TUNE_MFMA_PERS_TPW},
     {"mfma_chunk_l2cg", kq::TUNE_MFMA_CHUNK_L2CG}, {"moe_unfused", kq::TUNE_MOE_UNFUSED},
+    {"moe_min_wg", kq::TUNE_MOE_MIN_WG},
 };
 
 // Parse a tuning value: force_path and mfma_variant take names, the others integers.

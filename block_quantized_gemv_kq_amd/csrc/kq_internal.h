@@ -27,6 +27,7 @@ enum TuneKey {
   TUNE_MFMA_PERS_TPW,    // persistent kernel: tiles per wave
   TUNE_MFMA_CHUNK_L2CG,  // chunked kernel: log2 of groups per chunk
   TUNE_MOE_UNFUSED,      // 1: one-token MoE down + weighted sum as two kernels
+  TUNE_MOE_MIN_WG,       // routed-expert kernels: widen lane groups below this many workgroups
   TUNE_COUNT
 };
 enum MfmaVariant { MV_PERS = 1, MV_TEAMS, MV_TEAMS_SX, MV_CHUNK, MV_CHUNK_WHOLE, MV_CHUNK_SPLIT, MV_DIRECT };

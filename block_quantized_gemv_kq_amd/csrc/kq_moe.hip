@@ -506,11 +506,34 @@ int moe_lds_log2g(int units) {
   return ilog2(G);
 }
 
+// Few routed slots (one token): widen the lane groups (fewer rows per wave,
+// fewer units per lane) while the per-slot grid of 4-wave workgroups is below
+// MOE_MIN_WG, so the weights of 8 experts are spread over more CUs. The rule
+// depends on the slot count, not on which slots are duplicates, so the fused
+// one-token down kernel and the per-slot kernel pick the same G (the same
+// per-row sums, bit for bit). The moe_min_wg tuning override replaces the
+// threshold (0 keeps the byte-per-lane choice).
+constexpr int MOE_MIN_WG = 512;
+
+template <int FMT>
+int moe_slot_log2g(int units, int64_t N, int P) {
+  int log2g = moe_lds_log2g<FMT>(units);
+  const int tv = tune(TUNE_MOE_MIN_WG);
+  const int64_t min_wg = tv != TUNE_UNSET ? tv : MOE_MIN_WG;
+  while (log2g < 6 && ((units + (1 << log2g) - 1) >> log2g) > 1) {
+    const int64_t rpw = 64 >> log2g;
+    const int64_t wg = ((N + rpw - 1) / rpw + 3) / 4 * P;
+    if (wg >= min_wg) break;
+    ++log2g;
+  }
+  return log2g;
+}
+
 template <int FMT, bool GATE_UP>
 int launch_moe_lds(const uint8_t* W0, const uint8_t* W1, const uint16_t* x, const int32_t* ids, void* out, int64_t N,
                    int64_t K, int M, int top_k, int n_experts, int x_per_slot, int64_t eb, hipStream_t stream) {
   const int units = (int)(K / (32 * Fmt<FMT>::UB));
-  const int log2g = moe_lds_log2g<FMT>(units);
+  const int log2g = moe_slot_log2g<FMT>(units, N, M * top_k);
   const int iters = (units + (1 << log2g) - 1) >> log2g;
   const int64_t rpw = 64 >> log2g;
   const int64_t waves = (N + rpw - 1) / rpw;
@@ -574,7 +597,7 @@ template <int FMT>
 int launch_moe_down_sum_fmt(const MoeArgs& a, const float* rw, float* y) {
   const int64_t eb = a.N * (a.K / 32) * Fmt<FMT>::BB;
   const int units = (int)(a.K / (32 * Fmt<FMT>::UB));
-  const int log2g = moe_lds_log2g<FMT>(units);
+  const int log2g = moe_slot_log2g<FMT>(units, a.N, a.M * a.top_k);
   const int iters = (units + (1 << log2g) - 1) >> log2g;
   const int64_t rpw = 64 >> log2g;
   const dim3 grid((unsigned)((a.N + rpw - 1) / rpw)), block((unsigned)(64 * a.top_k));
