@@ -374,7 +374,7 @@ def bench_small_stack(torch, kq, S, steps):
     return out
 
 
-VERIFY_INVARIANT_M = (4, 8)   # verify widths also timed through kq_gemv_invariant
+VERIFY_INVARIANT_M = (4, 8, 16, 48)   # verify widths also timed through kq_gemv_invariant
 
 
 def bench_verify_all(torch, kq, S, ds, t1_ms, steps):
@@ -398,11 +398,24 @@ def bench_verify_all(torch, kq, S, ds, t1_ms, steps):
             ms2 = float(np.median(per2))
             out[str(M)]["invariant"] = {"entry": "kq_gemv_invariant", "ms_per_pass": ms2,
                                         "gbps": dv.alg_bytes / (ms2 * 1e-3) / 1e9, "t_ratio_vs_m1": ms2 / t1_ms,
+                                        "ratio_vs_kq_gemv": ms2 / ms,
                                         "tokens_per_s_upper_bound": M / (ms2 * 1e-3)}
             log(f"verify M={M} batch-invariant: {ms2 * 1000:.1f} us per pass, t(M)/t(1) = {ms2 / t1_ms:.2f}")
             del g2
         del g, dv
         torch.cuda.empty_cache()
+    # decode (one column) through the batch-invariant entry point: the bits a
+    # verify pass through it reproduces
+    dv = ds.with_columns(S, 1, S.VERIFY_WORKLOAD_ID)
+    dv.invariant = True
+    g = capture(torch, dv.step)
+    per, _, _ = time_graph(torch, g, steps, 3)
+    ms = float(np.median(per))
+    out["1_invariant"] = {"entry": "kq_gemv_invariant", "M": 1, "ms_per_pass": ms, "t_ratio_vs_m1": ms / t1_ms,
+                          "gbps": dv.alg_bytes / (ms * 1e-3) / 1e9, "tokens_per_s": 1 / (ms * 1e-3)}
+    log(f"decode M=1 batch-invariant: {ms * 1000:.1f} us per token, {ms / t1_ms:.2f} x kq_gemv")
+    del g, dv
+    torch.cuda.empty_cache()
     return out
 
 

@@ -461,32 +461,14 @@ int launch_gemv(const GemvArgs& a) {
 
 namespace {
 
-// Batch-invariant dispatch: the kernel that `dispatch` picks for one column,
-// run over all M columns. Each of these kernels sums a column in an order
-// that depends on N and K only (the lane-group size, units per lane and
-// passes of the LDS and register-x kernels come from N and K; the generic
-// kernel loops over columns), so column m gets the bits of an M = 1 call.
+// Batch-invariant dispatch: the matrix-core kernels with configurations that
+// depend on N and K only, for every M including 1, so column m gets the bits
+// of a one-column call of this entry point. Rows of 2-byte-aligned blocks take
+// the generic kernel, which loops over the columns (also invariant).
 template <int FMT>
 int dispatch_invariant(const GemvArgs& a) {
   if (a.K % (32 * Fmt<FMT>::UB) != 0) return launch_generic<FMT>(a);
-  const int64_t col_bytes = a.K * 2 + a.K / 4;   // x and block sums of one column in LDS
-  if (col_bytes > LDS_MAX_BYTES) return launch_valu<FMT>(a);
-  const int64_t fit = LDS_MAX_BYTES / col_bytes;
-  const int max_mt = fit < LDS_MAX_MT ? (int)fit : LDS_MAX_MT;
-  const int units = (int)(a.K / (32 * Fmt<FMT>::UB));
-  const LdsCfg c = lds_cfg(a.N, units, Fmt<FMT>::BB * Fmt<FMT>::UB);
-  for (int m0 = 0; m0 < a.M; m0 += max_mt) {
-    const int mt = a.M - m0 < max_mt ? a.M - m0 : max_mt;
-    int err;
-    switch (mt) {
-      case 1: err = launch_lds_mt<FMT, 1>(a, m0, c); break;
-      case 2: err = launch_lds_mt<FMT, 2>(a, m0, c); break;
-      case 3: err = launch_lds_mt<FMT, 3>(a, m0, c); break;
-      default: err = launch_lds_mt<FMT, 4>(a, m0, c); break;
-    }
-    if (err) return err;
-  }
-  return 0;
+  return launch_gemv_mfma_invariant(a);
 }
 
 }  // namespace

@@ -65,6 +65,9 @@ int64_t gemv_argmax_fused_parts(const GemvArgs& a);
 // current device (KQ_NOALLOC_SCRATCH_BYTES; the caller checks the size).
 int launch_gemv_argmax_noalloc(const GemvArgs& a, int32_t* out);
 int launch_gemv_mfma(const GemvArgs& a);
+// The matrix-core GEMV with every configuration chosen from N and K alone
+// (batch-invariant columns).
+int launch_gemv_mfma_invariant(const GemvArgs& a);
 
 struct MoeArgs {
   int fmt;

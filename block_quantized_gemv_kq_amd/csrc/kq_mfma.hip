@@ -1184,7 +1184,61 @@ int launch_mfma_fmt(const GemvArgs& a) {
   return 0;
 }
 
+// Batch-invariant matrix-core GEMV: every launch configuration is chosen from
+// N and K alone, so a column's sum (the groups each wave takes, the order of
+// the matrix-core products and scale FMAs, the fixed-order sum over the waves
+// of a tile) is the same whatever M is; M only sets how many operand rows hold
+// real columns (a matrix-core product's output element depends on its own row
+// and column alone). Persistent waves (many tiles: each wave sums a tile's
+// groups in order, no split) and the chunked and per-wave kernels (their
+// configuration does not involve M) take columns 16 at a time; the split-K
+// teams kernel takes them 8 at a time with the configuration it has at 8
+// columns (the verify width), staged for as many as are real.
+constexpr int INV_TEAMS_COLS = 8;
+
+template <int FMT>
+int launch_mfma_invariant_fmt(const GemvArgs& a) {
+  const int64_t tiles = (a.N + 15) / 16;
+  const int ngroups = (int)((a.K / 32 + 3) / 4);
+  const bool pers = tiles >= MFMA_PERS_MIN_TILES && mfma_x_lds_bytes(a.K, 4, true) <= MFMA_LDS_MAX_BYTES &&
+                    mfma_x_pieces(ngroups, 4) <= (int64_t)XST_MAX * 512;
+  const MfmaLdsCfg teams = mfma_lds_cfg(a.N, a.K, INV_TEAMS_COLS, MfmaLdsMaxP<FMT>::v, true);
+  const int width = (!pers && teams.ok) ? INV_TEAMS_COLS : 16;
+  for (int m0 = 0; m0 < a.M; m0 += width) {
+    const int mt = a.M - m0 < width ? a.M - m0 : width;
+    int log2mp = 0;
+    while ((1 << log2mp) < mt) ++log2mp;
+    int err;
+    if (pers) {
+      GemvArgs b = a;
+      b.x = a.x + (int64_t)m0 * a.K;
+      b.y = a.y + (int64_t)m0 * a.N;
+      b.M = mt;
+      err = launch_mfma_pers_p<FMT, MfmaPersP<FMT>::v, true>(b, log2mp, (size_t)mfma_x_lds_bytes(a.K, log2mp, true));
+    } else if (teams.ok) {
+      MfmaLdsCfg c = teams;
+      c.log2mp = log2mp;
+      const int64_t xb = mfma_x_lds_bytes(a.K, log2mp, c.sx), rb = (int64_t)c.R * c.S * 64 * 16;
+      c.lds = (size_t)(xb > rb ? xb : rb);
+      err = launch_mfma_lds<FMT>(a, m0, mt, c);
+    } else {
+      err = launch_mfma_chunk<FMT, 1>(a, m0, mt);
+      if (err == -1) err = launch_mfma_t<FMT, 1>(a, m0, mt);
+    }
+    if (err) return err;
+  }
+  return 0;
+}
+
 }  // namespace
+
+int launch_gemv_mfma_invariant(const GemvArgs& a) {
+  switch (a.fmt) {
+    case KQ_Q8_0: return launch_mfma_invariant_fmt<F_Q8_0>(a);
+    case KQ_Q4_0: return launch_mfma_invariant_fmt<F_Q4_0>(a);
+    default: return launch_mfma_invariant_fmt<F_AFFINE4>(a);
+  }
+}
 
 int launch_gemv_mfma(const GemvArgs& a) {
   switch (a.fmt) {

@@ -135,13 +135,17 @@ int kq_gemv(int fmt, const void* W, const uint16_t* x, float* y,
             int64_t N, int64_t K, int M, void* stream);
 
 /* kq_gemv_invariant — the product of kq_gemv, batch-invariant: column m of y
- * has the same bits as kq_gemv returns for column m alone (M = 1), whatever M
- * is (Kinetic docs, "What makes it fast": every row of a batch is summed in
- * the order that token would be summed on its own). It runs the one-column
- * kernel over the M columns, up to 4 (LDS-staged rows) or 8 (other rows) per
- * pass, so the weights are read once per pass, not once per call; use kq_gemv
- * when a tolerance is enough. Arguments, layout, ownership, determinism and
- * errors as kq_gemv. */
+ * has the same bits as kq_gemv_invariant returns for column m alone (M = 1),
+ * whatever M is (Kinetic docs, "What makes it fast": every row of a batch is
+ * summed in the order that token would be summed on its own, so checking
+ * eight guesses at once gives the bits of plain decoding). It runs the
+ * matrix-core kernels with every launch configuration chosen from N and K
+ * alone, for every M including 1: columns go 8 at a time through the split-K
+ * kernel (the weights are read once per 8 columns) and 16 at a time through
+ * the others (vocabulary-sized outputs, long rows); rows of 2-byte-aligned
+ * blocks (an odd number of Q4_0/Q8_0 blocks) take a generic kernel. Its bits
+ * differ from kq_gemv's (another summation order), both within the same
+ * tolerance. Arguments, layout, ownership, determinism and errors as kq_gemv. */
 int kq_gemv_invariant(int fmt, const void* W, const uint16_t* x, float* y,
                       int64_t N, int64_t K, int M, void* stream);
 
