@@ -19,8 +19,22 @@ affine4 gs32 (20 bytes): fp16 scale ``s``, fp16 bias ``b``, 16 bytes of quants.
     s = fp16((hi - lo) / 15), b = fp16(lo)
     q_j = clamp(round((w_j - b) / s), 0, 15), or 0 for every j when s == 0
     w' = s * q + b
-Both 4-bit formats keep element j in the low nibble of byte j and element j+16
-in the high nibble. Scales and biases are little-endian fp16 ahead of the quants.
+Q5_0 (22 bytes): fp16 scale ``d``, 4 bytes of fifth bits, 16 bytes of low nibbles.
+    m = w_i for the FIRST index i that maximises |w_i| (the signed maximum)
+    d = fp16(m / -16)
+    q_j = clamp(round(w_j / d) + 16, 0, 31), or 16 for every j when d == 0
+    w' = d * (q - 16)
+Q5_1 (24 bytes): fp16 scale ``d``, fp16 minimum ``m``, 4 bytes of fifth bits,
+16 bytes of low nibbles.
+    lo = min_j w_j, hi = max_j w_j   (first index on ties)
+    d = fp16((hi - lo) / 31), m = fp16(lo)
+    q_j = clamp(round((w_j - m) / d), 0, 31), or 0 for every j when d == 0
+    w' = d * q + m
+All 4-bit nibble areas keep element j in the low nibble of byte j and element
+j+16 in the high nibble (the 5-bit formats keep the low four bits of q there);
+the 5-bit formats keep bit 4 of q_j in bit j of a little-endian 32-bit word
+ahead of the nibbles. Scales and biases are little-endian fp16 ahead of the
+quants.
 
 Readings of points the definitions leave open (each is pinned by a hand-worked
 block in tests/golden/):
@@ -31,15 +45,19 @@ block in tests/golden/):
 * Non-finite weights, or a scale/bias that overflows fp16, are rejected.
 
 The 4-bit formats are the ones the Kipp README, "How fast" contrasts (affine4
-carries a bias term, Q4_0 is scale-only); Q8_0 and Q4_0 are among the GGUF
-weight formats the Kinetic docs, "Supported models" list.
+carries a bias term, Q4_0 is scale-only); Q8_0, Q4_0, Q5_0 and Q5_1 are among
+the GGUF weight formats the Kinetic docs, "Supported models" list. The pages
+print no layout or quantizer for any of them: the 5-bit definitions above are
+this library's reading (Q5_0 is Q4_0 with sixteen levels either side of zero,
+Q5_1 is affine4 with 31 steps, each with the fifth bits in a word of their
+own), with the same rounding, tie and zero-scale rules as the 4-bit formats.
 """
 from __future__ import annotations
 
 import numpy as np
 
 BLOCK = 32
-BLOCK_BYTES = {"q8_0": 34, "q4_0": 18, "affine4": 20}
+BLOCK_BYTES = {"q8_0": 34, "q4_0": 18, "affine4": 20, "q5_0": 22, "q5_1": 24}
 FORMATS = tuple(BLOCK_BYTES)
 
 
@@ -95,6 +113,8 @@ def quantize(fmt: str, W: np.ndarray) -> dict:
     q8_0: {"d": f16[N,B], "q": int8[N,B,32]}
     q4_0: {"d": f16[N,B], "q": uint8[N,B,32] (0..15)}
     affine4: {"s": f16[N,B], "b": f16[N,B], "q": uint8[N,B,32] (0..15)}
+    q5_0: {"d": f16[N,B], "q": uint8[N,B,32] (0..31)}
+    q5_1: {"d": f16[N,B], "m": f16[N,B], "q": uint8[N,B,32] (0..31)}
     with B = K/32."""
     X = _blocks(W)
     with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
@@ -128,6 +148,27 @@ def quantize(fmt: str, W: np.ndarray) -> dict:
             q = np.clip(round_half_away(ratio), 0, 15)
             q = np.where((s32 == 0)[..., None], 0, q).astype(np.uint8)
             return {"s": s, "b": b, "q": q}
+        if fmt == "q5_0":
+            m = _first_index_value(X, np.abs(X), pick_max=True)  # signed max
+            d = to_f16(m / np.float32(-16.0))
+            _check_finite16(d)
+            d32 = d.astype(np.float32)
+            ratio = X / d32[..., None]
+            q = np.clip(round_half_away(ratio) + 16, 0, 31)
+            q = np.where((d32 == 0)[..., None], 16, q).astype(np.uint8)
+            return {"d": d, "q": q}
+        if fmt == "q5_1":
+            lo = _first_index_value(X, X, pick_max=False)
+            hi = _first_index_value(X, X, pick_max=True)
+            d = to_f16((hi - lo) / np.float32(31.0))
+            m = to_f16(lo)
+            _check_finite16(d, m)
+            d32 = d.astype(np.float32)
+            m32 = m.astype(np.float32)
+            ratio = (X - m32[..., None]) / d32[..., None]
+            q = np.clip(round_half_away(ratio), 0, 31)
+            q = np.where((d32 == 0)[..., None], 0, q).astype(np.uint8)
+            return {"d": d, "m": m, "q": q}
     raise ValueError(f"unknown format {fmt!r}")
 
 
@@ -139,6 +180,19 @@ def _nibbles(q: np.ndarray) -> np.ndarray:
 
 def _unnibble(nb: np.ndarray) -> np.ndarray:
     return np.concatenate([nb & 0x0F, nb >> 4], axis=-1).astype(np.uint8)
+
+
+def _high_bits(q: np.ndarray) -> np.ndarray:
+    """uint8[..., 32] 5-bit quants -> uint8[..., 4]: bit j of the
+    little-endian 32-bit word is bit 4 of q_j."""
+    h = ((q.astype(np.uint64) >> 4) & 1) << np.arange(32, dtype=np.uint64)
+    word = h.sum(axis=-1).astype(np.uint32)
+    return np.stack([((word >> (8 * i)) & 0xFF).astype(np.uint8) for i in range(4)], axis=-1)
+
+
+def _unhigh_bits(b4: np.ndarray) -> np.ndarray:
+    word = sum(b4[..., i].astype(np.uint32) << (8 * i) for i in range(4))
+    return ((word[..., None] >> np.arange(32, dtype=np.uint32)) & 1).astype(np.uint8)
 
 
 def _f16_bytes(h: np.ndarray) -> np.ndarray:
@@ -159,6 +213,11 @@ def encode(fmt: str, fields: dict) -> np.ndarray:
         parts = [_f16_bytes(fields["d"]), _nibbles(fields["q"])]
     elif fmt == "affine4":
         parts = [_f16_bytes(fields["s"]), _f16_bytes(fields["b"]), _nibbles(fields["q"])]
+    elif fmt == "q5_0":
+        parts = [_f16_bytes(fields["d"]), _high_bits(fields["q"]), _nibbles(fields["q"] & 0x0F)]
+    elif fmt == "q5_1":
+        parts = [_f16_bytes(fields["d"]), _f16_bytes(fields["m"]), _high_bits(fields["q"]),
+                 _nibbles(fields["q"] & 0x0F)]
     else:
         raise ValueError(f"unknown format {fmt!r}")
     blk = np.concatenate(parts, axis=-1)
@@ -178,6 +237,12 @@ def decode(fmt: str, packed: np.ndarray, n: int, k: int) -> dict:
     if fmt == "affine4":
         return {"s": _bytes_f16(blk[..., 0:2]), "b": _bytes_f16(blk[..., 2:4]),
                 "q": _unnibble(blk[..., 4:20])}
+    if fmt == "q5_0":
+        return {"d": _bytes_f16(blk[..., 0:2]),
+                "q": (_unnibble(blk[..., 6:22]) | (_unhigh_bits(blk[..., 2:6]) << 4)).astype(np.uint8)}
+    if fmt == "q5_1":
+        return {"d": _bytes_f16(blk[..., 0:2]), "m": _bytes_f16(blk[..., 2:4]),
+                "q": (_unnibble(blk[..., 8:24]) | (_unhigh_bits(blk[..., 4:8]) << 4)).astype(np.uint8)}
     raise ValueError(f"unknown format {fmt!r}")
 
 
@@ -196,6 +261,11 @@ def dequantize(fmt: str, fields: dict, rows: slice | None = None) -> np.ndarray:
     elif fmt == "affine4":
         w = (fields["s"][sl].astype(np.float64)[..., None] * q
              + fields["b"][sl].astype(np.float64)[..., None])
+    elif fmt == "q5_0":
+        w = fields["d"][sl].astype(np.float64)[..., None] * (q - 16.0)
+    elif fmt == "q5_1":
+        w = (fields["d"][sl].astype(np.float64)[..., None] * q
+             + fields["m"][sl].astype(np.float64)[..., None])
     else:
         raise ValueError(f"unknown format {fmt!r}")
     n, nb, _ = w.shape

@@ -77,6 +77,10 @@ def _exact_wprime(fmt, fields):
                     v = Fraction(float(fields["d"][r, b])) * qq
                 elif fmt == "q4_0":
                     v = Fraction(float(fields["d"][r, b])) * (qq - 8)
+                elif fmt == "q5_0":
+                    v = Fraction(float(fields["d"][r, b])) * (qq - 16)
+                elif fmt == "q5_1":
+                    v = Fraction(float(fields["d"][r, b])) * qq + Fraction(float(fields["m"][r, b]))
                 else:
                     v = Fraction(float(fields["s"][r, b])) * qq + Fraction(float(fields["b"][r, b]))
                 out[r][b * 32 + j] = v
@@ -288,6 +292,52 @@ def test_affine4_roundtrip(seed):
     assert np.all(np.take_along_axis(q, np.argmax(X, -1)[..., None], -1) == 15)
     err = np.abs(X - (s * q + b))
     assert np.all(err <= s / 2 * (1 + 2.0 ** -9) + np.abs(b - lo) + 1e-12)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_q5_0_roundtrip(seed):
+    W = S.weights((93, seed, 0, 0), 64, 512)
+    f = F.quantize("q5_0", W)
+    q = f["q"].astype(np.int32)
+    d = f["d"].astype(np.float64)
+    X = W.reshape(64, 16, 32).astype(np.float64)
+    assert q.min() >= 0 and q.max() <= 31
+    istar = np.argmax(np.abs(X), axis=-1)
+    assert np.all(np.take_along_axis(q, istar[..., None], -1) == 0)
+    err = np.abs(X - d[..., None] * (q - 16))
+    # as Q4_0 with 16 levels: the opposite side of the signed maximum can
+    # reach w/d = 16(1+2^-11) and clamps to q = 31
+    clamped = (q == 31) & (X / d[..., None] > 15.5)
+    bound = np.abs(d)[..., None] / 2 * (1 + 2.0 ** -10)
+    assert np.all((err <= bound) | (clamped & (err <= (1 + 2.0 ** -8) * np.abs(d)[..., None])))
+    assert np.array_equal(F.pack("q5_0", F.dequantize("q5_0", f).astype(np.float32)), F.encode("q5_0", f))
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_q5_1_roundtrip(seed):
+    W = S.weights((92, seed, 0, 0), 64, 512)
+    f = F.quantize("q5_1", W)
+    q = f["q"].astype(np.int32)
+    d = f["d"].astype(np.float64)[..., None]
+    m = f["m"].astype(np.float64)[..., None]
+    X = W.reshape(64, 16, 32).astype(np.float64)
+    lo = X.min(-1, keepdims=True)
+    assert q.min() >= 0 and q.max() <= 31
+    assert np.all(np.take_along_axis(q, np.argmin(X, -1)[..., None], -1) == 0)
+    assert np.all(np.take_along_axis(q, np.argmax(X, -1)[..., None], -1) == 31)
+    err = np.abs(X - (d * q + m))
+    assert np.all(err <= d / 2 * (1 + 2.0 ** -9) + np.abs(m - lo) + 1e-12)
+
+
+def test_fifth_bits_word_layout():
+    """Bit j of the little-endian word after the scale(s) is bit 4 of q_j:
+    q with only element 9 at 16 (Q5_0) gives the word 0x00000200."""
+    f = {"d": np.array([[1.0]], np.float16), "q": np.full((1, 1, 32), 0, np.uint8)}
+    f["q"][0, 0, 9] = 16
+    b = F.encode("q5_0", f)[0]
+    assert b[2:6].tolist() == [0x00, 0x02, 0x00, 0x00]
+    assert b[6:22].tolist() == [0] * 16
+    assert np.array_equal(F.decode("q5_0", b, 1, 32)["q"], f["q"])
 
 
 def test_encode_decode_inverse():

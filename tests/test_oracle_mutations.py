@@ -164,3 +164,62 @@ def test_abs_of_sum_instead_of_sum_of_abs_is_caught(monkeypatch):
         return y, np.abs(y)
     monkeypatch.setattr(R, "gemv", bad)
     assert _fails(T.check_abs_dot, "affine4")
+
+
+def test_reversed_fifth_bit_order_is_caught(monkeypatch):
+    orig_h, orig_u = F._high_bits, F._unhigh_bits
+    monkeypatch.setattr(F, "_high_bits", lambda q: orig_h(q[..., ::-1]))
+    monkeypatch.setattr(F, "_unhigh_bits", lambda b4: orig_u(b4)[..., ::-1])
+    assert _any_golden_fails("q5_0") and _any_golden_fails("q5_1")
+
+
+def test_dropped_fifth_bit_is_caught(monkeypatch):
+    orig = F.decode
+
+    def bad(fmt, packed, n, k):
+        f = orig(fmt, packed, n, k)
+        if fmt in ("q5_0", "q5_1"):
+            f = dict(f)
+            f["q"] = f["q"] & 0x0F
+        return f
+    monkeypatch.setattr(F, "decode", bad)
+    assert _any_golden_fails("q5_0") and _any_golden_fails("q5_1")
+
+
+def test_q5_0_offset_15_is_caught(monkeypatch):
+    orig = F.dequantize
+
+    def bad(fmt, fields, rows=None):
+        if fmt == "q5_0":
+            f2 = dict(fields)
+            f2["q"] = fields["q"].astype(np.int32) + 1      # w' = d*(q-15)
+            return orig(fmt, f2, rows)
+        return orig(fmt, fields, rows)
+    monkeypatch.setattr(F, "dequantize", bad)
+    assert _fails(T.check_unit_vectors, "q5_0")
+
+
+def test_q5_1_dropped_minimum_is_caught(monkeypatch):
+    orig = F.dequantize
+
+    def bad(fmt, fields, rows=None):
+        if fmt == "q5_1":
+            f2 = dict(fields)
+            f2["m"] = np.zeros_like(fields["m"])
+            return orig(fmt, f2, rows)
+        return orig(fmt, fields, rows)
+    monkeypatch.setattr(F, "dequantize", bad)
+    assert _fails(T.check_unit_vectors, "q5_1")
+
+
+def test_q5_1_fifteen_steps_is_caught(monkeypatch):
+    # the 4-bit step (hi - lo) / 15 planted in the 5-bit format
+    orig = F.quantize
+
+    def bad(fmt, W):
+        if fmt != "q5_1":
+            return orig(fmt, W)
+        f = orig("affine4", W)
+        return {"d": f["s"], "m": f["b"], "q": f["q"]}
+    monkeypatch.setattr(F, "quantize", bad)
+    assert _any_golden_fails("q5_1")
