@@ -27,7 +27,9 @@ int ok() {
   return KQ_OK;
 }
 
-bool valid_fmt(int fmt) { return fmt == KQ_Q8_0 || fmt == KQ_Q4_0 || fmt == KQ_AFFINE4_G32; }
+bool valid_fmt(int fmt) {
+  return fmt == KQ_Q8_0 || fmt == KQ_Q4_0 || fmt == KQ_AFFINE4_G32 || fmt == KQ_Q5_0 || fmt == KQ_Q5_1;
+}
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -265,8 +267,8 @@ int kq_moe_ffn(int fmt, const void* W_gate, const void* W_up, const void* W_down
   if (st) return st;
   if ((st = check_moe_common(fmt, W_down, hidden, inter, M, top_k, n_experts))) return st;
   if (!aligned(W_up, 4)) return fail(KQ_ERR_ALIGN, "W_up must be 4-byte aligned");
-  if (fmt != KQ_AFFINE4_G32 && hidden % 64 != 0)
-    return fail(KQ_ERR_SHAPE, "kq_moe_ffn: Q8_0/Q4_0 need hidden %% 64 == 0");
+  if (fmt != KQ_AFFINE4_G32 && fmt != KQ_Q5_1 && hidden % 64 != 0)
+    return fail(KQ_ERR_SHAPE, "kq_moe_ffn: Q8_0/Q4_0/Q5_0 need hidden %% 64 == 0");
   if (M == 0 || hidden == 0 || inter == 0) return ok();
   if (!W_gate || !W_up || !W_down || !x || !route_ids || !route_w || !y)
     return fail(KQ_ERR_ARG, "kq_moe_ffn: null pointer");
@@ -329,6 +331,8 @@ int check_stages(const kq_stage* stages, int n, ChainLayout& L) {
     const kq_stage& s = stages[i];
     int st = check_fmt_k(s.fmt, s.K);
     if (st) return fail(st, "stage %d: %s", i, kq_last_error());
+    if (s.fmt == KQ_Q5_0 || s.fmt == KQ_Q5_1)
+      return fail(KQ_ERR_FORMAT, "stage %d: the persistent chain takes Q8_0, Q4_0 and affine4 only", i);
     if (s.reserved != 0) return fail(KQ_ERR_ARG, "stage %d: reserved must be 0", i);
     if (s.N < 1 || s.N > KQ_MAX_N) return fail(KQ_ERR_ARG, "stage %d: N=%lld out of range", i, (long long)s.N);
     if (!s.W || !s.x || !s.y) return fail(KQ_ERR_ARG, "stage %d: null pointer", i);

@@ -14,6 +14,10 @@
 //   Q8_0    (bytes q ^ 0x80 = q + 128):  sum (1152 + q) x = sum q x + 1152 sx
 //   Q4_0    (nibble q):                  sum (1024 + q) x = sum (q - 8) x + 1032 sx
 //   affine4 (nibble q):                  sum (1024 + q) x = sum q x + 1024 sx
+//   Q5_0    (nibble | fifth bit << 4):   sum (1024 + q) x = sum (q - 16) x + 1040 sx
+//   Q5_1    (nibble | fifth bit << 4):   sum (1024 + q) x = sum q x + 1024 sx
+// (1024 + q stays exact in fp16 for q < 1024; the fifth bit is OR-ed into bit 4
+// of each half, or bit 8 where the high nibble is kept in place as 16 q.)
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -23,9 +27,11 @@ namespace kqd {
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
-enum { F_Q8_0 = 0, F_Q4_0 = 1, F_AFFINE4 = 2 };
+enum { F_Q8_0 = 0, F_Q4_0 = 1, F_AFFINE4 = 2, F_Q5_0 = 3, F_Q5_1 = 4 };
 
 // BB: bytes per block; UB: blocks per load unit (smallest dword-aligned group);
 // UDW: dwords per unit.
@@ -33,6 +39,22 @@ template <int FMT> struct Fmt;
 template <> struct Fmt<F_AFFINE4> { static constexpr int BB = 20, UB = 1, UDW = 5; };
 template <> struct Fmt<F_Q4_0> { static constexpr int BB = 18, UB = 2, UDW = 9; };
 template <> struct Fmt<F_Q8_0> { static constexpr int BB = 34, UB = 2, UDW = 17; };
+template <> struct Fmt<F_Q5_0> { static constexpr int BB = 22, UB = 2, UDW = 11; };
+template <> struct Fmt<F_Q5_1> { static constexpr int BB = 24, UB = 1, UDW = 6; };
+
+// Per-format constants of the fix-up: the offset removed from the 1024 + q
+// halves (per half of a block in the split form, where the high nibbles stand
+// for 16 q and their offset is divided by 16 with them) and whether a bias
+// (affine4's b, Q5_1's m) times the block's activation sum is added.
+template <int FMT> struct Fix;
+template <> struct Fix<F_Q8_0> { static constexpr float lo = -1152.0f, hi = -1152.0f; static constexpr bool bias = false; };
+template <> struct Fix<F_Q4_0> { static constexpr float lo = -1032.0f, hi = -1152.0f; static constexpr bool bias = false; };
+template <> struct Fix<F_AFFINE4> { static constexpr float lo = -1024.0f, hi = -1024.0f; static constexpr bool bias = true; };
+template <> struct Fix<F_Q5_0> { static constexpr float lo = -1040.0f, hi = -1280.0f; static constexpr bool bias = false; };
+template <> struct Fix<F_Q5_1> { static constexpr float lo = -1024.0f, hi = -1024.0f; static constexpr bool bias = true; };
+
+// Formats the matrix-core kernels take (the others run on the VALU kernels).
+template <int FMT> constexpr bool has_mfma() { return FMT == F_Q8_0 || FMT == F_Q4_0 || FMT == F_AFFINE4; }
 
 constexpr uint32_t MAGIC = 0x64646464u;   // four 0x64 bytes: high byte of fp16 1024
 constexpr uint32_t SEL_LO = 0x04010400u;  // (u0, 64, u1, 64) -> fp16 pair (1024+u0, 1024+u1)
@@ -119,10 +141,12 @@ __device__ __forceinline__ uint32_t ld32(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }
 
-// Load one unit (UB blocks, UDW dwords) at byte offset `off` (4-aligned).
+// Load one unit (UB blocks, UDW dwords) at byte offset `off` (4-aligned):
+// 16-byte pieces, then one 4-, 8- or 12-byte load for the rest.
 template <int FMT>
 __device__ __forceinline__ void load_unit(rsrc_t r, uint32_t off, uint32_t* D) {
   constexpr int NV = Fmt<FMT>::UDW / 4;  // full 16-byte pieces
+  constexpr int REM = Fmt<FMT>::UDW % 4;
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
     const u32x4 t = ld128(r, off + 16u * v);
@@ -131,7 +155,41 @@ __device__ __forceinline__ void load_unit(rsrc_t r, uint32_t off, uint32_t* D) {
     D[4 * v + 2] = t.z;
     D[4 * v + 3] = t.w;
   }
-  D[Fmt<FMT>::UDW - 1] = ld32(r, off + 16u * NV);
+  if constexpr (REM == 1) {
+    D[4 * NV] = ld32(r, off + 16u * NV);
+  } else if constexpr (REM == 2) {
+    const u32x2v t = __builtin_amdgcn_raw_buffer_load_b64(r, off + 16u * NV, 0, 0);
+    D[4 * NV] = t.x;
+    D[4 * NV + 1] = t.y;
+  } else if constexpr (REM == 3) {
+    const u32x3 t = __builtin_amdgcn_raw_buffer_load_b96(r, off + 16u * NV, 0, 0);
+    D[4 * NV] = t.x;
+    D[4 * NV + 1] = t.y;
+    D[4 * NV + 2] = t.z;
+  }
+}
+
+// One 5-bit block (2-byte-aligned halfwords at blk) against 32 fp16 x in fp32,
+// plain dequantization: the generic kernels for rows of 2-byte-aligned blocks.
+template <int FMT>
+__device__ __forceinline__ float q5_block_plain(const uint16_t* blk, const uint16_t* xb, float acc) {
+  constexpr int HB = FMT == F_Q5_0 ? 1 : 2;   // the fifth-bit word, in halfwords
+  const float s = h2f(blk[0]);
+  const float mn = FMT == F_Q5_1 ? h2f(blk[1]) : 0.0f;
+  const uint32_t qh = (uint32_t)blk[HB] | ((uint32_t)blk[HB + 1] << 16);
+  const uint16_t* nib = blk + HB + 2;
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t two = nib[j];
+    const int e = 2 * j;  // bytes 2j, 2j+1 hold elements 2j, 2j+16, 2j+1, 2j+17
+    const int el[4] = {e, e + 16, e + 1, e + 17};
+    const uint32_t q4[4] = {two & 15u, (two >> 4) & 15u, (two >> 8) & 15u, (two >> 12) & 15u};
+    for (int i = 0; i < 4; ++i) {
+      const int q = (int)(q4[i] | (((qh >> el[i]) & 1u) << 4));
+      const float w = FMT == F_Q5_1 ? __builtin_fmaf(s, (float)q, mn) : s * (float)(q - 16);
+      acc = __builtin_fmaf(w, h2f(xb[el[i]]), acc);
+    }
+  }
+  return acc;
 }
 
 // (value, index) pairs for the argmax: the larger value wins; on equal values
@@ -178,6 +236,22 @@ __device__ __forceinline__ void unpack_nibbles(const uint32_t (&n)[4], uint32_t*
   }
 }
 
+// The fifth bits of a 5-bit block (bit j of `qh` is bit 4 of q_j) into the
+// fp16 pairs of unpack_nibbles: bit 4 of each half, both halves of the block
+// shifted to 1024 + q. `hi_shift` is 4 there, 8 for the split form, whose
+// high-nibble halves stand for 16 q.
+__device__ __forceinline__ void add_fifth_bits(uint32_t qh, uint32_t* A, int hi_shift) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const uint32_t h = qh >> (4 * t);          // elements 4t..4t+3
+    A[2 * t] |= ((h & 1u) << 4) | ((h & 2u) << 19);
+    A[2 * t + 1] |= ((h & 4u) << 2) | ((h & 8u) << 17);
+    const uint32_t g = qh >> (16 + 4 * t);     // elements 16+4t..19+4t
+    A[8 + 2 * t] |= ((g & 1u) << hi_shift) | ((g & 2u) << (hi_shift + 15));
+    A[9 + 2 * t] |= ((g & 4u) << (hi_shift - 2)) | ((g & 8u) << (hi_shift + 13));
+  }
+}
+
 // Eight int8 dwords of one Q8_0 block -> 16 fp16 pairs (1152 + q).
 __device__ __forceinline__ void unpack_int8(const uint32_t (&q)[8], uint32_t* A) {
 #pragma unroll
@@ -186,6 +260,47 @@ __device__ __forceinline__ void unpack_int8(const uint32_t (&q)[8], uint32_t* A)
     A[2 * t] = perm(MAGIC, u, SEL_LO);
     A[2 * t + 1] = perm(MAGIC, u, SEL_HI);
   }
+}
+
+// Four nibble dwords -> 16 fp16 pairs, high nibbles shifted down (SPLIT
+// false) or kept in place as 16 q (SPLIT true).
+template <bool SPLIT>
+__device__ __forceinline__ void unpack_nibbles_t(const uint32_t (&n)[4], uint32_t* A) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const uint32_t lo = n[t] & 0x0F0F0F0Fu;
+    const uint32_t hi = SPLIT ? (n[t] & 0xF0F0F0F0u) : ((n[t] >> 4) & 0x0F0F0F0Fu);
+    A[2 * t] = perm(MAGIC, lo, SEL_LO);
+    A[2 * t + 1] = perm(MAGIC, lo, SEL_HI);
+    A[8 + 2 * t] = perm(MAGIC, hi, SEL_LO);
+    A[9 + 2 * t] = perm(MAGIC, hi, SEL_HI);
+  }
+}
+
+// Q5_0 unit (two 22-byte blocks, 11 dwords). Block a: d at bytes 0-1, fifth
+// bits 2-5, nibbles 6-21; block b: d at 22-23, fifth bits 24-27, nibbles 28-43.
+template <bool SPLIT>
+__device__ __forceinline__ void q5_0_unit(const uint32_t* D, uint32_t* A, float* scale, float* bias) {
+  const uint32_t na[4] = {alignbyte2(D[2], D[1]), alignbyte2(D[3], D[2]), alignbyte2(D[4], D[3]),
+                          alignbyte2(D[5], D[4])};
+  const uint32_t nb[4] = {D[7], D[8], D[9], D[10]};
+  unpack_nibbles_t<SPLIT>(na, A);
+  unpack_nibbles_t<SPLIT>(nb, A + 16);
+  add_fifth_bits(alignbyte2(D[1], D[0]), A, SPLIT ? 8 : 4);
+  add_fifth_bits(D[6], A + 16, SPLIT ? 8 : 4);
+  scale[0] = h2f(D[0]);
+  scale[1] = h2f(D[5] >> 16);
+  bias[0] = bias[1] = 0.0f;
+}
+
+// Q5_1 unit (one 24-byte block, 6 dwords): d, m, fifth bits, nibbles.
+template <bool SPLIT>
+__device__ __forceinline__ void q5_1_unit(const uint32_t* D, uint32_t* A, float* scale, float* bias) {
+  const uint32_t n[4] = {D[2], D[3], D[4], D[5]};
+  unpack_nibbles_t<SPLIT>(n, A);
+  add_fifth_bits(D[1], A, SPLIT ? 8 : 4);
+  scale[0] = h2f(D[0]);
+  bias[0] = h2f(D[0] >> 16);
 }
 
 // A unit unpacked: 16 * UB fp16 pairs, and per block the fp32 factors of the
@@ -214,6 +329,10 @@ __device__ __forceinline__ void unpack_unit(const uint32_t* D, Unpacked<FMT>& u)
     u.scale[0] = h2f(D[0]);
     u.scale[1] = h2f(D[4] >> 16);
     u.bias[0] = u.bias[1] = 0.0f;
+  } else if constexpr (FMT == F_Q5_0) {
+    q5_0_unit<false>(D, u.A, u.scale, u.bias);
+  } else if constexpr (FMT == F_Q5_1) {
+    q5_1_unit<false>(D, u.A, u.scale, u.bias);
   } else {
     // block a: d at bytes 0-1, quants 2-33; block b: d at 34-35, quants 36-67
     uint32_t qa[8], qb[8];
@@ -230,10 +349,7 @@ __device__ __forceinline__ void unpack_unit(const uint32_t* D, Unpacked<FMT>& u)
   }
 }
 
-template <int FMT> struct Offset;
-template <> struct Offset<F_AFFINE4> { static constexpr float v = -1024.0f; };
-template <> struct Offset<F_Q4_0> { static constexpr float v = -1032.0f; };
-template <> struct Offset<F_Q8_0> { static constexpr float v = -1152.0f; };
+template <int FMT> struct Offset { static constexpr float v = Fix<FMT>::lo; };
 
 // Dot of one block (16 pairs) with 16 activation dwords; add its
 // dequantized contribution to y.
@@ -243,9 +359,9 @@ __device__ __forceinline__ float block_dot(const uint32_t* A, const uint32_t* X,
   float acc = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc = dot2(A[i], X[i], acc);
-  const float t = __builtin_fmaf(Offset<FMT>::v, sx, acc);   // sum of (q or q-8) * x
+  const float t = __builtin_fmaf(Offset<FMT>::v, sx, acc);   // sum of (q, q-8 or q-16) * x
   y = __builtin_fmaf(scale, t, y);
-  if constexpr (FMT == F_AFFINE4) y = __builtin_fmaf(bias, sx, y);
+  if constexpr (Fix<FMT>::bias) y = __builtin_fmaf(bias, sx, y);
   return y;
 }
 
@@ -399,6 +515,10 @@ __device__ __forceinline__ void unpack_unit_split(const uint32_t* D, Unpacked<FM
     u.scale[0] = h2f(D[0]);
     u.scale[1] = h2f(D[4] >> 16);
     u.bias[0] = u.bias[1] = 0.0f;
+  } else if constexpr (FMT == F_Q5_0) {
+    q5_0_unit<true>(D, u.A, u.scale, u.bias);
+  } else if constexpr (FMT == F_Q5_1) {
+    q5_1_unit<true>(D, u.A, u.scale, u.bias);
   } else {
     unpack_unit<FMT>(D, u);
   }
@@ -422,15 +542,14 @@ __device__ __forceinline__ float block_dot_split(const uint32_t* A, const uint32
     for (int i = 0; i < 8; ++i) lo = dot2(A[i], X[i], lo);
 #pragma unroll
     for (int i = 8; i < 16; ++i) hi = dot2(A[i], X[i], hi);
-    // Q4_0: sum (q-8) x = (lo - 1032 sx_lo) + (hi - 1152 sx_hi) / 16
-    // affine4: sum q x  = (lo - 1024 sx_lo) + (hi - 1024 sx_hi) / 16
-    const float c_lo = FMT == F_Q4_0 ? -1032.0f : -1024.0f;
-    const float c_hi = FMT == F_Q4_0 ? -1152.0f : -1024.0f;
-    const float t_lo = __builtin_fmaf(c_lo, sx_lo, lo);
-    const float t_hi = __builtin_fmaf(c_hi, sx_hi, hi);
+    // Q4_0: sum (q-8) x  = (lo - 1032 sx_lo) + (hi - 1152 sx_hi) / 16
+    // Q5_0: sum (q-16) x = (lo - 1040 sx_lo) + (hi - 1280 sx_hi) / 16
+    // affine4, Q5_1: sum q x = (lo - 1024 sx_lo) + (hi - 1024 sx_hi) / 16
+    const float t_lo = __builtin_fmaf(Fix<FMT>::lo, sx_lo, lo);
+    const float t_hi = __builtin_fmaf(Fix<FMT>::hi, sx_hi, hi);
     y = __builtin_fmaf(scale, t_lo, y);
     y = __builtin_fmaf(scale * 0.0625f, t_hi, y);
-    if constexpr (FMT == F_AFFINE4) {
+    if constexpr (Fix<FMT>::bias) {
       y = __builtin_fmaf(bias, sx_lo, y);
       y = __builtin_fmaf(bias, sx_hi, y);
     }

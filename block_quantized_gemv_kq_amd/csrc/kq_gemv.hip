@@ -189,7 +189,9 @@ __global__ __launch_bounds__(256) void k_gemv_generic(const uint8_t* __restrict_
       const uint16_t* blk = reinterpret_cast<const uint16_t*>(W + row * row_bytes + (int64_t)b * Fmt<FMT>::BB);
       const uint16_t* xb = x + (int64_t)m * K + b * 32;
       const float s = h2f(blk[0]);
-      if constexpr (FMT == F_Q8_0) {
+      if constexpr (FMT == F_Q5_0 || FMT == F_Q5_1) {
+        acc = q5_block_plain<FMT>(blk, xb, acc);
+      } else if constexpr (FMT == F_Q8_0) {
         for (int j = 0; j < 16; ++j) {
           const uint32_t two = blk[1 + j];
           acc = __builtin_fmaf(s * (float)(int8_t)(two & 0xff), h2f(xb[2 * j]), acc);
@@ -437,6 +439,17 @@ int launch_generic(const GemvArgs& a) {
 
 template <int FMT>
 int dispatch(const GemvArgs& a) {
+  if constexpr (!has_mfma<FMT>()) {
+    // the 5-bit formats: the one-column kernels up to 3 columns, then the
+    // register-x kernel 8 columns per pass (weights read once per pass)
+    if (a.K % (32 * Fmt<FMT>::UB) != 0) return launch_generic<FMT>(a);
+    const int force = tune_int(TUNE_FORCE_PATH);
+    if (force == 'g') return launch_generic<FMT>(a);
+    const bool lds_ok = (int64_t)(a.M < LDS_MAX_MT ? a.M : LDS_MAX_MT) * (a.K * 2 + a.K / 4) <= LDS_MAX_BYTES;
+    if (force == 'v') return launch_valu<FMT>(a);
+    if (lds_ok && (force == 'l' || a.M < MFMA_MIN_M)) return launch_lds<FMT>(a);
+    return launch_valu<FMT>(a);
+  }
   if (a.K % (32 * Fmt<FMT>::UB) != 0) return a.M >= MFMA_MIN_M_UNALIGNED ? launch_gemv_mfma(a) : launch_generic<FMT>(a);
   const int force = tune_int(TUNE_FORCE_PATH);  // tests: run a given path at any shape
   if (force == 'g') return launch_generic<FMT>(a);
@@ -455,6 +468,8 @@ int launch_gemv(const GemvArgs& a) {
   switch (a.fmt) {
     case KQ_Q8_0: return dispatch<F_Q8_0>(a);
     case KQ_Q4_0: return dispatch<F_Q4_0>(a);
+    case KQ_Q5_0: return dispatch<F_Q5_0>(a);
+    case KQ_Q5_1: return dispatch<F_Q5_1>(a);
     default: return dispatch<F_AFFINE4>(a);
   }
 }
@@ -468,7 +483,31 @@ namespace {
 template <int FMT>
 int dispatch_invariant(const GemvArgs& a) {
   if (a.K % (32 * Fmt<FMT>::UB) != 0) return launch_generic<FMT>(a);
-  return launch_gemv_mfma_invariant(a);
+  if constexpr (has_mfma<FMT>()) {
+    return launch_gemv_mfma_invariant(a);
+  } else {
+    // 5-bit formats: the one-column VALU kernels over the columns, up to 4
+    // per pass through LDS (or 8 with x in registers for long rows); their
+    // lane groups, units per lane and passes come from N and K alone
+    const int64_t col_bytes = a.K * 2 + a.K / 4;   // x and block sums of one column in LDS
+    if (col_bytes > LDS_MAX_BYTES) return launch_valu<FMT>(a);
+    const int64_t fit = LDS_MAX_BYTES / col_bytes;
+    const int max_mt = fit < LDS_MAX_MT ? (int)fit : LDS_MAX_MT;
+    const int units = (int)(a.K / (32 * Fmt<FMT>::UB));
+    const LdsCfg c = lds_cfg(a.N, units, Fmt<FMT>::BB * Fmt<FMT>::UB);
+    for (int m0 = 0; m0 < a.M; m0 += max_mt) {
+      const int mt = a.M - m0 < max_mt ? a.M - m0 : max_mt;
+      int err;
+      switch (mt) {
+        case 1: err = launch_lds_mt<FMT, 1>(a, m0, c); break;
+        case 2: err = launch_lds_mt<FMT, 2>(a, m0, c); break;
+        case 3: err = launch_lds_mt<FMT, 3>(a, m0, c); break;
+        default: err = launch_lds_mt<FMT, 4>(a, m0, c); break;
+      }
+      if (err) return err;
+    }
+    return 0;
+  }
 }
 
 }  // namespace
@@ -524,6 +563,8 @@ int64_t gemv_argmax_fused_parts(const GemvArgs& a) {
   switch (a.fmt) {
     case KQ_Q8_0: return gemv_argmax_parts_fmt<F_Q8_0>(a);
     case KQ_Q4_0: return gemv_argmax_parts_fmt<F_Q4_0>(a);
+    case KQ_Q5_0: return gemv_argmax_parts_fmt<F_Q5_0>(a);
+    case KQ_Q5_1: return gemv_argmax_parts_fmt<F_Q5_1>(a);
     default: return gemv_argmax_parts_fmt<F_AFFINE4>(a);
   }
 }
@@ -532,6 +573,8 @@ int launch_gemv_argmax(const GemvArgs& a, int32_t* out, void* ws) {
   switch (a.fmt) {
     case KQ_Q8_0: return gemv_argmax_fmt<F_Q8_0>(a, out, ws);
     case KQ_Q4_0: return gemv_argmax_fmt<F_Q4_0>(a, out, ws);
+    case KQ_Q5_0: return gemv_argmax_fmt<F_Q5_0>(a, out, ws);
+    case KQ_Q5_1: return gemv_argmax_fmt<F_Q5_1>(a, out, ws);
     default: return gemv_argmax_fmt<F_AFFINE4>(a, out, ws);
   }
 }
@@ -580,6 +623,8 @@ int launch_gemv_invariant(const GemvArgs& a) {
   switch (a.fmt) {
     case KQ_Q8_0: return dispatch_invariant<F_Q8_0>(a);
     case KQ_Q4_0: return dispatch_invariant<F_Q4_0>(a);
+    case KQ_Q5_0: return dispatch_invariant<F_Q5_0>(a);
+    case KQ_Q5_1: return dispatch_invariant<F_Q5_1>(a);
     default: return dispatch_invariant<F_AFFINE4>(a);
   }
 }

@@ -438,7 +438,9 @@ __global__ __launch_bounds__(256) void k_moe_generic(const uint8_t* __restrict__
     const uint16_t* blk = reinterpret_cast<const uint16_t*>(Wr + (int64_t)b * Fmt<FMT>::BB);
     const uint16_t* xb = xr + b * 32;
     const float s = h2f(blk[0]);
-    if constexpr (FMT == F_Q8_0) {
+    if constexpr (FMT == F_Q5_0 || FMT == F_Q5_1) {
+      acc = q5_block_plain<FMT>(blk, xb, acc);
+    } else if constexpr (FMT == F_Q8_0) {
       for (int j = 0; j < 16; ++j) {
         const uint32_t two = blk[1 + j];
         acc = __builtin_fmaf(s * (float)(int8_t)(two & 0xff), h2f(xb[2 * j]), acc);
@@ -619,7 +621,7 @@ int launch_moe_down_sum_fmt(const MoeArgs& a, const float* rw, float* y) {
 }  // namespace
 
 bool moe_down_sum_applies(const MoeArgs& a) {
-  const int ub = a.fmt == KQ_AFFINE4_G32 ? 1 : 2;
+  const int ub = (a.fmt == KQ_AFFINE4_G32 || a.fmt == KQ_Q5_1) ? 1 : 2;   // blocks per load unit
   return a.M == 1 && a.top_k >= 1 && a.top_k <= 16 && a.K % (32 * ub) == 0 && moe_lds_fits(a.K) &&
          a.K / 8 <= 64 * MOE_XCH;
 }
@@ -628,6 +630,8 @@ int launch_moe_down_sum(const MoeArgs& a, const float* route_w, float* y) {
   switch (a.fmt) {
     case KQ_Q8_0: return launch_moe_down_sum_fmt<F_Q8_0>(a, route_w, y);
     case KQ_Q4_0: return launch_moe_down_sum_fmt<F_Q4_0>(a, route_w, y);
+    case KQ_Q5_0: return launch_moe_down_sum_fmt<F_Q5_0>(a, route_w, y);
+    case KQ_Q5_1: return launch_moe_down_sum_fmt<F_Q5_1>(a, route_w, y);
     default: return launch_moe_down_sum_fmt<F_AFFINE4>(a, route_w, y);
   }
 }
@@ -636,6 +640,8 @@ int launch_moe_gemv(const MoeArgs& a) {
   switch (a.fmt) {
     case KQ_Q8_0: return moe_dispatch<F_Q8_0>(a);
     case KQ_Q4_0: return moe_dispatch<F_Q4_0>(a);
+    case KQ_Q5_0: return moe_dispatch<F_Q5_0>(a);
+    case KQ_Q5_1: return moe_dispatch<F_Q5_1>(a);
     default: return moe_dispatch<F_AFFINE4>(a);
   }
 }
@@ -644,6 +650,8 @@ int launch_moe_gate_up_swiglu(const MoeGateUpArgs& a) {
   switch (a.fmt) {
     case KQ_Q8_0: return gate_up_dispatch<F_Q8_0>(a);
     case KQ_Q4_0: return gate_up_dispatch<F_Q4_0>(a);
+    case KQ_Q5_0: return gate_up_dispatch<F_Q5_0>(a);
+    case KQ_Q5_1: return gate_up_dispatch<F_Q5_1>(a);
     default: return gate_up_dispatch<F_AFFINE4>(a);
   }
 }

@@ -1,9 +1,10 @@
 // kq_pack.cpp — host-side block-format packer and unpacker.
 //
-// Encodes fp32 weight rows into Q8_0, Q4_0 and affine4 gs32 blocks (the block
-// definitions are in include/kq.h). The 4-bit formats are the two the Kipp
-// README, "How fast" contrasts: affine4 carries a bias term, Q4_0 is
-// scale-only. Kinetic docs, "Switching from llama.cpp" describe a quantizer
+// Encodes fp32 weight rows into Q8_0, Q4_0, affine4 gs32, Q5_0 and Q5_1
+// blocks (the block definitions are in include/kq.h). The 4-bit formats are
+// the two the Kipp README, "How fast" contrasts: affine4 carries a bias term,
+// Q4_0 is scale-only; Q5_0 and Q5_1 are the same two schemes with a fifth bit
+// (Kinetic docs, "Supported models" list them among the GGUF weights). Kinetic docs, "Switching from llama.cpp" describe a quantizer
 // that writes fixed bytes per format; this packer writes the bytes fixed by
 // those definitions (byte equality with any other tool is not claimed).
 //
@@ -151,6 +152,77 @@ bool pack_affine4(const float* w, uint8_t* out) {
   return true;
 }
 
+// The 5-bit formats: bit 4 of q_j in bit j of a little-endian word, the low
+// four bits as nibbles (element j low, j + 16 high), after the scale(s).
+void put_q5_bits(const uint8_t (&q)[32], uint8_t* out) {
+  uint32_t hbits = 0;
+  for (int j = 0; j < 32; ++j) hbits |= (uint32_t)((q[j] >> 4) & 1u) << j;
+  for (int i = 0; i < 4; ++i) out[i] = (uint8_t)(hbits >> (8 * i));
+  for (int j = 0; j < 16; ++j) out[4 + j] = (uint8_t)((q[j] & 15) | ((q[j + 16] & 15) << 4));
+}
+
+bool pack_q5_0(const float* w, uint8_t* out) {
+  int istar = 0;
+  float amax = std::fabs(w[0]);
+  for (int j = 1; j < 32; ++j) {
+    const float a = std::fabs(w[j]);
+    if (a > amax) { amax = a; istar = j; }     // strict: first index wins ties
+  }
+  const uint16_t dh = f32_to_f16_bits(w[istar] / -16.0f);
+  if (!finite16(dh)) return false;
+  const float d = f16_bits_to_f32(dh);
+  put16(out, dh);
+  uint8_t q[32];
+  for (int j = 0; j < 32; ++j) {
+    int v = 16;
+    if (d != 0.0f) {
+      const float r = round_half_away(w[j] / d) + 16.0f;
+      v = (int)std::min(31.0f, std::max(0.0f, r));
+    }
+    q[j] = (uint8_t)v;
+  }
+  put_q5_bits(q, out + 2);
+  return true;
+}
+
+bool pack_q5_1(const float* w, uint8_t* out) {
+  float lo = w[0], hi = w[0];
+  for (int j = 1; j < 32; ++j) {               // strict: first index wins ties
+    if (w[j] < lo) lo = w[j];
+    if (w[j] > hi) hi = w[j];
+  }
+  const float range = hi - lo;
+  const uint16_t dh = f32_to_f16_bits(range / 31.0f);
+  const uint16_t mh = f32_to_f16_bits(lo);
+  if (!finite16(dh) || !finite16(mh)) return false;
+  const float d = f16_bits_to_f32(dh);
+  const float m = f16_bits_to_f32(mh);
+  put16(out, dh);
+  put16(out + 2, mh);
+  uint8_t q[32];
+  for (int j = 0; j < 32; ++j) {
+    int v = 0;
+    if (d != 0.0f) {
+      const float diff = w[j] - m;
+      const float r = round_half_away(diff / d);
+      v = (int)std::min(31.0f, std::max(0.0f, r));
+    }
+    q[j] = (uint8_t)v;
+  }
+  put_q5_bits(q, out + 4);
+  return true;
+}
+
+bool pack_block(int fmt, const float* w, uint8_t* out) {
+  switch (fmt) {
+    case KQ_Q8_0: return pack_q8_0(w, out);
+    case KQ_Q4_0: return pack_q4_0(w, out);
+    case KQ_AFFINE4_G32: return pack_affine4(w, out);
+    case KQ_Q5_0: return pack_q5_0(w, out);
+    default: return pack_q5_1(w, out);
+  }
+}
+
 bool pack_rows(int fmt, const float* W, int64_t r0, int64_t r1, int64_t K, uint8_t* out) {
   const int64_t nb = K / 32;
   const int64_t bb = block_bytes(fmt);
@@ -161,10 +233,7 @@ bool pack_rows(int fmt, const float* W, int64_t r0, int64_t r1, int64_t K, uint8
       const float* w = wr + b * 32;
       for (int j = 0; j < 32; ++j)
         if (!std::isfinite(w[j])) return false;
-      bool ok = fmt == KQ_Q8_0 ? pack_q8_0(w, orow + b * bb)
-              : fmt == KQ_Q4_0 ? pack_q4_0(w, orow + b * bb)
-                               : pack_affine4(w, orow + b * bb);
-      if (!ok) return false;
+      if (!pack_block(fmt, w, orow + b * bb)) return false;
     }
   }
   return true;
@@ -177,6 +246,8 @@ int64_t block_bytes(int fmt) {
     case KQ_Q8_0: return 34;
     case KQ_Q4_0: return 18;
     case KQ_AFFINE4_G32: return 20;
+    case KQ_Q5_0: return 22;
+    case KQ_Q5_1: return 24;
     default: return -1;
   }
 }
@@ -219,6 +290,17 @@ int unpack(int fmt, const void* packed, int64_t N, int64_t K, float* W) {
         for (int j = 0; j < 16; ++j) {
           w[j] = d * (float)((blk[2 + j] & 15) - 8);
           w[j + 16] = d * (float)((blk[2 + j] >> 4) - 8);
+        }
+      } else if (fmt == KQ_Q5_0 || fmt == KQ_Q5_1) {
+        const float d = f16_bits_to_f32(h0);
+        const int hb = fmt == KQ_Q5_0 ? 2 : 4;   // fifth-bit word offset
+        const float m = fmt == KQ_Q5_1 ? f16_bits_to_f32((uint16_t)(blk[2] | (blk[3] << 8))) : 0.0f;
+        const uint32_t hbits = (uint32_t)blk[hb] | ((uint32_t)blk[hb + 1] << 8) | ((uint32_t)blk[hb + 2] << 16) |
+                               ((uint32_t)blk[hb + 3] << 24);
+        for (int j = 0; j < 32; ++j) {
+          const uint8_t nib = blk[hb + 4 + (j & 15)];
+          const int q = (j < 16 ? (nib & 15) : (nib >> 4)) | (int)(((hbits >> j) & 1u) << 4);
+          w[j] = fmt == KQ_Q5_0 ? d * (float)(q - 16) : std::fma(d, (float)q, m);
         }
       } else {
         const float s = f16_bits_to_f32(h0);

@@ -24,8 +24,12 @@
  *   KQ_Q8_0        34 B: fp16 d, 32 x int8 q;            w' = d*q
  *   KQ_Q4_0        18 B: fp16 d, 16 B nibbles;            w' = d*(q-8)
  *   KQ_AFFINE4_G32 20 B: fp16 s, fp16 b, 16 B nibbles;    w' = s*q + b
- * fp16 values are little-endian; in the 4-bit formats element j sits in the
- * low nibble of byte j and element j+16 in the high nibble.
+ *   KQ_Q5_0        22 B: fp16 d, 4 B fifth bits, 16 B nibbles;          w' = d*(q-16)
+ *   KQ_Q5_1        24 B: fp16 d, fp16 m, 4 B fifth bits, 16 B nibbles;  w' = d*q + m
+ * fp16 values are little-endian; in the nibble areas element j sits in the
+ * low nibble of byte j and element j+16 in the high nibble (the low four bits
+ * of q in the 5-bit formats, whose bit 4 of q_j is bit j of the little-endian
+ * 32-bit word after the scale(s)).
  *
  * Conventions for every call:
  *  - Return 0 (KQ_OK) or a negative kq_status. kq_last_error() gives a
@@ -55,7 +59,9 @@ extern "C" {
 typedef enum kq_format {
   KQ_Q8_0 = 0,
   KQ_Q4_0 = 1,
-  KQ_AFFINE4_G32 = 2
+  KQ_AFFINE4_G32 = 2,
+  KQ_Q5_0 = 3,
+  KQ_Q5_1 = 4
 } kq_format;
 
 typedef enum kq_status {
@@ -81,7 +87,7 @@ const char* kq_status_string(int status);
 /* Message describing the last failure on this thread ("" if none). */
 const char* kq_last_error(void);
 
-/* Bytes per 32-weight block of `fmt` (34, 18, 20), or a negative kq_status. */
+/* Bytes per 32-weight block of `fmt` (34, 18, 20, 22, 24), or a negative kq_status. */
 int64_t kq_block_bytes(int fmt);
 
 /* Bytes of a packed N x K matrix: N * (K/32) * kq_block_bytes(fmt).
@@ -104,6 +110,9 @@ int64_t kq_packed_bytes(int fmt, int64_t N, int64_t K);
  *            q_j = clamp(round(w_j/d) + 8, 0, 15), 8 if d == 0
  *   AFFINE4: lo/hi = min/max w_j (first index on ties); s = fp16((hi-lo)/15),
  *            b = fp16(lo); q_j = clamp(round((w_j-b)/s), 0, 15), 0 if s == 0
+ *   Q5_0:    as Q4_0 with d = fp16(m / -16); q_j = clamp(round(w_j/d) + 16, 0, 31), 16 if d == 0
+ *   Q5_1:    as AFFINE4 with d = fp16((hi-lo)/31), m = fp16(lo);
+ *            q_j = clamp(round((w_j-m)/d), 0, 31), 0 if d == 0
  * The bytes are identical to those of the library's CPU reference.
  * Errors: KQ_ERR_ARG (null, N < 0), KQ_ERR_FORMAT, KQ_ERR_SHAPE,
  * KQ_ERR_RANGE (non-finite weight, or a scale/bias that is infinite in fp16;
@@ -127,7 +136,9 @@ int kq_unpack(int fmt, const void* packed, int64_t N, int64_t K, float* W_out);
  *   W: device, packed N x K matrix (kq_pack layout), 4-byte aligned.
  *   x: device, fp16 bits [M][K] (column m contiguous), 16-byte aligned.
  *   y: device, fp32 [M][N], 4-byte aligned; overwritten, never accumulated.
- * Every weight byte is read once per call whatever M is. Accumulation is fp32;
+ * Every weight byte is read once per call whatever M is (Q5_0 and Q5_1, which
+ * run on the VALU kernels only, read it once per 8 columns beyond 3 columns).
+ * Accumulation is fp32;
  * results are run-to-run deterministic (fixed reduction order, no atomics).
  * M == 0 or N == 0 is a valid empty call. 1 <= M <= KQ_MAX_M.
  * Errors: KQ_ERR_ARG, KQ_ERR_FORMAT, KQ_ERR_SHAPE, KQ_ERR_ALIGN, KQ_ERR_HIP. */
@@ -300,7 +311,8 @@ int64_t kq_stack_plan_bytes(const kq_stage* stages, int n_stages);
  * it once at set-up, not inside graph capture. The plan stays valid while the
  * buffers it names do, on the device it was made on (kq_stack_run checks the
  * compute-unit count). Errors: KQ_ERR_ARG (also the overlaps above),
- * KQ_ERR_FORMAT, KQ_ERR_SHAPE (also K > 16384, or N above 4096 rows per
+ * KQ_ERR_FORMAT (also Q5_0 and Q5_1: the chain takes the other three formats),
+ * KQ_ERR_SHAPE (also K > 16384, or N above 4096 rows per
  * compute unit), KQ_ERR_ALIGN (also an x starting at an element of an earlier
  * y16 that is not a multiple of 4), KQ_ERR_HIP. */
 int kq_stack_plan(const kq_stage* stages, int n_stages, void* plan, int64_t plan_bytes,

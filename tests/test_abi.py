@@ -41,12 +41,14 @@ def test_status_strings():
 
 
 def test_sizes():
-    assert [kq.kq_block_bytes(f) for f in ("q8_0", "q4_0", "affine4")] == [34, 18, 20]
+    assert [kq.kq_block_bytes(f) for f in ("q8_0", "q4_0", "affine4", "q5_0", "q5_1")] == [34, 18, 20, 22, 24]
+    assert kq.kq_packed_bytes("q5_0", 2560, 9728) == 2560 * 304 * 22
     assert kq.kq_packed_bytes("affine4", 4096, 2560) == 4096 * 80 * 20
     assert kq.kq_packed_bytes("q8_0", 151936, 2560) == 413265920
     assert kq.kq_packed_bytes("q4_0", 0, 1024) == 0
     L = kq.lib()
-    assert L.kq_packed_bytes(3, 1, 32) == kq.KQ_ERR_FORMAT
+    assert L.kq_packed_bytes(5, 1, 32) == kq.KQ_ERR_FORMAT
+    assert L.kq_packed_bytes(-1, 1, 32) == kq.KQ_ERR_FORMAT
     assert L.kq_packed_bytes(0, 1, 33) == kq.KQ_ERR_SHAPE
     assert L.kq_packed_bytes(0, 1, 0) == kq.KQ_ERR_SHAPE
     assert L.kq_packed_bytes(0, -1, 32) == kq.KQ_ERR_ARG
@@ -161,7 +163,7 @@ def test_argmax_validation():
 def test_pack_validation():
     W = np.zeros((2, 32), np.float32)
     with pytest.raises(kq.KQError) as e:
-        kq.kq_pack(4, W)
+        kq.kq_pack(5, W)
     assert e.value.status == kq.KQ_ERR_FORMAT
     W[0, 3] = np.inf
     with pytest.raises(kq.KQError) as e:
@@ -275,3 +277,10 @@ def test_environment_does_not_steer_the_library():
     for name in os.listdir(csrc):
         with open(os.path.join(csrc, name)) as f:
             assert "getenv" not in f.read(), name
+
+
+def test_stack_plan_rejects_five_bit_formats():
+    """The persistent chain takes Q8_0, Q4_0 and affine4 only (host check)."""
+    for fmt in (kq.KQ_Q5_0, kq.KQ_Q5_1):
+        arr = _stage_arr([dict(fmt=fmt, W=A16, x=A16, y=A16 + 4096, N=64, K=256)])
+        assert kq.lib().kq_stack_plan_bytes(arr, 1) == kq.KQ_ERR_FORMAT
