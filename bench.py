@@ -483,6 +483,35 @@ def bench_moe_eager(torch, kq, S):
     del mats
 
 
+def bench_formats(torch, kq, S, reps=7):
+    """One matrix shape (the 4B stack's gate|up, 19456 x 2560, seeded weights)
+    in every block format at M = 1 and M = 8: cold per-launch time (rotating
+    through copies totalling >= 1 GB, graph-replayed) and GB/s of its packed
+    weights + x + y. Q5_0 / Q5_1 run on the VALU kernels only (8 columns per
+    weight pass), the others on the matrix cores from 4 columns."""
+    N, K = 19456, 2560
+    W = S.weights((6, 0, 0, 0), N, K)
+    out = {}
+    for fmt in ("q8_0", "q4_0", "affine4", "q5_0", "q5_1"):
+        packed = torch.from_numpy(kq.kq_pack(fmt, W)).to("cuda").reshape(-1)
+        copies = max(2, (1 << 30) // packed.numel() + 1)
+        bank = packed.repeat(copies).view(copies, -1)
+        row = {"weight_bytes": int(packed.numel())}
+        for M in (1, 8):
+            x = torch.from_numpy(S.activations((6, 1), K, M)).to("cuda")
+            y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+            us, _ = _graph_time_us(torch, [lambda c=c: kq.kq_gemv(fmt, bank[c], x, y, N, K, M)
+                                           for c in range(copies)], reps, copies)
+            alg = packed.numel() + 2 * M * K + 4 * M * N
+            row[f"M{M}"] = {"us_per_launch": us, "gbps": alg / (us * 1e-6) / 1e9}
+        out[fmt] = row
+        log(f"format {fmt}: M=1 {row['M1']['us_per_launch']:.2f} us ({row['M1']['gbps']:.0f} GB/s), "
+            f"M=8 {row['M8']['us_per_launch']:.2f} us")
+        del bank, packed
+        torch.cuda.empty_cache()
+    return {"shape": f"{N}x{K} (gate|up), cold", "formats": out}
+
+
 def _probe_lib():
     import ctypes
     L = ctypes.CDLL(os.path.join(ROOT, "block_quantized_gemv_kq_amd", "libkq_probe.so"))
@@ -895,6 +924,7 @@ def main():
         configs["qwen3_0.6b_q4_0_stack"] = bench_small_stack(torch, kq, S, args.steps)
         log(f"0.6B stack: {configs['qwen3_0.6b_q4_0_stack']['us_per_step_cold']:.1f} us cold")
         configs["moe_q4_0"] = bench_moe(torch, kq, S, max(5, args.steps // 2))
+        configs["formats"] = bench_formats(torch, kq, S)
         configs["stream_ceiling"] = stream_ceiling(torch)
         sc = configs["stream_ceiling"]
         log(f"read-only ceiling: {sc['sizes']['1GiB']['gbps']:.0f} GB/s at 1 GiB, plain-read step "

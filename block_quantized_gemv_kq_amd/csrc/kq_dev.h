@@ -237,18 +237,28 @@ __device__ __forceinline__ void unpack_nibbles(const uint32_t (&n)[4], uint32_t*
 }
 
 // The fifth bits of a 5-bit block (bit j of `qh` is bit 4 of q_j) into the
-// fp16 pairs of unpack_nibbles: bit 4 of each half, both halves of the block
-// shifted to 1024 + q. `hi_shift` is 4 there, 8 for the split form, whose
-// high-nibble halves stand for 16 q.
-__device__ __forceinline__ void add_fifth_bits(uint32_t qh, uint32_t* A, int hi_shift) {
+// fp16 pairs of unpack_nibbles: bit 4 of each half, so both halves of the
+// block read 1024 + q. HI_SHIFT is 4 there, 8 for the high-nibble halves of
+// the split form, which stand for 1024 + 16 q.
+// Two bits b0, b1 (bits 0-1 of v) times 0x80010 land at bits 4 and 19 (b0)
+// and 5 and 20 (b1); masking with 0x100010 keeps b0 at bit 4 and b1 at bit 20,
+// the bit of 16 in each fp16 half of a pair (0x1000100 for bit 8 of each half:
+// the multiplier 0x800100). Two bits per extract, multiply and and-or.
+template <int SHIFT>
+__device__ __forceinline__ uint32_t spread2(uint32_t qh, int pos) {
+  constexpr uint32_t mul = SHIFT == 4 ? 0x80010u : 0x800100u;
+  constexpr uint32_t mask = SHIFT == 4 ? 0x100010u : 0x1000100u;
+  return (__builtin_amdgcn_ubfe(qh, (uint32_t)pos, 2u) * mul) & mask;
+}
+
+template <int HI_SHIFT>
+__device__ __forceinline__ void add_fifth_bits(uint32_t qh, uint32_t* A) {
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    const uint32_t h = qh >> (4 * t);          // elements 4t..4t+3
-    A[2 * t] |= ((h & 1u) << 4) | ((h & 2u) << 19);
-    A[2 * t + 1] |= ((h & 4u) << 2) | ((h & 8u) << 17);
-    const uint32_t g = qh >> (16 + 4 * t);     // elements 16+4t..19+4t
-    A[8 + 2 * t] |= ((g & 1u) << hi_shift) | ((g & 2u) << (hi_shift + 15));
-    A[9 + 2 * t] |= ((g & 4u) << (hi_shift - 2)) | ((g & 8u) << (hi_shift + 13));
+    A[2 * t] |= spread2<4>(qh, 4 * t);                  // elements 4t, 4t+1
+    A[2 * t + 1] |= spread2<4>(qh, 4 * t + 2);          // elements 4t+2, 4t+3
+    A[8 + 2 * t] |= spread2<HI_SHIFT>(qh, 16 + 4 * t);  // elements 16+4t, 17+4t
+    A[9 + 2 * t] |= spread2<HI_SHIFT>(qh, 18 + 4 * t);  // elements 18+4t, 19+4t
   }
 }
 
@@ -286,8 +296,8 @@ __device__ __forceinline__ void q5_0_unit(const uint32_t* D, uint32_t* A, float*
   const uint32_t nb[4] = {D[7], D[8], D[9], D[10]};
   unpack_nibbles_t<SPLIT>(na, A);
   unpack_nibbles_t<SPLIT>(nb, A + 16);
-  add_fifth_bits(alignbyte2(D[1], D[0]), A, SPLIT ? 8 : 4);
-  add_fifth_bits(D[6], A + 16, SPLIT ? 8 : 4);
+  add_fifth_bits<SPLIT ? 8 : 4>(alignbyte2(D[1], D[0]), A);
+  add_fifth_bits<SPLIT ? 8 : 4>(D[6], A + 16);
   scale[0] = h2f(D[0]);
   scale[1] = h2f(D[5] >> 16);
   bias[0] = bias[1] = 0.0f;
@@ -298,7 +308,7 @@ template <bool SPLIT>
 __device__ __forceinline__ void q5_1_unit(const uint32_t* D, uint32_t* A, float* scale, float* bias) {
   const uint32_t n[4] = {D[2], D[3], D[4], D[5]};
   unpack_nibbles_t<SPLIT>(n, A);
-  add_fifth_bits(D[1], A, SPLIT ? 8 : 4);
+  add_fifth_bits<SPLIT ? 8 : 4>(D[1], A);
   scale[0] = h2f(D[0]);
   bias[0] = h2f(D[0] >> 16);
 }

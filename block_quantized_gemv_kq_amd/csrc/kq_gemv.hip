@@ -440,15 +440,17 @@ int launch_generic(const GemvArgs& a) {
 template <int FMT>
 int dispatch(const GemvArgs& a) {
   if constexpr (!has_mfma<FMT>()) {
-    // the 5-bit formats: the one-column kernels up to 3 columns, then the
-    // register-x kernel 8 columns per pass (weights read once per pass)
+    // the 5-bit formats: the LDS-staged VALU kernel, up to 4 columns per pass
+    // (weights read once per pass); the register-x kernel (8 columns per
+    // pass) where x does not fit. On the 19456 x 2560 and 2560 x 9728
+    // shapes at 8 columns the passes of 4 take Q5_0 54 / 53 us against 110 /
+    // 74 us on the register-x kernel, Q5_1 34 us either way.
     if (a.K % (32 * Fmt<FMT>::UB) != 0) return launch_generic<FMT>(a);
     const int force = tune_int(TUNE_FORCE_PATH);
     if (force == 'g') return launch_generic<FMT>(a);
     const bool lds_ok = (int64_t)(a.M < LDS_MAX_MT ? a.M : LDS_MAX_MT) * (a.K * 2 + a.K / 4) <= LDS_MAX_BYTES;
-    if (force == 'v') return launch_valu<FMT>(a);
-    if (lds_ok && (force == 'l' || a.M < MFMA_MIN_M)) return launch_lds<FMT>(a);
-    return launch_valu<FMT>(a);
+    if (force == 'v' || !lds_ok) return launch_valu<FMT>(a);
+    return launch_lds<FMT>(a);
   }
   if (a.K % (32 * Fmt<FMT>::UB) != 0) return a.M >= MFMA_MIN_M_UNALIGNED ? launch_gemv_mfma(a) : launch_generic<FMT>(a);
   const int force = tune_int(TUNE_FORCE_PATH);  // tests: run a given path at any shape

@@ -1,8 +1,9 @@
 """GPU tests of the 5-bit formats (Q5_0, Q5_1) through the C ABI: packer bytes
 equal the oracle's (every case packs through kq_pack and checks), parity of
 kq_gemv with the fp64 oracle on every kernel path these formats take (the
-one-column LDS kernel, the register-x kernel 8 columns per pass, the generic
-kernel for 2-byte-aligned Q5_0 rows), unit vectors giving w' exactly (which
+LDS-staged kernel 4 columns per pass, the register-x kernel 8 columns per pass
+for rows whose x does not fit, the generic kernel for 2-byte-aligned Q5_0
+rows), unit vectors giving w' exactly (which
 pins the fifth-bit and nibble order on the GPU), the output-layer argmax,
 batch-invariant columns, and the routed-expert FFN."""
 import numpy as np
