@@ -59,7 +59,7 @@ const TuneName kTuneNames[] = {
     {"mfma_r", kq::TUNE_MFMA_R},                 {"mfma_waves", kq::TUNE_MFMA_WAVES},
     {"mfma_xf", kq::TUNE_MFMA_XF},               {"mfma_pers_tpw", kq::TUNE_MFMA_PERS_TPW},
     {"mfma_chunk_l2cg", kq::TUNE_MFMA_CHUNK_L2CG}, {"moe_unfused", kq::TUNE_MOE_UNFUSED},
-    {"moe_min_wg", kq::TUNE_MOE_MIN_WG},
+    {"moe_min_wg", kq::TUNE_MOE_MIN_WG},          {"log", kq::TUNE_LOG},
 };
 
 // Parse a tuning value: force_path and mfma_variant take names, the others integers.
@@ -96,6 +96,19 @@ namespace kq {
 int tune(TuneKey k) {
   const int v = g_tune[k].load(std::memory_order_relaxed);
   return v == 0 ? TUNE_UNSET : v - 1;
+}
+
+void dispatch_log(const char* kernel, int fmt, int64_t N, int64_t K, int M, unsigned gx, unsigned gy,
+                  unsigned block, size_t lds, const char* cfg_fmt, ...) {
+  if (tune(TUNE_LOG) != 1) return;
+  static const char* names[] = {"q8_0", "q4_0", "affine4", "q5_0", "q5_1"};
+  char cfg[256];
+  va_list ap;
+  va_start(ap, cfg_fmt);
+  vsnprintf(cfg, sizeof(cfg), cfg_fmt, ap);
+  va_end(ap);
+  fprintf(stderr, "kq: %s fmt=%s N=%lld K=%lld M=%d grid=(%u,%u) block=%u lds=%zu %s\n", kernel,
+          fmt >= 0 && fmt < 5 ? names[fmt] : "-", (long long)N, (long long)K, M, gx, gy, block, lds, cfg);
 }
 }  // namespace kq
 

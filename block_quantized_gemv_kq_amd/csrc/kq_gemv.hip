@@ -278,6 +278,8 @@ int launch_valu_mt(const GemvArgs& a, int m0, ValuCfg c) {
   const int64_t tile = (int64_t)(64 >> c.log2g) * c.R;
   const int64_t waves = (a.N + tile - 1) / tile;
   const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
+  dispatch_log("k_gemv_valu", a.fmt, a.N, a.K, MT, grid.x, 1, 256, 0, "register-x G=%d R=%d m0=%d", 1 << c.log2g,
+               c.R, m0);
   if (c.R == 4)
     hipLaunchKernelGGL((k_gemv_valu<FMT, MT, 4>), grid, block, 0, a.stream, a.W, a.x, a.y, (int)a.N, (int)a.K, c.log2g, m0);
   else if (c.R == 2)
@@ -372,6 +374,9 @@ int launch_lds_wpg(const GemvArgs& a, int m0, LdsCfg c, Best* part) {
   const dim3 grid((unsigned)nwg), block(64 * WPG);
   const size_t lds = (size_t)MT * a.K * 2 + (size_t)MT * (a.K / 32) * 8;  // x + block sums
   const bool xreg = (int64_t)MT * a.K / 8 <= 64 * WPG * xreg_chunks<MT>();
+  dispatch_log("k_gemv_lds", a.fmt, a.N, a.K, MT, grid.x, 1, 64 * WPG, lds,
+               "G=%d units/lane=%d passes=%d x=%s m0=%d argmax=%d", 1 << c.log2g, ITERS, c.passes,
+               xreg ? "registers" : "lds-dma", m0, part ? 1 : 0);
   if (MT == 1 && part) {   // the argmax epilogue (one column only)
     if (xreg)
       hipLaunchKernelGGL((k_gemv_lds<FMT, MT, ITERS, true, WPG, MT == 1>), grid, block, lds, a.stream, a.W, a.x, a.y,
@@ -433,6 +438,7 @@ int launch_lds(const GemvArgs& a) {
 template <int FMT>
 int launch_generic(const GemvArgs& a) {
   const dim3 grid((unsigned)((a.N + 3) / 4)), block(256);
+  dispatch_log("k_gemv_generic", a.fmt, a.N, a.K, a.M, grid.x, 1, 256, 0, "one wave per row");
   hipLaunchKernelGGL((k_gemv_generic<FMT>), grid, block, 0, a.stream, a.W, a.x, a.y, (int)a.N, (int)a.K, a.M);
   return (int)hipGetLastError();
 }

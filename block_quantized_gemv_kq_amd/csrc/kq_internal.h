@@ -28,12 +28,18 @@ enum TuneKey {
   TUNE_MFMA_CHUNK_L2CG,  // chunked kernel: log2 of groups per chunk
   TUNE_MOE_UNFUSED,      // 1: one-token MoE down + weighted sum as two kernels
   TUNE_MOE_MIN_WG,       // routed-expert kernels: widen lane groups below this many workgroups
+  TUNE_LOG,              // 1: one line per kernel launch on stderr (the dispatch log)
   TUNE_COUNT
 };
 enum MfmaVariant { MV_PERS = 1, MV_TEAMS, MV_TEAMS_SX, MV_CHUNK, MV_CHUNK_WHOLE, MV_CHUNK_SPLIT, MV_DIRECT };
 constexpr int TUNE_UNSET = -0x7fffffff;
 // The override of `k`, or TUNE_UNSET.
 int tune(TuneKey k);
+// Dispatch log: when the log override is 1, one line on stderr per kernel
+// launch: kernel, format, shape, grid, workgroup size, LDS bytes and the
+// configuration the dispatcher chose (free text).
+void dispatch_log(const char* kernel, int fmt, int64_t N, int64_t K, int M, unsigned gx, unsigned gy,
+                  unsigned block, size_t lds, const char* cfg_fmt, ...);
 
 // ---- host packer (kq_pack.cpp)
 int64_t block_bytes(int fmt);

@@ -868,6 +868,8 @@ int launch_mfma_t(const GemvArgs& a, int m0, int mt) {
   const MfmaCfg c = mfma_cfg(a.N, a.K, P, MfmaMaxWaves<T>::v);
   const dim3 grid((unsigned)((a.N + 15) / 16)), block((unsigned)(64 * c.waves));
   const size_t lds = (size_t)c.waves * T * 64 * sizeof(float4_t);
+  dispatch_log("k_gemv_mfma", a.fmt, a.N, a.K, mt, grid.x, 1, block.x, lds, "direct T=%d P=%d groups/wave=%d m0=%d",
+               T, P, c.gpw, m0);
   hipLaunchKernelGGL((k_gemv_mfma<FMT, T, P>), grid, block, lds, a.stream, a.W, a.x + (int64_t)m0 * a.K,
                      a.y + (int64_t)m0 * a.N, (int)a.N, (int)a.K, mt, c.gpw);
   return (int)hipGetLastError();
@@ -971,6 +973,9 @@ int launch_mfma_lds_p(const GemvArgs& a, int m0, int mt, const MfmaLdsCfg& c) {
   // The mfma_xf tuning override (0 / 1) forces one order.
   const int exf = tune(TUNE_MFMA_XF);
   const bool xf = exf != TUNE_UNSET ? exf != 0 : !(c.log2mp == 3 && tiles >= 1024);
+  dispatch_log("k_gemv_mfma_lds", a.fmt, a.N, a.K, mt, grid.x, 1, block.x, c.lds,
+               "teams R=%d S=%d P=%d Mp=%d sums=%d x_first=%d m0=%d", c.R, c.S, P, 1 << c.log2mp, SX ? 1 : 0,
+               xf ? 1 : 0, m0);
   if (xf)
     hipLaunchKernelGGL((k_gemv_mfma_lds<FMT, P, SX, true>), grid, block, c.lds, a.stream, a.W, a.x + (int64_t)m0 * a.K,
                        a.y + (int64_t)m0 * a.N, (int)a.N, (int)a.K, mt, c.R, c.S, c.log2mp);
@@ -1061,6 +1066,8 @@ int launch_mfma_chunk_p(const GemvArgs& a, int m0, int mt, const MfmaChunkCfg& c
   const int64_t tiles = (a.N + 15) / 16;
   const unsigned cgroups = (unsigned)((mt + 16 * T - 1) / (16 * T));   // column groups of 16 T along y
   const dim3 grid((unsigned)((tiles + c.R - 1) / c.R), cgroups), block((unsigned)(64 * c.R * c.S));
+  dispatch_log("k_gemv_mfma_chunk", a.fmt, a.N, a.K, mt, grid.x, grid.y, block.x, c.lds,
+               "T=%d R=%d S=%d P=%d groups/chunk=%d m0=%d", T, c.R, c.S, P, 1 << c.log2cg, m0);
   hipLaunchKernelGGL((k_gemv_mfma_chunk<FMT, P, T>), grid, block, c.lds, a.stream, a.W, a.x + (int64_t)m0 * a.K,
                      a.y + (int64_t)m0 * a.N, (int)a.N, (int)a.K, mt, c.R, c.S, c.log2cg);
   return (int)hipGetLastError();
@@ -1113,6 +1120,8 @@ int launch_mfma_pers_p(const GemvArgs& a, int log2mp, size_t lds) {
   }
   const int64_t waves = (tiles + tpw - 1) / tpw;
   const dim3 grid((unsigned)((waves + 7) / 8)), block(512);
+  dispatch_log("k_gemv_mfma_pers", a.fmt, a.N, a.K, (int)a.M, grid.x, 1, 512, lds,
+               "persistent P=%d tiles/wave=%d Mp=%d", P, (int)tpw, 1 << log2mp);
   hipLaunchKernelGGL((k_gemv_mfma_pers<FMT, P, SX>), grid, block, lds, a.stream, a.W, a.x, a.y, (int)a.N, (int)a.K,
                      (int)a.M, log2mp, (int)tpw);
   return (int)hipGetLastError();

@@ -115,6 +115,7 @@ int launch_argmax_final(const void* part, int nparts, int M, int32_t* out, hipSt
 int launch_argmax(const float* y, int64_t N, int M, int32_t* out, void* ws, hipStream_t stream) {
   const int nparts = (int)argmax_partials(N);
   Best* part = static_cast<Best*>(ws);
+  dispatch_log("k_argmax_partial+final", -1, N, 0, M, (unsigned)nparts, (unsigned)M, 256, 0, "two passes");
   hipLaunchKernelGGL(k_argmax_partial, dim3((unsigned)nparts, (unsigned)M), dim3(256), 0, stream, y, N,
                      part, nparts);
   int err = (int)hipGetLastError();

@@ -542,6 +542,8 @@ int launch_moe_lds(const uint8_t* W0, const uint8_t* W1, const uint16_t* x, cons
   const int P = M * top_k;
   const dim3 grid((unsigned)((waves + 3) / 4), (unsigned)P), block(256);
   const size_t lds = (size_t)MOE_COLS * K * 2 + (size_t)MOE_COLS * (K / 32) * 8 + (size_t)2 * P * 4 + 32;
+  dispatch_log(GATE_UP ? "k_moe_lds(gate|up+swiglu)" : "k_moe_lds", FMT, N, K, M, grid.x, grid.y, 256, lds,
+               "G=%d units/lane=%d slots=%d", 1 << log2g, iters, P);
 #define KQ_MOE_LAUNCH(IT)                                                                                       \
   hipLaunchKernelGGL((k_moe_lds<FMT, IT, GATE_UP>), grid, block, lds, stream, W0, W1, x, ids, out, (int)N, (int)K, \
                      M, top_k, n_experts, x_per_slot, log2g, eb)
@@ -604,6 +606,8 @@ int launch_moe_down_sum_fmt(const MoeArgs& a, const float* rw, float* y) {
   const int64_t rpw = 64 >> log2g;
   const dim3 grid((unsigned)((a.N + rpw - 1) / rpw)), block((unsigned)(64 * a.top_k));
   const size_t lds = (size_t)a.top_k * ((size_t)a.K * 2 + (size_t)(a.K / 32) * 8) + (size_t)a.top_k * rpw * 4;
+  dispatch_log("k_moe_down_sum", FMT, a.N, a.K, a.M, grid.x, 1, block.x, lds, "G=%d units/lane=%d top_k=%d",
+               1 << log2g, iters, a.top_k);
 #define KQ_MOE_DS(IT)                                                                                          \
   hipLaunchKernelGGL((k_moe_down_sum<FMT, IT>), grid, block, lds, a.stream, a.W, a.x, a.ids, rw, y, (int)a.N,   \
                      (int)a.K, a.top_k, a.n_experts, a.x_per_slot, log2g, eb)
