@@ -522,8 +522,10 @@ def _probe_lib():
 
 
 # bytes per launch of the step's matrices (packed weights) and a large read
-CEILING_SIZES = {"o": 6553600, "qkv": 15728640, "down": 15564800, "gate_up": 31129600,
-                 "lm_head": 413265920, "1GiB": 1 << 30}
+# packed bytes of the step's matrices: affine4 rows of K/32 blocks of 20 bytes,
+# the Q8_0 output layer 34 bytes per block
+CEILING_SIZES = {"o": 2560 * 128 * 20, "qkv": 6144 * 80 * 20, "down": 2560 * 304 * 20, "gate_up": 19456 * 80 * 20,
+                 "lm_head": 151936 * 80 * 34, "1GiB": 1 << 30}
 
 
 def stream_ceiling(torch, reps=7):

@@ -15,6 +15,7 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <atomic>
 #include <mutex>
 
 #include "kq_dev.h"
@@ -57,10 +58,12 @@ __global__ __launch_bounds__(256) void k_gemv_valu(const uint8_t* __restrict__ W
   }
 }
 
-// 16-byte activation chunks per thread in the register variant: 5, or 10 for
-// two columns (so that two 9728-long columns go through registers rather
-// than LDS DMA).
-template <int MT> constexpr int xreg_chunks() { return MT == 2 ? 10 : 5; }
+// 16-byte activation chunks per thread in the register variant: enough for
+// 1280 chunks per workgroup (one 10240-long column), 2560 for two columns (so
+// that two 9728-long columns go through registers rather than LDS DMA).
+template <int MT, int WPG> constexpr int xreg_chunks() {
+  return ((MT == 2 ? 2560 : 1280) + 64 * WPG - 1) / (64 * WPG);
+}
 
 // ------------------------------------------- VALU path, loads-first + LDS x
 // One row per lane group (G lanes), 64/G rows per wave. Each lane issues the
@@ -107,7 +110,7 @@ __global__ __launch_bounds__(64 * WPG) void k_gemv_lds(const uint8_t* __restrict
   // the first barrier waits for together with the weights. The two variants
   // are separate kernels: with an LDS DMA anywhere in the kernel the compiler
   // would make the register path's LDS writes wait for every load.
-  constexpr int XCH = xreg_chunks<MT>();
+  constexpr int XCH = xreg_chunks<MT, WPG>();
   const int n16 = MT * K / 8;   // columns m0 .. m0+MT-1 are contiguous
   u32x4 xr[XCH];
   const u32x4* xsrc = reinterpret_cast<const u32x4*>(x + (int64_t)m0 * K);
@@ -236,6 +239,18 @@ using namespace kqd;
 
 const char* hip_error_string(int err) { return hipGetErrorString(static_cast<hipError_t>(err)); }
 
+int device_cus() {
+  static std::atomic<int> cus_of[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;   // only shapes launches
+  int v = cus_of[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v < 1) v = 256;
+    cus_of[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
 namespace {
 
 int ilog2(int v) {
@@ -249,15 +264,15 @@ struct ValuCfg {
   int R;
 };
 
-// Lanes per row (G) and rows per lane (R) for the VALU path. G is a power of
-// two near units/4, so each lane walks a few units of a row; R grows while
-// the grid still holds >= 2048 waves (8 per CU) to keep loads in flight.
-// The valu_g / valu_r tuning overrides replace the choice (sweeps and tests).
 int tune_int(TuneKey k) {
   const int v = tune(k);
   return v == TUNE_UNSET ? 0 : v;
 }
 
+// Lanes per row (G) and rows per lane (R) for the VALU path. G is a power of
+// two near units/4, so each lane walks a few units of a row; R grows while
+// the grid still holds >= 2048 waves (8 per CU) to keep loads in flight.
+// The valu_g / valu_r tuning overrides replace the choice (sweeps and tests).
 ValuCfg valu_cfg(int64_t N, int units) {
   const int env_g = tune_int(TUNE_VALU_G);
   const int env_r = tune_int(TUNE_VALU_R);
@@ -360,9 +375,20 @@ LdsCfg lds_cfg(int64_t N, int units, int unit_bytes) {
   int iters = (units + G - 1) / G;
   if (iters > MAX_ITERS) iters = MAX_ITERS;
   const int passes = (units + G * iters - 1) / (G * iters);
+  // Waves per workgroup (one column): 4, or 12 where a row is 64 lanes of
+  // exactly two units each and the grid fits the device at once (fewer
+  // workgroups, each staging x for more rows). Measured on MI355X (cold,
+  // graph-replayed, medians of 3, std about 0.01 us): 2560 x 4096 affine4 3.33
+  // against 3.60 us, Q5_1 3.91 against 4.06; every other shape tried is as
+  // fast or faster at 4 (q|k|v 4.16 against 4.22, down 5.80 against 6.15,
+  // Q8_0 6144 x 2560 with two units on 32 lanes 5.58 against 6.73, the 0.6B
+  // Q4_0 shapes with one unit per lane 2.7-3.3 against 3.3-3.7). Spreading
+  // row waves evenly over the CUs (5 per workgroup on 2560 rows: 10 on every
+  // CU instead of 12 on half and 8 on the rest) did not help: 3.58, 5.86 us.
   int wpg = 4;
+  if (iters == 2 && G == 64 && passes == 1 && N <= 16 * (int64_t)device_cus()) wpg = 12;
   const int env_w = tune_int(TUNE_LDS_WPG);
-  if (env_w == 4 || env_w == 8 || env_w == 16) wpg = env_w;
+  if (env_w == 4 || env_w == 8 || env_w == 12 || env_w == 16) wpg = env_w;
   return {ilog2(G), iters, passes, wpg};
 }
 
@@ -373,7 +399,7 @@ int launch_lds_wpg(const GemvArgs& a, int m0, LdsCfg c, Best* part) {
   const int64_t nwg = (waves + WPG - 1) / WPG;
   const dim3 grid((unsigned)nwg), block(64 * WPG);
   const size_t lds = (size_t)MT * a.K * 2 + (size_t)MT * (a.K / 32) * 8;  // x + block sums
-  const bool xreg = (int64_t)MT * a.K / 8 <= 64 * WPG * xreg_chunks<MT>();
+  const bool xreg = (int64_t)MT * a.K / 8 <= 64 * WPG * xreg_chunks<MT, WPG>();
   dispatch_log("k_gemv_lds", a.fmt, a.N, a.K, MT, grid.x, 1, 64 * WPG, lds,
                "G=%d units/lane=%d passes=%d x=%s m0=%d argmax=%d", 1 << c.log2g, ITERS, c.passes,
                xreg ? "registers" : "lds-dma", m0, part ? 1 : 0);
@@ -397,8 +423,12 @@ int launch_lds_wpg(const GemvArgs& a, int m0, LdsCfg c, Best* part) {
 template <int FMT, int MT, int ITERS>
 int launch_lds_it(const GemvArgs& a, int m0, LdsCfg c, Best* part) {
   if constexpr (MT == 1) {
-    if (c.wpg == 16) return launch_lds_wpg<FMT, MT, ITERS, 16>(a, m0, c, part);
-    if (c.wpg == 8) return launch_lds_wpg<FMT, MT, ITERS, 8>(a, m0, c, part);
+    switch (c.wpg) {
+      case 8: return launch_lds_wpg<FMT, MT, ITERS, 8>(a, m0, c, part);
+      case 12: return launch_lds_wpg<FMT, MT, ITERS, 12>(a, m0, c, part);
+      case 16: return launch_lds_wpg<FMT, MT, ITERS, 16>(a, m0, c, part);
+      default: break;
+    }
   }
   return launch_lds_wpg<FMT, MT, ITERS, 4>(a, m0, c, part);
 }

@@ -25,6 +25,7 @@ enum TuneKey {
   TUNE_MFMA_WAVES,       // wave count below which the teams kernel doubles S
   TUNE_MFMA_XF,          // teams kernel issue order: 1 x first, 0 weights first
   TUNE_MFMA_PERS_TPW,    // persistent kernel: tiles per wave
+  TUNE_MFMA_PERS_WAVES,  // persistent kernel: waves per workgroup
   TUNE_MFMA_CHUNK_L2CG,  // chunked kernel: log2 of groups per chunk
   TUNE_MOE_UNFUSED,      // 1: one-token MoE down + weighted sum as two kernels
   TUNE_MOE_MIN_WG,       // routed-expert kernels: widen lane groups below this many workgroups
@@ -35,6 +36,8 @@ enum MfmaVariant { MV_PERS = 1, MV_TEAMS, MV_TEAMS_SX, MV_CHUNK, MV_CHUNK_WHOLE,
 constexpr int TUNE_UNSET = -0x7fffffff;
 // The override of `k`, or TUNE_UNSET.
 int tune(TuneKey k);
+// Compute units of the current device (looked up once per device).
+int device_cus();
 // Dispatch log: when the log override is 1, one line on stderr per kernel
 // launch: kernel, format, shape, grid, workgroup size, LDS bytes and the
 // configuration the dispatcher chose (free text).

@@ -394,7 +394,6 @@ __device__ __forceinline__ void stage_x_mfma(const uint16_t* __restrict__ x, int
   const int Mp = 1 << log2mp;
   const int kq8 = K / 8, kq8p = 16 * ngroups;
   const uint32_t sx_base = (uint32_t)kq8p * (uint32_t)Mp * 16u;
-  const uint32_t dummy = SX ? sx_base + (uint32_t)(4 * ngroups * Mp) * 4u : sx_base;
   const int nthreads = (int)blockDim.x;
   const int nwaves = nthreads >> 6;
   const int lane = (int)threadIdx.x & 63;
@@ -428,11 +427,11 @@ __device__ __forceinline__ void stage_x_mfma(const uint16_t* __restrict__ x, int
     for (int c = 0; c < XST_MAX; ++c) {
       const int q = wv + nwaves * c;
       const int col = q & (Mp - 1), k8 = 64 * (q >> log2mp) + lane;
-      const bool ok = k8 < kq8p;
-      const uint32_t a0 = ok ? (uint32_t)((4 * (k8 >> 2) + g0) * Mp + (col ^ sw)) * 16u + part : dummy;
-      const uint32_t a1 = ok ? a0 + (uint32_t)Mp * 16u : dummy + 8u;
-      *reinterpret_cast<u32x2*>(xlb + a0) = u32x2{xr[c].x, xr[c].y};
-      *reinterpret_cast<u32x2*>(xlb + a1) = u32x2{xr[c].z, xr[c].w};
+      if (k8 < kq8p) {   // pieces past the padded K have no slot
+        const uint32_t a0 = (uint32_t)((4 * (k8 >> 2) + g0) * Mp + (col ^ sw)) * 16u + part;
+        *reinterpret_cast<u32x2*>(xlb + a0) = u32x2{xr[c].x, xr[c].y};
+        *reinterpret_cast<u32x2*>(xlb + a0 + (uint32_t)Mp * 16u) = u32x2{xr[c].z, xr[c].w};
+      }
     }
   }
   if constexpr (XF) {
@@ -893,10 +892,10 @@ struct MfmaLdsCfg {
 };
 
 // LDS bytes of staged x (M columns padded to Mp, K to whole groups), with or
-// without the block sums, plus a 16-byte slot for idle threads.
+// without the block sums (gate|up at 8 columns: 40 KB, four workgroups per CU).
 int64_t mfma_x_lds_bytes(int64_t K, int log2mp, bool sums) {
   const int64_t ngroups = (K / 32 + 3) / 4, Mp = (int64_t)1 << log2mp;
-  return Mp * 16 * ngroups * 16 + (sums ? 4 * ngroups * Mp * 4 : 0) + 16;
+  return Mp * 16 * ngroups * 16 + (sums ? 4 * ngroups * Mp * 4 : 0);
 }
 
 // Waves per tile S: enough that each wave holds at most maxp groups,
@@ -1107,11 +1106,19 @@ int launch_mfma_pers_p(const GemvArgs& a, int log2mp, size_t lds) {
   if (!cus_of[dev] && hipDeviceGetAttribute(&cus_of[dev], hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return (int)hipErrorInvalidDevice;
   const int cus = cus_of[dev];
+  // waves per workgroup: 8, or fewer (more workgroups, each staging x once)
+  // where enough threads remain to stage x
+  int nw = 8;
+  {
+    const int v = tune(TUNE_MFMA_PERS_WAVES);
+    if (v >= 1 && v <= 8 && mfma_x_pieces((int)((a.K / 32 + 3) / 4), log2mp) <= (int64_t)XST_MAX * 64 * v) nw = v;
+  }
   int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_gemv_mfma_pers<FMT, P, SX>, 512, lds) != hipSuccess || per_cu < 1)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_gemv_mfma_pers<FMT, P, SX>, 64 * nw, lds) != hipSuccess ||
+      per_cu < 1)
     per_cu = 1;
   const int64_t tiles = (a.N + 15) / 16;
-  const int64_t max_waves = (int64_t)cus * per_cu * 8;
+  const int64_t max_waves = (int64_t)cus * per_cu * nw;
   int64_t tpw = (tiles + max_waves - 1) / max_waves;
   if (tpw > MFMA_PERS_TPW) tpw = MFMA_PERS_TPW;   // more workgroups than fit at once
   {
@@ -1119,8 +1126,8 @@ int launch_mfma_pers_p(const GemvArgs& a, int log2mp, size_t lds) {
     if (v >= 1 && v <= MFMA_PERS_TPW) tpw = v;
   }
   const int64_t waves = (tiles + tpw - 1) / tpw;
-  const dim3 grid((unsigned)((waves + 7) / 8)), block(512);
-  dispatch_log("k_gemv_mfma_pers", a.fmt, a.N, a.K, (int)a.M, grid.x, 1, 512, lds,
+  const dim3 grid((unsigned)((waves + nw - 1) / nw)), block((unsigned)(64 * nw));
+  dispatch_log("k_gemv_mfma_pers", a.fmt, a.N, a.K, (int)a.M, grid.x, 1, 64 * nw, lds,
                "persistent P=%d tiles/wave=%d Mp=%d", P, (int)tpw, 1 << log2mp);
   hipLaunchKernelGGL((k_gemv_mfma_pers<FMT, P, SX>), grid, block, lds, a.stream, a.W, a.x, a.y, (int)a.N, (int)a.K,
                      (int)a.M, log2mp, (int)tpw);

@@ -220,3 +220,45 @@ def test_chunk_column_groups(fmt, N, K, M):
     yr, ad = R.gemv(fmt, fields, x)
     U.assert_parity(y, yr, ad, f"{fmt} chunk column groups N={N} K={K} M={M}")
     assert np.array_equal(y, y2), "not deterministic run to run"
+
+
+@pytest.mark.parametrize("fmt", ("q8_0", "q4_0", "affine4", "q5_0", "q5_1"))
+@pytest.mark.parametrize("wpg", ("8", "12", "16"))
+def test_lds_waves_per_workgroup(fmt, wpg):
+    """The one-column LDS kernel at every workgroup size the launcher may pick:
+    within the oracle's bar and bitwise equal to 4 waves per workgroup (each
+    lane's sum and the per-workgroup staging do not depend on it)."""
+    for N, K, g in ((333, 1024, None), (2560, 4096, None), (17, 9728, None), (300, 2560, "16"), (1, 64, None)):
+        packed, fields, x = _case(fmt, N, K, 1, 13)
+        Wd = U.to_dev(packed)
+        extra = {"valu_g": g} if g else {}
+        with U.tuning({"lds_wpg": wpg, **extra}):
+            y = U.gemv_gpu(fmt, Wd, x, N, K, path="lds")
+        with U.tuning({"lds_wpg": "4", **extra}):
+            y4 = U.gemv_gpu(fmt, Wd, x, N, K, path="lds")
+        yr, ad = R.gemv(fmt, fields, x)
+        U.assert_parity(y, yr, ad, f"{fmt} wpg={wpg} N={N} K={K}")
+        assert np.array_equal(y.view(np.uint32), y4.view(np.uint32)), (fmt, wpg, N, K)
+
+
+@pytest.mark.parametrize("fmt", ("q8_0", "affine4"))
+@pytest.mark.parametrize("N", (2560, 6144, 5000))
+def test_lds_workgroup_size_argmax(fmt, N):
+    """kq_gemv_argmax at one column where the launcher picks 12 waves per
+    workgroup (2560 x 2560 affine4: two units per lane) or 4: y equals
+    kq_gemv's, the index is the first maximum of y, and y meets the bar."""
+    K = 2560
+    packed, fields, x = _case(fmt, N, K, 1, 14)
+    Wd = U.to_dev(packed)
+    xd = U.to_dev(x)
+    wsb = kq.kq_gemv_argmax_workspace_bytes(fmt, N, K, 1)
+    ws = U.empty_dev(((max(wsb, 4) + 3) // 4,))
+    y = U.empty_dev((1, N))
+    out = U.empty_dev((1,), "int32")
+    kq.kq_gemv_argmax(fmt, Wd, xd, y, N, K, 1, out, ws, wsb)
+    yh = U.to_host(y)
+    y1 = U.gemv_gpu(fmt, Wd, x, N, K)
+    yr, ad = R.gemv(fmt, fields, x)
+    U.assert_parity(yh, yr, ad, f"{fmt} balanced argmax N={N}")
+    assert np.array_equal(yh.view(np.uint32), y1.view(np.uint32))
+    assert int(U.to_host(out)[0]) == int(np.argmax(yh[0]))
