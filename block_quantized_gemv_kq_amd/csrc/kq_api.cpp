@@ -60,7 +60,7 @@ const TuneName kTuneNames[] = {
     {"mfma_xf", kq::TUNE_MFMA_XF},               {"mfma_pers_tpw", kq::TUNE_MFMA_PERS_TPW},
     {"mfma_chunk_l2cg", kq::TUNE_MFMA_CHUNK_L2CG}, {"moe_unfused", kq::TUNE_MOE_UNFUSED},
     {"moe_min_wg", kq::TUNE_MOE_MIN_WG},          {"log", kq::TUNE_LOG},
-    {"mfma_pers_waves", kq::TUNE_MFMA_PERS_WAVES},
+    {"mfma_pers_waves", kq::TUNE_MFMA_PERS_WAVES}, {"moe_one", kq::TUNE_MOE_ONE},
 };
 
 // Parse a tuning value: force_path and mfma_variant take names, the others integers.

@@ -29,6 +29,7 @@ enum TuneKey {
   TUNE_MFMA_CHUNK_L2CG,  // chunked kernel: log2 of groups per chunk
   TUNE_MOE_UNFUSED,      // 1: one-token MoE down + weighted sum as two kernels
   TUNE_MOE_MIN_WG,       // routed-expert kernels: widen lane groups below this many workgroups
+  TUNE_MOE_ONE,          // 0: one-token gate|up through the general routed-expert kernel
   TUNE_LOG,              // 1: one line per kernel launch on stderr (the dispatch log)
   TUNE_COUNT
 };

@@ -335,6 +335,96 @@ __global__ __launch_bounds__(256) void k_moe_lds(const uint8_t* __restrict__ W0,
   }
 }
 
+// One token (M = 1): gate|up + SwiGLU with the routing off the weights' path.
+// Grid and lane layout as k_moe_lds (row tiles x top_k slots, G lanes per
+// row). The workgroup of slot p reads its expert id e with a scalar load,
+// issues the token's activation loads, then its gate and up weight loads,
+// and only then checks (scalar loads of the earlier slots' ids) whether an
+// earlier slot names e: then it stops, and that slot's workgroup writes h for
+// every slot routed to e. A router gives one token distinct experts, so the
+// early weight loads are normally all used. The sums are those of k_moe_lds
+// for one column (the same h bits). Dynamic LDS: x (K fp16), its block sums,
+// a 16-byte idle slot. K <= 256 * 8 * XCH, top_k <= 16, expert_bytes < 2^31.
+typedef const __attribute__((address_space(4))) int32_t* const_id_ptr;
+
+template <int FMT, int ITERS, int XCH, int NIDS>
+__global__ __launch_bounds__(256) void k_moe_gate_up_one(const uint8_t* __restrict__ Wg,
+                                                        const uint8_t* __restrict__ Wu,
+                                                        const uint16_t* __restrict__ x,
+                                                        const int32_t* __restrict__ ids,
+                                                        uint16_t* __restrict__ h, int expert_bytes, int N, int K,
+                                                        int top_k, int n_experts, int log2g) {
+  extern __shared__ u32x4 x_lds4[];
+  uint32_t* xl = reinterpret_cast<uint32_t*>(x_lds4);
+  const int kdw = K / 2;
+  const int nblk = K / 32;
+  float* xs = reinterpret_cast<float*>(xl + kdw);
+  const int p = blockIdx.y;
+  // the token's activations: registers, ahead of the weights
+  const int kq8 = K / 8;
+  const rsrc_t xsrc = make_rsrc(x, (uint32_t)K * 2u);
+  u32x4 xr[XCH];
+#pragma unroll
+  for (int c = 0; c < XCH; ++c) {
+    const int i = (int)threadIdx.x + 256 * c;
+    xr[c] = ld128(xsrc, i < kq8 ? (uint32_t)i * 16u : OOB);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // every slot's id in one round of scalar loads (NIDS >= top_k of them,
+  // indexes clamped into the table), this slot's picked out by selects
+  const const_id_ptr sid = (const_id_ptr)ids;
+  int idv[NIDS];
+#pragma unroll
+  for (int q = 0; q < NIDS; ++q) idv[q] = sid[q < top_k ? q : top_k - 1];
+  int e = idv[0];
+#pragma unroll
+  for (int q = 1; q < NIDS; ++q) e = q == p ? idv[q] : e;
+  const bool ok = e >= 0 && e < n_experts;   // else read nothing, write NaN
+  const int lane = threadIdx.x & 63;
+  const int G = 1 << log2g;
+  const int rpw = 64 >> log2g;
+  const int64_t row_base = (int64_t)(blockIdx.x * 4 + wave_id()) * rpw;
+  const int rho = lane >> log2g, g = lane & (G - 1);
+  const uint32_t row_bytes = (uint32_t)nblk * Fmt<FMT>::BB;
+  const int rows = row_base < N ? (int)min<int64_t>(rpw, N - row_base) : 0;
+  const int valid = ok ? rows : 0;
+  const int64_t off = valid ? (int64_t)e * expert_bytes + row_base * row_bytes : 0;
+  const rsrc_t r0 = make_rsrc(Wg + off, (uint32_t)valid * row_bytes);
+  const rsrc_t r1 = make_rsrc(Wu + off, (uint32_t)valid * row_bytes);
+  const uint32_t roff = (uint32_t)rho * row_bytes;
+  const int units = K / (32 * Fmt<FMT>::UB);
+  Loaded<FMT, ITERS> w0, w1;
+  issue_units<FMT, ITERS>(r0, roff, g, G, units, w0);
+  issue_units<FMT, ITERS>(r1, roff, g, G, units, w1);
+  __builtin_amdgcn_sched_barrier(0);
+  // an earlier slot with the same expert serves this one
+  bool dup = false;
+#pragma unroll
+  for (int q = 0; q < NIDS; ++q) dup |= q < p && idv[q] == e;
+  if (dup) return;   // uniform over the workgroup
+  const int idle = (kdw + nblk * 2 + 3) / 4;
+#pragma unroll
+  for (int c = 0; c < XCH; ++c) {
+    const int i = (int)threadIdx.x + 256 * c;
+    x_lds4[i < kq8 ? i : idle] = xr[c];   // unused pieces land in the idle slot
+  }
+  __syncthreads();
+  block_sums_to_lds(xl, kdw, 1, xs, 256);
+  __syncthreads();
+  float b0[1] = {0.0f}, b1[1] = {0.0f};
+  consume_units<FMT, 1, ITERS>(w0, xl, xs, kdw, g, G, units, b0);
+  consume_units<FMT, 1, ITERS>(w1, xl, xs, kdw, g, G, units, b1);
+  group_reduce<1>(b0, G);
+  group_reduce<1>(b1, G);
+  if (g == 0 && rho < rows) {
+    const float z = b0[0];
+    const uint16_t hv = ok ? (uint16_t)f2h_bits(z / (1.0f + __expf(-z)) * b1[0]) : (uint16_t)0x7e00;
+#pragma unroll
+    for (int q = 0; q < NIDS; ++q)
+      if (q >= p && q < top_k && idv[q] == e) h[(int64_t)q * N + row_base + rho] = hv;
+  }
+}
+
 // One token (M = 1), weighted: the down projection of every routed slot and
 // their weighted sum in one launch. Workgroup = top_k waves over the same rpw
 // rows; wave j computes slot j exactly as k_moe_lds does for one column (x of
@@ -346,9 +436,9 @@ __global__ __launch_bounds__(256) void k_moe_lds(const uint8_t* __restrict__ W0,
 // then top_k x rpw fp32 slot results.
 template <int FMT, int ITERS>
 __global__ __launch_bounds__(1024) void k_moe_down_sum(const uint8_t* __restrict__ W, const uint16_t* __restrict__ x,
-                                                      const int32_t* __restrict__ ids, const float* __restrict__ rw,
-                                                      float* __restrict__ y, int N, int K, int top_k, int n_experts,
-                                                      int x_per_slot, int log2g, int64_t expert_bytes) {
+                                                      const int32_t* __restrict__ ids, int expert_bytes, int N, int K,
+                                                      int n_experts, int log2g, int x_per_slot, int top_k,
+                                                      const float* __restrict__ rw, float* __restrict__ y) {
   extern __shared__ u32x4 x_lds4[];
   const int lane = threadIdx.x & 63;
   const int j = wave_id();                       // this wave's slot
@@ -362,15 +452,10 @@ __global__ __launch_bounds__(1024) void k_moe_down_sum(const uint8_t* __restrict
   const int64_t row_base = (int64_t)blockIdx.x * rpw;
   const int rho = lane >> log2g, g = lane & (G - 1);
   const int valid = row_base < N ? (int)min<int64_t>(rpw, N - row_base) : 0;
-  const int e = ids[j];
-  const bool e_ok = e >= 0 && e < n_experts;
-  const uint32_t row_bytes = (uint32_t)nblk * Fmt<FMT>::BB;
-  const int64_t off = (int64_t)(e_ok ? e : 0) * expert_bytes + (valid ? row_base * row_bytes : 0);
-  const rsrc_t rs = make_rsrc(W + off, e_ok ? (uint32_t)valid * row_bytes : 0u);
-  const uint32_t roff = (uint32_t)rho * row_bytes;
-  const int units = K / (32 * Fmt<FMT>::UB);
   const int kq8 = K / 8;
-  // x of this slot into registers, then the weights, then x into LDS
+  // x of this slot into registers (it does not depend on the route id), then
+  // the id (a scalar load; the arguments it needs are in preloaded
+  // registers), then the weights, then x into LDS
   const rsrc_t xsrc = make_rsrc(x + (int64_t)(x_per_slot ? j : 0) * K, (uint32_t)K * 2u);
   u32x4 xr[MOE_XCH];
 #pragma unroll
@@ -379,6 +464,13 @@ __global__ __launch_bounds__(1024) void k_moe_down_sum(const uint8_t* __restrict
     xr[c] = ld128(xsrc, i < kq8 ? (uint32_t)i * 16u : OOB);
   }
   __builtin_amdgcn_sched_barrier(0);
+  const int e = ((const_id_ptr)ids)[j];
+  const bool e_ok = e >= 0 && e < n_experts;
+  const uint32_t row_bytes = (uint32_t)nblk * Fmt<FMT>::BB;
+  const int64_t off = (int64_t)(e_ok ? e : 0) * expert_bytes + (valid ? row_base * row_bytes : 0);
+  const rsrc_t rs = make_rsrc(W + off, e_ok ? (uint32_t)valid * row_bytes : 0u);
+  const uint32_t roff = (uint32_t)rho * row_bytes;
+  const int units = K / (32 * Fmt<FMT>::UB);
   Loaded<FMT, ITERS> w;
   issue_units<FMT, ITERS>(rs, roff, g, G, units, w);
   __builtin_amdgcn_sched_barrier(0);
@@ -580,11 +672,45 @@ int moe_dispatch(const MoeArgs& a) {
   return (int)hipGetLastError();
 }
 
+template <int FMT, int XCH, int NIDS>
+int launch_moe_gate_up_one(const MoeGateUpArgs& a, int64_t eb) {
+  const int units = (int)(a.hidden / (32 * Fmt<FMT>::UB));
+  const int log2g = moe_slot_log2g<FMT>(units, a.inter, a.top_k);
+  const int iters = (units + (1 << log2g) - 1) >> log2g;
+  const int64_t rpw = 64 >> log2g;
+  const int64_t waves = (a.inter + rpw - 1) / rpw;
+  const dim3 grid((unsigned)((waves + 3) / 4), (unsigned)a.top_k), block(256);
+  const size_t lds = (size_t)a.hidden * 2 + (size_t)(a.hidden / 32) * 8 + 16 + 16;
+  dispatch_log("k_moe_gate_up_one", FMT, a.inter, a.hidden, 1, grid.x, grid.y, 256, lds, "G=%d units/lane=%d slots=%d",
+               1 << log2g, iters, a.top_k);
+#define KQ_MOE_ONE(IT)                                                                                        \
+  hipLaunchKernelGGL((k_moe_gate_up_one<FMT, IT, XCH, NIDS>), grid, block, lds, a.stream, a.Wg, a.Wu, a.x, a.ids, a.h, \
+                     (int)eb, (int)a.inter, (int)a.hidden, a.top_k, a.n_experts, log2g)
+  switch (iters) {
+    case 1: KQ_MOE_ONE(1); break;
+    case 2: KQ_MOE_ONE(2); break;
+    case 3: KQ_MOE_ONE(3); break;
+    case 4: KQ_MOE_ONE(4); break;
+    default: KQ_MOE_ONE(5); break;
+  }
+#undef KQ_MOE_ONE
+  return (int)hipGetLastError();
+}
+
 template <int FMT>
 int gate_up_dispatch(const MoeGateUpArgs& a) {
   const int64_t eb = a.inter * (a.hidden / 32) * Fmt<FMT>::BB;
   const int P = a.M * a.top_k;
   const int units = (int)(a.hidden / (32 * Fmt<FMT>::UB));
+  // one token: the routing-off-the-path kernel (the moe_one tuning override,
+  // 0, forces the general kernel)
+  if (a.M == 1 && a.top_k <= 16 && a.hidden % (32 * Fmt<FMT>::UB) == 0 && tune(TUNE_MOE_ONE) != 0 &&
+      eb <= INT32_MAX && (int64_t)a.hidden * 2 + (a.hidden / 32) * 8 + 32 <= 64 * 1024) {
+    if (a.hidden / 8 <= 256)
+      return a.top_k <= 8 ? launch_moe_gate_up_one<FMT, 1, 8>(a, eb) : launch_moe_gate_up_one<FMT, 1, 16>(a, eb);
+    if (a.hidden / 8 <= 1024)
+      return a.top_k <= 8 ? launch_moe_gate_up_one<FMT, 4, 8>(a, eb) : launch_moe_gate_up_one<FMT, 4, 16>(a, eb);
+  }
   if (moe_lds_fits(a.hidden))
     return launch_moe_lds<FMT, true>(a.Wg, a.Wu, a.x, a.ids, a.h, a.inter, a.hidden, a.M, a.top_k, a.n_experts, 0,
                                      eb, a.stream);
@@ -609,8 +735,8 @@ int launch_moe_down_sum_fmt(const MoeArgs& a, const float* rw, float* y) {
   dispatch_log("k_moe_down_sum", FMT, a.N, a.K, a.M, grid.x, 1, block.x, lds, "G=%d units/lane=%d top_k=%d",
                1 << log2g, iters, a.top_k);
 #define KQ_MOE_DS(IT)                                                                                          \
-  hipLaunchKernelGGL((k_moe_down_sum<FMT, IT>), grid, block, lds, a.stream, a.W, a.x, a.ids, rw, y, (int)a.N,   \
-                     (int)a.K, a.top_k, a.n_experts, a.x_per_slot, log2g, eb)
+  hipLaunchKernelGGL((k_moe_down_sum<FMT, IT>), grid, block, lds, a.stream, a.W, a.x, a.ids, (int)eb, (int)a.N,    \
+                     (int)a.K, a.n_experts, log2g, a.x_per_slot, a.top_k, rw, y)
   switch (iters) {
     case 1: KQ_MOE_DS(1); break;
     case 2: KQ_MOE_DS(2); break;
@@ -627,7 +753,7 @@ int launch_moe_down_sum_fmt(const MoeArgs& a, const float* rw, float* y) {
 bool moe_down_sum_applies(const MoeArgs& a) {
   const int ub = (a.fmt == KQ_AFFINE4_G32 || a.fmt == KQ_Q5_1) ? 1 : 2;   // blocks per load unit
   return a.M == 1 && a.top_k >= 1 && a.top_k <= 16 && a.K % (32 * ub) == 0 && moe_lds_fits(a.K) &&
-         a.K / 8 <= 64 * MOE_XCH;
+         a.K / 8 <= 64 * MOE_XCH && a.N * (a.K / 32) * 34 <= INT32_MAX;   // expert bytes as an int
 }
 
 int launch_moe_down_sum(const MoeArgs& a, const float* route_w, float* y) {

@@ -187,3 +187,52 @@ def test_moe_ffn_one_token_same_bits_as_three_kernels():
         outs.append(U.to_host(y))
     assert np.all(np.isfinite(outs[0]))
     assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt", ("q4_0", "q8_0", "affine4", "q5_0", "q5_1"))
+@pytest.mark.parametrize("hidden", (768, 2048, 4096))
+@pytest.mark.parametrize("top_k,ids_row", [(8, None), (1, None), (4, [6, 6, 2, 6]), (3, [5, -1, 2]), (16, None)])
+def test_moe_ffn_one_token_gate_up_kernel(fmt, hidden, top_k, ids_row):
+    """One token: the gate|up kernel that reads the route ids with scalar loads
+    and issues its weight loads before the dedupe test gives the h and y bits
+    of the general routed-expert kernel (moe_one = 0) where that kernel also
+    stages x in LDS (hidden <= 2048), including a repeated expert (one
+    workgroup serves all its slots) and a bad id (NaN); and h is within the
+    bar of the oracle where the ids are valid."""
+    inter, E = 352, 16                  # 11 blocks per down row (odd for Q4_0/Q8_0 units)
+    if ids_row is None:
+        ids, rw = _route(1, E, top_k, 60 + top_k)
+    else:
+        ids = np.array([ids_row], np.int32)
+        rw = np.linspace(0.3, 0.8, top_k, dtype=np.float32)[None, :]
+    used = [v for v in ids.ravel() if 0 <= v < E]
+    gate = Experts(fmt, E, inter, hidden, used, lambda e: (76, e, 0, 0))
+    up = Experts(fmt, E, inter, hidden, used, lambda e: (76, e, 1, 0))
+    down = Experts(fmt, E, hidden, inter, used, lambda e: (76, e, 2, 0))
+    x = S.activations((76, top_k, hidden), hidden, 1)
+    wsb = kq.kq_moe_ffn_workspace_bytes(hidden, inter, 1, top_k)
+    outs = []
+    for one in ("1", "0"):
+        y = U.empty_dev((1, hidden))
+        h = U.empty_dev((1, top_k, inter), "float16")
+        h.fill_(3.0)
+        ws = U.empty_dev((wsb // 4 + 1,))
+        with U.tuning({"moe_one": one}):
+            kq.kq_moe_ffn(fmt, gate.dev, up.dev, down.dev, U.to_dev(x), U.to_dev(ids), U.to_dev(rw), y, h,
+                          hidden, inter, 1, top_k, E, ws, wsb)
+        outs.append((U.to_host(y), U.to_host(h)))
+    (y1, h1), (y0, h0) = outs
+    if hidden <= 2048:   # the general kernel stages x in LDS too: the same lanes and order
+        assert np.array_equal(h1.view(np.uint16), h0.view(np.uint16))
+        assert np.array_equal(y1.view(np.uint32), y0.view(np.uint32))
+    if np.any(ids < 0):
+        bad = np.flatnonzero(ids[0] < 0)
+        assert np.all(np.isnan(h1[0, bad])) and np.all(np.isnan(y1))
+        return
+    _, _, (g, g_abs), (u, u_abs), h_ref = R.moe_ffn(fmt, gate.field_list(E), up.field_list(E), down.field_list(E),
+                                                   x, ids, rw)
+    sig = 1.0 / (1.0 + np.exp(-g))
+    dsilu = sig * (1.0 + g * (1.0 - sig))
+    tol_h = (np.abs(dsilu * u) * R.tolerance(g_abs) + np.abs(g * sig) * R.tolerance(u_abs)
+             + 2.0 ** -10 * np.abs(h_ref.astype(np.float64)) + 2.0 ** -24)
+    assert np.all(np.abs(h1.astype(np.float64) - h_ref.astype(np.float64)) <= tol_h)
