@@ -1,9 +1,10 @@
 """Full-size workloads on the GPU, in the launch configuration the benchmark
 times (row-concatenated q|k|v and gate|up, M columns per call):
 
-* Qwen3-4B-shaped affine4 layer + Q8_0 lm_head (151936 x 2560), M = 1;
+* every layer of the Qwen3-4B-shaped affine4 stack + the Q8_0 lm_head
+  (151936 x 2560), M = 1;
 * speculative verify on those weights, M in {2, 4, 8, 16, 48};
-* Qwen3-0.6B-shaped Q4_0 layer, M = 1.
+* every layer of the Qwen3-0.6B-shaped Q4_0 stack, M = 1.
 
 Dense layers are compared with the oracle on sampled rows (first, last and
 random); the lm_head is compared in full, with bit-identical argmax."""
@@ -48,7 +49,7 @@ def _check_group(stack, layer, group, x, act_desc):
     return y, ratio
 
 
-@pytest.mark.parametrize("layer", [0, 35])
+@pytest.mark.parametrize("layer", range(36))
 def test_qwen3_4b_layer_m1(layer):
     st = S.QWEN3_4B_AFFINE4
     for group in st.launch_groups:
@@ -59,13 +60,14 @@ def test_qwen3_4b_layer_m1(layer):
         assert ratio < 1e-4
 
 
-def test_qwen3_0_6b_layer_m1():
+@pytest.mark.parametrize("layer", range(28))
+def test_qwen3_0_6b_layer_m1(layer):
     st = S.QWEN3_0_6B_Q4_0
     for group in st.launch_groups:
         slot = st.per_layer[group[0]].input_slot
         K = st.per_layer[group[0]].k
-        x = S.activation_column(st.act_seed_prefix(0, slot) + (1, 0), K)[None, :]
-        _check_group(st, 0, group, x, "M=1")
+        x = S.activation_column(st.act_seed_prefix(layer, slot) + (1, 0), K)[None, :]
+        _check_group(st, layer, group, x, "M=1")
 
 
 @pytest.mark.parametrize("M", S.VERIFY_M)
