@@ -53,8 +53,6 @@ template <> struct Fix<F_AFFINE4> { static constexpr float lo = -1024.0f, hi = -
 template <> struct Fix<F_Q5_0> { static constexpr float lo = -1040.0f, hi = -1280.0f; static constexpr bool bias = false; };
 template <> struct Fix<F_Q5_1> { static constexpr float lo = -1024.0f, hi = -1024.0f; static constexpr bool bias = true; };
 
-// Formats the matrix-core kernels take (the others run on the VALU kernels).
-template <int FMT> constexpr bool has_mfma() { return FMT == F_Q8_0 || FMT == F_Q4_0 || FMT == F_AFFINE4; }
 
 constexpr uint32_t MAGIC = 0x64646464u;   // four 0x64 bytes: high byte of fp16 1024
 constexpr uint32_t SEL_LO = 0x04010400u;  // (u0, 64, u1, 64) -> fp16 pair (1024+u0, 1024+u1)

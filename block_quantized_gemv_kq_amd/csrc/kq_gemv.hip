@@ -475,19 +475,6 @@ int launch_generic(const GemvArgs& a) {
 
 template <int FMT>
 int dispatch(const GemvArgs& a) {
-  if constexpr (!has_mfma<FMT>()) {
-    // the 5-bit formats: the LDS-staged VALU kernel, up to 4 columns per pass
-    // (weights read once per pass); the register-x kernel (8 columns per
-    // pass) where x does not fit. On the 19456 x 2560 and 2560 x 9728
-    // shapes at 8 columns the passes of 4 take Q5_0 54 / 53 us against 110 /
-    // 74 us on the register-x kernel, Q5_1 34 us either way.
-    if (a.K % (32 * Fmt<FMT>::UB) != 0) return launch_generic<FMT>(a);
-    const int force = tune_int(TUNE_FORCE_PATH);
-    if (force == 'g') return launch_generic<FMT>(a);
-    const bool lds_ok = (int64_t)(a.M < LDS_MAX_MT ? a.M : LDS_MAX_MT) * (a.K * 2 + a.K / 4) <= LDS_MAX_BYTES;
-    if (force == 'v' || !lds_ok) return launch_valu<FMT>(a);
-    return launch_lds<FMT>(a);
-  }
   if (a.K % (32 * Fmt<FMT>::UB) != 0) return a.M >= MFMA_MIN_M_UNALIGNED ? launch_gemv_mfma(a) : launch_generic<FMT>(a);
   const int force = tune_int(TUNE_FORCE_PATH);  // tests: run a given path at any shape
   if (force == 'g') return launch_generic<FMT>(a);
@@ -521,31 +508,7 @@ namespace {
 template <int FMT>
 int dispatch_invariant(const GemvArgs& a) {
   if (a.K % (32 * Fmt<FMT>::UB) != 0) return launch_generic<FMT>(a);
-  if constexpr (has_mfma<FMT>()) {
-    return launch_gemv_mfma_invariant(a);
-  } else {
-    // 5-bit formats: the one-column VALU kernels over the columns, up to 4
-    // per pass through LDS (or 8 with x in registers for long rows); their
-    // lane groups, units per lane and passes come from N and K alone
-    const int64_t col_bytes = a.K * 2 + a.K / 4;   // x and block sums of one column in LDS
-    if (col_bytes > LDS_MAX_BYTES) return launch_valu<FMT>(a);
-    const int64_t fit = LDS_MAX_BYTES / col_bytes;
-    const int max_mt = fit < LDS_MAX_MT ? (int)fit : LDS_MAX_MT;
-    const int units = (int)(a.K / (32 * Fmt<FMT>::UB));
-    const LdsCfg c = lds_cfg(a.N, units, Fmt<FMT>::BB * Fmt<FMT>::UB);
-    for (int m0 = 0; m0 < a.M; m0 += max_mt) {
-      const int mt = a.M - m0 < max_mt ? a.M - m0 : max_mt;
-      int err;
-      switch (mt) {
-        case 1: err = launch_lds_mt<FMT, 1>(a, m0, c); break;
-        case 2: err = launch_lds_mt<FMT, 2>(a, m0, c); break;
-        case 3: err = launch_lds_mt<FMT, 3>(a, m0, c); break;
-        default: err = launch_lds_mt<FMT, 4>(a, m0, c); break;
-      }
-      if (err) return err;
-    }
-    return 0;
-  }
+  return launch_gemv_mfma_invariant(a);
 }
 
 }  // namespace

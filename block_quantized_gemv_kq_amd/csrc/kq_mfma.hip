@@ -63,6 +63,8 @@ template <int FMT> struct GroupRaw;
 template <> struct GroupRaw<F_AFFINE4> { uint32_t D[5]; };    // s|b, 4 nibble dwords
 template <> struct GroupRaw<F_Q4_0> { uint32_t D[6]; };       // from the aligned dword before the nibbles
 template <> struct GroupRaw<F_Q8_0> { uint32_t D[10]; };      // idem, 8 quant dwords
+template <> struct GroupRaw<F_Q5_0> { uint32_t D[7]; };       // idem, fifth-bit word + 4 nibble dwords
+template <> struct GroupRaw<F_Q5_1> { uint32_t D[6]; };       // d|m, fifth-bit word, 4 nibble dwords
 
 // byte offset of block `blk` of the row at `roff`
 template <int FMT>
@@ -73,6 +75,12 @@ __device__ __forceinline__ void load_group(rsrc_t rs, uint32_t roff, int blk, bo
     const u32x4 t = ld128(rs, o);
     r.D[0] = t.x; r.D[1] = t.y; r.D[2] = t.z; r.D[3] = t.w;
     r.D[4] = ld32(rs, o + 16);
+  } else if constexpr (FMT == F_Q5_1) {   // 24-byte blocks: 8-byte aligned
+    const uint32_t o = valid ? off : OOB;
+    const u32x4 t = ld128(rs, o);
+    const u32x2 u = __builtin_amdgcn_raw_buffer_load_b64(rs, o + 16u, 0, 0);
+    r.D[0] = t.x; r.D[1] = t.y; r.D[2] = t.z; r.D[3] = t.w;
+    r.D[4] = u.x; r.D[5] = u.y;
   } else {
     // Quants start at qs = off + 2, 2-byte aligned. Load the aligned dwords
     // from qs & ~3 (D[1]...), and the dword before them (D[0]) only when the
@@ -85,12 +93,121 @@ __device__ __forceinline__ void load_group(rsrc_t rs, uint32_t roff, int blk, bo
     r.D[1] = t.x; r.D[2] = t.y; r.D[3] = t.z; r.D[4] = t.w;
     if constexpr (FMT == F_Q4_0) {
       r.D[5] = ld32(rs, o + 16);
+    } else if constexpr (FMT == F_Q5_0) {
+      const u32x2 u = __builtin_amdgcn_raw_buffer_load_b64(rs, o + 16u, 0, 0);
+      r.D[5] = u.x; r.D[6] = u.y;
     } else {
       const u32x4 u = ld128(rs, o + 16);
       r.D[5] = u.x; r.D[6] = u.y; r.D[7] = u.z; r.D[8] = u.w;
       r.D[9] = ld32(rs, o + 32);
     }
   }
+}
+
+// A lane's own block of a group, from its raw load: the header word (scale;
+// scale|bias for affine4; d|m for Q5_1), the quant dwords (q, and p for Q8_0's
+// second half) and the fifth-bit word (Q5_0, Q5_1).
+struct OwnBlock {
+  uint32_t hdr, q[4], p[4], qh;
+};
+
+template <int FMT>
+__device__ __forceinline__ OwnBlock own_block(const GroupRaw<FMT>& cur, uint32_t roff, int blk) {
+  OwnBlock b;
+  b.qh = 0;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) b.p[t] = 0;
+  if constexpr (FMT == F_AFFINE4) {
+    b.hdr = cur.D[0];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) b.q[t] = cur.D[1 + t];
+  } else if constexpr (FMT == F_Q5_1) {
+    b.hdr = cur.D[0];
+    b.qh = cur.D[1];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) b.q[t] = cur.D[2 + t];
+  } else {
+    // the data after the 2-byte scale starts 0 or 2 bytes into D[1]
+    const uint32_t r2 = ((roff + (uint32_t)blk * Fmt<FMT>::BB + 2u) & 3u) * 8u;  // bit shift 0/16
+    b.hdr = r2 ? (cur.D[1] & 0xffffu) : (cur.D[0] >> 16);
+    const uint32_t sh = r2 >> 3;   // byte shift 0 or 2
+    if constexpr (FMT == F_Q5_0) {
+      b.qh = __builtin_amdgcn_alignbyte(cur.D[2], cur.D[1], sh);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) b.q[t] = __builtin_amdgcn_alignbyte(cur.D[3 + t], cur.D[2 + t], sh);
+    } else {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) b.q[t] = __builtin_amdgcn_alignbyte(cur.D[2 + t], cur.D[1 + t], sh);
+      if constexpr (FMT == F_Q8_0) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) b.p[t] = __builtin_amdgcn_alignbyte(cur.D[6 + t], cur.D[5 + t], sh);
+      }
+    }
+  }
+  return b;
+}
+
+// Per-block fix-up: y += sc * D + c * (sum of x over the block), D the product
+// with the magic-number operands 1024 + q (Q8_0: 1152 + q). c removes the
+// 1024 and applies the format's offset or minimum.
+template <int FMT>
+__device__ __forceinline__ float fix_const(uint32_t hdr, float sc) {
+  if constexpr (FMT == F_AFFINE4 || FMT == F_Q5_1) return __builtin_fmaf(-1024.0f, sc, h2f(hdr >> 16));
+  else if constexpr (FMT == F_Q4_0) return -1032.0f * sc;
+  else if constexpr (FMT == F_Q5_0) return -1040.0f * sc;
+  else return -1152.0f * sc;
+}
+
+// A group's blocks in operand order: after the exchange, lane group g holds
+// for block j of the group its quant dword g (and Q8_0's dword 4 + g), its
+// header word and its fifth-bit word.
+struct GroupOps {
+  uint32_t qs[4], ps[4], hs[4], qhs[4];
+};
+
+template <int FMT>
+__device__ __forceinline__ void exchange(const OwnBlock& b, GroupOps& o) {
+  uint32_t q0 = b.q[0], q1 = b.q[1], q2 = b.q[2], q3 = b.q[3];
+  transpose4(q0, q1, q2, q3);
+  o.qs[0] = q0; o.qs[1] = q1; o.qs[2] = q2; o.qs[3] = q3;
+  if constexpr (FMT == F_Q8_0) {
+    uint32_t p0 = b.p[0], p1 = b.p[1], p2 = b.p[2], p3 = b.p[3];
+    transpose4(p0, p1, p2, p3);
+    o.ps[0] = p0; o.ps[1] = p1; o.ps[2] = p2; o.ps[3] = p3;
+  }
+  uint32_t h0 = b.hdr, h1 = b.hdr, h2 = b.hdr, h3 = b.hdr;
+  transpose4(h0, h1, h2, h3);
+  o.hs[0] = h0; o.hs[1] = h1; o.hs[2] = h2; o.hs[3] = h3;
+  if constexpr (FMT == F_Q5_0 || FMT == F_Q5_1) {
+    uint32_t e0 = b.qh, e1 = b.qh, e2 = b.qh, e3 = b.qh;
+    transpose4(e0, e1, e2, e3);
+    o.qhs[0] = e0; o.qhs[1] = e1; o.qhs[2] = e2; o.qhs[3] = e3;
+  }
+}
+
+// B operand of block j for lane group g: 8 fp16 (1024 + q, Q8_0 1152 + q) for
+// elements {4g..4g+3, 16+4g..19+4g}; a 5-bit format's fifth bits (bit i of
+// the word for element i) become +16 in those fp16 halves.
+template <int FMT>
+__device__ __forceinline__ half8_t b_operand(const GroupOps& o, int j, int g) {
+  uint32_t b0, b1, b2, b3;
+  if constexpr (FMT == F_Q8_0) {
+    const uint32_t u = o.qs[j] ^ 0x80808080u, v = o.ps[j] ^ 0x80808080u;
+    b0 = perm(MAGIC, u, SEL_LO); b1 = perm(MAGIC, u, SEL_HI);
+    b2 = perm(MAGIC, v, SEL_LO); b3 = perm(MAGIC, v, SEL_HI);
+  } else {
+    const uint32_t lo = o.qs[j] & 0x0F0F0F0Fu, hi = (o.qs[j] >> 4) & 0x0F0F0F0Fu;
+    b0 = perm(MAGIC, lo, SEL_LO); b1 = perm(MAGIC, lo, SEL_HI);
+    b2 = perm(MAGIC, hi, SEL_LO); b3 = perm(MAGIC, hi, SEL_HI);
+    if constexpr (FMT == F_Q5_0 || FMT == F_Q5_1) {
+      const uint32_t qh = o.qhs[j];
+      b0 |= spread2<4>(qh, 4 * g);
+      b1 |= spread2<4>(qh, 4 * g + 2);
+      b2 |= spread2<4>(qh, 16 + 4 * g);
+      b3 |= spread2<4>(qh, 18 + 4 * g);
+    }
+  }
+  return as_half8(b0, b1, b2, b3);
 }
 
 // Activations of one 4-block group for one 16-column tile: for block j the
@@ -117,52 +234,14 @@ template <int FMT, int T>
 __device__ __forceinline__ void consume_group(const GroupRaw<FMT>& cur, const GroupX (&cx)[T], uint32_t roff,
                                               int gi, int g, int nblk, float4_t (&acc)[T]) {
   const half8_t ones = as_half8(ONES, ONES, ONES, ONES);
-  uint32_t hdr, q0, q1, q2, q3, p0 = 0, p1 = 0, p2 = 0, p3 = 0;
-  if constexpr (FMT == F_AFFINE4) {
-    hdr = cur.D[0];
-    q0 = cur.D[1]; q1 = cur.D[2]; q2 = cur.D[3]; q3 = cur.D[4];
-  } else {
-    const uint32_t r2 = ((roff + (uint32_t)(4 * gi + g) * Fmt<FMT>::BB + 2u) & 3u) * 8u;  // bit shift 0/16
-    hdr = r2 ? (cur.D[1] & 0xffffu) : (cur.D[0] >> 16);
-    const uint32_t sh = r2 >> 3;   // byte shift 0 or 2
-    q0 = __builtin_amdgcn_alignbyte(cur.D[2], cur.D[1], sh);
-    q1 = __builtin_amdgcn_alignbyte(cur.D[3], cur.D[2], sh);
-    q2 = __builtin_amdgcn_alignbyte(cur.D[4], cur.D[3], sh);
-    q3 = __builtin_amdgcn_alignbyte(cur.D[5], cur.D[4], sh);
-    if constexpr (FMT == F_Q8_0) {
-      p0 = __builtin_amdgcn_alignbyte(cur.D[6], cur.D[5], sh);
-      p1 = __builtin_amdgcn_alignbyte(cur.D[7], cur.D[6], sh);
-      p2 = __builtin_amdgcn_alignbyte(cur.D[8], cur.D[7], sh);
-      p3 = __builtin_amdgcn_alignbyte(cur.D[9], cur.D[8], sh);
-    }
-  }
-  transpose4(q0, q1, q2, q3);
-  if constexpr (FMT == F_Q8_0) transpose4(p0, p1, p2, p3);
-  uint32_t h0 = hdr, h1 = hdr, h2 = hdr, h3 = hdr;
-  transpose4(h0, h1, h2, h3);
-  const uint32_t qs[4] = {q0, q1, q2, q3};
-  const uint32_t ps[4] = {p0, p1, p2, p3};
-  const uint32_t hs[4] = {h0, h1, h2, h3};
+  GroupOps o;
+  exchange<FMT>(own_block<FMT>(cur, roff, 4 * gi + g), o);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     if (4 * gi + j >= nblk) break;      // uniform
-    // B operand: 8 fp16 (offset + q) for elements {4g..4g+3, 16+4g..19+4g}
-    uint32_t b0, b1, b2, b3;
-    if constexpr (FMT == F_Q8_0) {
-      const uint32_t u = qs[j] ^ 0x80808080u, v = ps[j] ^ 0x80808080u;
-      b0 = perm(MAGIC, u, SEL_LO); b1 = perm(MAGIC, u, SEL_HI);
-      b2 = perm(MAGIC, v, SEL_LO); b3 = perm(MAGIC, v, SEL_HI);
-    } else {
-      const uint32_t lo = qs[j] & 0x0F0F0F0Fu, hi = (qs[j] >> 4) & 0x0F0F0F0Fu;
-      b0 = perm(MAGIC, lo, SEL_LO); b1 = perm(MAGIC, lo, SEL_HI);
-      b2 = perm(MAGIC, hi, SEL_LO); b3 = perm(MAGIC, hi, SEL_HI);
-    }
-    const half8_t B = as_half8(b0, b1, b2, b3);
-    const float sc = h2f(hs[j]);
-    float c;
-    if constexpr (FMT == F_AFFINE4) c = __builtin_fmaf(-1024.0f, sc, h2f(hs[j] >> 16));
-    else if constexpr (FMT == F_Q4_0) c = -1032.0f * sc;
-    else c = -1152.0f * sc;
+    const half8_t B = b_operand<FMT>(o, j, g);
+    const float sc = h2f(o.hs[j]);
+    const float c = fix_const<FMT>(o.hs[j], sc);
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       const half8_t A = as_half8(cx[t].lo[j].x, cx[t].lo[j].y, cx[t].hi[j].x, cx[t].hi[j].y);
@@ -309,60 +388,23 @@ __global__ __launch_bounds__(1024) void k_gemv_mfma_lds(const uint8_t* __restric
 template <int FMT, bool SX = true>
 __device__ __forceinline__ void mfma_group(const GroupRaw<FMT>& cur, uint32_t roff, int gi, int g, int ncol,
                                            const u32x4* xa, const float* sxa, int Mp, float4_t& acc) {
-  uint32_t hdr, q0, q1, q2, q3, p0 = 0, p1 = 0, p2 = 0, p3 = 0;
-  if constexpr (FMT == F_AFFINE4) {
-    hdr = cur.D[0];
-    q0 = cur.D[1]; q1 = cur.D[2]; q2 = cur.D[3]; q3 = cur.D[4];
-  } else {
-    const uint32_t r2 = ((roff + (uint32_t)(4 * gi + g) * Fmt<FMT>::BB + 2u) & 3u) * 8u;
-    hdr = r2 ? (cur.D[1] & 0xffffu) : (cur.D[0] >> 16);
-    const uint32_t sh = r2 >> 3;
-    q0 = __builtin_amdgcn_alignbyte(cur.D[2], cur.D[1], sh);
-    q1 = __builtin_amdgcn_alignbyte(cur.D[3], cur.D[2], sh);
-    q2 = __builtin_amdgcn_alignbyte(cur.D[4], cur.D[3], sh);
-    q3 = __builtin_amdgcn_alignbyte(cur.D[5], cur.D[4], sh);
-    if constexpr (FMT == F_Q8_0) {
-      p0 = __builtin_amdgcn_alignbyte(cur.D[6], cur.D[5], sh);
-      p1 = __builtin_amdgcn_alignbyte(cur.D[7], cur.D[6], sh);
-      p2 = __builtin_amdgcn_alignbyte(cur.D[8], cur.D[7], sh);
-      p3 = __builtin_amdgcn_alignbyte(cur.D[9], cur.D[8], sh);
-    }
-  }
+  const OwnBlock own = own_block<FMT>(cur, roff, 4 * gi + g);
   if constexpr (SX) {
-    float cown;
-    const float so = h2f(hdr);
-    if constexpr (FMT == F_AFFINE4) cown = __builtin_fmaf(-1024.0f, so, h2f(hdr >> 16));
-    else if constexpr (FMT == F_Q4_0) cown = -1032.0f * so;
-    else cown = -1152.0f * so;
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sxa[4 * gi * Mp], cown, acc, 0, 0, 0);
+    const float so = h2f(own.hdr);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sxa[4 * gi * Mp], fix_const<FMT>(own.hdr, so), acc, 0, 0, 0);
   }
-  transpose4(q0, q1, q2, q3);
-  if constexpr (FMT == F_Q8_0) transpose4(p0, p1, p2, p3);
-  uint32_t h0 = hdr, h1 = hdr, h2 = hdr, h3 = hdr;
-  transpose4(h0, h1, h2, h3);
-  const uint32_t qs[4] = {q0, q1, q2, q3};
-  const uint32_t ps[4] = {p0, p1, p2, p3};
-  const uint32_t hs[4] = {h0, h1, h2, h3};
+  GroupOps o;
+  exchange<FMT>(own, o);
   const int bstride = 4 * Mp;
   float4_t D[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const half8_t A = __builtin_bit_cast(half8_t, xa[(4 * gi + j) * bstride + (ncol ^ xsw(j, g, Mp))]);
-    uint32_t b0, b1, b2, b3;
-    if constexpr (FMT == F_Q8_0) {
-      const uint32_t u = qs[j] ^ 0x80808080u, v = ps[j] ^ 0x80808080u;
-      b0 = perm(MAGIC, u, SEL_LO); b1 = perm(MAGIC, u, SEL_HI);
-      b2 = perm(MAGIC, v, SEL_LO); b3 = perm(MAGIC, v, SEL_HI);
-    } else {
-      const uint32_t lo = qs[j] & 0x0F0F0F0Fu, hi = (qs[j] >> 4) & 0x0F0F0F0Fu;
-      b0 = perm(MAGIC, lo, SEL_LO); b1 = perm(MAGIC, lo, SEL_HI);
-      b2 = perm(MAGIC, hi, SEL_LO); b3 = perm(MAGIC, hi, SEL_HI);
-    }
-    D[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, as_half8(b0, b1, b2, b3), float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+    D[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, b_operand<FMT>(o, j, g), float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const float sc = h2f(hs[j]);
+    const float sc = h2f(o.hs[j]);
 #pragma unroll
     for (int v = 0; v < 4; ++v) acc[v] = __builtin_fmaf(sc, D[j][v], acc[v]);
   }
@@ -373,11 +415,8 @@ __device__ __forceinline__ void mfma_group(const GroupRaw<FMT>& cur, uint32_t ro
     for (int j = 0; j < 4; ++j) {
       const half8_t A = __builtin_bit_cast(half8_t, xa[(4 * gi + j) * bstride + (ncol ^ xsw(j, g, Mp))]);
       const float4_t Dx = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, ones, float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-      const float sc = h2f(hs[j]);
-      float c;
-      if constexpr (FMT == F_AFFINE4) c = __builtin_fmaf(-1024.0f, sc, h2f(hs[j] >> 16));
-      else if constexpr (FMT == F_Q4_0) c = -1032.0f * sc;
-      else c = -1152.0f * sc;
+      const float sc = h2f(o.hs[j]);
+      const float c = fix_const<FMT>(o.hs[j], sc);
 #pragma unroll
       for (int v = 0; v < 4; ++v) acc[v] = __builtin_fmaf(c, Dx[v], acc[v]);
     }
@@ -655,59 +694,22 @@ __global__ __launch_bounds__(512) void k_gemv_mfma_chunk(const uint8_t* __restri
       const int gi = gb + p;
       if (gi >= ge) break;   // uniform
       const int gl = gi - cg0;
-      const GroupRaw<FMT>& cur = wr[p];
-      uint32_t hdr, q0, q1, q2, q3, p0 = 0, p1 = 0, p2 = 0, p3 = 0;
-      if constexpr (FMT == F_AFFINE4) {
-        hdr = cur.D[0];
-        q0 = cur.D[1]; q1 = cur.D[2]; q2 = cur.D[3]; q3 = cur.D[4];
-      } else {
-        const uint32_t r2 = ((roff + (uint32_t)(4 * gi + g) * Fmt<FMT>::BB + 2u) & 3u) * 8u;
-        hdr = r2 ? (cur.D[1] & 0xffffu) : (cur.D[0] >> 16);
-        const uint32_t sh = r2 >> 3;
-        q0 = __builtin_amdgcn_alignbyte(cur.D[2], cur.D[1], sh);
-        q1 = __builtin_amdgcn_alignbyte(cur.D[3], cur.D[2], sh);
-        q2 = __builtin_amdgcn_alignbyte(cur.D[4], cur.D[3], sh);
-        q3 = __builtin_amdgcn_alignbyte(cur.D[5], cur.D[4], sh);
-        if constexpr (FMT == F_Q8_0) {
-          p0 = __builtin_amdgcn_alignbyte(cur.D[6], cur.D[5], sh);
-          p1 = __builtin_amdgcn_alignbyte(cur.D[7], cur.D[6], sh);
-          p2 = __builtin_amdgcn_alignbyte(cur.D[8], cur.D[7], sh);
-          p3 = __builtin_amdgcn_alignbyte(cur.D[9], cur.D[8], sh);
-        }
-      }
+      const OwnBlock own = own_block<FMT>(wr[p], roff, 4 * gi + g);
       {
-        float cown;
-        const float so = h2f(hdr);
-        if constexpr (FMT == F_AFFINE4) cown = __builtin_fmaf(-1024.0f, so, h2f(hdr >> 16));
-        else if constexpr (FMT == F_Q4_0) cown = -1032.0f * so;
-        else cown = -1152.0f * so;
+        const float so = h2f(own.hdr);
+        const float cown = fix_const<FMT>(own.hdr, so);
         const float* sx = reinterpret_cast<const float*>(xlb + sx_base);
 #pragma unroll
         for (int t = 0; t < T; ++t)
           acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(sx[(t << (6 + log2cg)) + (4 * gl + g) * 16 + n], cown,
                                                         acc[t], 0, 0, 0);
       }
-      transpose4(q0, q1, q2, q3);
-      if constexpr (FMT == F_Q8_0) transpose4(p0, p1, p2, p3);
-      uint32_t h0 = hdr, h1 = hdr, h2 = hdr, h3 = hdr;
-      transpose4(h0, h1, h2, h3);
-      const uint32_t qs[4] = {q0, q1, q2, q3};
-      const uint32_t ps[4] = {p0, p1, p2, p3};
-      const uint32_t hs[4] = {h0, h1, h2, h3};
+      GroupOps o;
+      exchange<FMT>(own, o);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        uint32_t b0, b1, b2, b3;
-        if constexpr (FMT == F_Q8_0) {
-          const uint32_t u = qs[j] ^ 0x80808080u, v = ps[j] ^ 0x80808080u;
-          b0 = perm(MAGIC, u, SEL_LO); b1 = perm(MAGIC, u, SEL_HI);
-          b2 = perm(MAGIC, v, SEL_LO); b3 = perm(MAGIC, v, SEL_HI);
-        } else {
-          const uint32_t lo = qs[j] & 0x0F0F0F0Fu, hi = (qs[j] >> 4) & 0x0F0F0F0Fu;
-          b0 = perm(MAGIC, lo, SEL_LO); b1 = perm(MAGIC, lo, SEL_HI);
-          b2 = perm(MAGIC, hi, SEL_LO); b3 = perm(MAGIC, hi, SEL_HI);
-        }
-        const half8_t B = as_half8(b0, b1, b2, b3);
-        const float sc = h2f(hs[j]);
+        const half8_t B = b_operand<FMT>(o, j, g);
+        const float sc = h2f(o.hs[j]);
 #pragma unroll
         for (int t = 0; t < T; ++t) {
           const u32x4* xt = reinterpret_cast<const u32x4*>(xlb + (uint32_t)t * tile_bytes);
@@ -1137,7 +1139,9 @@ int launch_mfma_pers_p(const GemvArgs& a, int log2mp, size_t lds) {
 // Groups in flight per wave. Deeper rings win even where they cost occupancy
 // (measured at M = 8 on 151936 x 2560: Q8_0 P = 6 / 8: 95.6 / 94.0 us, Q4_0
 // P = 8 / 10: 78.1 / 65.6 us, affine4 P = 8 / 12: 74.1 / 64.8 us).
-template <int FMT> struct MfmaPersP { static constexpr int v = FMT == F_Q8_0 ? 8 : (FMT == F_Q4_0 ? 10 : 12); };
+template <int FMT> struct MfmaPersP {
+  static constexpr int v = FMT == F_Q8_0 ? 8 : (FMT == F_AFFINE4 ? 12 : 10);   // 5-bit formats: 6-7 dwords a group
+};
 // From this many 16-row tiles on, persistent waves (one tile at a time per
 // wave) fill the device; below it, tiles are split over the waves of a workgroup.
 constexpr int64_t MFMA_PERS_MIN_TILES = 4096;
@@ -1252,6 +1256,8 @@ int launch_gemv_mfma_invariant(const GemvArgs& a) {
   switch (a.fmt) {
     case KQ_Q8_0: return launch_mfma_invariant_fmt<F_Q8_0>(a);
     case KQ_Q4_0: return launch_mfma_invariant_fmt<F_Q4_0>(a);
+    case KQ_Q5_0: return launch_mfma_invariant_fmt<F_Q5_0>(a);
+    case KQ_Q5_1: return launch_mfma_invariant_fmt<F_Q5_1>(a);
     default: return launch_mfma_invariant_fmt<F_AFFINE4>(a);
   }
 }
@@ -1260,6 +1266,8 @@ int launch_gemv_mfma(const GemvArgs& a) {
   switch (a.fmt) {
     case KQ_Q8_0: return launch_mfma_fmt<F_Q8_0>(a);
     case KQ_Q4_0: return launch_mfma_fmt<F_Q4_0>(a);
+    case KQ_Q5_0: return launch_mfma_fmt<F_Q5_0>(a);
+    case KQ_Q5_1: return launch_mfma_fmt<F_Q5_1>(a);
     default: return launch_mfma_fmt<F_AFFINE4>(a);
   }
 }

@@ -15,7 +15,7 @@ from tests import gpu_util as U
 
 pytestmark = pytest.mark.gpu
 
-FMTS = ("q8_0", "q4_0", "affine4")
+FMTS = ("q8_0", "q4_0", "affine4", "q5_0", "q5_1")
 M_LIST = (1, 2, 3, 4, 7, 8, 9, 15, 16, 17, 32, 48, 64)
 
 
@@ -51,8 +51,9 @@ def test_parity_shapes(fmt, N, K, M):
 @pytest.mark.parametrize("K", (32, 96, 160, 2592))
 @pytest.mark.parametrize("M", (2, 17))
 def test_mfma_odd_block_counts(fmt, K, M):
-    """Rows whose length is an odd number of blocks leave Q4_0/Q8_0 blocks
-    only 2-byte aligned; the matrix-core path realigns them in registers."""
+    """Rows whose length is an odd number of blocks leave Q4_0/Q8_0/Q5_0
+    blocks only 2-byte aligned; the matrix-core path realigns them in
+    registers."""
     N = 45
     packed, fields, x = _case(fmt, N, K, M, 6)
     y = U.gemv_gpu(fmt, U.to_dev(packed), x, N, K)
@@ -207,7 +208,7 @@ def test_mfma_variants_parity(fmt, variant, N, K, M):
     assert np.array_equal(y, y2), "not deterministic run to run"
 
 
-@pytest.mark.parametrize("fmt", ("q8_0", "q4_0", "affine4"))
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("N,K,M", [(50, 2048, 17), (130, 1024, 64), (4000, 256, 48), (4096, 512, 33)])
 def test_chunk_column_groups(fmt, N, K, M):
     """Past 16 columns the chunked kernel runs one workgroup per tile and 16

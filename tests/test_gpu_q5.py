@@ -1,9 +1,9 @@
 """GPU tests of the 5-bit formats (Q5_0, Q5_1) through the C ABI: packer bytes
 equal the oracle's (every case packs through kq_pack and checks), parity of
 kq_gemv with the fp64 oracle on every kernel path these formats take (the
-LDS-staged kernel 4 columns per pass, the register-x kernel 8 columns per pass
-for rows whose x does not fit, the generic kernel for 2-byte-aligned Q5_0
-rows), unit vectors giving w' exactly (which
+one-column LDS-staged and register-x kernels, the matrix-core kernels from 4
+columns on, the generic kernel for 2-byte-aligned Q5_0 rows at one column),
+unit vectors giving w' exactly (which
 pins the fifth-bit and nibble order on the GPU), the output-layer argmax,
 batch-invariant columns, and the routed-expert FFN."""
 import numpy as np
@@ -40,7 +40,7 @@ def test_parity(fmt, N, K, M):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("path", ("lds", "valu", "generic"))
+@pytest.mark.parametrize("path", ("lds", "valu", "generic", "mfma"))
 @pytest.mark.parametrize("M", (1, 3, 5))
 def test_every_path(fmt, path, M):
     for N, K in ((300, 2560), (17, 9728), (64, 4096)):
@@ -51,7 +51,7 @@ def test_every_path(fmt, path, M):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("path", (None, "valu", "generic"))
+@pytest.mark.parametrize("path", (None, "valu", "generic", "mfma"))
 def test_unit_vectors_exact(fmt, path):
     """x = e_k gives y[n] = w'[n][k] bit for bit: w' = d(q - 16) or dq + m is
     exact in fp32, so every fifth bit and nibble lands on its element."""
@@ -64,6 +64,30 @@ def test_unit_vectors_exact(fmt, path):
         x[0, k] = 1.0
         y = U.gemv_gpu(fmt, Wdev, x, N, K, path=path)
         assert np.array_equal(y[0].astype(np.float64), Wd[:, k]), (fmt, path, k)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("variant", ("teams", "teams_sx", "pers", "chunk", "direct"))
+def test_unit_vectors_exact_matrix_cores(fmt, variant):
+    """Sixteen columns at once, column m = e_k for k over every element slot
+    of a block (both nibble halves, every fifth-bit position) and block
+    boundaries: each matrix-core kernel gives y[m][n] = w'[n][k_m] bit for bit
+    (1024 + q and the fix-up terms are exact in fp32), so the fifth bits reach
+    the right halves of the operand in every lane group."""
+    N, K = 40, 128
+    packed, fields, _ = _case(fmt, N, K, 1, 5)
+    Wd = F.dequantize(fmt, fields)
+    Wdev = U.to_dev(packed)
+    for ks in ((0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15),
+               (16, 17, 18, 19, 20, 21, 22, 23, 24, 25, 26, 27, 28, 29, 30, 31),
+               (32, 47, 48, 63, 64, 79, 80, 95, 96, 100, 111, 112, 113, 119, 126, 127)):
+        x = np.zeros((16, K), np.float16)
+        for m, k in enumerate(ks):
+            x[m, k] = 1.0
+        with U.tuning({"mfma_variant": variant}):
+            y = U.gemv_gpu(fmt, Wdev, x, N, K, path="mfma")
+        for m, k in enumerate(ks):
+            assert np.array_equal(y[m].astype(np.float64), Wd[:, k]), (fmt, variant, k)
 
 
 @pytest.mark.parametrize("fmt", FMTS)
