@@ -440,14 +440,19 @@ __device__ __forceinline__ void stage_x_mfma(const uint16_t* __restrict__ x, int
   const rsrc_t xs = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
   // Wave chunk q = wv + nwaves * c: 64 consecutive 16-byte pieces of one
   // column, column q & (Mp - 1), pieces 64 (q >> log2mp) + lane, so the lanes
-  // of one load read 1 KB of contiguous memory.
+  // of one load read 1 KB of contiguous memory. Chunks past the nq the
+  // staging needs are not issued at all (a branch uniform over the wave): a
+  // load that reads nothing still takes the CU's address unit as long as a
+  // real one, and every workgroup on the CU stages its own copy of x.
+  const int nq = Mp * ((kq8p + 63) / 64);
   u32x4 xr[XST_MAX];
 #pragma unroll
   for (int c = 0; c < XST_MAX; ++c) {
     const int q = wv + nwaves * c;
     const int col = q & (Mp - 1), k8 = 64 * (q >> log2mp) + lane;
     const bool ok = col < M && k8 < kq8;
-    xr[c] = ld128(xs, ok ? ((uint32_t)col * (uint32_t)kq8 + (uint32_t)k8) * 16u : OOB);
+    xr[c] = q < nq ? ld128(xs, ok ? ((uint32_t)col * (uint32_t)kq8 + (uint32_t)k8) * 16u : OOB)
+                   : u32x4{0u, 0u, 0u, 0u};
   }
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (!XF) {
@@ -466,7 +471,7 @@ __device__ __forceinline__ void stage_x_mfma(const uint16_t* __restrict__ x, int
     for (int c = 0; c < XST_MAX; ++c) {
       const int q = wv + nwaves * c;
       const int col = q & (Mp - 1), k8 = 64 * (q >> log2mp) + lane;
-      if (k8 < kq8p) {   // pieces past the padded K have no slot
+      if (q < nq && k8 < kq8p) {   // pieces past the padded K have no slot
         const uint32_t a0 = (uint32_t)((4 * (k8 >> 2) + g0) * Mp + (col ^ sw)) * 16u + part;
         *reinterpret_cast<u32x2*>(xlb + a0) = u32x2{xr[c].x, xr[c].y};
         *reinterpret_cast<u32x2*>(xlb + a0 + (uint32_t)Mp * 16u) = u32x2{xr[c].z, xr[c].w};

@@ -136,8 +136,7 @@ int kq_unpack(int fmt, const void* packed, int64_t N, int64_t K, float* W_out);
  *   W: device, packed N x K matrix (kq_pack layout), 4-byte aligned.
  *   x: device, fp16 bits [M][K] (column m contiguous), 16-byte aligned.
  *   y: device, fp32 [M][N], 4-byte aligned; overwritten, never accumulated.
- * Every weight byte is read once per call whatever M is (Q5_0 and Q5_1, which
- * run on the VALU kernels only, read it once per 4 columns).
+ * Every weight byte is read once per call whatever M is.
  * Accumulation is fp32;
  * results are run-to-run deterministic (fixed reduction order, no atomics).
  * M == 0 or N == 0 is a valid empty call. 1 <= M <= KQ_MAX_M.
