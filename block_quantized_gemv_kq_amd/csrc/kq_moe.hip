@@ -275,17 +275,21 @@ __global__ __launch_bounds__(256) void k_moe_lds(const uint8_t* __restrict__ W0,
   for (int c0 = 0; c0 < cnt; c0 += MOE_COLS) {
     const int mt = cnt - c0 < MOE_COLS ? cnt - c0 : MOE_COLS;
     if (c0 > 0) __syncthreads();   // the previous pass has finished reading LDS
-    // x of this pass's tokens, then the weights (so writing x waits for x alone)
-    // (branch-free: a load used only inside a branch would be moved behind
-    // the weight loads, and writing x would then wait for them too)
+    // x of this pass's tokens, then the weights (so writing x waits for x alone).
+    // The stores below are unconditional: a load used only inside a branch
+    // would be moved behind the weight loads, and writing x would then wait
+    // for them too. Loads a whole wave would make past the pass's x are not
+    // issued (a wave-uniform test): they would still occupy the address unit.
     u32x4 xr[MOE_XCH];
+    const int wave_i0 = wave_id() * 64;
 #pragma unroll
     for (int c = 0; c < MOE_XCH; ++c) {
       const int i = (int)threadIdx.x + 256 * c;
       const int m = i / kq8, k8 = i - m * kq8;
       const int q = s_list[c0 + (m < mt ? m : 0)];
       const uint32_t xrow = (uint32_t)((GATE_UP || !x_per_slot) ? q / top_k : q);
-      xr[c] = ld128(xsrc, m < mt ? (xrow * (uint32_t)kq8 + (uint32_t)k8) * 16u : OOB);
+      xr[c] = wave_i0 + 256 * c < mt * kq8 ? ld128(xsrc, m < mt ? (xrow * (uint32_t)kq8 + (uint32_t)k8) * 16u : OOB)
+                                           : u32x4{0u, 0u, 0u, 0u};
     }
     __builtin_amdgcn_sched_barrier(0);
     Loaded<FMT, ITERS> w0, w1;
@@ -364,10 +368,11 @@ __global__ __launch_bounds__(256) void k_moe_gate_up_one(const uint8_t* __restri
   const int kq8 = K / 8;
   const rsrc_t xsrc = make_rsrc(x, (uint32_t)K * 2u);
   u32x4 xr[XCH];
+  const int wave_i0 = wave_id() * 64;
 #pragma unroll
-  for (int c = 0; c < XCH; ++c) {
+  for (int c = 0; c < XCH; ++c) {   // (loads a whole wave would make past x are not issued)
     const int i = (int)threadIdx.x + 256 * c;
-    xr[c] = ld128(xsrc, i < kq8 ? (uint32_t)i * 16u : OOB);
+    xr[c] = wave_i0 + 256 * c < kq8 ? ld128(xsrc, i < kq8 ? (uint32_t)i * 16u : OOB) : u32x4{0u, 0u, 0u, 0u};
   }
   __builtin_amdgcn_sched_barrier(0);
   // every slot's id in one round of scalar loads (NIDS >= top_k of them,
