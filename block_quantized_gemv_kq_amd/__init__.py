@@ -33,6 +33,8 @@ SIGNATURES = {
     "kq_pack": (_I32, [_I32, _P, _I64, _I64, _P, _I32]),
     "kq_unpack": (_I32, [_I32, _P, _I64, _I64, _P]),
     "kq_gemv": (_I32, [_I32, _P, _P, _P, _I64, _I64, _I32, _P]),
+    "kq_gemv_ws": (_I32, [_I32, _P, _P, _P, _I64, _I64, _I32, _P, _I64, _P]),
+    "kq_gemv_workspace_bytes": (_I64, [_I32, _I64, _I64, _I32]),
     "kq_gemv_invariant": (_I32, [_I32, _P, _P, _P, _I64, _I64, _I32, _P]),
     "kq_gemv_argmax_workspace_bytes": (_I64, [_I32, _I64, _I64, _I32]),
     "kq_gemv_argmax": (_I32, [_I32, _P, _P, _P, _I64, _I64, _I32, _P, _P, _I64, _P]),
@@ -193,6 +195,16 @@ def kq_set_tuning(name: str | None, value: str | None) -> None:
 def kq_gemv(fmt, W, x, y, N: int, K: int, M: int, stream=None) -> None:
     """y[M][N] (fp32, device) = dequant(W)[N][K] @ x[M][K]^T (x fp16 bits, device)."""
     _check(lib().kq_gemv(_fmt(fmt), _ptr(W), _ptr(x), _ptr(y), N, K, M, _stream(stream)), "kq_gemv")
+
+
+def kq_gemv_workspace_bytes(fmt, N: int, K: int, M: int) -> int:
+    return _check(lib().kq_gemv_workspace_bytes(_fmt(fmt), N, K, M), "kq_gemv_workspace_bytes")
+
+
+def kq_gemv_ws(fmt, W, x, y, N: int, K: int, M: int, workspace, workspace_bytes: int, stream=None) -> None:
+    """kq_gemv with a caller-owned workspace (K split across workgroups where it pays)."""
+    _check(lib().kq_gemv_ws(_fmt(fmt), _ptr(W), _ptr(x), _ptr(y), N, K, M, _ptr(workspace), workspace_bytes,
+                            _stream(stream)), "kq_gemv_ws")
 
 
 def kq_gemv_argmax_workspace_bytes(fmt, N: int, K: int, M: int) -> int:

@@ -61,6 +61,7 @@ const TuneName kTuneNames[] = {
     {"mfma_chunk_l2cg", kq::TUNE_MFMA_CHUNK_L2CG}, {"moe_unfused", kq::TUNE_MOE_UNFUSED},
     {"moe_min_wg", kq::TUNE_MOE_MIN_WG},          {"log", kq::TUNE_LOG},
     {"mfma_pers_waves", kq::TUNE_MFMA_PERS_WAVES}, {"moe_one", kq::TUNE_MOE_ONE},
+    {"mfma_split", kq::TUNE_MFMA_SPLIT},
 };
 
 // Parse a tuning value: force_path and mfma_variant take names, the others integers.
@@ -200,6 +201,38 @@ int kq_gemv(int fmt, const void* W, const uint16_t* x, float* y, int64_t N, int6
   if (!aligned(x, 16)) return fail(KQ_ERR_ALIGN, "kq_gemv: x must be 16-byte aligned");
   kq::GemvArgs a{fmt, static_cast<const uint8_t*>(W), x, y, N, K, M, static_cast<hipStream_t>(stream)};
   return hip_status(kq::launch_gemv(a), "kq_gemv");
+}
+
+int64_t kq_gemv_workspace_bytes(int fmt, int64_t N, int64_t K, int M) {
+  int st = check_fmt_k(fmt, K);
+  if (st) return st;
+  if ((st = check_n(N, "N"))) return st;
+  if (M < 0 || M > KQ_MAX_M) return fail(KQ_ERR_ARG, "M=%d must be in [0, %d]", M, KQ_MAX_M);
+  kq::GemvArgs a{fmt, nullptr, nullptr, nullptr, N, K, M, nullptr};
+  return kq::gemv_split_bytes(a);
+}
+
+int kq_gemv_ws(int fmt, const void* W, const uint16_t* x, float* y, int64_t N, int64_t K, int M, void* workspace,
+               int64_t workspace_bytes, void* stream) {
+  int st = check_fmt_k(fmt, K);
+  if (st) return st;
+  if ((st = check_n(N, "N"))) return st;
+  if (M < 0 || M > KQ_MAX_M) return fail(KQ_ERR_ARG, "M=%d must be in [0, %d]", M, KQ_MAX_M);
+  if (M == 0 || N == 0) return ok();
+  if (!W || !x || !y) return fail(KQ_ERR_ARG, "kq_gemv_ws: null pointer");
+  if (!aligned(W, 4) || !aligned(y, 4)) return fail(KQ_ERR_ALIGN, "kq_gemv_ws: W and y must be 4-byte aligned");
+  if (!aligned(x, 16)) return fail(KQ_ERR_ALIGN, "kq_gemv_ws: x must be 16-byte aligned");
+  if (workspace_bytes < 0) return fail(KQ_ERR_ARG, "kq_gemv_ws: negative workspace size");
+  kq::GemvArgs a{fmt, static_cast<const uint8_t*>(W), x, y, N, K, M, static_cast<hipStream_t>(stream)};
+  const int64_t need = kq::gemv_split_bytes(a);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need)
+      return fail(KQ_ERR_ARG, "kq_gemv_ws: workspace of %lld bytes needed", (long long)need);
+    if (!aligned(workspace, 16)) return fail(KQ_ERR_ALIGN, "kq_gemv_ws: workspace must be 16-byte aligned");
+    a.ws = workspace;
+    a.ws_bytes = workspace_bytes;
+  }
+  return hip_status(kq::launch_gemv(a), "kq_gemv_ws");
 }
 
 int kq_gemv_invariant(int fmt, const void* W, const uint16_t* x, float* y, int64_t N, int64_t K, int M,

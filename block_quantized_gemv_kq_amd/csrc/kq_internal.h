@@ -30,6 +30,7 @@ enum TuneKey {
   TUNE_MOE_UNFUSED,      // 1: one-token MoE down + weighted sum as two kernels
   TUNE_MOE_MIN_WG,       // routed-expert kernels: widen lane groups below this many workgroups
   TUNE_MOE_ONE,          // 0: one-token gate|up through the general routed-expert kernel
+  TUNE_MFMA_SPLIT,       // K splits of the teams kernel when a workspace is given (1: none)
   TUNE_LOG,              // 1: one line per kernel launch on stderr (the dispatch log)
   TUNE_COUNT
 };
@@ -64,7 +65,12 @@ struct GemvArgs {
   int64_t K;
   int M;
   hipStream_t stream;
+  void* ws = nullptr;        // caller's workspace for K-split partial sums (kq_gemv_ws), or none
+  int64_t ws_bytes = 0;
 };
+// Workspace bytes the matrix-core path would use for a K split of this call
+// (0: no split).
+int64_t gemv_split_bytes(const GemvArgs& a);
 int launch_gemv(const GemvArgs& a);
 int launch_gemv_invariant(const GemvArgs& a);
 // GEMV then the argmax of every column (out: device int32 [M]); ws holds the

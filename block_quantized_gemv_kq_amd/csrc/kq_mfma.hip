@@ -386,12 +386,12 @@ __global__ __launch_bounds__(1024) void k_gemv_mfma_lds(const uint8_t* __restric
 // index 4 gi + g) against the staged x: the group's offset term as one fp32
 // MFMA, then per block D = x . (offset + q) and acc += scale * D.
 template <int FMT, bool SX = true>
-__device__ __forceinline__ void mfma_group(const GroupRaw<FMT>& cur, uint32_t roff, int gi, int g, int ncol,
+__device__ __forceinline__ void mfma_group(const GroupRaw<FMT>& cur, uint32_t roff, int gi, int gl, int g, int ncol,
                                            const u32x4* xa, const float* sxa, int Mp, float4_t& acc) {
   const OwnBlock own = own_block<FMT>(cur, roff, 4 * gi + g);
   if constexpr (SX) {
     const float so = h2f(own.hdr);
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sxa[4 * gi * Mp], fix_const<FMT>(own.hdr, so), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sxa[4 * gl * Mp], fix_const<FMT>(own.hdr, so), acc, 0, 0, 0);
   }
   GroupOps o;
   exchange<FMT>(own, o);
@@ -399,7 +399,7 @@ __device__ __forceinline__ void mfma_group(const GroupRaw<FMT>& cur, uint32_t ro
   float4_t D[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const half8_t A = __builtin_bit_cast(half8_t, xa[(4 * gi + j) * bstride + (ncol ^ xsw(j, g, Mp))]);
+    const half8_t A = __builtin_bit_cast(half8_t, xa[(4 * gl + j) * bstride + (ncol ^ xsw(j, g, Mp))]);
     D[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, b_operand<FMT>(o, j, g), float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
   }
 #pragma unroll
@@ -413,7 +413,7 @@ __device__ __forceinline__ void mfma_group(const GroupRaw<FMT>& cur, uint32_t ro
     const half8_t ones = as_half8(ONES, ONES, ONES, ONES);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const half8_t A = __builtin_bit_cast(half8_t, xa[(4 * gi + j) * bstride + (ncol ^ xsw(j, g, Mp))]);
+      const half8_t A = __builtin_bit_cast(half8_t, xa[(4 * gl + j) * bstride + (ncol ^ xsw(j, g, Mp))]);
       const float4_t Dx = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, ones, float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
       const float sc = h2f(o.hs[j]);
       const float c = fix_const<FMT>(o.hs[j], sc);
@@ -427,11 +427,14 @@ __device__ __forceinline__ void mfma_group(const GroupRaw<FMT>& cur, uint32_t ro
 // the block sums. Called by every thread of the workgroup; `issue_more` runs
 // between issuing the x loads and writing them (the caller's weight loads),
 // after a barrier that puts every wave's x loads ahead of them in the queue.
+// With a K split, the staged range starts at piece k8_0 of every column
+// (column stride stays K) and covers ngroups groups.
 template <bool SX, typename F, bool XF = false>
 __device__ __forceinline__ void stage_x_mfma(const uint16_t* __restrict__ x, int M, int K, int ngroups,
-                                             int log2mp, uint8_t* xlb, F issue_more) {
+                                             int log2mp, uint8_t* xlb, F issue_more, int k8_0 = 0) {
   const int Mp = 1 << log2mp;
   const int kq8 = K / 8, kq8p = 16 * ngroups;
+  const int k8_lim = kq8 - k8_0;   // pieces of the column from the range start on
   const uint32_t sx_base = (uint32_t)kq8p * (uint32_t)Mp * 16u;
   const int nthreads = (int)blockDim.x;
   const int nwaves = nthreads >> 6;
@@ -450,8 +453,8 @@ __device__ __forceinline__ void stage_x_mfma(const uint16_t* __restrict__ x, int
   for (int c = 0; c < XST_MAX; ++c) {
     const int q = wv + nwaves * c;
     const int col = q & (Mp - 1), k8 = 64 * (q >> log2mp) + lane;
-    const bool ok = col < M && k8 < kq8;
-    xr[c] = q < nq ? ld128(xs, ok ? ((uint32_t)col * (uint32_t)kq8 + (uint32_t)k8) * 16u : OOB)
+    const bool ok = col < M && k8 < k8_lim;
+    xr[c] = q < nq ? ld128(xs, ok ? ((uint32_t)col * (uint32_t)kq8 + (uint32_t)(k8_0 + k8)) * 16u : OOB)
                    : u32x4{0u, 0u, 0u, 0u};
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -527,9 +530,16 @@ __global__ __launch_bounds__(1024) void k_gemv_mfma_lds(const uint8_t* __restric
   const int n = lane & 15, g = lane >> 4;
   const int64_t row0 = ((int64_t)blockIdx.x * R + r) * 16;
   const int nblk = K / 32;
-  const int ngroups = (nblk + 3) / 4;
+  // K split (grid y): this workgroup's groups [gs0, gs1) of the row, its
+  // output the partial sums y[blockIdx.y][M][N] (one split: y itself)
+  const int ngroups_all = (nblk + 3) / 4;
+  const int nsplit = (int)gridDim.y;
+  const int gs0 = (int)((int64_t)blockIdx.y * ngroups_all / nsplit);
+  const int gs1 = (int)((int64_t)(blockIdx.y + 1) * ngroups_all / nsplit);
+  const int ngroups = gs1 - gs0;
+  y += (int64_t)blockIdx.y * M * N;
   const int Mp = 1 << log2mp;
-  const int gb = s * P;
+  const int gb = gs0 + s * P;
   const uint32_t row_bytes = (uint32_t)nblk * Fmt<FMT>::BB;
   const int valid_rows = row0 < N ? (int)min<int64_t>(16, N - row0) : 0;
   const rsrc_t rs = make_rsrc(W + (valid_rows ? row0 * row_bytes : 0), ((uint32_t)valid_rows * row_bytes + 3u) & ~3u);
@@ -541,10 +551,10 @@ __global__ __launch_bounds__(1024) void k_gemv_mfma_lds(const uint8_t* __restric
 #pragma unroll
     for (int p = 0; p < P; ++p) {
       const int gi = gb + p;
-      load_group<FMT>(rs, roff, 4 * gi + g, gi < ngroups && row_ok && 4 * gi + g < nblk, wr[p]);
+      load_group<FMT>(rs, roff, 4 * gi + g, gi < gs1 && row_ok && 4 * gi + g < nblk, wr[p]);
     }
   };
-  stage_x_mfma<SX, decltype(issue), XF>(x, M, K, ngroups, log2mp, xlb, issue);
+  stage_x_mfma<SX, decltype(issue), XF>(x, M, K, ngroups, log2mp, xlb, issue, 16 * gs0);
   const int ncol = n < M ? n : M - 1;
   const u32x4* xa = xl4 + g * Mp;
   const float* sxa = reinterpret_cast<const float*>(xlb + (uint32_t)(16 * ngroups) * (uint32_t)Mp * 16u) + g * Mp + ncol;
@@ -552,8 +562,8 @@ __global__ __launch_bounds__(1024) void k_gemv_mfma_lds(const uint8_t* __restric
 #pragma unroll
   for (int p = 0; p < P; ++p) {
     const int gi = gb + p;
-    if (gi >= ngroups) break;   // uniform
-    mfma_group<FMT, SX>(wr[p], roff, gi, g, ncol, xa, sxa, Mp, acc);
+    if (gi >= gs1) break;   // uniform
+    mfma_group<FMT, SX>(wr[p], roff, gi, gi - gs0, g, ncol, xa, sxa, Mp, acc);
   }
   // fixed-order sum over the S waves of each tile (the x area is reused)
   __syncthreads();
@@ -802,7 +812,7 @@ __global__ __launch_bounds__(512) void k_gemv_mfma_pers(const uint8_t* __restric
     for (int p = 0; p < P; ++p) {
       const int q = base + p;
       if (q < Q) {   // uniform
-        mfma_group<FMT, SX>(wr[p], roff, cg, g, ncol, xa, sxa, Mp, acc);
+        mfma_group<FMT, SX>(wr[p], roff, cg, cg, g, ncol, xa, sxa, Mp, acc);
         if (++cg == ngroups) {   // tile complete: lane holds D[col 4g+v][row n]
 #pragma unroll
           for (int k = MFMA_PERS_TPW - 1; k > 0; --k) done[k] = done[k - 1];
@@ -829,6 +839,17 @@ __global__ __launch_bounds__(512) void k_gemv_mfma_pers(const uint8_t* __restric
       }
     }
   }
+}
+
+// Sum of the K-split partial results in split order (fixed, so the result is
+// deterministic): y[i] = part[0][i] + part[1][i] + ... for i < mn.
+__global__ __launch_bounds__(256) void k_split_sum(const float* __restrict__ part, float* __restrict__ y, int64_t mn,
+                                                   int nsplit) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= mn) return;
+  float t = part[i];
+  for (int s = 1; s < nsplit; ++s) t += part[(int64_t)s * mn + i];
+  y[i] = t;
 }
 
 }  // namespace kqd
@@ -1012,6 +1033,90 @@ int launch_mfma_lds(const GemvArgs& a, int m0, int mt, const MfmaLdsCfg& c) {
   return c.sx ? launch_mfma_lds_sx<FMT, true>(a, m0, mt, c) : launch_mfma_lds_sx<FMT, false>(a, m0, mt, c);
 }
 
+// K split of the teams kernel (only with a caller's workspace, kq_gemv_ws):
+// outputs with few row tiles and long rows run as tiles x splits workgroups,
+// each staging x for its part of K only; a second kernel adds the partial
+// results in split order. Measured on MI355X (2560 x 9728 affine4, the same
+// bytes as 4 splits timed as a 10240 x 2432 matrix): 12.3 -> 8.2 us at 8
+// columns before the sum, 15.8 -> 9.9 at 16; 2560 x 4096 gains nothing
+// (6.1 against 5.7 us before the sum), so rows of fewer than 48 groups
+// (6144 elements) are not split.
+constexpr int SPLIT_MAX_TILES = 256;
+constexpr int SPLIT_MIN_GROUPS = 48;
+constexpr int SPLIT_GROUPS_EACH = 16;   // groups per split at least
+constexpr int SPLIT_MAX = 8;
+
+int split_count(const GemvArgs& a) {
+  const int64_t tiles = (a.N + 15) / 16;
+  const int ngroups = (int)((a.K / 32 + 3) / 4);
+  if (a.M > 16 || a.M < 4) return 1;
+  int ns = 1;
+  if (tiles < SPLIT_MAX_TILES && ngroups >= SPLIT_MIN_GROUPS) {
+    ns = ngroups / SPLIT_GROUPS_EACH;
+    while (ns > 1 && tiles * ns > 4 * SPLIT_MAX_TILES) --ns;
+    if (ns > 4) ns = 4;
+  }
+  const int v = tune(TUNE_MFMA_SPLIT);
+  if (v >= 1 && v <= SPLIT_MAX && v <= ngroups) ns = v;
+  return ns;
+}
+
+// teams configuration of one split (its groups as the row, the grid's tiles
+// times the splits as the tile count)
+MfmaLdsCfg split_cfg(const GemvArgs& a, int ns, int maxp, bool no_sums) {
+  const int ngroups = (int)((a.K / 32 + 3) / 4);
+  const int64_t kpart = (int64_t)((ngroups + ns - 1) / ns) * 128;
+  return mfma_lds_cfg(a.N * ns, kpart, (int)a.M, maxp, no_sums);
+}
+
+template <int FMT>
+int launch_mfma_split(const GemvArgs& a, int ns, const MfmaLdsCfg& c) {
+  // the teams kernel with grid y = ns and its output in the workspace
+  GemvArgs b = a;
+  b.y = static_cast<float*>(a.ws);
+  MfmaLdsCfg cc = c;
+  const int64_t tiles = (a.N + 15) / 16;
+  int err;
+  {
+    const int exf = tune(TUNE_MFMA_XF);
+    const bool xf = exf != TUNE_UNSET ? exf != 0 : true;
+    const dim3 grid((unsigned)((tiles + cc.R - 1) / cc.R), (unsigned)ns), block((unsigned)(64 * cc.R * cc.S));
+    dispatch_log("k_gemv_mfma_lds", a.fmt, a.N, a.K, (int)a.M, grid.x, grid.y, block.x, cc.lds,
+                 "teams K-split=%d R=%d S=%d P=%d Mp=%d sums=%d x_first=%d", ns, cc.R, cc.S, cc.P, 1 << cc.log2mp,
+                 cc.sx ? 1 : 0, xf ? 1 : 0);
+#define KQ_SPLIT_LAUNCH(PP, SXX)                                                                                  \
+  do {                                                                                                           \
+    if (xf)                                                                                                      \
+      hipLaunchKernelGGL((k_gemv_mfma_lds<FMT, PP, SXX, true>), grid, block, cc.lds, a.stream, a.W, a.x, b.y,   \
+                         (int)a.N, (int)a.K, (int)a.M, cc.R, cc.S, cc.log2mp);                                   \
+    else                                                                                                         \
+      hipLaunchKernelGGL((k_gemv_mfma_lds<FMT, PP, SXX, false>), grid, block, cc.lds, a.stream, a.W, a.x, b.y,  \
+                         (int)a.N, (int)a.K, (int)a.M, cc.R, cc.S, cc.log2mp);                                   \
+  } while (0)
+    switch (cc.P) {
+      case 1: if (cc.sx) KQ_SPLIT_LAUNCH(1, true); else KQ_SPLIT_LAUNCH(1, false); break;
+      case 2: if (cc.sx) KQ_SPLIT_LAUNCH(2, true); else KQ_SPLIT_LAUNCH(2, false); break;
+      case 3: if (cc.sx) KQ_SPLIT_LAUNCH(3, true); else KQ_SPLIT_LAUNCH(3, false); break;
+      case 4: if (cc.sx) KQ_SPLIT_LAUNCH(4, true); else KQ_SPLIT_LAUNCH(4, false); break;
+      default:
+        if constexpr (MfmaLdsMaxP<FMT>::v >= 6) {
+          if (cc.P == 5) { if (cc.sx) KQ_SPLIT_LAUNCH(5, true); else KQ_SPLIT_LAUNCH(5, false); }
+          else { if (cc.sx) KQ_SPLIT_LAUNCH(6, true); else KQ_SPLIT_LAUNCH(6, false); }
+        } else {
+          return (int)hipErrorInvalidValue;
+        }
+    }
+#undef KQ_SPLIT_LAUNCH
+    err = (int)hipGetLastError();
+  }
+  if (err) return err;
+  const int64_t mn = (int64_t)a.M * a.N;
+  dispatch_log("k_split_sum", a.fmt, a.N, a.K, (int)a.M, (unsigned)((mn + 255) / 256), 1, 256, 0, "splits=%d", ns);
+  hipLaunchKernelGGL(k_split_sum, dim3((unsigned)((mn + 255) / 256)), dim3(256), 0, a.stream,
+                     static_cast<const float*>(a.ws), a.y, mn, ns);
+  return (int)hipGetLastError();
+}
+
 struct MfmaChunkCfg {
   int R, S, P, log2cg;
   size_t lds;
@@ -1177,8 +1282,17 @@ int launch_mfma_fmt(const GemvArgs& a) {
     if ((tiles >= MFMA_PERS_MIN_TILES || want_pers) && !want_teams && !want_chunk && lds <= MFMA_LDS_MAX_BYTES &&
         pieces <= (int64_t)XST_MAX * 512)
       return launch_mfma_pers_p<FMT, MfmaPersP<FMT>::v, true>(a, log2mp, (size_t)lds);
-    const MfmaLdsCfg c = mfma_lds_cfg(a.N, a.K, (int)a.M, MfmaLdsMaxP<FMT>::v, var != MV_TEAMS_SX);
-    if (c.ok && !want_chunk) return launch_mfma_lds<FMT>(a, 0, (int)a.M, c);
+    if (!want_chunk) {
+      // with a workspace, a K split where it pays (also where all of x would
+      // not fit one workgroup's LDS)
+      const int ns = a.ws ? split_count(a) : 1;
+      if (ns > 1) {
+        const MfmaLdsCfg cs = split_cfg(a, ns, MfmaLdsMaxP<FMT>::v, var != MV_TEAMS_SX);
+        if (cs.ok && a.ws_bytes >= (int64_t)ns * a.M * a.N * 4) return launch_mfma_split<FMT>(a, ns, cs);
+      }
+      const MfmaLdsCfg c = mfma_lds_cfg(a.N, a.K, (int)a.M, MfmaLdsMaxP<FMT>::v, var != MV_TEAMS_SX);
+      if (c.ok) return launch_mfma_lds<FMT>(a, 0, (int)a.M, c);
+    }
   }
   for (int m0 = 0; m0 < a.M; m0 += 64) {
     const int mt = a.M - m0 < 64 ? a.M - m0 : 64;
@@ -1265,6 +1379,21 @@ int launch_gemv_mfma_invariant(const GemvArgs& a) {
     case KQ_Q5_1: return launch_mfma_invariant_fmt<F_Q5_1>(a);
     default: return launch_mfma_invariant_fmt<F_AFFINE4>(a);
   }
+}
+
+int64_t gemv_split_bytes(const GemvArgs& a) {
+  // the splits the matrix-core path would take with a workspace (the teams
+  // kernel applies, its split configuration fits)
+  if (a.M < 4 || a.M > 16 || a.N < 1) return 0;
+  const int64_t tiles = (a.N + 15) / 16;
+  if (tiles >= MFMA_PERS_MIN_TILES) return 0;
+  GemvArgs b = a;
+  b.ws = reinterpret_cast<void*>(1);
+  const int ns = split_count(b);
+  if (ns <= 1) return 0;
+  const int maxp = a.fmt == KQ_Q8_0 ? MfmaLdsMaxP<F_Q8_0>::v : MfmaLdsMaxP<F_AFFINE4>::v;
+  if (!split_cfg(a, ns, maxp, true).ok) return 0;
+  return (int64_t)ns * a.M * a.N * 4;
 }
 
 int launch_gemv_mfma(const GemvArgs& a) {

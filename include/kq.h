@@ -144,6 +144,28 @@ int kq_unpack(int fmt, const void* packed, int64_t N, int64_t K, float* W_out);
 int kq_gemv(int fmt, const void* W, const uint16_t* x, float* y,
             int64_t N, int64_t K, int M, void* stream);
 
+/* kq_gemv_ws — kq_gemv with a caller-owned workspace, so that outputs with
+ * few rows and long rows at verify widths (Kinetic docs, "What makes it
+ * fast": several guessed tokens checked in one pass over the weights) can
+ * split K across workgroups: each stages the activations of its part of K
+ * only, and a second kernel adds the partial results in split order (the
+ * result is deterministic; its bits may differ from kq_gemv's by the
+ * summation order, within the same tolerance).
+ *   workspace: device, 16-byte aligned, at least kq_gemv_workspace_bytes(fmt,
+ *     N, K, M) bytes; may be NULL when that is 0 (then the call is kq_gemv).
+ *     Its contents are scratch: nothing is kept between calls, and calls that
+ *     share one workspace must not overlap.
+ * Other arguments as kq_gemv.
+ * Errors: as kq_gemv, and KQ_ERR_ARG (workspace missing or too small),
+ * KQ_ERR_ALIGN (workspace not 16-byte aligned). */
+int kq_gemv_ws(int fmt, const void* W, const uint16_t* x, float* y, int64_t N, int64_t K, int M,
+               void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes kq_gemv_ws needs for this call shape (M * N * 4 per K
+ * split), 0 when it does not split; or a negative error code (KQ_ERR_FORMAT,
+ * KQ_ERR_SHAPE, KQ_ERR_ARG). */
+int64_t kq_gemv_workspace_bytes(int fmt, int64_t N, int64_t K, int M);
+
 /* kq_gemv_invariant — the product of kq_gemv, batch-invariant: column m of y
  * has the same bits as kq_gemv_invariant returns for column m alone (M = 1),
  * whatever M is (Kinetic docs, "What makes it fast": every row of a batch is
@@ -344,7 +366,7 @@ int kq_stack_status(const void* plan, const kq_stack_info* info, int* error, voi
  *                    "chunk_split", "direct"
  *   valu_g, valu_r, lds_wpg, mfma_s, mfma_r, mfma_waves, mfma_xf,
  *   mfma_pers_tpw, mfma_pers_waves, mfma_chunk_l2cg, moe_unfused,
- *   moe_min_wg, moe_one                                       (decimal integers)
+ *   moe_min_wg, moe_one, mfma_split                           (decimal integers)
  *   log              "1": one line per kernel launch on stderr (kernel, format,
  *                    shape, grid, workgroup, LDS bytes, chosen configuration)
  * Errors: KQ_ERR_ARG (unknown name or malformed value). Not synchronised

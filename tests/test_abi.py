@@ -129,6 +129,35 @@ def test_moe_ffn_validation():
     assert call(top_k=129) == kq.KQ_ERR_ARG
 
 
+def test_gemv_ws_sizes_and_validation():
+    """kq_gemv_ws: the workspace it asks for (M * N * 4 bytes per K split:
+    4 splits for the 2560 x 9728 down projection at 4..16 columns, none for
+    2560 x 4096, for one column, past 16 columns or for many row tiles), and
+    the host checks before any device call."""
+    L = kq.lib()
+    for fmt in (0, 1, 2, 3, 4):
+        assert kq.kq_gemv_workspace_bytes(fmt, 2560, 9728, 8) == 4 * 8 * 2560 * 4
+        assert kq.kq_gemv_workspace_bytes(fmt, 2560, 9728, 16) == 4 * 16 * 2560 * 4
+        assert kq.kq_gemv_workspace_bytes(fmt, 2560, 4096, 8) == 0
+        assert kq.kq_gemv_workspace_bytes(fmt, 2560, 9728, 1) == 0
+        assert kq.kq_gemv_workspace_bytes(fmt, 2560, 9728, 32) == 0
+        assert kq.kq_gemv_workspace_bytes(fmt, 19456, 9728, 8) == 0
+    assert L.kq_gemv_workspace_bytes(7, 2560, 9728, 8) == kq.KQ_ERR_FORMAT
+    assert L.kq_gemv_workspace_bytes(0, 2560, 100, 8) == kq.KQ_ERR_SHAPE
+    assert L.kq_gemv_workspace_bytes(0, 2560, 9728, 65) == kq.KQ_ERR_ARG
+    need = kq.kq_gemv_workspace_bytes(2, 2560, 9728, 8)
+
+    def call(fmt=2, W=A16, x=A16, y=A16, N=2560, K=9728, M=8, ws=A16, wsb=need):
+        return L.kq_gemv_ws(fmt, W, x, y, N, K, M, ws, wsb, 0)
+    assert call(ws=None) == kq.KQ_ERR_ARG
+    assert call(wsb=need - 4) == kq.KQ_ERR_ARG
+    assert call(ws=A16 + 8) == kq.KQ_ERR_ALIGN
+    assert call(wsb=-1) == kq.KQ_ERR_ARG
+    assert call(fmt=9) == kq.KQ_ERR_FORMAT
+    assert call(x=A4) == kq.KQ_ERR_ALIGN
+    assert call(M=0, W=None, x=None, y=None, ws=None, wsb=0) == kq.KQ_OK
+
+
 def test_gemv_argmax_validation():
     L = kq.lib()
     need = kq.kq_gemv_argmax_workspace_bytes(0, 151936, 2560, 1)
