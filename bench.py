@@ -144,6 +144,15 @@ class DeviceStack:
             digests[(self.layers, 0)] = hashlib.sha256(packed).digest() + hashlib.sha256(x).digest()
         # SHA-256 over every launch's packed weights and activations, in step order
         self.input_sha256 = hashlib.sha256(b"".join(digests[k] for k in sorted(digests))).hexdigest()
+        self._split_workspace()
+
+    def _split_workspace(self):
+        """One workspace for the launch groups that kq_gemv_ws splits along K
+        (their launches run one after another on one stream, so they share it)."""
+        self.split_bytes = {gi: self.kq.kq_gemv_workspace_bytes(fmt, N, K, self.M)
+                            for gi, (fmt, _, _, _, N, K, _) in enumerate(self.groups[0])} if self.groups else {}
+        need = max(self.split_bytes.values(), default=0)
+        self.split_ws = self.torch.empty(need, dtype=self.torch.uint8, device="cuda") if need else None
 
     def with_columns(self, S, M, act_workload_id):
         """A view with the same resident weights and M fresh activation columns."""
@@ -172,6 +181,7 @@ class DeviceStack:
             am = torch.empty(M, dtype=torch.int32, device="cuda")
             v.head = (fmt, Wd, torch.from_numpy(x).to("cuda"), yd, N, K, ws, wsb, am)
             v.alg_bytes += Wd.numel() + x.nbytes + 2 * M * N * 4 + M * 4
+        v._split_workspace()
         return v
 
     invariant = False   # kq_gemv_invariant (per-column bits of one-column calls) instead of kq_gemv
@@ -181,7 +191,10 @@ class DeviceStack:
 
     def launch_group(self, layer, gi):
         fmt, Wd, xd, yd, N, K, _ = self.groups[layer][gi]
-        self._gemv()(fmt, Wd, xd, yd, N, K, self.M)
+        if not self.invariant and self.split_bytes.get(gi):
+            self.kq.kq_gemv_ws(fmt, Wd, xd, yd, N, K, self.M, self.split_ws, self.split_bytes[gi])
+        else:
+            self._gemv()(fmt, Wd, xd, yd, N, K, self.M)
 
     def launch_head(self):
         fmt, Wd, xd, yd, N, K, ws, wsb, am = self.head
@@ -295,6 +308,9 @@ def kernel_table(torch, ds, reps=10):
         out[name] = {"N": N, "K": K, "fmt": fmt, "M": ds.M, "launches_per_step": ds.layers,
                      "us_per_launch": us, "bytes_per_launch": int(nbytes),
                      "gbps": nbytes / (us * 1e-6) / 1e9}
+        if not ds.invariant and ds.split_bytes.get(gi):
+            out[name]["entry"] = "kq_gemv_ws"
+            out[name]["k_splits"] = ds.split_bytes[gi] // (4 * ds.M * N)
     if ds.head is not None:
         fmt, Wd, xd, yd, N, K, ws, wsb, am = ds.head
         head = lambda: ds.kq.kq_gemv(fmt, Wd, xd, yd, N, K, ds.M)
@@ -389,7 +405,9 @@ def bench_verify_all(torch, kq, S, ds, t1_ms, steps):
         ms = float(np.median(per))
         out[str(M)] = {"ms_per_pass": ms, "ms_p10_p90": [float(np.percentile(per, 10)), float(np.percentile(per, 90))],
                        "alg_bytes": int(dv.alg_bytes), "gbps": dv.alg_bytes / (ms * 1e-3) / 1e9,
-                       "t_ratio_vs_m1": ms / t1_ms, "tokens_per_s_upper_bound": M / (ms * 1e-3)}
+                       "t_ratio_vs_m1": ms / t1_ms, "tokens_per_s_upper_bound": M / (ms * 1e-3),
+                       "k_split_groups": {GROUP_NAMES[gi]: b // (4 * M * dv.groups[0][gi][4])
+                                          for gi, b in dv.split_bytes.items() if b}}
         log(f"verify M={M}: {ms * 1000:.1f} us per pass, t(M)/t(1) = {ms / t1_ms:.2f}")
         if M in VERIFY_INVARIANT_M:
             dv.invariant = True
