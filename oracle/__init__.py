@@ -18,5 +18,8 @@ Sources (page titles and sections):
   kernel is gated against a scalar CPU oracle.
 * The per-format byte definitions (Q8_0, Q4_0, affine4 gs32) stated with the
   workloads; each function below restates the one it follows.
+* Kinetic docs, "What makes it fast" (the Shortlist paragraph): an exact
+  argmax over an output layer that computes exact scores only for the rows
+  a bound from a small copy cannot rule out (shortlist.py).
 """
-from . import formats, ref  # noqa: F401
+from . import formats, ref, shortlist  # noqa: F401

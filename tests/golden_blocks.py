@@ -41,3 +41,41 @@ def load(path: str) -> dict:
 
 def all_blocks():
     return [load(p) for p in sorted(glob.glob(os.path.join(GOLDEN, "*.txt"))) if not p.endswith("README.txt")]
+
+
+def load_shortlist(path: str) -> dict:
+    """A hand-worked bound-copy row (tests/golden/shortlist/): K, the Q8_0
+    block scales and quants of one row (blocks not listed are all zero), the
+    residual norm E and the expected bytes."""
+    out = {"name": os.path.basename(path), "q": {}}
+    raw = []
+    with open(path) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, _, rest = line.partition(":")
+            toks = rest.split()
+            if key == "k":
+                out["k"] = int(toks[0])
+            elif key == "d":
+                out["d"] = np.array([_value(t) for t in toks], dtype=np.float64)
+            elif key == "E":
+                out["E"] = _value(toks[0])
+            elif key == "bytes":
+                raw += [int(t, 16) for t in toks]
+            elif re.fullmatch(r"q[0-9]+", key):
+                out["q"][int(key[1:])] = [int(t) for t in toks]
+    nb = out["k"] // 32
+    d = out["d"].astype(np.float16)
+    assert np.array_equal(d.astype(np.float64), out["d"]), f"{path}: scale not exact in fp16"
+    q = np.zeros((1, nb, 32), np.int8)
+    for b, vals in out["q"].items():
+        q[0, b] = vals
+    out["fields"] = {"d": d[None, :], "q": q}
+    out["bytes"] = np.array(raw, dtype=np.uint8)
+    return out
+
+
+def all_shortlist_rows():
+    return [load_shortlist(p) for p in sorted(glob.glob(os.path.join(GOLDEN, "shortlist", "*.txt")))]

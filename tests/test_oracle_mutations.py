@@ -223,3 +223,57 @@ def test_q5_1_fifteen_steps_is_caught(monkeypatch):
         return {"d": f["s"], "m": f["b"], "q": f["q"]}
     monkeypatch.setattr(F, "quantize", bad)
     assert _any_golden_fails("q5_1")
+
+
+# ------------------------------------------------------------- Shortlist
+from oracle import shortlist as SL  # noqa: E402
+from tests import test_oracle_shortlist as TS  # noqa: E402
+
+
+def test_shortlist_centre_4_is_caught(monkeypatch):
+    monkeypatch.setattr(SL, "SPLIT_CENTRE", 4.0)
+    assert _fails(TS.check_bound_exact, TS._q8(4, 256, seed=200), TS._x(256, 300))
+
+
+def test_shortlist_norm_rounded_to_nearest_is_caught(monkeypatch):
+    import math
+
+    def nearest(d_row, ql_row):
+        d = np.asarray(d_row, np.float16).astype(np.float64)
+        Q = ((2 * np.asarray(ql_row, np.int64) - 7) ** 2).sum(axis=-1)
+        return np.float32(math.sqrt(math.fsum((d * d) * (Q / 4.0))))
+    monkeypatch.setattr(SL, "residual_norm_up", nearest)
+    assert any(_fails(TS.check_golden_row, r) for r in TS.ROWS)
+
+
+def test_shortlist_split_toward_zero_is_caught(monkeypatch):
+    def trunc_split(q):
+        qi = np.asarray(q).astype(np.int64)
+        v = np.trunc(qi / 8).astype(np.int64) + 16
+        return v.astype(np.uint8), (qi - 8 * (v - 16)).astype(np.uint8)
+    monkeypatch.setattr(SL, "split_quants", trunc_split)
+    assert _fails(TS.check_split_every_int8)
+
+
+def test_shortlist_dropped_fifth_bit_is_caught(monkeypatch):
+    monkeypatch.setattr(F, "_high_bits", lambda q: np.zeros(q.shape[:-1] + (4,), np.uint8))
+    assert any(_fails(TS.check_golden_row, r) for r in TS.ROWS)
+
+
+def test_shortlist_l1_radius_is_caught(monkeypatch):
+    orig = SL.bound_terms
+
+    def l1(bound, x16):
+        t = orig(bound, x16)
+        x = np.asarray(x16, np.float16).astype(np.float64)
+        l2 = np.sqrt((x * x).sum())
+        scale = np.abs(x).sum() / l2 if l2 else 1.0
+        t["r"] = t["r"] * scale
+        return t
+    monkeypatch.setattr(SL, "bound_terms", l1)
+    assert _fails(TS.check_equality_case)
+
+
+def test_shortlist_dropped_centre_term_is_caught(monkeypatch):
+    monkeypatch.setattr(SL, "SPLIT_CENTRE", 0.0)
+    assert _fails(TS.check_yhat_block_constant)
