@@ -329,6 +329,87 @@ def kernel_table(torch, ds, reps=10):
     return out
 
 
+def shortlist_head(torch, ds, steps, warmup):
+    """The lm_head's argmax through kq_shortlist_argmax (M = 1): the bound copy
+    packed on the host from the head's Q8_0 bytes, the call timed alone (a
+    graph of 8 calls, as the kernel table) and as the step's last call in
+    place of kq_gemv_argmax (the layer launches unchanged, the step captured
+    and replayed like the headline's), the rows it scored exactly, and whether
+    its index is kq_gemv_argmax's. Bytes read per call: the bound copy, the
+    kept rows' Q8_0 bytes, x three times, u written and read."""
+    kq = ds.kq
+    fmt, Wd, xd, yd, N, K, ws, wsb, am = ds.head
+    packed = Wd.cpu().numpy()
+    t0 = time.perf_counter()
+    copy = kq.kq_shortlist_pack(packed, N, K)
+    pack_s = time.perf_counter() - t0
+    del packed
+    Cd = torch.from_numpy(copy).to("cuda")
+    swsb = kq.kq_shortlist_workspace_bytes(N, K)
+    sws = torch.empty(swsb, dtype=torch.uint8, device="cuda")
+    out = torch.empty(1, dtype=torch.int32, device="cuda")
+    kept = torch.empty(1, dtype=torch.int32, device="cuda")
+    call = lambda: kq.kq_shortlist_argmax(Wd, Cd, xd, N, K, sws, swsb, out, kept)
+    us = _graph_us(torch, [call] * 8, 10)
+    call()
+    ds.launch_head()
+    torch.cuda.synchronize()
+    idx, ref, nkept = int(out.cpu()[0]), int(am.cpu()[0]), int(kept.cpu()[0])
+
+    def step():
+        for layer in range(ds.layers):
+            for gi in range(len(ds.groups[layer])):
+                ds.launch_group(layer, gi)
+        call()
+    g = capture(torch, step)
+    per, total, _ = time_graph(torch, g, steps, warmup)
+    del g
+    ms = total / steps
+    nbytes = copy.nbytes + nkept * (K // 32) * 34 + 3 * 2 * K + 2 * 4 * N
+    del Cd, sws
+    return {"entry": "kq_shortlist_argmax", "us_per_call": us, "kernels_per_call": 4,
+            "rows": N, "rows_scored_exactly": nkept, "pct_rows_scored_exactly": 100.0 * nkept / N,
+            "bound_copy_bytes": int(copy.nbytes), "bytes_read_per_call": int(nbytes),
+            "gbps_of_bytes_read": nbytes / (us * 1e-6) / 1e9,
+            "index": idx, "index_equals_kq_gemv_argmax": idx == ref, "host_pack_s": pack_s,
+            "step_ms_with_shortlist": ms, "tokens_per_s_with_shortlist": 1000.0 / ms,
+            "step_us_p10_p50_p90": [float(np.percentile(per, q)) * 1000 for q in (10, 50, 90)]}
+
+
+def bench_shortlist_head(torch, kq, S, copies=3, reps=10):
+    """The 4B-shaped Q8_0 head alone (151936 x 2560, M = 1): kq_shortlist_argmax
+    against kq_gemv_argmax, each as a graph of 9 calls rotating over `copies`
+    copies of the weights (and of the bound copy), so every call reads from
+    HBM; per call: median over `reps` replays / 9. Also the rows kept for the
+    bench's seeded column and the index of both calls."""
+    h = S.QWEN3_4B_AFFINE4.head
+    W = S.weights(S.QWEN3_4B_AFFINE4.weight_seed(S.QWEN3_4B_AFFINE4.layers, 0), h.n, h.k)
+    packed = kq.kq_pack(h.fmt, W)
+    del W
+    copy = kq.kq_shortlist_pack(packed, h.n, h.k)
+    N, K = h.n, h.k
+    Ws = [torch.from_numpy(packed).cuda() for _ in range(copies)]
+    Cs = [torch.from_numpy(copy).cuda() for _ in range(copies)]
+    x = torch.from_numpy(S.activations((S.QWEN3_4B_AFFINE4.workload_id, S.QWEN3_4B_AFFINE4.layers, 0), K, 1)).cuda()
+    swsb = kq.kq_shortlist_workspace_bytes(N, K)
+    sws = torch.empty(swsb, dtype=torch.uint8, device="cuda")
+    awsb = kq.kq_gemv_argmax_workspace_bytes(h.fmt, N, K, 1)
+    aws = torch.empty(awsb, dtype=torch.uint8, device="cuda")
+    y = torch.empty((1, N), dtype=torch.float32, device="cuda")
+    out = torch.zeros(2, dtype=torch.int32, device="cuda")
+    kept = torch.zeros(1, dtype=torch.int32, device="cuda")
+    sl = [lambda i=i: kq.kq_shortlist_argmax(Ws[i % copies], Cs[i % copies], x, N, K, sws, swsb, out[0:1], kept)
+          for i in range(9)]
+    ga = [lambda i=i: kq.kq_gemv_argmax(h.fmt, Ws[i % copies], x, y, N, K, 1, out[1:2], aws, awsb)
+          for i in range(9)]
+    us_sl = _graph_us(torch, sl, reps)
+    us_ga = _graph_us(torch, ga, reps)
+    o = out.cpu().numpy()
+    return {"rows": N, "K": K, "us_per_call_shortlist": us_sl, "us_per_call_gemv_argmax": us_ga,
+            "rows_scored_exactly": int(kept.cpu()[0]), "index_shortlist": int(o[0]), "index_gemv_argmax": int(o[1]),
+            "bound_copy_bytes": int(copy.nbytes), "copies": copies}
+
+
 def _graph_time_us(torch, fns, reps, per):
     """Median over `reps` replays of a graph of `fns`, divided by `per`."""
     g = capture(torch, lambda: [f() for f in fns])
@@ -793,6 +874,8 @@ def main():
     ap.add_argument("--kernels-only", type=int, nargs="?", const=1, default=0, metavar="M",
                     help="short run for counter collection: eager launches of 4 layers and the lm_head at M "
                          "columns (default 1), then a copy of known size")
+    ap.add_argument("--shortlist-only", action="store_true",
+                    help="only the Q8_0 head's argmax: kq_shortlist_argmax against kq_gemv_argmax")
     ap.add_argument("--moe-only", action="store_true",
                     help="short run: only the Q4_0 MoE layer at each token count")
     ap.add_argument("--eager", action="store_true",
@@ -811,6 +894,9 @@ def main():
     kq.lib()
     stack = S.QWEN3_4B_AFFINE4
 
+    if args.shortlist_only:
+        print(json.dumps({"shortlist_only": bench_shortlist_head(torch, kq, S, reps=max(5, args.steps))}))
+        return
     if args.moe_only:
         if args.eager:
             bench_moe_eager(torch, kq, S)
@@ -900,6 +986,14 @@ def main():
                 "us_per_launch": d["us_per_launch"], "bytes_per_launch": d["bytes_per_launch"],
                 "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)"}
 
+    shortlist = shortlist_head(torch, ds, args.steps, args.warmup)
+    log(f"lm_head argmax through Shortlist: {shortlist['us_per_call']:.1f} us per call "
+        f"({shortlist['pct_rows_scored_exactly']:.2f} % of rows scored exactly), step "
+        f"{shortlist['step_ms_with_shortlist'] * 1000:.1f} us")
+    if not shortlist["index_equals_kq_gemv_argmax"]:
+        raise SystemExit("Shortlist argmax differs from kq_gemv_argmax")
+    torch.cuda.empty_cache()
+
     verify = None
     if not args.no_verify:
         dv = ds.with_columns(S, 8, S.VERIFY_WORKLOAD_ID)
@@ -985,6 +1079,7 @@ def main():
         "alg_bytes_per_step": alg_bytes_step,
         "roofline": roofline,
         "kernels": ktab,
+        "lm_head_shortlist": shortlist,
         "verify_m8": verify,
         "verify_all": verify_all,
         "other_configs": configs,

@@ -39,6 +39,10 @@ SIGNATURES = {
     "kq_gemv_argmax_workspace_bytes": (_I64, [_I32, _I64, _I64, _I32]),
     "kq_gemv_argmax": (_I32, [_I32, _P, _P, _P, _I64, _I64, _I32, _P, _P, _I64, _P]),
     "kq_gemv_argmax_noalloc": (_I32, [_I32, _P, _P, _P, _I64, _I64, _I32, _P, _P]),
+    "kq_shortlist_copy_bytes": (_I64, [_I64, _I64]),
+    "kq_shortlist_pack": (_I32, [_P, _I64, _I64, _P, _I32]),
+    "kq_shortlist_workspace_bytes": (_I64, [_I64, _I64]),
+    "kq_shortlist_argmax": (_I32, [_P, _P, _P, _I64, _I64, _P, _I64, _P, _P, _P]),
     "kq_moe_gemv_workspace_bytes": (_I64, [_I64, _I32, _I32, _I32]),
     "kq_moe_gemv": (_I32, [_I32, _P, _P, _P, _P, _P, _I64, _I64, _I32, _I32, _I32, _I32, _P, _I64, _P]),
     "kq_moe_ffn_workspace_bytes": (_I64, [_I64, _I64, _I32, _I32]),
@@ -263,6 +267,36 @@ def kq_argmax_workspace_bytes(N: int, M: int) -> int:
 def kq_argmax(y, N: int, M: int, out, workspace, workspace_bytes: int, stream=None) -> None:
     _check(lib().kq_argmax(_ptr(y), N, M, _ptr(out), _ptr(workspace), workspace_bytes, _stream(stream)),
            "kq_argmax")
+
+
+def kq_shortlist_copy_bytes(N: int, K: int) -> int:
+    return _check(lib().kq_shortlist_copy_bytes(N, K), "kq_shortlist_copy_bytes")
+
+
+def kq_shortlist_pack(q8_packed: np.ndarray, N: int, K: int, out: np.ndarray | None = None,
+                      n_threads: int = 0) -> np.ndarray:
+    """Bound copy (host uint8) of a packed Q8_0 matrix (host uint8)."""
+    q8_packed = np.ascontiguousarray(q8_packed)
+    nbytes = kq_shortlist_copy_bytes(N, K)
+    if q8_packed.dtype != np.uint8 or q8_packed.nbytes < kq_packed_bytes("q8_0", N, K):
+        raise ValueError("q8_packed must hold the packed Q8_0 matrix as uint8")
+    if out is None:
+        out = np.empty(nbytes, np.uint8)
+    if not out.flags.c_contiguous or out.nbytes < nbytes:
+        raise ValueError("out too small or not contiguous")
+    _check(lib().kq_shortlist_pack(q8_packed.ctypes.data, N, K, out.ctypes.data, n_threads), "kq_shortlist_pack")
+    return out
+
+
+def kq_shortlist_workspace_bytes(N: int, K: int) -> int:
+    return _check(lib().kq_shortlist_workspace_bytes(N, K), "kq_shortlist_workspace_bytes")
+
+
+def kq_shortlist_argmax(W, W_copy, x, N: int, K: int, workspace, workspace_bytes: int, out, kept=None,
+                        stream=None) -> None:
+    """out[0] = argmax of the N scores of Q8_0 W against fp16 x, through its bound copy."""
+    _check(lib().kq_shortlist_argmax(_ptr(W), _ptr(W_copy), _ptr(x), N, K, _ptr(workspace), workspace_bytes,
+                                     _ptr(out), _ptr(kept), _stream(stream)), "kq_shortlist_argmax")
 
 
 def _stage_array(stages):

@@ -34,7 +34,7 @@ HIPCC = os.path.join(ROCM, "bin", "hipcc")
 ARCH = "gfx950"
 
 HOST_SOURCES = ["kq_api.cpp", "kq_pack.cpp"]
-HIP_SOURCES = ["kq_gemv.hip", "kq_mfma.hip", "kq_moe.hip", "kq_misc.hip", "kq_stack.hip"]
+HIP_SOURCES = ["kq_gemv.hip", "kq_mfma.hip", "kq_moe.hip", "kq_misc.hip", "kq_stack.hip", "kq_shortlist.hip"]
 # Measurement only: a read-only streaming kernel for the benchmark's ceiling,
 # in a library of its own that the GEMV library never loads.
 PROBE_SOURCES = ["kq_probe.hip"]

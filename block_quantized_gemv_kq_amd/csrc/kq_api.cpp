@@ -61,7 +61,7 @@ const TuneName kTuneNames[] = {
     {"mfma_chunk_l2cg", kq::TUNE_MFMA_CHUNK_L2CG}, {"moe_unfused", kq::TUNE_MOE_UNFUSED},
     {"moe_min_wg", kq::TUNE_MOE_MIN_WG},          {"log", kq::TUNE_LOG},
     {"mfma_pers_waves", kq::TUNE_MFMA_PERS_WAVES}, {"moe_one", kq::TUNE_MOE_ONE},
-    {"mfma_split", kq::TUNE_MFMA_SPLIT},
+    {"mfma_split", kq::TUNE_MFMA_SPLIT},         {"sl_g", kq::TUNE_SL_G},
 };
 
 // Parse a tuning value: force_path and mfma_variant take names, the others integers.
@@ -622,6 +622,63 @@ int kq_argmax(const float* y, int64_t N, int M, int32_t* out, void* workspace,
   if (!aligned(workspace, 8)) return fail(KQ_ERR_ALIGN, "kq_argmax: workspace must be 8-byte aligned");
   return hip_status(kq::launch_argmax(y, N, M, out, workspace, static_cast<hipStream_t>(stream)),
                     "kq_argmax");
+}
+
+// ------------------------------------------------------------- Shortlist
+namespace {
+// Shapes the Shortlist path takes: K a multiple of 256 up to KQ_SHORTLIST_MAX_K
+// (x and its block sums fit one workgroup's LDS), the Q8_0 matrix and its
+// bound copy each below 2 GiB (32-bit buffer offsets with room for the
+// out-of-range marker).
+int check_shortlist_shape(int64_t N, int64_t K, const char* who) {
+  if (N < 1 || N > KQ_MAX_N) return fail(KQ_ERR_ARG, "%s: N=%lld out of range", who, (long long)N);
+  if (K <= 0 || K % 256 != 0 || K > KQ_SHORTLIST_MAX_K)
+    return fail(KQ_ERR_SHAPE, "%s: K=%lld must be a positive multiple of 256 and <= %d", who, (long long)K,
+                KQ_SHORTLIST_MAX_K);
+  const int64_t limit = (int64_t)1 << 31;
+  if (N * (K / 32) * 34 >= limit || kq::shortlist_copy_bytes(N, K) >= limit)
+    return fail(KQ_ERR_SHAPE, "%s: the matrix or its bound copy reaches 2 GiB", who);
+  return KQ_OK;
+}
+}  // namespace
+
+int64_t kq_shortlist_copy_bytes(int64_t N, int64_t K) {
+  const int st = check_shortlist_shape(N, K, "kq_shortlist_copy_bytes");
+  if (st) return st;
+  return kq::shortlist_copy_bytes(N, K);
+}
+
+int kq_shortlist_pack(const void* q8_packed, int64_t N, int64_t K, void* out, int n_threads) {
+  int st = check_shortlist_shape(N, K, "kq_shortlist_pack");
+  if (st) return st;
+  if (!q8_packed || !out) return fail(KQ_ERR_ARG, "kq_shortlist_pack: null pointer");
+  st = kq::shortlist_pack(q8_packed, N, K, out, n_threads);
+  if (st) return fail(st, "kq_shortlist_pack: a block scale is infinite or NaN");
+  return ok();
+}
+
+int64_t kq_shortlist_workspace_bytes(int64_t N, int64_t K) {
+  const int st = check_shortlist_shape(N, K, "kq_shortlist_workspace_bytes");
+  if (st) return st;
+  return kq::shortlist_workspace_bytes(N, K);
+}
+
+int kq_shortlist_argmax(const void* W, const void* W_copy, const uint16_t* x, int64_t N, int64_t K,
+                        void* workspace, int64_t workspace_bytes, int32_t* out, int32_t* kept, void* stream) {
+  int st = check_shortlist_shape(N, K, "kq_shortlist_argmax");
+  if (st) return st;
+  if (!W || !W_copy || !x || !out) return fail(KQ_ERR_ARG, "kq_shortlist_argmax: null pointer");
+  if (!aligned(W, 16) || !aligned(W_copy, 16) || !aligned(x, 16))
+    return fail(KQ_ERR_ALIGN, "kq_shortlist_argmax: W, W_copy and x must be 16-byte aligned");
+  if (!aligned(out, 4) || (kept && !aligned(kept, 4)))
+    return fail(KQ_ERR_ALIGN, "kq_shortlist_argmax: out and kept must be 4-byte aligned");
+  const int64_t need = kq::shortlist_workspace_bytes(N, K);
+  if (!workspace || workspace_bytes < need)
+    return fail(KQ_ERR_ARG, "kq_shortlist_argmax: workspace of %lld bytes needed", (long long)need);
+  if (!aligned(workspace, 256)) return fail(KQ_ERR_ALIGN, "kq_shortlist_argmax: workspace must be 256-byte aligned");
+  kq::ShortlistArgs a{static_cast<const uint8_t*>(W), static_cast<const uint8_t*>(W_copy), x, N, K, workspace,
+                      out, kept, static_cast<hipStream_t>(stream)};
+  return hip_status(kq::launch_shortlist_argmax(a), "kq_shortlist_argmax");
 }
 
 }  // extern "C"

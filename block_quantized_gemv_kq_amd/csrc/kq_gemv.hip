@@ -489,6 +489,11 @@ int dispatch(const GemvArgs& a) {
 
 }  // namespace
 
+RowCfg q8_row_cfg(int64_t N, int64_t K) {
+  const LdsCfg c = lds_cfg(N, (int)(K / (32 * Fmt<F_Q8_0>::UB)), Fmt<F_Q8_0>::BB * Fmt<F_Q8_0>::UB);
+  return {c.log2g, c.iters, c.passes};
+}
+
 int launch_gemv(const GemvArgs& a) {
   switch (a.fmt) {
     case KQ_Q8_0: return dispatch<F_Q8_0>(a);

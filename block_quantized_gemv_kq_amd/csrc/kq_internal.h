@@ -31,6 +31,7 @@ enum TuneKey {
   TUNE_MOE_MIN_WG,       // routed-expert kernels: widen lane groups below this many workgroups
   TUNE_MOE_ONE,          // 0: one-token gate|up through the general routed-expert kernel
   TUNE_MFMA_SPLIT,       // K splits of the teams kernel when a workspace is given (1: none)
+  TUNE_SL_G,             // lanes per row of the Shortlist bound kernel
   TUNE_LOG,              // 1: one line per kernel launch on stderr (the dispatch log)
   TUNE_COUNT
 };
@@ -52,6 +53,9 @@ int pack(int fmt, const float* W, int64_t N, int64_t K, void* out, int n_threads
 int unpack(int fmt, const void* packed, int64_t N, int64_t K, float* W);
 uint16_t f32_to_f16_bits(float f);
 float f16_bits_to_f32(uint16_t h);
+// Shortlist bound copy of a Q8_0 matrix (K a multiple of 256).
+int64_t shortlist_copy_bytes(int64_t N, int64_t K);
+int shortlist_pack(const void* q8, int64_t N, int64_t K, void* out, int n_threads);
 
 // ---- launchers (kernels in *.hip). Each returns 0 or a HIP error code.
 // Arguments are validated by the C-ABI layer before these are called.
@@ -81,6 +85,28 @@ int64_t gemv_argmax_fused_parts(const GemvArgs& a);
 // current device (KQ_NOALLOC_SCRATCH_BYTES; the caller checks the size).
 int launch_gemv_argmax_noalloc(const GemvArgs& a, int32_t* out);
 int launch_gemv_mfma(const GemvArgs& a);
+// Per-row configuration of the one-column GEMV kernel for a Q8_0 matrix of
+// this shape: lanes per row (log2), units per lane, passes. A row computed
+// with it has the bits kq_gemv gives that row.
+struct RowCfg {
+  int log2g, iters, passes;
+};
+RowCfg q8_row_cfg(int64_t N, int64_t K);
+
+// Shortlist argmax over a Q8_0 output layer (one column).
+struct ShortlistArgs {
+  const uint8_t* W;     // Q8_0 matrix
+  const uint8_t* Wc;    // its bound copy
+  const uint16_t* x;
+  int64_t N;
+  int64_t K;
+  void* ws;
+  int32_t* out;         // device int32 [1]
+  int32_t* kept;        // device int32 [1] or null: rows scored exactly
+  hipStream_t stream;
+};
+int64_t shortlist_workspace_bytes(int64_t N, int64_t K);
+int launch_shortlist_argmax(const ShortlistArgs& a);
 // The matrix-core GEMV with every configuration chosen from N and K alone
 // (batch-invariant columns).
 int launch_gemv_mfma_invariant(const GemvArgs& a);

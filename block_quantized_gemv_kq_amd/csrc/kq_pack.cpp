@@ -315,4 +315,123 @@ int unpack(int fmt, const void* packed, int64_t N, int64_t K, float* W) {
   return KQ_OK;
 }
 
+// ------------------------------------------------------- Shortlist bound copy
+// From the bytes of a Q8_0 matrix (K a multiple of 256), the bound copy the
+// Shortlist argmax reads instead of the full layer (Kinetic docs, "What makes
+// it fast": a small copy bounds every row's score). Each int8 quant q splits
+// as q = 8 (v - 16) + ql with v = floor(q / 8) + 16 (0..31) and ql = q & 7; per
+// row the copy keeps the block scales, v as Q5_0-style fifth-bit words and
+// nibbles, and E, the least fp32 with E^2 >= S = sum_b d_b^2 sum_j (ql_j - 3.5)^2
+// (the squared 2-norm of the row's error when ql is replaced by 3.5). S is
+// formed exactly in integers: with |d| = M 2^e (M < 2^11, e in -24..5 from
+// the fp16 bits) and Q = sum_j (2 ql_j - 7)^2 (< 2^11), 4 S 2^48 is the sum of
+// M^2 Q 2^(2e + 48), each term below 2^91.
+namespace {
+
+typedef unsigned __int128 u128;
+
+// fp16 magnitude as M * 2^e; false for inf/NaN.
+bool f16_mant_exp(uint16_t h, uint32_t* M, int* e) {
+  const uint32_t ex = (h >> 10) & 0x1fu, m = h & 0x3ffu;
+  if (ex == 0x1f) return false;
+  if (ex == 0) {
+    *M = m;
+    *e = -24;
+  } else {
+    *M = m | 0x400u;
+    *e = (int)ex - 25;
+  }
+  return true;
+}
+
+// Is f^2 >= S, with S = s4 * 2^-50 (s4 as above)? f >= 0 finite fp32.
+bool square_covers(float f, u128 s4) {
+  uint32_t x;
+  memcpy(&x, &f, 4);
+  const uint32_t ex = (x >> 23) & 0xffu;
+  const uint64_t F = ex ? ((x & 0x7fffffu) | 0x800000u) : (x & 0x7fffffu);
+  const int G = ex ? (int)ex - 150 : -149;            // f = F 2^G
+  const u128 F2 = (u128)F * F;                         // < 2^48
+  const int sh = 2 * G + 50;                           // f^2 2^50 = F2 2^sh
+  if (F2 == 0) return s4 == 0;
+  if (sh >= 0) {
+    if (sh > 79) return true;                          // F2 2^sh >= 2^79 > any s4 here
+    return (F2 << sh) >= s4;
+  }
+  const int k = -sh;
+  if (k >= 128) return s4 == 0;
+  if (s4 >> (127 - k)) return false;                   // s4 2^k >= 2^127 > F2
+  return F2 >= (s4 << k);
+}
+
+float norm_up(u128 s4) {
+  if (s4 == 0) return 0.0f;
+  const double S = std::ldexp((double)s4, -50);
+  float f = (float)std::sqrt(S);
+  while (!square_covers(f, s4)) f = std::nextafter(f, INFINITY);
+  while (f > 0.0f && square_covers(std::nextafter(f, 0.0f), s4)) f = std::nextafter(f, 0.0f);
+  return f;
+}
+
+bool shortlist_rows(const uint8_t* q8, int64_t r0, int64_t r1, int64_t K, int64_t N, uint8_t* out) {
+  const int64_t nb = K / 32;
+  const int64_t rb = 22 * nb;
+  float* E = reinterpret_cast<float*>(out + N * rb);
+  for (int64_t r = r0; r < r1; ++r) {
+    uint8_t* dpl = out + r * rb;
+    uint8_t* fpl = dpl + 2 * nb;
+    uint8_t* npl = dpl + 6 * nb;
+    u128 s4 = 0;
+    for (int64_t b = 0; b < nb; ++b) {
+      const uint8_t* blk = q8 + (r * nb + b) * 34;
+      const uint16_t h = (uint16_t)(blk[0] | (blk[1] << 8));
+      uint32_t M;
+      int e;
+      if (!f16_mant_exp(h, &M, &e)) return false;
+      dpl[2 * b] = blk[0];
+      dpl[2 * b + 1] = blk[1];
+      uint32_t word = 0, Q = 0;
+      uint8_t v[32];
+      for (int j = 0; j < 32; ++j) {
+        const int q = (int8_t)blk[2 + j];
+        const int hi = q >> 3;                     // arithmetic shift: floor(q / 8)
+        v[j] = (uint8_t)(hi + 16);
+        const int ql = q - 8 * hi;
+        Q += (uint32_t)((2 * ql - 7) * (2 * ql - 7));
+        word |= (uint32_t)((v[j] >> 4) & 1u) << j;
+      }
+      for (int i = 0; i < 4; ++i) fpl[4 * b + i] = (uint8_t)(word >> (8 * i));
+      for (int j = 0; j < 16; ++j) npl[16 * b + j] = (uint8_t)((v[j] & 15u) | ((v[j + 16] & 15u) << 4));
+      s4 += ((u128)((uint64_t)M * M) * Q) << (2 * e + 48);
+    }
+    const float f = norm_up(s4);
+    memcpy(E + r, &f, 4);
+  }
+  return true;
+}
+
+}  // namespace
+
+int64_t shortlist_copy_bytes(int64_t N, int64_t K) { return N * (22 * (K / 32) + 4); }
+
+int shortlist_pack(const void* q8, int64_t N, int64_t K, void* out, int n_threads) {
+  const uint8_t* p = static_cast<const uint8_t*>(q8);
+  uint8_t* o = static_cast<uint8_t*>(out);
+  int nt = n_threads;
+  if (nt <= 0) nt = (int)std::min<unsigned>(64u, std::max(1u, std::thread::hardware_concurrency()));
+  if (N * K < (1 << 20)) nt = 1;
+  nt = (int)std::min<int64_t>(nt, N);
+  if (nt <= 1) return shortlist_rows(p, 0, N, K, N, o) ? KQ_OK : KQ_ERR_RANGE;
+  std::vector<std::thread> th;
+  std::vector<char> ok(nt, 1);
+  for (int t = 0; t < nt; ++t) {
+    const int64_t r0 = N * t / nt, r1 = N * (t + 1) / nt;
+    th.emplace_back([=, &ok] { ok[t] = shortlist_rows(p, r0, r1, K, N, o) ? 1 : 0; });
+  }
+  for (auto& t : th) t.join();
+  for (char c : ok)
+    if (!c) return KQ_ERR_RANGE;
+  return KQ_OK;
+}
+
 }  // namespace kq

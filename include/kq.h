@@ -281,6 +281,75 @@ int kq_gemv_argmax(int fmt, const void* W, const uint16_t* x, float* y,
 int kq_gemv_argmax_noalloc(int fmt, const void* W, const uint16_t* x, float* y,
                            int64_t N, int64_t K, int M, int32_t* out, void* stream);
 
+/* ---- Shortlist: an exact argmax that scores only the rows that can win ----
+ * Kinetic docs, "What makes it fast" (the Shortlist paragraph): choosing the
+ * next token reads an output layer with up to a quarter of a million rows; a
+ * small copy of the layer bounds every row's score, and exact scores are
+ * computed only for the rows whose bound still lets them win. The pages give
+ * no copy or bound; this library's reading, for a Q8_0 layer (w' = d q):
+ *
+ * Each int8 quant splits as q = 8 (v - 16) + ql, v = floor(q / 8) + 16 (0..31),
+ * ql = q - 8 (v - 16) (0..7). The bound copy of an N x K Q8_0 matrix (K a
+ * multiple of 256, nb = K / 32) holds per row 22 nb bytes in three planes,
+ * rows back to back: the nb fp16 block scales d (bit copies, little-endian);
+ * nb little-endian uint32 words whose bit j is bit 4 of v_j; nb blocks of 16
+ * nibble bytes, byte j = (v_j & 15) | (v_{j+16} & 15) << 4. After the N rows:
+ * N little-endian fp32 E_n, the least fp32 with E_n^2 >= the sum over the
+ * row's blocks of d^2 (ql_j - 3.5)^2 (computed exactly). 65 % of the Q8_0
+ * bytes plus 4 per row.
+ *
+ * For one fp16 column x, per row n (real arithmetic): yhat = sum_b d_b (8
+ * sum_j (v_j - 16) x_j + 3.5 sum_j x_j) differs from the exact score y by at
+ * most E_n ||x||_2 (Cauchy-Schwarz on the error d (ql - 3.5)). On the device,
+ * u_n = yhat + r + s and l_n = yhat - r - s with r = E_n ||x||_2 and
+ * s = T/4 + r/256 + 2^-80, T = sum_b |d_b| sum_j |x_j|. s covers the fp32
+ * rounding of yhat and of the exact score: each fp32 step rounds once (a
+ * pair-dot step at most twice), on intermediates of at most
+ * 8 (1055 + 1040) |d_b| sum|x| per block for yhat and (1279 + 1152) |d_b| sum|x|
+ * for the exact score, plus running sums of at most 128 T and 127 T over at
+ * most 2 K/32 + 6 steps: below 0.05 T together for K <= 16384. The row c
+ * with the largest l is scored exactly (tau); rows with u_n < tau score below
+ * row c and are skipped; every other row is scored exactly and the largest
+ * wins (lowest index on ties, NaN never wins). */
+
+/* Bytes of the bound copy of an N x K Q8_0 matrix (< 0: the error of an
+ * invalid shape: K not a positive multiple of 256 or above
+ * KQ_SHORTLIST_MAX_K, N out of range, or the matrix or copy reaching 2 GiB). */
+#define KQ_SHORTLIST_MAX_K 16384
+int64_t kq_shortlist_copy_bytes(int64_t N, int64_t K);
+
+/* kq_shortlist_pack — host: the bound copy (above) of the packed Q8_0 matrix
+ * q8_packed (host, kq_packed_bytes(KQ_Q8_0, N, K) bytes) into out (host,
+ * kq_shortlist_copy_bytes(N, K) bytes). n_threads as kq_pack. The bytes are
+ * fixed by the definition above.
+ * Errors: the shape errors of kq_shortlist_copy_bytes, KQ_ERR_ARG (null
+ * pointer), KQ_ERR_RANGE (a block scale is infinite or NaN). */
+int kq_shortlist_pack(const void* q8_packed, int64_t N, int64_t K, void* out, int n_threads);
+
+/* Workspace bytes kq_shortlist_argmax needs (< 0: invalid shape). About
+ * 4 N + 12 N / 256 + 8 N / rows-per-workgroup bytes. */
+int64_t kq_shortlist_workspace_bytes(int64_t N, int64_t K);
+
+/* kq_shortlist_argmax — the index of the largest of the N scores W x of one
+ * fp16 column x (device, K halves, 16-B aligned), through the bound copy
+ * W_copy (device, kq_shortlist_pack's bytes, 16-B aligned) of the Q8_0
+ * matrix W (device, 16-B aligned): out[0] (device int32) is the index
+ * kq_gemv_argmax gives for (KQ_Q8_0, W, x, N, K, M = 1) — the rows it scores
+ * exactly have the bits kq_gemv gives them, and every other row is shown to
+ * score below one of them. kept (device int32, or NULL) receives the number
+ * of rows scored exactly. y is not written. Four kernels on `stream`, no
+ * host synchronisation, no allocation: the workspace (device,
+ * kq_shortlist_workspace_bytes, 256-B aligned, caller-owned, no initial
+ * contents) holds the bounds and partial results; calls sharing a workspace
+ * must not overlap in time. It reads 65 % of W's bytes plus the rows it
+ * scores exactly: on seeded N(0, 0.02) weights with a standard normal x,
+ * about 3 % of a 151936-row layer.
+ * Errors: the shape errors of kq_shortlist_copy_bytes, KQ_ERR_ARG (null
+ * pointer, small workspace), KQ_ERR_ALIGN, KQ_ERR_HIP. */
+int kq_shortlist_argmax(const void* W, const void* W_copy, const uint16_t* x, int64_t N, int64_t K,
+                        void* workspace, int64_t workspace_bytes, int32_t* out, int32_t* kept,
+                        void* stream);
+
 /* ---- A chain of dependent M = 1 GEMVs in one persistent launch ----------
  * Kinetic docs, "What makes it fast": a decode step is hundreds of small GPU
  * kernels, recorded once and replayed with one call per token. kq_stack_run
@@ -366,7 +435,7 @@ int kq_stack_status(const void* plan, const kq_stack_info* info, int* error, voi
  *                    "chunk_split", "direct"
  *   valu_g, valu_r, lds_wpg, mfma_s, mfma_r, mfma_waves, mfma_xf,
  *   mfma_pers_tpw, mfma_pers_waves, mfma_chunk_l2cg, moe_unfused,
- *   moe_min_wg, moe_one, mfma_split                           (decimal integers)
+ *   moe_min_wg, moe_one, mfma_split, sl_g                     (decimal integers)
  *   log              "1": one line per kernel launch on stderr (kernel, format,
  *                    shape, grid, workgroup, LDS bytes, chosen configuration)
  * Errors: KQ_ERR_ARG (unknown name or malformed value). Not synchronised

@@ -313,3 +313,41 @@ def test_stack_plan_rejects_five_bit_formats():
     for fmt in (kq.KQ_Q5_0, kq.KQ_Q5_1):
         arr = _stage_arr([dict(fmt=fmt, W=A16, x=A16, y=A16 + 4096, N=64, K=256)])
         assert kq.lib().kq_stack_plan_bytes(arr, 1) == kq.KQ_ERR_FORMAT
+
+
+def test_shortlist_sizes_and_validation():
+    L = kq.lib()
+    assert kq.kq_shortlist_copy_bytes(151936, 2560) == 151936 * (22 * 80 + 4)
+    assert L.kq_shortlist_copy_bytes(100, 2048 + 32) == kq.KQ_ERR_SHAPE     # K not a multiple of 256
+    assert L.kq_shortlist_copy_bytes(100, 16384 + 256) == kq.KQ_ERR_SHAPE   # above KQ_SHORTLIST_MAX_K
+    assert L.kq_shortlist_copy_bytes(0, 2560) == kq.KQ_ERR_ARG
+    assert L.kq_shortlist_copy_bytes(8_000_000, 16384) == kq.KQ_ERR_SHAPE   # the matrix reaches 2 GiB
+    need = kq.kq_shortlist_workspace_bytes(151936, 2560)
+    assert need >= 4 * 151936 + 12 * (151936 // 256)
+
+    def call(W=A16, Wc=A16, x=A16, N=151936, K=2560, ws=A16, wsb=need, out=A16, kept=None):
+        return L.kq_shortlist_argmax(W, Wc, x, N, K, ws, wsb, out, kept, 0)
+    assert call(K=2304 + 32) == kq.KQ_ERR_SHAPE
+    assert call(N=0) == kq.KQ_ERR_ARG
+    assert call(Wc=None) == kq.KQ_ERR_ARG
+    assert call(out=None) == kq.KQ_ERR_ARG
+    assert call(wsb=need - 4) == kq.KQ_ERR_ARG
+    assert call(ws=None) == kq.KQ_ERR_ARG
+    assert call(W=A16 + 4) == kq.KQ_ERR_ALIGN
+    assert call(Wc=A16 + 8) == kq.KQ_ERR_ALIGN
+    assert call(x=A4) == kq.KQ_ERR_ALIGN
+    assert call(out=A16 + 2) == kq.KQ_ERR_ALIGN
+    assert call(kept=A16 + 2) == kq.KQ_ERR_ALIGN
+    assert call(ws=A16 + 16) == kq.KQ_ERR_ALIGN
+
+
+def test_shortlist_pack_validation():
+    L = kq.lib()
+    q8 = np.zeros(kq.kq_packed_bytes("q8_0", 2, 256), np.uint8)
+    out = np.zeros(kq.kq_shortlist_copy_bytes(2, 256), np.uint8)
+    assert L.kq_shortlist_pack(None, 2, 256, out.ctypes.data, 1) == kq.KQ_ERR_ARG
+    assert L.kq_shortlist_pack(q8.ctypes.data, 2, 288, out.ctypes.data, 1) == kq.KQ_ERR_SHAPE
+    q8[34 * 9 + 1] = 0x7C          # row 1, block 1: scale bits 0x7C00 = +inf
+    with pytest.raises(kq.KQError) as e:
+        kq.kq_shortlist_pack(q8, 2, 256)
+    assert e.value.status == kq.KQ_ERR_RANGE

@@ -103,3 +103,46 @@ def test_fp16_conversion_exhaustive_near_range():
             got = kq.kq_f32_to_f16(f)
             bad = np.nonzero(got != want)[0]
             assert bad.size == 0, f"{bad.size} mismatches, first {f[bad[0]]!r}: {got[bad[0]]:#x} vs {want[bad[0]]:#x}"
+
+
+# ------------------------------------------------------- Shortlist bound copy
+from oracle import shortlist as SL  # noqa: E402
+
+
+@pytest.mark.parametrize("row", G.all_shortlist_rows(), ids=lambda r: r["name"])
+def test_shortlist_golden_rows_through_c_packer(row):
+    q8 = F.encode("q8_0", row["fields"])
+    got = kq.kq_shortlist_pack(q8, 1, row["k"])
+    assert got.tobytes() == row["bytes"].tobytes()
+
+
+def _raw_q8(n, k, seed):
+    """Q8_0 bytes with every int8 (including -128) and scales across fp16's
+    range: subnormal, tiny, ordinary, huge, zero."""
+    rng = np.random.default_rng(seed)
+    nb = k // 32
+    d = rng.choice(np.array([0.0, 2.0 ** -24, 3 * 2.0 ** -20, 1e-3, 0.02, 1.0, 300.0, 65504.0], np.float16),
+                   size=(n, nb))
+    q = rng.integers(-128, 128, size=(n, nb, 32)).astype(np.int8)
+    return F.encode("q8_0", {"d": d, "q": q}), {"d": d, "q": q}
+
+
+@pytest.mark.parametrize("n,k,seed", [(3, 256, 0), (17, 512, 1), (64, 2560, 2), (5, 16384, 3)])
+def test_shortlist_copy_bytes_identical(n, k, seed):
+    q8, fields = _raw_q8(n, k, seed)
+    got = kq.kq_shortlist_pack(q8, n, k)
+    assert got.tobytes() == SL.encode_bound_copy(fields).tobytes()
+
+
+def test_shortlist_copy_of_seeded_layer_identical():
+    W = S.weights((92, 0, 0, 0), 300, 2560)
+    q8 = kq.kq_pack("q8_0", W)
+    got = kq.kq_shortlist_pack(q8, 300, 2560)
+    assert got.tobytes() == SL.encode_bound_copy(F.decode("q8_0", q8, 300, 2560)).tobytes()
+
+
+def test_shortlist_pack_multithreaded_identical():
+    q8, _ = _raw_q8(4096, 512, 9)
+    one = kq.kq_shortlist_pack(q8, 4096, 512, n_threads=1)
+    many = kq.kq_shortlist_pack(q8, 4096, 512, n_threads=8)
+    assert one.tobytes() == many.tobytes()
