@@ -1285,12 +1285,18 @@ int launch_mfma_fmt(const GemvArgs& a) {
     if (!want_chunk) {
       // with a workspace, a K split where it pays (also where all of x would
       // not fit one workgroup's LDS)
+      // Offset terms from block sums staged in LDS up to 4 columns, from an
+      // MFMA against ones beyond (measured on the decode shapes, cold, M = 4:
+      // q|k|v 6.62 -> 6.32 us, gate|up 12.29 -> 11.63, down with its K split
+      // 10.97 -> 10.83, o 6.22 / 6.24; at 6..16 columns the sums lose, e.g.
+      // gate|up 12.46 -> 13.45 at 8). "teams" / "teams_sx" force one way.
+      const bool no_sums = !(var == MV_TEAMS_SX || (var != MV_TEAMS && a.M <= 4));
       const int ns = a.ws ? split_count(a) : 1;
       if (ns > 1) {
-        const MfmaLdsCfg cs = split_cfg(a, ns, MfmaLdsMaxP<FMT>::v, var != MV_TEAMS_SX);
+        const MfmaLdsCfg cs = split_cfg(a, ns, MfmaLdsMaxP<FMT>::v, no_sums);
         if (cs.ok && a.ws_bytes >= (int64_t)ns * a.M * a.N * 4) return launch_mfma_split<FMT>(a, ns, cs);
       }
-      const MfmaLdsCfg c = mfma_lds_cfg(a.N, a.K, (int)a.M, MfmaLdsMaxP<FMT>::v, var != MV_TEAMS_SX);
+      const MfmaLdsCfg c = mfma_lds_cfg(a.N, a.K, (int)a.M, MfmaLdsMaxP<FMT>::v, no_sums);
       if (c.ok) return launch_mfma_lds<FMT>(a, 0, (int)a.M, c);
     }
   }
