@@ -18,7 +18,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libkq.so")
 
 KQ_Q8_0, KQ_Q4_0, KQ_AFFINE4_G32, KQ_Q5_0, KQ_Q5_1 = 0, 1, 2, 3, 4
-FORMATS = {"q8_0": KQ_Q8_0, "q4_0": KQ_Q4_0, "affine4": KQ_AFFINE4_G32, "q5_0": KQ_Q5_0, "q5_1": KQ_Q5_1}
+KQ_Q4_1 = KQ_AFFINE4_G32   # the same scale-and-minimum 4-bit block
+FORMATS = {"q8_0": KQ_Q8_0, "q4_0": KQ_Q4_0, "affine4": KQ_AFFINE4_G32, "q5_0": KQ_Q5_0, "q5_1": KQ_Q5_1,
+           "q4_1": KQ_Q4_1}
 KQ_OK, KQ_ERR_ARG, KQ_ERR_FORMAT, KQ_ERR_SHAPE, KQ_ERR_ALIGN, KQ_ERR_RANGE, KQ_ERR_HIP = 0, -1, -2, -3, -4, -5, -6
 KQ_MAX_M = 64
 

@@ -26,6 +26,9 @@
  *   KQ_AFFINE4_G32 20 B: fp16 s, fp16 b, 16 B nibbles;    w' = s*q + b
  *   KQ_Q5_0        22 B: fp16 d, 4 B fifth bits, 16 B nibbles;          w' = d*(q-16)
  *   KQ_Q5_1        24 B: fp16 d, fp16 m, 4 B fifth bits, 16 B nibbles;  w' = d*q + m
+ * KQ_Q4_1 names the affine4 gs32 block: the scale-and-minimum 4-bit format
+ * (Kinetic docs, "Supported models" list Q4_1 but print no layout; read as
+ * Q5_1 with four bits, it is this block, 15 steps from the minimum).
  * fp16 values are little-endian; in the nibble areas element j sits in the
  * low nibble of byte j and element j+16 in the high nibble (the low four bits
  * of q in the 5-bit formats, whose bit 4 of q_j is bit j of the little-endian
@@ -61,7 +64,8 @@ typedef enum kq_format {
   KQ_Q4_0 = 1,
   KQ_AFFINE4_G32 = 2,
   KQ_Q5_0 = 3,
-  KQ_Q5_1 = 4
+  KQ_Q5_1 = 4,
+  KQ_Q4_1 = KQ_AFFINE4_G32
 } kq_format;
 
 typedef enum kq_status {

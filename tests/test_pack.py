@@ -79,6 +79,19 @@ def test_unpack_matches_oracle_dequant(fmt):
     assert np.array_equal(back.astype(np.float64), ref)
 
 
+def test_q4_1_is_the_affine4_block():
+    """Q4_1 read as Q5_1 with four bits is the affine4 gs32 block: the same
+    enum value, the same bytes from the packer, the affine4 golden blocks
+    under the Q4_1 name."""
+    assert kq.KQ_Q4_1 == kq.KQ_AFFINE4_G32 and kq.FORMATS["q4_1"] == kq.KQ_AFFINE4_G32
+    assert kq.kq_block_bytes("q4_1") == 20
+    W = S.weights((92, 0, 0, 0), 33, 512)
+    assert np.array_equal(kq.kq_pack("q4_1", W), kq.kq_pack("affine4", W))
+    for blk in G.all_blocks():
+        if blk["format"] == "affine4":
+            assert kq.kq_pack("q4_1", blk["weights"][None, :])[0].tobytes() == blk["bytes"].tobytes()
+
+
 def test_multithreaded_pack_identical():
     W = S.weights((89, 0, 0, 0), 1000, 2048)
     a = kq.kq_pack("affine4", W, n_threads=1)
