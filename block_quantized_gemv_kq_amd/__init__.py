@@ -23,6 +23,8 @@ FORMATS = {"q8_0": KQ_Q8_0, "q4_0": KQ_Q4_0, "affine4": KQ_AFFINE4_G32, "q5_0": 
            "q4_1": KQ_Q4_1}
 KQ_OK, KQ_ERR_ARG, KQ_ERR_FORMAT, KQ_ERR_SHAPE, KQ_ERR_ALIGN, KQ_ERR_RANGE, KQ_ERR_HIP = 0, -1, -2, -3, -4, -5, -6
 KQ_MAX_M = 64
+KQ_MAX_K = 1 << 20       # inputs per row
+KQ_MAX_N = 0x7FFFFFFF   # output rows per call
 
 # Every symbol include/kq.h declares, with (restype, argtypes).
 _I64, _I32, _P = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p

@@ -113,6 +113,14 @@ def test_moe_validation():
     assert _moe(M=0) == kq.KQ_OK
 
 
+def test_limit_constants_match_header():
+    src = open(HEADER).read()
+    for name in ("KQ_MAX_M", "KQ_MAX_K", "KQ_MAX_N"):
+        m = re.search(r"#define\s+%s\s+(.+?)\s*/\*" % name, src)
+        assert m, name
+        assert eval(m.group(1), {}) == getattr(kq, name), name
+
+
 def test_moe_ffn_validation():
     L = kq.lib()
     need = kq.kq_moe_ffn_workspace_bytes(2048, 768, 4, 8)
