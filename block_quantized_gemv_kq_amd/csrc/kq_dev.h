@@ -470,6 +470,34 @@ __device__ __forceinline__ void stage_to_lds(const void* src, uint32_t* dst, int
   }
 }
 
+// Padded staging of activations. The lane groups of a wave read x of
+// consecutive load units (UP = 4 UB pieces of 16 bytes each) at the same
+// piece offset, so with the pieces back to back the lanes of one LDS read
+// fall into two 16-byte bank slots (8-way conflicts on 32 banks). With one
+// idle piece after every unit the unit stride is UP + 1 pieces, an odd number
+// that walks every bank slot: piece P of the staged run sits at slot
+// xphys(P) = P + P / UP, and a run of n16 pieces (a multiple of UP) takes
+// xrun_pieces(n16) slots. Offsets within a unit stay immediate.
+template <int UP>
+__host__ __device__ constexpr int xphys(int P) { return UP ? P + P / UP : P; }
+template <int UP>
+__host__ __device__ constexpr int xrun_pieces(int n16) { return UP ? n16 + n16 / UP : n16; }
+
+// stage_to_lds into the padded layout: slot s holds piece s - s / (UP + 1)
+// unless it is a unit's idle slot (s % (UP + 1) == UP), which is not written.
+template <int UP>
+__device__ __forceinline__ void stage_to_lds_padded(const void* src, uint32_t* dst, int n16, int nthreads) {
+  const int nslot = xrun_pieces<UP>(n16);
+  for (int i = threadIdx.x; i < nslot; i += nthreads) {
+    const int q = i / (UP + 1), r = i - q * (UP + 1);
+    if (r < UP) {
+      const int wave_first = i - (int)(threadIdx.x & 63);   // lane L lands at wave_first + L
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(reinterpret_cast<const u32x4*>(src) + q * UP + r),
+                                       (lds_void_t*)(dst + 4 * wave_first), 16, 0, 0);
+    }
+  }
+}
+
 // Offset that lies past every buffer's num_records: loads there return 0.
 constexpr uint32_t OOB = 0x80000000u;
 
@@ -571,10 +599,11 @@ __device__ __forceinline__ float block_dot_split(const uint32_t* A, const uint32
 // i.e. xs[h] is the sum of half-block h of the run. Every thread of the
 // workgroup (nthreads, as for stage_to_lds) takes part; follow with
 // __syncthreads().
+template <int UP = 0>
 __device__ __forceinline__ void block_sums_to_lds(const uint32_t* xl, int kdw, int mt, float* xs, int nthreads) {
   const int halves = mt * kdw / 8;
   for (int h = threadIdx.x; h < halves; h += nthreads) {
-    const u32x4* p = reinterpret_cast<const u32x4*>(xl) + 2 * h;
+    const u32x4* p = reinterpret_cast<const u32x4*>(xl) + xphys<UP>(2 * h);   // both pieces in one unit
     const u32x4 a = p[0], c = p[1];
     float s = 0.0f;
     s = dot2(a.x, ONES, s);
@@ -590,12 +619,14 @@ __device__ __forceinline__ void block_sums_to_lds(const uint32_t* xl, int kdw, i
 }
 
 // Consume loaded units against MT activation columns held in LDS (column m
-// at xl + m * kdw dwords) with their per-block sums in xs.
-template <int FMT, int MT, int ITERS>
+// at xl + m * kdw dwords, or at piece m * K / 8 of the padded layout when
+// PAD) with their per-block sums in xs.
+template <int FMT, int MT, int ITERS, bool PAD = false>
 __device__ __forceinline__ void consume_units(const Loaded<FMT, ITERS>& w, const uint32_t* xl,
                                               const float* xs, int kdw, int first, int G, int units,
                                               float (&acc)[MT]) {
   constexpr int UB = Fmt<FMT>::UB;
+  constexpr int UP = PAD ? 4 * UB : 0;
   const int nblk = kdw / 16;
 #pragma unroll
   for (int it = 0; it < ITERS; ++it) {
@@ -605,7 +636,7 @@ __device__ __forceinline__ void consume_units(const Loaded<FMT, ITERS>& w, const
       unpack_unit_split<FMT>(w.D[it], up);
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
-        const u32x4* xp = reinterpret_cast<const u32x4*>(xl + m * kdw + u * 16 * UB);
+        const u32x4* xp = reinterpret_cast<const u32x4*>(xl) + xphys<UP>(m * (kdw / 4) + 4 * UB * u);
         const float2* sp = reinterpret_cast<const float2*>(xs) + m * nblk + u * UB;
         uint32_t X[16 * UB];
 #pragma unroll

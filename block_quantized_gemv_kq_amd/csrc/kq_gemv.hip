@@ -102,7 +102,8 @@ __global__ __launch_bounds__(64 * WPG) void k_gemv_lds(const uint8_t* __restrict
   const int g = lane & (G - 1);
   const uint32_t roff = (uint32_t)rho * row_bytes;
   const int kdw = K / 2;
-  float* xs = reinterpret_cast<float*>(xl + MT * kdw);
+  constexpr int UP = 4 * Fmt<FMT>::UB;   // pieces per load unit: x is staged with one idle piece after each
+  float* xs = reinterpret_cast<float*>(xl + 4 * xrun_pieces<UP>(MT * K / 8));
   // XREG: the activations go ahead of the weights in this CU's memory queue,
   // loaded into registers (at most xreg_chunks 16-byte chunks per thread), so
   // writing them to LDS waits for them alone and the block sums below overlap
@@ -130,21 +131,20 @@ __global__ __launch_bounds__(64 * WPG) void k_gemv_lds(const uint8_t* __restrict
 #pragma unroll
     for (int c = 0; c < XCH; ++c) {
       const int i = (int)threadIdx.x + 64 * WPG * c;
-      if (i < n16) xl4[i] = xr[c];
+      if (i < n16) xl4[xphys<UP>(i)] = xr[c];
     }
   } else {
-#pragma unroll
-    for (int m = 0; m < MT; ++m) stage_to_lds(x + (int64_t)(m0 + m) * K, xl + m * kdw, K / 8, 64 * WPG);
+    stage_to_lds_padded<UP>(x + (int64_t)m0 * K, xl, n16, 64 * WPG);
   }
   __syncthreads();
-  block_sums_to_lds(xl, kdw, MT, xs, 64 * WPG);
+  block_sums_to_lds<UP>(xl, kdw, MT, xs, 64 * WPG);
   __syncthreads();
   float acc[MT];
 #pragma unroll
   for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
   const int span = G * ITERS;
   for (int p = 0;;) {
-    consume_units<FMT, MT, ITERS>(w, xl, xs, kdw, p * span + g, G, units, acc);
+    consume_units<FMT, MT, ITERS, true>(w, xl, xs, kdw, p * span + g, G, units, acc);
     if (++p >= passes) break;
     issue_units<FMT, ITERS>(rs, roff, p * span + g, G, units, w);
   }
@@ -334,6 +334,13 @@ constexpr int LDS_MAX_MT = 4;
 constexpr int MFMA_MIN_M = 4;
 constexpr int MFMA_MIN_M_UNALIGNED = 2;
 constexpr int LDS_MAX_BYTES = 96 * 1024;
+
+// LDS bytes of the one-column-family kernel: x of mt columns in the padded
+// layout (one idle 16-byte piece per load unit), then the half-block sums.
+template <int FMT>
+int64_t lds_kernel_bytes(int mt, int64_t K) {
+  return 16 * (int64_t)xrun_pieces<4 * Fmt<FMT>::UB>((int)(mt * K / 8)) + (int64_t)mt * (K / 32) * 8;
+}
 constexpr int MAX_ITERS = 5;
 
 struct LdsCfg {
@@ -398,7 +405,7 @@ int launch_lds_wpg(const GemvArgs& a, int m0, LdsCfg c, Best* part) {
   const int64_t waves = (a.N + rpw - 1) / rpw;
   const int64_t nwg = (waves + WPG - 1) / WPG;
   const dim3 grid((unsigned)nwg), block(64 * WPG);
-  const size_t lds = (size_t)MT * a.K * 2 + (size_t)MT * (a.K / 32) * 8;  // x + block sums
+  const size_t lds = (size_t)lds_kernel_bytes<FMT>(MT, a.K);   // x (padded) + block sums
   const bool xreg = (int64_t)MT * a.K / 8 <= 64 * WPG * xreg_chunks<MT, WPG>();
   dispatch_log("k_gemv_lds", a.fmt, a.N, a.K, MT, grid.x, 1, 64 * WPG, lds,
                "G=%d units/lane=%d passes=%d x=%s m0=%d argmax=%d", 1 << c.log2g, ITERS, c.passes,
@@ -478,7 +485,7 @@ int dispatch(const GemvArgs& a) {
   if (a.K % (32 * Fmt<FMT>::UB) != 0) return a.M >= MFMA_MIN_M_UNALIGNED ? launch_gemv_mfma(a) : launch_generic<FMT>(a);
   const int force = tune_int(TUNE_FORCE_PATH);  // tests: run a given path at any shape
   if (force == 'g') return launch_generic<FMT>(a);
-  const bool lds_fits = (int64_t)(a.M < LDS_MAX_MT ? a.M : LDS_MAX_MT) * (a.K * 2 + a.K / 4) <= LDS_MAX_BYTES;
+  const bool lds_fits = lds_kernel_bytes<FMT>(a.M < LDS_MAX_MT ? a.M : LDS_MAX_MT, a.K) <= LDS_MAX_BYTES;
   if (force == 'v') return launch_valu<FMT>(a);     // register-x VALU kernel
   if (force == 'l' && lds_fits) return launch_lds<FMT>(a);
   if (force == 'm') return launch_gemv_mfma(a);
@@ -529,7 +536,7 @@ namespace {
 template <int FMT>
 bool argmax_fusable(const GemvArgs& a, LdsCfg* cfg) {
   if (a.K % (32 * Fmt<FMT>::UB) != 0 || a.M != 1) return false;
-  if ((int64_t)a.M * (a.K * 2 + a.K / 4) > LDS_MAX_BYTES) return false;
+  if (lds_kernel_bytes<FMT>(a.M, a.K) > LDS_MAX_BYTES) return false;
   if (tune(TUNE_FORCE_PATH) != TUNE_UNSET) return false;
   const int units = (int)(a.K / (32 * Fmt<FMT>::UB));
   *cfg = lds_cfg(a.N, units, Fmt<FMT>::BB * Fmt<FMT>::UB);
