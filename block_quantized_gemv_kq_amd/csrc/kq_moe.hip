@@ -219,7 +219,9 @@ __global__ __launch_bounds__(256) void k_moe_lds(const uint8_t* __restrict__ W0,
   uint32_t* xl = reinterpret_cast<uint32_t*>(x_lds4);
   const int kdw = K / 2;
   const int nblk = K / 32;
-  float* xs = reinterpret_cast<float*>(xl + MOE_COLS * kdw);
+  constexpr int UP = 4 * Fmt<FMT>::UB;   // x staged with an idle piece after each load unit
+  const int xdw = 4 * xrun_pieces<UP>(MOE_COLS * (K / 8));
+  float* xs = reinterpret_cast<float*>(xl + xdw);
   int* s_ids = reinterpret_cast<int*>(xs + MOE_COLS * nblk * 2);
   const int P = M * top_k;
   int* s_list = s_ids + P;
@@ -271,7 +273,7 @@ __global__ __launch_bounds__(256) void k_moe_lds(const uint8_t* __restrict__ W0,
   const int xrows = (GATE_UP || !x_per_slot) ? M : P;
   const rsrc_t xsrc = make_rsrc(x, (uint32_t)xrows * (uint32_t)K * 2u);
   // a 16-byte slot after the slot list for pieces past the x area
-  const int idle = (int)(((uint32_t)(MOE_COLS * kdw + MOE_COLS * nblk * 2 + 2 * P) * 4u + 15u) / 16u);
+  const int idle = (int)(((uint32_t)(xdw + MOE_COLS * nblk * 2 + 2 * P) * 4u + 15u) / 16u);
   for (int c0 = 0; c0 < cnt; c0 += MOE_COLS) {
     const int mt = cnt - c0 < MOE_COLS ? cnt - c0 : MOE_COLS;
     if (c0 > 0) __syncthreads();   // the previous pass has finished reading LDS
@@ -299,10 +301,10 @@ __global__ __launch_bounds__(256) void k_moe_lds(const uint8_t* __restrict__ W0,
 #pragma unroll
     for (int c = 0; c < MOE_XCH; ++c) {
       const int i = (int)threadIdx.x + 256 * c;
-      x_lds4[i < MOE_COLS * kq8 ? i : idle] = xr[c];   // unused pieces land past the x of this pass
+      x_lds4[i < MOE_COLS * kq8 ? xphys<UP>(i) : idle] = xr[c];   // unused pieces land past the x of this pass
     }
     __syncthreads();
-    block_sums_to_lds(xl, kdw, mt, xs, 256);
+    block_sums_to_lds<UP>(xl, kdw, mt, xs, 256);
     __syncthreads();
     float a0[MOE_COLS], a1[MOE_COLS];
 #pragma unroll
@@ -312,8 +314,8 @@ __global__ __launch_bounds__(256) void k_moe_lds(const uint8_t* __restrict__ W0,
   case MTV: {                                                                                                \
     float b0[MTV], b1[MTV];                                                                                  \
     for (int m = 0; m < MTV; ++m) b0[m] = b1[m] = 0.0f;                                                      \
-    consume_units<FMT, MTV, ITERS>(w0, xl, xs, kdw, g, G, units, b0);                                        \
-    if constexpr (GATE_UP) consume_units<FMT, MTV, ITERS>(w1, xl, xs, kdw, g, G, units, b1);                 \
+    consume_units<FMT, MTV, ITERS, true>(w0, xl, xs, kdw, g, G, units, b0);                                  \
+    if constexpr (GATE_UP) consume_units<FMT, MTV, ITERS, true>(w1, xl, xs, kdw, g, G, units, b1);           \
     group_reduce<MTV>(b0, G);                                                                                \
     if constexpr (GATE_UP) group_reduce<MTV>(b1, G);                                                         \
     for (int m = 0; m < MTV; ++m) { a0[m] = b0[m]; a1[m] = b1[m]; }                                          \
@@ -362,7 +364,9 @@ __global__ __launch_bounds__(256) void k_moe_gate_up_one(const uint8_t* __restri
   uint32_t* xl = reinterpret_cast<uint32_t*>(x_lds4);
   const int kdw = K / 2;
   const int nblk = K / 32;
-  float* xs = reinterpret_cast<float*>(xl + kdw);
+  constexpr int UP = 4 * Fmt<FMT>::UB;   // x staged with an idle piece after each load unit
+  const int xdw = 4 * xrun_pieces<UP>(K / 8);
+  float* xs = reinterpret_cast<float*>(xl + xdw);
   const int p = blockIdx.y;
   // the token's activations: registers, ahead of the weights
   const int kq8 = K / 8;
@@ -407,18 +411,18 @@ __global__ __launch_bounds__(256) void k_moe_gate_up_one(const uint8_t* __restri
 #pragma unroll
   for (int q = 0; q < NIDS; ++q) dup |= q < p && idv[q] == e;
   if (dup) return;   // uniform over the workgroup
-  const int idle = (kdw + nblk * 2 + 3) / 4;
+  const int idle = (xdw + nblk * 2 + 3) / 4;
 #pragma unroll
   for (int c = 0; c < XCH; ++c) {
     const int i = (int)threadIdx.x + 256 * c;
-    x_lds4[i < kq8 ? i : idle] = xr[c];   // unused pieces land in the idle slot
+    x_lds4[i < kq8 ? xphys<UP>(i) : idle] = xr[c];   // unused pieces land in the idle slot
   }
   __syncthreads();
-  block_sums_to_lds(xl, kdw, 1, xs, 256);
+  block_sums_to_lds<UP>(xl, kdw, 1, xs, 256);
   __syncthreads();
   float b0[1] = {0.0f}, b1[1] = {0.0f};
-  consume_units<FMT, 1, ITERS>(w0, xl, xs, kdw, g, G, units, b0);
-  consume_units<FMT, 1, ITERS>(w1, xl, xs, kdw, g, G, units, b1);
+  consume_units<FMT, 1, ITERS, true>(w0, xl, xs, kdw, g, G, units, b0);
+  consume_units<FMT, 1, ITERS, true>(w1, xl, xs, kdw, g, G, units, b1);
   group_reduce<1>(b0, G);
   group_reduce<1>(b1, G);
   if (g == 0 && rho < rows) {
@@ -448,9 +452,11 @@ __global__ __launch_bounds__(1024) void k_moe_down_sum(const uint8_t* __restrict
   const int lane = threadIdx.x & 63;
   const int j = wave_id();                       // this wave's slot
   const int kdw = K / 2, nblk = K / 32;
-  const int slot_dw = kdw + nblk * 2;            // x dwords + block sums of one slot
+  constexpr int UP = 4 * Fmt<FMT>::UB;           // x staged with an idle piece after each load unit
+  const int xdw = 4 * xrun_pieces<UP>(K / 8);
+  const int slot_dw = xdw + nblk * 2;            // x dwords + block sums of one slot
   uint32_t* xl = reinterpret_cast<uint32_t*>(x_lds4) + (int64_t)j * slot_dw;
-  float* xs = reinterpret_cast<float*>(xl + kdw);
+  float* xs = reinterpret_cast<float*>(xl + xdw);
   float* s_y = reinterpret_cast<float*>(reinterpret_cast<uint32_t*>(x_lds4) + (int64_t)top_k * slot_dw);
   const int G = 1 << log2g;
   const int rpw = 64 >> log2g;
@@ -483,12 +489,12 @@ __global__ __launch_bounds__(1024) void k_moe_down_sum(const uint8_t* __restrict
 #pragma unroll
   for (int c = 0; c < MOE_XCH; ++c) {
     const int i = lane + 64 * c;
-    if (i < kq8) xl4[i] = xr[c];
+    if (i < kq8) xl4[xphys<UP>(i)] = xr[c];
   }
   __syncthreads();
   // block sums of this slot's x (as block_sums_to_lds for one column)
   for (int h = lane; h < kdw / 8; h += 64) {
-    const u32x4* q = reinterpret_cast<const u32x4*>(xl) + 2 * h;
+    const u32x4* q = reinterpret_cast<const u32x4*>(xl) + xphys<UP>(2 * h);
     const u32x4 a = q[0], c = q[1];
     float v = 0.0f;
     v = dot2(a.x, ONES, v); v = dot2(a.y, ONES, v); v = dot2(a.z, ONES, v); v = dot2(a.w, ONES, v);
@@ -497,7 +503,7 @@ __global__ __launch_bounds__(1024) void k_moe_down_sum(const uint8_t* __restrict
   }
   __syncthreads();
   float acc[1] = {0.0f};
-  consume_units<FMT, 1, ITERS>(w, xl, xs, kdw, g, G, units, acc);
+  consume_units<FMT, 1, ITERS, true>(w, xl, xs, kdw, g, G, units, acc);
   group_reduce<1>(acc, G);
   if (g == 0 && rho < valid) s_y[j * rpw + rho] = e_ok ? acc[0] : __builtin_nanf("");
   __syncthreads();
@@ -638,7 +644,8 @@ int launch_moe_lds(const uint8_t* W0, const uint8_t* W1, const uint16_t* x, cons
   const int64_t waves = (N + rpw - 1) / rpw;
   const int P = M * top_k;
   const dim3 grid((unsigned)((waves + 3) / 4), (unsigned)P), block(256);
-  const size_t lds = (size_t)MOE_COLS * K * 2 + (size_t)MOE_COLS * (K / 32) * 8 + (size_t)2 * P * 4 + 32;
+  const size_t lds = (size_t)16 * xrun_pieces<4 * Fmt<FMT>::UB>((int)(MOE_COLS * K / 8)) +
+                     (size_t)MOE_COLS * (K / 32) * 8 + (size_t)2 * P * 4 + 32;
   dispatch_log(GATE_UP ? "k_moe_lds(gate|up+swiglu)" : "k_moe_lds", FMT, N, K, M, grid.x, grid.y, 256, lds,
                "G=%d units/lane=%d slots=%d", 1 << log2g, iters, P);
 #define KQ_MOE_LAUNCH(IT)                                                                                       \
@@ -677,6 +684,12 @@ int moe_dispatch(const MoeArgs& a) {
   return (int)hipGetLastError();
 }
 
+// LDS bytes of k_moe_gate_up_one: x (padded), its block sums, an idle slot.
+template <int FMT>
+int64_t moe_one_lds_bytes(int64_t hidden) {
+  return 16 * (int64_t)xrun_pieces<4 * Fmt<FMT>::UB>((int)(hidden / 8)) + (hidden / 32) * 8 + 32;
+}
+
 template <int FMT, int XCH, int NIDS>
 int launch_moe_gate_up_one(const MoeGateUpArgs& a, int64_t eb) {
   const int units = (int)(a.hidden / (32 * Fmt<FMT>::UB));
@@ -685,7 +698,7 @@ int launch_moe_gate_up_one(const MoeGateUpArgs& a, int64_t eb) {
   const int64_t rpw = 64 >> log2g;
   const int64_t waves = (a.inter + rpw - 1) / rpw;
   const dim3 grid((unsigned)((waves + 3) / 4), (unsigned)a.top_k), block(256);
-  const size_t lds = (size_t)a.hidden * 2 + (size_t)(a.hidden / 32) * 8 + 16 + 16;
+  const size_t lds = moe_one_lds_bytes<FMT>(a.hidden);
   dispatch_log("k_moe_gate_up_one", FMT, a.inter, a.hidden, 1, grid.x, grid.y, 256, lds, "G=%d units/lane=%d slots=%d",
                1 << log2g, iters, a.top_k);
 #define KQ_MOE_ONE(IT)                                                                                        \
@@ -710,7 +723,7 @@ int gate_up_dispatch(const MoeGateUpArgs& a) {
   // one token: the routing-off-the-path kernel (the moe_one tuning override,
   // 0, forces the general kernel)
   if (a.M == 1 && a.top_k <= 16 && a.hidden % (32 * Fmt<FMT>::UB) == 0 && tune(TUNE_MOE_ONE) != 0 &&
-      eb <= INT32_MAX && (int64_t)a.hidden * 2 + (a.hidden / 32) * 8 + 32 <= 64 * 1024) {
+      eb <= INT32_MAX && moe_one_lds_bytes<FMT>(a.hidden) <= 64 * 1024) {
     if (a.hidden / 8 <= 256)
       return a.top_k <= 8 ? launch_moe_gate_up_one<FMT, 1, 8>(a, eb) : launch_moe_gate_up_one<FMT, 1, 16>(a, eb);
     if (a.hidden / 8 <= 1024)
@@ -736,7 +749,8 @@ int launch_moe_down_sum_fmt(const MoeArgs& a, const float* rw, float* y) {
   const int iters = (units + (1 << log2g) - 1) >> log2g;
   const int64_t rpw = 64 >> log2g;
   const dim3 grid((unsigned)((a.N + rpw - 1) / rpw)), block((unsigned)(64 * a.top_k));
-  const size_t lds = (size_t)a.top_k * ((size_t)a.K * 2 + (size_t)(a.K / 32) * 8) + (size_t)a.top_k * rpw * 4;
+  const size_t lds = (size_t)a.top_k * ((size_t)16 * xrun_pieces<4 * Fmt<FMT>::UB>((int)(a.K / 8)) +
+                                         (size_t)(a.K / 32) * 8) + (size_t)a.top_k * rpw * 4;
   dispatch_log("k_moe_down_sum", FMT, a.N, a.K, a.M, grid.x, 1, block.x, lds, "G=%d units/lane=%d top_k=%d",
                1 << log2g, iters, a.top_k);
 #define KQ_MOE_DS(IT)                                                                                          \

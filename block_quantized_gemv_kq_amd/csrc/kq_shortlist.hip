@@ -42,6 +42,11 @@ namespace kqd {
 
 constexpr int SL_UB = 4;          // blocks per load unit of the bound copy
 constexpr int SL_WPG = 4;         // waves per workgroup (bound and exact kernels)
+// x in LDS with an idle 16-byte piece after each load unit's pieces (no LDS
+// bank conflicts between lane groups): 16 pieces per bound-copy unit, 8 per
+// Q8_0 unit of the exact scores
+constexpr int SL_XUP = 4 * SL_UB;
+constexpr int Q8_XUP = 4 * Fmt<F_Q8_0>::UB;
 
 // Pivot record in the workspace: tau = exact score of row c (NaN: keep every row).
 struct SlPivot {
@@ -114,7 +119,7 @@ __device__ __forceinline__ void sl_consume(const SlUnit (&w)[ITERS], const uint3
           A[8 + 2 * i] = perm(MAGIC, hi, SEL_LO);
           A[9 + 2 * i] = perm(MAGIC, hi, SEL_HI);
         }
-        const u32x4* xp = reinterpret_cast<const u32x4*>(xl + 16 * b);
+        const u32x4* xp = reinterpret_cast<const u32x4*>(xl) + xphys<SL_XUP>(4 * b);
         float dot = 0.0f;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
@@ -153,7 +158,7 @@ __device__ __forceinline__ void sl_x_load(const uint16_t* __restrict__ x, int K,
 // one-column GEMV kernel forms them; with ABS also the per-block sums of |x|
 // (xa) and ||x||_2 (returned, the same value in every thread; s_red holds
 // NT / 64 floats). Two barriers.
-template <int XCH, int NT, bool ABS>
+template <int XCH, int NT, bool ABS, int UP>
 __device__ __forceinline__ float sl_x_store(const u32x4 (&xr)[XCH], int K, uint32_t* xl, float* xs, float* xa,
                                             float* s_red) {
   const int n16 = K / 8;
@@ -162,7 +167,7 @@ __device__ __forceinline__ float sl_x_store(const u32x4 (&xr)[XCH], int K, uint3
 #pragma unroll
   for (int c = 0; c < XCH; ++c) {
     const int i = (int)threadIdx.x + NT * c;
-    if (i < n16) xl4[i] = xr[c];
+    if (i < n16) xl4[xphys<UP>(i)] = xr[c];
     if constexpr (ABS) {   // pieces past K are zero
       sq = dot2(xr[c].x, xr[c].x, sq);
       sq = dot2(xr[c].y, xr[c].y, sq);
@@ -171,12 +176,12 @@ __device__ __forceinline__ float sl_x_store(const u32x4 (&xr)[XCH], int K, uint3
     }
   }
   __syncthreads();
-  block_sums_to_lds(xl, K / 2, 1, xs, NT);
+  block_sums_to_lds<UP>(xl, K / 2, 1, xs, NT);
   float nrm = 0.0f;
   if constexpr (ABS) {
     const int nb = K / 32;
     for (int b = (int)threadIdx.x; b < nb; b += NT) {
-      const u32x4* p = xl4 + 4 * b;
+      const u32x4* p = xl4 + xphys<UP>(4 * b);
       float s = 0.0f;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
@@ -216,7 +221,7 @@ __global__ __launch_bounds__(256) void k_sl_bound(const uint8_t* __restrict__ Wc
   extern __shared__ u32x4 sl_lds[];
   uint32_t* xl = reinterpret_cast<uint32_t*>(sl_lds);
   const int nb = K / 32;
-  float* xs = reinterpret_cast<float*>(xl + K / 2);
+  float* xs = reinterpret_cast<float*>(xl + 4 * xrun_pieces<SL_XUP>(K / 8));
   float* xa = xs + 2 * nb;
   __shared__ float s_red[SL_WPG];
   __shared__ unsigned long long s_key;
@@ -243,7 +248,7 @@ __global__ __launch_bounds__(256) void k_sl_bound(const uint8_t* __restrict__ Wc
   SlUnit w[ITERS];
   sl_issue<ITERS>(rs, roff, nb, g, G, units, w);
   __builtin_amdgcn_sched_barrier(0);
-  const float xnorm = sl_x_store<XCH, 256, true>(xr, K, xl, xs, xa, s_red);
+  const float xnorm = sl_x_store<XCH, 256, true, SL_XUP>(xr, K, xl, xs, xa, s_red);
   float acc = 0.0f, C = 0.0f, T = 0.0f;
   const int span = G * ITERS;
   for (int p = 0;;) {
@@ -278,7 +283,7 @@ __device__ __forceinline__ float q8_row_finish(Loaded<F_Q8_0, ITERS>& w, rsrc_t 
   float acc[1] = {0.0f};
   const int span = G * ITERS;
   for (int p = 0;;) {
-    consume_units<F_Q8_0, 1, ITERS>(w, xl, xs, K / 2, p * span + g, G, units, acc);
+    consume_units<F_Q8_0, 1, ITERS, true>(w, xl, xs, K / 2, p * span + g, G, units, acc);
     if (++p >= passes) break;
     issue_units<F_Q8_0, ITERS>(rs, roff, p * span + g, G, units, w);
   }
@@ -299,7 +304,7 @@ __global__ __launch_bounds__(SL_PIVOT_NT) void k_sl_pivot(const uint8_t* __restr
                                                           int log2g, int passes) {
   extern __shared__ u32x4 sl_lds[];
   uint32_t* xl = reinterpret_cast<uint32_t*>(sl_lds);
-  float* xs = reinterpret_cast<float*>(xl + K / 2);
+  float* xs = reinterpret_cast<float*>(xl + 4 * xrun_pieces<Q8_XUP>(K / 8));
   __shared__ unsigned long long s_key;
   if (threadIdx.x == 0) s_key = 0ull;
   u32x4 xr[SL_PIVOT_XCH];
@@ -315,7 +320,7 @@ __global__ __launch_bounds__(SL_PIVOT_NT) void k_sl_pivot(const uint8_t* __restr
 #pragma unroll
     for (int j = 0; j < SL_PIVOT_KEYS; ++j) k = v[j] > k ? v[j] : k;
   }
-  sl_x_store<SL_PIVOT_XCH, SL_PIVOT_NT, false>(xr, K, xl, xs, nullptr, nullptr);
+  sl_x_store<SL_PIVOT_XCH, SL_PIVOT_NT, false, Q8_XUP>(xr, K, xl, xs, nullptr, nullptr);
   k = wg_max_key(k, &s_key);
   if (threadIdx.x >= 64) return;
   const Best b = best_of_key(k);
@@ -340,7 +345,7 @@ __global__ __launch_bounds__(256) void k_sl_exact(const uint8_t* __restrict__ W,
                                                   int N, int K, int log2g, int passes) {
   extern __shared__ u32x4 sl_lds[];
   uint32_t* xl = reinterpret_cast<uint32_t*>(sl_lds);
-  float* xs = reinterpret_cast<float*>(xl + K / 2);
+  float* xs = reinterpret_cast<float*>(xl + 4 * xrun_pieces<Q8_XUP>(K / 8));
   __shared__ unsigned long long s_key;
   __shared__ int32_t s_cnt;
   if (threadIdx.x == 0) {
@@ -384,7 +389,7 @@ __global__ __launch_bounds__(256) void k_sl_exact(const uint8_t* __restrict__ W,
   Loaded<F_Q8_0, ITERS> w;
   uint32_t roff = row >= 0 ? (uint32_t)row * row_bytes : OOB;
   issue_units<F_Q8_0, ITERS>(rs, roff, g, G, units, w);
-  sl_x_store<XCH, 256, false>(xr, K, xl, xs, nullptr, nullptr);
+  sl_x_store<XCH, 256, false, Q8_XUP>(xr, K, xl, xs, nullptr, nullptr);
   unsigned long long best = 0ull;
   for (;;) {
     const float y = q8_row_finish<ITERS>(w, rs, roff, xl, xs, K, g, G, passes);
@@ -546,8 +551,9 @@ int64_t shortlist_workspace_bytes(int64_t N, int64_t K) {
 int launch_shortlist_argmax(const ShortlistArgs& a) {
   const SlCfg c = sl_cfg(a.N, a.K);
   const SlWs w = sl_ws(a.ws, a.N, c);
-  const size_t lds_bound = (size_t)a.K * 2 + (size_t)(a.K / 32) * 12;   // x, half-block sums, block |x| sums
-  const size_t lds_exact = (size_t)a.K * 2 + (size_t)(a.K / 32) * 8;
+  // x (padded), half-block sums, block |x| sums / x (padded), half-block sums
+  const size_t lds_bound = (size_t)16 * xrun_pieces<SL_XUP>((int)(a.K / 8)) + (size_t)(a.K / 32) * 12;
+  const size_t lds_exact = (size_t)16 * xrun_pieces<Q8_XUP>((int)(a.K / 8)) + (size_t)(a.K / 32) * 8;
   dispatch_log("k_sl_bound", KQ_Q8_0, a.N, a.K, 1, (unsigned)c.parts1, 1, 256, lds_bound,
                "G=%d units/lane=%d passes=%d; exact rows G=%d units/lane=%d passes=%d", 1 << c.log2g, c.iters,
                c.passes, 1 << c.q8.log2g, c.q8.iters, c.q8.passes);
