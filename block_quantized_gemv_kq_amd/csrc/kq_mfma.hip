@@ -373,6 +373,14 @@ __global__ __launch_bounds__(64 * MfmaMaxWaves<T>::v) void k_gemv_mfma(const uin
 // are discarded.
 constexpr int XST_MAX = 12;   // 16-byte x pieces per thread while staging
 
+// floor(a / b) for 0 <= a < 2^16 and b >= 1 without an integer division
+// sequence (tens of scalar instructions ahead of a kernel's first load): the
+// quotient (a + 1/2) / b is at least 1 / (2 b) away from an integer, far more
+// than the error of the reciprocal and the product.
+__device__ __forceinline__ int div_small(int a, int b) {
+  return (int)(((float)a + 0.5f) * __builtin_amdgcn_rcpf((float)b));
+}
+
 // Column swizzle of the x slots of block b, lane group g.
 __device__ __forceinline__ int xsw(int b, int g, int Mp) { return (((b & 3) << 1) | (g >> 1)) & (Mp - 1); }
 
@@ -380,7 +388,7 @@ template <int FMT, int P, bool SX, bool XF>
 __global__ __launch_bounds__(1024) void k_gemv_mfma_lds(const uint8_t* __restrict__ W,
                                                        const uint16_t* __restrict__ x,
                                                        float* __restrict__ y, int N, int K, int M, int R,
-                                                       int S, int log2mp);
+                                                       int S, int log2mp, int nsplit);
 
 // One 4-block group of a 16-row tile (the lane's raw block `cur`, block
 // index 4 gi + g) against the staged x: the group's offset term as one fp32
@@ -431,13 +439,12 @@ __device__ __forceinline__ void mfma_group(const GroupRaw<FMT>& cur, uint32_t ro
 // (column stride stays K) and covers ngroups groups.
 template <bool SX, typename F, bool XF = false>
 __device__ __forceinline__ void stage_x_mfma(const uint16_t* __restrict__ x, int M, int K, int ngroups,
-                                             int log2mp, uint8_t* xlb, F issue_more, int k8_0 = 0) {
+                                             int log2mp, uint8_t* xlb, int nthreads, F issue_more, int k8_0 = 0) {
   const int Mp = 1 << log2mp;
   const int kq8 = K / 8, kq8p = 16 * ngroups;
   const int k8_lim = kq8 - k8_0;   // pieces of the column from the range start on
   const uint32_t sx_base = (uint32_t)kq8p * (uint32_t)Mp * 16u;
-  const int nthreads = (int)blockDim.x;
-  const int nwaves = nthreads >> 6;
+  const int nwaves = nthreads >> 6;   // nthreads: the workgroup size, from the caller's arguments
   const int lane = (int)threadIdx.x & 63;
   const int wv = wave_id();
   const rsrc_t xs = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
@@ -522,20 +529,19 @@ template <int FMT, int P, bool SX, bool XF>
 __global__ __launch_bounds__(1024) void k_gemv_mfma_lds(const uint8_t* __restrict__ W,
                                                        const uint16_t* __restrict__ x,
                                                        float* __restrict__ y, int N, int K, int M, int R,
-                                                       int S, int log2mp) {
+                                                       int S, int log2mp, int nsplit) {
   extern __shared__ u32x4 xl4[];
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
-  const int r = wave / S, s = wave - r * S;
+  const int r = div_small(wave, S), s = wave - r * S;
   const int n = lane & 15, g = lane >> 4;
   const int64_t row0 = ((int64_t)blockIdx.x * R + r) * 16;
   const int nblk = K / 32;
   // K split (grid y): this workgroup's groups [gs0, gs1) of the row, its
   // output the partial sums y[blockIdx.y][M][N] (one split: y itself)
-  const int ngroups_all = (nblk + 3) / 4;
-  const int nsplit = (int)gridDim.y;
-  const int gs0 = (int)((int64_t)blockIdx.y * ngroups_all / nsplit);
-  const int gs1 = (int)((int64_t)(blockIdx.y + 1) * ngroups_all / nsplit);
+  const int ngroups_all = (nblk + 3) / 4;   // nsplit = the grid's y extent (an argument)
+  const int gs0 = nsplit == 1 ? 0 : div_small((int)blockIdx.y * ngroups_all, nsplit);
+  const int gs1 = nsplit == 1 ? ngroups_all : div_small(((int)blockIdx.y + 1) * ngroups_all, nsplit);
   const int ngroups = gs1 - gs0;
   y += (int64_t)blockIdx.y * M * N;
   const int Mp = 1 << log2mp;
@@ -554,7 +560,7 @@ __global__ __launch_bounds__(1024) void k_gemv_mfma_lds(const uint8_t* __restric
       load_group<FMT>(rs, roff, 4 * gi + g, gi < gs1 && row_ok && 4 * gi + g < nblk, wr[p]);
     }
   };
-  stage_x_mfma<SX, decltype(issue), XF>(x, M, K, ngroups, log2mp, xlb, issue, 16 * gs0);
+  stage_x_mfma<SX, decltype(issue), XF>(x, M, K, ngroups, log2mp, xlb, 64 * R * S, issue, 16 * gs0);
   const int ncol = n < M ? n : M - 1;
   const u32x4* xa = xl4 + g * Mp;
   const float* sxa = reinterpret_cast<const float*>(xlb + (uint32_t)(16 * ngroups) * (uint32_t)Mp * 16u) + g * Mp + ncol;
@@ -610,13 +616,13 @@ __global__ __launch_bounds__(512) void k_gemv_mfma_chunk(const uint8_t* __restri
   }
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
-  const int r = wave / S, s = wave - r * S;
+  const int r = div_small(wave, S), s = wave - r * S;
   const int n = lane & 15, g = lane >> 4;
   const int64_t row0 = ((int64_t)blockIdx.x * R + r) * 16;
   const int nblk = K / 32;
   const int ngroups = (nblk + 3) / 4;
   const int CG = 1 << log2cg;
-  const int nchunks = (ngroups + CG - 1) / CG;
+  const int nchunks = (ngroups + CG - 1) >> log2cg;
   const uint32_t row_bytes = (uint32_t)nblk * Fmt<FMT>::BB;
   const int valid_rows = row0 < N ? (int)min<int64_t>(16, N - row0) : 0;
   const rsrc_t rs = make_rsrc(W + (valid_rows ? row0 * row_bytes : 0), ((uint32_t)valid_rows * row_bytes + 3u) & ~3u);
@@ -628,6 +634,9 @@ __global__ __launch_bounds__(512) void k_gemv_mfma_chunk(const uint8_t* __restri
   const uint32_t sx_base = (uint32_t)T * tile_bytes;           // fp32 [T][4 CG][16]
   const uint32_t dummy = sx_base + (uint32_t)T * (64u << log2cg) * 4u;
   const int npieces = T * (256 << log2cg);
+  // The workgroup size as the hardware reports it: written as 64 R S, the
+  // piece addresses of the staging loop below were re-derived with 32-bit
+  // multiplies per piece, and the 48-column verify pass took 8 % longer.
   const int nthreads = (int)blockDim.x;
   const rsrc_t xs = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
   float4_t acc[T];
@@ -766,21 +775,22 @@ template <int FMT, int P, bool SX>
 __global__ __launch_bounds__(512) void k_gemv_mfma_pers(const uint8_t* __restrict__ W,
                                                        const uint16_t* __restrict__ x,
                                                        float* __restrict__ y, int N, int K, int M,
-                                                       int log2mp, int tpw) {
+                                                       int log2mp, int tpw, int nw, int nwg) {
   extern __shared__ u32x4 xl4[];
-  const int lane = threadIdx.x & 63;
-  const int nw = (int)(blockDim.x >> 6);
+  const int lane = threadIdx.x & 63;   // nw: waves per workgroup, nwg: workgroups (arguments)
   const int n = lane & 15, g = lane >> 4;
   const int nblk = K / 32;
   const int ngroups = (nblk + 3) / 4;
   const int Mp = 1 << log2mp;
   const int64_t tiles = (N + 15) / 16;
-  const int64_t T = (int64_t)gridDim.x * nw;
+  const int64_t T = (int64_t)nwg * nw;
   const int64_t t0 = (int64_t)blockIdx.x * nw + wave_id();
   const uint32_t row_bytes = (uint32_t)nblk * Fmt<FMT>::BB;
   const uint32_t roff = (uint32_t)n * row_bytes;
   // this wave's sequence: tiles t0 + k T (k < tpw, tile < tiles), groups 0..ngroups-1 each
-  const int64_t mine = t0 < tiles ? min<int64_t>(tpw, (tiles - 1 - t0) / T + 1) : 0;
+  int64_t mine = 0;   // min(tpw, tiles of t0 + k T below `tiles`), tpw <= MFMA_PERS_TPW
+#pragma unroll
+  for (int k = 0; k < MFMA_PERS_TPW; ++k) mine += (k < tpw && t0 + (int64_t)k * T < tiles) ? 1 : 0;
   const int Q = (int)mine * ngroups;
   GroupRaw<FMT> wr[P];
   // issue pointer (tile index k, group) of the next group to load
@@ -794,7 +804,7 @@ __global__ __launch_bounds__(512) void k_gemv_mfma_pers(const uint8_t* __restric
     if (++ig == ngroups) { ig = 0; ++ik; }
   };
   uint8_t* xlb = reinterpret_cast<uint8_t*>(xl4);
-  stage_x_mfma<SX>(x, M, K, ngroups, log2mp, xlb, [&]() {
+  stage_x_mfma<SX>(x, M, K, ngroups, log2mp, xlb, 64 * nw, [&]() {
 #pragma unroll
     for (int p = 0; p < P; ++p) issue(wr[p], p < Q);
   });
@@ -1005,10 +1015,10 @@ int launch_mfma_lds_p(const GemvArgs& a, int m0, int mt, const MfmaLdsCfg& c) {
                xf ? 1 : 0, m0);
   if (xf)
     hipLaunchKernelGGL((k_gemv_mfma_lds<FMT, P, SX, true>), grid, block, c.lds, a.stream, a.W, a.x + (int64_t)m0 * a.K,
-                       a.y + (int64_t)m0 * a.N, (int)a.N, (int)a.K, mt, c.R, c.S, c.log2mp);
+                       a.y + (int64_t)m0 * a.N, (int)a.N, (int)a.K, mt, c.R, c.S, c.log2mp, 1);
   else
     hipLaunchKernelGGL((k_gemv_mfma_lds<FMT, P, SX, false>), grid, block, c.lds, a.stream, a.W, a.x + (int64_t)m0 * a.K,
-                       a.y + (int64_t)m0 * a.N, (int)a.N, (int)a.K, mt, c.R, c.S, c.log2mp);
+                       a.y + (int64_t)m0 * a.N, (int)a.N, (int)a.K, mt, c.R, c.S, c.log2mp, 1);
   return (int)hipGetLastError();
 }
 
@@ -1088,10 +1098,10 @@ int launch_mfma_split(const GemvArgs& a, int ns, const MfmaLdsCfg& c) {
   do {                                                                                                           \
     if (xf)                                                                                                      \
       hipLaunchKernelGGL((k_gemv_mfma_lds<FMT, PP, SXX, true>), grid, block, cc.lds, a.stream, a.W, a.x, b.y,   \
-                         (int)a.N, (int)a.K, (int)a.M, cc.R, cc.S, cc.log2mp);                                   \
+                         (int)a.N, (int)a.K, (int)a.M, cc.R, cc.S, cc.log2mp, ns);                               \
     else                                                                                                         \
       hipLaunchKernelGGL((k_gemv_mfma_lds<FMT, PP, SXX, false>), grid, block, cc.lds, a.stream, a.W, a.x, b.y,  \
-                         (int)a.N, (int)a.K, (int)a.M, cc.R, cc.S, cc.log2mp);                                   \
+                         (int)a.N, (int)a.K, (int)a.M, cc.R, cc.S, cc.log2mp, ns);                               \
   } while (0)
     switch (cc.P) {
       case 1: if (cc.sx) KQ_SPLIT_LAUNCH(1, true); else KQ_SPLIT_LAUNCH(1, false); break;
@@ -1242,7 +1252,7 @@ int launch_mfma_pers_p(const GemvArgs& a, int log2mp, size_t lds) {
   dispatch_log("k_gemv_mfma_pers", a.fmt, a.N, a.K, (int)a.M, grid.x, 1, 64 * nw, lds,
                "persistent P=%d tiles/wave=%d Mp=%d", P, (int)tpw, 1 << log2mp);
   hipLaunchKernelGGL((k_gemv_mfma_pers<FMT, P, SX>), grid, block, lds, a.stream, a.W, a.x, a.y, (int)a.N, (int)a.K,
-                     (int)a.M, log2mp, (int)tpw);
+                     (int)a.M, log2mp, (int)tpw, nw, (int)grid.x);
   return (int)hipGetLastError();
 }
 

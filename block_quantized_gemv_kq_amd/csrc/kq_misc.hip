@@ -34,6 +34,7 @@ __global__ __launch_bounds__(256) void k_weighted_slot_sum(const float* __restri
 }
 
 
+template <int NT>
 __device__ __forceinline__ Best block_best(Best b, Best* s_red) {
   for (int off = 32; off > 0; off >>= 1) {
     Best o{__shfl_xor(b.v, off, 64), __shfl_xor(b.i, off, 64)};
@@ -44,7 +45,7 @@ __device__ __forceinline__ Best block_best(Best b, Best* s_red) {
   __syncthreads();
   if (threadIdx.x == 0) {
     Best r = s_red[0];
-    for (int w = 1; w < (int)(blockDim.x >> 6); ++w) r = better(r, s_red[w]);
+    for (int w = 1; w < NT / 64; ++w) r = better(r, s_red[w]);
     s_red[0] = r;
   }
   __syncthreads();
@@ -70,24 +71,27 @@ __global__ __launch_bounds__(256) void k_argmax_partial(const float* __restrict_
     for (int t = 0; t < 8; ++t) b = better(b, Best{v[t], (int32_t)(i + t * 256)});
   }
   for (; i < c1; i += 256) b = better(b, Best{row[i], (int32_t)i});
-  b = block_best(b, s_red);
+  b = block_best<256>(b, s_red);
   if (threadIdx.x == 0) part[(int64_t)m * nparts + blockIdx.x] = b;
 }
 
-__global__ __launch_bounds__(1024) void k_argmax_final(const Best* __restrict__ part, int nparts,
-                                                       int32_t* __restrict__ out) {
+// NT threads (the workgroup size as a constant: reading it at run time would
+// put a scalar load of the dispatch arguments ahead of the first loads).
+template <int NT>
+__global__ __launch_bounds__(NT) void k_argmax_final(const Best* __restrict__ part, int nparts,
+                                                     int32_t* __restrict__ out) {
   __shared__ Best s_red[16];
   const int m = blockIdx.x;
   const Best* p = part + (int64_t)m * nparts;
   Best b{-__builtin_inff(), INT32_MAX};
-  const int nt = (int)blockDim.x;
+  constexpr int nt = NT;
   int i = threadIdx.x;
   for (; i + 3 * nt < nparts; i += 4 * nt) {   // four loads in flight per thread
     const Best a0 = p[i], a1 = p[i + nt], a2 = p[i + 2 * nt], a3 = p[i + 3 * nt];
     b = better(better(b, a0), better(better(a1, a2), a3));
   }
   for (; i < nparts; i += nt) b = better(b, p[i]);
-  b = block_best(b, s_red);
+  b = block_best<NT>(b, s_red);
   if (threadIdx.x == 0) out[m] = b.i == INT32_MAX ? 0 : b.i;
 }
 
@@ -107,8 +111,12 @@ int launch_weighted_slot_sum(const float* ys, const float* w, float* y, int64_t 
 int64_t argmax_partials(int64_t N) { return (N + ARGMAX_CHUNK - 1) / ARGMAX_CHUNK; }
 
 int launch_argmax_final(const void* part, int nparts, int M, int32_t* out, hipStream_t stream) {
-  hipLaunchKernelGGL(k_argmax_final, dim3((unsigned)M), dim3(nparts >= 4096 ? 1024 : 256), 0, stream,
-                     static_cast<const Best*>(part), nparts, out);
+  if (nparts >= 4096)
+    hipLaunchKernelGGL(k_argmax_final<1024>, dim3((unsigned)M), dim3(1024), 0, stream,
+                       static_cast<const Best*>(part), nparts, out);
+  else
+    hipLaunchKernelGGL(k_argmax_final<256>, dim3((unsigned)M), dim3(256), 0, stream,
+                       static_cast<const Best*>(part), nparts, out);
   return (int)hipGetLastError();
 }
 
@@ -120,7 +128,7 @@ int launch_argmax(const float* y, int64_t N, int M, int32_t* out, void* ws, hipS
                      part, nparts);
   int err = (int)hipGetLastError();
   if (err) return err;
-  hipLaunchKernelGGL(k_argmax_final, dim3((unsigned)M), dim3(256), 0, stream, part, nparts, out);
+  hipLaunchKernelGGL(k_argmax_final<256>, dim3((unsigned)M), dim3(256), 0, stream, part, nparts, out);
   return (int)hipGetLastError();
 }
 

@@ -27,7 +27,7 @@ __device__ int gather_expert_slots(const int32_t* __restrict__ ids, int p, int P
                                    int* s_cnt) {
   const int e = ids[p];
   int dup = 0;
-  for (int q = threadIdx.x; q < p; q += blockDim.x) dup |= (ids[q] == e);
+  for (int q = threadIdx.x; q < p; q += 256) dup |= (ids[q] == e);   // 256-thread workgroups
   dup = __syncthreads_or(dup);
   if (dup) return 0;
   if (threadIdx.x < 64) {
@@ -228,11 +228,11 @@ __global__ __launch_bounds__(256) void k_moe_lds(const uint8_t* __restrict__ W0,
   __shared__ int s_cnt;
   const int p = blockIdx.y;
   // 1. routing: ids into LDS, then the owner test and the gather from LDS
-  for (int q = threadIdx.x; q < P; q += blockDim.x) s_ids[q] = ids[q];
+  for (int q = threadIdx.x; q < P; q += 256) s_ids[q] = ids[q];
   __syncthreads();
   const int e = s_ids[p];
   int dup = 0;
-  for (int q = threadIdx.x; q < p; q += blockDim.x) dup |= (s_ids[q] == e);
+  for (int q = threadIdx.x; q < p; q += 256) dup |= (s_ids[q] == e);
   if (__syncthreads_or(dup)) return;
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
