@@ -658,52 +658,6 @@ __device__ __forceinline__ void consume_units(const Loaded<FMT, ITERS>& w, const
   }
 }
 
-// The same two steps on a flat register buffer (ITERS * UDW dwords), so one
-// buffer can serve whichever format a stage uses.
-template <int FMT, int ITERS>
-__device__ __forceinline__ void issue_units_raw(rsrc_t rs, uint32_t roff, int first, int G, int units,
-                                                uint32_t* raw) {
-  constexpr uint32_t UBYTES = Fmt<FMT>::BB * Fmt<FMT>::UB;
-#pragma unroll
-  for (int it = 0; it < ITERS; ++it) {
-    const int u = first + it * G;
-    const uint32_t off = u < units ? roff + (uint32_t)u * UBYTES : OOB;
-    load_unit<FMT>(rs, off, raw + it * Fmt<FMT>::UDW);
-  }
-}
-
-template <int FMT, int ITERS>
-__device__ __forceinline__ float consume_units_raw(const uint32_t* raw, const uint32_t* xl,
-                                                   const float* xs, int first, int G, int units) {
-  constexpr int UB = Fmt<FMT>::UB;
-  float acc = 0.0f;
-#pragma unroll
-  for (int it = 0; it < ITERS; ++it) {
-    const int u = first + it * G;
-    if (u < units) {
-      Unpacked<FMT> up;
-      unpack_unit_split<FMT>(raw + it * Fmt<FMT>::UDW, up);
-      const u32x4* xp = reinterpret_cast<const u32x4*>(xl + u * 16 * UB);
-      const float2* sp = reinterpret_cast<const float2*>(xs) + u * UB;
-      uint32_t X[16 * UB];
-#pragma unroll
-      for (int v = 0; v < 4 * UB; ++v) {
-        const u32x4 t = xp[v];
-        X[4 * v] = t.x;
-        X[4 * v + 1] = t.y;
-        X[4 * v + 2] = t.z;
-        X[4 * v + 3] = t.w;
-      }
-#pragma unroll
-      for (int b = 0; b < UB; ++b) {
-        const float2 sx = sp[b];
-        acc = block_dot_split<FMT>(up.A + 16 * b, X + 16 * b, sx.x, sx.y, up.scale[b], up.bias[b], acc);
-      }
-    }
-  }
-  return acc;
-}
-
 template <int MT>
 __device__ __forceinline__ void group_reduce(float (&acc)[MT], int G) {
 #pragma unroll
