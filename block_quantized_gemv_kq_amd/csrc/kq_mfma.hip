@@ -384,7 +384,7 @@ __device__ __forceinline__ int div_small(int a, int b) {
 // Column swizzle of the x slots of block b, lane group g.
 __device__ __forceinline__ int xsw(int b, int g, int Mp) { return (((b & 3) << 1) | (g >> 1)) & (Mp - 1); }
 
-template <int FMT, int P, bool SX, bool XF>
+template <int FMT, int P, bool SX, int XM>
 __global__ __launch_bounds__(1024) void k_gemv_mfma_lds(const uint8_t* __restrict__ W,
                                                        const uint16_t* __restrict__ x,
                                                        float* __restrict__ y, int N, int K, int M, int R,
@@ -451,18 +451,19 @@ __device__ __forceinline__ void stage_x_mfma(const uint16_t* __restrict__ x, int
   // Wave chunk q = wv + nwaves * c: 64 consecutive 16-byte pieces of one
   // column, column q & (Mp - 1), pieces 64 (q >> log2mp) + lane, so the lanes
   // of one load read 1 KB of contiguous memory. Chunks past the nq the
-  // staging needs are not issued at all (a branch uniform over the wave): a
-  // load that reads nothing still takes the CU's address unit as long as a
-  // real one, and every workgroup on the CU stages its own copy of x.
+  // staging needs, and chunks of the padding columns M..Mp - 1 (whose slots no
+  // operand read uses), are not issued at all (a branch uniform over the
+  // wave): a load that reads nothing still takes the CU's address unit as
+  // long as a real one, and every workgroup on the CU stages its own copy of x.
   const int nq = Mp * ((kq8p + 63) / 64);
   u32x4 xr[XST_MAX];
 #pragma unroll
   for (int c = 0; c < XST_MAX; ++c) {
     const int q = wv + nwaves * c;
     const int col = q & (Mp - 1), k8 = 64 * (q >> log2mp) + lane;
-    const bool ok = col < M && k8 < k8_lim;
-    xr[c] = q < nq ? ld128(xs, ok ? ((uint32_t)col * (uint32_t)kq8 + (uint32_t)(k8_0 + k8)) * 16u : OOB)
-                   : u32x4{0u, 0u, 0u, 0u};
+    const bool ok = k8 < k8_lim;
+    xr[c] = q < nq && col < M ? ld128(xs, ok ? ((uint32_t)col * (uint32_t)kq8 + (uint32_t)(k8_0 + k8)) * 16u : OOB)
+                              : u32x4{0u, 0u, 0u, 0u};
   }
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (!XF) {
@@ -514,6 +515,79 @@ __device__ __forceinline__ void stage_x_mfma(const uint16_t* __restrict__ x, int
   __syncthreads();
 }
 
+// x by buffer-to-LDS DMA for the teams kernel without block sums (more than
+// four columns), column-major: piece p of column c (x[c][8 (k8_0 + p) .. +7],
+// p < P = 16 ngroups) at slot c P + (p ^ (c & 15)). One load instruction of a
+// wave fills 64 consecutive slots, so its lanes read one column's 1 KB with
+// the pieces permuted inside aligned runs of 16 (every quad of lanes still
+// reads one 64-byte run); pieces past the column's end are written as zeros.
+// Nothing passes through registers: the caller's weight loads are issued
+// right behind x, and the barrier after them waits for both. The swizzle puts
+// the pieces the 16 lanes of an operand read (one column each) in distinct
+// bank groups.
+template <typename F>
+__device__ __forceinline__ void stage_x_cm(const uint16_t* __restrict__ x, int M, int K, int ngroups, uint8_t* xlb,
+                                           int nthreads, F issue_more, int k8_0) {
+  const int P = 16 * ngroups, nslot = M * P, kq8 = K / 8;
+  const int lane = (int)threadIdx.x & 63, nwaves = nthreads >> 6;
+  const rsrc_t xs = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
+  for (int base = 64 * wave_id(); base < nslot; base += 64 * nwaves) {   // uniform over the wave
+    const int s = base + lane;
+    const int c = div_small(s, P);   // s < 2^16: the slots fit in LDS
+    const int p = (s - c * P) ^ (c & 15);
+    if (s < nslot) {
+      if (k8_0 + p < kq8)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xs, (lds_void_t*)(xlb + 16 * base), 16,
+                                                 ((uint32_t)c * (uint32_t)kq8 + (uint32_t)(k8_0 + p)) * 16u, 0, 0, 0);
+      else
+        *reinterpret_cast<u32x4*>(xlb + 16 * s) = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  issue_more();
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();
+}
+
+// mfma_group on x staged by stage_x_cm (no block sums): xc is the first slot
+// of the lane's column, csw its swizzle; the A operand of block j is read as
+// two 8-byte halves, x[c][32 b + 4 g .. +3] and x[c][32 b + 16 + 4 g .. +3].
+template <int FMT>
+__device__ __forceinline__ void mfma_group_cm(const GroupRaw<FMT>& cur, uint32_t roff, int gi, int gl, int g,
+                                              const uint8_t* xc, int csw, float4_t& acc) {
+  const OwnBlock own = own_block<FMT>(cur, roff, 4 * gi + g);
+  GroupOps o;
+  exchange<FMT>(own, o);
+  const uint32_t half = 8u * (uint32_t)(g & 1);
+  half8_t A[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int p0 = 4 * (4 * gl + j) + (g >> 1);
+    const u32x2 lo = *reinterpret_cast<const u32x2*>(xc + 16u * (uint32_t)(p0 ^ csw) + half);
+    const u32x2 hi = *reinterpret_cast<const u32x2*>(xc + 16u * (uint32_t)((p0 + 2) ^ csw) + half);
+    A[j] = as_half8(lo.x, lo.y, hi.x, hi.y);
+  }
+  float4_t D[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    D[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[j], b_operand<FMT>(o, j, g), float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float sc = h2f(o.hs[j]);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) acc[v] = __builtin_fmaf(sc, D[j][v], acc[v]);
+  }
+  const half8_t ones = as_half8(ONES, ONES, ONES, ONES);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float4_t Dx = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[j], ones, float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+    const float sc = h2f(o.hs[j]);
+    const float c = fix_const<FMT>(o.hs[j], sc);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) acc[v] = __builtin_fmaf(c, Dx[v], acc[v]);
+  }
+}
+
 // Many tiles (large N): persistent waves. x is staged once per workgroup;
 // then every wave on its own streams whole 16-row tiles (no K split, so no
 // reduction), tiles t0, t0 + T, ... (T = waves in the grid, `tpw` tiles per
@@ -525,11 +599,12 @@ __device__ __forceinline__ void stage_x_mfma(const uint16_t* __restrict__ x, int
 // groups [s P, (s + 1) P) of tile r, all loaded before any arithmetic, and the
 // S partial results of a tile are summed in LDS in a fixed order. SX: block
 // sums in LDS (else, when x alone just fits, from an MFMA per block).
-template <int FMT, int P, bool SX, bool XF>
+template <int FMT, int P, bool SX, int XM>
 __global__ __launch_bounds__(1024) void k_gemv_mfma_lds(const uint8_t* __restrict__ W,
                                                        const uint16_t* __restrict__ x,
                                                        float* __restrict__ y, int N, int K, int M, int R,
                                                        int S, int log2mp, int nsplit) {
+  static_assert(XM != 2 || !SX, "x by DMA has no block sums");
   extern __shared__ u32x4 xl4[];
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
@@ -560,16 +635,23 @@ __global__ __launch_bounds__(1024) void k_gemv_mfma_lds(const uint8_t* __restric
       load_group<FMT>(rs, roff, 4 * gi + g, gi < gs1 && row_ok && 4 * gi + g < nblk, wr[p]);
     }
   };
-  stage_x_mfma<SX, decltype(issue), XF>(x, M, K, ngroups, log2mp, xlb, 64 * R * S, issue, 16 * gs0);
+  if constexpr (XM == 2)
+    stage_x_cm(x, M, K, ngroups, xlb, 64 * R * S, issue, 16 * gs0);
+  else
+    stage_x_mfma<SX, decltype(issue), XM == 1>(x, M, K, ngroups, log2mp, xlb, 64 * R * S, issue, 16 * gs0);
   const int ncol = n < M ? n : M - 1;
   const u32x4* xa = xl4 + g * Mp;
   const float* sxa = reinterpret_cast<const float*>(xlb + (uint32_t)(16 * ngroups) * (uint32_t)Mp * 16u) + g * Mp + ncol;
+  const uint8_t* xc = xlb + (uint32_t)(16 * ngroups) * (uint32_t)ncol * 16u;
   float4_t acc = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int p = 0; p < P; ++p) {
     const int gi = gb + p;
     if (gi >= gs1) break;   // uniform
-    mfma_group<FMT, SX>(wr[p], roff, gi, gi - gs0, g, ncol, xa, sxa, Mp, acc);
+    if constexpr (XM == 2)
+      mfma_group_cm<FMT>(wr[p], roff, gi, gi - gs0, g, xc, ncol & 15, acc);
+    else
+      mfma_group<FMT, SX>(wr[p], roff, gi, gi - gs0, g, ncol, xa, sxa, Mp, acc);
   }
   // fixed-order sum over the S waves of each tile (the x area is reused)
   __syncthreads();
@@ -996,6 +1078,21 @@ MfmaLdsCfg mfma_lds_cfg(int64_t N, int64_t K, int M, int maxp, bool no_sums) {
   return c;
 }
 
+// Teams kernel without block sums (5..16 columns): x staged by DMA in
+// column-major order (stage_x_cm) or through registers in operand order; the
+// same bits either way. Measured per launch on the decode shapes (12 layers,
+// cold, DMA against registers): q|k|v (384 workgroups) -0.25..-0.39 us at 6,
+// 8, 12, 16 columns; down split along K (640) -0.12..-0.45 us; gate|up (1216
+// tiles) -0.43 us at 6, even at 8, +0.23..+0.35 at 12 and 16; o (160
+// workgroups, fewer than the CUs) +0.16..+0.34 us. So DMA on grids of more
+// than 256 workgroups, and from 1024 tiles on only up to 8 columns. The
+// mfma_xdma override (0 / 1) forces one way.
+bool mfma_x_dma(int M, int64_t workgroups, int64_t tiles) {
+  const int v = tune(TUNE_MFMA_XDMA);
+  if (v != TUNE_UNSET) return v == 1;
+  return workgroups > 256 && (tiles < 1024 || M <= 8);
+}
+
 template <int FMT, int P, bool SX>
 int launch_mfma_lds_p(const GemvArgs& a, int m0, int mt, const MfmaLdsCfg& c) {
   const int64_t tiles = (a.N + 15) / 16;
@@ -1011,14 +1108,23 @@ int launch_mfma_lds_p(const GemvArgs& a, int m0, int mt, const MfmaLdsCfg& c) {
   const int exf = tune(TUNE_MFMA_XF);
   const bool xf = exf != TUNE_UNSET ? exf != 0 : !(c.log2mp == 3 && tiles >= 1024);
   dispatch_log("k_gemv_mfma_lds", a.fmt, a.N, a.K, mt, grid.x, 1, block.x, c.lds,
-               "teams R=%d S=%d P=%d Mp=%d sums=%d x_first=%d m0=%d", c.R, c.S, P, 1 << c.log2mp, SX ? 1 : 0,
-               xf ? 1 : 0, m0);
+               "teams R=%d S=%d P=%d Mp=%d sums=%d x_first=%d x_dma=%d m0=%d", c.R, c.S, P, 1 << c.log2mp,
+               SX ? 1 : 0, xf ? 1 : 0, !SX && mfma_x_dma(mt, grid.x, tiles) ? 1 : 0, m0);
+  const uint16_t* xm = a.x + (int64_t)m0 * a.K;
+  float* ym = a.y + (int64_t)m0 * a.N;
+  if constexpr (!SX) {
+    if (mfma_x_dma(mt, grid.x, tiles)) {
+      hipLaunchKernelGGL((k_gemv_mfma_lds<FMT, P, false, 2>), grid, block, c.lds, a.stream, a.W, xm, ym, (int)a.N,
+                         (int)a.K, mt, c.R, c.S, c.log2mp, 1);
+      return (int)hipGetLastError();
+    }
+  }
   if (xf)
-    hipLaunchKernelGGL((k_gemv_mfma_lds<FMT, P, SX, true>), grid, block, c.lds, a.stream, a.W, a.x + (int64_t)m0 * a.K,
-                       a.y + (int64_t)m0 * a.N, (int)a.N, (int)a.K, mt, c.R, c.S, c.log2mp, 1);
+    hipLaunchKernelGGL((k_gemv_mfma_lds<FMT, P, SX, 1>), grid, block, c.lds, a.stream, a.W, xm, ym, (int)a.N, (int)a.K,
+                       mt, c.R, c.S, c.log2mp, 1);
   else
-    hipLaunchKernelGGL((k_gemv_mfma_lds<FMT, P, SX, false>), grid, block, c.lds, a.stream, a.W, a.x + (int64_t)m0 * a.K,
-                       a.y + (int64_t)m0 * a.N, (int)a.N, (int)a.K, mt, c.R, c.S, c.log2mp, 1);
+    hipLaunchKernelGGL((k_gemv_mfma_lds<FMT, P, SX, 0>), grid, block, c.lds, a.stream, a.W, xm, ym, (int)a.N, (int)a.K,
+                       mt, c.R, c.S, c.log2mp, 1);
   return (int)hipGetLastError();
 }
 
@@ -1091,16 +1197,20 @@ int launch_mfma_split(const GemvArgs& a, int ns, const MfmaLdsCfg& c) {
     const int exf = tune(TUNE_MFMA_XF);
     const bool xf = exf != TUNE_UNSET ? exf != 0 : true;
     const dim3 grid((unsigned)((tiles + cc.R - 1) / cc.R), (unsigned)ns), block((unsigned)(64 * cc.R * cc.S));
+    const bool xdma = !cc.sx && mfma_x_dma((int)a.M, (int64_t)grid.x * ns, tiles);
     dispatch_log("k_gemv_mfma_lds", a.fmt, a.N, a.K, (int)a.M, grid.x, grid.y, block.x, cc.lds,
-                 "teams K-split=%d R=%d S=%d P=%d Mp=%d sums=%d x_first=%d", ns, cc.R, cc.S, cc.P, 1 << cc.log2mp,
-                 cc.sx ? 1 : 0, xf ? 1 : 0);
+                 "teams K-split=%d R=%d S=%d P=%d Mp=%d sums=%d x_first=%d x_dma=%d", ns, cc.R, cc.S, cc.P,
+                 1 << cc.log2mp, cc.sx ? 1 : 0, xf ? 1 : 0, xdma ? 1 : 0);
 #define KQ_SPLIT_LAUNCH(PP, SXX)                                                                                  \
   do {                                                                                                           \
-    if (xf)                                                                                                      \
-      hipLaunchKernelGGL((k_gemv_mfma_lds<FMT, PP, SXX, true>), grid, block, cc.lds, a.stream, a.W, a.x, b.y,   \
+    if (!(SXX) && xdma)                                                                                          \
+      hipLaunchKernelGGL((k_gemv_mfma_lds<FMT, PP, false, 2>), grid, block, cc.lds, a.stream, a.W, a.x, b.y,    \
+                         (int)a.N, (int)a.K, (int)a.M, cc.R, cc.S, cc.log2mp, ns);                               \
+    else if (xf)                                                                                                 \
+      hipLaunchKernelGGL((k_gemv_mfma_lds<FMT, PP, SXX, 1>), grid, block, cc.lds, a.stream, a.W, a.x, b.y,      \
                          (int)a.N, (int)a.K, (int)a.M, cc.R, cc.S, cc.log2mp, ns);                               \
     else                                                                                                         \
-      hipLaunchKernelGGL((k_gemv_mfma_lds<FMT, PP, SXX, false>), grid, block, cc.lds, a.stream, a.W, a.x, b.y,  \
+      hipLaunchKernelGGL((k_gemv_mfma_lds<FMT, PP, SXX, 0>), grid, block, cc.lds, a.stream, a.W, a.x, b.y,      \
                          (int)a.N, (int)a.K, (int)a.M, cc.R, cc.S, cc.log2mp, ns);                               \
   } while (0)
     switch (cc.P) {

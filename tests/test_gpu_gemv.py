@@ -179,8 +179,8 @@ def test_zero_and_constant_weights():
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("variant", ("pers", "pers_tpw3", "teams", "teams_sx", "teams_x0", "teams_x1", "chunk",
-                                     "chunk_whole", "direct"))
+@pytest.mark.parametrize("variant", ("pers", "pers_tpw3", "teams", "teams_sx", "teams_x0", "teams_x1", "teams_xdma",
+                                     "chunk", "chunk_whole", "direct"))
 @pytest.mark.parametrize("N,K,M", [(1000, 2560, 8), (37, 96, 5), (300, 4128, 16), (16, 32, 2), (529, 640, 13),
                                    (300, 4128, 40), (77, 9728, 33)])
 def test_mfma_variants_parity(fmt, variant, N, K, M):
@@ -193,19 +193,40 @@ def test_mfma_variants_parity(fmt, variant, N, K, M):
     kernel runs one workgroup per 16 columns (chunk), or one for all columns
     of a tile (chunk_whole)."""
     packed, fields, x = _case(fmt, N, K, M, 9)
-    env = {"mfma_variant": {"pers_tpw3": "pers", "teams_x0": "teams", "teams_x1": "teams"}.get(variant, variant)}
+    env = {"mfma_variant": {"pers_tpw3": "pers", "teams_x0": "teams", "teams_x1": "teams",
+                            "teams_xdma": "teams"}.get(variant, variant)}
     if variant == "pers_tpw3":
         env["mfma_pers_tpw"] = "3"
     if variant == "teams_x0":          # weights issued before x is written (the other load order)
         env["mfma_xf"] = "0"
     if variant == "teams_x1":          # x written before the weights are issued, at any grid size
         env["mfma_xf"] = "1"
+    if variant == "teams_xdma":        # x by DMA into column-major LDS (without block sums), or through registers
+        env["mfma_xdma"] = "1"
     with U.tuning(env):
         y = U.gemv_gpu(fmt, U.to_dev(packed), x, N, K, path="mfma")
         y2 = U.gemv_gpu(fmt, U.to_dev(packed), x, N, K, path="mfma")
     yr, ad = R.gemv(fmt, fields, x)
     U.assert_parity(y, yr, ad, f"{fmt} {variant} N={N} K={K} M={M}")
     assert np.array_equal(y, y2), "not deterministic run to run"
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("N,K,M", [(1000, 2560, 8), (37, 96, 5), (300, 4128, 16), (529, 640, 13), (2560, 4096, 8),
+                                   (6144, 2560, 7), (160, 9728, 12)])
+def test_teams_x_dma_same_bits(fmt, N, K, M):
+    """The teams kernel without block sums gives the same bits whether x is
+    staged by DMA in column-major order or through registers in operand order
+    (the same operands, products and sums in the same order)."""
+    packed, fields, x = _case(fmt, N, K, M, 19)
+    Wd = U.to_dev(packed)
+    with U.tuning({"mfma_variant": "teams", "mfma_xdma": "1"}):
+        y1 = U.gemv_gpu(fmt, Wd, x, N, K, path="mfma")
+    with U.tuning({"mfma_variant": "teams", "mfma_xdma": "0"}):
+        y0 = U.gemv_gpu(fmt, Wd, x, N, K, path="mfma")
+    yr, ad = R.gemv(fmt, fields, x)
+    U.assert_parity(y1, yr, ad, f"{fmt} teams x by DMA N={N} K={K} M={M}")
+    assert np.array_equal(y1.view(np.uint32), y0.view(np.uint32))
 
 
 @pytest.mark.parametrize("fmt", FMTS)

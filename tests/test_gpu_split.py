@@ -39,28 +39,33 @@ def _gemv_ws(fmt, Wd, x, N, K):
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("N,K", [(2560, 9728), (77, 9728), (300, 6176), (33, 8192)])
 @pytest.mark.parametrize("M", (4, 8, 13, 16))
-def test_split_parity(fmt, N, K, M):
+@pytest.mark.parametrize("xdma", ("0", "1"))
+def test_split_parity(fmt, N, K, M, xdma):
+    """xdma: x of each split by DMA into column-major LDS, or through registers."""
     packed, fields, x = _case(fmt, N, K, M, 1)
     Wd = U.to_dev(packed)
-    y, need = _gemv_ws(fmt, Wd, x, N, K)
+    with U.tuning({"mfma_xdma": xdma}):
+        y, need = _gemv_ws(fmt, Wd, x, N, K)
+        y2, _ = _gemv_ws(fmt, Wd, x, N, K)
     assert need > 0, "this shape is expected to split"
     yr, ad = R.gemv(fmt, fields, x)
-    U.assert_parity(y, yr, ad, f"{fmt} split N={N} K={K} M={M}")
-    y2, _ = _gemv_ws(fmt, Wd, x, N, K)
+    U.assert_parity(y, yr, ad, f"{fmt} split N={N} K={K} M={M} xdma={xdma}")
     assert np.array_equal(y.view(np.uint32), y2.view(np.uint32)), "not deterministic run to run"
 
 
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("splits", ("2", "3", "5", "8"))
 @pytest.mark.parametrize("N,K,M", [(40, 2048, 8), (130, 4160, 5), (16, 1024, 16)])
-def test_forced_split_counts(fmt, splits, N, K, M):
+@pytest.mark.parametrize("xdma", ("0", "1"))
+def test_forced_split_counts(fmt, splits, N, K, M, xdma):
     """Any split count (uneven group ranges, one or two groups per split,
-    ragged rows, a partial last group) meets the bar; where one split's x
-    would need more staging threads than its workgroup has, the call does not
-    split (workspace 0) and is kq_gemv."""
+    ragged rows, a partial last group) meets the bar, with x of each split
+    staged through registers or by DMA; where one split's x would need more
+    staging threads than its workgroup has, the call does not split
+    (workspace 0) and is kq_gemv."""
     packed, fields, x = _case(fmt, N, K, M, 2)
     Wd = U.to_dev(packed)
-    with U.tuning({"mfma_split": splits}):
+    with U.tuning({"mfma_split": splits, "mfma_xdma": xdma}):
         y, need = _gemv_ws(fmt, Wd, x, N, K)
     assert need in (0, int(splits) * M * N * 4)
     if (N, K, M, splits) != (16, 1024, 16, "8"):
