@@ -44,9 +44,9 @@ GROUP_NAMES = ("qkv", "o", "gate_up", "down")
 # taken with: a changed file (sha256 prefix below, paths under the package)
 # reports traffic as unknown.
 MEASURED_TRAFFIC = {
-    "sources": {"csrc/kq_gemv.hip": "45d74ba3c42c85a9", "csrc/kq_dev.h": "a3211cff506226da",
+    "sources": {"csrc/kq_gemv.hip": "45d74ba3c42c85a9", "csrc/kq_dev.h": "8e989717f32c9c9d",
                 "build.py": "f8d9dfd3b4ceed6e"},
-    "bytes": {"qkv": 9962584, "o": 6669336, "gate_up": 31330218, "down": 15823509, "lm_head": 414290275},
+    "bytes": {"qkv": 9962456, "o": 6669336, "gate_up": 31331274, "down": 15822870, "lm_head": 414289780},
 }
 
 
@@ -55,8 +55,8 @@ MFMA_PEAK_F16_TFLOPS = 2500.0   # MI355X dense fp16 matrix-core peak, published
 # MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE * SIMDs), percent) per
 # launch group of the verify pass, from a counter run over `bench.py
 # --kernels-only M`; valid only for the kernel sources it was taken with.
-MEASURED_MFMA = {"sources": {"csrc/kq_mfma.hip": "d68512fb3677e0fd", "csrc/kq_dev.h": "a3211cff506226da", "build.py": "f8d9dfd3b4ceed6e"},
-                 "verify_m8": {"qkv": 2.61, "o": 1.84, "gate_up": 6.57, "down": 3.99, "lm_head": 7.86}}
+MEASURED_MFMA = {"sources": {"csrc/kq_mfma.hip": "f599f4ce2aa7f3c7", "csrc/kq_dev.h": "8e989717f32c9c9d", "build.py": "f8d9dfd3b4ceed6e"},
+                 "verify_m8": {"qkv": 2.71, "o": 1.85, "gate_up": 6.42, "down": 4.21, "lm_head": 7.83}}
 
 
 def measured_mfma(run, group):
