@@ -46,7 +46,7 @@ GROUP_NAMES = ("qkv", "o", "gate_up", "down")
 MEASURED_TRAFFIC = {
     "sources": {"csrc/kq_gemv.hip": "45d74ba3c42c85a9", "csrc/kq_dev.h": "8e989717f32c9c9d",
                 "build.py": "f8d9dfd3b4ceed6e"},
-    "bytes": {"qkv": 9962456, "o": 6669336, "gate_up": 31331274, "down": 15822870, "lm_head": 414289780},
+    "bytes": {"qkv": 9963512, "o": 6669080, "gate_up": 31330954, "down": 15823413, "lm_head": 414289316},
 }
 
 
@@ -55,8 +55,8 @@ MFMA_PEAK_F16_TFLOPS = 2500.0   # MI355X dense fp16 matrix-core peak, published
 # MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE * SIMDs), percent) per
 # launch group of the verify pass, from a counter run over `bench.py
 # --kernels-only M`; valid only for the kernel sources it was taken with.
-MEASURED_MFMA = {"sources": {"csrc/kq_mfma.hip": "f599f4ce2aa7f3c7", "csrc/kq_dev.h": "8e989717f32c9c9d", "build.py": "f8d9dfd3b4ceed6e"},
-                 "verify_m8": {"qkv": 2.71, "o": 1.85, "gate_up": 6.42, "down": 4.21, "lm_head": 7.83}}
+MEASURED_MFMA = {"sources": {"csrc/kq_mfma.hip": "cc9637ac7f2fd732", "csrc/kq_dev.h": "8e989717f32c9c9d", "build.py": "f8d9dfd3b4ceed6e"},
+                 "verify_m8": {"qkv": 2.72, "o": 1.88, "gate_up": 6.46, "down": 4.12, "lm_head": 7.75}}
 
 
 def measured_mfma(run, group):

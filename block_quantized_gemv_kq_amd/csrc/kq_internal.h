@@ -33,7 +33,7 @@ enum TuneKey {
   TUNE_MFMA_SPLIT,       // K splits of the teams kernel when a workspace is given (1: none)
   TUNE_SL_G,             // lanes per row of the Shortlist bound kernel
   TUNE_LOG,              // 1: one line per kernel launch on stderr (the dispatch log)
-  TUNE_MFMA_XDMA,        // teams kernel without block sums: 1 x by DMA, column-major; 0 through registers
+  TUNE_MFMA_XDMA,        // teams kernel: 1 x by DMA, column-major; 0 through registers
   TUNE_COUNT
 };
 enum MfmaVariant { MV_PERS = 1, MV_TEAMS, MV_TEAMS_SX, MV_CHUNK, MV_CHUNK_WHOLE, MV_CHUNK_SPLIT, MV_DIRECT };

@@ -515,8 +515,7 @@ __device__ __forceinline__ void stage_x_mfma(const uint16_t* __restrict__ x, int
   __syncthreads();
 }
 
-// x by buffer-to-LDS DMA for the teams kernel without block sums (more than
-// four columns), column-major: piece p of column c (x[c][8 (k8_0 + p) .. +7],
+// x by buffer-to-LDS DMA for the teams kernel, column-major: piece p of column c (x[c][8 (k8_0 + p) .. +7],
 // p < P = 16 ngroups) at slot c P + (p ^ (c & 15)). One load instruction of a
 // wave fills 64 consecutive slots, so its lanes read one column's 1 KB with
 // the pieces permuted inside aligned runs of 16 (every quad of lanes still
@@ -525,9 +524,9 @@ __device__ __forceinline__ void stage_x_mfma(const uint16_t* __restrict__ x, int
 // right behind x, and the barrier after them waits for both. The swizzle puts
 // the pieces the 16 lanes of an operand read (one column each) in distinct
 // bank groups.
-template <typename F>
-__device__ __forceinline__ void stage_x_cm(const uint16_t* __restrict__ x, int M, int K, int ngroups, uint8_t* xlb,
-                                           int nthreads, F issue_more, int k8_0) {
+template <bool SX, typename F>
+__device__ __forceinline__ void stage_x_cm(const uint16_t* __restrict__ x, int M, int K, int ngroups, int log2mp,
+                                           uint8_t* xlb, int nthreads, F issue_more, int k8_0) {
   const int P = 16 * ngroups, nslot = M * P, kq8 = K / 8;
   const int lane = (int)threadIdx.x & 63, nwaves = nthreads >> 6;
   const rsrc_t xs = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
@@ -547,15 +546,46 @@ __device__ __forceinline__ void stage_x_cm(const uint16_t* __restrict__ x, int M
   issue_more();
   __builtin_amdgcn_sched_barrier(0);
   __syncthreads();
+  if constexpr (!SX) return;
+  // block sums sx[b][c] (fp32, at the offset and in the order stage_x_mfma
+  // leaves them), for the real columns: no operand read uses the others
+  const int Mp = 1 << log2mp;
+  float* sx = reinterpret_cast<float*>(xlb + (uint32_t)P * (uint32_t)Mp * 16u);
+  const int ntask = 4 * ngroups * Mp;
+  for (int t = (int)threadIdx.x; t < ntask; t += nthreads) {
+    const int bb = t >> log2mp, col = t & (Mp - 1);
+    if (col >= M) continue;
+    // the elements in the order of the operand-order sums: lane group gg's
+    // x[32 bb + 4 gg .. +3], then x[32 bb + 16 + 4 gg .. +3]
+    const uint8_t* xc = xlb + (uint32_t)(col * P) * 16u;
+    float v = 0.0f;
+#pragma unroll
+    for (int gg = 0; gg < 4; ++gg) {
+      const uint32_t half = 8u * (uint32_t)(gg & 1);
+      const int p0 = 4 * bb + (gg >> 1);
+      const u32x2 lo = *reinterpret_cast<const u32x2*>(xc + 16u * (uint32_t)(p0 ^ (col & 15)) + half);
+      const u32x2 hi = *reinterpret_cast<const u32x2*>(xc + 16u * (uint32_t)((p0 + 2) ^ (col & 15)) + half);
+      v = dot2(lo.x, ONES, v);
+      v = dot2(lo.y, ONES, v);
+      v = dot2(hi.x, ONES, v);
+      v = dot2(hi.y, ONES, v);
+    }
+    sx[t] = v;
+  }
+  __syncthreads();
 }
 
-// mfma_group on x staged by stage_x_cm (no block sums): xc is the first slot
+// mfma_group on x staged by stage_x_cm: xc is the first slot
 // of the lane's column, csw its swizzle; the A operand of block j is read as
 // two 8-byte halves, x[c][32 b + 4 g .. +3] and x[c][32 b + 16 + 4 g .. +3].
-template <int FMT>
+template <int FMT, bool SX>
 __device__ __forceinline__ void mfma_group_cm(const GroupRaw<FMT>& cur, uint32_t roff, int gi, int gl, int g,
-                                              const uint8_t* xc, int csw, float4_t& acc) {
+                                              const uint8_t* xc, int csw, const float* sxa, int Mp, float4_t& acc) {
   const OwnBlock own = own_block<FMT>(cur, roff, 4 * gi + g);
+  if constexpr (SX) {
+    const float so = h2f(own.hdr);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sxa[4 * gl * Mp], fix_const<FMT>(own.hdr, so), acc, 0, 0, 0);
+  }
   GroupOps o;
   exchange<FMT>(own, o);
   const uint32_t half = 8u * (uint32_t)(g & 1);
@@ -577,6 +607,7 @@ __device__ __forceinline__ void mfma_group_cm(const GroupRaw<FMT>& cur, uint32_t
 #pragma unroll
     for (int v = 0; v < 4; ++v) acc[v] = __builtin_fmaf(sc, D[j][v], acc[v]);
   }
+  if constexpr (SX) return;
   const half8_t ones = as_half8(ONES, ONES, ONES, ONES);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -604,7 +635,6 @@ __global__ __launch_bounds__(1024) void k_gemv_mfma_lds(const uint8_t* __restric
                                                        const uint16_t* __restrict__ x,
                                                        float* __restrict__ y, int N, int K, int M, int R,
                                                        int S, int log2mp, int nsplit) {
-  static_assert(XM != 2 || !SX, "x by DMA has no block sums");
   extern __shared__ u32x4 xl4[];
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
@@ -636,7 +666,7 @@ __global__ __launch_bounds__(1024) void k_gemv_mfma_lds(const uint8_t* __restric
     }
   };
   if constexpr (XM == 2)
-    stage_x_cm(x, M, K, ngroups, xlb, 64 * R * S, issue, 16 * gs0);
+    stage_x_cm<SX>(x, M, K, ngroups, log2mp, xlb, 64 * R * S, issue, 16 * gs0);
   else
     stage_x_mfma<SX, decltype(issue), XM == 1>(x, M, K, ngroups, log2mp, xlb, 64 * R * S, issue, 16 * gs0);
   const int ncol = n < M ? n : M - 1;
@@ -649,7 +679,7 @@ __global__ __launch_bounds__(1024) void k_gemv_mfma_lds(const uint8_t* __restric
     const int gi = gb + p;
     if (gi >= gs1) break;   // uniform
     if constexpr (XM == 2)
-      mfma_group_cm<FMT>(wr[p], roff, gi, gi - gs0, g, xc, ncol & 15, acc);
+      mfma_group_cm<FMT, SX>(wr[p], roff, gi, gi - gs0, g, xc, ncol & 15, sxa, Mp, acc);
     else
       mfma_group<FMT, SX>(wr[p], roff, gi, gi - gs0, g, ncol, xa, sxa, Mp, acc);
   }
@@ -1078,15 +1108,14 @@ MfmaLdsCfg mfma_lds_cfg(int64_t N, int64_t K, int M, int maxp, bool no_sums) {
   return c;
 }
 
-// Teams kernel without block sums (5..16 columns): x staged by DMA in
-// column-major order (stage_x_cm) or through registers in operand order; the
-// same bits either way. Measured per launch on the decode shapes (12 layers,
-// cold, DMA against registers): q|k|v (384 workgroups) -0.25..-0.39 us at 6,
-// 8, 12, 16 columns; down split along K (640) -0.12..-0.45 us; gate|up (1216
-// tiles) -0.43 us at 6, even at 8, +0.23..+0.35 at 12 and 16; o (160
-// workgroups, fewer than the CUs) +0.16..+0.34 us. So DMA on grids of more
-// than 256 workgroups, and from 1024 tiles on only up to 8 columns. The
-// mfma_xdma override (0 / 1) forces one way.
+// Teams kernel: x staged by DMA in column-major order (stage_x_cm) or through
+// registers in operand order; the same bits either way. Measured per launch
+// on the decode shapes (12 layers, cold, DMA against registers): q|k|v (384
+// workgroups) -0.25..-0.41 us at 4, 6, 8, 12, 16 columns; down split along K
+// (640) -0.09..-0.45 us; gate|up (1216 tiles) -0.56 us at 4, -0.43 at 6, even
+// at 8, +0.23..+0.35 at 12 and 16; o (160 workgroups, fewer than the CUs)
+// +0.16..+0.34 us. So DMA on grids of more than 256 workgroups, and from 1024
+// tiles on only up to 8 columns. The mfma_xdma override (0 / 1) forces one way.
 bool mfma_x_dma(int M, int64_t workgroups, int64_t tiles) {
   const int v = tune(TUNE_MFMA_XDMA);
   if (v != TUNE_UNSET) return v == 1;
@@ -1109,15 +1138,13 @@ int launch_mfma_lds_p(const GemvArgs& a, int m0, int mt, const MfmaLdsCfg& c) {
   const bool xf = exf != TUNE_UNSET ? exf != 0 : !(c.log2mp == 3 && tiles >= 1024);
   dispatch_log("k_gemv_mfma_lds", a.fmt, a.N, a.K, mt, grid.x, 1, block.x, c.lds,
                "teams R=%d S=%d P=%d Mp=%d sums=%d x_first=%d x_dma=%d m0=%d", c.R, c.S, P, 1 << c.log2mp,
-               SX ? 1 : 0, xf ? 1 : 0, !SX && mfma_x_dma(mt, grid.x, tiles) ? 1 : 0, m0);
+               SX ? 1 : 0, xf ? 1 : 0, mfma_x_dma(mt, grid.x, tiles) ? 1 : 0, m0);
   const uint16_t* xm = a.x + (int64_t)m0 * a.K;
   float* ym = a.y + (int64_t)m0 * a.N;
-  if constexpr (!SX) {
-    if (mfma_x_dma(mt, grid.x, tiles)) {
-      hipLaunchKernelGGL((k_gemv_mfma_lds<FMT, P, false, 2>), grid, block, c.lds, a.stream, a.W, xm, ym, (int)a.N,
-                         (int)a.K, mt, c.R, c.S, c.log2mp, 1);
-      return (int)hipGetLastError();
-    }
+  if (mfma_x_dma(mt, grid.x, tiles)) {
+    hipLaunchKernelGGL((k_gemv_mfma_lds<FMT, P, SX, 2>), grid, block, c.lds, a.stream, a.W, xm, ym, (int)a.N,
+                       (int)a.K, mt, c.R, c.S, c.log2mp, 1);
+    return (int)hipGetLastError();
   }
   if (xf)
     hipLaunchKernelGGL((k_gemv_mfma_lds<FMT, P, SX, 1>), grid, block, c.lds, a.stream, a.W, xm, ym, (int)a.N, (int)a.K,
@@ -1197,14 +1224,14 @@ int launch_mfma_split(const GemvArgs& a, int ns, const MfmaLdsCfg& c) {
     const int exf = tune(TUNE_MFMA_XF);
     const bool xf = exf != TUNE_UNSET ? exf != 0 : true;
     const dim3 grid((unsigned)((tiles + cc.R - 1) / cc.R), (unsigned)ns), block((unsigned)(64 * cc.R * cc.S));
-    const bool xdma = !cc.sx && mfma_x_dma((int)a.M, (int64_t)grid.x * ns, tiles);
+    const bool xdma = mfma_x_dma((int)a.M, (int64_t)grid.x * ns, tiles);
     dispatch_log("k_gemv_mfma_lds", a.fmt, a.N, a.K, (int)a.M, grid.x, grid.y, block.x, cc.lds,
                  "teams K-split=%d R=%d S=%d P=%d Mp=%d sums=%d x_first=%d x_dma=%d", ns, cc.R, cc.S, cc.P,
                  1 << cc.log2mp, cc.sx ? 1 : 0, xf ? 1 : 0, xdma ? 1 : 0);
 #define KQ_SPLIT_LAUNCH(PP, SXX)                                                                                  \
   do {                                                                                                           \
-    if (!(SXX) && xdma)                                                                                          \
-      hipLaunchKernelGGL((k_gemv_mfma_lds<FMT, PP, false, 2>), grid, block, cc.lds, a.stream, a.W, a.x, b.y,    \
+    if (xdma)                                                                                                    \
+      hipLaunchKernelGGL((k_gemv_mfma_lds<FMT, PP, SXX, 2>), grid, block, cc.lds, a.stream, a.W, a.x, b.y,      \
                          (int)a.N, (int)a.K, (int)a.M, cc.R, cc.S, cc.log2mp, ns);                               \
     else if (xf)                                                                                                 \
       hipLaunchKernelGGL((k_gemv_mfma_lds<FMT, PP, SXX, 1>), grid, block, cc.lds, a.stream, a.W, a.x, b.y,      \

@@ -212,20 +212,23 @@ def test_mfma_variants_parity(fmt, variant, N, K, M):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("variant", ("teams", "teams_sx"))
 @pytest.mark.parametrize("N,K,M", [(1000, 2560, 8), (37, 96, 5), (300, 4128, 16), (529, 640, 13), (2560, 4096, 8),
-                                   (6144, 2560, 7), (160, 9728, 12)])
-def test_teams_x_dma_same_bits(fmt, N, K, M):
-    """The teams kernel without block sums gives the same bits whether x is
-    staged by DMA in column-major order or through registers in operand order
-    (the same operands, products and sums in the same order)."""
+                                   (6144, 2560, 7), (160, 9728, 12), (1000, 2560, 4), (300, 4128, 3), (37, 96, 2),
+                                   (6144, 2560, 4), (2560, 9728, 4)])
+def test_teams_x_dma_same_bits(fmt, variant, N, K, M):
+    """The teams kernel, with block sums in LDS or an MFMA against ones per
+    block, gives the same bits whether x is staged by DMA in column-major
+    order or through registers in operand order (the same operands, block
+    sums, products and sums in the same order)."""
     packed, fields, x = _case(fmt, N, K, M, 19)
     Wd = U.to_dev(packed)
-    with U.tuning({"mfma_variant": "teams", "mfma_xdma": "1"}):
+    with U.tuning({"mfma_variant": variant, "mfma_xdma": "1"}):
         y1 = U.gemv_gpu(fmt, Wd, x, N, K, path="mfma")
-    with U.tuning({"mfma_variant": "teams", "mfma_xdma": "0"}):
+    with U.tuning({"mfma_variant": variant, "mfma_xdma": "0"}):
         y0 = U.gemv_gpu(fmt, Wd, x, N, K, path="mfma")
     yr, ad = R.gemv(fmt, fields, x)
-    U.assert_parity(y1, yr, ad, f"{fmt} teams x by DMA N={N} K={K} M={M}")
+    U.assert_parity(y1, yr, ad, f"{fmt} {variant} x by DMA N={N} K={K} M={M}")
     assert np.array_equal(y1.view(np.uint32), y0.view(np.uint32))
 
 
