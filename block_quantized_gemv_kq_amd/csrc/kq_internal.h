@@ -23,7 +23,7 @@ enum TuneKey {
   TUNE_MFMA_S,           // waves per tile (split-K teams kernel)
   TUNE_MFMA_R,           // tiles per workgroup (split-K teams kernel)
   TUNE_MFMA_WAVES,       // wave count below which the teams kernel doubles S
-  TUNE_MFMA_XF,          // teams kernel issue order: 1 x first, 0 weights first
+  TUNE_MFMA_XF,          // teams kernel, x through registers: 1 x written first, 0 weights first
   TUNE_MFMA_PERS_TPW,    // persistent kernel: tiles per wave
   TUNE_MFMA_PERS_WAVES,  // persistent kernel: waves per workgroup
   TUNE_MFMA_CHUNK_L2CG,  // chunked kernel: log2 of groups per chunk

@@ -629,7 +629,10 @@ __device__ __forceinline__ void mfma_group_cm(const GroupRaw<FMT>& cur, uint32_t
 // Few tiles (small N): a workgroup of R tiles x S waves; wave (r, s) owns
 // groups [s P, (s + 1) P) of tile r, all loaded before any arithmetic, and the
 // S partial results of a tile are summed in LDS in a fixed order. SX: block
-// sums in LDS (else, when x alone just fits, from an MFMA per block).
+// sums in LDS (else, when x alone just fits, from an MFMA per block). XM, how
+// x is staged: 2 by DMA in column-major order (stage_x_cm), 1 through
+// registers in operand order before the weight loads are issued, 0 through
+// registers with the weight loads issued first (stage_x_mfma).
 template <int FMT, int P, bool SX, int XM>
 __global__ __launch_bounds__(1024) void k_gemv_mfma_lds(const uint8_t* __restrict__ W,
                                                        const uint16_t* __restrict__ x,
