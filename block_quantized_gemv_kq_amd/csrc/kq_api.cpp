@@ -62,7 +62,7 @@ const TuneName kTuneNames[] = {
     {"moe_min_wg", kq::TUNE_MOE_MIN_WG},          {"log", kq::TUNE_LOG},
     {"mfma_pers_waves", kq::TUNE_MFMA_PERS_WAVES}, {"moe_one", kq::TUNE_MOE_ONE},
     {"mfma_split", kq::TUNE_MFMA_SPLIT},         {"sl_g", kq::TUNE_SL_G},
-    {"mfma_xdma", kq::TUNE_MFMA_XDMA},
+    {"mfma_xdma", kq::TUNE_MFMA_XDMA},           {"lds_xdma", kq::TUNE_LDS_XDMA},
 };
 
 // Parse a tuning value: force_path and mfma_variant take names, the others integers.

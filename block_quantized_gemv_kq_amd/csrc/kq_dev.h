@@ -458,18 +458,6 @@ __device__ __forceinline__ void valu_tile(rsrc_t rs, uint32_t row_bytes, int uni
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
 
-// Copy n16 16-byte chunks from global `src` to LDS `dst` (both 16-byte
-// aligned). Every thread of the workgroup (nthreads of them, a compile-time
-// constant at the call sites, so no kernel argument is read for it) must
-// call it; follow with __syncthreads() (which waits for the copies).
-__device__ __forceinline__ void stage_to_lds(const void* src, uint32_t* dst, int n16, int nthreads) {
-  for (int i = threadIdx.x; i < n16; i += nthreads) {
-    const int wave_first = i - (int)(threadIdx.x & 63);   // lane L lands at wave_first + L
-    __builtin_amdgcn_global_load_lds((glb_void_t*)(reinterpret_cast<const u32x4*>(src) + i),
-                                     (lds_void_t*)(dst + 4 * wave_first), 16, 0, 0);
-  }
-}
-
 // Padded staging of activations. The lane groups of a wave read x of
 // consecutive load units (UP = 4 UB pieces of 16 bytes each) at the same
 // piece offset, so with the pieces back to back the lanes of one LDS read
@@ -483,17 +471,24 @@ __host__ __device__ constexpr int xphys(int P) { return UP ? P + P / UP : P; }
 template <int UP>
 __host__ __device__ constexpr int xrun_pieces(int n16) { return UP ? n16 + n16 / UP : n16; }
 
-// stage_to_lds into the padded layout: slot s holds piece s - s / (UP + 1)
-// unless it is a unit's idle slot (s % (UP + 1) == UP), which is not written.
+// Copy n16 16-byte pieces from global `src` (16-byte aligned) into LDS `dst`
+// in the padded layout, with buffer-to-LDS loads (a wave instruction fills 64
+// consecutive slots, lane L slot wave_first + L): slot s holds piece
+// s - s / (UP + 1) unless it is a unit's idle slot (s % (UP + 1) == UP), which
+// is not written. Every thread of the workgroup (nthreads of them) must call
+// it; a later __syncthreads() waits for the copies. Buffer loads, not flat
+// ones: the compiler then counts them like the other loads, and a barrier
+// after later weight loads waits for the copies alone.
 template <int UP>
 __device__ __forceinline__ void stage_to_lds_padded(const void* src, uint32_t* dst, int n16, int nthreads) {
   const int nslot = xrun_pieces<UP>(n16);
+  const rsrc_t rs = make_rsrc(src, (uint32_t)n16 * 16u);
   for (int i = threadIdx.x; i < nslot; i += nthreads) {
     const int q = i / (UP + 1), r = i - q * (UP + 1);
     if (r < UP) {
-      const int wave_first = i - (int)(threadIdx.x & 63);   // lane L lands at wave_first + L
-      __builtin_amdgcn_global_load_lds((glb_void_t*)(reinterpret_cast<const u32x4*>(src) + q * UP + r),
-                                       (lds_void_t*)(dst + 4 * wave_first), 16, 0, 0);
+      const int wave_first = i - (int)(threadIdx.x & 63);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(dst + 4 * wave_first), 16,
+                                               (uint32_t)(q * UP + r) * 16u, 0, 0, 0);
     }
   }
 }

@@ -107,10 +107,11 @@ __global__ __launch_bounds__(64 * WPG) void k_gemv_lds(const uint8_t* __restrict
   // XREG: the activations go ahead of the weights in this CU's memory queue,
   // loaded into registers (at most xreg_chunks 16-byte chunks per thread), so
   // writing them to LDS waits for them alone and the block sums below overlap
-  // the weights' latency. Otherwise they are copied by LDS DMA (any K), which
-  // the first barrier waits for together with the weights. The two variants
-  // are separate kernels: with an LDS DMA anywhere in the kernel the compiler
-  // would make the register path's LDS writes wait for every load.
+  // the weights' latency. Otherwise they are copied by LDS DMA (any K), also
+  // ahead of the weights, so that the first barrier waits for the DMA alone
+  // (loads complete in order). The two variants are separate kernels: with an
+  // LDS DMA anywhere in the kernel the compiler would make the register
+  // path's LDS writes wait for every load.
   constexpr int XCH = xreg_chunks<MT, WPG>();
   const int n16 = MT * K / 8;   // columns m0 .. m0+MT-1 are contiguous
   u32x4 xr[XCH];
@@ -121,6 +122,8 @@ __global__ __launch_bounds__(64 * WPG) void k_gemv_lds(const uint8_t* __restrict
       const int i = (int)threadIdx.x + 64 * WPG * c;
       xr[c] = i < n16 ? xsrc[i] : u32x4{0u, 0u, 0u, 0u};
     }
+  } else {
+    stage_to_lds_padded<UP>(x + (int64_t)m0 * K, xl, n16, 64 * WPG);
   }
   __builtin_amdgcn_sched_barrier(0);
   Loaded<FMT, ITERS> w;
@@ -133,8 +136,6 @@ __global__ __launch_bounds__(64 * WPG) void k_gemv_lds(const uint8_t* __restrict
       const int i = (int)threadIdx.x + 64 * WPG * c;
       if (i < n16) xl4[xphys<UP>(i)] = xr[c];
     }
-  } else {
-    stage_to_lds_padded<UP>(x + (int64_t)m0 * K, xl, n16, 64 * WPG);
   }
   __syncthreads();
   block_sums_to_lds<UP>(xl, kdw, MT, xs, 64 * WPG);
@@ -406,7 +407,7 @@ int launch_lds_wpg(const GemvArgs& a, int m0, LdsCfg c, Best* part) {
   const int64_t nwg = (waves + WPG - 1) / WPG;
   const dim3 grid((unsigned)nwg), block(64 * WPG);
   const size_t lds = (size_t)lds_kernel_bytes<FMT>(MT, a.K);   // x (padded) + block sums
-  const bool xreg = (int64_t)MT * a.K / 8 <= 64 * WPG * xreg_chunks<MT, WPG>();
+  const bool xreg = (int64_t)MT * a.K / 8 <= 64 * WPG * xreg_chunks<MT, WPG>() && tune(TUNE_LDS_XDMA) != 1;
   dispatch_log("k_gemv_lds", a.fmt, a.N, a.K, MT, grid.x, 1, 64 * WPG, lds,
                "G=%d units/lane=%d passes=%d x=%s m0=%d argmax=%d", 1 << c.log2g, ITERS, c.passes,
                xreg ? "registers" : "lds-dma", m0, part ? 1 : 0);

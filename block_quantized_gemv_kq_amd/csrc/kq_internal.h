@@ -33,6 +33,7 @@ enum TuneKey {
   TUNE_MFMA_SPLIT,       // K splits of the teams kernel when a workspace is given (1: none)
   TUNE_SL_G,             // lanes per row of the Shortlist bound kernel
   TUNE_LOG,              // 1: one line per kernel launch on stderr (the dispatch log)
+  TUNE_LDS_XDMA,         // 1: the one-column LDS kernel copies x by DMA even where registers would do
   TUNE_MFMA_XDMA,        // teams kernel: 1 x by DMA, column-major; 0 through registers
   TUNE_COUNT
 };

@@ -439,7 +439,8 @@ int kq_stack_status(const void* plan, const kq_stack_info* info, int* error, voi
  *                    "chunk_split", "direct"
  *   valu_g, valu_r, lds_wpg, mfma_s, mfma_r, mfma_waves, mfma_xf,
  *   mfma_pers_tpw, mfma_pers_waves, mfma_chunk_l2cg, moe_unfused,
- *   moe_min_wg, moe_one, mfma_split, sl_g, mfma_xdma          (decimal integers)
+ *   moe_min_wg, moe_one, mfma_split, sl_g, mfma_xdma,
+ *   lds_xdma                                                  (decimal integers)
  *   log              "1": one line per kernel launch on stderr (kernel, format,
  *                    shape, grid, workgroup, LDS bytes, chosen configuration)
  * Errors: KQ_ERR_ARG (unknown name or malformed value). Not synchronised

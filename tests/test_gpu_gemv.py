@@ -247,6 +247,23 @@ def test_chunk_column_groups(fmt, N, K, M):
     assert np.array_equal(y, y2), "not deterministic run to run"
 
 
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("N,K,M", [(6144, 2560, 1), (2560, 4096, 1), (2560, 9728, 1), (19456, 2560, 1), (333, 1024, 2),
+                                   (77, 9728, 2), (1000, 640, 3), (151936 // 16, 2560, 1)])
+def test_lds_x_dma_same_bits(fmt, N, K, M):
+    """The one-column LDS kernel gives the same bits whether x goes through
+    registers or is copied by DMA ahead of the weight loads (the same padded
+    layout, block sums and products)."""
+    packed, fields, x = _case(fmt, N, K, M, 23)
+    Wd = U.to_dev(packed)
+    with U.tuning({"lds_xdma": "1"}):
+        y1 = U.gemv_gpu(fmt, Wd, x, N, K, path="lds")
+    y0 = U.gemv_gpu(fmt, Wd, x, N, K, path="lds")
+    yr, ad = R.gemv(fmt, fields, x)
+    U.assert_parity(y1, yr, ad, f"{fmt} lds x by DMA N={N} K={K} M={M}")
+    assert np.array_equal(y1.view(np.uint32), y0.view(np.uint32))
+
+
 @pytest.mark.parametrize("fmt", ("q8_0", "q4_0", "affine4", "q5_0", "q5_1"))
 @pytest.mark.parametrize("wpg", ("8", "12", "16"))
 def test_lds_waves_per_workgroup(fmt, wpg):
