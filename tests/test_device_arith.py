@@ -1,9 +1,7 @@
 """Host models of index arithmetic in the matrix-core kernels (no GPU): the
 small integer division, and the column-major x staging by DMA (below).
 
-The division:
-
-The teams and K-chunked kernels split a workgroup's wave index by the waves per
+The division: the teams and K-chunked kernels split a workgroup's wave index by the waves per
 tile, and a K split's group range by the split count, as
 floor((a + 1/2) * rcp(b)) in fp32 instead of an integer division sequence.
 The quotient (a + 1/2) / b lies at least 1 / (2 b) from an integer; the test
