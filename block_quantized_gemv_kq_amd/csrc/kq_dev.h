@@ -592,7 +592,7 @@ __device__ __forceinline__ float block_dot_split(const uint32_t* A, const uint32
 // xl + m * kdw dwords, so the columns are one contiguous run): for column m
 // and block b, xs[(m * nblk + b) * 2 + {0,1}] = sum of elements 0..15 / 16..31,
 // i.e. xs[h] is the sum of half-block h of the run. Every thread of the
-// workgroup (nthreads, as for stage_to_lds) takes part; follow with
+// workgroup (nthreads, as for stage_to_lds_padded) takes part; follow with
 // __syncthreads().
 template <int UP = 0>
 __device__ __forceinline__ void block_sums_to_lds(const uint32_t* xl, int kdw, int mt, float* xs, int nthreads) {
